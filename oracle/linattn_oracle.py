@@ -1,0 +1,373 @@
+"""fp64 CPU oracle for causal linear attention.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path imports, calls or
+links this module: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with the
+HIP library and never imports it.
+
+Everything is plain numpy in float64.  Inputs are taken exactly as the GPU
+path receives them (bf16/fp16/fp32 values) and upcast to float64 here.
+
+Sources (the three pages the method is described on):
+
+* [kb]     llm-arch-kb "Linear Attention", section 2 "Derivation" (causal
+           recurrence, symbol legend, compute cost) and section 3 "Reference
+           implementation" (non-causal and causal sketches).
+* [lesson] efficient-attention lesson "Linear attention": Researcher level,
+           "Derivation" (the general sim-attention sum, its factorised form,
+           the recurrence for S_i and z_i, and the read-out); Developer level,
+           "The regrouping, and the recurrence it implies" (bracketings,
+           masked-quadratic check, eps = 1e-6 in the divisor) and "Try it
+           yourself" (constant decay and its weighted quadratic form).
+* [card]   wikillm "Linear attention": "Implementation sketch" (scalar decay
+           applied to the old state and normaliser; current term undecayed),
+           "Variants / Random Fourier features (RFA)" (Gaussian random
+           projections, sigmoid gate that decays the old state and scales the
+           new term by one minus the gate), "Decaying linear attention with a
+           scalar state (SSD)" (decay 1 is the plain causal case).
+
+Every function is pinned by ``tests/test_oracle_pins.py`` against facts the
+pages or the mathematics fix (closed forms, brute force, printed values).
+
+Layout convention: ``[..., T, d]`` with any leading dims (batch, head);
+decay/gate arrays are ``[..., T]``.  Feature dimension ``d'`` is ``d_h`` for
+elu+1 and ``2 * D`` for random Fourier features.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+F64 = np.float64
+
+
+def _f64(x):
+    """Upcast a numpy array or torch tensor (any float dtype) to float64."""
+    if x is None:
+        return None
+    if hasattr(x, "detach"):  # torch tensor: bf16 has no numpy dtype
+        x = x.detach().cpu().double().numpy()
+    return np.asarray(x, dtype=F64)
+
+
+# --------------------------------------------------------------------------
+# Feature maps
+# --------------------------------------------------------------------------
+
+def phi_elu1(x):
+    """elu(x) + 1 with alpha = 1, element-wise, so d' = d_h.
+
+    [kb] section 2, symbol legend (phi(x) = elu(x) + 1, d' = d_h in the
+    paper's experiments); [lesson] Developer level (PyTorch's elu default).
+    elu(x) = x for x > 0 and exp(x) - 1 otherwise, hence phi = x + 1 or exp(x).
+    """
+    x = _f64(x)
+    return np.where(x > 0, x + 1.0, np.exp(np.minimum(x, 0.0)))
+
+
+def phi_rff(x, W):
+    """Random Fourier features: D^{-1/2} [sin(W x); cos(W x)].
+
+    [card] Variants / RFA: Gaussian random projections whose feature inner
+    products estimate a Gaussian kernel.  ``x``: [..., H, T, d_h];
+    ``W``: [H, D, d_h] (one projection per head).  Output: [..., H, T, 2D],
+    sines first, then cosines.  No bias/phase term, sigma = 1.
+    """
+    x = _f64(x)
+    W = _f64(W)
+    D = W.shape[-2]
+    proj = np.einsum("...htd,hjd->...htj", x, W)
+    return np.concatenate([np.sin(proj), np.cos(proj)], axis=-1) / np.sqrt(D)
+
+
+def features(x, phi="elu1", W=None):
+    if phi == "elu1":
+        return phi_elu1(x)
+    if phi == "rff":
+        if W is None:
+            raise ValueError("rff feature map needs W")
+        return phi_rff(x, W)
+    raise ValueError(f"unknown feature map {phi!r}")
+
+
+def decay_coefficients(decay=None, gate=None):
+    """Per-token (alpha, beta) of S_t = alpha_t S_{t-1} + beta_t phi(k_t) v_t^T.
+
+    * no decay: alpha = beta = 1 (returned as None, i.e. no multiply at all);
+    * SSD scalar decay a_t: alpha = a_t, beta = 1 ([card] Implementation
+      sketch: the decay multiplies the old state and the old normaliser);
+    * RFA gate g_t: alpha = g_t, beta = 1 - g_t ([card] Variants / RFA and
+      Implementation sketch: the gate decays the old state and scales the
+      new term by one minus the gate).
+    """
+    if decay is not None and gate is not None:
+        raise ValueError("decay and gate are exclusive")
+    if decay is not None:
+        return _f64(decay), None
+    if gate is not None:
+        g = _f64(gate)
+        return g, 1.0 - g
+    return None, None
+
+
+# --------------------------------------------------------------------------
+# The recurrence (the method's algorithm)
+# --------------------------------------------------------------------------
+
+def recurrence(fq, fk, v, alpha=None, beta=None, eps=1e-6, S0=None, z0=None):
+    """Causal linear attention as an RNN over t, in float64.
+
+    For each t (in order):
+        S_t = alpha_t S_{t-1} + beta_t phi(k_t) v_t^T      (d' x d_v)
+        z_t = alpha_t z_{t-1} + beta_t phi(k_t)            (d')
+        o_t = S_t^T phi(q_t) / (z_t^T phi(q_t) + eps)
+    The read-out uses the state after token t is added (inclusive causal
+    sum).  [lesson] Researcher level, Derivation (recurrence and read-out);
+    [kb] section 3 causal sketch (eps added to the denominator);
+    [card] Implementation sketch (decay on the old state only).
+
+    fq, fk: [..., T, d'] features; v: [..., T, d_v]; alpha, beta: [..., T]
+    or None.  S0: [..., d', d_v], z0: [..., d'] (default zero state).
+    Returns (o [..., T, d_v], S_T, z_T).
+    """
+    fq, fk, v = _f64(fq), _f64(fk), _f64(v)
+    lead = fq.shape[:-2]
+    T, dp = fq.shape[-2], fq.shape[-1]
+    dv = v.shape[-1]
+    S = np.zeros(lead + (dp, dv), F64) if S0 is None else _f64(S0).copy()
+    z = np.zeros(lead + (dp,), F64) if z0 is None else _f64(z0).copy()
+    alpha = _f64(alpha)
+    beta = _f64(beta)
+    o = np.empty(lead + (T, dv), F64)
+    for t in range(T):
+        k_t = fk[..., t, :]
+        new_S = k_t[..., :, None] * v[..., t, None, :]
+        new_z = k_t
+        if beta is not None:
+            b = beta[..., t]
+            new_S = b[..., None, None] * new_S
+            new_z = b[..., None] * new_z
+        if alpha is not None:
+            a = alpha[..., t]
+            S = a[..., None, None] * S + new_S
+            z = a[..., None] * z + new_z
+        else:
+            S = S + new_S
+            z = z + new_z
+        q_t = fq[..., t, :]
+        num = np.einsum("...d,...dv->...v", q_t, S)
+        den = np.einsum("...d,...d->...", q_t, z)
+        o[..., t, :] = num / (den + eps)[..., None]
+    return o, S, z
+
+
+def causal_linear_attention(q, k, v, phi="elu1", W=None, decay=None, gate=None,
+                            eps=1e-6, S0=None, z0=None):
+    """Feature map, then the recurrence.  Returns (o, S, z) in float64.
+
+    q, k: [..., H, T, d_h]; v: [..., H, T, d_v]; W: [H, D, d_h] for RFF.
+    [card] Implementation sketch (the pluggable-feature-map loop).
+    """
+    fq = features(q, phi, W)
+    fk = features(k, phi, W)
+    alpha, beta = decay_coefficients(decay, gate)
+    return recurrence(fq, fk, v, alpha, beta, eps, S0, z0)
+
+
+def decode_step(q, k, v, S, z, phi="elu1", W=None, decay=None, gate=None, eps=1e-6):
+    """One autoregressive step from state (S, z): q, k [..., H, d_h], v [..., H, d_v],
+    decay/gate [..., H].  Returns (o [..., H, d_v], S', z').
+
+    [kb] section 2, causal recurrence (constant-state RNN step).
+    """
+    q, k, v = _f64(q)[..., None, :], _f64(k)[..., None, :], _f64(v)[..., None, :]
+    decay = None if decay is None else _f64(decay)[..., None]
+    gate = None if gate is None else _f64(gate)[..., None]
+    o, S, z = causal_linear_attention(q, k, v, phi, W, decay, gate, eps, S, z)
+    return o[..., 0, :], S, z
+
+
+# --------------------------------------------------------------------------
+# The definition (masked quadratic form), used to pin the recurrence and to
+# compute sampled outputs at full size one by one
+# --------------------------------------------------------------------------
+
+def decay_products(alpha, T):
+    """P[..., t, s] = prod_{r=s+1..t} alpha_r for s <= t, else 0 (products
+    taken directly, no logarithms, so alpha = 0 is exact)."""
+    if alpha is None:
+        return np.tril(np.ones((T, T), F64))
+    alpha = _f64(alpha)
+    lead = alpha.shape[:-1]
+    P = np.zeros(lead + (T, T), F64)
+    for t in range(T):
+        run = np.ones(lead, F64)
+        for s in range(t, -1, -1):
+            P[..., t, s] = run
+            run = run * alpha[..., s]
+    return P
+
+
+def masked_quadratic(fq, fk, v, alpha=None, beta=None, eps=1e-6):
+    """o_t = sum_{s<=t} w_ts v_s / (sum_{s<=t} w_ts + eps) with
+    w_ts = (phi(q_t) . phi(k_s)) * beta_s * prod_{r=s+1..t} alpha_r.
+
+    With no decay this is scores * tril(1) ([lesson] Developer level, the
+    masked quadratic check; Researcher level, the sim-attention sum over
+    j <= i).  With a constant decay it is the weighted quadratic form asked
+    for in [lesson] "Try it yourself".  Zero initial state.  O(T^2).
+    """
+    fq, fk, v = _f64(fq), _f64(fk), _f64(v)
+    T = fq.shape[-2]
+    scores = fq @ np.swapaxes(fk, -1, -2)
+    w = scores * decay_products(alpha, T)
+    if beta is not None:
+        w = w * _f64(beta)[..., None, :]
+    num = w @ v
+    den = w.sum(axis=-1)
+    return num / (den + eps)[..., None]
+
+
+def kernel_attention_by_definition(fq, fk, v, alpha=None, beta=None, eps=1e-6):
+    """Pure-Python double loop over one head: o_i = sum_{j<=i} sim_ij v_j /
+    (sum_{j<=i} sim_ij + eps), sim_ij = phi(q_i).phi(k_j) times the decay
+    weight.  Tiny inputs only.  [lesson] Researcher level, Derivation."""
+    fq, fk, v = _f64(fq), _f64(fk), _f64(v)
+    T, dv = fq.shape[0], v.shape[1]
+    out = np.zeros((T, dv), F64)
+    for i in range(T):
+        num = [0.0] * dv
+        den = 0.0
+        for j in range(i + 1):
+            sim = sum(float(fq[i, c]) * float(fk[j, c]) for c in range(fq.shape[1]))
+            wgt = 1.0 if beta is None else float(beta[j])
+            for r in range(j + 1, i + 1):
+                wgt *= 1.0 if alpha is None else float(alpha[r])
+            sim *= wgt
+            den += sim
+            for c in range(dv):
+                num[c] += sim * float(v[j, c])
+        for c in range(dv):
+            out[i, c] = num[c] / (den + eps)
+    return out
+
+
+def output_at(fq_t, fk, v, t, alpha=None, beta=None, eps=1e-6, S0=None, z0=None):
+    """The definition evaluated at one position t (O(t d)), including the
+    carried-in state (S0, z0) decayed by prod_{r=0..t} alpha_r.
+
+    fq_t: [..., d'] (features of query t); fk: [..., T, d']; v: [..., T, d_v].
+    """
+    fq_t, fk, v = _f64(fq_t), _f64(fk)[..., : t + 1, :], _f64(v)[..., : t + 1, :]
+    sims = np.einsum("...d,...sd->...s", fq_t, fk)
+    lead = sims.shape[:-1]
+    if alpha is not None:
+        a = _f64(alpha)[..., : t + 1]
+        # weight of key s: prod_{r=s+1..t} alpha_r  (reverse cumulative product)
+        rev = np.cumprod(a[..., :0:-1], axis=-1)[..., ::-1]
+        wts = np.concatenate([rev, np.ones(lead + (1,), F64)], axis=-1)
+        carry = np.prod(a, axis=-1)
+    else:
+        wts = np.ones(lead + (t + 1,), F64)
+        carry = np.ones(lead, F64)
+    if beta is not None:
+        wts = wts * _f64(beta)[..., : t + 1]
+    w = sims * wts
+    num = np.einsum("...s,...sv->...v", w, v)
+    den = w.sum(axis=-1)
+    if S0 is not None:
+        num = num + carry[..., None] * np.einsum("...d,...dv->...v", fq_t, _f64(S0))
+    if z0 is not None:
+        den = den + carry * np.einsum("...d,...d->...", fq_t, _f64(z0))
+    return num / (den + eps)[..., None]
+
+
+def final_state(fk, v, alpha=None, beta=None, S0=None, z0=None):
+    """S_T = (prod alpha) S0 + sum_s w_s phi(k_s) v_s^T and likewise z_T, with
+    w_s = beta_s prod_{r=s+1..T-1} alpha_r: the closed form of the state after
+    T tokens ([lesson] Researcher level: both sums are prefix sums)."""
+    fk, v = _f64(fk), _f64(v)
+    T = fk.shape[-2]
+    lead = fk.shape[:-2]
+    if alpha is not None:
+        a = _f64(alpha)
+        rev = np.cumprod(a[..., :0:-1], axis=-1)[..., ::-1]
+        w = np.concatenate([rev, np.ones(lead + (1,), F64)], axis=-1)
+        carry = np.prod(a, axis=-1)
+    else:
+        w = np.ones(lead + (T,), F64)
+        carry = np.ones(lead, F64)
+    if beta is not None:
+        w = w * _f64(beta)
+    S = np.einsum("...s,...sd,...sv->...dv", w, fk, v)
+    z = np.einsum("...s,...sd->...d", w, fk)
+    if S0 is not None:
+        S = S + carry[..., None, None] * _f64(S0)
+    if z0 is not None:
+        z = z + carry[..., None] * _f64(z0)
+    return S, z
+
+
+# --------------------------------------------------------------------------
+# Non-causal bracketings ([kb] section 3 non-causal sketch; [lesson] Developer
+# level, "Two ways to bracket the same product")
+# --------------------------------------------------------------------------
+
+def noncausal_left(fq, fk, v, eps=1e-6):
+    """((phi(Q) phi(K)^T) V) / ((phi(Q) phi(K)^T) 1 + eps): T x T scores first."""
+    fq, fk, v = _f64(fq), _f64(fk), _f64(v)
+    A = fq @ np.swapaxes(fk, -1, -2)
+    return (A @ v) / (A.sum(axis=-1) + eps)[..., None]
+
+
+def noncausal_right(fq, fk, v, eps=1e-6):
+    """(phi(Q) (phi(K)^T V)) / (phi(Q) (phi(K)^T 1) + eps): d' x d_v state first."""
+    fq, fk, v = _f64(fq), _f64(fk), _f64(v)
+    S = np.swapaxes(fk, -1, -2) @ v
+    z = fk.sum(axis=-2)
+    return (fq @ S) / (np.einsum("...td,...d->...t", fq, z) + eps)[..., None]
+
+
+# --------------------------------------------------------------------------
+# Accounting the pages print
+# --------------------------------------------------------------------------
+
+def state_update_ops(T, d_prime, d_h):
+    """T rank-one updates of O(d' d_h) each ([kb] section 2, compute cost)."""
+    return T * d_prime * d_h
+
+
+def softmax_ops(T, d_h):
+    """The T x T score matrix times d_h ([kb] section 2, compute cost)."""
+    return T * T * d_h
+
+
+def state_numbers(d_prime, d_v):
+    """Numbers held by S ([lesson] Developer level: S is d x d, never grows)."""
+    return d_prime * d_v
+
+
+def kv_cache_numbers(t, d):
+    """A softmax KV cache at step t holds 2 t d numbers ([lesson] Developer level)."""
+    return 2 * t * d
+
+
+def worked_example_report(q, k, v, eps=1e-6):
+    """The checks of the pages' T=8, d=4 example, evaluated in float64:
+    bracketing agreement, shapes of (q k^T) and (k^T V), recurrent vs masked
+    quadratic agreement and their max difference, state size, KV-cache size.
+    ([lesson] Developer level, "The regrouping, and the recurrence it implies")."""
+    fq, fk, vv = phi_elu1(q), phi_elu1(k), _f64(v)
+    left = (fq @ fk.T) @ vv
+    right = fq @ (fk.T @ vv)
+    o_rnn, S, _ = recurrence(fq, fk, vv, eps=eps)
+    o_quad = masked_quadratic(fq, fk, vv, eps=eps)
+    T, d = fq.shape
+    return dict(
+        associative=bool(np.allclose(left, right, rtol=1e-5, atol=1e-5)),
+        qkT_shape=tuple((fq @ fk.T).shape),
+        kTv_shape=tuple((fk.T @ vv).shape),
+        recurrent_matches_quadratic=bool(np.allclose(o_rnn, o_quad, rtol=1e-5, atol=1e-4)),
+        max_difference=float(np.abs(o_rnn - o_quad).max()),
+        state_numel=int(S.size),
+        kv_cache_numbers=kv_cache_numbers(T, d),
+    )

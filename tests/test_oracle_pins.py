@@ -1,0 +1,351 @@
+"""Pins for the fp64 oracle: each check rests on something other than the
+oracle itself -- a value the pages print, a closed form, a brute-force
+definition, or an identity the mathematics fixes.  CPU only.
+
+The last group plants plausible mistakes in copies of the oracle's
+recurrence and checks that the pins catch every one of them.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import linattn_oracle as O
+from fixed_state_sequence_amd import inputs as I
+from conftest import read_golden
+
+RNG = np.random.default_rng(1234)
+
+
+def rand(*shape, rng=RNG):
+    return rng.standard_normal(shape)
+
+
+# ---------------------------------------------------------------- feature maps
+
+def test_elu1_closed_form():
+    x = np.array([-50.0, -2.0, -1.0, -1e-12, 0.0, 1e-12, 0.5, 1.0, 2.5, 30.0])
+    ref = np.array([math.exp(-50.0), math.exp(-2.0), math.exp(-1.0), math.exp(-1e-12),
+                    1.0, 1.0 + 1e-12, 1.5, 2.0, 3.5, 31.0])
+    np.testing.assert_allclose(O.phi_elu1(x), ref, rtol=1e-15, atol=0)
+    assert O.phi_elu1(0.0) == 1.0          # both branches meet at 1
+    assert np.all(O.phi_elu1(rand(1000) * 10) > 0)  # non-negative map
+    assert np.isfinite(O.phi_elu1(np.array([-1e30]))).all()
+
+
+def test_rff_unit_norm_any_input():
+    # sin^2 + cos^2 = 1 for each of the D pairs, scaled by 1/D: ||phi(x)||^2 = 1
+    W = rand(3, 16, 8)
+    x = rand(2, 3, 5, 8) * 7
+    f = O.phi_rff(x, W)
+    assert f.shape == (2, 3, 5, 32)
+    np.testing.assert_allclose((f * f).sum(-1), 1.0, rtol=0, atol=1e-14)
+
+
+def test_rff_estimates_gaussian_kernel():
+    # E[phi(x).phi(y)] = exp(-||x - y||^2 / 2) for W ~ N(0, I)  (RFA's kernel)
+    rng = np.random.default_rng(7)
+    d, D = 8, 1 << 16
+    x = rng.standard_normal(d); x /= np.linalg.norm(x)
+    y = rng.standard_normal(d); y /= np.linalg.norm(y)
+    W = rng.standard_normal((1, D, d))
+    fx = O.phi_rff(x[None, None, :], W)[0, 0]
+    fy = O.phi_rff(y[None, None, :], W)[0, 0]
+    expect = math.exp(-np.sum((x - y) ** 2) / 2)
+    # each of the D cos(w.(x-y)) terms has variance <= 1/2: 4 sigma < 0.012
+    assert abs(fx @ fy - expect) < 0.012
+
+
+def test_rff_output_invariant_to_feature_order():
+    W = rand(2, 6, 4)
+    q, k, v = rand(2, 7, 4), rand(2, 7, 4), rand(2, 7, 3)
+    o1, _, _ = O.causal_linear_attention(q, k, v, phi="rff", W=W)
+    perm = RNG.permutation(6)
+    o2, _, _ = O.causal_linear_attention(q, k, v, phi="rff", W=W[:, perm, :])
+    np.testing.assert_allclose(o1, o2, rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------- recurrence vs the definition
+
+KINDS = ["none", "ssd", "rfa"]
+
+
+def coeffs(kind, shape, rng=RNG):
+    if kind == "none":
+        return None, None
+    g = 1.0 / (1.0 + np.exp(-rng.standard_normal(shape)))
+    return O.decay_coefficients(decay=g) if kind == "ssd" else O.decay_coefficients(gate=g)
+
+
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("T,dp,dv", [(1, 1, 1), (2, 3, 2), (5, 4, 4), (9, 3, 5)])
+def test_recurrence_equals_bruteforce_definition(kind, T, dp, dv):
+    fq, fk = np.abs(rand(T, dp)) + 0.1, np.abs(rand(T, dp)) + 0.1
+    v = rand(T, dv)
+    alpha, beta = coeffs(kind, (T,))
+    o, _, _ = O.recurrence(fq, fk, v, alpha, beta, eps=1e-6)
+    ref = O.kernel_attention_by_definition(fq, fk, v, alpha, beta, eps=1e-6)
+    np.testing.assert_allclose(o, ref, rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("T,d,dv", [(64, 8, 8), (33, 16, 4), (17, 4, 12)])
+def test_recurrence_equals_masked_quadratic(kind, T, d, dv):
+    q, k, v = rand(2, 3, T, d), rand(2, 3, T, d), rand(2, 3, T, dv)
+    fq, fk = O.phi_elu1(q), O.phi_elu1(k)
+    alpha, beta = coeffs(kind, (2, 3, T))
+    o, _, _ = O.recurrence(fq, fk, v, alpha, beta)
+    ref = O.masked_quadratic(fq, fk, v, alpha, beta)
+    np.testing.assert_allclose(o, ref, rtol=1e-11, atol=1e-12)
+
+
+def test_masked_quadratic_equals_bruteforce_definition():
+    fq, fk, v = O.phi_elu1(rand(6, 3)), O.phi_elu1(rand(6, 3)), rand(6, 2)
+    a = np.array([0.9, 0.0, 0.5, 1.0, 0.3, 0.7])   # includes an exact reset (0)
+    np.testing.assert_allclose(O.masked_quadratic(fq, fk, v, a),
+                               O.kernel_attention_by_definition(fq, fk, v, a),
+                               rtol=1e-12, atol=1e-14)
+
+
+def test_decay_zero_resets_state():
+    # a_t = 0 forgets everything before t: o_t only sees token t
+    fq, fk, v = O.phi_elu1(rand(5, 4)), O.phi_elu1(rand(5, 4)), rand(5, 3)
+    a = np.array([1.0, 1.0, 0.0, 1.0, 1.0])
+    o, _, _ = O.recurrence(fq, fk, v, a)
+    o_tail, _, _ = O.recurrence(fq[2:], fk[2:], v[2:])
+    np.testing.assert_allclose(o[2:], o_tail, rtol=1e-14, atol=1e-15)
+
+
+def test_noncausal_bracketings_agree():
+    q, k, v = rand(3, 50, 8), rand(3, 50, 8), rand(3, 50, 5)
+    fq, fk = O.phi_elu1(q), O.phi_elu1(k)
+    np.testing.assert_allclose(O.noncausal_left(fq, fk, v), O.noncausal_right(fq, fk, v),
+                               rtol=1e-12, atol=1e-13)
+
+
+def test_weights_are_causal_and_sum_to_one():
+    # Feeding V = I makes o_t[s] the attention weight of key s at query t:
+    # zero for s > t, non-negative, and summing to one when eps = 0.
+    T, d = 12, 6
+    fq, fk = O.phi_elu1(rand(T, d)), O.phi_elu1(rand(T, d))
+    Wt, S, z = O.recurrence(fq, fk, np.eye(T), eps=0.0)
+    assert np.all(np.triu(Wt, 1) == 0.0)
+    assert np.all(Wt >= 0)
+    np.testing.assert_allclose(Wt.sum(-1), 1.0, rtol=0, atol=1e-14)
+    # weight = phi(q_t).phi(k_s) / phi(q_t).z_t, with z_T from the recurrence
+    np.testing.assert_allclose(Wt[-1], (fq[-1] @ fk.T) / (fq[-1] @ z), rtol=1e-13)
+
+
+def test_outputs_in_convex_hull_of_values():
+    T, d, dv = 40, 5, 3
+    fq, fk, v = O.phi_elu1(rand(T, d)), O.phi_elu1(rand(T, d)), rand(T, dv)
+    o, _, _ = O.recurrence(fq, fk, v, eps=0.0)
+    lo = np.minimum.accumulate(v, axis=0)
+    hi = np.maximum.accumulate(v, axis=0)
+    assert np.all(o >= lo - 1e-12) and np.all(o <= hi + 1e-12)
+
+
+def test_first_output_closed_form():
+    fq, fk, v = O.phi_elu1(rand(4, 3)), O.phi_elu1(rand(4, 3)), rand(4, 2)
+    o, _, _ = O.recurrence(fq, fk, v, eps=1e-6)
+    s = fq[0] @ fk[0]
+    np.testing.assert_allclose(o[0], s * v[0] / (s + 1e-6), rtol=1e-15)
+
+
+# ----------------------------------------------------------------- decay / gate
+
+def test_decay_one_is_bitwise_plain_causal():
+    q, k, v = rand(2, 30, 8), rand(2, 30, 8), rand(2, 30, 8)
+    o1, S1, z1 = O.causal_linear_attention(q, k, v)
+    o2, S2, z2 = O.causal_linear_attention(q, k, v, decay=np.ones((2, 30)))
+    assert np.array_equal(o1, o2) and np.array_equal(S1, S2) and np.array_equal(z1, z2)
+
+
+def test_constant_decay_matches_weighted_quadratic_form():
+    # The pages' exercise: S = 0.9 S + phi(k) v^T no longer matches the plain
+    # masked form; it matches weights 0.9^(t-s) on scores, s <= t.
+    T = 20
+    fq, fk, v = O.phi_elu1(rand(T, 4)), O.phi_elu1(rand(T, 4)), rand(T, 4)
+    o, _, _ = O.recurrence(fq, fk, v, alpha=np.full(T, 0.9))
+    t_idx = np.arange(T)
+    wts = np.where(t_idx[:, None] >= t_idx[None, :],
+                   0.9 ** (t_idx[:, None] - t_idx[None, :]).clip(min=0), 0.0)
+    scores = (fq @ fk.T) * wts
+    ref = (scores @ v) / (scores.sum(-1) + 1e-6)[:, None]
+    np.testing.assert_allclose(o, ref, rtol=1e-12, atol=1e-13)
+    plain = O.masked_quadratic(fq, fk, v)
+    assert np.abs(o - plain).max() > 1e-2
+
+
+def test_gate_zero_keeps_only_current_token():
+    T = 9
+    fq, fk, v = O.phi_elu1(rand(T, 4)), O.phi_elu1(rand(T, 4)), rand(T, 3)
+    alpha, beta = O.decay_coefficients(gate=np.zeros(T))
+    o, _, _ = O.recurrence(fq, fk, v, alpha, beta)
+    s = np.sum(fq * fk, axis=-1)
+    np.testing.assert_allclose(o, s[:, None] * v / (s + 1e-6)[:, None], rtol=1e-14)
+
+
+def test_gate_one_freezes_state():
+    T = 7
+    fq, fk, v = O.phi_elu1(rand(T, 4)), O.phi_elu1(rand(T, 4)), rand(T, 3)
+    S0, z0 = rand(4, 3), np.abs(rand(4)) + 1
+    alpha, beta = O.decay_coefficients(gate=np.ones(T))
+    o, S, z = O.recurrence(fq, fk, v, alpha, beta, S0=S0, z0=z0)
+    np.testing.assert_allclose(S, S0, rtol=0, atol=0)
+    np.testing.assert_allclose(o, (fq @ S0) / (fq @ z0 + 1e-6)[:, None], rtol=1e-14)
+
+
+def test_gate_equals_ssd_with_scaled_keys():
+    # S = g S + (1-g) phi(k) v^T is the SSD form with a = g and phi(k)*(1-g)
+    T = 25
+    fq, fk, v = O.phi_elu1(rand(T, 6)), O.phi_elu1(rand(T, 6)), rand(T, 5)
+    g = 1 / (1 + np.exp(-rand(T)))
+    a1, b1 = O.decay_coefficients(gate=g)
+    o1, S1, z1 = O.recurrence(fq, fk, v, a1, b1)
+    o2, S2, z2 = O.recurrence(fq, fk * (1 - g)[:, None], v, alpha=g)
+    np.testing.assert_allclose(o1, o2, rtol=1e-13)
+    np.testing.assert_allclose(S1, S2, rtol=1e-13)
+
+
+# ------------------------------------------------------------- state carrying
+
+@pytest.mark.parametrize("kind", KINDS)
+def test_continuation_is_bitwise(kind):
+    T, T1 = 40, 17
+    q, k, v = rand(2, T, 8), rand(2, T, 8), rand(2, T, 4)
+    g = 1 / (1 + np.exp(-rand(2, T)))
+    kw = {} if kind == "none" else ({"decay": g} if kind == "ssd" else {"gate": g})
+    cut = lambda d, sl: {n: a[:, sl] for n, a in d.items()}
+    o, S, z = O.causal_linear_attention(q, k, v, **kw)
+    oa, Sa, za = O.causal_linear_attention(q[:, :T1], k[:, :T1], v[:, :T1], **cut(kw, slice(0, T1)))
+    ob, Sb, zb = O.causal_linear_attention(q[:, T1:], k[:, T1:], v[:, T1:], S0=Sa, z0=za,
+                                           **cut(kw, slice(T1, T)))
+    assert np.array_equal(o, np.concatenate([oa, ob], axis=1))
+    assert np.array_equal(S, Sb) and np.array_equal(z, zb)
+
+
+def test_decode_steps_continue_prefill():
+    H, T, dh, D = 2, 10, 4, 3
+    W = rand(H, D, dh)
+    q, k, v = rand(H, T, dh), rand(H, T, dh), rand(H, T, 5)
+    g = 1 / (1 + np.exp(-rand(H, T)))
+    o, S, z = O.causal_linear_attention(q, k, v, phi="rff", W=W, gate=g)
+    oa, Sa, za = O.causal_linear_attention(q[:, :6], k[:, :6], v[:, :6], phi="rff", W=W,
+                                           gate=g[:, :6])
+    for t in range(6, T):
+        ot, Sa, za = O.decode_step(q[:, t], k[:, t], v[:, t], Sa, za, phi="rff", W=W,
+                                   gate=g[:, t])
+        np.testing.assert_allclose(ot, o[:, t], rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(Sa, S, rtol=1e-13, atol=1e-14)
+
+
+@pytest.mark.parametrize("kind", KINDS)
+def test_output_at_matches_recurrence_with_initial_state(kind):
+    T, d, dv = 50, 6, 3
+    fq, fk, v = O.phi_elu1(rand(2, T, d)), O.phi_elu1(rand(2, T, d)), rand(2, T, dv)
+    S0, z0 = rand(2, d, dv), np.abs(rand(2, d)) + 1
+    alpha, beta = coeffs(kind, (2, T))
+    o, S, z = O.recurrence(fq, fk, v, alpha, beta, S0=S0, z0=z0)
+    for t in [0, 1, 17, T - 1]:
+        ot = O.output_at(fq[:, t], fk, v, t, alpha, beta, S0=S0, z0=z0)
+        np.testing.assert_allclose(ot, o[:, t], rtol=1e-11, atol=1e-12)
+    Sf, zf = O.final_state(fk, v, alpha, beta, S0, z0)
+    np.testing.assert_allclose(Sf, S, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(zf, z, rtol=1e-12)
+
+
+# ------------------------------------------------------ the pages' own numbers
+
+def test_worked_example_reproduces_printed_output():
+    gold = read_golden("worked_example.txt")
+    q, k, v = I.tiny_worked_example()
+    rep = O.worked_example_report(q, k, v)
+    assert rep["associative"] is (gold["associative"] == "True")
+    assert rep["qkT_shape"] == tuple(int(s) for s in gold["qkT_shape"].split())
+    assert rep["kTv_shape"] == tuple(int(s) for s in gold["kTv_shape"].split())
+    assert rep["recurrent_matches_quadratic"] is (gold["recurrent_matches_quadratic"] == "True")
+    assert rep["state_numel"] == int(gold["state_numel"])
+    assert rep["kv_cache_numbers"] == int(gold["kv_cache_numbers"])
+    # the printed fp32 difference bounds the fp64 one (which is ~1e-16)
+    assert rep["max_difference"] <= float(gold["max_difference"])
+    assert rep["max_difference"] < 1e-13
+    # the inputs are the page's: first drawn value of Q under seed 0
+    assert abs(float(q[0, 0]) - (-1.1258)) < 1e-4
+
+
+def test_crossover_table():
+    gold = read_golden("worked_example.txt")
+    for row in gold["crossover"]:
+        n, sm, lin, ratio = row.split()
+        n = int(n)
+        assert O.softmax_ops(n, 4) == int(sm)
+        assert O.state_update_ops(n, 4, 4) == int(lin)
+        assert round(O.softmax_ops(n, 4) / O.state_update_ops(n, 4, 4), 1) == float(ratio)
+
+
+def test_op_counts_at_100k():
+    gold = read_golden("op_counts.txt")
+    T, d = int(gold["T"]), int(gold["d"])
+    lin, sm = O.state_update_ops(T, d, d), O.softmax_ops(T, d)
+    assert float(f"{lin:.1e}") == float(gold["linear_ops_2sf"])
+    assert float(f"{sm:.1e}") == float(gold["softmax_ops_2sf"])
+    assert O.state_numbers(d, d) + d == d * (d + 1)   # S and z: d'(d_h + 1) floats
+
+
+# ------------------------------------------------ planted mistakes are caught
+
+def _mut_readout_before_update(fq, fk, v, alpha=None, beta=None, eps=1e-6):
+    T, dp = fq.shape; S = np.zeros((dp, v.shape[1])); z = np.zeros(dp); o = []
+    for t in range(T):
+        o.append((fq[t] @ S) / (fq[t] @ z + eps))
+        a = 1.0 if alpha is None else alpha[t]
+        S = a * S + np.outer(fk[t], v[t]); z = a * z + fk[t]
+    return np.array(o)
+
+
+def _mut_decay_on_new_term(fq, fk, v, alpha=None, beta=None, eps=1e-6):
+    T, dp = fq.shape; S = np.zeros((dp, v.shape[1])); z = np.zeros(dp); o = []
+    for t in range(T):
+        a = 1.0 if alpha is None else alpha[t]
+        S = a * (S + np.outer(fk[t], v[t])); z = a * (z + fk[t])
+        o.append((fq[t] @ S) / (fq[t] @ z + eps))
+    return np.array(o)
+
+
+def _mut_transposed_state(fq, fk, v, alpha=None, beta=None, eps=1e-6):
+    # state built as v k^T instead of k v^T (same shape when d' = d_v)
+    T, dp = fq.shape; S = np.zeros((dp, v.shape[1])); z = np.zeros(dp); o = []
+    for t in range(T):
+        a = 1.0 if alpha is None else alpha[t]
+        S = a * S + np.outer(v[t], fk[t]); z = a * z + fk[t]
+        o.append((fq[t] @ S) / (fq[t] @ z + eps))
+    return np.array(o)
+
+
+def _mut_undecayed_normaliser(fq, fk, v, alpha=None, beta=None, eps=1e-6):
+    T, dp = fq.shape; S = np.zeros((dp, v.shape[1])); z = np.zeros(dp); o = []
+    for t in range(T):
+        a = 1.0 if alpha is None else alpha[t]
+        S = a * S + np.outer(fk[t], v[t]); z = z + fk[t]
+        o.append((fq[t] @ S) / (fq[t] @ z + eps))
+    return np.array(o)
+
+
+def _mut_query_key_swapped(fq, fk, v, alpha=None, beta=None, eps=1e-6):
+    return O.recurrence(fk, fq, v, alpha, beta, eps)[0]
+
+
+@pytest.mark.parametrize("mutant", [_mut_readout_before_update, _mut_decay_on_new_term,
+                                    _mut_transposed_state, _mut_undecayed_normaliser,
+                                    _mut_query_key_swapped])
+def test_planted_mistakes_fail_the_bruteforce_pin(mutant):
+    rng = np.random.default_rng(99)
+    T, dp, dv = 6, 3, 3
+    fq, fk, v = O.phi_elu1(rng.standard_normal((T, dp))), O.phi_elu1(rng.standard_normal((T, dp))), rng.standard_normal((T, dv))
+    alpha = np.linspace(0.5, 0.95, T)
+    ref = O.kernel_attention_by_definition(fq, fk, v, alpha)
+    got = np.nan_to_num(mutant(fq, fk, v, alpha), nan=1e9)
+    assert np.abs(got - ref).max() > 1e-6
+    # and the unmutated oracle passes the very same check
+    assert np.abs(O.recurrence(fq, fk, v, alpha)[0] - ref).max() < 1e-12
