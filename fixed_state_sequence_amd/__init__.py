@@ -1,0 +1,215 @@
+"""Causal linear attention with a fixed-size running state on MI355X (gfx950).
+
+Thin Python layer over the C ABI of liblinattn.so (include/linattn.h): it
+checks tensors, allocates outputs/workspace with PyTorch and passes raw device
+pointers and torch's current HIP stream.  Every step of the computation runs
+in the library's HIP kernels; there is no Python or CPU fallback.
+
+    out, S, z = prefill(q, k, v)                   # q, k, v: [B, H, T, d] on cuda
+    o = decode_step(q1, k1, v1, S, z)              # one token, updates S, z in place
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Tuple
+
+from . import _lib
+from ._lib import LinAttnError  # noqa: F401
+
+__all__ = ["prefill", "prefill_stage", "decode_step", "state_init", "feature_dim",
+           "prefill_plan", "prefill_workspace_size", "make_desc", "LinAttnError"]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(dt):
+    torch = _torch()
+    codes = {torch.float32: _lib.LA_F32, torch.bfloat16: _lib.LA_BF16, torch.float16: _lib.LA_F16}
+    if dt not in codes:
+        raise TypeError(f"unsupported element type {dt}; use float32, bfloat16 or float16")
+    return codes[dt]
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, name, device=None, dtype=None, shape=None):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def make_desc(B, H, T, d_h, d_v, dtype_code, phi="elu1", W=None, rff_D=None, decay=None,
+              gate=None, eps=1e-6, chunk=0, segments=0, out_dtype_code=None) -> _lib.LaDesc:
+    """Build an `la_desc`.  `decay` (SSD a_t) and `gate` (RFA g_t) are exclusive;
+    `out_dtype_code` defaults to the input type."""
+    d = _lib.LaDesc()
+    d.B, d.H, d.T, d.d_h, d.d_v = int(B), int(H), int(T), int(d_h), int(d_v)
+    d.dtype = int(dtype_code)
+    d.out_dtype = int(dtype_code if out_dtype_code is None else out_dtype_code)
+    if phi == "elu1":
+        d.phi, d.rff_D, d.rff_W = _lib.LA_PHI_ELU1, 0, None
+    elif phi == "rff":
+        d.phi = _lib.LA_PHI_RFF
+        d.rff_D = int(rff_D if rff_D is not None else (W.shape[-2] if W is not None else 0))
+        d.rff_W = None if W is None else W.data_ptr()
+    else:
+        raise ValueError(f"unknown feature map {phi!r}")
+    if decay is not None and gate is not None:
+        raise ValueError("decay and gate are exclusive")
+    if decay is not None:
+        d.decay_kind, d.decay = _lib.LA_DECAY_SSD, decay.data_ptr()
+    elif gate is not None:
+        d.decay_kind, d.decay = _lib.LA_GATE_RFA, gate.data_ptr()
+    else:
+        d.decay_kind, d.decay = _lib.LA_DECAY_NONE, None
+    d.eps = float(eps)
+    d.chunk, d.segments = int(chunk), int(segments)
+    return d
+
+
+def feature_dim(d_h: int, phi: str = "elu1", rff_D: int = 0) -> int:
+    return 2 * rff_D if phi == "rff" else d_h
+
+
+def _stream(device):
+    return ctypes.c_void_p(_torch().cuda.current_stream(device).cuda_stream)
+
+
+def state_init(B: int, H: int, d_prime: int, d_v: int, device="cuda") -> Tuple["torch.Tensor", "torch.Tensor"]:
+    """Allocate a state (S [B,H,d',d_v], z [B,H,d'], fp32) and zero it with la_state_init."""
+    torch = _torch()
+    device = torch.device(device)
+    S = torch.empty(B, H, d_prime, d_v, dtype=torch.float32, device=device)
+    z = torch.empty(B, H, d_prime, dtype=torch.float32, device=device)
+    desc = make_desc(B, H, 0, d_prime, d_v, _lib.LA_F32)
+    _lib.check(_lib.lib().la_state_init(ctypes.byref(desc), _ptr(S), _ptr(z), _stream(device)))
+    return S, z
+
+
+def _prefill_desc(q, k, v, phi, W, decay, gate, eps, chunk, segments, out_dtype=None):
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, device=q.device, dtype=q.dtype)
+    if q.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, T, d]")
+    B, H, T, d_h = q.shape
+    _need(k, "k", shape=(B, H, T, d_h))
+    d_v = v.shape[-1]
+    _need(v, "v", shape=(B, H, T, d_v))
+    if W is not None:
+        _need(W, "W", device=q.device, dtype=torch.float32)
+    for a, n in ((decay, "decay"), (gate, "gate")):
+        if a is not None:
+            _need(a, n, device=q.device, dtype=torch.float32, shape=(B, H, T))
+    desc = make_desc(B, H, T, d_h, d_v, _dtype_code(q.dtype), phi, W, None, decay, gate, eps,
+                     chunk, segments, _dtype_code(out_dtype or q.dtype))
+    return desc, (B, H, T, d_h, d_v)
+
+
+def prefill_workspace_size(desc: _lib.LaDesc) -> int:
+    n = ctypes.c_size_t(0)
+    _lib.check(_lib.lib().la_prefill_workspace_size(ctypes.byref(desc), ctypes.byref(n)))
+    return int(n.value)
+
+
+def prefill_plan(desc: _lib.LaDesc):
+    """(chunk, segments, path) la_prefill will use (path 1 = chunked MFMA)."""
+    c, s, p = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0)
+    _lib.check(_lib.lib().la_prefill_plan(ctypes.byref(desc), ctypes.byref(c), ctypes.byref(s),
+                                          ctypes.byref(p)))
+    return c.value, s.value, p.value
+
+
+def prefill(q, k, v, *, phi: str = "elu1", W=None, decay=None, gate=None, eps: float = 1e-6,
+            state: Optional[tuple] = None, chunk: int = 0, segments: int = 0, out=None,
+            workspace=None, out_dtype=None):
+    """Causal linear attention over [B, H, T, d] inputs on the GPU.
+
+    Returns (out, S, z).  If `state=(S, z)` is given the recurrence continues
+    from it and the final state is written back into those tensors (in place);
+    otherwise a zero state is allocated.  `out_dtype` is q's dtype (default)
+    or torch.float32.
+    """
+    torch = _torch()
+    out_dtype = out_dtype or q.dtype
+    desc, (B, H, T, d_h, d_v) = _prefill_desc(q, k, v, phi, W, decay, gate, eps, chunk, segments,
+                                              out_dtype)
+    dp = feature_dim(d_h, phi, desc.rff_D)
+    if state is None:
+        S, z = state_init(B, H, dp, d_v, q.device)
+    else:
+        S, z = state
+        _need(S, "S", device=q.device, dtype=torch.float32, shape=(B, H, dp, d_v))
+        _need(z, "z", device=q.device, dtype=torch.float32, shape=(B, H, dp))
+    if out is None:
+        out = torch.empty(B, H, T, d_v, dtype=out_dtype, device=q.device)
+    else:
+        _need(out, "out", device=q.device, dtype=out_dtype, shape=(B, H, T, d_v))
+    nws = prefill_workspace_size(desc)
+    if nws and (workspace is None or workspace.numel() * workspace.element_size() < nws):
+        workspace = torch.empty(nws, dtype=torch.uint8, device=q.device)
+    _lib.check(_lib.lib().la_prefill(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(S), _ptr(z),
+                                     _ptr(out), _ptr(workspace) if nws else None, nws,
+                                     _stream(q.device)))
+    return out, S, z
+
+
+def prefill_stage(stage: int, q, k, v, S, z, out, workspace, *, phi="elu1", W=None, decay=None,
+                  gate=None, eps=1e-6, chunk=0, segments=0):
+    """Run one of la_prefill's three stages (1 segment states, 2 scan, 3 outputs);
+    out's dtype selects the output type."""
+    desc, _ = _prefill_desc(q, k, v, phi, W, decay, gate, eps, chunk, segments, out.dtype)
+    nws = prefill_workspace_size(desc)
+    _lib.check(_lib.lib().la_prefill_stage(ctypes.byref(desc), int(stage), _ptr(q), _ptr(k), _ptr(v),
+                                           _ptr(S), _ptr(z), _ptr(out),
+                                           _ptr(workspace) if nws else None, nws,
+                                           _stream(q.device)))
+
+
+def decode_step(q, k, v, S, z, *, phi: str = "elu1", W=None, decay=None, gate=None,
+                eps: float = 1e-6, out=None, out_dtype=None):
+    """One token for B sequences x H heads: q, k [B, H, d_h], v [B, H, d_v].
+
+    Updates (S, z) in place and returns out [B, H, d_v] (dtype of q).
+    """
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, device=q.device, dtype=q.dtype)
+    if q.dim() != 3:
+        raise ValueError("decode inputs must be [B, H, d]")
+    B, H, d_h = q.shape
+    d_v = v.shape[-1]
+    _need(k, "k", shape=(B, H, d_h))
+    _need(v, "v", shape=(B, H, d_v))
+    if W is not None:
+        _need(W, "W", device=q.device, dtype=torch.float32)
+    for a, n in ((decay, "decay"), (gate, "gate")):
+        if a is not None:
+            _need(a, n, device=q.device, dtype=torch.float32, shape=(B, H))
+    out_dtype = out_dtype or q.dtype
+    desc = make_desc(B, H, 1, d_h, d_v, _dtype_code(q.dtype), phi, W, None, decay, gate, eps,
+                     out_dtype_code=_dtype_code(out_dtype))
+    dp = feature_dim(d_h, phi, desc.rff_D)
+    _need(S, "S", device=q.device, dtype=torch.float32, shape=(B, H, dp, d_v))
+    _need(z, "z", device=q.device, dtype=torch.float32, shape=(B, H, dp))
+    if out is None:
+        out = torch.empty(B, H, d_v, dtype=out_dtype, device=q.device)
+    else:
+        _need(out, "out", device=q.device, dtype=out_dtype, shape=(B, H, d_v))
+    _lib.check(_lib.lib().la_decode_step(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(S),
+                                         _ptr(z), _ptr(out), _stream(q.device)))
+    return out

@@ -1,0 +1,31 @@
+// Device-side helpers shared by the linattn kernels: element conversion for
+// the three storage types and the elu+1 feature map.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace la {
+
+// Storage types of q, k, v and out.  bf16 is carried as raw 16-bit words.
+using bf16_t = uint16_t;
+using f16_t = _Float16;
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16_t x) { return __uint_as_float(uint32_t(x) << 16); }
+__device__ __forceinline__ float to_f32(f16_t x) { return float(x); }
+
+// Round-to-nearest-even conversions (gfx950 v_cvt_pk_bf16_f32 / v_cvt_f16_f32).
+__device__ __forceinline__ void store_f32(float x, float* d) { *d = x; }
+__device__ __forceinline__ void store_f32(float x, bf16_t* d) {
+  *d = __builtin_bit_cast(bf16_t, static_cast<__bf16>(x));
+}
+__device__ __forceinline__ void store_f32(float x, f16_t* d) { *d = static_cast<f16_t>(x); }
+
+// phi(x) = elu(x) + 1 with alpha = 1: x + 1 for x > 0, exp(x) otherwise
+// (llm-arch-kb "Linear Attention", section 2, symbol legend).
+__device__ __forceinline__ float elu1_accurate(float x) { return x > 0.f ? x + 1.f : expf(x); }
+__device__ __forceinline__ float elu1_fast(float x) { return x > 0.f ? x + 1.f : __expf(x); }
+
+}  // namespace la

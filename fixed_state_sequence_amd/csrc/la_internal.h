@@ -1,0 +1,50 @@
+// Internal declarations shared by the host API and the kernel translation
+// units of the linattn library.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "linattn.h"
+
+namespace la {
+
+// A validated problem description (every field already checked on the host).
+struct Problem {
+  int B = 0, H = 0, T = 0;
+  int dh = 0, dv = 0, dp = 0;   // query/key width, value width, feature width d'
+  la_dtype dtype = LA_BF16;
+  la_dtype out_dtype = LA_BF16;
+  la_phi phi = LA_PHI_ELU1;
+  int D = 0;                    // RFF pairs
+  const float* W = nullptr;     // [H, D, dh]
+  la_decay decay_kind = LA_DECAY_NONE;
+  const float* decay = nullptr; // prefill [B,H,T], decode [B,H]
+  float eps = 1e-6f;
+  int chunk = 64;               // prefill chunk length (MFMA path)
+  int segments = 1;             // prefill segments per (b,h) (MFMA path)
+  int path = 0;                 // 1 = chunked MFMA, 0 = per-token recurrent kernel
+  int64_t BH() const { return int64_t(B) * H; }
+};
+
+// Per-token recurrent kernel (decode step, and the general prefill path).
+// The same device code runs T tokens with the state held in registers.
+bool recurrent_supported(int dh, int dp, int dv);
+hipError_t launch_recurrent(const Problem& p, const void* q, const void* k, const void* v,
+                            float* S, float* z, void* out, hipStream_t stream);
+
+// Zero-fill of the state.
+hipError_t launch_state_init(float* S, int64_t nS, float* z, int64_t nz, hipStream_t stream);
+
+// Chunked MFMA prefill (16-bit inputs, elu+1, d' = d_v in {64, 128}).
+bool mfma_supported(const Problem& p);
+bool mfma_chunk_fits(int d, int chunk);
+int mfma_default_segments(const Problem& p);
+size_t mfma_workspace_bytes(const Problem& p);
+hipError_t launch_mfma_stage(const Problem& p, int stage, const void* q, const void* k,
+                             const void* v, float* S, float* z, void* out, void* ws,
+                             hipStream_t stream);
+
+}  // namespace la

@@ -1,0 +1,165 @@
+/*
+ * linattn.h -- causal linear attention with a fixed-size running state, on
+ * AMD Instinct MI355X (gfx950).  Plain C ABI: device pointers, sizes and
+ * status codes; no allocation, no synchronisation, no host<->device copies.
+ *
+ * What is computed (see the three pages this library follows):
+ *   [lesson] efficient-attention lesson "Linear attention", Researcher level,
+ *            "Derivation": o_i = sum_{j<=i} sim(q_i,k_j) v_j / sum_{j<=i} sim(q_i,k_j)
+ *            with sim(q,k) = phi(q)^T phi(k), regrouped into the recurrence
+ *            S_i = S_{i-1} + phi(k_i) v_i^T,  z_i = z_{i-1} + phi(k_i),
+ *            o_i = S_i^T phi(q_i) / (z_i^T phi(q_i)).
+ *   [kb]     llm-arch-kb "Linear Attention", section 2 "Derivation" (causal
+ *            recurrence: the state (S, z) is an RNN hidden state of size
+ *            d'(d_h + 1)) and section 3 "Reference implementation" (eps = 1e-6
+ *            is added to the denominator).
+ *   [card]   wikillm "Linear attention", "Implementation sketch" (optional
+ *            per-token scalar decay a_t multiplies the old state and the old
+ *            normaliser; decay 1 is the plain causal case, per "Decaying linear
+ *            attention with a scalar state (SSD)") and "Variants / Random
+ *            Fourier features (RFA)" (Gaussian random projections as the
+ *            feature map; a sigmoid gate g decays the old state and scales the
+ *            new term by 1 - g).
+ *
+ * Per (batch b, head h), for t = 0 .. T-1:
+ *   S <- alpha_t S + beta_t phi(k_t) v_t^T          S: d' x d_v, fp32
+ *   z <- alpha_t z + beta_t phi(k_t)                z: d',       fp32
+ *   o_t = (phi(q_t)^T S) / (phi(q_t)^T z + eps)     read-out after the update
+ * with (alpha, beta) = (1, 1) for LA_DECAY_NONE, (a_t, 1) for LA_DECAY_SSD and
+ * (g_t, 1 - g_t) for LA_GATE_RFA.
+ *
+ * Feature maps:
+ *   LA_PHI_ELU1: phi(x) = elu(x) + 1 (alpha = 1), element-wise, d' = d_h.
+ *   LA_PHI_RFF:  phi(x) = D^{-1/2} [sin(W_h x); cos(W_h x)], W_h = rff_W[h]
+ *                (D x d_h, fp32), d' = 2 D; features 0..D-1 are the sines,
+ *                D..2D-1 the cosines.  No q/k scaling is applied.
+ *
+ * Layouts (all row-major, contiguous, device memory, 16-byte aligned):
+ *   prefill q, k [B, H, T, d_h]; v, out [B, H, T, d_v]; decay [B, H, T] fp32
+ *   decode  q, k [B, H, d_h];    v, out [B, H, d_v];    decay [B, H]    fp32
+ *   state   S [B, H, d', d_v] fp32; z [B, H, d'] fp32
+ * (for decode, B is the number of sequences).  q, k and v share one element
+ * type (dtype); out is either dtype or fp32 (out_dtype).  Arithmetic is fp32
+ * (MFMA operands bf16 for 16-bit inputs, with the intra-chunk scores split
+ * into a bf16 high and low part), the state is fp32, and a 16-bit out is
+ * rounded to nearest even.  Because outputs shrink like 1/sqrt(t) over long
+ * sequences while early ones stay O(1), a 16-bit out carries rounding far
+ * above 1e-2 of the output RMS at T ~ 1e5; fp32 out does not.
+ *
+ * Ownership and threading: the caller owns every buffer.  The library keeps no
+ * state between calls, allocates nothing, never synchronises, and enqueues all
+ * work on the caller's stream (a hipStream_t passed as void*; NULL is the null
+ * stream).  Calls are thread-safe.  Buffers must not overlap, except that S
+ * and z are read and written in place.
+ *
+ * Errors: every argument is validated on the host before anything is
+ * enqueued, so a call that returns LA_EINVAL or LA_EUNSUPPORTED has had no
+ * effect.  LA_EHIP means a launch failed (hipGetLastError after enqueue).
+ * la_last_error() gives a human-readable reason for the calling thread's most
+ * recent failure.  Non-finite values in the data are not errors: a zero
+ * denominator (possible with RFF features, which can be negative) yields
+ * inf/NaN outputs, as the recurrence would.
+ */
+#ifndef LINATTN_H
+#define LINATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LA_OK = 0,
+  LA_EINVAL = 1,        /* bad argument: NULL, size, alignment, workspace too small */
+  LA_EUNSUPPORTED = 2,  /* valid but not implemented (e.g. d' or d_v too large)    */
+  LA_EHIP = 3           /* a HIP launch failed                                    */
+} la_status;
+
+typedef enum { LA_F32 = 0, LA_BF16 = 1, LA_F16 = 2 } la_dtype;
+
+typedef enum { LA_PHI_ELU1 = 0, LA_PHI_RFF = 1 } la_phi;
+
+typedef enum {
+  LA_DECAY_NONE = 0,  /* alpha = 1,   beta = 1                          */
+  LA_DECAY_SSD = 1,   /* alpha = a_t, beta = 1      (a_t >= 0 expected)  */
+  LA_GATE_RFA = 2     /* alpha = g_t, beta = 1 - g_t                     */
+} la_decay;
+
+typedef struct la_desc {
+  int B;                 /* batch (prefill) or number of sequences (decode), >= 1 */
+  int H;                 /* heads, >= 1                                           */
+  int T;                 /* tokens per sequence (prefill only), >= 0              */
+  int d_h;               /* query/key width, >= 1                                 */
+  int d_v;               /* value width, >= 1                                     */
+  la_dtype dtype;        /* element type of q, k and v                            */
+  la_dtype out_dtype;    /* element type of out: dtype, or LA_F32 for any dtype   */
+  la_phi phi;            /* feature map                                           */
+  int rff_D;             /* RFF pairs (d' = 2 rff_D); must be 0 for ELU1          */
+  const float* rff_W;    /* device [H, rff_D, d_h] fp32; NULL for ELU1            */
+  la_decay decay_kind;   /* decay / gate kind                                     */
+  const float* decay;    /* device fp32 a_t or g_t; NULL iff LA_DECAY_NONE        */
+  float eps;             /* added to the denominator (finite); 1e-6 on the pages  */
+  int chunk;             /* prefill chunk length, 0 = default (64); 32/64/128     */
+  int segments;          /* prefill segments per (b, h), 0 = automatic            */
+} la_desc;
+
+/* Feature dimension d' of a descriptor (d_h for ELU1, 2 rff_D for RFF), or -1
+ * if the descriptor is invalid.  Host only. */
+int la_feature_dim(const la_desc* desc);
+
+/* Zero the state: S [B, H, d', d_v] and z [B, H, d'] (fp32) become 0, the
+ * initial state of the recurrence ([kb] section 3: S and z start at zero).
+ * Enqueued on `stream`. */
+la_status la_state_init(const la_desc* desc, float* S, float* z, void* stream);
+
+/* Bytes of device workspace la_prefill needs for `desc` (may be 0).  Host
+ * only; depends on B, H, T, d', d_v, chunk and segments alone. */
+la_status la_prefill_workspace_size(const la_desc* desc, size_t* bytes);
+
+/* Execution plan la_prefill will use for `desc`: chunk length, segments per
+ * (b, h), and path (1 = chunked MFMA for 16-bit inputs with elu+1 and
+ * d' = d_v in {64, 128}; 0 = general per-token kernel).  Host only. */
+la_status la_prefill_plan(const la_desc* desc, int* chunk, int* segments, int* path);
+
+/* Causal prefill over T tokens for all (b, h):
+ *   in:  q, k, v (dtype), decay/gate and rff_W through desc, the initial
+ *        state (S, z) -- the recurrence continues from it ([kb] section 2:
+ *        the state is carried between steps);
+ *   out: out [B, H, T, d_v] (out_dtype) and the final state written over (S, z).
+ * The result equals T applications of the recurrence above; the chunked
+ * schedule re-brackets the same sums ([lesson] Researcher level,
+ * "Implementation reality": quadratic inside chunks, a scan across them).
+ * `workspace` must hold la_prefill_workspace_size() bytes (NULL if 0).
+ * T = 0 is a no-op. */
+la_status la_prefill(const la_desc* desc, const void* q, const void* k, const void* v,
+                     float* S, float* z, void* out, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/* The three stages la_prefill enqueues, for callers that time or interleave
+ * them: 1 = per-segment state contributions (reads k, v), 2 = scan of the
+ * segment states (folds in the initial state), 3 = outputs and final state
+ * (reads q, k, v).  Running stages 1, 2, 3 in order with identical arguments
+ * is exactly la_prefill; a stage with nothing to do returns LA_OK. */
+la_status la_prefill_stage(const la_desc* desc, int stage, const void* q, const void* k,
+                           const void* v, float* S, float* z, void* out,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* One autoregressive step for B sequences x H heads ([kb] section 2, causal
+ * recurrence; [card] "When to use which": memory-bound decoding with a
+ * fixed-size state): reads q, k [B, H, d_h], v [B, H, d_v] and the gate or
+ * decay [B, H]; updates (S, z) in place and writes out [B, H, d_v]. */
+la_status la_decode_step(const la_desc* desc, const void* q, const void* k, const void* v,
+                         float* S, float* z, void* out, void* stream);
+
+/* Static name of a status code. */
+const char* la_status_str(la_status status);
+
+/* Reason for the calling thread's most recent failing call ("" if none). */
+const char* la_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LINATTN_H */

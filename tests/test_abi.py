@@ -1,0 +1,143 @@
+"""The C ABI without a GPU: the library loads, exports every declared entry
+point, and rejects bad arguments on the host before any HIP call."""
+import ctypes
+
+import pytest
+
+from fixed_state_sequence_amd import _lib
+import fixed_state_sequence_amd as la
+
+L = _lib.lib()
+FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation
+
+
+def desc(**kw):
+    base = dict(B=1, H=8, T=102400, d_h=128, d_v=128, dtype_code=_lib.LA_BF16)
+    base.update(kw)
+    return la.make_desc(**base)
+
+
+def status(rc):
+    return L.la_status_str(rc).decode()
+
+
+def test_every_declared_function_is_exported():
+    names = _lib.header_functions()
+    assert set(names) >= {"la_prefill", "la_decode_step", "la_state_init",
+                          "la_prefill_workspace_size", "la_prefill_plan", "la_prefill_stage",
+                          "la_feature_dim", "la_status_str", "la_last_error"}
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    assert [status(i) for i in range(4)] == ["LA_OK", "LA_EINVAL", "LA_EUNSUPPORTED", "LA_EHIP"]
+
+
+def test_feature_dim():
+    assert L.la_feature_dim(ctypes.byref(desc())) == 128
+    d = la.make_desc(256, 16, 1, 64, 64, _lib.LA_F32, phi="rff", rff_D=64)
+    d.rff_W = FAKE
+    assert L.la_feature_dim(ctypes.byref(d)) == 128
+    assert L.la_feature_dim(ctypes.byref(desc(B=0))) == -1
+    assert L.la_feature_dim(None) == -1
+
+
+def test_plan_for_the_measured_prefills():
+    # long context: chunked MFMA path, segments spread 8 heads over the chip
+    c, s, p = la.prefill_plan(desc())
+    assert (c, p) == (64, 1) and s > 1 and 1600 % ((1600 + s - 1) // s) >= 0
+    assert la.prefill_workspace_size(desc()) == 8 * s * (128 * 128 + 128) * 4 + (
+        (8 * s * 4 + 255) // 256) * 256
+    # fp32 inputs take the per-token kernel; no workspace
+    d = desc(T=8, d_h=4, d_v=4, dtype_code=_lib.LA_F32)
+    assert la.prefill_plan(d)[2] == 0 and la.prefill_workspace_size(d) == 0
+    # explicit segments are honoured up to the chunk count, never leaving one empty
+    d = desc(T=640, segments=4)
+    assert la.prefill_plan(d) == (64, 4, 1)
+    d = desc(T=9 * 64, segments=4)   # 9 chunks, 3 per segment -> 3 segments
+    assert la.prefill_plan(d)[1] == 3
+    d = desc(T=100, segments=50)
+    assert la.prefill_plan(d)[1] == 2
+
+
+@pytest.mark.parametrize("field,value", [("B", 0), ("H", -1), ("T", -5), ("d_h", 0), ("d_v", 0),
+                                         ("dtype", 7), ("phi", 9), ("decay_kind", 5),
+                                         ("chunk", 48), ("segments", -1)])
+def test_bad_descriptor_fields_are_rejected(field, value):
+    d = desc()
+    setattr(d, field, value)
+    rc = L.la_prefill(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
+    assert status(rc) == "LA_EINVAL"
+    assert L.la_last_error().decode() != ""
+
+
+def test_null_and_misaligned_pointers():
+    d = desc()
+    args = [FAKE] * 7
+    for i in range(6):
+        a = list(args)
+        a[i] = None
+        rc = L.la_prefill(ctypes.byref(d), *a, 1 << 40, None)
+        assert status(rc) == "LA_EINVAL"
+    a = list(args)
+    a[0] = FAKE + 2
+    assert status(L.la_prefill(ctypes.byref(d), *a, 1 << 40, None)) == "LA_EINVAL"
+    assert "aligned" in L.la_last_error().decode()
+
+
+def test_workspace_too_small():
+    d = desc()
+    need = la.prefill_workspace_size(d)
+    rc = L.la_prefill(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None)
+    assert status(rc) == "LA_EINVAL" and "workspace" in L.la_last_error().decode()
+    rc = L.la_prefill(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, need, None)
+    assert status(rc) == "LA_EINVAL"
+
+
+def test_decay_pointer_consistency():
+    d = desc()
+    d.decay = FAKE   # decay array with LA_DECAY_NONE
+    assert status(L.la_prefill(ctypes.byref(d), *([FAKE] * 7), 1 << 40, None)) == "LA_EINVAL"
+    d = desc()
+    d.decay_kind = _lib.LA_DECAY_SSD   # SSD with no array
+    assert status(L.la_prefill(ctypes.byref(d), *([FAKE] * 7), 1 << 40, None)) == "LA_EINVAL"
+
+
+def test_rff_descriptor_checks():
+    d = desc(T=16, d_h=64, d_v=64, dtype_code=_lib.LA_F32)
+    d.phi = _lib.LA_PHI_RFF
+    d.rff_D = 64   # W missing
+    assert status(L.la_prefill(ctypes.byref(d), *([FAKE] * 7), 0, None)) == "LA_EINVAL"
+    d = desc(T=16)
+    d.rff_D = 3    # elu+1 with rff_D set
+    assert status(L.la_prefill(ctypes.byref(d), *([FAKE] * 7), 0, None)) == "LA_EINVAL"
+
+
+def test_unsupported_widths():
+    d = desc(d_h=512, d_v=512, dtype_code=_lib.LA_F32)
+    assert status(L.la_prefill(ctypes.byref(d), *([FAKE] * 7), 0, None)) == "LA_EUNSUPPORTED"
+    d = desc(d_h=64, d_v=12, dtype_code=_lib.LA_F32)     # d_v / 4 not a power of two
+    assert status(L.la_decode_step(ctypes.byref(d), *([FAKE] * 6), None)) == "LA_EUNSUPPORTED"
+
+
+def test_stage_index_checked():
+    d = desc()
+    assert status(L.la_prefill_stage(ctypes.byref(d), 4, *([FAKE] * 7), 1 << 40, None)) == "LA_EINVAL"
+
+
+def test_decode_null_state():
+    d = la.make_desc(256, 16, 1, 64, 64, _lib.LA_F32)
+    assert status(L.la_decode_step(ctypes.byref(d), FAKE, FAKE, FAKE, None, FAKE, FAKE, None)) == "LA_EINVAL"
+    assert status(L.la_state_init(ctypes.byref(d), FAKE, None, None)) == "LA_EINVAL"
+
+
+def test_shares_torchs_hip_runtime():
+    # one HIP runtime per process: the library resolves to torch's copy
+    assert len(_lib._hip_runtimes()) == 1
+
+
+def test_chunk_128_needs_narrow_state():
+    d = desc(chunk=128)
+    assert status(L.la_prefill(ctypes.byref(d), *([FAKE] * 7), 1 << 40, None)) == "LA_EUNSUPPORTED"
+    assert la.prefill_plan(desc(chunk=128, d_h=64, d_v=64))[0] == 128
