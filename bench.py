@@ -1,0 +1,301 @@
+"""Benchmark of the causal linear attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one causal elu+1 prefill over the long-context workload
+(B=1, H=8, T=102400, d_h = d' = d_v = 128, bf16 q, k, v ~ N(0, 1)/sqrt(2),
+fp32 state, eps = 1e-6): la_state_init, then la_prefill (feature map,
+chunking, intra-chunk MFMA contraction, chunk-local state contribution,
+segment scan, inter-chunk read-out and normalisation).  Inputs are generated
+on the device before timing.  W untimed warm-up steps are followed by exactly
+K timed steps between two synchronisations, with HIP events on the stream the
+library launches on.
+
+Printed as one JSON line:
+  value        tokens/s (B*T tokens per step) over the K steps;
+  roofline     the output kernel (la_prefill stage 3, the one that dominates),
+               algorithmic bytes (q, k, v read + out written, bf16, plus the
+               state) over its average duration, timed with events around
+               that stage alone, against the 8 TB/s HBM peak;
+  mfma         algorithmic FLOPs of the recurrence, 4 d' d_v + 4 d' per
+               token-head, over the step time, against the 2.5 PFLOP/s bf16
+               dense peak;
+  decode       the gated random-feature decode workload (256 sequences x 16
+               heads, d_h = d_v = 64, D = 64 sine/cosine pairs so d' = 128,
+               fp32, 1024 one-token steps): state GB/s against 8 TB/s, and the
+               same with 1024 sequences so the state (545 MB) exceeds the
+               256 MB last-level cache;
+  cpu_baseline the fp64 oracle (the CPU reference the tests check against),
+               on a bounded sample of the same prefill workload, one worker
+               process per head.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
+
+# the long-context prefill workload
+PF = dict(B=1, H=8, T=102400, d=128, scale=2.0 ** -0.5, eps=1e-6)
+# the gated random-feature decode workload
+DEC = dict(N=256, H=16, d_h=64, d_v=64, D=64, steps=1024)
+
+
+# --------------------------------------------------------------------- CPU leg
+
+_SAMPLE = None   # the oracle's inputs, made in the parent and inherited by the forked workers
+
+
+def _oracle_head(h):
+    """One head of the prefill sample through the fp64 oracle (worker process)."""
+    from threadpoolctl import threadpool_limits
+    from oracle import linattn_oracle as O
+    x = _SAMPLE
+    q, k, v = x.q[:, h:h + 1], x.k[:, h:h + 1], x.v[:, h:h + 1]
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        O.causal_linear_attention(q, k, v, eps=PF["eps"])
+        return time.perf_counter() - t0
+
+
+def cpu_baseline(T_sample: int):
+    """Time the oracle on the first T_sample tokens of all H heads, one process
+    per head (the heads are independent), before the GPU is touched.  Input
+    generation is outside the timed region; the rate is taken over the slowest
+    worker's oracle time."""
+    global _SAMPLE
+    import multiprocessing as mp
+    from fixed_state_sequence_amd import inputs as I
+    _SAMPLE = I.prefill_inputs(PF["B"], PF["H"], T_sample, PF["d"], dtype="bf16", seed=0,
+                               scale=PF["scale"])
+    workers = min(PF["H"], os.cpu_count() or 1)
+    ctx = mp.get_context("fork")
+    with ctx.Pool(workers) as pool:
+        per_head = pool.map(_oracle_head, range(PF["H"]))
+    _SAMPLE = None
+    wall = max(per_head) if workers >= PF["H"] else sum(per_head) / workers
+    tokens = PF["B"] * T_sample
+    return {
+        "value": tokens / wall, "unit": "tokens/s", "cores": workers, "kind": "oracle",
+        "sample": (f"first {T_sample} of {PF['T']} tokens of the same workload, all {PF['H']} "
+                   f"heads, fp64 numpy recurrence, one process per head with 1 BLAS thread; "
+                   f"per-head oracle time {min(per_head):.2f}-{max(per_head):.2f} s; "
+                   f"{os.cpu_count()} host cores visible"),
+    }
+
+
+# --------------------------------------------------------------------- GPU leg
+
+def _events(torch):
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+def bench_prefill(torch, la, I, steps, warmup):
+    dev = torch.device("cuda:0")
+    B, H, T, d = PF["B"], PF["H"], PF["T"], PF["d"]
+    x = I.prefill_inputs(B, H, T, d, dtype="bf16", seed=0, scale=PF["scale"], device=dev)
+    q, k, v = x.q, x.k, x.v
+    desc = la.make_desc(B, H, T, d, d, la._lib.LA_BF16, eps=PF["eps"])
+    chunk, segments, path = la.prefill_plan(desc)
+    if path != 1:
+        raise RuntimeError("the long-context prefill did not take the chunked MFMA path")
+    nws = la.prefill_workspace_size(desc)
+    ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=dev)
+    out = torch.empty(B, H, T, d, dtype=torch.bfloat16, device=dev)
+    S = torch.empty(B, H, d, d, dtype=torch.float32, device=dev)
+    z = torch.empty(B, H, d, dtype=torch.float32, device=dev)
+    L = la._lib.lib()
+    P = ctypes.c_void_p
+    ptr = lambda t: P(t.data_ptr())
+    stream = P(torch.cuda.current_stream(dev).cuda_stream)
+    dref = ctypes.byref(desc)
+    args = (ptr(q), ptr(k), ptr(v), ptr(S), ptr(z), ptr(out))
+
+    def step():
+        la._lib.check(L.la_state_init(dref, ptr(S), ptr(z), stream))
+        la._lib.check(L.la_prefill(dref, *args, ptr(ws), nws, stream))
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = _events(torch)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / steps
+
+    # per-stage durations: the same calls, with events between the stages
+    reps = max(steps, 5)
+    stage_ms = [0.0, 0.0, 0.0]
+    for _ in range(reps):
+        L.la_state_init(dref, ptr(S), ptr(z), stream)
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        evs[0].record()
+        for s in (1, 2, 3):
+            la._lib.check(L.la_prefill_stage(dref, s, *args, ptr(ws), nws, stream))
+            evs[s].record()
+        torch.cuda.synchronize()
+        for s in range(3):
+            stage_ms[s] += evs[s].elapsed_time(evs[s + 1]) / reps
+    return dict(ms=ms, wall=wall, stage_ms=stage_ms, chunk=chunk, segments=segments)
+
+
+def bench_decode(torch, la, I, N, steps, warmup=8):
+    """`steps` one-token steps for N sequences; inputs for every step are made
+    on the device beforehand.  Returns ms per step."""
+    dev = torch.device("cuda:0")
+    H, d_h, d_v, D = DEC["H"], DEC["d_h"], DEC["d_v"], DEC["D"]
+    dp = 2 * D
+    W = I.rff_projection(H, D, d_h, seed=0, device=dev)
+    nin = steps   # a distinct input set for every timed step
+    x = I.rfa_decode_batch(nin, N, H, d_h, d_v, seed=1, device=dev)
+    q, k, v, gate = x.q, x.k, x.v, x.gate
+    S, z = la.state_init(N, H, dp, d_v, dev)
+    out = torch.empty(N, H, d_v, dtype=torch.float32, device=dev)
+    desc = la.make_desc(N, H, 1, d_h, d_v, la._lib.LA_F32, phi="rff", W=W, gate=gate[0],
+                        eps=1e-6)
+    L = la._lib.lib()
+    P = ctypes.c_void_p
+    stream = P(torch.cuda.current_stream(dev).cuda_stream)
+    dref = ctypes.byref(desc)
+    qp = [P(q[i].data_ptr()) for i in range(nin)]
+    kp = [P(k[i].data_ptr()) for i in range(nin)]
+    vp = [P(v[i].data_ptr()) for i in range(nin)]
+    gp = [gate[i].data_ptr() for i in range(nin)]
+    Sp, zp, op = P(S.data_ptr()), P(z.data_ptr()), P(out.data_ptr())
+
+    def run(n):
+        for t in range(n):
+            i = t % nin
+            desc.decay = gp[i]
+            rc = L.la_decode_step(dref, qp[i], kp[i], vp[i], Sp, zp, op, stream)
+            if rc:
+                la._lib.check(rc)
+
+    run(warmup)
+    torch.cuda.synchronize()
+    e0, e1 = _events(torch)
+    e0.record()
+    run(steps)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    state_b = N * H * (dp * d_v + dp) * 4
+    io_b = N * H * (2 * d_h + 2 * d_v + 1) * 4 + H * D * d_h * 4
+    bytes_step = 2 * state_b + io_b
+    return dict(ms_per_step=ms, bytes_per_step=bytes_step, gbs=bytes_step / (ms * 1e-3) / 1e9,
+                state_mb=state_b / 1e6)
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-tokens", type=int, default=102400,
+                    help="tokens per head in the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    a = ap.parse_args(argv)
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported "
+              "(the path needs no second GPU; heads and sequences shard with no exchange)",
+              file=sys.stderr)
+        return 2
+
+    cpu = None
+    if not a.no_cpu_baseline:
+        print(f"[bench] cpu baseline: oracle on {a.cpu_tokens} tokens x {PF['H']} heads",
+              file=sys.stderr, flush=True)
+        cpu = cpu_baseline(a.cpu_tokens)
+
+    import torch
+    import fixed_state_sequence_amd as la
+    from fixed_state_sequence_amd import inputs as I
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    la._lib.lib()
+
+    print(f"[bench] prefill B={PF['B']} H={PF['H']} T={PF['T']} d={PF['d']}: "
+          f"{a.warmup} warm-up + {a.steps} timed steps", file=sys.stderr, flush=True)
+    pf = bench_prefill(torch, la, I, a.steps, a.warmup)
+    B, H, T, d = PF["B"], PF["H"], PF["T"], PF["d"]
+    TH = B * H * T
+    tokens_per_s = B * T / (pf["ms"] * 1e-3)
+    state_bytes = B * H * (d * d + d) * 4
+    stage3_bytes = TH * 4 * d * 2 + 2 * state_bytes      # q, k, v in, out out (bf16); state
+    s3 = pf["stage_ms"][2]
+    achieved = stage3_bytes / (s3 * 1e-3) / 1e9
+    flops = TH * (4 * d * d + 4 * d)
+    tflops = flops / (pf["ms"] * 1e-3) / 1e12
+    step_bytes = TH * 4 * d * 2 + 2 * state_bytes
+
+    dec = dec_big = None
+    if not a.no_decode:
+        print(f"[bench] decode {DEC['N']} x {DEC['H']}, {DEC['steps']} steps", file=sys.stderr,
+              flush=True)
+        dec = bench_decode(torch, la, I, DEC["N"], DEC["steps"])
+        print("[bench] decode 1024 x 16, 256 steps", file=sys.stderr, flush=True)
+        dec_big = bench_decode(torch, la, I, 1024, 256)
+
+    res = {
+        "metric": "linear-attn fwd tokens/s + % MFMA peak at T=100K,d=128; decode state GB/s",
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": pf["ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "long-context causal elu+1 prefill", "B": B, "H": H, "T": T,
+                   "d_h": d, "d_prime": d, "d_v": d, "in_dtype": "bf16", "out_dtype": "bf16",
+                   "state_dtype": "fp32", "eps": PF["eps"], "decay": None,
+                   "chunk": pf["chunk"], "segments": pf["segments"]},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "output_kernel (la_prefill stage 3)",
+                     "kernel_ms": s3, "algorithmic_bytes": stage3_bytes},
+        "step": {"stage_ms": pf["stage_ms"], "algorithmic_bytes": step_bytes,
+                 "GBs": step_bytes / (pf["ms"] * 1e-3) / 1e9,
+                 "hbm_frac": step_bytes / (pf["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "mfma": {"algorithmic_flops": flops, "achieved": tflops, "peak": BF16_PEAK_TFLOPS,
+                 "unit": "TFLOP/s", "frac": tflops / BF16_PEAK_TFLOPS},
+        "cpu_baseline": cpu,
+    }
+    if dec is not None:
+        res["decode"] = {
+            "workload": "gated random-feature decode, fp32, D=64 pairs, d'=128, d_v=64",
+            "sequences": DEC["N"], "heads": DEC["H"], "steps": DEC["steps"],
+            "ms_per_step": dec["ms_per_step"], "bytes_per_step": dec["bytes_per_step"],
+            "achieved": dec["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": dec["gbs"] / HBM_PEAK_GBS, "state_MB": dec["state_mb"],
+            "note": "state fits the 256 MB last-level cache",
+            "large": {"sequences": 1024, "steps": 256, "ms_per_step": dec_big["ms_per_step"],
+                      "achieved": dec_big["gbs"], "frac": dec_big["gbs"] / HBM_PEAK_GBS,
+                      "state_MB": dec_big["state_mb"]},
+        }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -125,6 +125,23 @@ def rfa_decode_step_inputs(N: int, H: int, d_h: int, d_v: Optional[int] = None,
     return DecodeStep(q, k, v, gate.float())
 
 
+def rfa_decode_batch(steps: int, N: int, H: int, d_h: int, d_v: Optional[int] = None,
+                     seed: int = 1, device="cpu") -> DecodeStep:
+    """Inputs of `steps` decode steps drawn at once (for timing runs): q, k
+    [steps, N, H, d_h] unit norm (fp64 normalisation, stored fp32), v
+    [steps, N, H, d_v] ~ N(0, 1), gate [steps, N, H] = sigmoid(N(0, 1)).
+    Same distributions as ``rfa_decode_step_inputs``; one generator."""
+    d_v = d_h if d_v is None else d_v
+    g = _gen(seed, device)
+    q = torch.randn(steps, N, H, d_h, generator=g, device=device, dtype=torch.float64)
+    k = torch.randn(steps, N, H, d_h, generator=g, device=device, dtype=torch.float64)
+    v = torch.randn(steps, N, H, d_v, generator=g, device=device)
+    gate = torch.sigmoid(torch.randn(steps, N, H, generator=g, device=device))
+    q = (q / q.norm(dim=-1, keepdim=True)).float()
+    k = (k / k.norm(dim=-1, keepdim=True)).float()
+    return DecodeStep(q, k, v, gate.float().contiguous())
+
+
 # --- the five measured workloads, named by what they are ---------------------
 
 WORKLOADS = {
