@@ -227,7 +227,9 @@ la_status la_decode_step(const la_desc* desc, const void* q, const void* k, cons
   LA_TRY(check_ptr(S, "S"));
   LA_TRY(check_ptr(z, "z"));
   (void)hipGetLastError();
-  return launched(la::launch_recurrent(p, q, k, v, S, z, out, static_cast<hipStream_t>(stream)));
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (la::decode_supported(p)) return launched(la::launch_decode(p, q, k, v, S, z, out, st));
+  return launched(la::launch_recurrent(p, q, k, v, S, z, out, st));
 }
 
 const char* la_status_str(la_status status) {

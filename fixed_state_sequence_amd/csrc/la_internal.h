@@ -35,6 +35,13 @@ bool recurrent_supported(int dh, int dp, int dv);
 hipError_t launch_recurrent(const Problem& p, const void* q, const void* k, const void* v,
                             float* S, float* z, void* out, hipStream_t stream);
 
+// Decode step, one wave per state (d_v in {64, 128}, d' in {64, 128, 256};
+// RFF with d_h <= 128, or elu+1 with d_h = d').  Other shapes take the
+// recurrent kernel with T = 1.
+bool decode_supported(const Problem& p);
+hipError_t launch_decode(const Problem& p, const void* q, const void* k, const void* v,
+                         float* S, float* z, void* out, hipStream_t stream);
+
 // Zero-fill of the state.
 hipError_t launch_state_init(float* S, int64_t nS, float* z, int64_t nz, hipStream_t stream);
 
