@@ -85,13 +85,15 @@ la_status check_desc(const la_desc* d, bool prefill, la::Problem* p) {
   p->dh = d->d_h; p->dv = d->d_v; p->dp = dp;
   p->dtype = d->dtype; p->out_dtype = d->out_dtype; p->phi = d->phi; p->D = d->rff_D; p->W = d->rff_W;
   p->decay_kind = d->decay_kind; p->decay = d->decay; p->eps = d->eps;
-  p->chunk = d->chunk ? d->chunk : 64;
+  p->chunk = d->chunk ? d->chunk : 32;
   p->segments = 1;
   p->path = 0;
   if (prefill) {
     p->path = la::mfma_supported(*p) ? 1 : 0;
     if (p->path == 1 && !la::mfma_chunk_fits(p->dv, p->chunk))
       return fail(LA_EUNSUPPORTED, "chunk %d needs d' = d_v <= 64 (LDS)", p->chunk);
+    if (p->path == 1 && int64_t(p->T) * p->dv >= (int64_t(1) << 31))
+      return fail(LA_EUNSUPPORTED, "T * d_v must be < 2^31 per (b, h) for the chunked kernels");
     if (p->path == 1) {
       // effective count: ceil(nchunks / cps) with cps = ceil(nchunks / requested),
       // so that no segment is empty

@@ -104,29 +104,40 @@ struct Cfg {
   static constexpr int KS = D / 16;          // 16-feature k-steps
   static constexpr int KT = C / 16;          // 16-token k-steps
   static constexpr int MT = D / 32;          // 32-feature tiles of the state
-  static constexpr int ROW_B = 2 * D + 16;   // token-major rows: bf16, padded 16 B
-  static constexpr int TR_B = 2 * C;         // feature-major rows: bf16, XOR-swizzled
-  static constexpr int TR = D * TR_B;        // one feature-major tile
-  // stage 3: phi(q), phi(k) token-major; w phi(k) high/low and v (high/low
-  // when VS) feature-major; then small fp32 arrays
+  static constexpr int ND = C > 64 ? 2 : 1;  // decay values per lane (token lane, lane + 64)
+  static constexpr int TILE = C * 2 * D;     // one C x D bf16 tile
+  // Raw q, k, v of the next DEPTH chunks are held in registers (3 RPT
+  // 16-byte blocks per thread and chunk) while the current one is computed,
+  // so about 3 x 24 KB per compute unit stay in flight at C = 32.
+  // DEPTH = 0: each chunk is loaded when it is staged.
+  static constexpr int DEPTH = RPT <= 2 ? 3 : 0;
+  static constexpr int RING = DEPTH > 0 ? DEPTH : 1;
+  // Every tile is token-major (one row per token, D bf16 per row, 16-byte
+  // blocks XOR-swizzled per row by blk_swz):
+  //   Q, K   phi(q), phi(k); row = token, features at perm_pos order (read
+  //          row-wise as the k = feature operands of the read-out and scores)
+  //   KH, KL w phi(k) as bf16 high/low parts; row = perm_pos(token), natural
+  //          features (read transposed: the k = token operand of the fold)
+  //   VH, VL v (high/low parts only for fp16 inputs); row = perm_pos(token),
+  //          natural features (read transposed for P V and the fold)
   static constexpr int OFF_Q = 0;
-  static constexpr int OFF_K = OFF_Q + C * ROW_B;
-  static constexpr int OFF_KH = OFF_K + C * ROW_B;
-  static constexpr int OFF_KL = OFF_KH + TR;
-  static constexpr int OFF_VH = OFF_KL + TR;
-  static constexpr int OFF_VL = OFF_VH + TR;
-  static constexpr int OFF_L = OFF_VL + (VS ? TR : 0);  // lc_t, fp32 [C]
+  static constexpr int OFF_K = OFF_Q + TILE;
+  static constexpr int OFF_KH = OFF_K + TILE;
+  static constexpr int OFF_KL = OFF_KH + TILE;
+  static constexpr int OFF_VH = OFF_KL + TILE;
+  static constexpr int OFF_VL = OFF_VH + TILE;
+  static constexpr int OFF_L = OFF_VL + (VS ? TILE : 0);  // lc_t, fp32 [C]
   static constexpr int OFF_B = OFF_L + 4 * C;           // beta_t, fp32 [C]
   static constexpr int OFF_DEN = OFF_B + 4 * C;         // inter-chunk denominators, fp32 [C]
   static constexpr int OFF_Z = OFF_DEN + 4 * C;         // z, fp32 [D]
   static constexpr int OFF_DZ = OFF_Z + 4 * D;          // per-wave z increments, fp32 [NW][D]
   static constexpr int LDS = OFF_DZ + 4 * NW * D;
-  // stage 1: the feature-major tiles and the small arrays
+  // stage 1: KH, KL, VH (VL) and the small arrays
   static constexpr int S1_KH = 0;
-  static constexpr int S1_KL = S1_KH + TR;
-  static constexpr int S1_VH = S1_KL + TR;
-  static constexpr int S1_VL = S1_VH + TR;
-  static constexpr int S1_Z = S1_VL + (VS ? TR : 0);
+  static constexpr int S1_KL = S1_KH + TILE;
+  static constexpr int S1_VH = S1_KL + TILE;
+  static constexpr int S1_VL = S1_VH + TILE;
+  static constexpr int S1_Z = S1_VL + (VS ? TILE : 0);
   static constexpr int S1_DZ = S1_Z + 4 * D;
   static constexpr int S1_LDS = S1_DZ + 4 * NW * D;
   static_assert(RPT == C / 16, "row split");
@@ -135,55 +146,88 @@ struct Cfg {
   static_assert(LDS <= 160 * 1024, "LDS");
 };
 
-// XOR swizzle (in 16-byte blocks) of feature-major rows, chosen so that the
-// 16 lanes of an operand read (16 consecutive rows, one logical block) and
-// the transposing writes (rows 8 apart) spread over the LDS banks.
-template <int C>
-__device__ __forceinline__ int swz(int m) {
-  if constexpr (C == 128) return (m ^ (m >> 3)) & 15;
-  else if constexpr (C == 64) return ((m >> 1) ^ (m >> 4)) & 7;
-  else return ((m >> 2) ^ (m >> 4)) & 3;
+// XOR swizzle of the 16-byte blocks of tile row r.  Two read patterns must
+// spread over the 64 LDS banks: 16 lanes reading one block of 16
+// consecutive rows (row-wise operands), and 32 lanes reading 4 consecutive
+// rows x 4 consecutive blocks (transposed operands; rows start at a multiple
+// of 4).  D = 128: 16 blocks per row, the swizzle is a bijection on 0..15 for
+// any 16 consecutive rows and takes 4 values 4 apart over each aligned group
+// of 4 rows.  D = 64: 8 blocks per row (two rows per bank line), the same
+// with the row pair's parity taking one bit.
+template <int D>
+__device__ __forceinline__ int blk_swz(int r) {
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
 
-// Byte offset of (row m, permuted token position pos) in a feature-major tile.
-template <int C>
-__device__ __forceinline__ int tr_off(int m, int pos) {
-  const int blk = pos >> 3;
-  return m * (2 * C) + ((blk ^ swz<C>(m)) << 4) + ((pos & 7) << 1);
+// Byte offset of logical 16-byte block b of row r.
+template <int D>
+__device__ __forceinline__ int tile_off(int r, int b) {
+  return r * (2 * D) + ((b ^ blk_swz<D>(r)) << 4);
 }
 
-// Write RPT consecutive tokens (first = tok, a multiple of RPT) of one
-// feature-major row m as bf16 high parts, and (when lo != nullptr) the bf16
-// low parts x - high into a second tile.
-template <int C, int RPT>
-__device__ __forceinline__ void tr_write(char* hi, char* lo, int m, int tok, const float* vals) {
-  if constexpr (RPT == 2) {
-    uint32_t h, l;
-    split_bf16(vals[0], vals[1], h, l);
-    const int off = tr_off<C>(m, perm_pos(tok));
-    *reinterpret_cast<uint32_t*>(hi + off) = h;
-    if (lo) *reinterpret_cast<uint32_t*>(lo + off) = l;
-  } else {
+// Row-wise MFMA operand: the 8 bf16 of logical block b of row r.
+template <int D>
+__device__ __forceinline__ u32x4 row_operand(const char* tile, int r, int b) {
+  return *reinterpret_cast<const u32x4*>(tile + tile_off<D>(r, b));
+}
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// Transposed MFMA operand from a token-major tile, by two LDS transpose
+// reads (ds_read_b64_tr_b16).  Within each group of 16 lanes, lane s reads
+// 8 bytes at row k0 + 8 g + 4 h + s / 4, columns c + 4 (s % 4) .. + 3 of the
+// group's 16-column block; the instruction hands lane s back element s % 4 of
+// the reads of lanes s / 4 + {0, 4, 8, 12}, i.e. column (s) of the block at 4
+// consecutive rows.  Result: lane (n = lane % 32, g = lane / 32) holds rows
+// k0 + 8 g .. k0 + 8 g + 7 of column colbase + n, the operand layout of
+// v_mfma_f32_32x32x16_bf16 for a k = row operand.
+template <int D>
+__device__ __forceinline__ u32x4 tr_operand(const char* tile, int k0, int colbase, int lane) {
+  const int g = lane >> 5, s = lane & 15;
+  const int c = colbase + 16 * ((lane >> 4) & 1) + 4 * (s & 3);
+  u32x4 out;
 #pragma unroll
-    for (int qd = 0; qd < RPT / 4; ++qd) {
-      uint32_t h0, l0, h1, l1;
-      split_bf16(vals[4 * qd], vals[4 * qd + 1], h0, l0);
-      split_bf16(vals[4 * qd + 2], vals[4 * qd + 3], h1, l1);
-      const int off = tr_off<C>(m, perm_pos(tok + 4 * qd));
-      *reinterpret_cast<u32x2*>(hi + off) = u32x2{h0, h1};
-      if (lo) *reinterpret_cast<u32x2*>(lo + off) = u32x2{l0, l1};
-    }
+  for (int h = 0; h < 2; ++h) {
+    const int r = k0 + 8 * g + 4 * h + (s >> 2);
+    const char* p = tile + tile_off<D>(r, c >> 3) + ((c & 7) << 1);
+    const v4i16 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p));
+    const u32x2 y = __builtin_bit_cast(u32x2, x);
+    out[2 * h] = y[0];
+    out[2 * h + 1] = y[1];
   }
+  return out;
 }
 
-// Write 8 features (first = 8 fb) of token-major row r, permuted order.
-template <int ROW_B>
-__device__ __forceinline__ void row_write(char* base, int r, int fb, const float* x) {
-  const int f0 = 8 * fb;
-  u32x2 a = {pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3])};
-  u32x2 b = {pack_bf16(x[4], x[5]), pack_bf16(x[6], x[7])};
-  *reinterpret_cast<u32x2*>(base + r * ROW_B + 2 * perm_pos(f0)) = a;
-  *reinterpret_cast<u32x2*>(base + r * ROW_B + 2 * perm_pos(f0 + 4)) = b;
+// Features 8 fb .. 8 fb + 7 of row r (4 packed bf16 pairs) at their
+// perm_pos positions: two 8-byte pieces.
+template <int D>
+__device__ __forceinline__ void row_write_perm(char* tile, int r, int fb, const u32x4& w) {
+  const int p0 = perm_pos(8 * fb), p1 = perm_pos(8 * fb + 4);
+  *reinterpret_cast<u32x2*>(tile + tile_off<D>(r, p0 >> 3) + ((p0 & 7) << 1)) = u32x2{w[0], w[1]};
+  *reinterpret_cast<u32x2*>(tile + tile_off<D>(r, p1 >> 3) + ((p1 & 7) << 1)) = u32x2{w[2], w[3]};
+}
+
+// Features 8 fb .. 8 fb + 7 of row r in natural order: one 16-byte block.
+template <int D>
+__device__ __forceinline__ void blk_write(char* tile, int r, int fb, const u32x4& w) {
+  *reinterpret_cast<u32x4*>(tile + tile_off<D>(r, fb)) = w;
+}
+
+__device__ __forceinline__ u32x4 pack8(const float* x) {
+  return u32x4{pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]), pack_bf16(x[4], x[5]),
+               pack_bf16(x[6], x[7])};
+}
+
+// bf16 high parts (hi = pack8(x), given) and low parts x - hi.
+__device__ __forceinline__ u32x4 low8(const float* x, const u32x4& hi) {
+  u32x4 lo;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    lo[i] = pack_bf16(x[2 * i] - __uint_as_float(hi[i] << 16),
+                      x[2 * i + 1] - __uint_as_float(hi[i] & 0xffff0000u));
+  return lo;
 }
 
 struct PfArgs {
@@ -203,19 +247,53 @@ struct PfArgs {
   float eps;
 };
 
+// The raw inputs of one chunk as this thread loads them: RPT 16-byte blocks
+// (8 features of one token row) of q, k and v, and the decay/gate value of
+// token `lane` (and `lane + 64`) of the chunk, 1 past the end.  Rows past the
+// end of the sequence are zero.
+template <int RPT, int ND, bool HAS_Q>
+struct RawChunk {
+  u32x4 q[HAS_Q ? RPT : 1], k[RPT], v[RPT];
+  float d[ND];
+};
+
+template <int C, int D, int RPT, int ND, bool HAS_Q, int DECAY, typename DT>
+__device__ __forceinline__ void fetch_chunk(RawChunk<RPT, ND, HAS_Q>& r, const DT* qg, const DT* kg,
+                                            const DT* vg, const float* dg, int tok0, int T,
+                                            int rg, int fb, int lane) {
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int t = tok0 + RPT * rg + i;
+    if (t < T) {
+      // 32-bit element offsets within the (b, h) slab (T D < 2^31 is checked on the host)
+      const uint32_t off = uint32_t(t) * D + 8 * fb;
+      if constexpr (HAS_Q) r.q[i] = *reinterpret_cast<const u32x4*>(qg + off);
+      r.k[i] = *reinterpret_cast<const u32x4*>(kg + off);
+      r.v[i] = *reinterpret_cast<const u32x4*>(vg + off);
+    } else {
+      if constexpr (HAS_Q) r.q[i] = u32x4{0u, 0u, 0u, 0u};
+      r.k[i] = u32x4{0u, 0u, 0u, 0u};
+      r.v[i] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  if constexpr (DECAY != 0) {
+#pragma unroll
+    for (int j = 0; j < ND; ++j) {
+      const int rr = lane + 64 * j, t = tok0 + rr;
+      r.d[j] = (rr < C && t < T) ? dg[t] : 1.f;
+    }
+  }
+}
+
 // Within-chunk inclusive log-prefix of the decay, one wave: every wave of the
 // workgroup computes it redundantly (no barrier needed).  Returns lc for
 // token `lane` (and `lane + 64` in hi for C = 128) and the chunk total.
-template <int C, int DECAY>
-__device__ __forceinline__ void chunk_logprefix(const float* dg, int tok0, int T, int lane,
-                                                float& lo, float& hi, float& total) {
-  auto logdecay = [&](int r) -> float {
-    const int t = tok0 + r;
-    if (r >= C || t >= T) return 0.f;
-    return fmaxf(__logf(dg[t]), kLogFloor);
-  };
-  lo = logdecay(lane);
-  hi = C > 64 ? logdecay(lane + 64) : 0.f;
+// Tokens past the end of the chunk or the sequence contribute log 1 = 0.
+template <int C, int ND>
+__device__ __forceinline__ void chunk_logprefix(const float (&d)[ND], int lane, float& lo,
+                                                float& hi, float& total) {
+  lo = fmaxf(__logf(d[0]), kLogFloor);
+  hi = ND > 1 ? fmaxf(__logf(d[ND - 1]), kLogFloor) : 0.f;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
     const float a = __shfl_up(lo, off);
@@ -234,7 +312,7 @@ __device__ __forceinline__ void chunk_logprefix(const float* dg, int tok0, int T
 }
 
 template <int C>
-__device__ __forceinline__ float lc_of(float lo, float hi, int r) {
+__device__ __forceinline__ float lane_value(float lo, float hi, int r) {
   const float a = __shfl(lo, r & 63);
   if constexpr (C > 64) {
     const float b = __shfl(hi, r & 63);
@@ -246,6 +324,12 @@ __device__ __forceinline__ float lc_of(float lo, float hi, int r) {
 
 // ---------------------------------------------------------------- stage 1
 
+// Segment state: S_seg = sum_s w_s phi(k_s) v_s^T over the segment's tokens
+// with w_s = beta_s prod_{r > s in the segment} alpha_r (and z_seg alike),
+// plus log Gamma_seg = sum of log alpha over the segment.  The chunks are
+// walked back to front, so the weight of a token is the decay of the chunks
+// already folded (lsuf) times its within-chunk suffix, and the first chunks
+// of the segment are the most recently read when the output stage starts.
 template <int D, int C, int DECAY, typename DT>
 __global__ __launch_bounds__(2 * D) void segment_state_kernel(const PfArgs a) {
   constexpr bool VS = __is_same(DT, f16_t);   // fp16 v needs a bf16 low part too
@@ -255,7 +339,6 @@ __global__ __launch_bounds__(2 * D) void segment_state_kernel(const PfArgs a) {
   const int bh = blockIdx.x / (nseg - 1);
   const int seg = blockIdx.x % (nseg - 1);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 5, n = lane & 31;
   const int fb = tid % G::FB, rg = tid / G::FB;
   const int nchunks = (a.T + C - 1) / C;
   const int c0 = seg * a.cps;
@@ -271,50 +354,48 @@ __global__ __launch_bounds__(2 * D) void segment_state_kernel(const PfArgs a) {
 #pragma unroll
   for (int mt = 0; mt < G::MT; ++mt) acc[mt] = f32x16{};
   if (tid < D) zl[tid] = 0.f;
-  float logg = 0.f;
+  float lsuf = 0.f;   // log-decay of the chunks already folded
 
-  for (int c = c0; c < c1; ++c) {
+  auto fetch = [&](RawChunk<G::RPT, G::ND, false>& r, int c) {
+    fetch_chunk<C, D, G::RPT, G::ND, false, DECAY>(r, (const DT*)nullptr, kg, vg, dg, c * C, a.T,
+                                                    rg, fb, lane);
+  };
+  auto step = [&](RawChunk<G::RPT, G::ND, false>& raw, int c) {
     const int tok0 = c * C;
     float lo = 0.f, hi = 0.f, ltot = 0.f;
-    if constexpr (DECAY != 0) chunk_logprefix<C, DECAY>(dg, tok0, a.T, lane, lo, hi, ltot);
-    logg += ltot;
-    // ---- [A] load k, v rows; write w * phi(k) and v feature-major; z partials
-    float kx[G::RPT][8], vx[G::RPT][8];
+    if constexpr (DECAY != 0) chunk_logprefix<C, G::ND>(raw.d, lane, lo, hi, ltot);
+    // ---- [A] w phi(k) high/low and v into token-major tiles; z partials.
+    // Rows past the end have k = v = 0: phi(k) = 1 there and v = 0, so they
+    // add nothing to S; without decay their 1s are taken off z below.
     float dz[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < G::RPT; ++i) {
       const int r = G::RPT * rg + i;
-      const int t = tok0 + r;
-      u32x4 kw = {0u, 0u, 0u, 0u}, vw = {0u, 0u, 0u, 0u};
-      if (t < a.T) {
-        kw = *reinterpret_cast<const u32x4*>(kg + int64_t(t) * D + 8 * fb);
-        vw = *reinterpret_cast<const u32x4*>(vg + int64_t(t) * D + 8 * fb);
-      }
-      unpack8(kw, kx[i], DT{});
-      unpack8(vw, vx[i], DT{});
-      float w = t < a.T ? 1.f : 0.f;
+      float kx[8];
+      unpack8(raw.k[i], kx, DT{});
+      float w = 1.f;
       if constexpr (DECAY != 0) {
-        const float lct = lc_of<C>(lo, hi, r);
-        w *= __expf(ltot - lct);
-        if constexpr (DECAY == 2) w *= (t < a.T ? 1.f - dg[t] : 0.f);
+        w = tok0 + r < a.T ? __expf(lsuf + ltot - lane_value<C>(lo, hi, r)) : 0.f;
+        if constexpr (DECAY == 2) w *= 1.f - lane_value<C>(raw.d[0], G::ND > 1 ? raw.d[G::ND - 1] : 0.f, r);
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        kx[i][e] = w * elu1_fast(kx[i][e]);
-        dz[e] += kx[i][e];
+        kx[e] = elu1_fast(kx[e]);
+        if constexpr (DECAY != 0) kx[e] *= w;
+        dz[e] += kx[e];
       }
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float col_k[G::RPT], col_v[G::RPT];
-#pragma unroll
-      for (int i = 0; i < G::RPT; ++i) {
-        col_k[i] = kx[i][e];
-        col_v[i] = vx[i][e];
+      const u32x4 kh = pack8(kx);
+      blk_write<D>(smem + G::S1_KH, perm_pos(r), fb, kh);
+      blk_write<D>(smem + G::S1_KL, perm_pos(r), fb, low8(kx, kh));
+      if constexpr (VS) {
+        float vx[8];
+        unpack8(raw.v[i], vx, DT{});
+        const u32x4 vh = pack8(vx);
+        blk_write<D>(smem + G::S1_VH, perm_pos(r), fb, vh);
+        blk_write<D>(smem + G::S1_VL, perm_pos(r), fb, low8(vx, vh));
+      } else {
+        blk_write<D>(smem + G::S1_VH, perm_pos(r), fb, raw.v[i]);
       }
-      tr_write<C, G::RPT>(smem + G::S1_KH, smem + G::S1_KL, 8 * fb + e, G::RPT * rg, col_k);
-      tr_write<C, G::RPT>(smem + G::S1_VH, VS ? smem + G::S1_VL : nullptr, 8 * fb + e, G::RPT * rg,
-                          col_v);
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e)
@@ -325,38 +406,53 @@ __global__ __launch_bounds__(2 * D) void segment_state_kernel(const PfArgs a) {
       *reinterpret_cast<f32x4*>(d + 4) = f32x4{dz[4], dz[5], dz[6], dz[7]};
     }
     __syncthreads();
-    // ---- [B] z and S updates
-    const float gam = DECAY ? __expf(ltot) : 1.f;
+    // refill this register set with the chunk DEPTH further back
+    if constexpr (G::DEPTH > 0) {
+      if (c - G::DEPTH >= c0) fetch(raw, c - G::DEPTH);
+    }
+    // ---- [B] z and S updates (the weights already carry the decay)
     if (tid < D) {
-      float s = 0.f;
+      float s = DECAY ? 0.f : -float(max(tok0 + C - a.T, 0));
 #pragma unroll
       for (int w = 0; w < G::NW; ++w) s += dzl[w * D + tid];
-      zl[tid] = gam * zl[tid] + s;
+      zl[tid] += s;
     }
     u32x4 vh[G::KT], vl[G::KT];
 #pragma unroll
     for (int kk = 0; kk < G::KT; ++kk) {
-      const int off = tr_off<C>(32 * wave + n, 16 * kk + 8 * g);
-      vh[kk] = *reinterpret_cast<const u32x4*>(smem + G::S1_VH + off);
-      if constexpr (VS) vl[kk] = *reinterpret_cast<const u32x4*>(smem + G::S1_VL + off);
+      vh[kk] = tr_operand<D>(smem + G::S1_VH, 16 * kk, 32 * wave, lane);
+      if constexpr (VS) vl[kk] = tr_operand<D>(smem + G::S1_VL, 16 * kk, 32 * wave, lane);
     }
 #pragma unroll
     for (int mt = 0; mt < G::MT; ++mt) {
-      if constexpr (DECAY != 0) acc[mt] *= gam;
 #pragma unroll
       for (int kk = 0; kk < G::KT; ++kk) {
-        const int off = tr_off<C>(32 * mt + n, 16 * kk + 8 * g);
-        const u32x4 kh = *reinterpret_cast<const u32x4*>(smem + G::S1_KH + off);
-        const u32x4 kl = *reinterpret_cast<const u32x4*>(smem + G::S1_KL + off);
+        const u32x4 kh = tr_operand<D>(smem + G::S1_KH, 16 * kk, 32 * mt, lane);
+        const u32x4 kl = tr_operand<D>(smem + G::S1_KL, 16 * kk, 32 * mt, lane);
         acc[mt] = mfma(kh, vh[kk], acc[mt]);
         acc[mt] = mfma(kl, vh[kk], acc[mt]);
         if constexpr (VS) acc[mt] = mfma(kh, vl[kk], acc[mt]);
       }
     }
+    lsuf += ltot;
     __syncthreads();
+  };
+
+  RawChunk<G::RPT, G::ND, false> raw[G::RING];
+#pragma unroll
+  for (int j = 0; j < G::DEPTH; ++j)
+    if (c1 - 1 - j >= c0) fetch(raw[j], c1 - 1 - j);
+  for (int c = c1 - 1; c >= c0; c -= G::RING) {
+#pragma unroll
+    for (int j = 0; j < G::RING; ++j)
+      if (c - j >= c0) {
+        if constexpr (G::DEPTH == 0) fetch(raw[j], c - j);
+        step(raw[j], c - j);
+      }
   }
 
   // write the segment state: S row-major [f][v], then z, then log Gamma
+  const int g = lane >> 5, n = lane & 31;
   float* dst = a.ws_state + (int64_t(bh) * nseg + seg) * (D * D + D);
 #pragma unroll
   for (int mt = 0; mt < G::MT; ++mt)
@@ -366,14 +462,19 @@ __global__ __launch_bounds__(2 * D) void segment_state_kernel(const PfArgs a) {
       dst[f * D + 32 * wave + n] = acc[mt][r];
     }
   if (tid < D) dst[D * D + tid] = zl[tid];
-  if (tid == 0) a.ws_logg[int64_t(bh) * nseg + seg] = logg;
+  if (tid == 0) a.ws_logg[int64_t(bh) * nseg + seg] = lsuf;
 }
 
 // ---------------------------------------------------------------- stage 2
 
+// Exclusive scan of the segment states of one (b, h), one state element per
+// thread: the start state of segment s is Gamma_{s-1} (... (Gamma_0 S_init +
+// S_0) ...) + S_{s-1}.  Segment values are loaded 16 at a time, all in flight
+// together, then folded in order.
 template <int D>
 __global__ __launch_bounds__(256) void segment_scan_kernel(const PfArgs a) {
   constexpr int E = D * D + D;
+  constexpr int U = 16;
   const int per_bh = (E + 255) / 256;
   const int bh = blockIdx.x / per_bh;
   const int e = (blockIdx.x % per_bh) * 256 + threadIdx.x;
@@ -381,10 +482,21 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(const PfArgs a) {
   float carry = e < D * D ? a.S[int64_t(bh) * D * D + e] : a.z[int64_t(bh) * D + (e - D * D)];
   float* base = a.ws_state + int64_t(bh) * a.nseg * E + e;
   const float* lg = a.ws_logg + int64_t(bh) * a.nseg;
-  for (int s = 0; s < a.nseg; ++s) {
-    const float x = base[int64_t(s) * E];
-    base[int64_t(s) * E] = carry;
-    if (s + 1 < a.nseg) carry = __expf(lg[s]) * carry + x;
+  for (int s0 = 0; s0 < a.nseg; s0 += U) {
+    float x[U], gm[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int s = s0 + j;
+      const bool in = s + 1 < a.nseg;   // the last segment's own state is never needed
+      x[j] = in ? base[int64_t(s) * E] : 0.f;
+      gm[j] = in ? __expf(lg[s]) : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int s = s0 + j;
+      if (s < a.nseg) base[int64_t(s) * E] = carry;
+      carry = gm[j] * carry + x[j];
+    }
   }
 }
 
@@ -409,6 +521,7 @@ __global__ __launch_bounds__(2 * D) void output_kernel(const PfArgs a) {
   const DT* kg = static_cast<const DT*>(a.k) + int64_t(bh) * a.T * D;
   const DT* vg = static_cast<const DT*>(a.v) + int64_t(bh) * a.T * D;
   DT* og = static_cast<DT*>(a.out) + int64_t(bh) * a.T * D;
+  float* ogf = static_cast<float*>(a.out) + int64_t(bh) * a.T * D;
   const float* dg = DECAY ? a.decay + int64_t(bh) * a.T : nullptr;
   float* Ll = reinterpret_cast<float*>(smem + G::OFF_L);
   float* Bl = reinterpret_cast<float*>(smem + G::OFF_B);
@@ -434,51 +547,70 @@ __global__ __launch_bounds__(2 * D) void output_kernel(const PfArgs a) {
   if (tid < D) zl[tid] = z0[tid];
   __syncthreads();
 
-  for (int c = c0; c < c1; ++c) {
+  auto fetch = [&](RawChunk<G::RPT, G::ND, true>& r, int c) {
+    fetch_chunk<C, D, G::RPT, G::ND, true, DECAY>(r, qg, kg, vg, dg, c * C, a.T, rg, fb, lane);
+  };
+  auto step = [&](RawChunk<G::RPT, G::ND, true>& raw, int c) {
     const int tok0 = c * C;
     float lo = 0.f, hi = 0.f, ltot = 0.f;
-    if constexpr (DECAY != 0) chunk_logprefix<C, DECAY>(dg, tok0, a.T, lane, lo, hi, ltot);
+    if constexpr (DECAY != 0) chunk_logprefix<C, G::ND>(raw.d, lane, lo, hi, ltot);
 
-    // ---- [A] cooperative load: phi(q), phi(k) token-major; w phi(k), v
-    //      feature-major; inter-chunk denominators; z increments.
+    // ---- [A] phi(q), phi(k) and w phi(k) high/low, v into the tiles;
+    //      inter-chunk denominators; z increments.  Rows past the end of
+    //      the sequence hold k = v = 0 (phi = 1, no contribution to S; their
+    //      1s are taken off z without decay) and their outputs are not stored.
     {
       float zf[8];
       *reinterpret_cast<f32x4*>(zf) = *reinterpret_cast<const f32x4*>(zl + 8 * fb);
       *reinterpret_cast<f32x4*>(zf + 4) = *reinterpret_cast<const f32x4*>(zl + 8 * fb + 4);
-      float kw_[G::RPT][8], vx[G::RPT][8];
       float dz[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < G::RPT; ++i) {
         const int r = G::RPT * rg + i;
-        const int t = tok0 + r;
-        const bool valid = t < a.T;
-        u32x4 qw = {0u, 0u, 0u, 0u}, kw = {0u, 0u, 0u, 0u}, vw = {0u, 0u, 0u, 0u};
-        if (valid) {
-          qw = *reinterpret_cast<const u32x4*>(qg + int64_t(t) * D + 8 * fb);
-          kw = *reinterpret_cast<const u32x4*>(kg + int64_t(t) * D + 8 * fb);
-          vw = *reinterpret_cast<const u32x4*>(vg + int64_t(t) * D + 8 * fb);
-        }
         float qx[8], kx[8];
-        unpack8(qw, qx, DT{});
-        unpack8(kw, kx, DT{});
-        unpack8(vw, vx[i], DT{});
-        float lct = 0.f, w = valid ? 1.f : 0.f, beta = 1.f;
+        unpack8(raw.q[i], qx, DT{});
+        unpack8(raw.k[i], kx, DT{});
+        float lct = 0.f, w = 1.f, beta = 1.f;
         if constexpr (DECAY != 0) {
-          lct = lc_of<C>(lo, hi, r);
-          if constexpr (DECAY == 2) beta = valid ? 1.f - dg[t] : 0.f;
-          w *= beta * __expf(ltot - lct);
+          lct = lane_value<C>(lo, hi, r);
+          if constexpr (DECAY == 2)
+            beta = 1.f - lane_value<C>(raw.d[0], G::ND > 1 ? raw.d[G::ND - 1] : 0.f, r);
+          w = tok0 + r < a.T ? beta * __expf(ltot - lct) : 0.f;
         }
         float den = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          qx[e] = valid ? elu1_fast(qx[e]) : 0.f;
-          kx[e] = valid ? elu1_fast(kx[e]) : 0.f;
-          den += qx[e] * zf[e];
-          kw_[i][e] = w * kx[e];
-          dz[e] += kw_[i][e];
+          qx[e] = elu1_fast(qx[e]);
+          kx[e] = elu1_fast(kx[e]);
+          den = fmaf(qx[e], zf[e], den);
         }
-        row_write<G::ROW_B>(smem + G::OFF_Q, r, fb, qx);
-        row_write<G::ROW_B>(smem + G::OFF_K, r, fb, kx);
+        row_write_perm<D>(smem + G::OFF_Q, r, fb, pack8(qx));
+        const u32x4 kp = pack8(kx);
+        row_write_perm<D>(smem + G::OFF_K, r, fb, kp);
+        if constexpr (DECAY != 0) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            kx[e] *= w;
+            dz[e] += kx[e];
+          }
+          const u32x4 kh = pack8(kx);
+          blk_write<D>(smem + G::OFF_KH, perm_pos(r), fb, kh);
+          blk_write<D>(smem + G::OFF_KL, perm_pos(r), fb, low8(kx, kh));
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) dz[e] += kx[e];
+          blk_write<D>(smem + G::OFF_KH, perm_pos(r), fb, kp);
+          blk_write<D>(smem + G::OFF_KL, perm_pos(r), fb, low8(kx, kp));
+        }
+        if constexpr (VS) {
+          float vx[8];
+          unpack8(raw.v[i], vx, DT{});
+          const u32x4 vh = pack8(vx);
+          blk_write<D>(smem + G::OFF_VH, perm_pos(r), fb, vh);
+          blk_write<D>(smem + G::OFF_VL, perm_pos(r), fb, low8(vx, vh));
+        } else {
+          blk_write<D>(smem + G::OFF_VH, perm_pos(r), fb, raw.v[i]);
+        }
 #pragma unroll
         for (int off = 1; off < G::FB; off <<= 1) den += __shfl_xor(den, off);
         if (fb == 0) {
@@ -487,18 +619,6 @@ __global__ __launch_bounds__(2 * D) void output_kernel(const PfArgs a) {
           Ll[r] = lct;
           Bl[r] = beta;
         }
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float col_k[G::RPT], col_v[G::RPT];
-#pragma unroll
-        for (int i = 0; i < G::RPT; ++i) {
-          col_k[i] = kw_[i][e];
-          col_v[i] = vx[i][e];
-        }
-        tr_write<C, G::RPT>(smem + G::OFF_KH, smem + G::OFF_KL, 8 * fb + e, G::RPT * rg, col_k);
-        tr_write<C, G::RPT>(smem + G::OFF_VH, VS ? smem + G::OFF_VL : nullptr, 8 * fb + e,
-                            G::RPT * rg, col_v);
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e)
@@ -510,31 +630,26 @@ __global__ __launch_bounds__(2 * D) void output_kernel(const PfArgs a) {
       }
     }
     __syncthreads();
+    // refill this register set with the chunk DEPTH ahead: its loads are in
+    // flight while this chunk and the next DEPTH - 1 are computed
+    if constexpr (G::DEPTH > 0) {
+      if (c + G::DEPTH < c1) fetch(raw, c + G::DEPTH);
+    }
 
     // ---- [B] per wave: read-out of the carried state, masked intra-chunk
     //      attention, normalise and store, then fold the chunk into S and z.
     const float gam = DECAY ? __expf(ltot) : 1.f;
     if (tid < D) {
-      float s = 0.f;
+      float s = DECAY ? 0.f : -float(max(tok0 + C - a.T, 0));
 #pragma unroll
       for (int w = 0; w < G::NW; ++w) s += dzl[w * D + tid];
       zl[tid] = gam * zl[tid] + s;   // z of the next chunk; read again after the barrier
     }
-    // state as bf16 operands (k = features), from the accumulators
-    u32x4 sf[G::KS];
-#pragma unroll
-    for (int ks = 0; ks < G::KS; ++ks) {
-      const int mt = ks >> 1, j0 = 2 * (ks & 1);
-      const f32x16& s = acc[mt];
-      sf[ks] = u32x4{pack_bf16(s[4 * j0 + 0], s[4 * j0 + 1]), pack_bf16(s[4 * j0 + 2], s[4 * j0 + 3]),
-                     pack_bf16(s[4 * j0 + 4], s[4 * j0 + 5]), pack_bf16(s[4 * j0 + 6], s[4 * j0 + 7])};
-    }
     u32x4 vh[G::KT], vl[G::KT];
 #pragma unroll
     for (int kk = 0; kk < G::KT; ++kk) {
-      const int off = tr_off<C>(32 * wave + n, 16 * kk + 8 * g);
-      vh[kk] = *reinterpret_cast<const u32x4*>(smem + G::OFF_VH + off);
-      if constexpr (VS) vl[kk] = *reinterpret_cast<const u32x4*>(smem + G::OFF_VL + off);
+      vh[kk] = tr_operand<D>(smem + G::OFF_VH, 16 * kk, 32 * wave, lane);
+      if constexpr (VS) vl[kk] = tr_operand<D>(smem + G::OFF_VL, 16 * kk, 32 * wave, lane);
     }
 
 #pragma unroll
@@ -542,11 +657,18 @@ __global__ __launch_bounds__(2 * D) void output_kernel(const PfArgs a) {
       const int tl = 32 * tb + n;   // this lane's query token within the chunk
       u32x4 qf[G::KS];
 #pragma unroll
-      for (int ks = 0; ks < G::KS; ++ks)
-        qf[ks] = *reinterpret_cast<const u32x4*>(smem + G::OFF_Q + tl * G::ROW_B + 32 * ks + 16 * g);
+      for (int ks = 0; ks < G::KS; ++ks) qf[ks] = row_operand<D>(smem + G::OFF_Q, tl, 2 * ks + g);
+      // read-out of the carried state, O^T = S^T phi(Q)^T: the fp32
+      // accumulators become bf16 operands (k = features) one k-step at a time
       f32x16 o = f32x16{};
 #pragma unroll
-      for (int ks = 0; ks < G::KS; ++ks) o = mfma(sf[ks], qf[ks], o);
+      for (int ks = 0; ks < G::KS; ++ks) {
+        const f32x16& sa = acc[ks >> 1];
+        const int j0 = 8 * (ks & 1);
+        const u32x4 sf = {pack_bf16(sa[j0 + 0], sa[j0 + 1]), pack_bf16(sa[j0 + 2], sa[j0 + 3]),
+                          pack_bf16(sa[j0 + 4], sa[j0 + 5]), pack_bf16(sa[j0 + 6], sa[j0 + 7])};
+        o = mfma(sf, qf[ks], o);
+      }
       float lct = 0.f;
       if constexpr (DECAY != 0) {
         lct = Ll[tl];
@@ -557,10 +679,8 @@ __global__ __launch_bounds__(2 * D) void output_kernel(const PfArgs a) {
       for (int sb = 0; sb <= tb; ++sb) {
         f32x16 p = f32x16{};
 #pragma unroll
-        for (int ks = 0; ks < G::KS; ++ks) {
-          const u32x4 kf = *reinterpret_cast<const u32x4*>(smem + G::OFF_K + (32 * sb + n) * G::ROW_B + 32 * ks + 16 * g);
-          p = mfma(kf, qf[ks], p);
-        }
+        for (int ks = 0; ks < G::KS; ++ks)
+          p = mfma(row_operand<D>(smem + G::OFF_K, 32 * sb + n, 2 * ks + g), qf[ks], p);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int sl = 32 * sb + 8 * (r >> 2) + 4 * g + (r & 3);
@@ -590,17 +710,16 @@ __global__ __launch_bounds__(2 * D) void output_kernel(const PfArgs a) {
         }
       }
       dsum += __shfl_xor(dsum, 32);
-      const float inv = 1.0f / (denl[tl] + dsum + a.eps);
+      const float inv = __builtin_amdgcn_rcpf(denl[tl] + dsum + a.eps);
       const int t = tok0 + tl;
       if (t < a.T) {
+        const uint32_t orow = uint32_t(t) * D + 32 * wave + 4 * g;
         if (a.out_f32) {
-          float* orow = static_cast<float*>(a.out) + (int64_t(bh) * a.T + t) * D + 32 * wave + 4 * g;
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            *reinterpret_cast<f32x4*>(orow + 8 * j) =
+            *reinterpret_cast<f32x4*>(ogf + orow + 8 * j) =
                 f32x4{o[4 * j] * inv, o[4 * j + 1] * inv, o[4 * j + 2] * inv, o[4 * j + 3] * inv};
         } else {
-          DT* orow = og + int64_t(t) * D + 32 * wave + 4 * g;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const float y0 = o[4 * j] * inv, y1 = o[4 * j + 1] * inv;
@@ -613,7 +732,7 @@ __global__ __launch_bounds__(2 * D) void output_kernel(const PfArgs a) {
               w = u32x2{__builtin_bit_cast(uint32_t, h2{(f16_t)y0, (f16_t)y1}),
                         __builtin_bit_cast(uint32_t, h2{(f16_t)y2, (f16_t)y3})};
             }
-            *reinterpret_cast<u32x2*>(orow + 8 * j) = w;
+            *reinterpret_cast<u32x2*>(og + orow + 8 * j) = w;
           }
         }
       }
@@ -625,15 +744,27 @@ __global__ __launch_bounds__(2 * D) void output_kernel(const PfArgs a) {
       if constexpr (DECAY != 0) acc[mt] *= gam;
 #pragma unroll
       for (int kk = 0; kk < G::KT; ++kk) {
-        const int off = tr_off<C>(32 * mt + n, 16 * kk + 8 * g);
-        const u32x4 kh = *reinterpret_cast<const u32x4*>(smem + G::OFF_KH + off);
-        const u32x4 kl = *reinterpret_cast<const u32x4*>(smem + G::OFF_KL + off);
+        const u32x4 kh = tr_operand<D>(smem + G::OFF_KH, 16 * kk, 32 * mt, lane);
+        const u32x4 kl = tr_operand<D>(smem + G::OFF_KL, 16 * kk, 32 * mt, lane);
         acc[mt] = mfma(kh, vh[kk], acc[mt]);
         acc[mt] = mfma(kl, vh[kk], acc[mt]);
         if constexpr (VS) acc[mt] = mfma(kh, vl[kk], acc[mt]);
       }
     }
     __syncthreads();
+  };
+
+  RawChunk<G::RPT, G::ND, true> raw[G::RING];
+#pragma unroll
+  for (int j = 0; j < G::DEPTH; ++j)
+    if (c0 + j < c1) fetch(raw[j], c0 + j);
+  for (int c = c0; c < c1; c += G::RING) {
+#pragma unroll
+    for (int j = 0; j < G::RING; ++j)
+      if (c + j < c1) {
+        if constexpr (G::DEPTH == 0) fetch(raw[j], c + j);
+        step(raw[j], c + j);
+      }
   }
 
   if (seg == nseg - 1) {
@@ -705,10 +836,11 @@ bool mfma_supported(const Problem& p) {
 // Chunks whose stage-3 tiles fit in the 160 KB of LDS of one compute unit.
 bool mfma_chunk_fits(int d, int chunk) { return chunk <= 64 || d <= 64; }
 
-// Aim for about two workgroups per compute unit on a 256-CU part, with at
-// least two chunks per segment.
+// The output stage holds one 4-wave workgroup per compute unit at d = 128
+// (two 2-wave ones at d = 64): aim for exactly that many workgroups on the
+// 256 compute units, with at least two chunks per segment.
 int mfma_default_segments(const Problem& p) {
-  const int64_t target_wg = 512;
+  const int64_t target_wg = p.dv == 128 ? 256 : 512;
   const int64_t BH = p.BH();
   const int nchunks = (p.T + p.chunk - 1) / p.chunk;
   int64_t seg = (target_wg + BH - 1) / BH;

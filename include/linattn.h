@@ -100,7 +100,7 @@ typedef struct la_desc {
   la_decay decay_kind;   /* decay / gate kind                                     */
   const float* decay;    /* device fp32 a_t or g_t; NULL iff LA_DECAY_NONE        */
   float eps;             /* added to the denominator (finite); 1e-6 on the pages  */
-  int chunk;             /* prefill chunk length, 0 = default (64); 32/64/128     */
+  int chunk;             /* prefill chunk length, 0 = default (32); 32/64/128     */
   int segments;          /* prefill segments per (b, h), 0 = automatic            */
 } la_desc;
 

@@ -46,19 +46,21 @@ def test_feature_dim():
 def test_plan_for_the_measured_prefills():
     # long context: chunked MFMA path, segments spread 8 heads over the chip
     c, s, p = la.prefill_plan(desc())
-    assert (c, p) == (64, 1) and s > 1 and 1600 % ((1600 + s - 1) // s) >= 0
+    assert (c, s, p) == (32, 32, 1)    # one workgroup per compute unit: 8 heads x 32 segments
     assert la.prefill_workspace_size(desc()) == 8 * s * (128 * 128 + 128) * 4 + (
         (8 * s * 4 + 255) // 256) * 256
     # fp32 inputs take the per-token kernel; no workspace
     d = desc(T=8, d_h=4, d_v=4, dtype_code=_lib.LA_F32)
     assert la.prefill_plan(d)[2] == 0 and la.prefill_workspace_size(d) == 0
     # explicit segments are honoured up to the chunk count, never leaving one empty
-    d = desc(T=640, segments=4)
+    d = desc(T=640, segments=4, chunk=64)
     assert la.prefill_plan(d) == (64, 4, 1)
-    d = desc(T=9 * 64, segments=4)   # 9 chunks, 3 per segment -> 3 segments
+    d = desc(T=9 * 64, segments=4, chunk=64)   # 9 chunks, 3 per segment -> 3 segments
     assert la.prefill_plan(d)[1] == 3
-    d = desc(T=100, segments=50)
+    d = desc(T=100, segments=50, chunk=64)
     assert la.prefill_plan(d)[1] == 2
+    d = desc(T=100, segments=50)                # 4 chunks of 32 -> 4 segments
+    assert la.prefill_plan(d) == (32, 4, 1)
 
 
 @pytest.mark.parametrize("field,value", [("B", 0), ("H", -1), ("T", -5), ("d_h", 0), ("d_v", 0),

@@ -197,7 +197,7 @@ def test_prefill_stages_compose_to_prefill():
     q, k, v = x.q.to(dev), x.k.to(dev), x.v.to(dev)
     ref, _, _ = la.prefill(q, k, v, segments=5)
     desc = la.make_desc(1, 4, 700, 128, 128, 1, segments=5)
-    assert la.prefill_plan(desc)[1] == 4   # 11 chunks, 3 per segment
+    assert la.prefill_plan(desc)[1] == 5   # 22 chunks of 32, 5 per segment
     ws = torch.empty(la.prefill_workspace_size(desc), dtype=torch.uint8, device=dev)
     S, z = la.state_init(1, 4, 128, 128, dev)
     out = torch.empty_like(q)
