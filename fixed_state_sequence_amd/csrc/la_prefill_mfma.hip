@@ -120,30 +120,40 @@ struct Cfg {
   //          features (read transposed: the k = token operand of the fold)
   //   VH, VL v (high/low parts only for fp16 inputs); row = perm_pos(token),
   //          natural features (read transposed for P V and the fold)
-  static constexpr int OFF_Q = 0;
-  static constexpr int OFF_K = OFF_Q + TILE;
-  static constexpr int OFF_KH = OFF_K + TILE;
-  static constexpr int OFF_KL = OFF_KH + TILE;
-  static constexpr int OFF_VH = OFF_KL + TILE;
-  static constexpr int OFF_VL = OFF_VH + TILE;
-  static constexpr int OFF_L = OFF_VL + (VS ? TILE : 0);  // lc_t, fp32 [C]
-  static constexpr int OFF_B = OFF_L + 4 * C;           // beta_t, fp32 [C]
-  static constexpr int OFF_DEN = OFF_B + 4 * C;         // inter-chunk denominators, fp32 [C]
-  static constexpr int OFF_Z = OFF_DEN + 4 * C;         // z, fp32 [D]
-  static constexpr int OFF_DZ = OFF_Z + 4 * D;          // per-wave z increments, fp32 [NW][D]
-  static constexpr int LDS = OFF_DZ + 4 * NW * D;
-  // stage 1: KH, KL, VH (VL) and the small arrays
+  // followed by per-token fp32 arrays and the per-wave z increments.
+  static constexpr int B_Q = 0;
+  static constexpr int B_K = B_Q + TILE;
+  static constexpr int B_KH = B_K + TILE;
+  static constexpr int B_KL = B_KH + TILE;
+  static constexpr int B_VH = B_KL + TILE;
+  static constexpr int B_VL = B_VH + TILE;
+  static constexpr int B_L = B_VL + (VS ? TILE : 0);  // lc_t, fp32 [C]
+  static constexpr int B_B = B_L + 4 * C;             // beta_t, fp32 [C]
+  static constexpr int B_DEN = B_B + 4 * C;           // inter-chunk denominators, fp32 [C]
+  static constexpr int B_DZ = B_DEN + 4 * C;          // per-wave z increments, fp32 [NW][D]
+  static constexpr int BUF = B_DZ + 4 * NW * D;
+  // The output stage: producer waves stage chunk c + 1 into one buffer while
+  // consumer waves compute chunk c from the other, when two buffers fit; each
+  // buffer also carries the chunk's total log-decay.
+  static constexpr int B_LT = BUF;
+  static constexpr int BUF3 = BUF + 16;
+  static constexpr int NBUF = 2 * BUF3 <= 160 * 1024 ? 2 : 1;
+  static constexpr int LDS = NBUF * BUF3;
+  // producer prefetch depth (registers are not shared with the consumers'
+  // accumulators, so it can be deeper)
+  static constexpr int PDEPTH = RPT <= 2 ? 2 : 1;
+  // stage 1: KH, KL, VH (VL) and the z increments, two buffers
   static constexpr int S1_KH = 0;
   static constexpr int S1_KL = S1_KH + TILE;
   static constexpr int S1_VH = S1_KL + TILE;
   static constexpr int S1_VL = S1_VH + TILE;
-  static constexpr int S1_Z = S1_VL + (VS ? TILE : 0);
-  static constexpr int S1_DZ = S1_Z + 4 * D;
-  static constexpr int S1_LDS = S1_DZ + 4 * NW * D;
+  static constexpr int S1_DZ = S1_VL + (VS ? TILE : 0);
+  static constexpr int S1_BUF = S1_DZ + 4 * NW * D;
+  static constexpr int S1_LDS = 2 * S1_BUF;
   static_assert(RPT == C / 16, "row split");
   static_assert(C == 32 || C == 64 || C == 128, "chunk");
   static_assert(D == 64 || D == 128, "width");
-  static_assert(LDS <= 160 * 1024, "LDS");
+  static_assert(LDS <= 160 * 1024 && S1_LDS <= 160 * 1024, "LDS");
 };
 
 // XOR swizzle of the 16-byte blocks of tile row r.  Two read patterns must
@@ -249,8 +259,10 @@ struct PfArgs {
 
 // The raw inputs of one chunk as this thread loads them: RPT 16-byte blocks
 // (8 features of one token row) of q, k and v, and the decay/gate value of
-// token `lane` (and `lane + 64`) of the chunk, 1 past the end.  Rows past the
-// end of the sequence are zero.
+// token `lane` (and `lane + 64`) of the chunk.  The loads are unconditional
+// (rows past the end of the sequence read the last row) so that the compiler
+// can count the loads still in flight exactly when a later chunk's data is
+// used; clean_chunk() then zeroes those rows (and sets their decay to 1).
 template <int RPT, int ND, bool HAS_Q>
 struct RawChunk {
   u32x4 q[HAS_Q ? RPT : 1], k[RPT], v[RPT];
@@ -263,24 +275,39 @@ __device__ __forceinline__ void fetch_chunk(RawChunk<RPT, ND, HAS_Q>& r, const D
                                             int rg, int fb, int lane) {
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
-    const int t = tok0 + RPT * rg + i;
-    if (t < T) {
-      // 32-bit element offsets within the (b, h) slab (T D < 2^31 is checked on the host)
-      const uint32_t off = uint32_t(t) * D + 8 * fb;
-      if constexpr (HAS_Q) r.q[i] = *reinterpret_cast<const u32x4*>(qg + off);
-      r.k[i] = *reinterpret_cast<const u32x4*>(kg + off);
-      r.v[i] = *reinterpret_cast<const u32x4*>(vg + off);
-    } else {
-      if constexpr (HAS_Q) r.q[i] = u32x4{0u, 0u, 0u, 0u};
-      r.k[i] = u32x4{0u, 0u, 0u, 0u};
-      r.v[i] = u32x4{0u, 0u, 0u, 0u};
-    }
+    const int t = min(tok0 + RPT * rg + i, T - 1);
+    // 32-bit element offsets within the (b, h) slab (T D < 2^31 is checked on the host)
+    const uint32_t off = uint32_t(t) * D + 8 * fb;
+    if constexpr (HAS_Q) r.q[i] = *reinterpret_cast<const u32x4*>(qg + off);
+    r.k[i] = *reinterpret_cast<const u32x4*>(kg + off);
+    r.v[i] = *reinterpret_cast<const u32x4*>(vg + off);
+  }
+  if constexpr (DECAY != 0) {
+#pragma unroll
+    for (int j = 0; j < ND; ++j) r.d[j] = dg[min(tok0 + lane + 64 * j, T - 1)];
+  }
+}
+
+// Rows past the end of the sequence become 0 and decay values of tokens
+// outside the chunk or the sequence become 1 (the loads read in-bounds
+// stand-ins).  The row pass runs only for the chunk holding the end.
+template <int C, int RPT, int ND, bool HAS_Q, int DECAY>
+__device__ __forceinline__ void clean_chunk(RawChunk<RPT, ND, HAS_Q>& r, int tok0, int T, int rg,
+                                            int lane) {
+  if (tok0 + C > T) {
+#pragma unroll
+    for (int i = 0; i < RPT; ++i)
+      if (tok0 + RPT * rg + i >= T) {
+        if constexpr (HAS_Q) r.q[i] = u32x4{0u, 0u, 0u, 0u};
+        r.k[i] = u32x4{0u, 0u, 0u, 0u};
+        r.v[i] = u32x4{0u, 0u, 0u, 0u};
+      }
   }
   if constexpr (DECAY != 0) {
 #pragma unroll
     for (int j = 0; j < ND; ++j) {
-      const int rr = lane + 64 * j, t = tok0 + rr;
-      r.d[j] = (rr < C && t < T) ? dg[t] : 1.f;
+      const int rr = lane + 64 * j;
+      if (rr >= C || tok0 + rr >= T) r.d[j] = 1.f;
     }
   }
 }
@@ -347,26 +374,26 @@ __global__ __launch_bounds__(2 * D) void segment_state_kernel(const PfArgs a) {
   const DT* kg = static_cast<const DT*>(a.k) + int64_t(bh) * a.T * D;
   const DT* vg = static_cast<const DT*>(a.v) + int64_t(bh) * a.T * D;
   const float* dg = DECAY ? a.decay + int64_t(bh) * a.T : nullptr;
-  float* zl = reinterpret_cast<float*>(smem + G::S1_Z);
-  float* dzl = reinterpret_cast<float*>(smem + G::S1_DZ);
 
   f32x16 acc[G::MT];
 #pragma unroll
   for (int mt = 0; mt < G::MT; ++mt) acc[mt] = f32x16{};
-  if (tid < D) zl[tid] = 0.f;
-  float lsuf = 0.f;   // log-decay of the chunks already folded
+  float zf[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};   // z of features 8 fb .. 8 fb + 7
+  float lsuf = 0.f;   // log-decay of the chunks already staged (later in the segment)
 
   auto fetch = [&](RawChunk<G::RPT, G::ND, false>& r, int c) {
     fetch_chunk<C, D, G::RPT, G::ND, false, DECAY>(r, (const DT*)nullptr, kg, vg, dg, c * C, a.T,
                                                     rg, fb, lane);
   };
-  auto step = [&](RawChunk<G::RPT, G::ND, false>& raw, int c) {
+  // [A] chunk c into buffer buf: w phi(k) high/low and v as token-major
+  // tiles, per-wave z increments.  Rows past the end have k = v = 0: phi(k) =
+  // 1 there and v = 0, so they add nothing to S; without decay their 1s are
+  // taken off z when the increments are summed.
+  auto stage = [&](RawChunk<G::RPT, G::ND, false>& raw, int c, char* buf) {
     const int tok0 = c * C;
+    clean_chunk<C, G::RPT, G::ND, false, DECAY>(raw, tok0, a.T, rg, lane);
     float lo = 0.f, hi = 0.f, ltot = 0.f;
     if constexpr (DECAY != 0) chunk_logprefix<C, G::ND>(raw.d, lane, lo, hi, ltot);
-    // ---- [A] w phi(k) high/low and v into token-major tiles; z partials.
-    // Rows past the end have k = v = 0: phi(k) = 1 there and v = 0, so they
-    // add nothing to S; without decay their 1s are taken off z below.
     float dz[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < G::RPT; ++i) {
@@ -385,70 +412,85 @@ __global__ __launch_bounds__(2 * D) void segment_state_kernel(const PfArgs a) {
         dz[e] += kx[e];
       }
       const u32x4 kh = pack8(kx);
-      blk_write<D>(smem + G::S1_KH, perm_pos(r), fb, kh);
-      blk_write<D>(smem + G::S1_KL, perm_pos(r), fb, low8(kx, kh));
+      blk_write<D>(buf + G::S1_KH, perm_pos(r), fb, kh);
+      blk_write<D>(buf + G::S1_KL, perm_pos(r), fb, low8(kx, kh));
       if constexpr (VS) {
         float vx[8];
         unpack8(raw.v[i], vx, DT{});
         const u32x4 vh = pack8(vx);
-        blk_write<D>(smem + G::S1_VH, perm_pos(r), fb, vh);
-        blk_write<D>(smem + G::S1_VL, perm_pos(r), fb, low8(vx, vh));
+        blk_write<D>(buf + G::S1_VH, perm_pos(r), fb, vh);
+        blk_write<D>(buf + G::S1_VL, perm_pos(r), fb, low8(vx, vh));
       } else {
-        blk_write<D>(smem + G::S1_VH, perm_pos(r), fb, raw.v[i]);
+        blk_write<D>(buf + G::S1_VH, perm_pos(r), fb, raw.v[i]);
       }
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e)
       for (int off = G::FB; off < 64; off <<= 1) dz[e] += __shfl_xor(dz[e], off);
     if (lane < G::FB) {
-      float* d = dzl + wave * D + 8 * fb;
+      float* d = reinterpret_cast<float*>(buf + G::S1_DZ) + wave * D + 8 * fb;
       *reinterpret_cast<f32x4*>(d) = f32x4{dz[0], dz[1], dz[2], dz[3]};
       *reinterpret_cast<f32x4*>(d + 4) = f32x4{dz[4], dz[5], dz[6], dz[7]};
     }
-    __syncthreads();
-    // refill this register set with the chunk DEPTH further back
-    if constexpr (G::DEPTH > 0) {
-      if (c - G::DEPTH >= c0) fetch(raw, c - G::DEPTH);
-    }
-    // ---- [B] z and S updates (the weights already carry the decay)
-    if (tid < D) {
-      float s = DECAY ? 0.f : -float(max(tok0 + C - a.T, 0));
+    if (c >= c0) lsuf += ltot;
+    // refill this register set with the chunk DEPTH further back (clamped:
+    // the loads are issued on every path, see RawChunk)
+    if constexpr (G::DEPTH > 0) fetch(raw, max(c - G::DEPTH, c0));
+  };
+  // [B] fold chunk c (staged in buf) into S and z; the weights already
+  // carry the decay.
+  auto fold = [&](int c, const char* buf) {
+    const float* dzl = reinterpret_cast<const float*>(buf + G::S1_DZ);
+    const float pad = DECAY ? 0.f : float(max(c * C + C - a.T, 0));
 #pragma unroll
-      for (int w = 0; w < G::NW; ++w) s += dzl[w * D + tid];
-      zl[tid] += s;
+    for (int e = 0; e < 8; ++e) {
+      float s = -pad;
+#pragma unroll
+      for (int w = 0; w < G::NW; ++w) s += dzl[w * D + 8 * fb + e];
+      zf[e] += s;
     }
     u32x4 vh[G::KT], vl[G::KT];
 #pragma unroll
     for (int kk = 0; kk < G::KT; ++kk) {
-      vh[kk] = tr_operand<D>(smem + G::S1_VH, 16 * kk, 32 * wave, lane);
-      if constexpr (VS) vl[kk] = tr_operand<D>(smem + G::S1_VL, 16 * kk, 32 * wave, lane);
+      vh[kk] = tr_operand<D>(buf + G::S1_VH, 16 * kk, 32 * wave, lane);
+      if constexpr (VS) vl[kk] = tr_operand<D>(buf + G::S1_VL, 16 * kk, 32 * wave, lane);
     }
 #pragma unroll
     for (int mt = 0; mt < G::MT; ++mt) {
 #pragma unroll
       for (int kk = 0; kk < G::KT; ++kk) {
-        const u32x4 kh = tr_operand<D>(smem + G::S1_KH, 16 * kk, 32 * mt, lane);
-        const u32x4 kl = tr_operand<D>(smem + G::S1_KL, 16 * kk, 32 * mt, lane);
+        const u32x4 kh = tr_operand<D>(buf + G::S1_KH, 16 * kk, 32 * mt, lane);
+        const u32x4 kl = tr_operand<D>(buf + G::S1_KL, 16 * kk, 32 * mt, lane);
         acc[mt] = mfma(kh, vh[kk], acc[mt]);
         acc[mt] = mfma(kl, vh[kk], acc[mt]);
         if constexpr (VS) acc[mt] = mfma(kh, vl[kk], acc[mt]);
       }
     }
-    lsuf += ltot;
-    __syncthreads();
   };
 
+  // Chunks are walked back to front, c1 - 1 first; the i-th chunk walked
+  // uses register set i % RING and buffer i % 2.  Chunk i + 1 is staged while
+  // chunk i is folded.
+  // Every step stages a chunk (a repeat of chunk c0 past the start, whose
+  // tiles are never folded), so the loads are the same on every path.
   RawChunk<G::RPT, G::ND, false> raw[G::RING];
 #pragma unroll
-  for (int j = 0; j < G::DEPTH; ++j)
-    if (c1 - 1 - j >= c0) fetch(raw[j], c1 - 1 - j);
-  for (int c = c1 - 1; c >= c0; c -= G::RING) {
+  for (int j = 0; j < G::DEPTH; ++j) fetch(raw[j], max(c1 - 1 - j, c0));
+  if constexpr (G::DEPTH == 0) fetch(raw[0], c1 - 1);
+  stage(raw[0], c1 - 1, smem);
+  __syncthreads();
+  for (int i0 = 0; i0 < c1 - c0; i0 += G::RING) {
 #pragma unroll
-    for (int j = 0; j < G::RING; ++j)
-      if (c - j >= c0) {
-        if constexpr (G::DEPTH == 0) fetch(raw[j], c - j);
-        step(raw[j], c - j);
-      }
+    for (int j = 0; j < G::RING; ++j) {
+      const int i = i0 + j;
+      const int c = c1 - 1 - i;
+      char* cur = smem + (i & 1) * G::S1_BUF;
+      char* nxt = smem + ((i + 1) & 1) * G::S1_BUF;
+      if constexpr (G::DEPTH == 0) fetch(raw[0], max(c - 1, c0));
+      stage(raw[(j + 1) % G::RING], c - 1, nxt);
+      if (c >= c0) fold(c, cur);
+      __syncthreads();
+    }
   }
 
   // write the segment state: S row-major [f][v], then z, then log Gamma
@@ -461,7 +503,10 @@ __global__ __launch_bounds__(2 * D) void segment_state_kernel(const PfArgs a) {
       const int f = 32 * mt + 8 * (r >> 2) + 4 * g + (r & 3);
       dst[f * D + 32 * wave + n] = acc[mt][r];
     }
-  if (tid < D) dst[D * D + tid] = zl[tid];
+  if (rg == 0) {
+    *reinterpret_cast<f32x4*>(dst + D * D + 8 * fb) = f32x4{zf[0], zf[1], zf[2], zf[3]};
+    *reinterpret_cast<f32x4*>(dst + D * D + 8 * fb + 4) = f32x4{zf[4], zf[5], zf[6], zf[7]};
+  }
   if (tid == 0) a.ws_logg[int64_t(bh) * nseg + seg] = lsuf;
 }
 
@@ -502,67 +547,65 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(const PfArgs a) {
 
 // ---------------------------------------------------------------- stage 3
 
+// Output stage, warp-specialised: a workgroup of 2 NW waves holds NW
+// consumer waves (the MFMA work: read-out, scores, P V, fold; each owns 32
+// value columns of the state in accumulators) and NW producer waves (the
+// loads and the VALU staging: feature maps, bf16 splits, tiles, denominators
+// and z).  With two LDS buffers the producers stage chunk c + 1 while the
+// consumers compute chunk c, one barrier per chunk; each role fits in 256
+// registers, so a producer and a consumer wave share every SIMD.
 template <int D, int C, int DECAY, typename DT>
-__global__ __launch_bounds__(2 * D) void output_kernel(const PfArgs a) {
+__global__ __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void output_kernel(const PfArgs a) {
   constexpr bool VS = __is_same(DT, f16_t);   // fp16 v needs a bf16 low part too
   using G = Cfg<D, C, VS>;
   __shared__ __align__(16) char smem[G::LDS];
   const int nseg = a.nseg;
   const int bh = blockIdx.x / nseg;
   const int seg = blockIdx.x % nseg;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 5, n = lane & 31;
-  const int fb = tid % G::FB, rg = tid / G::FB;
   const int nchunks = (a.T + C - 1) / C;
   const int c0 = seg * a.cps;
   const int c1 = min(c0 + a.cps, nchunks);
+  const int nc = c1 - c0;
+  const bool last = seg == nseg - 1;
+  const float* Sstart = nseg > 1 ? a.ws_state + (int64_t(bh) * nseg + seg) * (D * D + D)
+                                 : a.S + int64_t(bh) * D * D;
+  const float* zstart = nseg > 1 ? Sstart + D * D : a.z + int64_t(bh) * D;
+  auto buffer = [&](int i) -> char* { return smem + (G::NBUF == 2 ? (i & 1) * G::BUF3 : 0); };
 
-  const DT* qg = static_cast<const DT*>(a.q) + int64_t(bh) * a.T * D;
-  const DT* kg = static_cast<const DT*>(a.k) + int64_t(bh) * a.T * D;
-  const DT* vg = static_cast<const DT*>(a.v) + int64_t(bh) * a.T * D;
-  DT* og = static_cast<DT*>(a.out) + int64_t(bh) * a.T * D;
-  float* ogf = static_cast<float*>(a.out) + int64_t(bh) * a.T * D;
-  const float* dg = DECAY ? a.decay + int64_t(bh) * a.T : nullptr;
-  float* Ll = reinterpret_cast<float*>(smem + G::OFF_L);
-  float* Bl = reinterpret_cast<float*>(smem + G::OFF_B);
-  float* denl = reinterpret_cast<float*>(smem + G::OFF_DEN);
-  float* zl = reinterpret_cast<float*>(smem + G::OFF_Z);
-  float* dzl = reinterpret_cast<float*>(smem + G::OFF_DZ);
+  // the role is uniform per wave: tell the compiler, so the two roles are
+  // separate paths rather than one masked sequence with both live sets
+  const int wave_id = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
+  if (wave_id >= G::NW) {
+    // =================================================== producer waves
+    const int ts = threadIdx.x - G::NT, lane = ts & 63, wave = ts >> 6;
+    const int fb = ts % G::FB, rg = ts / G::FB;
+    const DT* qg = static_cast<const DT*>(a.q) + int64_t(bh) * a.T * D;
+    const DT* kg = static_cast<const DT*>(a.k) + int64_t(bh) * a.T * D;
+    const DT* vg = static_cast<const DT*>(a.v) + int64_t(bh) * a.T * D;
+    const float* dg = DECAY ? a.decay + int64_t(bh) * a.T : nullptr;
+    float zf[8];   // z of features 8 fb .. 8 fb + 7 before the chunk being staged
+    *reinterpret_cast<f32x4*>(zf) = *reinterpret_cast<const f32x4*>(zstart + 8 * fb);
+    *reinterpret_cast<f32x4*>(zf + 4) = *reinterpret_cast<const f32x4*>(zstart + 8 * fb + 4);
 
-  // start state of this segment
-  const float* S0 = a.S + int64_t(bh) * D * D;
-  const float* z0 = a.z + int64_t(bh) * D;
-  if (nseg > 1) {
-    S0 = a.ws_state + (int64_t(bh) * nseg + seg) * (D * D + D);
-    z0 = S0 + D * D;
-  }
-  f32x16 acc[G::MT];
-#pragma unroll
-  for (int mt = 0; mt < G::MT; ++mt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int f = 32 * mt + 8 * (r >> 2) + 4 * g + (r & 3);
-      acc[mt][r] = S0[f * D + 32 * wave + n];
-    }
-  if (tid < D) zl[tid] = z0[tid];
-  __syncthreads();
-
-  auto fetch = [&](RawChunk<G::RPT, G::ND, true>& r, int c) {
-    fetch_chunk<C, D, G::RPT, G::ND, true, DECAY>(r, qg, kg, vg, dg, c * C, a.T, rg, fb, lane);
-  };
-  auto step = [&](RawChunk<G::RPT, G::ND, true>& raw, int c) {
-    const int tok0 = c * C;
-    float lo = 0.f, hi = 0.f, ltot = 0.f;
-    if constexpr (DECAY != 0) chunk_logprefix<C, G::ND>(raw.d, lane, lo, hi, ltot);
-
-    // ---- [A] phi(q), phi(k) and w phi(k) high/low, v into the tiles;
-    //      inter-chunk denominators; z increments.  Rows past the end of
-    //      the sequence hold k = v = 0 (phi = 1, no contribution to S; their
-    //      1s are taken off z without decay) and their outputs are not stored.
-    {
-      float zf[8];
-      *reinterpret_cast<f32x4*>(zf) = *reinterpret_cast<const f32x4*>(zl + 8 * fb);
-      *reinterpret_cast<f32x4*>(zf + 4) = *reinterpret_cast<const f32x4*>(zl + 8 * fb + 4);
+    auto fetch = [&](RawChunk<G::RPT, G::ND, true>& r, int c) {
+      fetch_chunk<C, D, G::RPT, G::ND, true, DECAY>(r, qg, kg, vg, dg, c * C, a.T, rg, fb, lane);
+    };
+    // [A] chunk c into buf: phi(q), phi(k) and w phi(k) high/low, v tiles;
+    // the inter-chunk denominators e^{lc_t} phi(q_t).z; lc_t, beta_t; the
+    // per-wave z increments; the chunk's total log-decay.  Rows past the end
+    // of the sequence hold k = v = 0 (phi = 1, no contribution to S; their
+    // 1s are taken off z without decay) and their outputs are not stored.
+    // Past the segment's last chunk this stages a repeat of it into a buffer
+    // nobody reads, so that the loads are the same on every path.
+    auto stage = [&](RawChunk<G::RPT, G::ND, true>& raw, int c, char* buf) -> float {
+      const int tok0 = c * C;
+      clean_chunk<C, G::RPT, G::ND, true, DECAY>(raw, tok0, a.T, rg, lane);
+      float lo = 0.f, hi = 0.f, ltot = 0.f;
+      if constexpr (DECAY != 0) chunk_logprefix<C, G::ND>(raw.d, lane, lo, hi, ltot);
+      float* Ll = reinterpret_cast<float*>(buf + G::B_L);
+      float* Bl = reinterpret_cast<float*>(buf + G::B_B);
+      float* denl = reinterpret_cast<float*>(buf + G::B_DEN);
       float dz[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < G::RPT; ++i) {
@@ -584,9 +627,9 @@ __global__ __launch_bounds__(2 * D) void output_kernel(const PfArgs a) {
           kx[e] = elu1_fast(kx[e]);
           den = fmaf(qx[e], zf[e], den);
         }
-        row_write_perm<D>(smem + G::OFF_Q, r, fb, pack8(qx));
+        row_write_perm<D>(buf + G::B_Q, r, fb, pack8(qx));
         const u32x4 kp = pack8(kx);
-        row_write_perm<D>(smem + G::OFF_K, r, fb, kp);
+        row_write_perm<D>(buf + G::B_K, r, fb, kp);
         if constexpr (DECAY != 0) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
@@ -594,22 +637,22 @@ __global__ __launch_bounds__(2 * D) void output_kernel(const PfArgs a) {
             dz[e] += kx[e];
           }
           const u32x4 kh = pack8(kx);
-          blk_write<D>(smem + G::OFF_KH, perm_pos(r), fb, kh);
-          blk_write<D>(smem + G::OFF_KL, perm_pos(r), fb, low8(kx, kh));
+          blk_write<D>(buf + G::B_KH, perm_pos(r), fb, kh);
+          blk_write<D>(buf + G::B_KL, perm_pos(r), fb, low8(kx, kh));
         } else {
 #pragma unroll
           for (int e = 0; e < 8; ++e) dz[e] += kx[e];
-          blk_write<D>(smem + G::OFF_KH, perm_pos(r), fb, kp);
-          blk_write<D>(smem + G::OFF_KL, perm_pos(r), fb, low8(kx, kp));
+          blk_write<D>(buf + G::B_KH, perm_pos(r), fb, kp);
+          blk_write<D>(buf + G::B_KL, perm_pos(r), fb, low8(kx, kp));
         }
         if constexpr (VS) {
           float vx[8];
           unpack8(raw.v[i], vx, DT{});
           const u32x4 vh = pack8(vx);
-          blk_write<D>(smem + G::OFF_VH, perm_pos(r), fb, vh);
-          blk_write<D>(smem + G::OFF_VL, perm_pos(r), fb, low8(vx, vh));
+          blk_write<D>(buf + G::B_VH, perm_pos(r), fb, vh);
+          blk_write<D>(buf + G::B_VL, perm_pos(r), fb, low8(vx, vh));
         } else {
-          blk_write<D>(smem + G::OFF_VH, perm_pos(r), fb, raw.v[i]);
+          blk_write<D>(buf + G::B_VH, perm_pos(r), fb, raw.v[i]);
         }
 #pragma unroll
         for (int off = 1; off < G::FB; off <<= 1) den += __shfl_xor(den, off);
@@ -624,159 +667,227 @@ __global__ __launch_bounds__(2 * D) void output_kernel(const PfArgs a) {
       for (int e = 0; e < 8; ++e)
         for (int off = G::FB; off < 64; off <<= 1) dz[e] += __shfl_xor(dz[e], off);
       if (lane < G::FB) {
-        float* d = dzl + wave * D + 8 * fb;
+        float* d = reinterpret_cast<float*>(buf + G::B_DZ) + wave * D + 8 * fb;
         *reinterpret_cast<f32x4*>(d) = f32x4{dz[0], dz[1], dz[2], dz[3]};
         *reinterpret_cast<f32x4*>(d + 4) = f32x4{dz[4], dz[5], dz[6], dz[7]};
       }
-    }
-    __syncthreads();
-    // refill this register set with the chunk DEPTH ahead: its loads are in
-    // flight while this chunk and the next DEPTH - 1 are computed
-    if constexpr (G::DEPTH > 0) {
-      if (c + G::DEPTH < c1) fetch(raw, c + G::DEPTH);
-    }
+      if (ts == 0) *reinterpret_cast<float*>(buf + G::B_LT) = ltot;
+      // refill this register set with the chunk PDEPTH ahead (clamped)
+      fetch(raw, min(c + G::PDEPTH, c1 - 1));
+      return ltot;
+    };
+    // z after chunk c (staged in buf): zf = e^{ltot} zf + sum of the increments
+    auto zstep = [&](int c, const char* buf, float ltot) {
+      const float* dzl = reinterpret_cast<const float*>(buf + G::B_DZ);
+      const float gam = DECAY ? __expf(ltot) : 1.f;
+      const float pad = DECAY ? 0.f : float(max(c * C + C - a.T, 0));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float s = -pad;
+#pragma unroll
+        for (int w = 0; w < G::NW; ++w) s += dzl[w * D + 8 * fb + e];
+        zf[e] = fmaf(gam, zf[e], s);
+      }
+    };
 
-    // ---- [B] per wave: read-out of the carried state, masked intra-chunk
-    //      attention, normalise and store, then fold the chunk into S and z.
-    const float gam = DECAY ? __expf(ltot) : 1.f;
-    if (tid < D) {
-      float s = DECAY ? 0.f : -float(max(tok0 + C - a.T, 0));
+    RawChunk<G::RPT, G::ND, true> raw[G::PDEPTH];
 #pragma unroll
-      for (int w = 0; w < G::NW; ++w) s += dzl[w * D + tid];
-      zl[tid] = gam * zl[tid] + s;   // z of the next chunk; read again after the barrier
-    }
-    u32x4 vh[G::KT], vl[G::KT];
+    for (int j = 0; j < G::PDEPTH; ++j) fetch(raw[j], min(c0 + j, c1 - 1));
+    if constexpr (G::NBUF == 2) {
+      float lt = stage(raw[0], c0, buffer(0));
+      __syncthreads();
+      for (int i0 = 0; i0 < nc; i0 += G::PDEPTH) {
 #pragma unroll
-    for (int kk = 0; kk < G::KT; ++kk) {
-      vh[kk] = tr_operand<D>(smem + G::OFF_VH, 16 * kk, 32 * wave, lane);
-      if constexpr (VS) vl[kk] = tr_operand<D>(smem + G::OFF_VL, 16 * kk, 32 * wave, lane);
-    }
-
-#pragma unroll
-    for (int tb = 0; tb < G::TB; ++tb) {
-      const int tl = 32 * tb + n;   // this lane's query token within the chunk
-      u32x4 qf[G::KS];
-#pragma unroll
-      for (int ks = 0; ks < G::KS; ++ks) qf[ks] = row_operand<D>(smem + G::OFF_Q, tl, 2 * ks + g);
-      // read-out of the carried state, O^T = S^T phi(Q)^T: the fp32
-      // accumulators become bf16 operands (k = features) one k-step at a time
-      f32x16 o = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < G::KS; ++ks) {
-        const f32x16& sa = acc[ks >> 1];
-        const int j0 = 8 * (ks & 1);
-        const u32x4 sf = {pack_bf16(sa[j0 + 0], sa[j0 + 1]), pack_bf16(sa[j0 + 2], sa[j0 + 3]),
-                          pack_bf16(sa[j0 + 4], sa[j0 + 5]), pack_bf16(sa[j0 + 6], sa[j0 + 7])};
-        o = mfma(sf, qf[ks], o);
-      }
-      float lct = 0.f;
-      if constexpr (DECAY != 0) {
-        lct = Ll[tl];
-        o *= __expf(lct);
-      }
-      float dsum = 0.f;
-#pragma unroll
-      for (int sb = 0; sb <= tb; ++sb) {
-        f32x16 p = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < G::KS; ++ks)
-          p = mfma(row_operand<D>(smem + G::OFF_K, 32 * sb + n, 2 * ks + g), qf[ks], p);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int sl = 32 * sb + 8 * (r >> 2) + 4 * g + (r & 3);
-          float x = p[r];
-          if constexpr (DECAY != 0) x *= __expf(lct - Ll[sl]) * Bl[sl];
-          if (sb == tb && sl > tl) x = 0.f;
-          p[r] = x;
-          dsum += x;
-        }
-        // P = P_hi + P_lo (bf16 each): the P V product then carries the
-        // fp32 scores the denominator sums, to ~2^-16.
-        u32x4 ph0, pl0, ph1, pl1;
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          uint32_t a0, b0, a1, b1;
-          split_bf16(p[2 * h], p[2 * h + 1], a0, b0);
-          split_bf16(p[8 + 2 * h], p[8 + 2 * h + 1], a1, b1);
-          ph0[h] = a0; pl0[h] = b0; ph1[h] = a1; pl1[h] = b1;
-        }
-        o = mfma(vh[2 * sb], ph0, o);
-        o = mfma(vh[2 * sb], pl0, o);
-        o = mfma(vh[2 * sb + 1], ph1, o);
-        o = mfma(vh[2 * sb + 1], pl1, o);
-        if constexpr (VS) {
-          o = mfma(vl[2 * sb], ph0, o);
-          o = mfma(vl[2 * sb + 1], ph1, o);
+        for (int j = 0; j < G::PDEPTH; ++j) {
+          const int i = i0 + j;
+          if (i < nc) zstep(c0 + i, buffer(i), lt);   // zf: the normaliser after chunk c0 + i
+          lt = stage(raw[(j + 1) % G::PDEPTH], c0 + i + 1, buffer(i + 1));
+          if (i < nc) __syncthreads();
         }
       }
-      dsum += __shfl_xor(dsum, 32);
-      const float inv = __builtin_amdgcn_rcpf(denl[tl] + dsum + a.eps);
-      const int t = tok0 + tl;
-      if (t < a.T) {
-        const uint32_t orow = uint32_t(t) * D + 32 * wave + 4 * g;
-        if (a.out_f32) {
+    } else {
+      for (int i0 = 0; i0 < nc; i0 += G::PDEPTH) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            *reinterpret_cast<f32x4*>(ogf + orow + 8 * j) =
-                f32x4{o[4 * j] * inv, o[4 * j + 1] * inv, o[4 * j + 2] * inv, o[4 * j + 3] * inv};
-        } else {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float y0 = o[4 * j] * inv, y1 = o[4 * j + 1] * inv;
-            const float y2 = o[4 * j + 2] * inv, y3 = o[4 * j + 3] * inv;
-            u32x2 w;
-            if constexpr (__is_same(DT, bf16_t)) {
-              w = u32x2{pack_bf16(y0, y1), pack_bf16(y2, y3)};
-            } else {
-              typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-              w = u32x2{__builtin_bit_cast(uint32_t, h2{(f16_t)y0, (f16_t)y1}),
-                        __builtin_bit_cast(uint32_t, h2{(f16_t)y2, (f16_t)y3})};
-            }
-            *reinterpret_cast<u32x2*>(og + orow + 8 * j) = w;
+        for (int j = 0; j < G::PDEPTH; ++j) {
+          const int i = i0 + j;
+          const float lt = stage(raw[j], c0 + i, buffer(0));
+          if (i < nc) {
+            __syncthreads();
+            zstep(c0 + i, buffer(0), lt);
+            __syncthreads();
           }
         }
       }
     }
-
-    // fold this chunk into the carried state: w phi(k) as high + low parts
-#pragma unroll
-    for (int mt = 0; mt < G::MT; ++mt) {
-      if constexpr (DECAY != 0) acc[mt] *= gam;
-#pragma unroll
-      for (int kk = 0; kk < G::KT; ++kk) {
-        const u32x4 kh = tr_operand<D>(smem + G::OFF_KH, 16 * kk, 32 * mt, lane);
-        const u32x4 kl = tr_operand<D>(smem + G::OFF_KL, 16 * kk, 32 * mt, lane);
-        acc[mt] = mfma(kh, vh[kk], acc[mt]);
-        acc[mt] = mfma(kl, vh[kk], acc[mt]);
-        if constexpr (VS) acc[mt] = mfma(kh, vl[kk], acc[mt]);
-      }
+    if (last && rg == 0) {
+      float* zd = a.z + int64_t(bh) * D + 8 * fb;
+      *reinterpret_cast<f32x4*>(zd) = f32x4{zf[0], zf[1], zf[2], zf[3]};
+      *reinterpret_cast<f32x4*>(zd + 4) = f32x4{zf[4], zf[5], zf[6], zf[7]};
     }
-    __syncthreads();
-  };
-
-  RawChunk<G::RPT, G::ND, true> raw[G::RING];
-#pragma unroll
-  for (int j = 0; j < G::DEPTH; ++j)
-    if (c0 + j < c1) fetch(raw[j], c0 + j);
-  for (int c = c0; c < c1; c += G::RING) {
-#pragma unroll
-    for (int j = 0; j < G::RING; ++j)
-      if (c + j < c1) {
-        if constexpr (G::DEPTH == 0) fetch(raw[j], c + j);
-        step(raw[j], c + j);
-      }
-  }
-
-  if (seg == nseg - 1) {
-    float* Sd = a.S + int64_t(bh) * D * D;
+  } else {
+    // =================================================== consumer waves
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 5, n = lane & 31;
+    DT* og = static_cast<DT*>(a.out) + int64_t(bh) * a.T * D;
+    float* ogf = static_cast<float*>(a.out) + int64_t(bh) * a.T * D;
+    f32x16 acc[G::MT];
 #pragma unroll
     for (int mt = 0; mt < G::MT; ++mt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int f = 32 * mt + 8 * (r >> 2) + 4 * g + (r & 3);
-        Sd[f * D + 32 * wave + n] = acc[mt][r];
+        acc[mt][r] = Sstart[f * D + 32 * wave + n];
       }
-    if (tid < D) a.z[int64_t(bh) * D + tid] = zl[tid];
+
+    // [B] read-out of the carried state, masked intra-chunk attention,
+    // normalise and store, then fold the chunk into S.
+    auto compute = [&](int c, const char* buf) {
+      const int tok0 = c * C;
+      const float* Ll = reinterpret_cast<const float*>(buf + G::B_L);
+      const float* Bl = reinterpret_cast<const float*>(buf + G::B_B);
+      const float* denl = reinterpret_cast<const float*>(buf + G::B_DEN);
+      u32x4 vh[G::KT], vl[G::KT];
+#pragma unroll
+      for (int kk = 0; kk < G::KT; ++kk) {
+        vh[kk] = tr_operand<D>(buf + G::B_VH, 16 * kk, 32 * wave, lane);
+        if constexpr (VS) vl[kk] = tr_operand<D>(buf + G::B_VL, 16 * kk, 32 * wave, lane);
+      }
+#pragma unroll
+      for (int tb = 0; tb < G::TB; ++tb) {
+        const int tl = 32 * tb + n;   // this lane's query token within the chunk
+        // read-out of the carried state O^T = S^T phi(Q)^T (the fp32
+        // accumulators become bf16 operands, k = features) and the diagonal
+        // score block in one pass over the feature k-steps
+        f32x16 o = f32x16{}, p = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < G::KS; ++ks) {
+          const u32x4 qf = row_operand<D>(buf + G::B_Q, tl, 2 * ks + g);
+          const f32x16& sa = acc[ks >> 1];
+          const int j0 = 8 * (ks & 1);
+          const u32x4 sf = {pack_bf16(sa[j0 + 0], sa[j0 + 1]), pack_bf16(sa[j0 + 2], sa[j0 + 3]),
+                            pack_bf16(sa[j0 + 4], sa[j0 + 5]), pack_bf16(sa[j0 + 6], sa[j0 + 7])};
+          o = mfma(sf, qf, o);
+          p = mfma(row_operand<D>(buf + G::B_K, 32 * tb + n, 2 * ks + g), qf, p);
+        }
+        float lct = 0.f;
+        if constexpr (DECAY != 0) {
+          lct = Ll[tl];
+          o *= __expf(lct);
+        }
+        float dsum = 0.f;
+#pragma unroll
+        for (int sb = tb; sb >= 0; --sb) {
+          if (sb != tb) {
+            p = f32x16{};
+#pragma unroll
+            for (int ks = 0; ks < G::KS; ++ks)
+              p = mfma(row_operand<D>(buf + G::B_K, 32 * sb + n, 2 * ks + g),
+                       row_operand<D>(buf + G::B_Q, tl, 2 * ks + g), p);
+          }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int sl = 32 * sb + 8 * (r >> 2) + 4 * g + (r & 3);
+            float x = p[r];
+            if constexpr (DECAY != 0) x *= __expf(lct - Ll[sl]) * Bl[sl];
+            if (sb == tb && sl > tl) x = 0.f;
+            p[r] = x;
+            dsum += x;
+          }
+          // P = P_hi + P_lo (bf16 each): the P V product then carries the
+          // fp32 scores the denominator sums, to ~2^-16.
+          u32x4 ph0, pl0, ph1, pl1;
+#pragma unroll
+          for (int h = 0; h < 4; ++h) {
+            uint32_t a0, b0, a1, b1;
+            split_bf16(p[2 * h], p[2 * h + 1], a0, b0);
+            split_bf16(p[8 + 2 * h], p[8 + 2 * h + 1], a1, b1);
+            ph0[h] = a0; pl0[h] = b0; ph1[h] = a1; pl1[h] = b1;
+          }
+          o = mfma(vh[2 * sb], ph0, o);
+          o = mfma(vh[2 * sb], pl0, o);
+          o = mfma(vh[2 * sb + 1], ph1, o);
+          o = mfma(vh[2 * sb + 1], pl1, o);
+          if constexpr (VS) {
+            o = mfma(vl[2 * sb], ph0, o);
+            o = mfma(vl[2 * sb + 1], ph1, o);
+          }
+        }
+        dsum += __shfl_xor(dsum, 32);
+        const float inv = __builtin_amdgcn_rcpf(denl[tl] + dsum + a.eps);
+        const int t = tok0 + tl;
+        if (t < a.T) {
+          const uint32_t orow = uint32_t(t) * D + 32 * wave + 4 * g;
+          if (a.out_f32) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              *reinterpret_cast<f32x4*>(ogf + orow + 8 * j) =
+                  f32x4{o[4 * j] * inv, o[4 * j + 1] * inv, o[4 * j + 2] * inv, o[4 * j + 3] * inv};
+          } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float y0 = o[4 * j] * inv, y1 = o[4 * j + 1] * inv;
+              const float y2 = o[4 * j + 2] * inv, y3 = o[4 * j + 3] * inv;
+              u32x2 w;
+              if constexpr (__is_same(DT, bf16_t)) {
+                w = u32x2{pack_bf16(y0, y1), pack_bf16(y2, y3)};
+              } else {
+                typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+                w = u32x2{__builtin_bit_cast(uint32_t, h2{(f16_t)y0, (f16_t)y1}),
+                          __builtin_bit_cast(uint32_t, h2{(f16_t)y2, (f16_t)y3})};
+              }
+              *reinterpret_cast<u32x2*>(og + orow + 8 * j) = w;
+            }
+          }
+        }
+      }
+      // fold this chunk into the carried state: w phi(k) as high + low parts
+      // (kept apart from the read-out so that its operand loads do not add
+      // to the read-out's register pressure)
+      __builtin_amdgcn_sched_barrier(0);
+      const float gam = DECAY ? __expf(*reinterpret_cast<const float*>(buf + G::B_LT)) : 1.f;
+#pragma unroll
+      for (int mt = 0; mt < G::MT; ++mt) {
+        if constexpr (DECAY != 0) acc[mt] *= gam;
+#pragma unroll
+        for (int kk = 0; kk < G::KT; ++kk) {
+          const u32x4 kh = tr_operand<D>(buf + G::B_KH, 16 * kk, 32 * mt, lane);
+          const u32x4 kl = tr_operand<D>(buf + G::B_KL, 16 * kk, 32 * mt, lane);
+          acc[mt] = mfma(kh, vh[kk], acc[mt]);
+          acc[mt] = mfma(kl, vh[kk], acc[mt]);
+          if constexpr (VS) acc[mt] = mfma(kh, vl[kk], acc[mt]);
+        }
+      }
+    };
+
+    if constexpr (G::NBUF == 2) {
+      __syncthreads();   // the producers' first chunk
+      for (int i0 = 0; i0 < nc; i0 += 2) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int i = i0 + j;
+          if (i < nc) {
+            compute(c0 + i, smem + j * G::BUF3);
+            __syncthreads();
+          }
+        }
+      }
+    } else {
+      for (int i = 0; i < nc; ++i) {
+        __syncthreads();   // chunk c0 + i staged
+        compute(c0 + i, smem);
+        __syncthreads();
+      }
+    }
+    if (last) {
+      float* Sd = a.S + int64_t(bh) * D * D;
+#pragma unroll
+      for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int f = 32 * mt + 8 * (r >> 2) + 4 * g + (r & 3);
+          Sd[f * D + 32 * wave + n] = acc[mt][r];
+        }
+    }
   }
 }
 
@@ -793,7 +904,7 @@ hipError_t launch3(const PfArgs& a, int64_t BH, int stage, hipStream_t st) {
     const int per_bh = (D * D + D + 255) / 256;
     segment_scan_kernel<D><<<dim3(unsigned(BH * per_bh)), dim3(256), 0, st>>>(a);
   } else {
-    output_kernel<D, C, DECAY, DT><<<dim3(unsigned(BH * a.nseg)), dim3(G::NT), 0, st>>>(a);
+    output_kernel<D, C, DECAY, DT><<<dim3(unsigned(BH * a.nseg)), dim3(2 * G::NT), 0, st>>>(a);
   }
   return hipGetLastError();
 }
