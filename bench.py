@@ -1,6 +1,6 @@
 """Benchmark of the causal linear attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W]
+    python bench.py [--gpus 1] [--steps K] [--warmup W]      (defaults K = 200, W = 50)
 
 A step is one causal elu+1 prefill over the long-context workload
 (B=1, H=8, T=102400, d_h = d' = d_v = 128, bf16 q, k, v ~ N(0, 1)/sqrt(2),
@@ -9,7 +9,9 @@ chunking, intra-chunk MFMA contraction, chunk-local state contribution,
 segment scan, inter-chunk read-out and normalisation).  Inputs are generated
 on the device before timing.  W untimed warm-up steps are followed by exactly
 K timed steps between two synchronisations, with HIP events on the stream the
-library launches on.
+library launches on.  The step time settles only after a few milliseconds of
+back-to-back work (the clocks first dip, then recover), hence the defaults
+of 50 warm-up and 200 timed steps (about 0.1 s of GPU time).
 
 Printed as one JSON line:
   value        tokens/s (B*T tokens per step) over the K steps;
@@ -138,19 +140,20 @@ def bench_prefill(torch, la, I, steps, warmup):
     wall = time.perf_counter() - t0
     ms = e0.elapsed_time(e1) / steps
 
-    # per-stage durations: the same calls, with events between the stages
+    # per-stage durations: the same calls back to back (no synchronisation
+    # between repetitions, so the clocks stay where the timed steps had them),
+    # with events between the stages
     reps = max(steps, 5)
-    stage_ms = [0.0, 0.0, 0.0]
-    for _ in range(reps):
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps)]
+    for r in range(reps):
         L.la_state_init(dref, ptr(S), ptr(z), stream)
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-        evs[0].record()
+        evs[r][0].record()
         for s in (1, 2, 3):
             la._lib.check(L.la_prefill_stage(dref, s, *args, ptr(ws), nws, stream))
-            evs[s].record()
-        torch.cuda.synchronize()
-        for s in range(3):
-            stage_ms[s] += evs[s].elapsed_time(evs[s + 1]) / reps
+            evs[r][s].record()
+    torch.cuda.synchronize()
+    stage_ms = [sum(evs[r][s].elapsed_time(evs[r][s + 1]) for r in range(reps)) / reps
+                for s in range(3)]
     return dict(ms=ms, wall=wall, stage_ms=stage_ms, chunk=chunk, segments=segments)
 
 
@@ -204,8 +207,8 @@ def bench_decode(torch, la, I, N, steps, warmup=8):
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--cpu-tokens", type=int, default=102400,
                     help="tokens per head in the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")

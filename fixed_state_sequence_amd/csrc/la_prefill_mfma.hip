@@ -248,11 +248,19 @@ struct PfArgs {
   float* S;          // caller's state [BH, D, D] (initial in, final out)
   float* z;          // caller's normaliser [BH, D]
   const float* decay;  // [BH, T] or null
-  float* ws_state;   // [BH, nseg, D*D + D]
-  float* ws_logg;    // [BH, nseg]
+  // Workspace, per (b, h), NSLOT = nsub (nseg - 1) + 1 slots of D*D + D
+  // floats: stage 1 writes sub-segment u's state into slot u (the segments
+  // before the last are each cut into nsub sub-segments, so that stage 1 has
+  // enough workgroups); the scan turns slot nsub s into the start state of
+  // segment s.
+  float* ws_state;   // [BH, NSLOT, D*D + D]
+  float* ws_logg;    // [BH, NSLOT]: log Gamma of each sub-segment
   int T;
   int nseg;
   int cps;           // chunks per segment
+  int nsub;          // stage-1 sub-segments per segment
+  int cps_sub;       // chunks per sub-segment (the last one of a segment may be shorter)
+  int nslot;         // nsub (nseg - 1) + 1
   int out_f32;       // out is fp32 (else the input type)
   float eps;
 };
@@ -362,14 +370,14 @@ __global__ __launch_bounds__(2 * D) void segment_state_kernel(const PfArgs a) {
   constexpr bool VS = __is_same(DT, f16_t);   // fp16 v needs a bf16 low part too
   using G = Cfg<D, C, VS>;
   __shared__ __align__(16) char smem[G::S1_LDS];
-  const int nseg = a.nseg;
-  const int bh = blockIdx.x / (nseg - 1);
-  const int seg = blockIdx.x % (nseg - 1);
+  const int bh = blockIdx.x / (a.nslot - 1);
+  const int u = blockIdx.x % (a.nslot - 1);   // sub-segment: segment u / nsub, part u % nsub
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int fb = tid % G::FB, rg = tid / G::FB;
   const int nchunks = (a.T + C - 1) / C;
-  const int c0 = seg * a.cps;
-  const int c1 = min(c0 + a.cps, nchunks);
+  const int seg_first = (u / a.nsub) * a.cps;
+  const int c0 = seg_first + (u % a.nsub) * a.cps_sub;
+  const int c1 = min(min(c0 + a.cps_sub, seg_first + a.cps), nchunks);
 
   const DT* kg = static_cast<const DT*>(a.k) + int64_t(bh) * a.T * D;
   const DT* vg = static_cast<const DT*>(a.v) + int64_t(bh) * a.T * D;
@@ -495,7 +503,7 @@ __global__ __launch_bounds__(2 * D) void segment_state_kernel(const PfArgs a) {
 
   // write the segment state: S row-major [f][v], then z, then log Gamma
   const int g = lane >> 5, n = lane & 31;
-  float* dst = a.ws_state + (int64_t(bh) * nseg + seg) * (D * D + D);
+  float* dst = a.ws_state + (int64_t(bh) * a.nslot + u) * (D * D + D);
 #pragma unroll
   for (int mt = 0; mt < G::MT; ++mt)
 #pragma unroll
@@ -507,39 +515,47 @@ __global__ __launch_bounds__(2 * D) void segment_state_kernel(const PfArgs a) {
     *reinterpret_cast<f32x4*>(dst + D * D + 8 * fb) = f32x4{zf[0], zf[1], zf[2], zf[3]};
     *reinterpret_cast<f32x4*>(dst + D * D + 8 * fb + 4) = f32x4{zf[4], zf[5], zf[6], zf[7]};
   }
-  if (tid == 0) a.ws_logg[int64_t(bh) * nseg + seg] = lsuf;
+  if (tid == 0) a.ws_logg[int64_t(bh) * a.nslot + u] = lsuf;
 }
 
 // ---------------------------------------------------------------- stage 2
 
-// Exclusive scan of the segment states of one (b, h), one state element per
-// thread: the start state of segment s is Gamma_{s-1} (... (Gamma_0 S_init +
-// S_0) ...) + S_{s-1}.  Segment values are loaded 16 at a time, all in flight
-// together, then folded in order.
-template <int D>
+// Exclusive scan of the sub-segment states of one (b, h), one state element
+// per thread: carry = Gamma_u carry + S_u over the slots in order, starting
+// from the caller's initial state, and the carry before slot nsub s is the
+// start state of segment s, written in place.  Slot values are loaded U at a
+// time (all of them, for up to U slots), all in flight together, then folded
+// in order.
+template <int D, int U>
 __global__ __launch_bounds__(256) void segment_scan_kernel(const PfArgs a) {
   constexpr int E = D * D + D;
-  constexpr int U = 16;
   const int per_bh = (E + 255) / 256;
   const int bh = blockIdx.x / per_bh;
   const int e = (blockIdx.x % per_bh) * 256 + threadIdx.x;
   if (e >= E) return;
   float carry = e < D * D ? a.S[int64_t(bh) * D * D + e] : a.z[int64_t(bh) * D + (e - D * D)];
-  float* base = a.ws_state + int64_t(bh) * a.nseg * E + e;
-  const float* lg = a.ws_logg + int64_t(bh) * a.nseg;
-  for (int s0 = 0; s0 < a.nseg; s0 += U) {
+  float* base = a.ws_state + int64_t(bh) * a.nslot * E + e;
+  const float* lg = a.ws_logg + int64_t(bh) * a.nslot;
+  for (int s0 = 0; s0 < a.nslot; s0 += U) {
     float x[U], gm[U];
+    // unconditional loads (slot index clamped), so that all are in flight
+    // together; the last slot only receives a start state
 #pragma unroll
     for (int j = 0; j < U; ++j) {
-      const int s = s0 + j;
-      const bool in = s + 1 < a.nseg;   // the last segment's own state is never needed
-      x[j] = in ? base[int64_t(s) * E] : 0.f;
-      gm[j] = in ? __expf(lg[s]) : 0.f;
+      const int uc = min(s0 + j, a.nslot - 2);
+      x[j] = base[int64_t(uc) * E];
+      gm[j] = lg[uc];
     }
 #pragma unroll
     for (int j = 0; j < U; ++j) {
-      const int s = s0 + j;
-      if (s < a.nseg) base[int64_t(s) * E] = carry;
+      const bool in = s0 + j + 1 < a.nslot;
+      x[j] = in ? x[j] : 0.f;
+      gm[j] = in ? __expf(gm[j]) : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int u = s0 + j;
+      if (u < a.nslot && u % a.nsub == 0) base[int64_t(u) * E] = carry;
       carry = gm[j] * carry + x[j];
     }
   }
@@ -568,7 +584,7 @@ void output_kernel(const PfArgs a) {
   const int c1 = min(c0 + a.cps, nchunks);
   const int nc = c1 - c0;
   const bool last = seg == nseg - 1;
-  const float* Sstart = nseg > 1 ? a.ws_state + (int64_t(bh) * nseg + seg) * (D * D + D)
+  const float* Sstart = nseg > 1 ? a.ws_state + (int64_t(bh) * a.nslot + a.nsub * seg) * (D * D + D)
                                  : a.S + int64_t(bh) * D * D;
   const float* zstart = nseg > 1 ? Sstart + D * D : a.z + int64_t(bh) * D;
   auto buffer = [&](int i) -> char* { return smem + (G::NBUF == 2 ? (i & 1) * G::BUF3 : 0); };
@@ -898,11 +914,14 @@ hipError_t launch3(const PfArgs& a, int64_t BH, int stage, hipStream_t st) {
   using G = Cfg<D, C, __is_same(DT, f16_t)>;
   if (stage == 1) {
     if (a.nseg <= 1) return hipSuccess;
-    segment_state_kernel<D, C, DECAY, DT><<<dim3(unsigned(BH * (a.nseg - 1))), dim3(G::NT), 0, st>>>(a);
+    segment_state_kernel<D, C, DECAY, DT><<<dim3(unsigned(BH * (a.nslot - 1))), dim3(G::NT), 0, st>>>(a);
   } else if (stage == 2) {
     if (a.nseg <= 1) return hipSuccess;
     const int per_bh = (D * D + D + 255) / 256;
-    segment_scan_kernel<D><<<dim3(unsigned(BH * per_bh)), dim3(256), 0, st>>>(a);
+    if (a.nslot <= 32)
+      segment_scan_kernel<D, 32><<<dim3(unsigned(BH * per_bh)), dim3(256), 0, st>>>(a);
+    else
+      segment_scan_kernel<D, 64><<<dim3(unsigned(BH * per_bh)), dim3(256), 0, st>>>(a);
   } else {
     output_kernel<D, C, DECAY, DT><<<dim3(unsigned(BH * a.nseg)), dim3(2 * G::NT), 0, st>>>(a);
   }
@@ -932,9 +951,22 @@ hipError_t launch_chunk(const PfArgs& a, int64_t BH, int chunk, la_decay kind, i
   return hipErrorInvalidValue;
 }
 
-int chunks_per_segment(const Problem& p) {
+// Chunk bookkeeping of a plan: chunks per segment, segment count, stage-1
+// sub-segments per segment (two when a segment has at least two chunks, so
+// that stage 1 runs two workgroups per compute unit) and workspace slots.
+struct Split {
+  int cps, nseg, nsub, cps_sub, nslot;
+};
+
+Split split_of(const Problem& p) {
+  Split q;
   const int nchunks = (p.T + p.chunk - 1) / p.chunk;
-  return (nchunks + p.segments - 1) / p.segments;
+  q.cps = (nchunks + p.segments - 1) / p.segments;
+  q.nseg = q.cps > 0 ? (nchunks + q.cps - 1) / q.cps : 1;
+  q.nsub = q.cps >= 2 ? 2 : 1;
+  q.cps_sub = (q.cps + q.nsub - 1) / q.nsub;
+  q.nslot = q.nsub * (q.nseg - 1) + 1;
+  return q;
 }
 
 }  // namespace
@@ -947,8 +979,8 @@ bool mfma_supported(const Problem& p) {
 // Chunks whose stage-3 tiles fit in the 160 KB of LDS of one compute unit.
 bool mfma_chunk_fits(int d, int chunk) { return chunk <= 64 || d <= 64; }
 
-// The output stage holds one 4-wave workgroup per compute unit at d = 128
-// (two 2-wave ones at d = 64): aim for exactly that many workgroups on the
+// The output stage holds one 8-wave workgroup per compute unit at d = 128
+// (two 4-wave ones at d = 64): aim for exactly that many workgroups on the
 // 256 compute units, with at least two chunks per segment.
 int mfma_default_segments(const Problem& p) {
   const int64_t target_wg = p.dv == 128 ? 256 : 512;
@@ -966,7 +998,7 @@ int mfma_default_segments(const Problem& p) {
 size_t mfma_workspace_bytes(const Problem& p) {
   if (p.path != 1 || p.segments <= 1) return 0;
   const size_t E = size_t(p.dv) * p.dv + p.dv;
-  const size_t n = size_t(p.BH()) * p.segments;
+  const size_t n = size_t(p.BH()) * split_of(p).nslot;
   return n * E * sizeof(float) + ((n * sizeof(float) + 255) / 256) * 256;
 }
 
@@ -976,9 +1008,12 @@ hipError_t launch_mfma_stage(const Problem& p, int stage, const void* q, const v
   PfArgs a;
   a.q = q; a.k = k; a.v = v; a.out = out; a.S = S; a.z = z; a.decay = p.decay;
   a.T = p.T;
-  a.cps = chunks_per_segment(p);
-  const int nchunks = (p.T + p.chunk - 1) / p.chunk;
-  a.nseg = (nchunks + a.cps - 1) / a.cps;
+  const Split sp = split_of(p);
+  a.cps = sp.cps;
+  a.nseg = sp.nseg;
+  a.nsub = sp.nsub;
+  a.cps_sub = sp.cps_sub;
+  a.nslot = sp.nslot;
   a.eps = p.eps;
   a.out_f32 = p.out_dtype == LA_F32 ? 1 : 0;
   a.ws_logg = nullptr;
@@ -986,7 +1021,7 @@ hipError_t launch_mfma_stage(const Problem& p, int stage, const void* q, const v
   if (a.nseg > 1) {
     const size_t E = size_t(p.dv) * p.dv + p.dv;
     a.ws_state = static_cast<float*>(ws);
-    a.ws_logg = a.ws_state + size_t(p.BH()) * a.nseg * E;
+    a.ws_logg = a.ws_state + size_t(p.BH()) * a.nslot * E;
   }
   if (p.dv == 128) {
     return p.dtype == LA_BF16 ? launch_chunk<128, bf16_t>(a, p.BH(), p.chunk, p.decay_kind, stage, stream)

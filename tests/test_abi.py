@@ -47,8 +47,10 @@ def test_plan_for_the_measured_prefills():
     # long context: chunked MFMA path, segments spread 8 heads over the chip
     c, s, p = la.prefill_plan(desc())
     assert (c, s, p) == (32, 32, 1)    # one workgroup per compute unit: 8 heads x 32 segments
-    assert la.prefill_workspace_size(desc()) == 8 * s * (128 * 128 + 128) * 4 + (
-        (8 * s * 4 + 255) // 256) * 256
+    # stage 1 cuts each of the first 31 segments in two: 2 * 31 + 1 state slots per head
+    slots = 2 * (s - 1) + 1
+    assert la.prefill_workspace_size(desc()) == 8 * slots * (128 * 128 + 128) * 4 + (
+        (8 * slots * 4 + 255) // 256) * 256
     # fp32 inputs take the per-token kernel; no workspace
     d = desc(T=8, d_h=4, d_v=4, dtype_code=_lib.LA_F32)
     assert la.prefill_plan(d)[2] == 0 and la.prefill_workspace_size(d) == 0
