@@ -157,7 +157,27 @@ def bench_prefill(torch, la, I, steps, warmup):
     return dict(ms=ms, wall=wall, stage_ms=stage_ms, chunk=chunk, segments=segments)
 
 
-def bench_decode(torch, la, I, N, steps, warmup=8):
+def hbm_copy(torch, nbytes=1 << 30, reps=10):
+    """Device-to-device copy of `nbytes` (read + write): the achievable HBM
+    bandwidth this box shows for plain streaming, as a reference beside the
+    8 TB/s spec (also the known-size kernel the traffic counters are scaled by)."""
+    dev = torch.device("cuda:0")
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = _events(torch)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    return dict(bytes=2 * nbytes, ms=ms, gbs=2 * nbytes / (ms * 1e-3) / 1e9)
+
+
+def bench_decode(torch, la, I, N, steps, warmup=64):
     """`steps` one-token steps for N sequences; inputs for every step are made
     on the device beforehand.  Returns ms per step."""
     dev = torch.device("cuda:0")
@@ -248,6 +268,7 @@ def main(argv=None):
     tflops = flops / (pf["ms"] * 1e-3) / 1e12
     step_bytes = TH * 4 * d * 2 + 2 * state_bytes
 
+    cp = hbm_copy(torch)
     dec = dec_big = None
     if not a.no_decode:
         print(f"[bench] decode {DEC['N']} x {DEC['H']}, {DEC['steps']} steps", file=sys.stderr,
@@ -276,7 +297,8 @@ def main(argv=None):
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
                      "kernel": "output_kernel (la_prefill stage 3)",
-                     "kernel_ms": s3, "algorithmic_bytes": stage3_bytes},
+                     "kernel_ms": s3, "algorithmic_bytes": stage3_bytes,
+                     "measured_copy_GBs": cp["gbs"], "frac_of_copy": achieved / cp["gbs"]},
         "step": {"stage_ms": pf["stage_ms"], "algorithmic_bytes": step_bytes,
                  "GBs": step_bytes / (pf["ms"] * 1e-3) / 1e9,
                  "hbm_frac": step_bytes / (pf["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS},
@@ -291,6 +313,7 @@ def main(argv=None):
             "ms_per_step": dec["ms_per_step"], "bytes_per_step": dec["bytes_per_step"],
             "achieved": dec["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": dec["gbs"] / HBM_PEAK_GBS, "state_MB": dec["state_mb"],
+            "frac_of_copy": dec["gbs"] / cp["gbs"],
             "note": "state fits the 256 MB last-level cache",
             "large": {"sequences": 1024, "steps": 256, "ms_per_step": dec_big["ms_per_step"],
                       "achieved": dec_big["gbs"], "frac": dec_big["gbs"] / HBM_PEAK_GBS,

@@ -56,6 +56,17 @@ struct DecCfg {
 
 __device__ __forceinline__ float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
 
+// The state is read and written exactly once per step: stream it past the
+// caches (nontemporal loads and stores).
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 ld4_stream(const float* p) {
+  const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
+  return make_float4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void st4_stream(float* p, const float4& v) {
+  __builtin_nontemporal_store(f32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<f32x4_t*>(p));
+}
+
 // DHMAX bounds the q, k width held in LDS (d_h <= 128 for RFF, d' for elu+1).
 template <typename DT, int DV, int DP, bool RFF, int DECAY>
 __global__ __launch_bounds__(NT) void decode_kernel(const DecArgs a) {
@@ -81,7 +92,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(const DecArgs a) {
   float4 s[G::NI];
 #pragma unroll
   for (int i = 0; i < G::NI; ++i)
-    s[i] = valid ? ld4(Sg + (row0 + i) * DV + 4 * cg) : make_float4(0.f, 0.f, 0.f, 0.f);
+    s[i] = ld4_stream(Sg + (row0 + i) * DV + 4 * cg);   // st points at a real state even if !valid
   float* zg = a.z + st * DP;
   float zr[G::ZPL];
 #pragma unroll
@@ -189,7 +200,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(const DecArgs a) {
   }
   if (valid) {
 #pragma unroll
-    for (int i = 0; i < G::NI; ++i) *reinterpret_cast<float4*>(Sg + (row0 + i) * DV + 4 * cg) = s[i];
+    for (int i = 0; i < G::NI; ++i) st4_stream(Sg + (row0 + i) * DV + 4 * cg, s[i]);
   }
   float den = 0.f;
 #pragma unroll

@@ -16,12 +16,13 @@
 // remains.
 //
 // Parallel schedule.  Each (b, h) sequence is cut into `segments` runs of
-// whole chunks.  Stage 1: one workgroup per segment (except the last) folds
-// its chunks into a segment state (S_seg, z_seg, log Gamma_seg).  Stage 2:
-// per element of the state, an exclusive scan over segments turns those into
-// each segment's start state, folding in the caller's initial state.  Stage 3:
-// one workgroup per segment walks its chunks again from its start state and
-// writes the outputs; the last segment writes the final state.
+// whole chunks.  Stage 1: one workgroup per sub-segment (half a segment)
+// folds its chunks into a sub-segment state (S_u, z_u, log Gamma_u).  Stage 2:
+// per element of the state, a scan over the sub-segments, starting from the
+// caller's initial state, gives each segment's start state and the final
+// state.  Stage 3: one workgroup per segment walks its chunks again from its
+// start state and writes the outputs (with a single segment, stages 1 and 2
+// are skipped and stage 3 writes the final state).
 //
 // Work split inside a workgroup (D = d' = d_v, NW = D / 32 waves): wave w owns
 // value columns [32 w, 32 w + 32) of the state.  All MFMAs are
@@ -248,11 +249,11 @@ struct PfArgs {
   float* S;          // caller's state [BH, D, D] (initial in, final out)
   float* z;          // caller's normaliser [BH, D]
   const float* decay;  // [BH, T] or null
-  // Workspace, per (b, h), NSLOT = nsub (nseg - 1) + 1 slots of D*D + D
-  // floats: stage 1 writes sub-segment u's state into slot u (the segments
-  // before the last are each cut into nsub sub-segments, so that stage 1 has
-  // enough workgroups); the scan turns slot nsub s into the start state of
-  // segment s.
+  // Workspace, per (b, h), NSLOT = nsub nseg slots of D*D + D floats (with
+  // more than one segment): stage 1 writes sub-segment u's state into slot u
+  // (each segment is cut into nsub sub-segments, so that stage 1 has enough
+  // workgroups); the scan turns slot nsub s into the start state of segment s
+  // and writes the final state, carried past the last slot, into (S, z).
   float* ws_state;   // [BH, NSLOT, D*D + D]
   float* ws_logg;    // [BH, NSLOT]: log Gamma of each sub-segment
   int T;
@@ -260,7 +261,7 @@ struct PfArgs {
   int cps;           // chunks per segment
   int nsub;          // stage-1 sub-segments per segment
   int cps_sub;       // chunks per sub-segment (the last one of a segment may be shorter)
-  int nslot;         // nsub (nseg - 1) + 1
+  int nslot;         // nsub nseg
   int out_f32;       // out is fp32 (else the input type)
   float eps;
 };
@@ -357,6 +358,48 @@ __device__ __forceinline__ float lane_value(float lo, float hi, int r) {
   }
 }
 
+// Cross-lane sums without LDS traffic.  row_sum<FB>: sum over each aligned
+// group of FB (8 or 16) lanes, in every lane of the group (DPP quad
+// permutes and row mirrors).  group_sum<FB>: sum over the lanes that share
+// lane % FB (DPP rotate within a row for FB = 8, then the gfx950 row and
+// half-wave swaps), in every such lane.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
+                                                               0xF, 0xF, false));
+}
+// The swaps return both registers as a two-element vector.  Its elements are
+// read through one 64-bit cast: at -O3 this compiler folds a subscript of the
+// second element into the first.
+template <class V>
+__device__ __forceinline__ float pair_sum(const V& r) {
+  const unsigned long long u = __builtin_bit_cast(unsigned long long, r);
+  return __builtin_bit_cast(float, unsigned(u)) + __builtin_bit_cast(float, unsigned(u >> 32));
+}
+__device__ __forceinline__ float swap_sum16(float x) {   // x[l] + x[l ^ 16]
+  const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, x),
+                                                  __builtin_bit_cast(unsigned, x), false, false);
+  return pair_sum(r);
+}
+__device__ __forceinline__ float swap_sum32(float x) {   // x[l] + x[l ^ 32]
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
+                                                  __builtin_bit_cast(unsigned, x), false, false);
+  return pair_sum(r);
+}
+template <int FB>
+__device__ __forceinline__ float row_sum(float x) {
+  x += dpp<0xB1>(x);     // quad_perm [1, 0, 3, 2]
+  x += dpp<0x4E>(x);     // quad_perm [2, 3, 0, 1]
+  x += dpp<0x141>(x);    // row_half_mirror
+  if constexpr (FB == 16) x += dpp<0x140>(x);   // row_mirror
+  return x;
+}
+template <int FB>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (FB == 8) x += dpp<0x128>(x);     // row_ror:8
+  return swap_sum32(swap_sum16(x));
+}
+
 // ---------------------------------------------------------------- stage 1
 
 // Segment state: S_seg = sum_s w_s phi(k_s) v_s^T over the segment's tokens
@@ -370,8 +413,8 @@ __global__ __launch_bounds__(2 * D) void segment_state_kernel(const PfArgs a) {
   constexpr bool VS = __is_same(DT, f16_t);   // fp16 v needs a bf16 low part too
   using G = Cfg<D, C, VS>;
   __shared__ __align__(16) char smem[G::S1_LDS];
-  const int bh = blockIdx.x / (a.nslot - 1);
-  const int u = blockIdx.x % (a.nslot - 1);   // sub-segment: segment u / nsub, part u % nsub
+  const int bh = blockIdx.x / a.nslot;
+  const int u = blockIdx.x % a.nslot;   // sub-segment: segment u / nsub, part u % nsub
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int fb = tid % G::FB, rg = tid / G::FB;
   const int nchunks = (a.T + C - 1) / C;
@@ -433,8 +476,7 @@ __global__ __launch_bounds__(2 * D) void segment_state_kernel(const PfArgs a) {
       }
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      for (int off = G::FB; off < 64; off <<= 1) dz[e] += __shfl_xor(dz[e], off);
+    for (int e = 0; e < 8; ++e) dz[e] = group_sum<G::FB>(dz[e]);
     if (lane < G::FB) {
       float* d = reinterpret_cast<float*>(buf + G::S1_DZ) + wave * D + 8 * fb;
       *reinterpret_cast<f32x4*>(d) = f32x4{dz[0], dz[1], dz[2], dz[3]};
@@ -522,10 +564,11 @@ __global__ __launch_bounds__(2 * D) void segment_state_kernel(const PfArgs a) {
 
 // Exclusive scan of the sub-segment states of one (b, h), one state element
 // per thread: carry = Gamma_u carry + S_u over the slots in order, starting
-// from the caller's initial state, and the carry before slot nsub s is the
-// start state of segment s, written in place.  Slot values are loaded U at a
-// time (all of them, for up to U slots), all in flight together, then folded
-// in order.
+// from the caller's initial state; the carry before slot nsub s is the start
+// state of segment s (written in place) and the carry after the last slot is
+// the final state (written over the initial one).  Slot values are loaded U
+// at a time (all of them, for up to U slots), all in flight together, then
+// folded in order.
 template <int D, int U>
 __global__ __launch_bounds__(256) void segment_scan_kernel(const PfArgs a) {
   constexpr int E = D * D + D;
@@ -533,32 +576,30 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(const PfArgs a) {
   const int bh = blockIdx.x / per_bh;
   const int e = (blockIdx.x % per_bh) * 256 + threadIdx.x;
   if (e >= E) return;
-  float carry = e < D * D ? a.S[int64_t(bh) * D * D + e] : a.z[int64_t(bh) * D + (e - D * D)];
+  float* init = e < D * D ? a.S + int64_t(bh) * D * D + e : a.z + int64_t(bh) * D + (e - D * D);
+  float carry = *init;
   float* base = a.ws_state + int64_t(bh) * a.nslot * E + e;
   const float* lg = a.ws_logg + int64_t(bh) * a.nslot;
   for (int s0 = 0; s0 < a.nslot; s0 += U) {
     float x[U], gm[U];
     // unconditional loads (slot index clamped), so that all are in flight
-    // together; the last slot only receives a start state
+    // together
 #pragma unroll
     for (int j = 0; j < U; ++j) {
-      const int uc = min(s0 + j, a.nslot - 2);
+      const int uc = min(s0 + j, a.nslot - 1);
       x[j] = base[int64_t(uc) * E];
       gm[j] = lg[uc];
     }
 #pragma unroll
     for (int j = 0; j < U; ++j) {
-      const bool in = s0 + j + 1 < a.nslot;
-      x[j] = in ? x[j] : 0.f;
-      gm[j] = in ? __expf(gm[j]) : 0.f;
-    }
-#pragma unroll
-    for (int j = 0; j < U; ++j) {
       const int u = s0 + j;
-      if (u < a.nslot && u % a.nsub == 0) base[int64_t(u) * E] = carry;
-      carry = gm[j] * carry + x[j];
+      if (u < a.nslot) {
+        if (u % a.nsub == 0) base[int64_t(u) * E] = carry;
+        carry = fmaf(__expf(gm[j]), carry, x[j]);
+      }
     }
   }
+  *init = carry;
 }
 
 // ---------------------------------------------------------------- stage 3
@@ -583,7 +624,11 @@ void output_kernel(const PfArgs a) {
   const int c0 = seg * a.cps;
   const int c1 = min(c0 + a.cps, nchunks);
   const int nc = c1 - c0;
-  const bool last = seg == nseg - 1;
+  // With several segments the final state comes from stage 1 and the scan
+  // (which fold w phi(k) as bf16 high + low parts); the output stage then
+  // folds only the high parts, as its state feeds this segment's outputs
+  // alone.  A single segment folds both parts and writes the final state.
+  const bool fin = nseg == 1;
   const float* Sstart = nseg > 1 ? a.ws_state + (int64_t(bh) * a.nslot + a.nsub * seg) * (D * D + D)
                                  : a.S + int64_t(bh) * D * D;
   const float* zstart = nseg > 1 ? Sstart + D * D : a.z + int64_t(bh) * D;
@@ -654,12 +699,12 @@ void output_kernel(const PfArgs a) {
           }
           const u32x4 kh = pack8(kx);
           blk_write<D>(buf + G::B_KH, perm_pos(r), fb, kh);
-          blk_write<D>(buf + G::B_KL, perm_pos(r), fb, low8(kx, kh));
+          if (fin) blk_write<D>(buf + G::B_KL, perm_pos(r), fb, low8(kx, kh));
         } else {
 #pragma unroll
           for (int e = 0; e < 8; ++e) dz[e] += kx[e];
           blk_write<D>(buf + G::B_KH, perm_pos(r), fb, kp);
-          blk_write<D>(buf + G::B_KL, perm_pos(r), fb, low8(kx, kp));
+          if (fin) blk_write<D>(buf + G::B_KL, perm_pos(r), fb, low8(kx, kp));
         }
         if constexpr (VS) {
           float vx[8];
@@ -670,8 +715,7 @@ void output_kernel(const PfArgs a) {
         } else {
           blk_write<D>(buf + G::B_VH, perm_pos(r), fb, raw.v[i]);
         }
-#pragma unroll
-        for (int off = 1; off < G::FB; off <<= 1) den += __shfl_xor(den, off);
+        den = row_sum<G::FB>(den);
         if (fb == 0) {
           if constexpr (DECAY != 0) den *= __expf(lct);
           denl[r] = den;
@@ -680,8 +724,7 @@ void output_kernel(const PfArgs a) {
         }
       }
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        for (int off = G::FB; off < 64; off <<= 1) dz[e] += __shfl_xor(dz[e], off);
+      for (int e = 0; e < 8; ++e) dz[e] = group_sum<G::FB>(dz[e]);
       if (lane < G::FB) {
         float* d = reinterpret_cast<float*>(buf + G::B_DZ) + wave * D + 8 * fb;
         *reinterpret_cast<f32x4*>(d) = f32x4{dz[0], dz[1], dz[2], dz[3]};
@@ -735,7 +778,7 @@ void output_kernel(const PfArgs a) {
         }
       }
     }
-    if (last && rg == 0) {
+    if (fin && rg == 0) {
       float* zd = a.z + int64_t(bh) * D + 8 * fb;
       *reinterpret_cast<f32x4*>(zd) = f32x4{zf[0], zf[1], zf[2], zf[3]};
       *reinterpret_cast<f32x4*>(zd + 4) = f32x4{zf[4], zf[5], zf[6], zf[7]};
@@ -828,7 +871,7 @@ void output_kernel(const PfArgs a) {
             o = mfma(vl[2 * sb + 1], ph1, o);
           }
         }
-        dsum += __shfl_xor(dsum, 32);
+        dsum = swap_sum32(dsum);
         const float inv = __builtin_amdgcn_rcpf(denl[tl] + dsum + a.eps);
         const int t = tok0 + tl;
         if (t < a.T) {
@@ -856,10 +899,8 @@ void output_kernel(const PfArgs a) {
           }
         }
       }
-      // fold this chunk into the carried state: w phi(k) as high + low parts
-      // (kept apart from the read-out so that its operand loads do not add
-      // to the read-out's register pressure)
-      __builtin_amdgcn_sched_barrier(0);
+      // fold this chunk into the carried state (w phi(k) high parts, and
+      // the low parts for a single segment; see `fin`)
       const float gam = DECAY ? __expf(*reinterpret_cast<const float*>(buf + G::B_LT)) : 1.f;
 #pragma unroll
       for (int mt = 0; mt < G::MT; ++mt) {
@@ -867,10 +908,9 @@ void output_kernel(const PfArgs a) {
 #pragma unroll
         for (int kk = 0; kk < G::KT; ++kk) {
           const u32x4 kh = tr_operand<D>(buf + G::B_KH, 16 * kk, 32 * mt, lane);
-          const u32x4 kl = tr_operand<D>(buf + G::B_KL, 16 * kk, 32 * mt, lane);
           acc[mt] = mfma(kh, vh[kk], acc[mt]);
-          acc[mt] = mfma(kl, vh[kk], acc[mt]);
           if constexpr (VS) acc[mt] = mfma(kh, vl[kk], acc[mt]);
+          if (fin) acc[mt] = mfma(tr_operand<D>(buf + G::B_KL, 16 * kk, 32 * mt, lane), vh[kk], acc[mt]);
         }
       }
     };
@@ -894,7 +934,7 @@ void output_kernel(const PfArgs a) {
         __syncthreads();
       }
     }
-    if (last) {
+    if (fin) {
       float* Sd = a.S + int64_t(bh) * D * D;
 #pragma unroll
       for (int mt = 0; mt < G::MT; ++mt)
@@ -914,7 +954,7 @@ hipError_t launch3(const PfArgs& a, int64_t BH, int stage, hipStream_t st) {
   using G = Cfg<D, C, __is_same(DT, f16_t)>;
   if (stage == 1) {
     if (a.nseg <= 1) return hipSuccess;
-    segment_state_kernel<D, C, DECAY, DT><<<dim3(unsigned(BH * (a.nslot - 1))), dim3(G::NT), 0, st>>>(a);
+    segment_state_kernel<D, C, DECAY, DT><<<dim3(unsigned(BH * a.nslot)), dim3(G::NT), 0, st>>>(a);
   } else if (stage == 2) {
     if (a.nseg <= 1) return hipSuccess;
     const int per_bh = (D * D + D + 255) / 256;
@@ -965,7 +1005,7 @@ Split split_of(const Problem& p) {
   q.nseg = q.cps > 0 ? (nchunks + q.cps - 1) / q.cps : 1;
   q.nsub = q.cps >= 2 ? 2 : 1;
   q.cps_sub = (q.cps + q.nsub - 1) / q.nsub;
-  q.nslot = q.nsub * (q.nseg - 1) + 1;
+  q.nslot = q.nsub * q.nseg;
   return q;
 }
 

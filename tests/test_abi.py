@@ -47,8 +47,8 @@ def test_plan_for_the_measured_prefills():
     # long context: chunked MFMA path, segments spread 8 heads over the chip
     c, s, p = la.prefill_plan(desc())
     assert (c, s, p) == (32, 32, 1)    # one workgroup per compute unit: 8 heads x 32 segments
-    # stage 1 cuts each of the first 31 segments in two: 2 * 31 + 1 state slots per head
-    slots = 2 * (s - 1) + 1
+    # stage 1 cuts every segment in two: 2 * 32 state slots per head
+    slots = 2 * s
     assert la.prefill_workspace_size(desc()) == 8 * slots * (128 * 128 + 128) * 4 + (
         (8 * slots * 4 + 255) // 256) * 256
     # fp32 inputs take the per-token kernel; no workspace
