@@ -18,7 +18,9 @@ Printed as one JSON line:
   roofline     the output kernel (la_prefill stage 3, the one that dominates),
                algorithmic bytes (q, k, v read + out written, bf16, plus the
                state) over its average duration, timed with events around
-               that stage alone, against the 8 TB/s HBM peak;
+               that stage alone, against the 8 TB/s HBM peak; `traffic` is
+               the HBM bytes per launch the counters measured (committed
+               summary under profiles/), null once the kernel source changed;
   mfma         algorithmic FLOPs of the recurrence, 4 d' d_v + 4 d' per
                token-head, over the step time, against the 2.5 PFLOP/s bf16
                dense peak;
@@ -35,6 +37,7 @@ from __future__ import annotations
 
 import argparse
 import ctypes
+import hashlib
 import json
 import os
 import sys
@@ -94,6 +97,34 @@ def cpu_baseline(T_sample: int):
                    f"per-head oracle time {min(per_head):.2f}-{max(per_head):.2f} s; "
                    f"{os.cpu_count()} host cores visible"),
     }
+
+
+# ------------------------------------------------------ HBM traffic (counters)
+
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "output_kernel_t102400_d128_hbm_traffic.txt")
+KERNEL_SOURCE = os.path.join(ROOT, "fixed_state_sequence_amd", "csrc", "la_prefill_mfma.hip")
+
+
+def profiled_traffic():
+    """HBM bytes per output-kernel launch, from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE per dispatch, each scaled by what the counter
+    reads for a streaming kernel of known size).  None when the kernel's
+    source has changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_PROFILE) as f:
+            lines = f.read().splitlines()
+        with open(KERNEL_SOURCE, "rb") as f:
+            src = hashlib.sha256(f.read()).hexdigest()
+    except OSError:
+        return None
+    kv = {}
+    for ln in lines:
+        if "=" in ln and not ln[:1].isspace():
+            k, v = ln.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != src or "traffic_bytes_per_launch" not in kv:
+        return None
+    return float(kv["traffic_bytes_per_launch"])
 
 
 # --------------------------------------------------------------------- GPU leg
@@ -160,12 +191,16 @@ def bench_prefill(torch, la, I, steps, warmup):
 def hbm_copy(torch, nbytes=1 << 30, reps=10):
     """Device-to-device copy of `nbytes` (read + write): the achievable HBM
     bandwidth this box shows for plain streaming, as a reference beside the
-    8 TB/s spec (also the known-size kernel the traffic counters are scaled by)."""
+    8 TB/s spec.  Three negations of the same buffers follow, outside the
+    timing: a streaming kernel of known size that, like the path's kernels,
+    moves 16 bytes per lane, for scaling the traffic counters."""
     dev = torch.device("cuda:0")
     src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
     for _ in range(3):
         dst.copy_(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
     torch.cuda.synchronize()
     e0, e1 = _events(torch)
     e0.record()
@@ -295,7 +330,7 @@ def main(argv=None):
                    "state_dtype": "fp32", "eps": PF["eps"], "decay": None,
                    "chunk": pf["chunk"], "segments": pf["segments"]},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": profiled_traffic(),
                      "kernel": "output_kernel (la_prefill stage 3)",
                      "kernel_ms": s3, "algorithmic_bytes": stage3_bytes,
                      "measured_copy_GBs": cp["gbs"], "frac_of_copy": achieved / cp["gbs"]},

@@ -117,6 +117,11 @@ struct Cfg {
   // blocks XOR-swizzled per row by blk_swz):
   //   Q, K   phi(q), phi(k); row = token, features at perm_pos order (read
   //          row-wise as the k = feature operands of the read-out and scores)
+  //   KR     the bf16 low part phi(k) - K, laid out as K, in the chunks that
+  //          start before token EXACT: their scores take phi(q) . (K + KR).
+  //          An output there averages few values, so a rounding error in one
+  //          weight passes to the output nearly undamped; later outputs
+  //          average hundreds of weights and their rounding errors cancel.
   //   KH, KL w phi(k) as bf16 high/low parts; row = perm_pos(token), natural
   //          features (read transposed: the k = token operand of the fold)
   //   VH, VL v (high/low parts only for fp16 inputs); row = perm_pos(token),
@@ -124,11 +129,13 @@ struct Cfg {
   // followed by per-token fp32 arrays and the per-wave z increments.
   static constexpr int B_Q = 0;
   static constexpr int B_K = B_Q + TILE;
-  static constexpr int B_KH = B_K + TILE;
+  static constexpr int B_KR = B_K + TILE;
+  static constexpr int B_KH = B_KR + TILE;
   static constexpr int B_KL = B_KH + TILE;
   static constexpr int B_VH = B_KL + TILE;
   static constexpr int B_VL = B_VH + TILE;
   static constexpr int B_L = B_VL + (VS ? TILE : 0);  // lc_t, fp32 [C]
+  static constexpr int EXACT = 128;
   static constexpr int B_B = B_L + 4 * C;             // beta_t, fp32 [C]
   static constexpr int B_DEN = B_B + 4 * C;           // inter-chunk denominators, fp32 [C]
   static constexpr int B_DZ = B_DEN + 4 * C;          // per-wave z increments, fp32 [NW][D]
@@ -218,6 +225,17 @@ __device__ __forceinline__ void row_write_perm(char* tile, int r, int fb, const 
   const int p0 = perm_pos(8 * fb), p1 = perm_pos(8 * fb + 4);
   *reinterpret_cast<u32x2*>(tile + tile_off<D>(r, p0 >> 3) + ((p0 & 7) << 1)) = u32x2{w[0], w[1]};
   *reinterpret_cast<u32x2*>(tile + tile_off<D>(r, p1 >> 3) + ((p1 & 7) << 1)) = u32x2{w[2], w[3]};
+}
+
+// p += (low parts of phi(k), key rows kr) . phi(q) (query row qr), over all
+// feature k-steps: the second half of the scores phi(q) . (K + KR).
+template <int D, int KS>
+__device__ __forceinline__ f32x16 low_scores(const char* kr_tile, const char* q_tile, int kr,
+                                             int qr, int g, f32x16 p) {
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    p = mfma(row_operand<D>(kr_tile, kr, 2 * ks + g), row_operand<D>(q_tile, qr, 2 * ks + g), p);
+  return p;
 }
 
 // Features 8 fb .. 8 fb + 7 of row r in natural order: one 16-byte block.
@@ -691,6 +709,7 @@ void output_kernel(const PfArgs a) {
         row_write_perm<D>(buf + G::B_Q, r, fb, pack8(qx));
         const u32x4 kp = pack8(kx);
         row_write_perm<D>(buf + G::B_K, r, fb, kp);
+        if (tok0 < G::EXACT) row_write_perm<D>(buf + G::B_KR, r, fb, low8(kx, kp));
         if constexpr (DECAY != 0) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
@@ -828,6 +847,8 @@ void output_kernel(const PfArgs a) {
           o = mfma(sf, qf, o);
           p = mfma(row_operand<D>(buf + G::B_K, 32 * tb + n, 2 * ks + g), qf, p);
         }
+        if (tok0 < G::EXACT)
+          p = low_scores<D, G::KS>(buf + G::B_KR, buf + G::B_Q, 32 * tb + n, tl, g, p);
         float lct = 0.f;
         if constexpr (DECAY != 0) {
           lct = Ll[tl];
@@ -842,6 +863,8 @@ void output_kernel(const PfArgs a) {
             for (int ks = 0; ks < G::KS; ++ks)
               p = mfma(row_operand<D>(buf + G::B_K, 32 * sb + n, 2 * ks + g),
                        row_operand<D>(buf + G::B_Q, tl, 2 * ks + g), p);
+            if (tok0 < G::EXACT)
+              p = low_scores<D, G::KS>(buf + G::B_KR, buf + G::B_Q, 32 * sb + n, tl, g, p);
           }
 #pragma unroll
           for (int r = 0; r < 16; ++r) {

@@ -298,7 +298,8 @@ def final_state(fk, v, alpha=None, beta=None, S0=None, z0=None):
         carry = np.ones(lead, F64)
     if beta is not None:
         w = w * _f64(beta)
-    S = np.einsum("...s,...sd,...sv->...dv", w, fk, v)
+    # optimize=True lets numpy contract pairwise through BLAS; same sums
+    S = np.einsum("...s,...sd,...sv->...dv", w, fk, v, optimize=True)
     z = np.einsum("...s,...sd->...d", w, fk)
     if S0 is not None:
         S = S + carry[..., None, None] * _f64(S0)

@@ -1,0 +1,146 @@
+"""The measured prefill workloads at their full sizes, in the launch
+configuration the benchmark times (default chunk and segment plan, output in
+the input type), against the fp64 oracle.
+
+* elu+1 prefill, B=4, H=8, T=2048, d=64, bf16: every output and the final
+  state, element by element.
+* SSD-decay prefill, B=2, H=16, T=8192, d=128, bf16: four (b, h) sequences
+  end to end through the oracle's recurrence, sampled positions of every
+  other sequence through the definition, and every final state through its
+  closed form.
+* long-context prefill, B=1, H=8, T=102400, d=128, bf16 scaled by 1/sqrt(2):
+  two heads end to end, sampled positions (chunk, sub-segment and segment
+  edges among them) of the other six, every final state in closed form.
+
+A 16-bit output is the fp32 result rounded to nearest even, so each element
+may sit up to half an ulp (2^-8 relative, worst case in a binade) from the
+oracle beyond the compute error; the metric subtracts that allowance before
+dividing by rms(oracle).  Bar: 2e-2 (bf16 inputs).
+"""
+import numpy as np
+import pytest
+import torch
+
+import fixed_state_sequence_amd as la
+from fixed_state_sequence_amd import inputs as I
+from oracle import linattn_oracle as O
+from conftest import rel_err, TOL, gpu_device
+
+pytestmark = pytest.mark.gpu
+
+HALF_ULP_BF16 = 2.0 ** -8
+
+
+def excess_err(got, ref, rms):
+    """max(|got - ref| - half an ulp of ref) / rms, for outputs rounded to bf16."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    ex = np.abs(got - ref) - HALF_ULP_BF16 * np.abs(ref)
+    return float(max(ex.max(), 0.0) / rms)
+
+
+def rms(x):
+    return float(np.sqrt(np.mean(np.asarray(x, dtype=np.float64) ** 2)))
+
+
+def run_workload(name):
+    """Inputs drawn on the host (seed 0) and the prefill as the benchmark runs it."""
+    dev = gpu_device()
+    x = I.workload_inputs(name, seed=0)
+    B, H, T, d = x.q.shape
+    desc = la.make_desc(B, H, T, d, d, la._lib.LA_BF16,
+                        decay=x.decay)
+    chunk, segments, path = la.prefill_plan(desc)
+    assert path == 1
+    g = lambda t: None if t is None else t.to(dev)
+    out, S, z = la.prefill(g(x.q), g(x.k), g(x.v), decay=g(x.decay))
+    torch.cuda.synchronize()
+    assert out.dtype == torch.bfloat16
+    print(name, "plan", chunk, segments)
+    return x, out.double().cpu().numpy(), S.cpu().numpy(), z.cpu().numpy(), (chunk, segments)
+
+
+def sample_positions(T, chunk, segments, n_random, rng):
+    cps = -(-T // chunk) // segments * chunk        # tokens per segment (full segments)
+    edges = {0, 1, chunk - 1, chunk, T - 1, T - 2}
+    for s in range(1, min(segments, 4)):
+        for off in (-1, 0, 1):
+            edges.add(s * cps + off)
+            edges.add(s * cps - cps // 2 + off)     # sub-segment edge inside segment s-1
+    edges |= set(int(t) for t in rng.integers(0, T, n_random))
+    return sorted(t for t in edges if 0 <= t < T)
+
+
+def check_sampled(x, out, S, z, full, others, positions, rms_ref):
+    """Outputs at `positions` of the (b, h) pairs in `others` by the definition,
+    and every final state by its closed form."""
+    B, H, T, _ = x.q.shape
+    alpha = None if x.decay is None else O._f64(x.decay)
+    worst = 0.0
+    for b, h in others:
+        fq = O.features(x.q[b, h])
+        fk = O.features(x.k[b, h])
+        v = O._f64(x.v[b, h])
+        a = None if alpha is None else alpha[b, h]
+        for t in positions:
+            ref = O.output_at(fq[t], fk, v, t, alpha=a)
+            worst = max(worst, excess_err(out[b, h, t], ref, rms_ref))
+    s_worst = z_worst = 0.0
+    for b in range(B):
+        for h in range(H):
+            if (b, h) in full:
+                continue
+            S_ref, z_ref = O.final_state(O.features(x.k[b, h]), x.v[b, h],
+                                         alpha=None if alpha is None else alpha[b, h])
+            s_worst = max(s_worst, rel_err(S[b, h], S_ref))
+            z_worst = max(z_worst, rel_err(z[b, h], z_ref))
+    return worst, s_worst, z_worst
+
+
+def test_elu_prefill_b4_h8_t2048_d64_full():
+    x, out, S, z, _ = run_workload("elu_prefill_b4_h8_t2048_d64")
+    o_ref, S_ref, z_ref = O.causal_linear_attention(x.q, x.k, x.v)
+    r = rms(o_ref)
+    e = (excess_err(out, o_ref, r), rel_err(S, S_ref), rel_err(z, z_ref))
+    print("elu prefill 4x8x2048x64", e, "plain max|err|/rms", rel_err(out, o_ref))
+    assert max(e) < TOL["bf16"], e
+
+
+def test_ssd_prefill_b2_h16_t8192_d128_sampled():
+    x, out, S, z, (chunk, segments) = run_workload("ssd_prefill_b2_h16_t8192_d128")
+    B, H, T, _ = x.q.shape
+    full = [(0, 0), (0, 15), (1, 7), (1, 15)]
+    bs, hs = [p[0] for p in full], [p[1] for p in full]
+    o_ref, S_ref, z_ref = O.causal_linear_attention(x.q[bs, hs], x.k[bs, hs], x.v[bs, hs],
+                                                    decay=x.decay[bs, hs])
+    r = rms(o_ref)
+    e_full = (excess_err(out[bs, hs], o_ref, r), rel_err(S[bs, hs], S_ref),
+              rel_err(z[bs, hs], z_ref))
+    rng = np.random.default_rng(3)
+    others = [(int(b), int(h)) for b, h in zip(rng.integers(0, B, 4), rng.integers(0, H, 4))]
+    pos = sample_positions(T, chunk, segments, 8, rng)
+    e_s = check_sampled(x, out, S, z, full, others, pos, r)
+    print("ssd prefill 2x16x8192x128 full", e_full, "sampled", e_s)
+    assert max(e_full + e_s) < TOL["bf16"], (e_full, e_s)
+
+
+def test_long_prefill_b1_h8_t102400_d128_sampled():
+    x, out, S, z, (chunk, segments) = run_workload("long_prefill_b1_h8_t102400_d128")
+    B, H, T, _ = x.q.shape
+    full = [(0, 0), (0, 5)]
+    hs = [p[1] for p in full]
+    o_ref, S_ref, z_ref = O.causal_linear_attention(x.q[0, hs], x.k[0, hs], x.v[0, hs])
+    r = rms(o_ref)
+    got = out[0, hs]
+    e_full = (excess_err(got, o_ref, r), rel_err(S[0, hs], S_ref), rel_err(z[0, hs], z_ref))
+    # the outputs shrink like 1/sqrt(t): also report the worst error of a position
+    # relative to that position's own rms
+    per_pos = (np.abs(got - o_ref).max(axis=-1) /
+               np.sqrt(np.mean(o_ref ** 2, axis=-1))).max()
+    rng = np.random.default_rng(4)
+    others = [(0, 1), (0, 2), (0, 7)]
+    pos = sample_positions(T, chunk, segments, 12, rng)
+    e_s = check_sampled(x, out, S, z, full, others, pos, r)
+    print("long prefill 1x8x102400x128 full", e_full, "sampled", e_s,
+          "worst per-position", per_pos)
+    assert max(e_full + e_s) < TOL["bf16"], (e_full, e_s)
