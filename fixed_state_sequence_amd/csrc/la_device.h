@@ -26,6 +26,9 @@ __device__ __forceinline__ void store_f32(float x, f16_t* d) { *d = static_cast<
 // phi(x) = elu(x) + 1 with alpha = 1: x + 1 for x > 0, exp(x) otherwise
 // (llm-arch-kb "Linear Attention", section 2, symbol legend).
 __device__ __forceinline__ float elu1_accurate(float x) { return x > 0.f ? x + 1.f : expf(x); }
-__device__ __forceinline__ float elu1_fast(float x) { return x > 0.f ? x + 1.f : __expf(x); }
+// The same function as max(x + 1, e^{-|x|}): for x <= 0, e^x >= 1 + x; for
+// x > 0, e^{-x} < 1 < x + 1.  Four VALU operations (the multiply by log2 e
+// takes -|x| as an input modifier; no compare and select).
+__device__ __forceinline__ float elu1_fast(float x) { return fmaxf(x + 1.f, __expf(-fabsf(x))); }
 
 }  // namespace la

@@ -150,13 +150,12 @@ struct Cfg {
   // producer prefetch depth (registers are not shared with the consumers'
   // accumulators, so it can be deeper)
   static constexpr int PDEPTH = RPT <= 2 ? 2 : 1;
-  // stage 1: KH, KL, VH (VL) and the z increments, two buffers
+  // stage 1: KH, KL, VH (VL), two buffers
   static constexpr int S1_KH = 0;
   static constexpr int S1_KL = S1_KH + TILE;
   static constexpr int S1_VH = S1_KL + TILE;
   static constexpr int S1_VL = S1_VH + TILE;
-  static constexpr int S1_DZ = S1_VL + (VS ? TILE : 0);
-  static constexpr int S1_BUF = S1_DZ + 4 * NW * D;
+  static constexpr int S1_BUF = S1_VL + (VS ? TILE : 0);
   static constexpr int S1_LDS = 2 * S1_BUF;
   static_assert(RPT == C / 16, "row split");
   static_assert(C == 32 || C == 64 || C == 128, "chunk");
@@ -447,7 +446,10 @@ __global__ __launch_bounds__(2 * D) void segment_state_kernel(const PfArgs a) {
   f32x16 acc[G::MT];
 #pragma unroll
   for (int mt = 0; mt < G::MT; ++mt) acc[mt] = f32x16{};
-  float zf[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};   // z of features 8 fb .. 8 fb + 7
+  // this thread's share of z (features 8 fb .. 8 fb + 7, its own rows of
+  // every chunk): the weights already carry the decay, so z is a plain sum,
+  // reduced over the threads once at the end
+  float zp[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float lsuf = 0.f;   // log-decay of the chunks already staged (later in the segment)
 
   auto fetch = [&](RawChunk<G::RPT, G::ND, false>& r, int c) {
@@ -455,15 +457,16 @@ __global__ __launch_bounds__(2 * D) void segment_state_kernel(const PfArgs a) {
                                                     rg, fb, lane);
   };
   // [A] chunk c into buffer buf: w phi(k) high/low and v as token-major
-  // tiles, per-wave z increments.  Rows past the end have k = v = 0: phi(k) =
-  // 1 there and v = 0, so they add nothing to S; without decay their 1s are
-  // taken off z when the increments are summed.
+  // tiles; this thread's rows added to zp.  Rows past the end have k = v = 0:
+  // phi(k) = 1 there and v = 0, so they add nothing to S; without decay
+  // their 1s are taken off z at the end.  The chunk before the segment's
+  // first (staged only to keep the loads uniform) adds nothing to zp.
   auto stage = [&](RawChunk<G::RPT, G::ND, false>& raw, int c, char* buf) {
     const int tok0 = c * C;
     clean_chunk<C, G::RPT, G::ND, false, DECAY>(raw, tok0, a.T, rg, lane);
     float lo = 0.f, hi = 0.f, ltot = 0.f;
     if constexpr (DECAY != 0) chunk_logprefix<C, G::ND>(raw.d, lane, lo, hi, ltot);
-    float dz[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    const bool live = c >= c0;
 #pragma unroll
     for (int i = 0; i < G::RPT; ++i) {
       const int r = G::RPT * rg + i;
@@ -478,7 +481,7 @@ __global__ __launch_bounds__(2 * D) void segment_state_kernel(const PfArgs a) {
       for (int e = 0; e < 8; ++e) {
         kx[e] = elu1_fast(kx[e]);
         if constexpr (DECAY != 0) kx[e] *= w;
-        dz[e] += kx[e];
+        if (live) zp[e] += kx[e];
       }
       const u32x4 kh = pack8(kx);
       blk_write<D>(buf + G::S1_KH, perm_pos(r), fb, kh);
@@ -493,30 +496,14 @@ __global__ __launch_bounds__(2 * D) void segment_state_kernel(const PfArgs a) {
         blk_write<D>(buf + G::S1_VH, perm_pos(r), fb, raw.v[i]);
       }
     }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) dz[e] = group_sum<G::FB>(dz[e]);
-    if (lane < G::FB) {
-      float* d = reinterpret_cast<float*>(buf + G::S1_DZ) + wave * D + 8 * fb;
-      *reinterpret_cast<f32x4*>(d) = f32x4{dz[0], dz[1], dz[2], dz[3]};
-      *reinterpret_cast<f32x4*>(d + 4) = f32x4{dz[4], dz[5], dz[6], dz[7]};
-    }
-    if (c >= c0) lsuf += ltot;
+    if (live) lsuf += ltot;
     // refill this register set with the chunk DEPTH further back (clamped:
     // the loads are issued on every path, see RawChunk)
     if constexpr (G::DEPTH > 0) fetch(raw, max(c - G::DEPTH, c0));
   };
-  // [B] fold chunk c (staged in buf) into S and z; the weights already
-  // carry the decay.
-  auto fold = [&](int c, const char* buf) {
-    const float* dzl = reinterpret_cast<const float*>(buf + G::S1_DZ);
-    const float pad = DECAY ? 0.f : float(max(c * C + C - a.T, 0));
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float s = -pad;
-#pragma unroll
-      for (int w = 0; w < G::NW; ++w) s += dzl[w * D + 8 * fb + e];
-      zf[e] += s;
-    }
+  // [B] fold chunk c (staged in buf) into S; the weights already carry the
+  // decay.
+  auto fold = [&](const char* buf) {
     u32x4 vh[G::KT], vl[G::KT];
 #pragma unroll
     for (int kk = 0; kk < G::KT; ++kk) {
@@ -556,7 +543,7 @@ __global__ __launch_bounds__(2 * D) void segment_state_kernel(const PfArgs a) {
       char* nxt = smem + ((i + 1) & 1) * G::S1_BUF;
       if constexpr (G::DEPTH == 0) fetch(raw[0], max(c - 1, c0));
       stage(raw[(j + 1) % G::RING], c - 1, nxt);
-      if (c >= c0) fold(c, cur);
+      if (c >= c0) fold(cur);
       __syncthreads();
     }
   }
@@ -571,9 +558,23 @@ __global__ __launch_bounds__(2 * D) void segment_state_kernel(const PfArgs a) {
       const int f = 32 * mt + 8 * (r >> 2) + 4 * g + (r & 3);
       dst[f * D + 32 * wave + n] = acc[mt][r];
     }
-  if (rg == 0) {
-    *reinterpret_cast<f32x4*>(dst + D * D + 8 * fb) = f32x4{zf[0], zf[1], zf[2], zf[3]};
-    *reinterpret_cast<f32x4*>(dst + D * D + 8 * fb + 4) = f32x4{zf[4], zf[5], zf[6], zf[7]};
+  // z: the threads' shares, summed within each wave, then over the waves
+  // through LDS; less the 1s of the rows past the end (no decay)
+#pragma unroll
+  for (int e = 0; e < 8; ++e) zp[e] = group_sum<G::FB>(zp[e]);
+  float* zl = reinterpret_cast<float*>(smem);   // the tiles are no longer read
+  if (lane < G::FB) {
+    *reinterpret_cast<f32x4*>(zl + wave * D + 8 * fb) = f32x4{zp[0], zp[1], zp[2], zp[3]};
+    *reinterpret_cast<f32x4*>(zl + wave * D + 8 * fb + 4) = f32x4{zp[4], zp[5], zp[6], zp[7]};
+  }
+  __syncthreads();
+  if (tid < D) {
+    // (a sub-segment can be empty: c0 = c1 = nchunks at the end of a
+    // ragged split; it holds no rows at all)
+    float zs = (DECAY == 0 && c0 < c1 && c1 == nchunks) ? -float(nchunks * C - a.T) : 0.f;
+#pragma unroll
+    for (int w = 0; w < G::NW; ++w) zs += zl[w * D + tid];
+    dst[D * D + tid] = zs;
   }
   if (tid == 0) a.ws_logg[int64_t(bh) * a.nslot + u] = lsuf;
 }
