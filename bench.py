@@ -189,27 +189,31 @@ def bench_prefill(torch, la, I, steps, warmup):
 
 
 def hbm_copy(torch, nbytes=1 << 30, reps=10):
-    """Device-to-device copy of `nbytes` (read + write): the achievable HBM
-    bandwidth this box shows for plain streaming, as a reference beside the
-    8 TB/s spec.  Three negations of the same buffers follow, outside the
-    timing: a streaming kernel of known size that, like the path's kernels,
-    moves 16 bytes per lane, for scaling the traffic counters."""
+    """Device-to-device streaming of `nbytes` (read + write) by two kernels,
+    torch's copy and its vectorised negation (16 bytes per lane, like the
+    path's kernels): the faster is the achievable HBM bandwidth this box
+    shows for plain streaming, the reference beside the 8 TB/s spec.  The
+    negation is also the known-size kernel the traffic counters are scaled
+    by."""
     dev = torch.device("cuda:0")
     src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
-    for _ in range(3):
-        dst.copy_(src)
-    for _ in range(3):
-        torch.neg(src, out=dst)
-    torch.cuda.synchronize()
-    e0, e1 = _events(torch)
-    e0.record()
-    for _ in range(reps):
-        dst.copy_(src)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
-    return dict(bytes=2 * nbytes, ms=ms, gbs=2 * nbytes / (ms * 1e-3) / 1e9)
+    best = None
+    for name, fn in (("copy", lambda: dst.copy_(src)), ("neg", lambda: torch.neg(src, out=dst))):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = _events(torch)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        gbs = 2 * nbytes / (ms * 1e-3) / 1e9
+        if best is None or gbs > best["gbs"]:
+            best = dict(bytes=2 * nbytes, ms=ms, gbs=gbs, kernel=name)
+    return best
 
 
 def bench_decode(torch, la, I, N, steps, warmup=64):
@@ -333,7 +337,8 @@ def main(argv=None):
                      "frac": achieved / HBM_PEAK_GBS, "traffic": profiled_traffic(),
                      "kernel": "output_kernel (la_prefill stage 3)",
                      "kernel_ms": s3, "algorithmic_bytes": stage3_bytes,
-                     "measured_copy_GBs": cp["gbs"], "frac_of_copy": achieved / cp["gbs"]},
+                     "measured_copy_GBs": cp["gbs"], "copy_kernel": cp["kernel"],
+                     "frac_of_copy": achieved / cp["gbs"]},
         "step": {"stage_ms": pf["stage_ms"], "algorithmic_bytes": step_bytes,
                  "GBs": step_bytes / (pf["ms"] * 1e-3) / 1e9,
                  "hbm_frac": step_bytes / (pf["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS},

@@ -36,6 +36,8 @@
 // feeds the read-out MFMA straight from registers, and the intra-chunk score
 // tile feeds the P V product the same way.  Every LDS tile is stored in that
 // permuted k-order so all operands agree.
+#include <type_traits>
+
 #include "la_device.h"
 #include "la_internal.h"
 
@@ -411,6 +413,38 @@ __device__ __forceinline__ float row_sum(float x) {
   if constexpr (FB == 16) x += dpp<0x140>(x);   // row_mirror
   return x;
 }
+// x[l] + x[l ^ 32] of a in lanes 0-31 and of b in lanes 32-63 (the swap
+// trades lanes 32-63 of its first register with lanes 0-31 of its second).
+__device__ __forceinline__ float swap_fold32(float a, float b) {
+  return pair_sum(__builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, a),
+                                                   __builtin_bit_cast(unsigned, b), false, false));
+}
+// x[l] + x[l ^ 16] of a in even rows of 16 lanes and of b in odd rows (the
+// swap trades the odd rows of its first register with the even rows of its
+// second).
+__device__ __forceinline__ float swap_fold16(float a, float b) {
+  return pair_sum(__builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, a),
+                                                   __builtin_bit_cast(unsigned, b), false, false));
+}
+// Reduce-scatter of 8 per-lane values v[e] (feature 8 fb + e, fb = lane % FB)
+// over the lanes of a wave that share fb: on return every lane holds the
+// totals of features 8 fb + base + {0, 1} in s0, s1 and the function returns
+// base (lanes l and l ^ 8 hold the same pair when FB = 8).
+template <int FB>
+__device__ __forceinline__ int reduce_scatter8(const float (&v)[8], int lane, float& s0,
+                                               float& s1) {
+  float t[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) t[i] = swap_fold32(v[i], v[i + 4]);   // feature i + 4 (lane / 32)
+  s0 = swap_fold16(t[0], t[2]);   // feature 2 (row & 1) + 4 (lane / 32) + {0, 1}
+  s1 = swap_fold16(t[1], t[3]);
+  if constexpr (FB == 8) {
+    s0 += dpp<0x128>(s0);          // row_ror:8, lanes l and l ^ 8 share fb
+    s1 += dpp<0x128>(s1);
+  }
+  return 4 * (lane >> 5) + 2 * ((lane >> 4) & 1);
+}
+
 template <int FB>
 __device__ __forceinline__ float group_sum(float x) {
   if constexpr (FB == 8) x += dpp<0x128>(x);     // row_ror:8
@@ -743,12 +777,12 @@ void output_kernel(const PfArgs a) {
           Bl[r] = beta;
         }
       }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) dz[e] = group_sum<G::FB>(dz[e]);
-      if (lane < G::FB) {
-        float* d = reinterpret_cast<float*>(buf + G::B_DZ) + wave * D + 8 * fb;
-        *reinterpret_cast<f32x4*>(d) = f32x4{dz[0], dz[1], dz[2], dz[3]};
-        *reinterpret_cast<f32x4*>(d + 4) = f32x4{dz[4], dz[5], dz[6], dz[7]};
+      {
+        float s0, s1;
+        const int base = reduce_scatter8<G::FB>(dz, lane, s0, s1);
+        if (G::FB == 16 || !(lane & 8))
+          *reinterpret_cast<f32x2*>(reinterpret_cast<float*>(buf + G::B_DZ) + wave * D + 8 * fb +
+                                    base) = f32x2{s0, s1};
       }
       if (ts == 0) *reinterpret_cast<float*>(buf + G::B_LT) = ltot;
       // refill this register set with the chunk PDEPTH ahead (clamped)
@@ -924,19 +958,26 @@ void output_kernel(const PfArgs a) {
         }
       }
       // fold this chunk into the carried state (w phi(k) high parts, and
-      // the low parts for a single segment; see `fin`)
+      // the low parts for a single segment; see `fin`).  One branch picks
+      // a straight-line fold, so the tile reads are not held back behind a
+      // branch per MFMA.
       const float gam = DECAY ? __expf(*reinterpret_cast<const float*>(buf + G::B_LT)) : 1.f;
+      auto fold = [&](auto with_lo) {
 #pragma unroll
-      for (int mt = 0; mt < G::MT; ++mt) {
-        if constexpr (DECAY != 0) acc[mt] *= gam;
+        for (int mt = 0; mt < G::MT; ++mt) {
+          if constexpr (DECAY != 0) acc[mt] *= gam;
 #pragma unroll
-        for (int kk = 0; kk < G::KT; ++kk) {
-          const u32x4 kh = tr_operand<D>(buf + G::B_KH, 16 * kk, 32 * mt, lane);
-          acc[mt] = mfma(kh, vh[kk], acc[mt]);
-          if constexpr (VS) acc[mt] = mfma(kh, vl[kk], acc[mt]);
-          if (fin) acc[mt] = mfma(tr_operand<D>(buf + G::B_KL, 16 * kk, 32 * mt, lane), vh[kk], acc[mt]);
+          for (int kk = 0; kk < G::KT; ++kk) {
+            const u32x4 kh = tr_operand<D>(buf + G::B_KH, 16 * kk, 32 * mt, lane);
+            acc[mt] = mfma(kh, vh[kk], acc[mt]);
+            if constexpr (VS) acc[mt] = mfma(kh, vl[kk], acc[mt]);
+            if constexpr (decltype(with_lo)::value)
+              acc[mt] = mfma(tr_operand<D>(buf + G::B_KL, 16 * kk, 32 * mt, lane), vh[kk], acc[mt]);
+          }
         }
-      }
+      };
+      if (fin) fold(std::true_type{});
+      else fold(std::false_type{});
     };
 
     if constexpr (G::NBUF == 2) {
