@@ -140,8 +140,12 @@ struct Cfg {
   static constexpr int EXACT = 128;
   static constexpr int B_B = B_L + 4 * C;             // beta_t, fp32 [C]
   static constexpr int B_DEN = B_B + 4 * C;           // inter-chunk denominators, fp32 [C]
-  static constexpr int B_DZ = B_DEN + 4 * C;          // per-wave z increments, fp32 [NW][D]
-  static constexpr int BUF = B_DZ + 4 * NW * D;
+  static constexpr int B_DZ = B_DEN + 4 * C;          // per-wave z increments, fp32 [NW][DZS]
+  // z increment of feature 8 fb + e at dz_index: 4 floats of padding after
+  // the first 64, so that feature blocks fb and fb + 8 (read together by a
+  // wave) fall in different banks
+  static constexpr int DZS = D + (D > 64 ? 4 : 0);
+  static constexpr int BUF = B_DZ + 4 * NW * DZS;
   // The output stage: producer waves stage chunk c + 1 into one buffer while
   // consumer waves compute chunk c from the other, when two buffers fit; each
   // buffer also carries the chunk's total log-decay.
@@ -413,6 +417,9 @@ __device__ __forceinline__ float row_sum(float x) {
   if constexpr (FB == 16) x += dpp<0x140>(x);   // row_mirror
   return x;
 }
+// Padded position of feature 8 fb + e in a wave's z increments (see DZS).
+__device__ __forceinline__ int dz_index(int fb, int e) { return 8 * fb + e + ((fb >> 3) << 2); }
+
 // x[l] + x[l ^ 32] of a in lanes 0-31 and of b in lanes 32-63 (the swap
 // trades lanes 32-63 of its first register with lanes 0-31 of its second).
 __device__ __forceinline__ float swap_fold32(float a, float b) {
@@ -693,7 +700,15 @@ void output_kernel(const PfArgs a) {
   if (wave_id >= G::NW) {
     // =================================================== producer waves
     const int ts = threadIdx.x - G::NT, lane = ts & 63, wave = ts >> 6;
-    const int fb = ts % G::FB, rg = ts / G::FB;
+    const int fb = ts % G::FB;
+    // Row group of this thread (rows RPT rg .. RPT rg + RPT - 1 of a chunk).
+    // At 16 feature blocks and 2 rows per thread, bits 0 and 1 of the group
+    // index are swapped: the two row groups a half-wave writes (8-byte
+    // pieces of the Q and K rows) are then 4 rows apart, and the XOR
+    // swizzle puts them in disjoint banks.
+    const int rg0 = ts / G::FB;
+    const int rg = (G::FB == 16 && G::RPT == 2) ? ((rg0 & ~3) | ((rg0 & 1) << 1) | ((rg0 >> 1) & 1))
+                                                : rg0;
     const DT* qg = static_cast<const DT*>(a.q) + int64_t(bh) * a.T * D;
     const DT* kg = static_cast<const DT*>(a.k) + int64_t(bh) * a.T * D;
     const DT* vg = static_cast<const DT*>(a.v) + int64_t(bh) * a.T * D;
@@ -781,8 +796,8 @@ void output_kernel(const PfArgs a) {
         float s0, s1;
         const int base = reduce_scatter8<G::FB>(dz, lane, s0, s1);
         if (G::FB == 16 || !(lane & 8))
-          *reinterpret_cast<f32x2*>(reinterpret_cast<float*>(buf + G::B_DZ) + wave * D + 8 * fb +
-                                    base) = f32x2{s0, s1};
+          *reinterpret_cast<f32x2*>(reinterpret_cast<float*>(buf + G::B_DZ) + wave * G::DZS +
+                                    dz_index(fb, base)) = f32x2{s0, s1};
       }
       if (ts == 0) *reinterpret_cast<float*>(buf + G::B_LT) = ltot;
       // refill this register set with the chunk PDEPTH ahead (clamped)
@@ -798,7 +813,7 @@ void output_kernel(const PfArgs a) {
       for (int e = 0; e < 8; ++e) {
         float s = -pad;
 #pragma unroll
-        for (int w = 0; w < G::NW; ++w) s += dzl[w * D + 8 * fb + e];
+        for (int w = 0; w < G::NW; ++w) s += dzl[w * G::DZS + dz_index(fb, e)];
         zf[e] = fmaf(gam, zf[e], s);
       }
     };
