@@ -29,6 +29,7 @@ Printed as one JSON line:
                fp32, 1024 one-token steps): state GB/s against 8 TB/s, and the
                same with 1024 sequences so the state (545 MB) exceeds the
                256 MB last-level cache;
+  normaliser_free  the same prefill with the read-out phi(q)^T S alone;
   cpu_baseline the fp64 oracle (the CPU reference the tests check against),
                on a bounded sample of the same prefill workload, one worker
                process per head.
@@ -133,12 +134,12 @@ def _events(torch):
     return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
 
-def bench_prefill(torch, la, I, steps, warmup):
+def bench_prefill(torch, la, I, steps, warmup, normalize=True, stages=True):
     dev = torch.device("cuda:0")
     B, H, T, d = PF["B"], PF["H"], PF["T"], PF["d"]
     x = I.prefill_inputs(B, H, T, d, dtype="bf16", seed=0, scale=PF["scale"], device=dev)
     q, k, v = x.q, x.k, x.v
-    desc = la.make_desc(B, H, T, d, d, la._lib.LA_BF16, eps=PF["eps"])
+    desc = la.make_desc(B, H, T, d, d, la._lib.LA_BF16, eps=PF["eps"], normalize=normalize)
     chunk, segments, path = la.prefill_plan(desc)
     if path != 1:
         raise RuntimeError("the long-context prefill did not take the chunked MFMA path")
@@ -170,6 +171,8 @@ def bench_prefill(torch, la, I, steps, warmup):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = e0.elapsed_time(e1) / steps
+    if not stages:
+        return dict(ms=ms, wall=wall, chunk=chunk, segments=segments)
 
     # per-stage durations: the same calls back to back (no synchronisation
     # between repetitions, so the clocks stay where the timed steps had them),
@@ -307,6 +310,8 @@ def main(argv=None):
     tflops = flops / (pf["ms"] * 1e-3) / 1e12
     step_bytes = TH * 4 * d * 2 + 2 * state_bytes
 
+    print("[bench] prefill, normaliser-free read-out", file=sys.stderr, flush=True)
+    pf_nn = bench_prefill(torch, la, I, a.steps, a.warmup, normalize=False, stages=False)
     cp = hbm_copy(torch)
     dec = dec_big = None
     if not a.no_decode:
@@ -345,6 +350,11 @@ def main(argv=None):
         "mfma": {"algorithmic_flops": flops, "achieved": tflops, "peak": BF16_PEAK_TFLOPS,
                  "unit": "TFLOP/s", "frac": tflops / BF16_PEAK_TFLOPS},
         "cpu_baseline": cpu,
+        "normaliser_free": {
+            "workload": "the same prefill, read-out phi(q)^T S without the normaliser",
+            "ms_per_step": pf_nn["ms"], "tokens_per_s": B * T / (pf_nn["ms"] * 1e-3),
+            "GBs": step_bytes / (pf_nn["ms"] * 1e-3) / 1e9,
+            "hbm_frac": step_bytes / (pf_nn["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS},
     }
     if dec is not None:
         res["decode"] = {

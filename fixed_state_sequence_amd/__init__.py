@@ -53,9 +53,11 @@ def _need(t, name, device=None, dtype=None, shape=None):
 
 
 def make_desc(B, H, T, d_h, d_v, dtype_code, phi="elu1", W=None, rff_D=None, decay=None,
-              gate=None, eps=1e-6, chunk=0, segments=0, out_dtype_code=None) -> _lib.LaDesc:
+              gate=None, eps=1e-6, chunk=0, segments=0, out_dtype_code=None,
+              normalize=True) -> _lib.LaDesc:
     """Build an `la_desc`.  `decay` (SSD a_t) and `gate` (RFA g_t) are exclusive;
-    `out_dtype_code` defaults to the input type."""
+    `out_dtype_code` defaults to the input type; `normalize=False` selects the
+    read-out without the normaliser (LA_NORM_NONE)."""
     d = _lib.LaDesc()
     d.B, d.H, d.T, d.d_h, d.d_v = int(B), int(H), int(T), int(d_h), int(d_v)
     d.dtype = int(dtype_code)
@@ -78,6 +80,7 @@ def make_desc(B, H, T, d_h, d_v, dtype_code, phi="elu1", W=None, rff_D=None, dec
         d.decay_kind, d.decay = _lib.LA_DECAY_NONE, None
     d.eps = float(eps)
     d.chunk, d.segments = int(chunk), int(segments)
+    d.norm = _lib.LA_NORM_SUM if normalize else _lib.LA_NORM_NONE
     return d
 
 
@@ -100,7 +103,8 @@ def state_init(B: int, H: int, d_prime: int, d_v: int, device="cuda") -> Tuple["
     return S, z
 
 
-def _prefill_desc(q, k, v, phi, W, decay, gate, eps, chunk, segments, out_dtype=None):
+def _prefill_desc(q, k, v, phi, W, decay, gate, eps, chunk, segments, out_dtype=None,
+                  normalize=True):
     torch = _torch()
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, n, device=q.device, dtype=q.dtype)
@@ -116,7 +120,7 @@ def _prefill_desc(q, k, v, phi, W, decay, gate, eps, chunk, segments, out_dtype=
         if a is not None:
             _need(a, n, device=q.device, dtype=torch.float32, shape=(B, H, T))
     desc = make_desc(B, H, T, d_h, d_v, _dtype_code(q.dtype), phi, W, None, decay, gate, eps,
-                     chunk, segments, _dtype_code(out_dtype or q.dtype))
+                     chunk, segments, _dtype_code(out_dtype or q.dtype), normalize)
     return desc, (B, H, T, d_h, d_v)
 
 
@@ -136,18 +140,19 @@ def prefill_plan(desc: _lib.LaDesc):
 
 def prefill(q, k, v, *, phi: str = "elu1", W=None, decay=None, gate=None, eps: float = 1e-6,
             state: Optional[tuple] = None, chunk: int = 0, segments: int = 0, out=None,
-            workspace=None, out_dtype=None):
+            workspace=None, out_dtype=None, normalize: bool = True):
     """Causal linear attention over [B, H, T, d] inputs on the GPU.
 
     Returns (out, S, z).  If `state=(S, z)` is given the recurrence continues
     from it and the final state is written back into those tensors (in place);
     otherwise a zero state is allocated.  `out_dtype` is q's dtype (default)
-    or torch.float32.
+    or torch.float32.  `normalize=False` returns the numerator phi(q)^T S
+    alone (LA_NORM_NONE); z is still carried.
     """
     torch = _torch()
     out_dtype = out_dtype or q.dtype
     desc, (B, H, T, d_h, d_v) = _prefill_desc(q, k, v, phi, W, decay, gate, eps, chunk, segments,
-                                              out_dtype)
+                                              out_dtype, normalize)
     dp = feature_dim(d_h, phi, desc.rff_D)
     if state is None:
         S, z = state_init(B, H, dp, d_v, q.device)
@@ -169,10 +174,11 @@ def prefill(q, k, v, *, phi: str = "elu1", W=None, decay=None, gate=None, eps: f
 
 
 def prefill_stage(stage: int, q, k, v, S, z, out, workspace, *, phi="elu1", W=None, decay=None,
-                  gate=None, eps=1e-6, chunk=0, segments=0):
+                  gate=None, eps=1e-6, chunk=0, segments=0, normalize=True):
     """Run one of la_prefill's three stages (1 segment states, 2 scan, 3 outputs);
     out's dtype selects the output type."""
-    desc, _ = _prefill_desc(q, k, v, phi, W, decay, gate, eps, chunk, segments, out.dtype)
+    desc, _ = _prefill_desc(q, k, v, phi, W, decay, gate, eps, chunk, segments, out.dtype,
+                            normalize)
     nws = prefill_workspace_size(desc)
     _lib.check(_lib.lib().la_prefill_stage(ctypes.byref(desc), int(stage), _ptr(q), _ptr(k), _ptr(v),
                                            _ptr(S), _ptr(z), _ptr(out),
@@ -181,10 +187,11 @@ def prefill_stage(stage: int, q, k, v, S, z, out, workspace, *, phi="elu1", W=No
 
 
 def decode_step(q, k, v, S, z, *, phi: str = "elu1", W=None, decay=None, gate=None,
-                eps: float = 1e-6, out=None, out_dtype=None):
+                eps: float = 1e-6, out=None, out_dtype=None, normalize: bool = True):
     """One token for B sequences x H heads: q, k [B, H, d_h], v [B, H, d_v].
 
-    Updates (S, z) in place and returns out [B, H, d_v] (dtype of q).
+    Updates (S, z) in place and returns out [B, H, d_v] (dtype of q);
+    `normalize=False` returns the numerator alone.
     """
     torch = _torch()
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
@@ -202,7 +209,7 @@ def decode_step(q, k, v, S, z, *, phi: str = "elu1", W=None, decay=None, gate=No
             _need(a, n, device=q.device, dtype=torch.float32, shape=(B, H))
     out_dtype = out_dtype or q.dtype
     desc = make_desc(B, H, 1, d_h, d_v, _dtype_code(q.dtype), phi, W, None, decay, gate, eps,
-                     out_dtype_code=_dtype_code(out_dtype))
+                     out_dtype_code=_dtype_code(out_dtype), normalize=normalize)
     dp = feature_dim(d_h, phi, desc.rff_D)
     _need(S, "S", device=q.device, dtype=torch.float32, shape=(B, H, dp, d_v))
     _need(z, "z", device=q.device, dtype=torch.float32, shape=(B, H, dp))

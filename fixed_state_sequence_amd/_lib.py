@@ -17,6 +17,7 @@ LA_OK, LA_EINVAL, LA_EUNSUPPORTED, LA_EHIP = 0, 1, 2, 3
 LA_F32, LA_BF16, LA_F16 = 0, 1, 2
 LA_PHI_ELU1, LA_PHI_RFF = 0, 1
 LA_DECAY_NONE, LA_DECAY_SSD, LA_GATE_RFA = 0, 1, 2
+LA_NORM_SUM, LA_NORM_NONE = 0, 1
 
 
 class LaDesc(ctypes.Structure):
@@ -28,6 +29,7 @@ class LaDesc(ctypes.Structure):
         ("rff_D", ctypes.c_int), ("rff_W", ctypes.c_void_p),
         ("decay_kind", ctypes.c_int), ("decay", ctypes.c_void_p),
         ("eps", ctypes.c_float), ("chunk", ctypes.c_int), ("segments", ctypes.c_int),
+        ("norm", ctypes.c_int),
     ]
 
 

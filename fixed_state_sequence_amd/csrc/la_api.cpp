@@ -69,6 +69,8 @@ la_status check_desc(const la_desc* d, bool prefill, la::Problem* p) {
     return fail(LA_EINVAL, "unknown decay kind %d", int(d->decay_kind));
   }
   if (!std::isfinite(d->eps)) return fail(LA_EINVAL, "eps must be finite");
+  if (d->norm != LA_NORM_SUM && d->norm != LA_NORM_NONE)
+    return fail(LA_EINVAL, "unknown read-out form %d", int(d->norm));
   if (prefill) {
     if (d->chunk != 0 && d->chunk != 32 && d->chunk != 64 && d->chunk != 128)
       return fail(LA_EINVAL, "chunk must be 0, 32, 64 or 128 (got %d)", d->chunk);
@@ -85,6 +87,7 @@ la_status check_desc(const la_desc* d, bool prefill, la::Problem* p) {
   p->dh = d->d_h; p->dv = d->d_v; p->dp = dp;
   p->dtype = d->dtype; p->out_dtype = d->out_dtype; p->phi = d->phi; p->D = d->rff_D; p->W = d->rff_W;
   p->decay_kind = d->decay_kind; p->decay = d->decay; p->eps = d->eps;
+  p->nonorm = d->norm == LA_NORM_NONE ? 1 : 0;
   p->chunk = d->chunk ? d->chunk : 32;
   p->segments = 1;
   p->path = 0;

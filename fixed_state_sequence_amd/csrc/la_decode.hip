@@ -38,6 +38,7 @@ struct DecArgs {
   int N, H, dh;
   int dhp;              // padded LDS row of W (floats)
   int out_f32;
+  int nonorm;           // read-out without the normaliser
   float eps;
 };
 
@@ -237,7 +238,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(const DecArgs a) {
     }
   }
   if (valid && wsub == 0 && lane < G::CG) {
-    const float inv = 1.0f / (den + a.eps);
+    const float inv = a.nonorm ? 1.f : 1.0f / (den + a.eps);
     const int64_t o0 = st * DV + 4 * cg;
     if (a.out_f32) {
       *reinterpret_cast<float4*>(static_cast<float*>(a.out) + o0) =
@@ -309,6 +310,7 @@ hipError_t launch_decode(const Problem& p, const void* q, const void* k, const v
   a.dhp = ((p.dh + 3) / 4) * 4 + 4;
   a.out_f32 = p.out_dtype == LA_F32 ? 1 : 0;
   a.eps = p.eps;
+  a.nonorm = p.nonorm;
   switch (p.dtype) {
     case LA_F32: return launch_dt<float>(a, p.dp, p.dv, p.phi, p.decay_kind, stream);
     case LA_BF16: return launch_dt<bf16_t>(a, p.dp, p.dv, p.phi, p.decay_kind, stream);

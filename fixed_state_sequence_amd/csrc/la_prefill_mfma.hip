@@ -286,6 +286,7 @@ struct PfArgs {
   int cps_sub;       // chunks per sub-segment (the last one of a segment may be shorter)
   int nslot;         // nsub nseg
   int out_f32;       // out is fp32 (else the input type)
+  int nonorm;        // read-out without the normaliser
   float eps;
 };
 
@@ -945,7 +946,7 @@ void output_kernel(const PfArgs a) {
           }
         }
         dsum = swap_sum32(dsum);
-        const float inv = __builtin_amdgcn_rcpf(denl[tl] + dsum + a.eps);
+        const float inv = a.nonorm ? 1.f : __builtin_amdgcn_rcpf(denl[tl] + dsum + a.eps);
         const int t = tok0 + tl;
         if (t < a.T) {
           const uint32_t orow = uint32_t(t) * D + 32 * wave + 4 * g;
@@ -1135,6 +1136,7 @@ hipError_t launch_mfma_stage(const Problem& p, int stage, const void* q, const v
   a.cps_sub = sp.cps_sub;
   a.nslot = sp.nslot;
   a.eps = p.eps;
+  a.nonorm = p.nonorm;
   a.out_f32 = p.out_dtype == LA_F32 ? 1 : 0;
   a.ws_logg = nullptr;
   a.ws_state = nullptr;

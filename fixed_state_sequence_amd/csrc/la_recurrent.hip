@@ -34,6 +34,7 @@ struct RecArgs {
   int H, T, dh, dv, dp, D;
   int phi, decay_kind;
   int out_f32;  // out is fp32 (else the input type)
+  int nonorm;   // read-out without the normaliser
   float eps;
 };
 
@@ -151,7 +152,7 @@ __global__ __launch_bounds__(NT) void recurrent_kernel(const RecArgs a) {
         n += s_red[w][tid];
         d += s_red[w][256];
       }
-      const float o = n / (d + a.eps);
+      const float o = a.nonorm ? n : n / (d + a.eps);
       if (a.out_f32) ogf[int64_t(t) * a.dv + tid] = o;
       else store_f32(o, og + int64_t(t) * a.dv + tid);
     }
@@ -200,6 +201,7 @@ hipError_t launch_recurrent(const Problem& p, const void* q, const void* k, cons
   a.W = p.W; a.decay = p.decay;
   a.H = p.H; a.T = p.T; a.dh = p.dh; a.dv = p.dv; a.dp = p.dp; a.D = p.D;
   a.phi = int(p.phi); a.decay_kind = int(p.decay_kind); a.eps = p.eps;
+  a.nonorm = p.nonorm;
   a.out_f32 = p.out_dtype == LA_F32 ? 1 : 0;
   switch (p.dtype) {
     case LA_F32: return launch_dt<float>(a, p.BH(), stream);

@@ -26,7 +26,8 @@
  *   z <- alpha_t z + beta_t phi(k_t)                z: d',       fp32
  *   o_t = (phi(q_t)^T S) / (phi(q_t)^T z + eps)     read-out after the update
  * with (alpha, beta) = (1, 1) for LA_DECAY_NONE, (a_t, 1) for LA_DECAY_SSD and
- * (g_t, 1 - g_t) for LA_GATE_RFA.
+ * (g_t, 1 - g_t) for LA_GATE_RFA; with LA_NORM_NONE the read-out is the
+ * numerator alone, o_t = phi(q_t)^T S.
  *
  * Feature maps:
  *   LA_PHI_ELU1: phi(x) = elu(x) + 1 (alpha = 1), element-wise, d' = d_h.
@@ -86,6 +87,16 @@ typedef enum {
   LA_GATE_RFA = 2     /* alpha = g_t, beta = 1 - g_t                     */
 } la_decay;
 
+typedef enum {
+  LA_NORM_SUM = 0,    /* o_t = phi(q_t)^T S / (phi(q_t)^T z + eps)            */
+  LA_NORM_NONE = 1    /* o_t = phi(q_t)^T S: the normaliser is left out of the
+                         read-out ([card] "Decaying linear attention with a
+                         scalar state (SSD)": the normaliser-free form, which
+                         relies on a normalisation layer after the read-out).
+                         z is still carried and updated, so a state can move
+                         between the two forms.                            */
+} la_norm;
+
 typedef struct la_desc {
   int B;                 /* batch (prefill) or number of sequences (decode), >= 1 */
   int H;                 /* heads, >= 1                                           */
@@ -102,6 +113,7 @@ typedef struct la_desc {
   float eps;             /* added to the denominator (finite); 1e-6 on the pages  */
   int chunk;             /* prefill chunk length, 0 = default (32); 32/64/128     */
   int segments;          /* prefill segments per (b, h), 0 = automatic            */
+  la_norm norm;          /* read-out form, LA_NORM_SUM (0) by default             */
 } la_desc;
 
 /* Feature dimension d' of a descriptor (d_h for ELU1, 2 rff_D for RFF), or -1

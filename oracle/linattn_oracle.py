@@ -113,7 +113,7 @@ def decay_coefficients(decay=None, gate=None):
 # The recurrence (the method's algorithm)
 # --------------------------------------------------------------------------
 
-def recurrence(fq, fk, v, alpha=None, beta=None, eps=1e-6, S0=None, z0=None):
+def recurrence(fq, fk, v, alpha=None, beta=None, eps=1e-6, S0=None, z0=None, normalize=True):
     """Causal linear attention as an RNN over t, in float64.
 
     For each t (in order):
@@ -124,6 +124,9 @@ def recurrence(fq, fk, v, alpha=None, beta=None, eps=1e-6, S0=None, z0=None):
     sum).  [lesson] Researcher level, Derivation (recurrence and read-out);
     [kb] section 3 causal sketch (eps added to the denominator);
     [card] Implementation sketch (decay on the old state only).
+    normalize=False returns the numerator S_t^T phi(q_t) alone, the
+    normaliser-free read-out of [card] "Decaying linear attention with a
+    scalar state (SSD)"; z is still carried.
 
     fq, fk: [..., T, d'] features; v: [..., T, d_v]; alpha, beta: [..., T]
     or None.  S0: [..., d', d_v], z0: [..., d'] (default zero state).
@@ -155,13 +158,16 @@ def recurrence(fq, fk, v, alpha=None, beta=None, eps=1e-6, S0=None, z0=None):
             z = z + new_z
         q_t = fq[..., t, :]
         num = np.einsum("...d,...dv->...v", q_t, S)
-        den = np.einsum("...d,...d->...", q_t, z)
-        o[..., t, :] = num / (den + eps)[..., None]
+        if normalize:
+            den = np.einsum("...d,...d->...", q_t, z)
+            o[..., t, :] = num / (den + eps)[..., None]
+        else:
+            o[..., t, :] = num
     return o, S, z
 
 
 def causal_linear_attention(q, k, v, phi="elu1", W=None, decay=None, gate=None,
-                            eps=1e-6, S0=None, z0=None):
+                            eps=1e-6, S0=None, z0=None, normalize=True):
     """Feature map, then the recurrence.  Returns (o, S, z) in float64.
 
     q, k: [..., H, T, d_h]; v: [..., H, T, d_v]; W: [H, D, d_h] for RFF.
@@ -170,10 +176,11 @@ def causal_linear_attention(q, k, v, phi="elu1", W=None, decay=None, gate=None,
     fq = features(q, phi, W)
     fk = features(k, phi, W)
     alpha, beta = decay_coefficients(decay, gate)
-    return recurrence(fq, fk, v, alpha, beta, eps, S0, z0)
+    return recurrence(fq, fk, v, alpha, beta, eps, S0, z0, normalize)
 
 
-def decode_step(q, k, v, S, z, phi="elu1", W=None, decay=None, gate=None, eps=1e-6):
+def decode_step(q, k, v, S, z, phi="elu1", W=None, decay=None, gate=None, eps=1e-6,
+                normalize=True):
     """One autoregressive step from state (S, z): q, k [..., H, d_h], v [..., H, d_v],
     decay/gate [..., H].  Returns (o [..., H, d_v], S', z').
 
@@ -182,7 +189,7 @@ def decode_step(q, k, v, S, z, phi="elu1", W=None, decay=None, gate=None, eps=1e
     q, k, v = _f64(q)[..., None, :], _f64(k)[..., None, :], _f64(v)[..., None, :]
     decay = None if decay is None else _f64(decay)[..., None]
     gate = None if gate is None else _f64(gate)[..., None]
-    o, S, z = causal_linear_attention(q, k, v, phi, W, decay, gate, eps, S, z)
+    o, S, z = causal_linear_attention(q, k, v, phi, W, decay, gate, eps, S, z, normalize)
     return o[..., 0, :], S, z
 
 
@@ -207,7 +214,7 @@ def decay_products(alpha, T):
     return P
 
 
-def masked_quadratic(fq, fk, v, alpha=None, beta=None, eps=1e-6):
+def masked_quadratic(fq, fk, v, alpha=None, beta=None, eps=1e-6, normalize=True):
     """o_t = sum_{s<=t} w_ts v_s / (sum_{s<=t} w_ts + eps) with
     w_ts = (phi(q_t) . phi(k_s)) * beta_s * prod_{r=s+1..t} alpha_r.
 
@@ -223,11 +230,13 @@ def masked_quadratic(fq, fk, v, alpha=None, beta=None, eps=1e-6):
     if beta is not None:
         w = w * _f64(beta)[..., None, :]
     num = w @ v
+    if not normalize:
+        return num
     den = w.sum(axis=-1)
     return num / (den + eps)[..., None]
 
 
-def kernel_attention_by_definition(fq, fk, v, alpha=None, beta=None, eps=1e-6):
+def kernel_attention_by_definition(fq, fk, v, alpha=None, beta=None, eps=1e-6, normalize=True):
     """Pure-Python double loop over one head: o_i = sum_{j<=i} sim_ij v_j /
     (sum_{j<=i} sim_ij + eps), sim_ij = phi(q_i).phi(k_j) times the decay
     weight.  Tiny inputs only.  [lesson] Researcher level, Derivation."""
@@ -247,11 +256,12 @@ def kernel_attention_by_definition(fq, fk, v, alpha=None, beta=None, eps=1e-6):
             for c in range(dv):
                 num[c] += sim * float(v[j, c])
         for c in range(dv):
-            out[i, c] = num[c] / (den + eps)
+            out[i, c] = num[c] / (den + eps) if normalize else num[c]
     return out
 
 
-def output_at(fq_t, fk, v, t, alpha=None, beta=None, eps=1e-6, S0=None, z0=None):
+def output_at(fq_t, fk, v, t, alpha=None, beta=None, eps=1e-6, S0=None, z0=None,
+              normalize=True):
     """The definition evaluated at one position t (O(t d)), including the
     carried-in state (S0, z0) decayed by prod_{r=0..t} alpha_r.
 
@@ -278,6 +288,8 @@ def output_at(fq_t, fk, v, t, alpha=None, beta=None, eps=1e-6, S0=None, z0=None)
         num = num + carry[..., None] * np.einsum("...d,...dv->...v", fq_t, _f64(S0))
     if z0 is not None:
         den = den + carry * np.einsum("...d,...d->...", fq_t, _f64(z0))
+    if not normalize:
+        return num
     return num / (den + eps)[..., None]
 
 

@@ -67,7 +67,7 @@ def test_plan_for_the_measured_prefills():
 
 @pytest.mark.parametrize("field,value", [("B", 0), ("H", -1), ("T", -5), ("d_h", 0), ("d_v", 0),
                                          ("dtype", 7), ("phi", 9), ("decay_kind", 5),
-                                         ("chunk", 48), ("segments", -1)])
+                                         ("chunk", 48), ("segments", -1), ("norm", 2)])
 def test_bad_descriptor_fields_are_rejected(field, value):
     d = desc()
     setattr(d, field, value)

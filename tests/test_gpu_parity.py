@@ -229,3 +229,53 @@ def test_decode_steps_vs_oracle(phi, dtype, gate):
         e = rel_err(o, o_ref)
         assert e < TOL[dtype], (step, e)
     assert rel_err(S, S_ref) < TOL[dtype] and rel_err(z, z_ref) < TOL[dtype]
+
+
+# ---------------------------------------------- the normaliser-free read-out
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("decay", [None, "ssd", "rfa"])
+def test_prefill_unnormalised_mfma(d, decay):
+    # o_t = phi(q_t)^T S_t: the chunked path with the division left out, over
+    # one, the default and three segments
+    dev = gpu_device()
+    x = I.prefill_inputs(2, 3, 301, d, dtype="bf16", seed=7 + d, decay=decay)
+    o_ref, S_ref, z_ref = oracle_prefill(x, normalize=False)
+    for segments in (1, 0, 3):
+        out, S, z = run_prefill(x, dev, segments=segments, normalize=False)
+        e = (rel_err(out, o_ref), rel_err(S, S_ref), rel_err(z, z_ref))
+        print("unnormalised", d, decay, segments, e)
+        assert max(e) < TOL["bf16"], e
+
+
+@pytest.mark.parametrize("phi", ["elu1", "rff"])
+def test_prefill_unnormalised_per_token_fp32(phi):
+    dev = gpu_device()
+    x = I.prefill_inputs(2, 2, 70, 32, dtype="f32", seed=3, decay="rfa")
+    W = I.rff_projection(2, 16, 32, seed=4) if phi == "rff" else None
+    out, S, z = run_prefill(x, dev, phi=phi, W=None if W is None else W.to(dev),
+                            normalize=False)
+    o_ref, S_ref, z_ref = oracle_prefill(x, phi=phi, W=W, normalize=False)
+    e = (rel_err(out, o_ref), rel_err(S, S_ref), rel_err(z, z_ref))
+    assert max(e) < TOL["f32"], e
+
+
+@pytest.mark.parametrize("phi,dh,D", [("rff", 64, 64), ("elu1", 128, 0)])
+def test_decode_unnormalised(phi, dh, D):
+    dev = gpu_device()
+    N, H = 9, 3
+    W = I.rff_projection(H, D, dh, seed=1) if phi == "rff" else None
+    dp = 2 * D if phi == "rff" else dh
+    S, z = la.state_init(N, H, dp, 64, dev)
+    S_ref, z_ref = np.zeros((N, H, dp, 64)), np.zeros((N, H, dp))
+    for step in range(3):
+        st = I.rfa_decode_step_inputs(N, H, dh, 64, step=step, seed=2)
+        o = la.decode_step(st.q.to(dev), st.k.to(dev), st.v.to(dev), S, z, phi=phi,
+                           W=None if W is None else W.to(dev), gate=st.gate.to(dev),
+                           normalize=False)
+        torch.cuda.synchronize()
+        o_ref, S_ref, z_ref = O.decode_step(st.q, st.k, st.v, S_ref, z_ref, phi=phi, W=W,
+                                            gate=st.gate, normalize=False)
+        assert rel_err(o, o_ref) < TOL["f32"]
+    assert rel_err(S, S_ref) < TOL["f32"] and rel_err(z, z_ref) < TOL["f32"]
+

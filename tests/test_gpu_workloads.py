@@ -10,7 +10,8 @@ the input type), against the fp64 oracle.
   closed form.
 * long-context prefill, B=1, H=8, T=102400, d=128, bf16 scaled by 1/sqrt(2):
   two heads end to end, sampled positions (chunk, sub-segment and segment
-  edges among them) of the other six, every final state in closed form.
+  edges among them) of the other six, every final state in closed form; and
+  the same workload with the normaliser-free read-out, two heads end to end.
 
 A 16-bit output is the fp32 result rounded to nearest even, so each element
 may sit up to half an ulp (2^-8 relative, worst case in a binade) from the
@@ -43,7 +44,7 @@ def rms(x):
     return float(np.sqrt(np.mean(np.asarray(x, dtype=np.float64) ** 2)))
 
 
-def run_workload(name):
+def run_workload(name, normalize=True):
     """Inputs drawn on the host (seed 0) and the prefill as the benchmark runs it."""
     dev = gpu_device()
     x = I.workload_inputs(name, seed=0)
@@ -53,7 +54,7 @@ def run_workload(name):
     chunk, segments, path = la.prefill_plan(desc)
     assert path == 1
     g = lambda t: None if t is None else t.to(dev)
-    out, S, z = la.prefill(g(x.q), g(x.k), g(x.v), decay=g(x.decay))
+    out, S, z = la.prefill(g(x.q), g(x.k), g(x.v), decay=g(x.decay), normalize=normalize)
     torch.cuda.synchronize()
     assert out.dtype == torch.bfloat16
     print(name, "plan", chunk, segments)
@@ -144,3 +145,18 @@ def test_long_prefill_b1_h8_t102400_d128_sampled():
     print("long prefill 1x8x102400x128 full", e_full, "sampled", e_s,
           "worst per-position", per_pos)
     assert max(e_full + e_s) < TOL["bf16"], (e_full, e_s)
+
+
+def test_long_prefill_unnormalised_two_heads():
+    """The long-context workload with the normaliser-free read-out, in the
+    benchmark's launch configuration: two heads end to end against the
+    oracle's numerator, and their final states."""
+    x, out, S, z, _ = run_workload("long_prefill_b1_h8_t102400_d128", normalize=False)
+    hs = [3, 6]
+    o_ref, S_ref, z_ref = O.causal_linear_attention(x.q[0, hs], x.k[0, hs], x.v[0, hs],
+                                                    normalize=False)
+    r = rms(o_ref)
+    e = (excess_err(out[0, hs], o_ref, r), rel_err(S[0, hs], S_ref), rel_err(z[0, hs], z_ref))
+    print("long prefill unnormalised", e)
+    assert max(e) < TOL["bf16"], e
+

@@ -255,6 +255,49 @@ def test_output_at_matches_recurrence_with_initial_state(kind):
     np.testing.assert_allclose(zf, z, rtol=1e-12)
 
 
+# ---------------------------------------------- the normaliser-free read-out
+
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("T,dp,dv", [(1, 1, 1), (5, 4, 4), (9, 3, 5)])
+def test_unnormalised_recurrence_equals_bruteforce_numerator(kind, T, dp, dv):
+    # o_t = sum_{s<=t} w_ts v_s with no division: the recurrence's numerator
+    # against the double loop over the definition
+    fq, fk, v = rand(T, dp), rand(T, dp), rand(T, dv)
+    alpha, beta = coeffs(kind, (T,))
+    o, _, _ = O.recurrence(fq, fk, v, alpha, beta, normalize=False)
+    ref = O.kernel_attention_by_definition(fq, fk, v, alpha, beta, normalize=False)
+    np.testing.assert_allclose(o, ref, rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("kind", KINDS)
+def test_unnormalised_masked_quadratic_and_output_at(kind):
+    T, d, dv = 40, 6, 4
+    fq, fk, v = O.phi_elu1(rand(2, T, d)), O.phi_elu1(rand(2, T, d)), rand(2, T, dv)
+    alpha, beta = coeffs(kind, (2, T))
+    o, _, _ = O.recurrence(fq, fk, v, alpha, beta, normalize=False)
+    np.testing.assert_allclose(o, O.masked_quadratic(fq, fk, v, alpha, beta, normalize=False),
+                               rtol=1e-11, atol=1e-12)
+    for t in (0, 13, T - 1):
+        np.testing.assert_allclose(O.output_at(fq[:, t], fk, v, t, alpha, beta, normalize=False),
+                                   o[:, t], rtol=1e-11, atol=1e-12)
+
+
+def test_unnormalised_closed_forms():
+    # t = 0: (phi(q_0).phi(k_0)) v_0 exactly; with v = 1 the numerator is the
+    # unweighted score sum, the plain cumulative sum of phi(q_t).phi(k_s)
+    T, d = 11, 5
+    fq, fk, v = O.phi_elu1(rand(T, d)), O.phi_elu1(rand(T, d)), rand(T, 3)
+    o, _, _ = O.recurrence(fq, fk, v, normalize=False)
+    np.testing.assert_allclose(o[0], (fq[0] @ fk[0]) * v[0], rtol=1e-15)
+    ones, _, _ = O.recurrence(fq, fk, np.ones((T, 1)), normalize=False)
+    ref = np.array([sum(float(fq[t] @ fk[s]) for s in range(t + 1)) for t in range(T)])
+    np.testing.assert_allclose(ones[:, 0], ref, rtol=1e-13)
+    # the two read-outs share the state: same S, z either way
+    _, S1, z1 = O.recurrence(fq, fk, v)
+    _, S2, z2 = O.recurrence(fq, fk, v, normalize=False)
+    assert np.array_equal(S1, S2) and np.array_equal(z1, z2)
+
+
 # ------------------------------------------------------ the pages' own numbers
 
 def test_worked_example_reproduces_printed_output():
