@@ -30,6 +30,7 @@ Printed as one JSON line:
                same with 1024 sequences so the state (545 MB) exceeds the
                256 MB last-level cache;
   normaliser_free  the same prefill with the read-out phi(q)^T S alone;
+  noncausal    the same prefill in the non-causal form;
   cpu_baseline the fp64 oracle (the CPU reference the tests check against),
                on a bounded sample of the same prefill workload, one worker
                process per head.
@@ -134,12 +135,13 @@ def _events(torch):
     return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
 
-def bench_prefill(torch, la, I, steps, warmup, normalize=True, stages=True):
+def bench_prefill(torch, la, I, steps, warmup, normalize=True, stages=True, causal=True):
     dev = torch.device("cuda:0")
     B, H, T, d = PF["B"], PF["H"], PF["T"], PF["d"]
     x = I.prefill_inputs(B, H, T, d, dtype="bf16", seed=0, scale=PF["scale"], device=dev)
     q, k, v = x.q, x.k, x.v
-    desc = la.make_desc(B, H, T, d, d, la._lib.LA_BF16, eps=PF["eps"], normalize=normalize)
+    desc = la.make_desc(B, H, T, d, d, la._lib.LA_BF16, eps=PF["eps"], normalize=normalize,
+                        causal=causal)
     chunk, segments, path = la.prefill_plan(desc)
     if path != 1:
         raise RuntimeError("the long-context prefill did not take the chunked MFMA path")
@@ -312,6 +314,8 @@ def main(argv=None):
 
     print("[bench] prefill, normaliser-free read-out", file=sys.stderr, flush=True)
     pf_nn = bench_prefill(torch, la, I, a.steps, a.warmup, normalize=False, stages=False)
+    print("[bench] prefill, non-causal form", file=sys.stderr, flush=True)
+    pf_nc = bench_prefill(torch, la, I, a.steps, a.warmup, stages=False, causal=False)
     cp = hbm_copy(torch)
     dec = dec_big = None
     if not a.no_decode:
@@ -355,6 +359,12 @@ def main(argv=None):
             "ms_per_step": pf_nn["ms"], "tokens_per_s": B * T / (pf_nn["ms"] * 1e-3),
             "GBs": step_bytes / (pf_nn["ms"] * 1e-3) / 1e9,
             "hbm_frac": step_bytes / (pf_nn["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "noncausal": {
+            "workload": "the same prefill in the non-causal form: the whole sequence into "
+                        "the state, then every token reads it out",
+            "ms_per_step": pf_nc["ms"], "tokens_per_s": B * T / (pf_nc["ms"] * 1e-3),
+            "GBs": step_bytes / (pf_nc["ms"] * 1e-3) / 1e9,
+            "hbm_frac": step_bytes / (pf_nc["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS},
     }
     if dec is not None:
         res["decode"] = {

@@ -54,10 +54,11 @@ def _need(t, name, device=None, dtype=None, shape=None):
 
 def make_desc(B, H, T, d_h, d_v, dtype_code, phi="elu1", W=None, rff_D=None, decay=None,
               gate=None, eps=1e-6, chunk=0, segments=0, out_dtype_code=None,
-              normalize=True) -> _lib.LaDesc:
+              normalize=True, causal=True) -> _lib.LaDesc:
     """Build an `la_desc`.  `decay` (SSD a_t) and `gate` (RFA g_t) are exclusive;
     `out_dtype_code` defaults to the input type; `normalize=False` selects the
-    read-out without the normaliser (LA_NORM_NONE)."""
+    read-out without the normaliser (LA_NORM_NONE); `causal=False` the
+    non-causal prefill."""
     d = _lib.LaDesc()
     d.B, d.H, d.T, d.d_h, d.d_v = int(B), int(H), int(T), int(d_h), int(d_v)
     d.dtype = int(dtype_code)
@@ -81,6 +82,7 @@ def make_desc(B, H, T, d_h, d_v, dtype_code, phi="elu1", W=None, rff_D=None, dec
     d.eps = float(eps)
     d.chunk, d.segments = int(chunk), int(segments)
     d.norm = _lib.LA_NORM_SUM if normalize else _lib.LA_NORM_NONE
+    d.noncausal = 0 if causal else 1
     return d
 
 
@@ -104,7 +106,7 @@ def state_init(B: int, H: int, d_prime: int, d_v: int, device="cuda") -> Tuple["
 
 
 def _prefill_desc(q, k, v, phi, W, decay, gate, eps, chunk, segments, out_dtype=None,
-                  normalize=True):
+                  normalize=True, causal=True):
     torch = _torch()
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, n, device=q.device, dtype=q.dtype)
@@ -120,7 +122,7 @@ def _prefill_desc(q, k, v, phi, W, decay, gate, eps, chunk, segments, out_dtype=
         if a is not None:
             _need(a, n, device=q.device, dtype=torch.float32, shape=(B, H, T))
     desc = make_desc(B, H, T, d_h, d_v, _dtype_code(q.dtype), phi, W, None, decay, gate, eps,
-                     chunk, segments, _dtype_code(out_dtype or q.dtype), normalize)
+                     chunk, segments, _dtype_code(out_dtype or q.dtype), normalize, causal)
     return desc, (B, H, T, d_h, d_v)
 
 
@@ -140,19 +142,21 @@ def prefill_plan(desc: _lib.LaDesc):
 
 def prefill(q, k, v, *, phi: str = "elu1", W=None, decay=None, gate=None, eps: float = 1e-6,
             state: Optional[tuple] = None, chunk: int = 0, segments: int = 0, out=None,
-            workspace=None, out_dtype=None, normalize: bool = True):
+            workspace=None, out_dtype=None, normalize: bool = True, causal: bool = True):
     """Causal linear attention over [B, H, T, d] inputs on the GPU.
 
     Returns (out, S, z).  If `state=(S, z)` is given the recurrence continues
     from it and the final state is written back into those tensors (in place);
     otherwise a zero state is allocated.  `out_dtype` is q's dtype (default)
     or torch.float32.  `normalize=False` returns the numerator phi(q)^T S
-    alone (LA_NORM_NONE); z is still carried.
+    alone (LA_NORM_NONE); z is still carried.  `causal=False` is the
+    non-causal form: the state takes in the whole sequence, then every token
+    reads it out.
     """
     torch = _torch()
     out_dtype = out_dtype or q.dtype
     desc, (B, H, T, d_h, d_v) = _prefill_desc(q, k, v, phi, W, decay, gate, eps, chunk, segments,
-                                              out_dtype, normalize)
+                                              out_dtype, normalize, causal)
     dp = feature_dim(d_h, phi, desc.rff_D)
     if state is None:
         S, z = state_init(B, H, dp, d_v, q.device)
@@ -174,11 +178,11 @@ def prefill(q, k, v, *, phi: str = "elu1", W=None, decay=None, gate=None, eps: f
 
 
 def prefill_stage(stage: int, q, k, v, S, z, out, workspace, *, phi="elu1", W=None, decay=None,
-                  gate=None, eps=1e-6, chunk=0, segments=0, normalize=True):
+                  gate=None, eps=1e-6, chunk=0, segments=0, normalize=True, causal=True):
     """Run one of la_prefill's three stages (1 segment states, 2 scan, 3 outputs);
     out's dtype selects the output type."""
     desc, _ = _prefill_desc(q, k, v, phi, W, decay, gate, eps, chunk, segments, out.dtype,
-                            normalize)
+                            normalize, causal)
     nws = prefill_workspace_size(desc)
     _lib.check(_lib.lib().la_prefill_stage(ctypes.byref(desc), int(stage), _ptr(q), _ptr(k), _ptr(v),
                                            _ptr(S), _ptr(z), _ptr(out),

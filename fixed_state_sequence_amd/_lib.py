@@ -29,7 +29,7 @@ class LaDesc(ctypes.Structure):
         ("rff_D", ctypes.c_int), ("rff_W", ctypes.c_void_p),
         ("decay_kind", ctypes.c_int), ("decay", ctypes.c_void_p),
         ("eps", ctypes.c_float), ("chunk", ctypes.c_int), ("segments", ctypes.c_int),
-        ("norm", ctypes.c_int),
+        ("norm", ctypes.c_int), ("noncausal", ctypes.c_int),
     ]
 
 

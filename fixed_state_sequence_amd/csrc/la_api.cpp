@@ -71,6 +71,10 @@ la_status check_desc(const la_desc* d, bool prefill, la::Problem* p) {
   if (!std::isfinite(d->eps)) return fail(LA_EINVAL, "eps must be finite");
   if (d->norm != LA_NORM_SUM && d->norm != LA_NORM_NONE)
     return fail(LA_EINVAL, "unknown read-out form %d", int(d->norm));
+  if (d->noncausal != 0 && d->noncausal != 1)
+    return fail(LA_EINVAL, "noncausal must be 0 or 1 (got %d)", d->noncausal);
+  if (d->noncausal && d->decay_kind != LA_DECAY_NONE)
+    return fail(LA_EINVAL, "the non-causal form takes no decay or gate");
   if (prefill) {
     if (d->chunk != 0 && d->chunk != 32 && d->chunk != 64 && d->chunk != 128)
       return fail(LA_EINVAL, "chunk must be 0, 32, 64 or 128 (got %d)", d->chunk);
@@ -88,6 +92,7 @@ la_status check_desc(const la_desc* d, bool prefill, la::Problem* p) {
   p->dtype = d->dtype; p->out_dtype = d->out_dtype; p->phi = d->phi; p->D = d->rff_D; p->W = d->rff_W;
   p->decay_kind = d->decay_kind; p->decay = d->decay; p->eps = d->eps;
   p->nonorm = d->norm == LA_NORM_NONE ? 1 : 0;
+  p->noncausal = d->noncausal;
   p->chunk = d->chunk ? d->chunk : 32;
   p->segments = 1;
   p->path = 0;
@@ -225,6 +230,7 @@ la_status la_decode_step(const la_desc* desc, const void* q, const void* k, cons
                          float* S, float* z, void* out, void* stream) {
   la::Problem p;
   LA_TRY(check_desc(desc, false, &p));
+  if (p.noncausal) return fail(LA_EINVAL, "decode is causal: noncausal must be 0");
   LA_TRY(check_ptr(q, "q"));
   LA_TRY(check_ptr(k, "k"));
   LA_TRY(check_ptr(v, "v"));

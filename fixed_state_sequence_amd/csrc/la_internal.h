@@ -24,6 +24,7 @@ struct Problem {
   const float* decay = nullptr; // prefill [B,H,T], decode [B,H]
   float eps = 1e-6f;
   int nonorm = 0;               // 1: read-out without the normaliser (LA_NORM_NONE)
+  int noncausal = 0;            // 1: non-causal prefill (every output reads the whole state)
   int chunk = 64;               // prefill chunk length (MFMA path)
   int segments = 1;             // prefill segments per (b,h) (MFMA path)
   int path = 0;                 // 1 = chunked MFMA, 0 = per-token recurrent kernel

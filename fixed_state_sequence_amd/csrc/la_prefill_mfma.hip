@@ -287,6 +287,7 @@ struct PfArgs {
   int nslot;         // nsub nseg
   int out_f32;       // out is fp32 (else the input type)
   int nonorm;        // read-out without the normaliser
+  int nc;            // non-causal: every output reads the whole sequence's state
   float eps;
 };
 
@@ -296,24 +297,26 @@ struct PfArgs {
 // (rows past the end of the sequence read the last row) so that the compiler
 // can count the loads still in flight exactly when a later chunk's data is
 // used; clean_chunk() then zeroes those rows (and sets their decay to 1).
-template <int RPT, int ND, bool HAS_Q>
+template <int RPT, int ND, bool HAS_Q, bool HAS_KV = true>
 struct RawChunk {
-  u32x4 q[HAS_Q ? RPT : 1], k[RPT], v[RPT];
+  u32x4 q[HAS_Q ? RPT : 1], k[HAS_KV ? RPT : 1], v[HAS_KV ? RPT : 1];
   float d[ND];
 };
 
-template <int C, int D, int RPT, int ND, bool HAS_Q, int DECAY, typename DT>
-__device__ __forceinline__ void fetch_chunk(RawChunk<RPT, ND, HAS_Q>& r, const DT* qg, const DT* kg,
-                                            const DT* vg, const float* dg, int tok0, int T,
-                                            int rg, int fb, int lane) {
+template <int C, int D, int RPT, int ND, bool HAS_Q, int DECAY, typename DT, bool HAS_KV>
+__device__ __forceinline__ void fetch_chunk(RawChunk<RPT, ND, HAS_Q, HAS_KV>& r, const DT* qg,
+                                            const DT* kg, const DT* vg, const float* dg, int tok0,
+                                            int T, int rg, int fb, int lane) {
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
     const int t = min(tok0 + RPT * rg + i, T - 1);
     // 32-bit element offsets within the (b, h) slab (T D < 2^31 is checked on the host)
     const uint32_t off = uint32_t(t) * D + 8 * fb;
     if constexpr (HAS_Q) r.q[i] = *reinterpret_cast<const u32x4*>(qg + off);
-    r.k[i] = *reinterpret_cast<const u32x4*>(kg + off);
-    r.v[i] = *reinterpret_cast<const u32x4*>(vg + off);
+    if constexpr (HAS_KV) {
+      r.k[i] = *reinterpret_cast<const u32x4*>(kg + off);
+      r.v[i] = *reinterpret_cast<const u32x4*>(vg + off);
+    }
   }
   if constexpr (DECAY != 0) {
 #pragma unroll
@@ -324,16 +327,18 @@ __device__ __forceinline__ void fetch_chunk(RawChunk<RPT, ND, HAS_Q>& r, const D
 // Rows past the end of the sequence become 0 and decay values of tokens
 // outside the chunk or the sequence become 1 (the loads read in-bounds
 // stand-ins).  The row pass runs only for the chunk holding the end.
-template <int C, int RPT, int ND, bool HAS_Q, int DECAY>
-__device__ __forceinline__ void clean_chunk(RawChunk<RPT, ND, HAS_Q>& r, int tok0, int T, int rg,
-                                            int lane) {
+template <int C, int RPT, int ND, bool HAS_Q, int DECAY, bool HAS_KV>
+__device__ __forceinline__ void clean_chunk(RawChunk<RPT, ND, HAS_Q, HAS_KV>& r, int tok0, int T,
+                                            int rg, int lane) {
   if (tok0 + C > T) {
 #pragma unroll
     for (int i = 0; i < RPT; ++i)
       if (tok0 + RPT * rg + i >= T) {
         if constexpr (HAS_Q) r.q[i] = u32x4{0u, 0u, 0u, 0u};
-        r.k[i] = u32x4{0u, 0u, 0u, 0u};
-        r.v[i] = u32x4{0u, 0u, 0u, 0u};
+        if constexpr (HAS_KV) {
+          r.k[i] = u32x4{0u, 0u, 0u, 0u};
+          r.v[i] = u32x4{0u, 0u, 0u, 0u};
+        }
       }
   }
   if constexpr (DECAY != 0) {
@@ -672,7 +677,11 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(const PfArgs a) {
 // and z).  With two LDS buffers the producers stage chunk c + 1 while the
 // consumers compute chunk c, one barrier per chunk; each role fits in 256
 // registers, so a producer and a consumer wave share every SIMD.
-template <int D, int C, int DECAY, typename DT>
+// NC: the non-causal read-out.  Every segment starts from the state of the
+// whole sequence (stage 1 and the scan leave it in S, z), so the producers
+// stage phi(q) and the denominators only, and the consumers do the read-out
+// alone: no scores, no P V, no fold.
+template <int D, int C, int DECAY, typename DT, bool NC = false>
 __global__ __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void output_kernel(const PfArgs a) {
   constexpr bool VS = __is_same(DT, f16_t);   // fp16 v needs a bf16 low part too
@@ -689,10 +698,11 @@ void output_kernel(const PfArgs a) {
   // (which fold w phi(k) as bf16 high + low parts); the output stage then
   // folds only the high parts, as its state feeds this segment's outputs
   // alone.  A single segment folds both parts and writes the final state.
-  const bool fin = nseg == 1;
-  const float* Sstart = nseg > 1 ? a.ws_state + (int64_t(bh) * a.nslot + a.nsub * seg) * (D * D + D)
-                                 : a.S + int64_t(bh) * D * D;
-  const float* zstart = nseg > 1 ? Sstart + D * D : a.z + int64_t(bh) * D;
+  const bool fin = !NC && nseg == 1;
+  const bool from_ws = !NC && nseg > 1;
+  const float* Sstart = from_ws ? a.ws_state + (int64_t(bh) * a.nslot + a.nsub * seg) * (D * D + D)
+                                : a.S + int64_t(bh) * D * D;
+  const float* zstart = from_ws ? Sstart + D * D : a.z + int64_t(bh) * D;
   auto buffer = [&](int i) -> char* { return smem + (G::NBUF == 2 ? (i & 1) * G::BUF3 : 0); };
 
   // the role is uniform per wave: tell the compiler, so the two roles are
@@ -718,7 +728,8 @@ void output_kernel(const PfArgs a) {
     *reinterpret_cast<f32x4*>(zf) = *reinterpret_cast<const f32x4*>(zstart + 8 * fb);
     *reinterpret_cast<f32x4*>(zf + 4) = *reinterpret_cast<const f32x4*>(zstart + 8 * fb + 4);
 
-    auto fetch = [&](RawChunk<G::RPT, G::ND, true>& r, int c) {
+    using Raw = RawChunk<G::RPT, G::ND, true, !NC>;
+    auto fetch = [&](Raw& r, int c) {
       fetch_chunk<C, D, G::RPT, G::ND, true, DECAY>(r, qg, kg, vg, dg, c * C, a.T, rg, fb, lane);
     };
     // [A] chunk c into buf: phi(q), phi(k) and w phi(k) high/low, v tiles;
@@ -728,7 +739,7 @@ void output_kernel(const PfArgs a) {
     // 1s are taken off z without decay) and their outputs are not stored.
     // Past the segment's last chunk this stages a repeat of it into a buffer
     // nobody reads, so that the loads are the same on every path.
-    auto stage = [&](RawChunk<G::RPT, G::ND, true>& raw, int c, char* buf) -> float {
+    auto stage = [&](Raw& raw, int c, char* buf) -> float {
       const int tok0 = c * C;
       clean_chunk<C, G::RPT, G::ND, true, DECAY>(raw, tok0, a.T, rg, lane);
       float lo = 0.f, hi = 0.f, ltot = 0.f;
@@ -736,6 +747,26 @@ void output_kernel(const PfArgs a) {
       float* Ll = reinterpret_cast<float*>(buf + G::B_L);
       float* Bl = reinterpret_cast<float*>(buf + G::B_B);
       float* denl = reinterpret_cast<float*>(buf + G::B_DEN);
+      if constexpr (NC) {
+        // phi(q) and phi(q) . z of the whole sequence
+#pragma unroll
+        for (int i = 0; i < G::RPT; ++i) {
+          const int r = G::RPT * rg + i;
+          float qx[8];
+          unpack8(raw.q[i], qx, DT{});
+          float den = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            qx[e] = elu1_fast(qx[e]);
+            den = fmaf(qx[e], zf[e], den);
+          }
+          row_write_perm<D>(buf + G::B_Q, r, fb, pack8(qx));
+          den = row_sum<G::FB>(den);
+          if (fb == 0) denl[r] = den;
+        }
+        fetch(raw, min(c + G::PDEPTH, c1 - 1));
+        return 0.f;
+      }
       float dz[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < G::RPT; ++i) {
@@ -807,6 +838,7 @@ void output_kernel(const PfArgs a) {
     };
     // z after chunk c (staged in buf): zf = e^{ltot} zf + sum of the increments
     auto zstep = [&](int c, const char* buf, float ltot) {
+      if constexpr (NC) return;   // z is the whole sequence's throughout
       const float* dzl = reinterpret_cast<const float*>(buf + G::B_DZ);
       const float gam = DECAY ? __expf(ltot) : 1.f;
       const float pad = DECAY ? 0.f : float(max(c * C + C - a.T, 0));
@@ -819,7 +851,7 @@ void output_kernel(const PfArgs a) {
       }
     };
 
-    RawChunk<G::RPT, G::ND, true> raw[G::PDEPTH];
+    Raw raw[G::PDEPTH];
 #pragma unroll
     for (int j = 0; j < G::PDEPTH; ++j) fetch(raw[j], min(c0 + j, c1 - 1));
     if constexpr (G::NBUF == 2) {
@@ -878,6 +910,7 @@ void output_kernel(const PfArgs a) {
       u32x4 vh[G::KT], vl[G::KT];
 #pragma unroll
       for (int kk = 0; kk < G::KT; ++kk) {
+        if constexpr (NC) break;
         vh[kk] = tr_operand<D>(buf + G::B_VH, 16 * kk, 32 * wave, lane);
         if constexpr (VS) vl[kk] = tr_operand<D>(buf + G::B_VL, 16 * kk, 32 * wave, lane);
       }
@@ -896,9 +929,9 @@ void output_kernel(const PfArgs a) {
           const u32x4 sf = {pack_bf16(sa[j0 + 0], sa[j0 + 1]), pack_bf16(sa[j0 + 2], sa[j0 + 3]),
                             pack_bf16(sa[j0 + 4], sa[j0 + 5]), pack_bf16(sa[j0 + 6], sa[j0 + 7])};
           o = mfma(sf, qf, o);
-          p = mfma(row_operand<D>(buf + G::B_K, 32 * tb + n, 2 * ks + g), qf, p);
+          if constexpr (!NC) p = mfma(row_operand<D>(buf + G::B_K, 32 * tb + n, 2 * ks + g), qf, p);
         }
-        if (tok0 < G::EXACT)
+        if (!NC && tok0 < G::EXACT)
           p = low_scores<D, G::KS>(buf + G::B_KR, buf + G::B_Q, 32 * tb + n, tl, g, p);
         float lct = 0.f;
         if constexpr (DECAY != 0) {
@@ -908,6 +941,7 @@ void output_kernel(const PfArgs a) {
         float dsum = 0.f;
 #pragma unroll
         for (int sb = tb; sb >= 0; --sb) {
+          if constexpr (NC) break;
           if (sb != tb) {
             p = f32x16{};
 #pragma unroll
@@ -945,7 +979,7 @@ void output_kernel(const PfArgs a) {
             o = mfma(vl[2 * sb + 1], ph1, o);
           }
         }
-        dsum = swap_sum32(dsum);
+        if constexpr (!NC) dsum = swap_sum32(dsum);
         const float inv = a.nonorm ? 1.f : __builtin_amdgcn_rcpf(denl[tl] + dsum + a.eps);
         const int t = tok0 + tl;
         if (t < a.T) {
@@ -992,8 +1026,10 @@ void output_kernel(const PfArgs a) {
           }
         }
       };
-      if (fin) fold(std::true_type{});
-      else fold(std::false_type{});
+      if constexpr (!NC) {
+        if (fin) fold(std::true_type{});
+        else fold(std::false_type{});
+      }
     };
 
     if constexpr (G::NBUF == 2) {
@@ -1033,16 +1069,22 @@ void output_kernel(const PfArgs a) {
 template <int D, int C, int DECAY, typename DT>
 hipError_t launch3(const PfArgs& a, int64_t BH, int stage, hipStream_t st) {
   using G = Cfg<D, C, __is_same(DT, f16_t)>;
+  // a causal prefill of one segment needs neither stage 1 nor the scan (the
+  // output stage carries the state itself); a non-causal one always does
+  const bool scan = a.nseg > 1 || a.nc;
   if (stage == 1) {
-    if (a.nseg <= 1) return hipSuccess;
+    if (!scan) return hipSuccess;
     segment_state_kernel<D, C, DECAY, DT><<<dim3(unsigned(BH * a.nslot)), dim3(G::NT), 0, st>>>(a);
   } else if (stage == 2) {
-    if (a.nseg <= 1) return hipSuccess;
+    if (!scan) return hipSuccess;
     const int per_bh = (D * D + D + 255) / 256;
     if (a.nslot <= 32)
       segment_scan_kernel<D, 32><<<dim3(unsigned(BH * per_bh)), dim3(256), 0, st>>>(a);
     else
       segment_scan_kernel<D, 64><<<dim3(unsigned(BH * per_bh)), dim3(256), 0, st>>>(a);
+  } else if (a.nc) {
+    if constexpr (DECAY != 0) return hipErrorInvalidValue;   // rejected on the host
+    else output_kernel<D, C, 0, DT, true><<<dim3(unsigned(BH * a.nseg)), dim3(2 * G::NT), 0, st>>>(a);
   } else {
     output_kernel<D, C, DECAY, DT><<<dim3(unsigned(BH * a.nseg)), dim3(2 * G::NT), 0, st>>>(a);
   }
@@ -1117,7 +1159,7 @@ int mfma_default_segments(const Problem& p) {
 }
 
 size_t mfma_workspace_bytes(const Problem& p) {
-  if (p.path != 1 || p.segments <= 1) return 0;
+  if (p.path != 1 || (p.segments <= 1 && !p.noncausal)) return 0;
   const size_t E = size_t(p.dv) * p.dv + p.dv;
   const size_t n = size_t(p.BH()) * split_of(p).nslot;
   return n * E * sizeof(float) + ((n * sizeof(float) + 255) / 256) * 256;
@@ -1137,10 +1179,11 @@ hipError_t launch_mfma_stage(const Problem& p, int stage, const void* q, const v
   a.nslot = sp.nslot;
   a.eps = p.eps;
   a.nonorm = p.nonorm;
+  a.nc = p.noncausal;
   a.out_f32 = p.out_dtype == LA_F32 ? 1 : 0;
   a.ws_logg = nullptr;
   a.ws_state = nullptr;
-  if (a.nseg > 1) {
+  if (a.nseg > 1 || a.nc) {
     const size_t E = size_t(p.dv) * p.dv + p.dv;
     a.ws_state = static_cast<float*>(ws);
     a.ws_logg = a.ws_state + size_t(p.BH()) * a.nslot * E;

@@ -35,6 +35,7 @@ struct RecArgs {
   int phi, decay_kind;
   int out_f32;  // out is fp32 (else the input type)
   int nonorm;   // read-out without the normaliser
+  int mode;     // 0 causal: update, then read out; 1 update only; 2 read-out only
   float eps;
 };
 
@@ -118,12 +119,14 @@ __global__ __launch_bounds__(NT) void recurrent_kernel(const RecArgs a) {
     for (int i = 0; i < NF4; ++i) {
       const int f = r0 + i * rpp;
       if (f < a.dp) {
-        const float kb = beta * s_fk[f];
+        if (a.mode != 2) {
+          const float kb = beta * s_fk[f];
+          st[i].x = alpha * st[i].x + kb * v4.x;
+          st[i].y = alpha * st[i].y + kb * v4.y;
+          st[i].z = alpha * st[i].z + kb * v4.z;
+          st[i].w = alpha * st[i].w + kb * v4.w;
+        }
         const float qf = s_fq[f];
-        st[i].x = alpha * st[i].x + kb * v4.x;
-        st[i].y = alpha * st[i].y + kb * v4.y;
-        st[i].z = alpha * st[i].z + kb * v4.z;
-        st[i].w = alpha * st[i].w + kb * v4.w;
         num.x += qf * st[i].x;
         num.y += qf * st[i].y;
         num.z += qf * st[i].z;
@@ -132,7 +135,7 @@ __global__ __launch_bounds__(NT) void recurrent_kernel(const RecArgs a) {
     }
     float dpart = 0.f;
     if (tid < a.dp) {
-      zr = alpha * zr + beta * s_fk[tid];
+      if (a.mode != 2) zr = alpha * zr + beta * s_fk[tid];
       dpart = s_fq[tid] * zr;
     }
     for (int off = ncg; off < 64; off <<= 1) {
@@ -145,7 +148,7 @@ __global__ __launch_bounds__(NT) void recurrent_kernel(const RecArgs a) {
     if (lane < ncg) *reinterpret_cast<float4*>(&s_red[wave][4 * cg]) = num;
     if (lane == 0) s_red[wave][256] = dpart;
     __syncthreads();
-    if (tid < a.dv) {
+    if (tid < a.dv && a.mode != 1) {
       float n = 0.f, d = 0.f;
 #pragma unroll
       for (int w = 0; w < NT / 64; ++w) {
@@ -203,12 +206,21 @@ hipError_t launch_recurrent(const Problem& p, const void* q, const void* k, cons
   a.phi = int(p.phi); a.decay_kind = int(p.decay_kind); a.eps = p.eps;
   a.nonorm = p.nonorm;
   a.out_f32 = p.out_dtype == LA_F32 ? 1 : 0;
-  switch (p.dtype) {
-    case LA_F32: return launch_dt<float>(a, p.BH(), stream);
-    case LA_BF16: return launch_dt<bf16_t>(a, p.BH(), stream);
-    case LA_F16: return launch_dt<f16_t>(a, p.BH(), stream);
+  // non-causal: the whole sequence into the state first, then every token
+  // reads it out ([kb] section 3, non-causal sketch)
+  const int modes[2][2] = {{0, -1}, {1, 2}};
+  for (int m : modes[p.noncausal ? 1 : 0]) {
+    if (m < 0) break;
+    a.mode = m;
+    hipError_t e = hipErrorInvalidValue;
+    switch (p.dtype) {
+      case LA_F32: e = launch_dt<float>(a, p.BH(), stream); break;
+      case LA_BF16: e = launch_dt<bf16_t>(a, p.BH(), stream); break;
+      case LA_F16: e = launch_dt<f16_t>(a, p.BH(), stream); break;
+    }
+    if (e != hipSuccess) return e;
   }
-  return hipErrorInvalidValue;
+  return hipSuccess;
 }
 
 // ---------------------------------------------------------------- state init

@@ -114,6 +114,9 @@ typedef struct la_desc {
   int chunk;             /* prefill chunk length, 0 = default (32); 32/64/128     */
   int segments;          /* prefill segments per (b, h), 0 = automatic            */
   la_norm norm;          /* read-out form, LA_NORM_SUM (0) by default             */
+  int noncausal;         /* prefill only: 0 = causal (default); 1 = non-causal,
+                            every output reads the state of the whole sequence
+                            (see la_prefill); needs LA_DECAY_NONE             */
 } la_desc;
 
 /* Feature dimension d' of a descriptor (d_h for ELU1, 2 rff_D for RFF), or -1
@@ -143,7 +146,14 @@ la_status la_prefill_plan(const la_desc* desc, int* chunk, int* segments, int* p
  * schedule re-brackets the same sums ([lesson] Researcher level,
  * "Implementation reality": quadratic inside chunks, a scan across them).
  * `workspace` must hold la_prefill_workspace_size() bytes (NULL if 0).
- * T = 0 is a no-op. */
+ * T = 0 is a no-op.
+ * With desc->noncausal = 1 the prefill is the non-causal form ([kb] section
+ * 3, non-causal sketch; [lesson] Developer level, the phi(Q) (phi(K)^T V)
+ * bracketing): the state first takes in all T tokens, S <- S + sum_t
+ * phi(k_t) v_t^T and z <- z + sum_t phi(k_t), and then every token reads it
+ * out, o_t = phi(q_t)^T S / (phi(q_t)^T z + eps) (the numerator alone with
+ * LA_NORM_NONE).  The final state is the same as the causal form's.  No
+ * decay or gate (LA_EINVAL otherwise). */
 la_status la_prefill(const la_desc* desc, const void* q, const void* k, const void* v,
                      float* S, float* z, void* out, void* workspace,
                      size_t workspace_bytes, void* stream);
@@ -160,7 +170,8 @@ la_status la_prefill_stage(const la_desc* desc, int stage, const void* q, const 
 /* One autoregressive step for B sequences x H heads ([kb] section 2, causal
  * recurrence; [card] "When to use which": memory-bound decoding with a
  * fixed-size state): reads q, k [B, H, d_h], v [B, H, d_v] and the gate or
- * decay [B, H]; updates (S, z) in place and writes out [B, H, d_v]. */
+ * decay [B, H]; updates (S, z) in place and writes out [B, H, d_v].
+ * desc->noncausal must be 0. */
 la_status la_decode_step(const la_desc* desc, const void* q, const void* k, const void* v,
                          float* S, float* z, void* out, void* stream);
 

@@ -340,6 +340,52 @@ def noncausal_right(fq, fk, v, eps=1e-6):
     return (fq @ S) / (np.einsum("...td,...d->...t", fq, z) + eps)[..., None]
 
 
+def noncausal_linear_attention(q, k, v, phi="elu1", W=None, eps=1e-6, S0=None, z0=None,
+                               normalize=True):
+    """Non-causal linear attention ([kb] section 3, non-causal sketch; [lesson]
+    Developer level, the phi(Q) (phi(K)^T V) bracketing): every query reads
+    the state of the whole sequence, S = S0 + phi(K)^T V and z = z0 +
+    phi(K)^T 1, as o_t = phi(q_t)^T S / (phi(q_t)^T z + eps), or the
+    numerator alone with normalize=False.  The state is the one a causal pass
+    over the same tokens ends with.  Returns (o, S, z) in float64.
+
+    q, k: [..., H, T, d_h]; v: [..., H, T, d_v]; S0, z0 as for the causal form.
+    """
+    fq = features(q, phi, W)
+    fk = features(k, phi, W)
+    v = _f64(v)
+    S = np.swapaxes(fk, -1, -2) @ v
+    z = fk.sum(axis=-2)
+    if S0 is not None:
+        S = S + _f64(S0)
+    if z0 is not None:
+        z = z + _f64(z0)
+    num = fq @ S
+    if not normalize:
+        return num, S, z
+    den = np.einsum("...td,...d->...t", fq, z)
+    return num / (den + eps)[..., None], S, z
+
+
+def noncausal_by_definition(fq, fk, v, eps=1e-6, normalize=True):
+    """Pure-Python double loop over one head: o_i = sum_j sim_ij v_j /
+    (sum_j sim_ij + eps) over every key j.  Tiny inputs only."""
+    fq, fk, v = _f64(fq), _f64(fk), _f64(v)
+    T, dv = fq.shape[0], v.shape[1]
+    out = np.zeros((T, dv), F64)
+    for i in range(T):
+        num = [0.0] * dv
+        den = 0.0
+        for j in range(T):
+            sim = sum(float(fq[i, c]) * float(fk[j, c]) for c in range(fq.shape[1]))
+            den += sim
+            for c in range(dv):
+                num[c] += sim * float(v[j, c])
+        for c in range(dv):
+            out[i, c] = num[c] / (den + eps) if normalize else num[c]
+    return out
+
+
 # --------------------------------------------------------------------------
 # Accounting the pages print
 # --------------------------------------------------------------------------

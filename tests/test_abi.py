@@ -67,7 +67,8 @@ def test_plan_for_the_measured_prefills():
 
 @pytest.mark.parametrize("field,value", [("B", 0), ("H", -1), ("T", -5), ("d_h", 0), ("d_v", 0),
                                          ("dtype", 7), ("phi", 9), ("decay_kind", 5),
-                                         ("chunk", 48), ("segments", -1), ("norm", 2)])
+                                         ("chunk", 48), ("segments", -1), ("norm", 2),
+                                         ("noncausal", 3)])
 def test_bad_descriptor_fields_are_rejected(field, value):
     d = desc()
     setattr(d, field, value)
@@ -145,3 +146,16 @@ def test_chunk_128_needs_narrow_state():
     d = desc(chunk=128)
     assert status(L.la_prefill(ctypes.byref(d), *([FAKE] * 7), 1 << 40, None)) == "LA_EUNSUPPORTED"
     assert la.prefill_plan(desc(chunk=128, d_h=64, d_v=64))[0] == 128
+
+
+def test_noncausal_checks():
+    d = desc(causal=False)
+    d.decay_kind, d.decay = _lib.LA_DECAY_SSD, FAKE   # the non-causal form takes no decay
+    assert status(L.la_prefill(ctypes.byref(d), *([FAKE] * 7), 1 << 40, None)) == "LA_EINVAL"
+    d = la.make_desc(256, 16, 1, 64, 64, _lib.LA_F32, causal=False)   # decode is causal
+    assert status(L.la_decode_step(ctypes.byref(d), *([FAKE] * 6), None)) == "LA_EINVAL"
+    # a single segment still needs the workspace: the state comes first
+    one = desc(T=640, segments=1, causal=False)
+    assert la.prefill_plan(one)[1] == 1 and la.prefill_workspace_size(one) > 0
+    assert la.prefill_workspace_size(desc(T=640, segments=1)) == 0
+

@@ -279,3 +279,48 @@ def test_decode_unnormalised(phi, dh, D):
         assert rel_err(o, o_ref) < TOL["f32"]
     assert rel_err(S, S_ref) < TOL["f32"] and rel_err(z, z_ref) < TOL["f32"]
 
+
+# ------------------------------------------------------------ the non-causal form
+
+def oracle_noncausal(x, **kw):
+    return O.noncausal_linear_attention(x.q, x.k, x.v, **kw)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("normalize", [True, False])
+@pytest.mark.parametrize("chunk", [32, 64])
+def test_prefill_noncausal_mfma(d, normalize, chunk):
+    # every output reads the whole sequence's state, from one, the default
+    # and three segments, with and without a carried-in state
+    dev = gpu_device()
+    x = I.prefill_inputs(2, 3, 333, d, dtype="bf16", seed=11 + d + chunk)
+    o_ref, S_ref, z_ref = oracle_noncausal(x, normalize=normalize)
+    for segments in (1, 0, 3):
+        out, S, z = run_prefill(x, dev, chunk=chunk, segments=segments, normalize=normalize,
+                                causal=False)
+        e = (rel_err(out, o_ref), rel_err(S, S_ref), rel_err(z, z_ref))
+        print("noncausal", d, normalize, chunk, segments, e)
+        assert max(e) < TOL["bf16"], e
+    S0 = torch.rand(2, 3, d, d) * 0.1
+    z0 = torch.rand(2, 3, d) + 1.0
+    o_ref, S_ref, _ = oracle_noncausal(x, normalize=normalize, S0=S0, z0=z0)
+    out, S, z = run_prefill(x, dev, chunk=chunk, normalize=normalize, causal=False,
+                            state=(S0.to(dev), z0.to(dev)))
+    assert rel_err(out, o_ref) < TOL["bf16"] and rel_err(S, S_ref) < TOL["bf16"]
+
+
+@pytest.mark.parametrize("phi", ["elu1", "rff"])
+def test_prefill_noncausal_per_token_fp32(phi):
+    # random features with unit-norm q, k, as in the gated decode workload:
+    # with raw N(0, 1) inputs the kernel estimates sit near 0 and so do the
+    # denominators
+    dev = gpu_device()
+    rff = phi == "rff"
+    x = I.prefill_inputs(2, 2, 90, 32, dtype="f32", seed=8, rff_D=16 if rff else None,
+                         unit_norm_qk=rff)
+    W = x.W if rff else None
+    out, S, z = run_prefill(x, dev, phi=phi, W=None if W is None else W.to(dev), causal=False)
+    o_ref, S_ref, z_ref = oracle_noncausal(x, phi=phi, W=W)
+    e = (rel_err(out, o_ref), rel_err(S, S_ref), rel_err(z, z_ref))
+    assert max(e) < TOL["f32"], e
+

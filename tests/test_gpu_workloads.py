@@ -11,7 +11,8 @@ the input type), against the fp64 oracle.
 * long-context prefill, B=1, H=8, T=102400, d=128, bf16 scaled by 1/sqrt(2):
   two heads end to end, sampled positions (chunk, sub-segment and segment
   edges among them) of the other six, every final state in closed form; and
-  the same workload with the normaliser-free read-out, two heads end to end.
+  the same workload with the normaliser-free read-out, two heads end to end,
+  and in the non-causal form, every output.
 
 A 16-bit output is the fp32 result rounded to nearest even, so each element
 may sit up to half an ulp (2^-8 relative, worst case in a binade) from the
@@ -44,7 +45,7 @@ def rms(x):
     return float(np.sqrt(np.mean(np.asarray(x, dtype=np.float64) ** 2)))
 
 
-def run_workload(name, normalize=True):
+def run_workload(name, normalize=True, causal=True):
     """Inputs drawn on the host (seed 0) and the prefill as the benchmark runs it."""
     dev = gpu_device()
     x = I.workload_inputs(name, seed=0)
@@ -54,7 +55,8 @@ def run_workload(name, normalize=True):
     chunk, segments, path = la.prefill_plan(desc)
     assert path == 1
     g = lambda t: None if t is None else t.to(dev)
-    out, S, z = la.prefill(g(x.q), g(x.k), g(x.v), decay=g(x.decay), normalize=normalize)
+    out, S, z = la.prefill(g(x.q), g(x.k), g(x.v), decay=g(x.decay), normalize=normalize,
+                           causal=causal)
     torch.cuda.synchronize()
     assert out.dtype == torch.bfloat16
     print(name, "plan", chunk, segments)
@@ -158,5 +160,16 @@ def test_long_prefill_unnormalised_two_heads():
     r = rms(o_ref)
     e = (excess_err(out[0, hs], o_ref, r), rel_err(S[0, hs], S_ref), rel_err(z[0, hs], z_ref))
     print("long prefill unnormalised", e)
+    assert max(e) < TOL["bf16"], e
+
+
+def test_long_prefill_noncausal_full():
+    """The long-context workload in the non-causal form, in the benchmark's
+    launch configuration: every output and every final state."""
+    x, out, S, z, _ = run_workload("long_prefill_b1_h8_t102400_d128", causal=False)
+    o_ref, S_ref, z_ref = O.noncausal_linear_attention(x.q, x.k, x.v)
+    r = rms(o_ref)
+    e = (excess_err(out, o_ref, r), rel_err(S, S_ref), rel_err(z, z_ref))
+    print("long prefill non-causal", e, "plain", rel_err(out, o_ref))
     assert max(e) < TOL["bf16"], e
 

@@ -298,6 +298,39 @@ def test_unnormalised_closed_forms():
     assert np.array_equal(S1, S2) and np.array_equal(z1, z2)
 
 
+# ------------------------------------------------------ the non-causal form
+
+@pytest.mark.parametrize("normalize", [True, False])
+@pytest.mark.parametrize("T,d,dv", [(1, 2, 1), (6, 3, 2), (9, 4, 5)])
+def test_noncausal_equals_bruteforce_definition(normalize, T, d, dv):
+    q, k, v = rand(1, T, d), rand(1, T, d), rand(1, T, dv)
+    o, _, _ = O.noncausal_linear_attention(q, k, v, normalize=normalize)
+    ref = O.noncausal_by_definition(O.phi_elu1(q[0]), O.phi_elu1(k[0]), v[0],
+                                    normalize=normalize)
+    np.testing.assert_allclose(o[0], ref, rtol=1e-12, atol=1e-13)
+
+
+def test_noncausal_state_bracketing_and_final_state():
+    # the state-first form equals the scores-first form, and its state is
+    # the one a causal pass over the same tokens ends with; a carried-in
+    # state enters like keys seen before the sequence
+    q, k, v = rand(2, 40, 6), rand(2, 40, 6), rand(2, 40, 3)
+    o, S, z = O.noncausal_linear_attention(q, k, v)
+    np.testing.assert_allclose(o, O.noncausal_left(O.phi_elu1(q), O.phi_elu1(k), v),
+                               rtol=1e-12, atol=1e-13)
+    _, Sc, zc = O.causal_linear_attention(q, k, v)
+    np.testing.assert_allclose(S, Sc, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(z, zc, rtol=1e-12)
+    q0, k0, v0 = rand(2, 7, 6), rand(2, 7, 6), rand(2, 7, 3)
+    _, S0, z0 = O.causal_linear_attention(q0, k0, v0)
+    o2, S2, _ = O.noncausal_linear_attention(q, k, v, S0=S0, z0=z0)
+    allk = np.concatenate([k0, k], axis=1)
+    allv = np.concatenate([v0, v], axis=1)
+    num = O.phi_elu1(q) @ np.swapaxes(O.phi_elu1(allk), -1, -2)
+    ref = (num @ allv) / (num.sum(-1) + 1e-6)[..., None]
+    np.testing.assert_allclose(o2, ref, rtol=1e-12, atol=1e-13)
+
+
 # ------------------------------------------------------ the pages' own numbers
 
 def test_worked_example_reproduces_printed_output():
