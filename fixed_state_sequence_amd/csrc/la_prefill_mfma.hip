@@ -163,6 +163,8 @@ struct Cfg {
   static constexpr int S1_VL = S1_VH + TILE;
   static constexpr int S1_BUF = S1_VL + (VS ? TILE : 0);
   static constexpr int S1_LDS = 2 * S1_BUF;
+  // stage-1 producer prefetch depth (chunks of k, v held in registers)
+  static constexpr int S1_PD = RPT <= 2 ? 3 : 1;
   static_assert(RPT == C / 16, "row split");
   static_assert(C == 32 || C == 64 || C == 128, "chunk");
   static_assert(D == 64 || D == 128, "width");
@@ -472,158 +474,167 @@ __device__ __forceinline__ float group_sum(float x) {
 // walked back to front, so the weight of a token is the decay of the chunks
 // already folded (lsuf) times its within-chunk suffix, and the first chunks
 // of the segment are the most recently read when the output stage starts.
+//
+// Warp-specialised like the output stage: NW producer waves load k, v
+// S1_PD chunks ahead into registers, form w phi(k) (bf16 high and low parts)
+// and the v tiles in one of two LDS buffers, and keep their share of z; NW
+// consumer waves fold each staged chunk into the state held in their
+// accumulators (32 value columns each).  One barrier per chunk.
 template <int D, int C, int DECAY, typename DT>
-__global__ __launch_bounds__(2 * D) void segment_state_kernel(const PfArgs a) {
+__global__ __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4, 4)))
+void segment_state_kernel(const PfArgs a) {
   constexpr bool VS = __is_same(DT, f16_t);   // fp16 v needs a bf16 low part too
   using G = Cfg<D, C, VS>;
   __shared__ __align__(16) char smem[G::S1_LDS];
+  __shared__ __align__(16) float zl[G::NW][D];
   const int bh = blockIdx.x / a.nslot;
   const int u = blockIdx.x % a.nslot;   // sub-segment: segment u / nsub, part u % nsub
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int fb = tid % G::FB, rg = tid / G::FB;
   const int nchunks = (a.T + C - 1) / C;
   const int seg_first = (u / a.nsub) * a.cps;
   const int c0 = seg_first + (u % a.nsub) * a.cps_sub;
   const int c1 = min(min(c0 + a.cps_sub, seg_first + a.cps), nchunks);
+  const int n = max(c1 - c0, 0);   // chunks to fold (a sub-segment can be empty)
+  float* dst = a.ws_state + (int64_t(bh) * a.nslot + u) * (D * D + D);
+  auto buffer = [&](int i) -> char* { return smem + (i & 1) * G::S1_BUF; };
 
-  const DT* kg = static_cast<const DT*>(a.k) + int64_t(bh) * a.T * D;
-  const DT* vg = static_cast<const DT*>(a.v) + int64_t(bh) * a.T * D;
-  const float* dg = DECAY ? a.decay + int64_t(bh) * a.T : nullptr;
-
-  f32x16 acc[G::MT];
+  const int wave_id = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
+  if (wave_id >= G::NW) {
+    // =================================================== producer waves
+    const int ts = threadIdx.x - G::NT, lane = ts & 63, wave = ts >> 6;
+    const int fb = ts % G::FB, rg = ts / G::FB;
+    const DT* kg = static_cast<const DT*>(a.k) + int64_t(bh) * a.T * D;
+    const DT* vg = static_cast<const DT*>(a.v) + int64_t(bh) * a.T * D;
+    const float* dg = DECAY ? a.decay + int64_t(bh) * a.T : nullptr;
+    // this thread's share of z (features 8 fb .. 8 fb + 7, its own rows of
+    // every chunk): the weights already carry the decay, so z is a plain
+    // sum, reduced over the threads once at the end
+    float zp[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float lsuf = 0.f;   // log-decay of the chunks already staged (later in the segment)
+    using Raw = RawChunk<G::RPT, G::ND, false>;
+    // walk step i stages chunk c1 - 1 - i; steps past the segment's first
+    // chunk load a repeat of it (clamped), so the loads are the same on every
+    // path, and add nothing
+    auto fetch = [&](Raw& r, int i) {
+      fetch_chunk<C, D, G::RPT, G::ND, false, DECAY>(r, (const DT*)nullptr, kg, vg, dg,
+                                                      max(c1 - 1 - i, c0) * C, a.T, rg, fb, lane);
+    };
+    // [A] chunk c into buffer buf: w phi(k) high/low and v as token-major
+    // tiles; this thread's rows added to zp.  Rows past the end have k = v =
+    // 0: phi(k) = 1 there and v = 0, so they add nothing to S; without decay
+    // their 1s are taken off z at the end.
+    auto stage = [&](Raw& raw, int i, char* buf) {
+      const int c = c1 - 1 - i;
+      const bool live = i < n;
+      const int tok0 = max(c, c0) * C;
+      clean_chunk<C, G::RPT, G::ND, false, DECAY>(raw, tok0, a.T, rg, lane);
+      float lo = 0.f, hi = 0.f, ltot = 0.f;
+      if constexpr (DECAY != 0) chunk_logprefix<C, G::ND>(raw.d, lane, lo, hi, ltot);
 #pragma unroll
-  for (int mt = 0; mt < G::MT; ++mt) acc[mt] = f32x16{};
-  // this thread's share of z (features 8 fb .. 8 fb + 7, its own rows of
-  // every chunk): the weights already carry the decay, so z is a plain sum,
-  // reduced over the threads once at the end
-  float zp[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float lsuf = 0.f;   // log-decay of the chunks already staged (later in the segment)
-
-  auto fetch = [&](RawChunk<G::RPT, G::ND, false>& r, int c) {
-    fetch_chunk<C, D, G::RPT, G::ND, false, DECAY>(r, (const DT*)nullptr, kg, vg, dg, c * C, a.T,
-                                                    rg, fb, lane);
-  };
-  // [A] chunk c into buffer buf: w phi(k) high/low and v as token-major
-  // tiles; this thread's rows added to zp.  Rows past the end have k = v = 0:
-  // phi(k) = 1 there and v = 0, so they add nothing to S; without decay
-  // their 1s are taken off z at the end.  The chunk before the segment's
-  // first (staged only to keep the loads uniform) adds nothing to zp.
-  auto stage = [&](RawChunk<G::RPT, G::ND, false>& raw, int c, char* buf) {
-    const int tok0 = c * C;
-    clean_chunk<C, G::RPT, G::ND, false, DECAY>(raw, tok0, a.T, rg, lane);
-    float lo = 0.f, hi = 0.f, ltot = 0.f;
-    if constexpr (DECAY != 0) chunk_logprefix<C, G::ND>(raw.d, lane, lo, hi, ltot);
-    const bool live = c >= c0;
+      for (int ii = 0; ii < G::RPT; ++ii) {
+        const int r = G::RPT * rg + ii;
+        float kx[8];
+        unpack8(raw.k[ii], kx, DT{});
+        float w = 1.f;
+        if constexpr (DECAY != 0) {
+          w = tok0 + r < a.T ? __expf(lsuf + ltot - lane_value<C>(lo, hi, r)) : 0.f;
+          if constexpr (DECAY == 2)
+            w *= 1.f - lane_value<C>(raw.d[0], G::ND > 1 ? raw.d[G::ND - 1] : 0.f, r);
+        }
 #pragma unroll
-    for (int i = 0; i < G::RPT; ++i) {
-      const int r = G::RPT * rg + i;
-      float kx[8];
-      unpack8(raw.k[i], kx, DT{});
-      float w = 1.f;
-      if constexpr (DECAY != 0) {
-        w = tok0 + r < a.T ? __expf(lsuf + ltot - lane_value<C>(lo, hi, r)) : 0.f;
-        if constexpr (DECAY == 2) w *= 1.f - lane_value<C>(raw.d[0], G::ND > 1 ? raw.d[G::ND - 1] : 0.f, r);
+        for (int e = 0; e < 8; ++e) {
+          kx[e] = elu1_fast(kx[e]);
+          if constexpr (DECAY != 0) kx[e] *= w;
+          if (live) zp[e] += kx[e];
+        }
+        const u32x4 kh = pack8(kx);
+        blk_write<D>(buf + G::S1_KH, perm_pos(r), fb, kh);
+        blk_write<D>(buf + G::S1_KL, perm_pos(r), fb, low8(kx, kh));
+        if constexpr (VS) {
+          float vx[8];
+          unpack8(raw.v[ii], vx, DT{});
+          const u32x4 vh = pack8(vx);
+          blk_write<D>(buf + G::S1_VH, perm_pos(r), fb, vh);
+          blk_write<D>(buf + G::S1_VL, perm_pos(r), fb, low8(vx, vh));
+        } else {
+          blk_write<D>(buf + G::S1_VH, perm_pos(r), fb, raw.v[ii]);
+        }
       }
+      if (live) lsuf += ltot;
+      // refill this register set with the step S1_PD further on
+      fetch(raw, i + G::S1_PD);
+    };
+
+    Raw raw[G::S1_PD];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        kx[e] = elu1_fast(kx[e]);
-        if constexpr (DECAY != 0) kx[e] *= w;
-        if (live) zp[e] += kx[e];
-      }
-      const u32x4 kh = pack8(kx);
-      blk_write<D>(buf + G::S1_KH, perm_pos(r), fb, kh);
-      blk_write<D>(buf + G::S1_KL, perm_pos(r), fb, low8(kx, kh));
-      if constexpr (VS) {
-        float vx[8];
-        unpack8(raw.v[i], vx, DT{});
-        const u32x4 vh = pack8(vx);
-        blk_write<D>(buf + G::S1_VH, perm_pos(r), fb, vh);
-        blk_write<D>(buf + G::S1_VL, perm_pos(r), fb, low8(vx, vh));
-      } else {
-        blk_write<D>(buf + G::S1_VH, perm_pos(r), fb, raw.v[i]);
+    for (int j = 0; j < G::S1_PD; ++j) fetch(raw[j], j);
+    stage(raw[0], 0, buffer(0));
+    __syncthreads();
+    for (int i0 = 0; i0 < n; i0 += G::S1_PD) {
+#pragma unroll
+      for (int j = 0; j < G::S1_PD; ++j) {
+        const int i = i0 + j;
+        stage(raw[(j + 1) % G::S1_PD], i + 1, buffer(i + 1));
+        if (i < n) __syncthreads();   // chunk i folded, chunk i + 1 staged
       }
     }
-    if (live) lsuf += ltot;
-    // refill this register set with the chunk DEPTH further back (clamped:
-    // the loads are issued on every path, see RawChunk)
-    if constexpr (G::DEPTH > 0) fetch(raw, max(c - G::DEPTH, c0));
-  };
-  // [B] fold chunk c (staged in buf) into S; the weights already carry the
-  // decay.
-  auto fold = [&](const char* buf) {
-    u32x4 vh[G::KT], vl[G::KT];
+    // z: the shares summed within each wave, then over the producer waves;
+    // less the 1s of the rows past the end (no decay)
 #pragma unroll
-    for (int kk = 0; kk < G::KT; ++kk) {
-      vh[kk] = tr_operand<D>(buf + G::S1_VH, 16 * kk, 32 * wave, lane);
-      if constexpr (VS) vl[kk] = tr_operand<D>(buf + G::S1_VL, 16 * kk, 32 * wave, lane);
+    for (int e = 0; e < 8; ++e) zp[e] = group_sum<G::FB>(zp[e]);
+    if (lane < G::FB) {
+      *reinterpret_cast<f32x4*>(&zl[wave][8 * fb]) = f32x4{zp[0], zp[1], zp[2], zp[3]};
+      *reinterpret_cast<f32x4*>(&zl[wave][8 * fb + 4]) = f32x4{zp[4], zp[5], zp[6], zp[7]};
     }
+    __syncthreads();
+    if (ts < D) {
+      float zs = (DECAY == 0 && n > 0 && c1 == nchunks) ? -float(nchunks * C - a.T) : 0.f;
 #pragma unroll
-    for (int mt = 0; mt < G::MT; ++mt) {
+      for (int w = 0; w < G::NW; ++w) zs += zl[w][ts];
+      dst[D * D + ts] = zs;
+    }
+    if (ts == 0) a.ws_logg[int64_t(bh) * a.nslot + u] = lsuf;
+  } else {
+    // =================================================== consumer waves
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    f32x16 acc[G::MT];
+#pragma unroll
+    for (int mt = 0; mt < G::MT; ++mt) acc[mt] = f32x16{};
+    // [B] fold the staged chunk into S; the weights already carry the decay
+    auto fold = [&](const char* buf) {
+      u32x4 vh[G::KT], vl[G::KT];
 #pragma unroll
       for (int kk = 0; kk < G::KT; ++kk) {
-        const u32x4 kh = tr_operand<D>(buf + G::S1_KH, 16 * kk, 32 * mt, lane);
-        const u32x4 kl = tr_operand<D>(buf + G::S1_KL, 16 * kk, 32 * mt, lane);
-        acc[mt] = mfma(kh, vh[kk], acc[mt]);
-        acc[mt] = mfma(kl, vh[kk], acc[mt]);
-        if constexpr (VS) acc[mt] = mfma(kh, vl[kk], acc[mt]);
+        vh[kk] = tr_operand<D>(buf + G::S1_VH, 16 * kk, 32 * wave, lane);
+        if constexpr (VS) vl[kk] = tr_operand<D>(buf + G::S1_VL, 16 * kk, 32 * wave, lane);
       }
-    }
-  };
-
-  // Chunks are walked back to front, c1 - 1 first; the i-th chunk walked
-  // uses register set i % RING and buffer i % 2.  Chunk i + 1 is staged while
-  // chunk i is folded.
-  // Every step stages a chunk (a repeat of chunk c0 past the start, whose
-  // tiles are never folded), so the loads are the same on every path.
-  RawChunk<G::RPT, G::ND, false> raw[G::RING];
 #pragma unroll
-  for (int j = 0; j < G::DEPTH; ++j) fetch(raw[j], max(c1 - 1 - j, c0));
-  if constexpr (G::DEPTH == 0) fetch(raw[0], c1 - 1);
-  stage(raw[0], c1 - 1, smem);
-  __syncthreads();
-  for (int i0 = 0; i0 < c1 - c0; i0 += G::RING) {
+      for (int mt = 0; mt < G::MT; ++mt) {
 #pragma unroll
-    for (int j = 0; j < G::RING; ++j) {
-      const int i = i0 + j;
-      const int c = c1 - 1 - i;
-      char* cur = smem + (i & 1) * G::S1_BUF;
-      char* nxt = smem + ((i + 1) & 1) * G::S1_BUF;
-      if constexpr (G::DEPTH == 0) fetch(raw[0], max(c - 1, c0));
-      stage(raw[(j + 1) % G::RING], c - 1, nxt);
-      if (c >= c0) fold(cur);
+        for (int kk = 0; kk < G::KT; ++kk) {
+          const u32x4 kh = tr_operand<D>(buf + G::S1_KH, 16 * kk, 32 * mt, lane);
+          const u32x4 kl = tr_operand<D>(buf + G::S1_KL, 16 * kk, 32 * mt, lane);
+          acc[mt] = mfma(kh, vh[kk], acc[mt]);
+          acc[mt] = mfma(kl, vh[kk], acc[mt]);
+          if constexpr (VS) acc[mt] = mfma(kh, vl[kk], acc[mt]);
+        }
+      }
+    };
+    __syncthreads();   // the producers' first chunk
+    for (int i = 0; i < n; ++i) {
+      fold(buffer(i));
       __syncthreads();
     }
+    // the state, row-major [f][v]
+    const int g = lane >> 5, nn = lane & 31;
+#pragma unroll
+    for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int f = 32 * mt + 8 * (r >> 2) + 4 * g + (r & 3);
+        dst[f * D + 32 * wave + nn] = acc[mt][r];
+      }
+    __syncthreads();   // matches the producers' z barrier
   }
-
-  // write the segment state: S row-major [f][v], then z, then log Gamma
-  const int g = lane >> 5, n = lane & 31;
-  float* dst = a.ws_state + (int64_t(bh) * a.nslot + u) * (D * D + D);
-#pragma unroll
-  for (int mt = 0; mt < G::MT; ++mt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int f = 32 * mt + 8 * (r >> 2) + 4 * g + (r & 3);
-      dst[f * D + 32 * wave + n] = acc[mt][r];
-    }
-  // z: the threads' shares, summed within each wave, then over the waves
-  // through LDS; less the 1s of the rows past the end (no decay)
-#pragma unroll
-  for (int e = 0; e < 8; ++e) zp[e] = group_sum<G::FB>(zp[e]);
-  float* zl = reinterpret_cast<float*>(smem);   // the tiles are no longer read
-  if (lane < G::FB) {
-    *reinterpret_cast<f32x4*>(zl + wave * D + 8 * fb) = f32x4{zp[0], zp[1], zp[2], zp[3]};
-    *reinterpret_cast<f32x4*>(zl + wave * D + 8 * fb + 4) = f32x4{zp[4], zp[5], zp[6], zp[7]};
-  }
-  __syncthreads();
-  if (tid < D) {
-    // (a sub-segment can be empty: c0 = c1 = nchunks at the end of a
-    // ragged split; it holds no rows at all)
-    float zs = (DECAY == 0 && c0 < c1 && c1 == nchunks) ? -float(nchunks * C - a.T) : 0.f;
-#pragma unroll
-    for (int w = 0; w < G::NW; ++w) zs += zl[w * D + tid];
-    dst[D * D + tid] = zs;
-  }
-  if (tid == 0) a.ws_logg[int64_t(bh) * a.nslot + u] = lsuf;
 }
 
 // ---------------------------------------------------------------- stage 2
@@ -1074,7 +1085,7 @@ hipError_t launch3(const PfArgs& a, int64_t BH, int stage, hipStream_t st) {
   const bool scan = a.nseg > 1 || a.nc;
   if (stage == 1) {
     if (!scan) return hipSuccess;
-    segment_state_kernel<D, C, DECAY, DT><<<dim3(unsigned(BH * a.nslot)), dim3(G::NT), 0, st>>>(a);
+    segment_state_kernel<D, C, DECAY, DT><<<dim3(unsigned(BH * a.nslot)), dim3(2 * G::NT), 0, st>>>(a);
   } else if (stage == 2) {
     if (!scan) return hipSuccess;
     const int per_bh = (D * D + D + 255) / 256;
