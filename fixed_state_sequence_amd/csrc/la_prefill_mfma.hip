@@ -925,6 +925,31 @@ void output_kernel(const PfArgs a) {
         vh[kk] = tr_operand<D>(buf + G::B_VH, 16 * kk, 32 * wave, lane);
         if constexpr (VS) vl[kk] = tr_operand<D>(buf + G::B_VL, 16 * kk, 32 * wave, lane);
       }
+      // Fold this chunk into the carried state: w phi(k) high parts, and
+      // (fold_lo) the low parts when this one segment also produces the
+      // final state (`fin`).  With one 32-token block the high-part fold
+      // follows the read-out directly (which has consumed the state by
+      // then), so its MFMA chains overlap the masking and P V work.
+      auto fold_hi = [&]() {
+        const float gam = DECAY ? __expf(*reinterpret_cast<const float*>(buf + G::B_LT)) : 1.f;
+#pragma unroll
+        for (int mt = 0; mt < G::MT; ++mt) {
+          if constexpr (DECAY != 0) acc[mt] *= gam;
+#pragma unroll
+          for (int kk = 0; kk < G::KT; ++kk) {
+            const u32x4 kh = tr_operand<D>(buf + G::B_KH, 16 * kk, 32 * mt, lane);
+            acc[mt] = mfma(kh, vh[kk], acc[mt]);
+            if constexpr (VS) acc[mt] = mfma(kh, vl[kk], acc[mt]);
+          }
+        }
+      };
+      auto fold_lo = [&]() {
+#pragma unroll
+        for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+          for (int kk = 0; kk < G::KT; ++kk)
+            acc[mt] = mfma(tr_operand<D>(buf + G::B_KL, 16 * kk, 32 * mt, lane), vh[kk], acc[mt]);
+      };
 #pragma unroll
       for (int tb = 0; tb < G::TB; ++tb) {
         const int tl = 32 * tb + n;   // this lane's query token within the chunk
@@ -944,6 +969,7 @@ void output_kernel(const PfArgs a) {
         }
         if (!NC && tok0 < G::EXACT)
           p = low_scores<D, G::KS>(buf + G::B_KR, buf + G::B_Q, 32 * tb + n, tl, g, p);
+        if constexpr (!NC && G::TB == 1) fold_hi();
         float lct = 0.f;
         if constexpr (DECAY != 0) {
           lct = Ll[tl];
@@ -1018,28 +1044,9 @@ void output_kernel(const PfArgs a) {
           }
         }
       }
-      // fold this chunk into the carried state (w phi(k) high parts, and
-      // the low parts for a single segment; see `fin`).  One branch picks
-      // a straight-line fold, so the tile reads are not held back behind a
-      // branch per MFMA.
-      const float gam = DECAY ? __expf(*reinterpret_cast<const float*>(buf + G::B_LT)) : 1.f;
-      auto fold = [&](auto with_lo) {
-#pragma unroll
-        for (int mt = 0; mt < G::MT; ++mt) {
-          if constexpr (DECAY != 0) acc[mt] *= gam;
-#pragma unroll
-          for (int kk = 0; kk < G::KT; ++kk) {
-            const u32x4 kh = tr_operand<D>(buf + G::B_KH, 16 * kk, 32 * mt, lane);
-            acc[mt] = mfma(kh, vh[kk], acc[mt]);
-            if constexpr (VS) acc[mt] = mfma(kh, vl[kk], acc[mt]);
-            if constexpr (decltype(with_lo)::value)
-              acc[mt] = mfma(tr_operand<D>(buf + G::B_KL, 16 * kk, 32 * mt, lane), vh[kk], acc[mt]);
-          }
-        }
-      };
       if constexpr (!NC) {
-        if (fin) fold(std::true_type{});
-        else fold(std::false_type{});
+        if constexpr (G::TB > 1) fold_hi();
+        if (fin) fold_lo();
       }
     };
 
