@@ -425,6 +425,16 @@ __device__ __forceinline__ float row_sum(float x) {
   if constexpr (FB == 16) x += dpp<0x140>(x);   // row_mirror
   return x;
 }
+// Exchange lanes 32-63 of a with lanes 0-31 of b (v_permlane32_swap): a
+// keeps its lower half and takes b's lower half into its upper lanes, b
+// takes a's upper half into its lower lanes and keeps its upper half.
+__device__ __forceinline__ void swap_halves(uint32_t& a, uint32_t& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+  const unsigned long long u = __builtin_bit_cast(unsigned long long, r);   // see pair_sum
+  a = unsigned(u);
+  b = unsigned(u >> 32);
+}
+
 // Padded position of feature 8 fb + e in a wave's z increments (see DZS).
 __device__ __forceinline__ int dz_index(int fb, int e) { return 8 * fb + e + ((fb >> 3) << 2); }
 
@@ -1027,19 +1037,29 @@ void output_kernel(const PfArgs a) {
               *reinterpret_cast<f32x4*>(ogf + orow + 8 * j) =
                   f32x4{o[4 * j] * inv, o[4 * j + 1] * inv, o[4 * j + 2] * inv, o[4 * j + 3] * inv};
           } else {
+            // lane (g, n) holds value columns 8 j + 4 g .. + 3 (j = 0..3) of
+            // token n; a half-wave swap of the odd and even groups leaves
+            // lane g with columns 16 m + 8 g .. + 7 (m = 0, 1): 16-byte stores
+            uint32_t w[8];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               const float y0 = o[4 * j] * inv, y1 = o[4 * j + 1] * inv;
               const float y2 = o[4 * j + 2] * inv, y3 = o[4 * j + 3] * inv;
-              u32x2 w;
               if constexpr (__is_same(DT, bf16_t)) {
-                w = u32x2{pack_bf16(y0, y1), pack_bf16(y2, y3)};
+                w[2 * j] = pack_bf16(y0, y1);
+                w[2 * j + 1] = pack_bf16(y2, y3);
               } else {
                 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-                w = u32x2{__builtin_bit_cast(uint32_t, h2{(f16_t)y0, (f16_t)y1}),
-                          __builtin_bit_cast(uint32_t, h2{(f16_t)y2, (f16_t)y3})};
+                w[2 * j] = __builtin_bit_cast(uint32_t, h2{(f16_t)y0, (f16_t)y1});
+                w[2 * j + 1] = __builtin_bit_cast(uint32_t, h2{(f16_t)y2, (f16_t)y3});
               }
-              *reinterpret_cast<u32x2*>(og + orow + 8 * j) = w;
+            }
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+              swap_halves(w[4 * m], w[4 * m + 2]);
+              swap_halves(w[4 * m + 1], w[4 * m + 3]);
+              *reinterpret_cast<u32x4*>(og + uint32_t(t) * D + 32 * wave + 16 * m + 8 * g) =
+                  u32x4{w[4 * m], w[4 * m + 1], w[4 * m + 2], w[4 * m + 3]};
             }
           }
         }
