@@ -75,6 +75,17 @@ def _oracle_head(h):
         return time.perf_counter() - t0
 
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(T_sample: int):
     """Time the oracle on the first T_sample tokens of all H heads, one process
     per head (the heads are independent), before the GPU is touched.  Input
@@ -97,6 +108,7 @@ def cpu_baseline(T_sample: int):
         "sample": (f"first {T_sample} of {PF['T']} tokens of the same workload, all {PF['H']} "
                    f"heads, fp64 numpy recurrence, one process per head with 1 BLAS thread; "
                    f"per-head oracle time {min(per_head):.2f}-{max(per_head):.2f} s; "
+                   f"CPU {_cpu_model()}; "
                    f"{os.cpu_count()} host cores visible"),
     }
 
@@ -190,7 +202,10 @@ def bench_prefill(torch, la, I, steps, warmup, normalize=True, stages=True, caus
     torch.cuda.synchronize()
     stage_ms = [sum(evs[r][s].elapsed_time(evs[r][s + 1]) for r in range(reps)) / reps
                 for s in range(3)]
-    return dict(ms=ms, wall=wall, stage_ms=stage_ms, chunk=chunk, segments=segments)
+    # per-repetition totals of the three stages: median and minimum
+    per = sorted(evs[r][0].elapsed_time(evs[r][3]) for r in range(reps))
+    return dict(ms=ms, wall=wall, stage_ms=stage_ms, chunk=chunk, segments=segments,
+                rep_median_ms=per[len(per) // 2], rep_min_ms=per[0])
 
 
 def hbm_copy(torch, nbytes=1 << 30, reps=10):
@@ -348,7 +363,8 @@ def main(argv=None):
                      "kernel_ms": s3, "algorithmic_bytes": stage3_bytes,
                      "measured_copy_GBs": cp["gbs"], "copy_kernel": cp["kernel"],
                      "frac_of_copy": achieved / cp["gbs"]},
-        "step": {"stage_ms": pf["stage_ms"], "algorithmic_bytes": step_bytes,
+        "step": {"stage_ms": pf["stage_ms"], "prefill_median_ms": pf["rep_median_ms"],
+                 "prefill_min_ms": pf["rep_min_ms"], "algorithmic_bytes": step_bytes,
                  "GBs": step_bytes / (pf["ms"] * 1e-3) / 1e9,
                  "hbm_frac": step_bytes / (pf["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS},
         "mfma": {"algorithmic_flops": flops, "achieved": tflops, "peak": BF16_PEAK_TFLOPS,

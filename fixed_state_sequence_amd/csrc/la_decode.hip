@@ -8,8 +8,8 @@
 // it, so it is bound by HBM bandwidth (wikillm "When to use which": decoding
 // with a fixed-size state is memory-bound).
 //
-// Work split.  One wave (or WPS waves, when the state is larger than 32 KB)
-// owns one state; a 256-thread workgroup holds 4 / WPS states of the same
+// Work split.  One wave (WPS waves for states of 32 KB and more) owns one
+// state; a 256-thread workgroup holds 4 / WPS states of the same
 // head, so the RFF projection W_h is staged once in LDS and shared.  Within a
 // wave, lane l owns float4 column group l % CG of a contiguous run of NI rows;
 // one load instruction of the wave covers RPI = 64 / CG whole rows, so every
@@ -44,7 +44,10 @@ struct DecArgs {
 
 template <int DV, int DP>
 struct DecCfg {
-  static constexpr int WPS = DP * DV > 8192 ? DP * DV / 8192 : 1;  // waves per state
+  // waves per state: a 32 KB state is split over two waves (16 rows of
+  // float4 per lane), so that four waves fit per SIMD; larger states take
+  // one wave per 32 KB
+  static constexpr int WPS = DP * DV > 8192 ? DP * DV / 8192 : (DP * DV == 8192 ? 2 : 1);
   static constexpr int SPW = 4 / WPS;                              // states per workgroup
   static constexpr int CG = DV / 4;                                // float4 column groups
   static constexpr int RPI = 64 / CG;                              // rows per wave instruction
