@@ -9,7 +9,7 @@
 // with a fixed-size state is memory-bound).
 //
 // Work split.  One wave (WPS waves for states of 32 KB and more) owns one
-// state; a 256-thread workgroup holds 4 / WPS states of the same
+// state; a 512-thread workgroup holds 8 / WPS states of the same
 // head, so the RFF projection W_h is staged once in LDS and shared.  Within a
 // wave, lane l owns float4 column group l % CG of a contiguous run of NI rows;
 // one load instruction of the wave covers RPI = 64 / CG whole rows, so every
@@ -24,7 +24,7 @@
 namespace la {
 namespace {
 
-constexpr int NT = 256;
+constexpr int NT = 512;
 
 struct DecArgs {
   const void* q;
@@ -48,14 +48,14 @@ struct DecCfg {
   // float4 per lane), so that four waves fit per SIMD; larger states take
   // one wave per 32 KB
   static constexpr int WPS = DP * DV > 8192 ? DP * DV / 8192 : (DP * DV == 8192 ? 2 : 1);
-  static constexpr int SPW = 4 / WPS;                              // states per workgroup
+  static constexpr int SPW = (NT / 64) / WPS;                      // states per workgroup
   static constexpr int CG = DV / 4;                                // float4 column groups
   static constexpr int RPI = 64 / CG;                              // rows per wave instruction
   static constexpr int NI = DP / (RPI * WPS);                      // rows per lane
   static constexpr int ZPL = (DP + 64 * WPS - 1) / (64 * WPS);     // z entries per lane
   static_assert(NI * RPI * WPS == DP, "row split");
   static_assert(NI % 4 == 0 && NI <= 32, "rows per lane");
-  static_assert(SPW * WPS == 4, "waves");
+  static_assert(SPW * WPS == NT / 64, "waves");
 };
 
 __device__ __forceinline__ float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
@@ -80,7 +80,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(const DecArgs a) {
   __shared__ __align__(16) float s_x[G::SPW][2][DHMAX];
   __shared__ __align__(16) float s_v[G::SPW][DV];
   __shared__ __align__(16) float s_phi[G::SPW][2][DP];
-  __shared__ __align__(16) float s_red[G::WPS > 1 ? 4 : 1][DV + 4];
+  __shared__ __align__(16) float s_red[G::WPS > 1 ? NT / 64 : 1][DV + 4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int sidx = wave / G::WPS, wsub = wave % G::WPS;
