@@ -125,55 +125,67 @@ __global__ __launch_bounds__(NT) void decode_kernel(const DecArgs a) {
   if constexpr (RFF) {
     constexpr int D = DP / 2;
     const float* Wh = a.W + int64_t(h) * D * a.dh;
-    for (int e = tid; e < D * a.dh; e += NT) {
-      const int j = e / a.dh, i = e - j * a.dh;
-      s_W[j * a.dhp + i] = Wh[e];
+    if ((a.dh & 3) == 0 && (reinterpret_cast<uintptr_t>(a.W) & 15) == 0) {
+      // float4 pieces (W 16-byte aligned): each group of q4 lanes takes one
+      // row, no division
+      const int q4 = a.dh >> 2;                 // float4 per row, <= 32
+      const int rpg = 64 / q4 > 0 ? 64 / q4 : 1;   // rows per wave and pass
+      const int sub = lane / q4, col = 4 * (lane - sub * q4);
+      if (sub < rpg) {
+        for (int j = wave * rpg + sub; j < D; j += (NT / 64) * rpg)
+          *reinterpret_cast<float4*>(s_W + j * a.dhp + col) =
+              *reinterpret_cast<const float4*>(Wh + j * a.dh + col);
+      }
+    } else {
+      for (int j = wave; j < D; j += NT / 64)
+        for (int i = lane; i < a.dh; i += 64) s_W[j * a.dhp + i] = Wh[j * a.dh + i];
     }
   }
   __syncthreads();
 
-  // ---- feature maps (the first wave of each state)
-  if (wsub == 0) {
-    float* fq = s_phi[sidx][0];
-    float* fk = s_phi[sidx][1];
-    if constexpr (RFF) {
+  // ---- feature maps: with one wave per state it forms phi(q) and phi(k);
+  // with two or more, the first forms phi(q) and the second phi(k)
+  if constexpr (RFF) {
+    if (wsub < (G::WPS > 1 ? 2 : 1)) {
       // phi(x) = D^{-1/2} [sin(W_h x); cos(W_h x)] (wikillm, Variants / RFA)
       constexpr int D = DP / 2;
       const float rs = 1.0f / sqrtf(float(D));
+      auto project = [&](int which) {
+        const float* x = s_x[sidx][which];
+        float* f = s_phi[sidx][which];
 #pragma unroll
-      for (int jj = 0; jj < (D + 63) / 64; ++jj) {
-        const int j = lane + 64 * jj;
-        if (j < D) {
-          const float* w = s_W + j * a.dhp;
-          const float* xq = s_x[sidx][0];
-          const float* xk = s_x[sidx][1];
-          float pq = 0.f, pk = 0.f;
-          int i = 0;
-          for (; i + 4 <= a.dh; i += 4) {
-            const float4 w4 = ld4(w + i), q4 = ld4(xq + i), k4 = ld4(xk + i);
-            pq = fmaf(w4.x, q4.x, pq); pq = fmaf(w4.y, q4.y, pq);
-            pq = fmaf(w4.z, q4.z, pq); pq = fmaf(w4.w, q4.w, pq);
-            pk = fmaf(w4.x, k4.x, pk); pk = fmaf(w4.y, k4.y, pk);
-            pk = fmaf(w4.z, k4.z, pk); pk = fmaf(w4.w, k4.w, pk);
+        for (int jj = 0; jj < (D + 63) / 64; ++jj) {
+          const int j = lane + 64 * jj;
+          if (j < D) {
+            const float* w = s_W + j * a.dhp;
+            float p = 0.f;
+            int i = 0;
+            for (; i + 4 <= a.dh; i += 4) {
+              const float4 w4 = ld4(w + i), x4 = ld4(x + i);
+              p = fmaf(w4.x, x4.x, p); p = fmaf(w4.y, x4.y, p);
+              p = fmaf(w4.z, x4.z, p); p = fmaf(w4.w, x4.w, p);
+            }
+            for (; i < a.dh; ++i) p = fmaf(w[i], x[i], p);
+            float sn, cs;
+            sincosf(p, &sn, &cs);
+            f[j] = sn * rs;
+            f[D + j] = cs * rs;
           }
-          for (; i < a.dh; ++i) {
-            pq = fmaf(w[i], xq[i], pq);
-            pk = fmaf(w[i], xk[i], pk);
-          }
-          float sq, cq, sk, ck;
-          sincosf(pq, &sq, &cq);
-          sincosf(pk, &sk, &ck);
-          fq[j] = sq * rs;
-          fq[D + j] = cq * rs;
-          fk[j] = sk * rs;
-          fk[D + j] = ck * rs;
         }
+      };
+      if constexpr (G::WPS > 1) {
+        project(wsub);
+      } else {
+        project(0);
+        project(1);
       }
-    } else {
-      for (int f = lane; f < DP; f += 64) {
-        fq[f] = elu1_accurate(s_x[sidx][0][f]);
-        fk[f] = elu1_accurate(s_x[sidx][1][f]);
-      }
+    }
+  } else if (wsub == 0) {
+    float* fq = s_phi[sidx][0];
+    float* fk = s_phi[sidx][1];
+    for (int f = lane; f < DP; f += 64) {
+      fq[f] = elu1_accurate(s_x[sidx][0][f]);
+      fk[f] = elu1_accurate(s_x[sidx][1][f]);
     }
   }
   __syncthreads();
