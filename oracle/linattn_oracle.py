@@ -24,14 +24,20 @@ Sources (the three pages the method is described on):
            "Variants / Random Fourier features (RFA)" (Gaussian random
            projections, sigmoid gate that decays the old state and scales the
            new term by one minus the gate), "Decaying linear attention with a
-           scalar state (SSD)" (decay 1 is the plain causal case).
+           scalar state (SSD)" (decay 1 is the plain causal case),
+           "Variants / Matrix memory with exponential gates (mLSTM)" (matrix
+           memory and normaliser with a forget and an exponential input gate,
+           a read-out divided by max(|n^T q|, 1), a stabiliser state against
+           overflow) and, in "Implementation sketch", the remark that the
+           mLSTM step is this loop with the identity feature map.
 
-Every function is pinned by ``tests/test_oracle_pins.py`` against facts the
-pages or the mathematics fix (closed forms, brute force, printed values).
+Every function is pinned by ``tests/test_oracle_pins.py`` and
+``tests/test_oracle_mlstm_pins.py`` against facts the pages or the
+mathematics fix (closed forms, brute force, printed values).
 
 Layout convention: ``[..., T, d]`` with any leading dims (batch, head);
 decay/gate arrays are ``[..., T]``.  Feature dimension ``d'`` is ``d_h`` for
-elu+1 and ``2 * D`` for random Fourier features.
+elu+1 and the identity map, and ``2 * D`` for random Fourier features.
 """
 from __future__ import annotations
 
@@ -79,9 +85,17 @@ def phi_rff(x, W):
     return np.concatenate([np.sin(proj), np.cos(proj)], axis=-1) / np.sqrt(D)
 
 
+def phi_identity(x):
+    """The identity feature map of the mLSTM step ([card] Implementation
+    sketch: mLSTM fits the loop with the identity as its feature map)."""
+    return _f64(x).copy()
+
+
 def features(x, phi="elu1", W=None):
     if phi == "elu1":
         return phi_elu1(x)
+    if phi == "identity":
+        return phi_identity(x)
     if phi == "rff":
         if W is None:
             raise ValueError("rff feature map needs W")
@@ -109,6 +123,33 @@ def decay_coefficients(decay=None, gate=None):
     return None, None
 
 
+def readout(num, den, eps=1e-6, normalize=True):
+    """The read-out from the numerator phi(q)^T S and the denominator
+    phi(q)^T z:
+      normalize=True  -- num / (den + eps) ([kb] section 3 sketch);
+      normalize=False -- num alone, the normaliser-free form ([card] SSD);
+      "max1"          -- num / max(|den|, 1) ([card] mLSTM read-out).
+    num: [..., d_v]; den: [...]."""
+    num, den = _f64(num), _f64(den)
+    if normalize is True:
+        return num / (den + eps)[..., None]
+    if normalize is False:
+        return num
+    if normalize == "max1":
+        return num / np.maximum(np.abs(den), 1.0)[..., None]
+    raise ValueError(f"unknown read-out {normalize!r}")
+
+
+def _readout_scalar(num, den, eps, normalize):
+    if normalize is True:
+        return num / (den + eps)
+    if normalize is False:
+        return num
+    if normalize == "max1":
+        return num / max(abs(den), 1.0)
+    raise ValueError(f"unknown read-out {normalize!r}")
+
+
 # --------------------------------------------------------------------------
 # The recurrence (the method's algorithm)
 # --------------------------------------------------------------------------
@@ -126,7 +167,8 @@ def recurrence(fq, fk, v, alpha=None, beta=None, eps=1e-6, S0=None, z0=None, nor
     [card] Implementation sketch (decay on the old state only).
     normalize=False returns the numerator S_t^T phi(q_t) alone, the
     normaliser-free read-out of [card] "Decaying linear attention with a
-    scalar state (SSD)"; z is still carried.
+    scalar state (SSD)"; z is still carried.  normalize="max1" divides by
+    max(|z_t^T phi(q_t)|, 1) instead ([card] mLSTM read-out).
 
     fq, fk: [..., T, d'] features; v: [..., T, d_v]; alpha, beta: [..., T]
     or None.  S0: [..., d', d_v], z0: [..., d'] (default zero state).
@@ -158,11 +200,8 @@ def recurrence(fq, fk, v, alpha=None, beta=None, eps=1e-6, S0=None, z0=None, nor
             z = z + new_z
         q_t = fq[..., t, :]
         num = np.einsum("...d,...dv->...v", q_t, S)
-        if normalize:
-            den = np.einsum("...d,...d->...", q_t, z)
-            o[..., t, :] = num / (den + eps)[..., None]
-        else:
-            o[..., t, :] = num
+        den = np.einsum("...d,...d->...", q_t, z)
+        o[..., t, :] = readout(num, den, eps, normalize)
     return o, S, z
 
 
@@ -229,11 +268,7 @@ def masked_quadratic(fq, fk, v, alpha=None, beta=None, eps=1e-6, normalize=True)
     w = scores * decay_products(alpha, T)
     if beta is not None:
         w = w * _f64(beta)[..., None, :]
-    num = w @ v
-    if not normalize:
-        return num
-    den = w.sum(axis=-1)
-    return num / (den + eps)[..., None]
+    return readout(w @ v, w.sum(axis=-1), eps, normalize)
 
 
 def kernel_attention_by_definition(fq, fk, v, alpha=None, beta=None, eps=1e-6, normalize=True):
@@ -256,7 +291,7 @@ def kernel_attention_by_definition(fq, fk, v, alpha=None, beta=None, eps=1e-6, n
             for c in range(dv):
                 num[c] += sim * float(v[j, c])
         for c in range(dv):
-            out[i, c] = num[c] / (den + eps) if normalize else num[c]
+            out[i, c] = _readout_scalar(num[c], den, eps, normalize)
     return out
 
 
@@ -288,9 +323,7 @@ def output_at(fq_t, fk, v, t, alpha=None, beta=None, eps=1e-6, S0=None, z0=None,
         num = num + carry[..., None] * np.einsum("...d,...dv->...v", fq_t, _f64(S0))
     if z0 is not None:
         den = den + carry * np.einsum("...d,...d->...", fq_t, _f64(z0))
-    if not normalize:
-        return num
-    return num / (den + eps)[..., None]
+    return readout(num, den, eps, normalize)
 
 
 def final_state(fk, v, alpha=None, beta=None, S0=None, z0=None):
@@ -318,6 +351,157 @@ def final_state(fk, v, alpha=None, beta=None, S0=None, z0=None):
     if z0 is not None:
         z = z + carry[..., None] * _f64(z0)
     return S, z
+
+
+# --------------------------------------------------------------------------
+# mLSTM: matrix memory with exponential gates ([card] Variants / "Matrix
+# memory with exponential gates (mLSTM)"; [card] Implementation sketch: the
+# mLSTM step is the loop above with the identity feature map,
+# input-dependent gates and a normaliser read-out)
+#
+# Per token, with forget gate f_t and input gate i_t = exp(itilde_t):
+#     C_t = f_t C_{t-1} + i_t k_t v_t^T,   n_t = f_t n_{t-1} + i_t k_t,
+#     o_t = C_t^T q_t / max(|n_t^T q_t|, 1),
+# i.e. the recurrence with phi = identity, alpha = f, beta = i and the
+# "max1" read-out (the page's C is this library's S transposed, n is z).
+# f_t = sigmoid(ftilde_t), or exp(ftilde_t) in the exponential form.
+#
+# The stabiliser: the page says only that a stabiliser state keeps the
+# exponentials from overflowing.  Reading: a log-domain running maximum
+#     m_t = max(log f_t + m_{t-1}, itilde_t),
+# with the state kept as (S', z', m) = (e^{-m} S, e^{-m} z, m):
+#     S'_t = e^{log f_t + m_{t-1} - m_t} S'_{t-1} + e^{itilde_t - m_t} k_t v_t^T,
+# both factors <= 1, and the read-out floor 1 becoming e^{-m_t}
+#     o_t = q_t^T S'_t / max(|q_t^T z'_t|, e^{-m_t}),
+# which is the same number as the unstabilised read-out.  A zero state has
+# m = 0.
+# --------------------------------------------------------------------------
+
+def log_forget(fgate, exp_form=False):
+    """log f_t from the forget-gate pre-activation: log sigmoid(x) =
+    -log(1 + e^{-x}), or x itself for the exponential forget gate."""
+    x = _f64(fgate)
+    return x.copy() if exp_form else -np.logaddexp(0.0, -x)
+
+
+def mlstm_coefficients(igate, fgate, exp_form=False):
+    """Unstabilised (alpha, beta) = (f_t, i_t) = (sigmoid or exp of the forget
+    pre-activation, exp of the input pre-activation), for the definition."""
+    return np.exp(log_forget(fgate, exp_form)), np.exp(_f64(igate))
+
+
+def mlstm_by_definition(q, k, v, igate, fgate, exp_form=False, eps=1e-6, S0=None, z0=None,
+                        normalize="max1"):
+    """The mLSTM recurrence taken literally (no stabiliser), in float64:
+    identity features, alpha = f, beta = i.  Returns (o, S, z) with the true
+    (unscaled) state.  Overflows for input pre-activations beyond ~700."""
+    f, i = mlstm_coefficients(igate, fgate, exp_form)
+    return recurrence(phi_identity(q), phi_identity(k), v, f, i, eps, S0, z0, normalize)
+
+
+def _scaled_readout(num, den, eps, normalize, m):
+    """Read-out of a state scaled by e^{-m}: the same number as readout() of
+    the unscaled numerator and denominator."""
+    if normalize is True:
+        return num / (den + eps * np.exp(-m))[..., None]
+    if normalize is False:
+        return num * np.exp(m)[..., None]
+    if normalize == "max1":
+        return num / np.maximum(np.abs(den), np.exp(-m))[..., None]
+    raise ValueError(f"unknown read-out {normalize!r}")
+
+
+def mlstm_recurrence(q, k, v, igate, fgate, exp_form=False, eps=1e-6, S0=None, z0=None,
+                     m0=None, normalize="max1"):
+    """The stabilised mLSTM recurrence (the reading in the comment above),
+    token by token in float64.
+
+    q, k: [..., T, d]; v: [..., T, d_v]; igate, fgate: [..., T] (input and
+    forget pre-activations).  (S0, z0, m0): the scaled start state (zero, and
+    m0 = 0, by default).  Returns (o, S', z', m) with S = e^m S'.
+    """
+    fq, fk, v = phi_identity(q), phi_identity(k), _f64(v)
+    lead = fq.shape[:-2]
+    T, dp = fq.shape[-2], fq.shape[-1]
+    dv = v.shape[-1]
+    S = np.zeros(lead + (dp, dv), F64) if S0 is None else _f64(S0).copy()
+    z = np.zeros(lead + (dp,), F64) if z0 is None else _f64(z0).copy()
+    m = np.zeros(lead, F64) if m0 is None else _f64(m0).copy()
+    lf = log_forget(fgate, exp_form)
+    it = _f64(igate)
+    o = np.empty(lead + (T, dv), F64)
+    for t in range(T):
+        m_new = np.maximum(lf[..., t] + m, it[..., t])
+        fs = np.exp(lf[..., t] + m - m_new)      # stabilised forget factor
+        is_ = np.exp(it[..., t] - m_new)         # stabilised input factor
+        k_t = fk[..., t, :]
+        S = fs[..., None, None] * S + is_[..., None, None] * (k_t[..., :, None] * v[..., t, None, :])
+        z = fs[..., None] * z + is_[..., None] * k_t
+        m = m_new
+        q_t = fq[..., t, :]
+        num = np.einsum("...d,...dv->...v", q_t, S)
+        den = np.einsum("...d,...d->...", q_t, z)
+        o[..., t, :] = _scaled_readout(num, den, eps, normalize, m)
+    return o, S, z, m
+
+
+def mlstm_log_weights(igate, fgate, t, exp_form=False):
+    """lambda_s = itilde_s + sum_{r=s+1..t} log f_r for s = 0..t (the log
+    weight of key s at step t) and the log decay of the start state,
+    sum_{r=0..t} log f_r.  [..., t+1] and [...]."""
+    lf = log_forget(fgate, exp_form)[..., : t + 1]
+    it = _f64(igate)[..., : t + 1]
+    # suffix sums of log f after s: total - inclusive prefix
+    pref = np.cumsum(lf, axis=-1)
+    total = pref[..., -1]
+    return it + (total[..., None] - pref), total
+
+
+def mlstm_output_at(q_t, k, v, t, igate, fgate, exp_form=False, eps=1e-6, S0=None, z0=None,
+                    m0=None, normalize="max1"):
+    """The mLSTM output at one position t by its definition, O(t d):
+    o_t = sum_{s<=t} w_s (q_t.k_s) v_s / max(|sum_s w_s q_t.k_s|, 1) with
+    w_s = i_s prod_{r=s+1..t} f_r, plus the start state decayed by
+    prod_{r<=t} f_r.  Numerator and denominator are both scaled by e^{-M},
+    M the largest log weight, so nothing overflows; the quotient is
+    unchanged."""
+    q_t, k, v = _f64(q_t), _f64(k)[..., : t + 1, :], _f64(v)[..., : t + 1, :]
+    lam, carry = mlstm_log_weights(igate, fgate, t, exp_form)
+    lead = lam.shape[:-1]
+    m0 = np.zeros(lead, F64) if m0 is None else _f64(m0)
+    lc = carry + m0                                   # log scale of the start state's term
+    M = np.maximum(lam.max(axis=-1), lc)
+    w = np.exp(lam - M[..., None]) * np.einsum("...d,...sd->...s", q_t, k)
+    num = np.einsum("...s,...sv->...v", w, v)
+    den = w.sum(axis=-1)
+    if S0 is not None:
+        num = num + np.exp(lc - M)[..., None] * np.einsum("...d,...dv->...v", q_t, _f64(S0))
+    if z0 is not None:
+        den = den + np.exp(lc - M) * np.einsum("...d,...d->...", q_t, _f64(z0))
+    return _scaled_readout(num, den, eps, normalize, M)
+
+
+def mlstm_final_state(k, v, igate, fgate, exp_form=False, S0=None, z0=None, m0=None):
+    """The scaled state after T tokens in closed form: the stabiliser is the
+    max-plus unrolling of its recurrence,
+        m_T = max(m0 + sum_r log f_r, max_s (itilde_s + sum_{r>s} log f_r)),
+    and S' = sum_s e^{lambda_s - m_T} k_s v_s^T + e^{m0 + sum log f - m_T} S0'
+    (z' likewise).  Returns (S', z', m_T)."""
+    k, v = _f64(k), _f64(v)
+    T = k.shape[-2]
+    lam, carry = mlstm_log_weights(igate, fgate, T - 1, exp_form)
+    lead = lam.shape[:-1]
+    m0 = np.zeros(lead, F64) if m0 is None else _f64(m0)
+    lc = carry + m0
+    m = np.maximum(lam.max(axis=-1), lc)
+    w = np.exp(lam - m[..., None])
+    S = np.einsum("...s,...sd,...sv->...dv", w, k, v, optimize=True)
+    z = np.einsum("...s,...sd->...d", w, k)
+    if S0 is not None:
+        S = S + np.exp(lc - m)[..., None, None] * _f64(S0)
+    if z0 is not None:
+        z = z + np.exp(lc - m)[..., None] * _f64(z0)
+    return S, z, m
 
 
 # --------------------------------------------------------------------------
@@ -361,10 +545,8 @@ def noncausal_linear_attention(q, k, v, phi="elu1", W=None, eps=1e-6, S0=None, z
     if z0 is not None:
         z = z + _f64(z0)
     num = fq @ S
-    if not normalize:
-        return num, S, z
     den = np.einsum("...td,...d->...t", fq, z)
-    return num / (den + eps)[..., None], S, z
+    return readout(num, den, eps, normalize), S, z
 
 
 def noncausal_by_definition(fq, fk, v, eps=1e-6, normalize=True):
@@ -382,7 +564,7 @@ def noncausal_by_definition(fq, fk, v, eps=1e-6, normalize=True):
             for c in range(dv):
                 num[c] += sim * float(v[j, c])
         for c in range(dv):
-            out[i, c] = num[c] / (den + eps) if normalize else num[c]
+            out[i, c] = _readout_scalar(num[c], den, eps, normalize)
     return out
 
 
