@@ -7,6 +7,13 @@ in the library's HIP kernels; there is no Python or CPU fallback.
 
     out, S, z = prefill(q, k, v)                   # q, k, v: [B, H, T, d] on cuda
     o = decode_step(q1, k1, v1, S, z)              # one token, updates S, z in place
+
+mLSTM gates (identity features, forget and exponential input gates, the
+max(|den|, 1) read-out and a stabiliser m carried with the state):
+
+    out, S, z, m = prefill(q, k, v, phi="identity", igate=ig, fgate=fg, normalize="max1")
+    o = decode_step(q1, k1, v1, S, z, phi="identity", igate=ig1, fgate=fg1, stab=m,
+                    normalize="max1")
 """
 from __future__ import annotations
 
@@ -52,13 +59,27 @@ def _need(t, name, device=None, dtype=None, shape=None):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
+_NORMS = {True: _lib.LA_NORM_SUM, "sum": _lib.LA_NORM_SUM, False: _lib.LA_NORM_NONE,
+          "none": _lib.LA_NORM_NONE, "max1": _lib.LA_NORM_MAX1}
+
+
+def _norm_code(normalize):
+    for key, code in _NORMS.items():
+        if normalize is key or (isinstance(key, str) and normalize == key):
+            return code
+    raise ValueError(f"unknown read-out {normalize!r}; use True, False or 'max1'")
+
+
 def make_desc(B, H, T, d_h, d_v, dtype_code, phi="elu1", W=None, rff_D=None, decay=None,
               gate=None, eps=1e-6, chunk=0, segments=0, out_dtype_code=None,
-              normalize=True, causal=True) -> _lib.LaDesc:
-    """Build an `la_desc`.  `decay` (SSD a_t) and `gate` (RFA g_t) are exclusive;
-    `out_dtype_code` defaults to the input type; `normalize=False` selects the
-    read-out without the normaliser (LA_NORM_NONE); `causal=False` the
-    non-causal prefill."""
+              normalize=True, causal=True, igate=None, fgate=None, fgate_exp=False,
+              stab=None) -> _lib.LaDesc:
+    """Build an `la_desc`.  `decay` (SSD a_t), `gate` (RFA g_t) and the mLSTM
+    gates (`fgate` forget and `igate` input pre-activations, with the
+    stabiliser tensor `stab`) are exclusive; `out_dtype_code` defaults to the
+    input type; `normalize` is True (phi(q).S / (phi(q).z + eps)), False (the
+    numerator alone) or "max1" (divided by max(|phi(q).z|, 1)); `causal=False`
+    the non-causal prefill."""
     d = _lib.LaDesc()
     d.B, d.H, d.T, d.d_h, d.d_v = int(B), int(H), int(T), int(d_h), int(d_v)
     d.dtype = int(dtype_code)
@@ -69,19 +90,29 @@ def make_desc(B, H, T, d_h, d_v, dtype_code, phi="elu1", W=None, rff_D=None, dec
         d.phi = _lib.LA_PHI_RFF
         d.rff_D = int(rff_D if rff_D is not None else (W.shape[-2] if W is not None else 0))
         d.rff_W = None if W is None else W.data_ptr()
+    elif phi == "identity":
+        d.phi, d.rff_D, d.rff_W = _lib.LA_PHI_IDENTITY, 0, None
     else:
         raise ValueError(f"unknown feature map {phi!r}")
-    if decay is not None and gate is not None:
-        raise ValueError("decay and gate are exclusive")
+    mlstm = igate is not None or fgate is not None
+    if sum(x is not None for x in (decay, gate)) + (1 if mlstm else 0) > 1:
+        raise ValueError("decay, gate and the mLSTM gates are exclusive")
+    d.igate, d.fgate_exp, d.stab = None, 0, None
     if decay is not None:
         d.decay_kind, d.decay = _lib.LA_DECAY_SSD, decay.data_ptr()
     elif gate is not None:
         d.decay_kind, d.decay = _lib.LA_GATE_RFA, gate.data_ptr()
+    elif mlstm:
+        if igate is None or fgate is None:
+            raise ValueError("the mLSTM gates need both igate and fgate")
+        d.decay_kind, d.decay = _lib.LA_GATE_MLSTM, fgate.data_ptr()
+        d.igate, d.fgate_exp = igate.data_ptr(), int(bool(fgate_exp))
+        d.stab = None if stab is None else stab.data_ptr()
     else:
         d.decay_kind, d.decay = _lib.LA_DECAY_NONE, None
     d.eps = float(eps)
     d.chunk, d.segments = int(chunk), int(segments)
-    d.norm = _lib.LA_NORM_SUM if normalize else _lib.LA_NORM_NONE
+    d.norm = _norm_code(normalize)
     d.noncausal = 0 if causal else 1
     return d
 
@@ -94,19 +125,28 @@ def _stream(device):
     return ctypes.c_void_p(_torch().cuda.current_stream(device).cuda_stream)
 
 
-def state_init(B: int, H: int, d_prime: int, d_v: int, device="cuda") -> Tuple["torch.Tensor", "torch.Tensor"]:
-    """Allocate a state (S [B,H,d',d_v], z [B,H,d'], fp32) and zero it with la_state_init."""
+def state_init(B: int, H: int, d_prime: int, d_v: int, device="cuda", stab: bool = False):
+    """Allocate a state (S [B,H,d',d_v], z [B,H,d'], fp32) and zero it with
+    la_state_init; with stab=True also the mLSTM stabiliser m [B,H] (zero),
+    returned as a third tensor."""
     torch = _torch()
     device = torch.device(device)
     S = torch.empty(B, H, d_prime, d_v, dtype=torch.float32, device=device)
     z = torch.empty(B, H, d_prime, dtype=torch.float32, device=device)
-    desc = make_desc(B, H, 0, d_prime, d_v, _lib.LA_F32)
+    if stab:
+        m = torch.empty(B, H, dtype=torch.float32, device=device)
+        g = torch.empty(1, dtype=torch.float32, device=device)   # stands in for the gates
+        desc = make_desc(B, H, 0, d_prime, d_v, _lib.LA_F32, phi="identity", igate=g, fgate=g,
+                         stab=m)
+    else:
+        desc = make_desc(B, H, 0, d_prime, d_v, _lib.LA_F32)
     _lib.check(_lib.lib().la_state_init(ctypes.byref(desc), _ptr(S), _ptr(z), _stream(device)))
-    return S, z
+    return (S, z, m) if stab else (S, z)
 
 
 def _prefill_desc(q, k, v, phi, W, decay, gate, eps, chunk, segments, out_dtype=None,
-                  normalize=True, causal=True):
+                  normalize=True, causal=True, igate=None, fgate=None, fgate_exp=False,
+                  stab=None):
     torch = _torch()
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, n, device=q.device, dtype=q.dtype)
@@ -118,11 +158,14 @@ def _prefill_desc(q, k, v, phi, W, decay, gate, eps, chunk, segments, out_dtype=
     _need(v, "v", shape=(B, H, T, d_v))
     if W is not None:
         _need(W, "W", device=q.device, dtype=torch.float32)
-    for a, n in ((decay, "decay"), (gate, "gate")):
+    for a, n in ((decay, "decay"), (gate, "gate"), (igate, "igate"), (fgate, "fgate")):
         if a is not None:
             _need(a, n, device=q.device, dtype=torch.float32, shape=(B, H, T))
+    if stab is not None:
+        _need(stab, "stab", device=q.device, dtype=torch.float32, shape=(B, H))
     desc = make_desc(B, H, T, d_h, d_v, _dtype_code(q.dtype), phi, W, None, decay, gate, eps,
-                     chunk, segments, _dtype_code(out_dtype or q.dtype), normalize, causal)
+                     chunk, segments, _dtype_code(out_dtype or q.dtype), normalize, causal,
+                     igate, fgate, fgate_exp, stab)
     return desc, (B, H, T, d_h, d_v)
 
 
@@ -142,28 +185,42 @@ def prefill_plan(desc: _lib.LaDesc):
 
 def prefill(q, k, v, *, phi: str = "elu1", W=None, decay=None, gate=None, eps: float = 1e-6,
             state: Optional[tuple] = None, chunk: int = 0, segments: int = 0, out=None,
-            workspace=None, out_dtype=None, normalize: bool = True, causal: bool = True):
+            workspace=None, out_dtype=None, normalize=True, causal: bool = True,
+            igate=None, fgate=None, fgate_exp: bool = False):
     """Causal linear attention over [B, H, T, d] inputs on the GPU.
 
     Returns (out, S, z).  If `state=(S, z)` is given the recurrence continues
     from it and the final state is written back into those tensors (in place);
     otherwise a zero state is allocated.  `out_dtype` is q's dtype (default)
     or torch.float32.  `normalize=False` returns the numerator phi(q)^T S
-    alone (LA_NORM_NONE); z is still carried.  `causal=False` is the
-    non-causal form: the state takes in the whole sequence, then every token
-    reads it out.
+    alone (LA_NORM_NONE); z is still carried; "max1" divides by
+    max(|phi(q)^T z|, 1).  `causal=False` is the non-causal form: the state
+    takes in the whole sequence, then every token reads it out.
+
+    mLSTM gates: `fgate` and `igate` ([B, H, T] fp32 pre-activations; forget
+    gate sigmoid(fgate), or exp(fgate) with fgate_exp=True; input gate
+    exp(igate)).  The state then carries the stabiliser m [B, H]: `state` is
+    (S, z, m) and the result (out, S, z, m), with S, z held scaled by e^{-m}.
     """
     torch = _torch()
     out_dtype = out_dtype or q.dtype
-    desc, (B, H, T, d_h, d_v) = _prefill_desc(q, k, v, phi, W, decay, gate, eps, chunk, segments,
-                                              out_dtype, normalize, causal)
-    dp = feature_dim(d_h, phi, desc.rff_D)
+    mlstm = igate is not None or fgate is not None
+    B, H = q.shape[0], q.shape[1]
     if state is None:
-        S, z = state_init(B, H, dp, d_v, q.device)
+        dp = feature_dim(q.shape[-1], phi, W.shape[-2] if W is not None else 0)
+        st = state_init(B, H, dp, v.shape[-1], q.device, stab=mlstm)
     else:
-        S, z = state
-        _need(S, "S", device=q.device, dtype=torch.float32, shape=(B, H, dp, d_v))
-        _need(z, "z", device=q.device, dtype=torch.float32, shape=(B, H, dp))
+        st = tuple(state)
+        if len(st) != (3 if mlstm else 2):
+            raise ValueError("state is (S, z, m) with the mLSTM gates, (S, z) otherwise")
+    m = st[2] if mlstm else None
+    desc, (B, H, T, d_h, d_v) = _prefill_desc(q, k, v, phi, W, decay, gate, eps, chunk, segments,
+                                              out_dtype, normalize, causal, igate, fgate,
+                                              fgate_exp, m)
+    dp = feature_dim(d_h, phi, desc.rff_D)
+    S, z = st[0], st[1]
+    _need(S, "S", device=q.device, dtype=torch.float32, shape=(B, H, dp, d_v))
+    _need(z, "z", device=q.device, dtype=torch.float32, shape=(B, H, dp))
     if out is None:
         out = torch.empty(B, H, T, d_v, dtype=out_dtype, device=q.device)
     else:
@@ -174,15 +231,16 @@ def prefill(q, k, v, *, phi: str = "elu1", W=None, decay=None, gate=None, eps: f
     _lib.check(_lib.lib().la_prefill(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(S), _ptr(z),
                                      _ptr(out), _ptr(workspace) if nws else None, nws,
                                      _stream(q.device)))
-    return out, S, z
+    return (out, S, z, m) if mlstm else (out, S, z)
 
 
 def prefill_stage(stage: int, q, k, v, S, z, out, workspace, *, phi="elu1", W=None, decay=None,
-                  gate=None, eps=1e-6, chunk=0, segments=0, normalize=True, causal=True):
+                  gate=None, eps=1e-6, chunk=0, segments=0, normalize=True, causal=True,
+                  igate=None, fgate=None, fgate_exp=False, stab=None):
     """Run one of la_prefill's three stages (1 segment states, 2 scan, 3 outputs);
     out's dtype selects the output type."""
     desc, _ = _prefill_desc(q, k, v, phi, W, decay, gate, eps, chunk, segments, out.dtype,
-                            normalize, causal)
+                            normalize, causal, igate, fgate, fgate_exp, stab)
     nws = prefill_workspace_size(desc)
     _lib.check(_lib.lib().la_prefill_stage(ctypes.byref(desc), int(stage), _ptr(q), _ptr(k), _ptr(v),
                                            _ptr(S), _ptr(z), _ptr(out),
@@ -191,11 +249,14 @@ def prefill_stage(stage: int, q, k, v, S, z, out, workspace, *, phi="elu1", W=No
 
 
 def decode_step(q, k, v, S, z, *, phi: str = "elu1", W=None, decay=None, gate=None,
-                eps: float = 1e-6, out=None, out_dtype=None, normalize: bool = True):
+                eps: float = 1e-6, out=None, out_dtype=None, normalize=True, igate=None,
+                fgate=None, fgate_exp: bool = False, stab=None):
     """One token for B sequences x H heads: q, k [B, H, d_h], v [B, H, d_v].
 
     Updates (S, z) in place and returns out [B, H, d_v] (dtype of q);
-    `normalize=False` returns the numerator alone.
+    `normalize=False` returns the numerator alone, "max1" divides by
+    max(|phi(q).z|, 1).  mLSTM gates: `igate`, `fgate` [B, H] and the
+    stabiliser `stab` [B, H], updated in place with the state.
     """
     torch = _torch()
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
@@ -208,12 +269,14 @@ def decode_step(q, k, v, S, z, *, phi: str = "elu1", W=None, decay=None, gate=No
     _need(v, "v", shape=(B, H, d_v))
     if W is not None:
         _need(W, "W", device=q.device, dtype=torch.float32)
-    for a, n in ((decay, "decay"), (gate, "gate")):
+    for a, n in ((decay, "decay"), (gate, "gate"), (igate, "igate"), (fgate, "fgate"),
+                 (stab, "stab")):
         if a is not None:
             _need(a, n, device=q.device, dtype=torch.float32, shape=(B, H))
     out_dtype = out_dtype or q.dtype
     desc = make_desc(B, H, 1, d_h, d_v, _dtype_code(q.dtype), phi, W, None, decay, gate, eps,
-                     out_dtype_code=_dtype_code(out_dtype), normalize=normalize)
+                     out_dtype_code=_dtype_code(out_dtype), normalize=normalize, igate=igate,
+                     fgate=fgate, fgate_exp=fgate_exp, stab=stab)
     dp = feature_dim(d_h, phi, desc.rff_D)
     _need(S, "S", device=q.device, dtype=torch.float32, shape=(B, H, dp, d_v))
     _need(z, "z", device=q.device, dtype=torch.float32, shape=(B, H, dp))

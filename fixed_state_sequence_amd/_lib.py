@@ -15,9 +15,9 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "linattn.h")
 
 LA_OK, LA_EINVAL, LA_EUNSUPPORTED, LA_EHIP = 0, 1, 2, 3
 LA_F32, LA_BF16, LA_F16 = 0, 1, 2
-LA_PHI_ELU1, LA_PHI_RFF = 0, 1
-LA_DECAY_NONE, LA_DECAY_SSD, LA_GATE_RFA = 0, 1, 2
-LA_NORM_SUM, LA_NORM_NONE = 0, 1
+LA_PHI_ELU1, LA_PHI_RFF, LA_PHI_IDENTITY = 0, 1, 2
+LA_DECAY_NONE, LA_DECAY_SSD, LA_GATE_RFA, LA_GATE_MLSTM = 0, 1, 2, 3
+LA_NORM_SUM, LA_NORM_NONE, LA_NORM_MAX1 = 0, 1, 2
 
 
 class LaDesc(ctypes.Structure):
@@ -30,6 +30,7 @@ class LaDesc(ctypes.Structure):
         ("decay_kind", ctypes.c_int), ("decay", ctypes.c_void_p),
         ("eps", ctypes.c_float), ("chunk", ctypes.c_int), ("segments", ctypes.c_int),
         ("norm", ctypes.c_int), ("noncausal", ctypes.c_int),
+        ("igate", ctypes.c_void_p), ("fgate_exp", ctypes.c_int), ("stab", ctypes.c_void_p),
     ]
 
 

@@ -51,6 +51,10 @@ la_status check_desc(const la_desc* d, bool prefill, la::Problem* p) {
     if (d->rff_D != 0 || d->rff_W != nullptr)
       return fail(LA_EINVAL, "elu+1 feature map takes no rff_D / rff_W");
     dp = d->d_h;
+  } else if (d->phi == LA_PHI_IDENTITY) {
+    if (d->rff_D != 0 || d->rff_W != nullptr)
+      return fail(LA_EINVAL, "identity feature map takes no rff_D / rff_W");
+    dp = d->d_h;
   } else if (d->phi == LA_PHI_RFF) {
     if (d->rff_D < 1) return fail(LA_EINVAL, "RFF needs rff_D >= 1 (got %d)", d->rff_D);
     if (!d->rff_W) return fail(LA_EINVAL, "RFF needs rff_W");
@@ -62,14 +66,25 @@ la_status check_desc(const la_desc* d, bool prefill, la::Problem* p) {
   }
   if (d->decay_kind == LA_DECAY_NONE) {
     if (d->decay) return fail(LA_EINVAL, "decay array given with LA_DECAY_NONE");
-  } else if (d->decay_kind == LA_DECAY_SSD || d->decay_kind == LA_GATE_RFA) {
+  } else if (d->decay_kind == LA_DECAY_SSD || d->decay_kind == LA_GATE_RFA ||
+             d->decay_kind == LA_GATE_MLSTM) {
     if (!d->decay) return fail(LA_EINVAL, "decay/gate array missing");
     if (!aligned(d->decay, 4)) return fail(LA_EINVAL, "decay must be 4-byte aligned");
   } else {
     return fail(LA_EINVAL, "unknown decay kind %d", int(d->decay_kind));
   }
+  if (d->decay_kind == LA_GATE_MLSTM) {
+    if (!d->igate) return fail(LA_EINVAL, "mLSTM gates need igate (input-gate pre-activations)");
+    if (!aligned(d->igate, 4)) return fail(LA_EINVAL, "igate must be 4-byte aligned");
+    if (!d->stab) return fail(LA_EINVAL, "mLSTM gates need stab (stabiliser state [B, H])");
+    if (!aligned(d->stab, 4)) return fail(LA_EINVAL, "stab must be 4-byte aligned");
+    if (d->fgate_exp != 0 && d->fgate_exp != 1)
+      return fail(LA_EINVAL, "fgate_exp must be 0 or 1 (got %d)", d->fgate_exp);
+  } else if (d->igate || d->stab || d->fgate_exp) {
+    return fail(LA_EINVAL, "igate, stab and fgate_exp are for LA_GATE_MLSTM only");
+  }
   if (!std::isfinite(d->eps)) return fail(LA_EINVAL, "eps must be finite");
-  if (d->norm != LA_NORM_SUM && d->norm != LA_NORM_NONE)
+  if (d->norm != LA_NORM_SUM && d->norm != LA_NORM_NONE && d->norm != LA_NORM_MAX1)
     return fail(LA_EINVAL, "unknown read-out form %d", int(d->norm));
   if (d->noncausal != 0 && d->noncausal != 1)
     return fail(LA_EINVAL, "noncausal must be 0 or 1 (got %d)", d->noncausal);
@@ -91,7 +106,10 @@ la_status check_desc(const la_desc* d, bool prefill, la::Problem* p) {
   p->dh = d->d_h; p->dv = d->d_v; p->dp = dp;
   p->dtype = d->dtype; p->out_dtype = d->out_dtype; p->phi = d->phi; p->D = d->rff_D; p->W = d->rff_W;
   p->decay_kind = d->decay_kind; p->decay = d->decay; p->eps = d->eps;
-  p->nonorm = d->norm == LA_NORM_NONE ? 1 : 0;
+  p->norm = int(d->norm);
+  p->igate = d->igate;
+  p->fgate_exp = d->fgate_exp;
+  p->stab = d->stab;
   p->noncausal = d->noncausal;
   p->chunk = d->chunk ? d->chunk : 32;
   p->segments = 1;
@@ -184,8 +202,8 @@ la_status la_state_init(const la_desc* desc, float* S, float* z, void* stream) {
   LA_TRY(check_ptr(S, "S"));
   LA_TRY(check_ptr(z, "z"));
   (void)hipGetLastError();
-  return launched(la::launch_state_init(S, p.BH() * p.dp * p.dv, z, p.BH() * p.dp,
-                                        static_cast<hipStream_t>(stream)));
+  return launched(la::launch_state_init(S, p.BH() * p.dp * p.dv, z, p.BH() * p.dp, p.stab,
+                                        p.stab ? p.BH() : 0, static_cast<hipStream_t>(stream)));
 }
 
 la_status la_prefill_workspace_size(const la_desc* desc, size_t* bytes) {

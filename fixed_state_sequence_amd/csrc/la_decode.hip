@@ -4,6 +4,10 @@
 // wikillm "Linear attention", Implementation sketch and Variants / RFA):
 //   S <- alpha S + beta phi(k) v^T,  z <- alpha z + beta phi(k),
 //   o  = phi(q)^T S / (phi(q)^T z + eps).
+// mLSTM gates (wikillm "Linear attention", Variants / mLSTM): alpha, beta are
+// the forget gate and the exponential input gate, applied to a state held
+// scaled by e^{-m} as e^{log f + m - m'} and e^{itilde - m'}, with the
+// stabiliser m' = max(log f + m, itilde) stored back per state.
 // The step reads and writes the whole state once and does O(d' d_v) work on
 // it, so it is bound by HBM bandwidth (wikillm "When to use which": decoding
 // with a fixed-size state is memory-bound).
@@ -34,11 +38,15 @@ struct DecArgs {
   float* S;
   float* z;
   const float* W;       // [H, D, dh] (RFF)
-  const float* decay;   // [N, H] (SSD a or RFA g)
+  const float* decay;   // [N, H] (SSD a, RFA g or the mLSTM forget pre-activation)
+  const float* igate;   // [N, H] mLSTM input-gate pre-activation
+  float* stab;          // [N, H] mLSTM stabiliser
   int N, H, dh;
   int dhp;              // padded LDS row of W (floats)
   int out_f32;
-  int nonorm;           // read-out without the normaliser
+  int norm;             // read-out form (LA_NORM_*)
+  int ident;            // identity feature map (else elu+1), when not RFF
+  int fgate_exp;        // mLSTM forget gate: sigmoid (0) or exp (1)
   float eps;
 };
 
@@ -104,8 +112,16 @@ __global__ __launch_bounds__(NT) void decode_kernel(const DecArgs a) {
     const int f = (j * G::WPS + wsub) * 64 + lane;
     zr[j] = (valid && f < DP) ? zg[f] : 0.f;
   }
-  float alpha = 1.f, beta = 1.f;
-  if constexpr (DECAY != 0) {
+  float alpha = 1.f, beta = 1.f, m = 0.f;
+  if constexpr (DECAY == 3) {
+    // stabilised mLSTM gates: m = max(log f + m_old, itilde)
+    const float lf = valid ? log_forget(a.decay[st], a.fgate_exp) : 0.f;
+    const float it = valid ? a.igate[st] : 0.f;
+    const float mo = valid ? a.stab[st] : 0.f;
+    m = fmaxf(lf + mo, it);
+    alpha = expf(lf + mo - m);
+    beta = expf(it - m);
+  } else if constexpr (DECAY != 0) {
     alpha = valid ? a.decay[st] : 0.f;
     if constexpr (DECAY == 2) beta = 1.f - alpha;
   }
@@ -184,8 +200,9 @@ __global__ __launch_bounds__(NT) void decode_kernel(const DecArgs a) {
     float* fq = s_phi[sidx][0];
     float* fk = s_phi[sidx][1];
     for (int f = lane; f < DP; f += 64) {
-      fq[f] = elu1_accurate(s_x[sidx][0][f]);
-      fk[f] = elu1_accurate(s_x[sidx][1][f]);
+      const float x = s_x[sidx][0][f], y = s_x[sidx][1][f];
+      fq[f] = a.ident ? x : elu1_accurate(x);
+      fk[f] = a.ident ? y : elu1_accurate(y);
     }
   }
   __syncthreads();
@@ -252,8 +269,12 @@ __global__ __launch_bounds__(NT) void decode_kernel(const DecArgs a) {
       }
     }
   }
+  if constexpr (DECAY == 3) {
+    if (valid && wsub == 0 && lane == 0) a.stab[st] = m;
+  }
   if (valid && wsub == 0 && lane < G::CG) {
-    const float inv = a.nonorm ? 1.f : 1.0f / (den + a.eps);
+    const float inv = a.norm == LA_NORM_SUM && DECAY != 3 ? 1.0f / (den + a.eps)
+                                                          : readout_factor(a.norm, den, a.eps, m);
     const int64_t o0 = st * DV + 4 * cg;
     if (a.out_f32) {
       *reinterpret_cast<float4*>(static_cast<float*>(a.out) + o0) =
@@ -278,6 +299,7 @@ hipError_t launch_decay(const DecArgs& a, la_decay kind, hipStream_t st) {
     case LA_DECAY_NONE: decode_kernel<DT, DV, DP, RFF, 0><<<grid, block, lds, st>>>(a); break;
     case LA_DECAY_SSD: decode_kernel<DT, DV, DP, RFF, 1><<<grid, block, lds, st>>>(a); break;
     case LA_GATE_RFA: decode_kernel<DT, DV, DP, RFF, 2><<<grid, block, lds, st>>>(a); break;
+    case LA_GATE_MLSTM: decode_kernel<DT, DV, DP, RFF, 3><<<grid, block, lds, st>>>(a); break;
   }
   return hipGetLastError();
 }
@@ -320,12 +342,14 @@ hipError_t launch_decode(const Problem& p, const void* q, const void* k, const v
                          float* z, void* out, hipStream_t stream) {
   DecArgs a;
   a.q = q; a.k = k; a.v = v; a.out = out; a.S = S; a.z = z;
-  a.W = p.W; a.decay = p.decay;
+  a.W = p.W; a.decay = p.decay; a.igate = p.igate; a.stab = p.stab;
   a.N = p.B; a.H = p.H; a.dh = p.dh;
   a.dhp = ((p.dh + 3) / 4) * 4 + 4;
   a.out_f32 = p.out_dtype == LA_F32 ? 1 : 0;
   a.eps = p.eps;
-  a.nonorm = p.nonorm;
+  a.norm = p.norm;
+  a.ident = p.phi == LA_PHI_IDENTITY ? 1 : 0;
+  a.fgate_exp = p.fgate_exp;
   switch (p.dtype) {
     case LA_F32: return launch_dt<float>(a, p.dp, p.dv, p.phi, p.decay_kind, stream);
     case LA_BF16: return launch_dt<bf16_t>(a, p.dp, p.dv, p.phi, p.decay_kind, stream);

@@ -6,6 +6,8 @@
 
 #include <cstdint>
 
+#include "linattn.h"
+
 namespace la {
 
 // Storage types of q, k, v and out.  bf16 is carried as raw 16-bit words.
@@ -30,5 +32,29 @@ __device__ __forceinline__ float elu1_accurate(float x) { return x > 0.f ? x + 1
 // x > 0, e^{-x} < 1 < x + 1.  Four VALU operations (the multiply by log2 e
 // takes -|x| as an input modifier; no compare and select).
 __device__ __forceinline__ float elu1_fast(float x) { return fmaxf(x + 1.f, __expf(-fabsf(x))); }
+
+// log f of an mLSTM forget gate from its pre-activation x (wikillm "Linear
+// attention", Variants / mLSTM: a sigmoid forget gate, or an exponential
+// one): log sigmoid(x) = min(x, 0) - log(1 + e^{-|x|}), or x itself.
+__device__ __forceinline__ float log_forget(float x, int exp_form) {
+  return exp_form ? x : fminf(x, 0.f) - log1pf(expf(-fabsf(x)));
+}
+
+// Reciprocal-like read-out factor for the three read-out forms, of a state
+// held scaled by e^{-m} (m = 0 unless the mLSTM stabiliser is on); the
+// output is the numerator times this factor:
+//   LA_NORM_SUM  1 / (den + eps e^{-m})   = true num / (true den + eps)
+//   LA_NORM_NONE e^{m}                    = true num
+//   LA_NORM_MAX1 1 / max(|den|, e^{-m})   = true num / max(|true den|, 1)
+__device__ __forceinline__ float readout_factor(int norm, float den, float eps, float m) {
+  if (norm == LA_NORM_NONE) return expf(m);
+  const float floor = expf(-m);
+  if (norm == LA_NORM_MAX1) return 1.f / fmaxf(fabsf(den), floor);
+  return 1.f / (den + eps * floor);
+}
+
+// Stand-in log weight of a token outside the chunk or the sequence: its
+// exponential is 0 and it never raises a running maximum.
+constexpr float kNoToken = -1e30f;
 
 }  // namespace la

@@ -23,7 +23,10 @@ struct Problem {
   la_decay decay_kind = LA_DECAY_NONE;
   const float* decay = nullptr; // prefill [B,H,T], decode [B,H]
   float eps = 1e-6f;
-  int nonorm = 0;               // 1: read-out without the normaliser (LA_NORM_NONE)
+  int norm = 0;                 // read-out form: LA_NORM_SUM, LA_NORM_NONE or LA_NORM_MAX1
+  const float* igate = nullptr; // mLSTM input-gate pre-activations, shaped like decay
+  int fgate_exp = 0;            // mLSTM forget gate: 0 sigmoid(decay), 1 exp(decay)
+  float* stab = nullptr;        // mLSTM stabiliser m [B, H]
   int noncausal = 0;            // 1: non-causal prefill (every output reads the whole state)
   int chunk = 64;               // prefill chunk length (MFMA path)
   int segments = 1;             // prefill segments per (b,h) (MFMA path)
@@ -44,10 +47,12 @@ bool decode_supported(const Problem& p);
 hipError_t launch_decode(const Problem& p, const void* q, const void* k, const void* v,
                          float* S, float* z, void* out, hipStream_t stream);
 
-// Zero-fill of the state.
-hipError_t launch_state_init(float* S, int64_t nS, float* z, int64_t nz, hipStream_t stream);
+// Zero-fill of the state (m may be null).
+hipError_t launch_state_init(float* S, int64_t nS, float* z, int64_t nz, float* m, int64_t nm,
+                             hipStream_t stream);
 
-// Chunked MFMA prefill (16-bit inputs, elu+1, d' = d_v in {64, 128}).
+// Chunked MFMA prefill (16-bit inputs, d' = d_v in {64, 128}; elu+1 with no
+// decay, SSD decay or the RFA gate, or the identity map with the mLSTM gates).
 bool mfma_supported(const Problem& p);
 bool mfma_chunk_fits(int d, int chunk);
 int mfma_default_segments(const Problem& p);

@@ -15,6 +15,18 @@
 // and z' likewise.  No decay: all exponentials are 1 and only the causal mask
 // remains.
 //
+// mLSTM gates (wikillm "Linear attention", Variants / mLSTM; identity
+// features, alpha = f, beta = e^{itilde}): the state is held scaled by e^{-m},
+// m the stabiliser m_t = max(log f_t + m_{t-1}, itilde_t).  Inside a chunk
+// that starts from (S', z', m0), with a_s = itilde_s - lc_s and the running
+// maximum mu_t = max(m0, max_{s<=t} a_s), the stabiliser is m_t = lc_t + mu_t
+// and every factor is at most 1:
+//   inter-chunk read-out  e^{m0 - mu_t},   key s at query t  e^{a_s - mu_t},
+//   carry  e^{m0 - mu_last},   fold weight  e^{a_s - mu_last};
+// they take the places of e^{lc_t}, e^{lc_t - lc_s} beta_s, e^{lc_last} and
+// w_s above (with "lc_t" := m0 - mu_t and beta_s := e^{a_s - mu_s}), and the
+// read-out divides by max(|den'|, e^{-m_t}) (or den' + eps e^{-m_t}).
+//
 // Parallel schedule.  Each (b, h) sequence is cut into `segments` runs of
 // whole chunks.  Stage 1: one workgroup per sub-segment (half a segment)
 // folds its chunks into a sub-segment state (S_u, z_u, log Gamma_u).  Stage 2:
@@ -140,7 +152,8 @@ struct Cfg {
   static constexpr int EXACT = 128;
   static constexpr int B_B = B_L + 4 * C;             // beta_t, fp32 [C]
   static constexpr int B_DEN = B_B + 4 * C;           // inter-chunk denominators, fp32 [C]
-  static constexpr int B_DZ = B_DEN + 4 * C;          // per-wave z increments, fp32 [NW][DZS]
+  static constexpr int B_M = B_DEN + 4 * C;           // mLSTM stabiliser m_t, fp32 [C]
+  static constexpr int B_DZ = B_M + 4 * C;            // per-wave z increments, fp32 [NW][DZS]
   // z increment of feature 8 fb + e at dz_index: 4 floats of padding after
   // the first 64, so that feature blocks fb and fb + 8 (read together by a
   // wave) fall in different banks
@@ -273,7 +286,10 @@ struct PfArgs {
   void* out;
   float* S;          // caller's state [BH, D, D] (initial in, final out)
   float* z;          // caller's normaliser [BH, D]
-  const float* decay;  // [BH, T] or null
+  const float* decay;  // [BH, T] or null (mLSTM: forget-gate pre-activations)
+  const float* igate;  // [BH, T] mLSTM input-gate pre-activations, or null
+  float* stab;         // [BH] mLSTM stabiliser (initial in, final out), or null
+  int fgate_exp;       // mLSTM forget gate: sigmoid (0) or exp (1)
   // Workspace, per (b, h), NSLOT = nsub nseg slots of D*D + D floats (with
   // more than one segment): stage 1 writes sub-segment u's state into slot u
   // (each segment is cut into nsub sub-segments, so that stage 1 has enough
@@ -281,6 +297,8 @@ struct PfArgs {
   // and writes the final state, carried past the last slot, into (S, z).
   float* ws_state;   // [BH, NSLOT, D*D + D]
   float* ws_logg;    // [BH, NSLOT]: log Gamma of each sub-segment
+  float* ws_m;       // [BH, NSLOT]: mLSTM stabiliser of each sub-segment's state
+  float* ws_m0;      // [BH, nseg + 1]: mLSTM start stabiliser of each segment, then the final one
   int T;
   int nseg;
   int cps;           // chunks per segment
@@ -288,27 +306,31 @@ struct PfArgs {
   int cps_sub;       // chunks per sub-segment (the last one of a segment may be shorter)
   int nslot;         // nsub nseg
   int out_f32;       // out is fp32 (else the input type)
-  int nonorm;        // read-out without the normaliser
+  int norm;          // read-out form (LA_NORM_*)
   int nc;            // non-causal: every output reads the whole sequence's state
   float eps;
 };
 
 // The raw inputs of one chunk as this thread loads them: RPT 16-byte blocks
 // (8 features of one token row) of q, k and v, and the decay/gate value of
-// token `lane` (and `lane + 64`) of the chunk.  The loads are unconditional
-// (rows past the end of the sequence read the last row) so that the compiler
-// can count the loads still in flight exactly when a later chunk's data is
-// used; clean_chunk() then zeroes those rows (and sets their decay to 1).
-template <int RPT, int ND, bool HAS_Q, bool HAS_KV = true>
+// token `lane` (and `lane + 64`) of the chunk (with the mLSTM gates, the
+// forget and the input pre-activation).  The loads are unconditional (rows
+// past the end of the sequence read the last row) so that the compiler can
+// count the loads still in flight exactly when a later chunk's data is used;
+// clean_chunk() then zeroes those rows (and sets their decay to 1).
+template <int RPT, int ND, bool HAS_Q, bool HAS_KV = true, bool HAS_I = false>
 struct RawChunk {
   u32x4 q[HAS_Q ? RPT : 1], k[HAS_KV ? RPT : 1], v[HAS_KV ? RPT : 1];
   float d[ND];
+  float ig[HAS_I ? ND : 1];
 };
 
-template <int C, int D, int RPT, int ND, bool HAS_Q, int DECAY, typename DT, bool HAS_KV>
-__device__ __forceinline__ void fetch_chunk(RawChunk<RPT, ND, HAS_Q, HAS_KV>& r, const DT* qg,
-                                            const DT* kg, const DT* vg, const float* dg, int tok0,
-                                            int T, int rg, int fb, int lane) {
+template <int C, int D, int RPT, int ND, bool HAS_Q, int DECAY, typename DT, bool HAS_KV,
+          bool HAS_I>
+__device__ __forceinline__ void fetch_chunk(RawChunk<RPT, ND, HAS_Q, HAS_KV, HAS_I>& r,
+                                            const DT* qg, const DT* kg, const DT* vg,
+                                            const float* dg, const float* igp, int tok0, int T,
+                                            int rg, int fb, int lane) {
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
     const int t = min(tok0 + RPT * rg + i, T - 1);
@@ -324,14 +346,20 @@ __device__ __forceinline__ void fetch_chunk(RawChunk<RPT, ND, HAS_Q, HAS_KV>& r,
 #pragma unroll
     for (int j = 0; j < ND; ++j) r.d[j] = dg[min(tok0 + lane + 64 * j, T - 1)];
   }
+  if constexpr (DECAY == 3) {
+#pragma unroll
+    for (int j = 0; j < ND; ++j) r.ig[j] = igp[min(tok0 + lane + 64 * j, T - 1)];
+  }
 }
 
 // Rows past the end of the sequence become 0 and decay values of tokens
 // outside the chunk or the sequence become 1 (the loads read in-bounds
-// stand-ins).  The row pass runs only for the chunk holding the end.
-template <int C, int RPT, int ND, bool HAS_Q, int DECAY, bool HAS_KV>
-__device__ __forceinline__ void clean_chunk(RawChunk<RPT, ND, HAS_Q, HAS_KV>& r, int tok0, int T,
-                                            int rg, int lane) {
+// stand-ins).  The row pass runs only for the chunk holding the end.  With
+// the mLSTM gates the forget pre-activation becomes log f (0 outside) and
+// the input pre-activation of a token outside becomes kNoToken.
+template <int C, int RPT, int ND, bool HAS_Q, int DECAY, bool HAS_KV, bool HAS_I>
+__device__ __forceinline__ void clean_chunk(RawChunk<RPT, ND, HAS_Q, HAS_KV, HAS_I>& r, int tok0,
+                                            int T, int rg, int lane, int fgate_exp = 0) {
   if (tok0 + C > T) {
 #pragma unroll
     for (int i = 0; i < RPT; ++i)
@@ -343,7 +371,15 @@ __device__ __forceinline__ void clean_chunk(RawChunk<RPT, ND, HAS_Q, HAS_KV>& r,
         }
       }
   }
-  if constexpr (DECAY != 0) {
+  if constexpr (DECAY == 3) {
+#pragma unroll
+    for (int j = 0; j < ND; ++j) {
+      const int rr = lane + 64 * j;
+      const bool out = rr >= C || tok0 + rr >= T;
+      r.d[j] = out ? 0.f : log_forget(r.d[j], fgate_exp);
+      if (out) r.ig[j] = kNoToken;
+    }
+  } else if constexpr (DECAY != 0) {
 #pragma unroll
     for (int j = 0; j < ND; ++j) {
       const int rr = lane + 64 * j;
@@ -356,11 +392,12 @@ __device__ __forceinline__ void clean_chunk(RawChunk<RPT, ND, HAS_Q, HAS_KV>& r,
 // workgroup computes it redundantly (no barrier needed).  Returns lc for
 // token `lane` (and `lane + 64` in hi for C = 128) and the chunk total.
 // Tokens past the end of the chunk or the sequence contribute log 1 = 0.
-template <int C, int ND>
+// IS_LOG: d already holds log alpha (the mLSTM forget gate).
+template <int C, int ND, bool IS_LOG = false>
 __device__ __forceinline__ void chunk_logprefix(const float (&d)[ND], int lane, float& lo,
                                                 float& hi, float& total) {
-  lo = fmaxf(__logf(d[0]), kLogFloor);
-  hi = ND > 1 ? fmaxf(__logf(d[ND - 1]), kLogFloor) : 0.f;
+  lo = IS_LOG ? d[0] : fmaxf(__logf(d[0]), kLogFloor);
+  hi = ND > 1 ? (IS_LOG ? d[ND - 1] : fmaxf(__logf(d[ND - 1]), kLogFloor)) : 0.f;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
     const float a = __shfl_up(lo, off);
@@ -375,6 +412,37 @@ __device__ __forceinline__ void chunk_logprefix(const float (&d)[ND], int lane, 
     total = __shfl(hi, 63);
   } else {
     total = __shfl(lo, C - 1);
+  }
+}
+
+// mLSTM stabiliser inside one chunk, one wave (every wave redundantly): from
+// the inclusive log-forget prefix lc (lo, hi) and the input pre-activations,
+// a_t = itilde_t - lc_t and the running maximum mu_t = max(m0, max_{s<=t} a_s)
+// of token `lane` (and `lane + 64` in the hi values), and mu at the chunk's
+// last token.  Tokens outside hold kNoToken and never raise the maximum.
+template <int C, int ND>
+__device__ __forceinline__ void chunk_runmax(const float (&ig)[ND], float lo, float hi, float m0,
+                                             int lane, float& alo, float& ahi, float& mlo,
+                                             float& mhi, float& mend) {
+  alo = ig[0] - lo;
+  ahi = ND > 1 ? ig[ND - 1] - hi : kNoToken;
+  mlo = alo;
+  mhi = ahi;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float x = __shfl_up(mlo, off);
+    const float y = __shfl_up(mhi, off);
+    if (lane >= off) {
+      mlo = fmaxf(mlo, x);
+      mhi = fmaxf(mhi, y);
+    }
+  }
+  mlo = fmaxf(mlo, m0);
+  if constexpr (C > 64) {
+    mhi = fmaxf(mhi, __shfl(mlo, 63));
+    mend = __shfl(mhi, 63);
+  } else {
+    mend = __shfl(mlo, C - 1);
   }
 }
 
@@ -497,6 +565,9 @@ void segment_state_kernel(const PfArgs a) {
   using G = Cfg<D, C, VS>;
   __shared__ __align__(16) char smem[G::S1_LDS];
   __shared__ __align__(16) float zl[G::NW][D];
+  // mLSTM: factor e^{M_old - M_new} that rescales the state before the
+  // chunk in buffer i & 1 is folded in (the running maximum grew)
+  __shared__ float s1_scale[2];
   const int bh = blockIdx.x / a.nslot;
   const int u = blockIdx.x % a.nslot;   // sub-segment: segment u / nsub, part u % nsub
   const int nchunks = (a.T + C - 1) / C;
@@ -515,17 +586,22 @@ void segment_state_kernel(const PfArgs a) {
     const DT* kg = static_cast<const DT*>(a.k) + int64_t(bh) * a.T * D;
     const DT* vg = static_cast<const DT*>(a.v) + int64_t(bh) * a.T * D;
     const float* dg = DECAY ? a.decay + int64_t(bh) * a.T : nullptr;
+    const float* igp = DECAY == 3 ? a.igate + int64_t(bh) * a.T : nullptr;
     // this thread's share of z (features 8 fb .. 8 fb + 7, its own rows of
     // every chunk): the weights already carry the decay, so z is a plain
     // sum, reduced over the threads once at the end
     float zp[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float lsuf = 0.f;   // log-decay of the chunks already staged (later in the segment)
-    using Raw = RawChunk<G::RPT, G::ND, false>;
+    // mLSTM: running maximum of the log weights itilde_s + (log decay from s
+    // to the sub-segment's end) over the chunks staged so far; the state and
+    // zp are held scaled by e^{-M}
+    float M = kNoToken;
+    using Raw = RawChunk<G::RPT, G::ND, false, true, DECAY == 3>;
     // walk step i stages chunk c1 - 1 - i; steps past the segment's first
     // chunk load a repeat of it (clamped), so the loads are the same on every
     // path, and add nothing
     auto fetch = [&](Raw& r, int i) {
-      fetch_chunk<C, D, G::RPT, G::ND, false, DECAY>(r, (const DT*)nullptr, kg, vg, dg,
+      fetch_chunk<C, D, G::RPT, G::ND, false, DECAY>(r, (const DT*)nullptr, kg, vg, dg, igp,
                                                       max(c1 - 1 - i, c0) * C, a.T, rg, fb, lane);
     };
     // [A] chunk c into buffer buf: w phi(k) high/low and v as token-major
@@ -536,23 +612,48 @@ void segment_state_kernel(const PfArgs a) {
       const int c = c1 - 1 - i;
       const bool live = i < n;
       const int tok0 = max(c, c0) * C;
-      clean_chunk<C, G::RPT, G::ND, false, DECAY>(raw, tok0, a.T, rg, lane);
+      clean_chunk<C, G::RPT, G::ND, false, DECAY>(raw, tok0, a.T, rg, lane, a.fgate_exp);
       float lo = 0.f, hi = 0.f, ltot = 0.f;
-      if constexpr (DECAY != 0) chunk_logprefix<C, G::ND>(raw.d, lane, lo, hi, ltot);
+      if constexpr (DECAY != 0) chunk_logprefix<C, G::ND, DECAY == 3>(raw.d, lane, lo, hi, ltot);
+      // mLSTM: the chunk's largest log weight relative to the sub-segment's
+      // end raises the running maximum; the state folded so far is rescaled
+      float alo = 0.f, ahi = 0.f, Mn = M;
+      if constexpr (DECAY == 3) {
+        alo = raw.ig[0] - lo;
+        ahi = G::ND > 1 ? raw.ig[G::ND - 1] - hi : kNoToken;
+        float cm = fmaxf(alo, ahi);
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) cm = fmaxf(cm, __shfl_xor(cm, off));
+        Mn = fmaxf(M, cm + lsuf + ltot);
+        const float sc = __expf(M - Mn);
+        if (live) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) zp[e] *= sc;
+        }
+        if (ts == 0) s1_scale[i & 1] = sc;
+      }
 #pragma unroll
       for (int ii = 0; ii < G::RPT; ++ii) {
         const int r = G::RPT * rg + ii;
         float kx[8];
         unpack8(raw.k[ii], kx, DT{});
+        // The cross-lane reads run in every lane, outside the per-row
+        // condition: a lane left out of a shuffle does not supply its value,
+        // and the rows past the end belong to lanes whose token values the
+        // last valid rows still need.
         float w = 1.f;
-        if constexpr (DECAY != 0) {
-          w = tok0 + r < a.T ? __expf(lsuf + ltot - lane_value<C>(lo, hi, r)) : 0.f;
+        if constexpr (DECAY == 3) {
+          const float ar = lane_value<C>(alo, ahi, r);
+          w = tok0 + r < a.T ? __expf(ar + lsuf + ltot - Mn) : 0.f;
+        } else if constexpr (DECAY != 0) {
+          const float lcr = lane_value<C>(lo, hi, r);
+          w = tok0 + r < a.T ? __expf(lsuf + ltot - lcr) : 0.f;
           if constexpr (DECAY == 2)
             w *= 1.f - lane_value<C>(raw.d[0], G::ND > 1 ? raw.d[G::ND - 1] : 0.f, r);
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          kx[e] = elu1_fast(kx[e]);
+          if constexpr (DECAY != 3) kx[e] = elu1_fast(kx[e]);   // mLSTM: identity
           if constexpr (DECAY != 0) kx[e] *= w;
           if (live) zp[e] += kx[e];
         }
@@ -569,7 +670,10 @@ void segment_state_kernel(const PfArgs a) {
           blk_write<D>(buf + G::S1_VH, perm_pos(r), fb, raw.v[ii]);
         }
       }
-      if (live) lsuf += ltot;
+      if (live) {
+        lsuf += ltot;
+        M = Mn;
+      }
       // refill this register set with the step S1_PD further on
       fetch(raw, i + G::S1_PD);
     };
@@ -602,7 +706,10 @@ void segment_state_kernel(const PfArgs a) {
       for (int w = 0; w < G::NW; ++w) zs += zl[w][ts];
       dst[D * D + ts] = zs;
     }
-    if (ts == 0) a.ws_logg[int64_t(bh) * a.nslot + u] = lsuf;
+    if (ts == 0) {
+      a.ws_logg[int64_t(bh) * a.nslot + u] = lsuf;
+      if constexpr (DECAY == 3) a.ws_m[int64_t(bh) * a.nslot + u] = M;
+    }
   } else {
     // =================================================== consumer waves
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -610,7 +717,13 @@ void segment_state_kernel(const PfArgs a) {
 #pragma unroll
     for (int mt = 0; mt < G::MT; ++mt) acc[mt] = f32x16{};
     // [B] fold the staged chunk into S; the weights already carry the decay
-    auto fold = [&](const char* buf) {
+    // (mLSTM: the state is first rescaled to the new running maximum)
+    auto fold = [&](const char* buf, int i) {
+      if constexpr (DECAY == 3) {
+        const float sc = s1_scale[i & 1];
+#pragma unroll
+        for (int mt = 0; mt < G::MT; ++mt) acc[mt] *= sc;
+      }
       u32x4 vh[G::KT], vl[G::KT];
 #pragma unroll
       for (int kk = 0; kk < G::KT; ++kk) {
@@ -631,7 +744,7 @@ void segment_state_kernel(const PfArgs a) {
     };
     __syncthreads();   // the producers' first chunk
     for (int i = 0; i < n; ++i) {
-      fold(buffer(i));
+      fold(buffer(i), i);
       __syncthreads();
     }
     // the state, row-major [f][v]
@@ -656,7 +769,14 @@ void segment_state_kernel(const PfArgs a) {
 // the final state (written over the initial one).  Slot values are loaded U
 // at a time (all of them, for up to U slots), all in flight together, then
 // folded in order.
-template <int D, int U>
+// ML (mLSTM gates): every state is held scaled by e^{-m}; slot u carries its
+// own stabiliser m_u, and carry (S', m) then slot u combine as
+//   m <- max(m + log Gamma_u, m_u),
+//   S' <- e^{m_old + log Gamma_u - m} S' + e^{m_u - m} S'_u,
+// the max-plus form of the stabiliser's recurrence.  The start stabiliser
+// of each segment and the final one go to ws_m0 (the output stage copies
+// the final one to the caller's, after every block here has read it).
+template <int D, int U, bool ML>
 __global__ __launch_bounds__(256) void segment_scan_kernel(const PfArgs a) {
   constexpr int E = D * D + D;
   const int per_bh = (E + 255) / 256;
@@ -665,10 +785,13 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(const PfArgs a) {
   if (e >= E) return;
   float* init = e < D * D ? a.S + int64_t(bh) * D * D + e : a.z + int64_t(bh) * D + (e - D * D);
   float carry = *init;
+  float mc = ML ? a.stab[bh] : 0.f;
   float* base = a.ws_state + int64_t(bh) * a.nslot * E + e;
   const float* lg = a.ws_logg + int64_t(bh) * a.nslot;
+  const float* mg = ML ? a.ws_m + int64_t(bh) * a.nslot : nullptr;
+  float* m0g = ML ? a.ws_m0 + int64_t(bh) * (a.nseg + 1) : nullptr;
   for (int s0 = 0; s0 < a.nslot; s0 += U) {
-    float x[U], gm[U];
+    float x[U], gm[U], mu[ML ? U : 1];
     // unconditional loads (slot index clamped), so that all are in flight
     // together
 #pragma unroll
@@ -676,17 +799,28 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(const PfArgs a) {
       const int uc = min(s0 + j, a.nslot - 1);
       x[j] = base[int64_t(uc) * E];
       gm[j] = lg[uc];
+      if constexpr (ML) mu[j] = mg[uc];
     }
 #pragma unroll
     for (int j = 0; j < U; ++j) {
       const int u = s0 + j;
       if (u < a.nslot) {
-        if (u % a.nsub == 0) base[int64_t(u) * E] = carry;
-        carry = fmaf(__expf(gm[j]), carry, x[j]);
+        if (u % a.nsub == 0) {
+          base[int64_t(u) * E] = carry;
+          if (ML && e == 0) m0g[u / a.nsub] = mc;
+        }
+        if constexpr (ML) {
+          const float mn = fmaxf(mc + gm[j], mu[j]);
+          carry = fmaf(__expf(mc + gm[j] - mn), carry, __expf(mu[j] - mn) * x[j]);
+          mc = mn;
+        } else {
+          carry = fmaf(__expf(gm[j]), carry, x[j]);
+        }
       }
     }
   }
   *init = carry;
+  if (ML && e == 0) m0g[a.nseg] = mc;
 }
 
 // ---------------------------------------------------------------- stage 3
@@ -745,13 +879,18 @@ void output_kernel(const PfArgs a) {
     const DT* kg = static_cast<const DT*>(a.k) + int64_t(bh) * a.T * D;
     const DT* vg = static_cast<const DT*>(a.v) + int64_t(bh) * a.T * D;
     const float* dg = DECAY ? a.decay + int64_t(bh) * a.T : nullptr;
+    const float* igp = DECAY == 3 ? a.igate + int64_t(bh) * a.T : nullptr;
     float zf[8];   // z of features 8 fb .. 8 fb + 7 before the chunk being staged
     *reinterpret_cast<f32x4*>(zf) = *reinterpret_cast<const f32x4*>(zstart + 8 * fb);
     *reinterpret_cast<f32x4*>(zf + 4) = *reinterpret_cast<const f32x4*>(zstart + 8 * fb + 4);
+    // mLSTM: stabiliser of the state before the chunk being staged
+    float m0 = 0.f;
+    if constexpr (DECAY == 3) m0 = from_ws ? a.ws_m0[int64_t(bh) * (nseg + 1) + seg] : a.stab[bh];
 
-    using Raw = RawChunk<G::RPT, G::ND, true, !NC>;
+    using Raw = RawChunk<G::RPT, G::ND, true, !NC, DECAY == 3>;
     auto fetch = [&](Raw& r, int c) {
-      fetch_chunk<C, D, G::RPT, G::ND, true, DECAY>(r, qg, kg, vg, dg, c * C, a.T, rg, fb, lane);
+      fetch_chunk<C, D, G::RPT, G::ND, true, DECAY>(r, qg, kg, vg, dg, igp, c * C, a.T, rg, fb,
+                                                     lane);
     };
     // [A] chunk c into buf: phi(q), phi(k) and w phi(k) high/low, v tiles;
     // the inter-chunk denominators e^{lc_t} phi(q_t).z; lc_t, beta_t; the
@@ -762,12 +901,15 @@ void output_kernel(const PfArgs a) {
     // nobody reads, so that the loads are the same on every path.
     auto stage = [&](Raw& raw, int c, char* buf) -> float {
       const int tok0 = c * C;
-      clean_chunk<C, G::RPT, G::ND, true, DECAY>(raw, tok0, a.T, rg, lane);
+      clean_chunk<C, G::RPT, G::ND, true, DECAY>(raw, tok0, a.T, rg, lane, a.fgate_exp);
       float lo = 0.f, hi = 0.f, ltot = 0.f;
-      if constexpr (DECAY != 0) chunk_logprefix<C, G::ND>(raw.d, lane, lo, hi, ltot);
+      if constexpr (DECAY != 0) chunk_logprefix<C, G::ND, DECAY == 3>(raw.d, lane, lo, hi, ltot);
+      float alo = 0.f, ahi = 0.f, mlo = 0.f, mhi = 0.f, mend = 0.f;
+      if constexpr (DECAY == 3) chunk_runmax<C, G::ND>(raw.ig, lo, hi, m0, lane, alo, ahi, mlo, mhi, mend);
       float* Ll = reinterpret_cast<float*>(buf + G::B_L);
       float* Bl = reinterpret_cast<float*>(buf + G::B_B);
       float* denl = reinterpret_cast<float*>(buf + G::B_DEN);
+      float* Ml = reinterpret_cast<float*>(buf + G::B_M);
       if constexpr (NC) {
         // phi(q) and phi(q) . z of the whole sequence
 #pragma unroll
@@ -795,8 +937,16 @@ void output_kernel(const PfArgs a) {
         float qx[8], kx[8];
         unpack8(raw.q[i], qx, DT{});
         unpack8(raw.k[i], kx, DT{});
-        float lct = 0.f, w = 1.f, beta = 1.f;
-        if constexpr (DECAY != 0) {
+        float lct = 0.f, w = 1.f, beta = 1.f, mt = 0.f;
+        if constexpr (DECAY == 3) {
+          // lct := m0 - mu_t (inter-chunk factor e^{lct}); beta := e^{a_t - mu_t},
+          // so that e^{lct_t - lct_s} beta_s = e^{a_s - mu_t}; m_t = lc_t + mu_t
+          const float mu = lane_value<C>(mlo, mhi, r), at = lane_value<C>(alo, ahi, r);
+          lct = m0 - mu;
+          beta = __expf(at - mu);
+          w = tok0 + r < a.T ? __expf(at - mend) : 0.f;
+          mt = lane_value<C>(lo, hi, r) + mu;
+        } else if constexpr (DECAY != 0) {
           lct = lane_value<C>(lo, hi, r);
           if constexpr (DECAY == 2)
             beta = 1.f - lane_value<C>(raw.d[0], G::ND > 1 ? raw.d[G::ND - 1] : 0.f, r);
@@ -805,8 +955,10 @@ void output_kernel(const PfArgs a) {
         float den = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          qx[e] = elu1_fast(qx[e]);
-          kx[e] = elu1_fast(kx[e]);
+          if constexpr (DECAY != 3) {   // mLSTM: identity features
+            qx[e] = elu1_fast(qx[e]);
+            kx[e] = elu1_fast(kx[e]);
+          }
           den = fmaf(qx[e], zf[e], den);
         }
         row_write_perm<D>(buf + G::B_Q, r, fb, pack8(qx));
@@ -821,7 +973,7 @@ void output_kernel(const PfArgs a) {
           }
           const u32x4 kh = pack8(kx);
           blk_write<D>(buf + G::B_KH, perm_pos(r), fb, kh);
-          if (fin) blk_write<D>(buf + G::B_KL, perm_pos(r), fb, low8(kx, kh));
+          if (fin || DECAY == 3) blk_write<D>(buf + G::B_KL, perm_pos(r), fb, low8(kx, kh));
         } else {
 #pragma unroll
           for (int e = 0; e < 8; ++e) dz[e] += kx[e];
@@ -843,6 +995,7 @@ void output_kernel(const PfArgs a) {
           denl[r] = den;
           Ll[r] = lct;
           Bl[r] = beta;
+          if constexpr (DECAY == 3) Ml[r] = mt;
         }
       }
       {
@@ -852,10 +1005,15 @@ void output_kernel(const PfArgs a) {
           *reinterpret_cast<f32x2*>(reinterpret_cast<float*>(buf + G::B_DZ) + wave * G::DZS +
                                     dz_index(fb, base)) = f32x2{s0, s1};
       }
-      if (ts == 0) *reinterpret_cast<float*>(buf + G::B_LT) = ltot;
+      // log of the carry factor: the chunk's total log-decay (mLSTM: m0 - mu_last)
+      const float lgam = DECAY == 3 ? m0 - mend : ltot;
+      if (ts == 0) *reinterpret_cast<float*>(buf + G::B_LT) = lgam;
+      if constexpr (DECAY == 3) {
+        if (c < c1) m0 = ltot + mend;   // the stabiliser after this chunk
+      }
       // refill this register set with the chunk PDEPTH ahead (clamped)
       fetch(raw, min(c + G::PDEPTH, c1 - 1));
-      return ltot;
+      return lgam;
     };
     // z after chunk c (staged in buf): zf = e^{ltot} zf + sum of the increments
     auto zstep = [&](int c, const char* buf, float ltot) {
@@ -906,6 +1064,11 @@ void output_kernel(const PfArgs a) {
       *reinterpret_cast<f32x4*>(zd) = f32x4{zf[0], zf[1], zf[2], zf[3]};
       *reinterpret_cast<f32x4*>(zd + 4) = f32x4{zf[4], zf[5], zf[6], zf[7]};
     }
+    if constexpr (DECAY == 3) {
+      // the final stabiliser: this segment's (one segment) or the scan's
+      if (ts == 0 && (fin || seg == 0))
+        a.stab[bh] = fin ? m0 : a.ws_m0[int64_t(bh) * (nseg + 1) + nseg];
+    }
   } else {
     // =================================================== consumer waves
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -928,6 +1091,7 @@ void output_kernel(const PfArgs a) {
       const float* Ll = reinterpret_cast<const float*>(buf + G::B_L);
       const float* Bl = reinterpret_cast<const float*>(buf + G::B_B);
       const float* denl = reinterpret_cast<const float*>(buf + G::B_DEN);
+      const float* Ml = reinterpret_cast<const float*>(buf + G::B_M);
       u32x4 vh[G::KT], vl[G::KT];
 #pragma unroll
       for (int kk = 0; kk < G::KT; ++kk) {
@@ -972,9 +1136,25 @@ void output_kernel(const PfArgs a) {
           const u32x4 qf = row_operand<D>(buf + G::B_Q, tl, 2 * ks + g);
           const f32x16& sa = acc[ks >> 1];
           const int j0 = 8 * (ks & 1);
-          const u32x4 sf = {pack_bf16(sa[j0 + 0], sa[j0 + 1]), pack_bf16(sa[j0 + 2], sa[j0 + 3]),
-                            pack_bf16(sa[j0 + 4], sa[j0 + 5]), pack_bf16(sa[j0 + 6], sa[j0 + 7])};
-          o = mfma(sf, qf, o);
+          if constexpr (DECAY == 3) {
+            // identity features cancel in phi(q) . S, so the state enters as
+            // bf16 high + low parts (elu+1 features are positive and average
+            // the rounding out)
+            u32x4 sh, sl;
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+              uint32_t x, y;
+              split_bf16(sa[j0 + 2 * h], sa[j0 + 2 * h + 1], x, y);
+              sh[h] = x;
+              sl[h] = y;
+            }
+            o = mfma(sh, qf, o);
+            o = mfma(sl, qf, o);
+          } else {
+            const u32x4 sf = {pack_bf16(sa[j0 + 0], sa[j0 + 1]), pack_bf16(sa[j0 + 2], sa[j0 + 3]),
+                              pack_bf16(sa[j0 + 4], sa[j0 + 5]), pack_bf16(sa[j0 + 6], sa[j0 + 7])};
+            o = mfma(sf, qf, o);
+          }
           if constexpr (!NC) p = mfma(row_operand<D>(buf + G::B_K, 32 * tb + n, 2 * ks + g), qf, p);
         }
         if (!NC && tok0 < G::EXACT)
@@ -1027,7 +1207,19 @@ void output_kernel(const PfArgs a) {
           }
         }
         if constexpr (!NC) dsum = swap_sum32(dsum);
-        const float inv = a.nonorm ? 1.f : __builtin_amdgcn_rcpf(denl[tl] + dsum + a.eps);
+        const float dn = denl[tl] + dsum;
+        float inv;
+        if constexpr (DECAY == 3) {
+          // state scaled by e^{-m_t}: the read-out's floor and eps scale with it
+          const float mt = Ml[tl];
+          inv = a.norm == LA_NORM_NONE ? __expf(mt)
+              : a.norm == LA_NORM_MAX1 ? __builtin_amdgcn_rcpf(fmaxf(fabsf(dn), __expf(-mt)))
+                                       : __builtin_amdgcn_rcpf(dn + a.eps * __expf(-mt));
+        } else {
+          inv = a.norm == LA_NORM_NONE ? 1.f
+              : a.norm == LA_NORM_MAX1 ? __builtin_amdgcn_rcpf(fmaxf(fabsf(dn), 1.f))
+                                       : __builtin_amdgcn_rcpf(dn + a.eps);
+        }
         const int t = tok0 + tl;
         if (t < a.T) {
           const uint32_t orow = uint32_t(t) * D + 32 * wave + 4 * g;
@@ -1066,7 +1258,7 @@ void output_kernel(const PfArgs a) {
       }
       if constexpr (!NC) {
         if constexpr (G::TB > 1) fold_hi();
-        if (fin) fold_lo();
+        if (fin || DECAY == 3) fold_lo();   // mLSTM: the state always as high + low
       }
     };
 
@@ -1117,9 +1309,9 @@ hipError_t launch3(const PfArgs& a, int64_t BH, int stage, hipStream_t st) {
     if (!scan) return hipSuccess;
     const int per_bh = (D * D + D + 255) / 256;
     if (a.nslot <= 32)
-      segment_scan_kernel<D, 32><<<dim3(unsigned(BH * per_bh)), dim3(256), 0, st>>>(a);
+      segment_scan_kernel<D, 32, DECAY == 3><<<dim3(unsigned(BH * per_bh)), dim3(256), 0, st>>>(a);
     else
-      segment_scan_kernel<D, 64><<<dim3(unsigned(BH * per_bh)), dim3(256), 0, st>>>(a);
+      segment_scan_kernel<D, 64, DECAY == 3><<<dim3(unsigned(BH * per_bh)), dim3(256), 0, st>>>(a);
   } else if (a.nc) {
     if constexpr (DECAY != 0) return hipErrorInvalidValue;   // rejected on the host
     else output_kernel<D, C, 0, DT, true><<<dim3(unsigned(BH * a.nseg)), dim3(2 * G::NT), 0, st>>>(a);
@@ -1135,6 +1327,7 @@ hipError_t launch_decay(const PfArgs& a, int64_t BH, la_decay kind, int stage, h
     case LA_DECAY_NONE: return launch3<D, C, 0, DT>(a, BH, stage, st);
     case LA_DECAY_SSD: return launch3<D, C, 1, DT>(a, BH, stage, st);
     case LA_GATE_RFA: return launch3<D, C, 2, DT>(a, BH, stage, st);
+    case LA_GATE_MLSTM: return launch3<D, C, 3, DT>(a, BH, stage, st);
   }
   return hipErrorInvalidValue;
 }
@@ -1173,8 +1366,15 @@ Split split_of(const Problem& p) {
 }  // namespace
 
 bool mfma_supported(const Problem& p) {
-  return (p.dtype == LA_BF16 || p.dtype == LA_F16) && p.phi == LA_PHI_ELU1 && p.dp == p.dv &&
-         (p.dv == 64 || p.dv == 128);
+  // elu+1 with no decay, SSD decay or the RFA gate (bf16 or fp16 inputs);
+  // identity features with the mLSTM gates, bf16 inputs only: the MFMA
+  // operands are bf16, which holds bf16 q, k exactly, while fp16 q, k would
+  // be rounded, and identity features cancel in q.k (elu+1 features are
+  // positive and average that rounding out)
+  const bool mlstm = p.decay_kind == LA_GATE_MLSTM;
+  const bool pair = mlstm ? p.phi == LA_PHI_IDENTITY && p.dtype == LA_BF16
+                          : p.phi == LA_PHI_ELU1 && (p.dtype == LA_BF16 || p.dtype == LA_F16);
+  return pair && p.dp == p.dv && (p.dv == 64 || p.dv == 128);
 }
 
 // Chunks whose stage-3 tiles fit in the 160 KB of LDS of one compute unit.
@@ -1196,11 +1396,19 @@ int mfma_default_segments(const Problem& p) {
   return int(cps > 0 ? (nchunks + cps - 1) / cps : 1);
 }
 
+// Workspace: the slot states, then three fp32 arrays each rounded up to 256
+// bytes: log Gamma per slot, the mLSTM stabiliser per slot, and the mLSTM
+// start stabiliser per segment plus the final one (reserved for every decay
+// kind, so the size does not depend on it).
+static size_t round256(size_t bytes) { return ((bytes + 255) / 256) * 256; }
+
 size_t mfma_workspace_bytes(const Problem& p) {
   if (p.path != 1 || (p.segments <= 1 && !p.noncausal)) return 0;
   const size_t E = size_t(p.dv) * p.dv + p.dv;
-  const size_t n = size_t(p.BH()) * split_of(p).nslot;
-  return n * E * sizeof(float) + ((n * sizeof(float) + 255) / 256) * 256;
+  const Split sp = split_of(p);
+  const size_t n = size_t(p.BH()) * sp.nslot;
+  return n * E * sizeof(float) + 2 * round256(n * sizeof(float)) +
+         round256(size_t(p.BH()) * (sp.nseg + 1) * sizeof(float));
 }
 
 hipError_t launch_mfma_stage(const Problem& p, int stage, const void* q, const void* k,
@@ -1208,6 +1416,7 @@ hipError_t launch_mfma_stage(const Problem& p, int stage, const void* q, const v
                              hipStream_t stream) {
   PfArgs a;
   a.q = q; a.k = k; a.v = v; a.out = out; a.S = S; a.z = z; a.decay = p.decay;
+  a.igate = p.igate; a.stab = p.stab; a.fgate_exp = p.fgate_exp;
   a.T = p.T;
   const Split sp = split_of(p);
   a.cps = sp.cps;
@@ -1216,15 +1425,24 @@ hipError_t launch_mfma_stage(const Problem& p, int stage, const void* q, const v
   a.cps_sub = sp.cps_sub;
   a.nslot = sp.nslot;
   a.eps = p.eps;
-  a.nonorm = p.nonorm;
+  a.norm = p.norm;
   a.nc = p.noncausal;
   a.out_f32 = p.out_dtype == LA_F32 ? 1 : 0;
   a.ws_logg = nullptr;
   a.ws_state = nullptr;
+  a.ws_m = nullptr;
+  a.ws_m0 = nullptr;
   if (a.nseg > 1 || a.nc) {
     const size_t E = size_t(p.dv) * p.dv + p.dv;
-    a.ws_state = static_cast<float*>(ws);
-    a.ws_logg = a.ws_state + size_t(p.BH()) * a.nslot * E;
+    const size_t n = size_t(p.BH()) * a.nslot;
+    char* base = static_cast<char*>(ws);
+    a.ws_state = reinterpret_cast<float*>(base);
+    base += n * E * sizeof(float);
+    a.ws_logg = reinterpret_cast<float*>(base);
+    base += round256(n * sizeof(float));
+    a.ws_m = reinterpret_cast<float*>(base);
+    base += round256(n * sizeof(float));
+    a.ws_m0 = reinterpret_cast<float*>(base);
   }
   if (p.dv == 128) {
     return p.dtype == LA_BF16 ? launch_chunk<128, bf16_t>(a, p.BH(), p.chunk, p.decay_kind, stage, stream)

@@ -7,6 +7,11 @@
 // wikillm "Linear attention", Implementation sketch and Variants / RFA):
 //   S <- alpha S + beta phi(k) v^T,  z <- alpha z + beta phi(k),
 //   o  = phi(q)^T S / (phi(q)^T z + eps).
+// With the mLSTM gates (wikillm "Linear attention", Variants / mLSTM) alpha
+// is the forget gate and beta the exponential input gate; the state is held
+// scaled by e^{-m}, m the log-domain running maximum
+// m_t = max(log f_t + m_{t-1}, itilde_t), so the factors applied are
+// e^{log f_t + m_{t-1} - m_t} and e^{itilde_t - m_t}, both <= 1.
 //
 // Layout of the work: the state S [d', d_v] (fp32, row-major) is cut into
 // float4 column groups; thread t owns column group t % (d_v/4) of rows
@@ -31,10 +36,13 @@ struct RecArgs {
   float* z;
   const float* W;
   const float* decay;
+  const float* igate;   // mLSTM input-gate pre-activations
+  float* stab;          // mLSTM stabiliser [B, H]
   int H, T, dh, dv, dp, D;
   int phi, decay_kind;
+  int fgate_exp;        // mLSTM forget gate: sigmoid (0) or exp (1)
   int out_f32;  // out is fp32 (else the input type)
-  int nonorm;   // read-out without the normaliser
+  int norm;     // read-out form (LA_NORM_*)
   int mode;     // 0 causal: update, then read out; 1 update only; 2 read-out only
   float eps;
 };
@@ -73,7 +81,10 @@ __global__ __launch_bounds__(NT) void recurrent_kernel(const RecArgs a) {
   DT* og = static_cast<DT*>(a.out) + bh * int64_t(a.T) * a.dv;
   float* ogf = static_cast<float*>(a.out) + bh * int64_t(a.T) * a.dv;
   const float* dg = a.decay ? a.decay + bh * int64_t(a.T) : nullptr;
+  const float* ig = a.igate ? a.igate + bh * int64_t(a.T) : nullptr;
   const float rsD = a.D > 0 ? 1.0f / sqrtf(float(a.D)) : 0.f;
+  const bool mlstm = a.decay_kind == LA_GATE_MLSTM;
+  float m = mlstm ? a.stab[bh] : 0.f;   // stabiliser (0: the state is unscaled)
 
   for (int t = 0; t < a.T; ++t) {
     if (tid < a.dh) {
@@ -87,6 +98,12 @@ __global__ __launch_bounds__(NT) void recurrent_kernel(const RecArgs a) {
     } else if (a.decay_kind == LA_GATE_RFA) {
       alpha = dg[t];
       beta = 1.f - alpha;
+    } else if (mlstm) {
+      const float lf = log_forget(dg[t], a.fgate_exp), it = ig[t];
+      const float mn = fmaxf(lf + m, it);
+      alpha = expf(lf + m - mn);
+      beta = expf(it - mn);
+      m = mn;
     }
     __syncthreads();
 
@@ -94,6 +111,11 @@ __global__ __launch_bounds__(NT) void recurrent_kernel(const RecArgs a) {
       if (tid < a.dp) {
         s_fq[tid] = elu1_accurate(s_q[tid]);
         s_fk[tid] = elu1_accurate(s_k[tid]);
+      }
+    } else if (a.phi == LA_PHI_IDENTITY) {
+      if (tid < a.dp) {
+        s_fq[tid] = s_q[tid];
+        s_fk[tid] = s_k[tid];
       }
     } else {
       // phi(x) = D^{-1/2} [sin(W_h x); cos(W_h x)]: thread j < D projects q,
@@ -155,7 +177,8 @@ __global__ __launch_bounds__(NT) void recurrent_kernel(const RecArgs a) {
         n += s_red[w][tid];
         d += s_red[w][256];
       }
-      const float o = a.nonorm ? n : n / (d + a.eps);
+      const float o = a.norm == LA_NORM_SUM && !mlstm ? n / (d + a.eps)
+                                                      : n * readout_factor(a.norm, d, a.eps, m);
       if (a.out_f32) ogf[int64_t(t) * a.dv + tid] = o;
       else store_f32(o, og + int64_t(t) * a.dv + tid);
     }
@@ -167,6 +190,7 @@ __global__ __launch_bounds__(NT) void recurrent_kernel(const RecArgs a) {
     if (f < a.dp) *reinterpret_cast<float4*>(Sg + int64_t(f) * a.dv + 4 * cg) = st[i];
   }
   if (tid < a.dp) zg[tid] = zr;
+  if (mlstm && tid == 0) a.stab[bh] = m;
 }
 
 int passes(int dp, int dv) {
@@ -201,10 +225,11 @@ hipError_t launch_recurrent(const Problem& p, const void* q, const void* k, cons
                             float* S, float* z, void* out, hipStream_t stream) {
   RecArgs a;
   a.q = q; a.k = k; a.v = v; a.out = out; a.S = S; a.z = z;
-  a.W = p.W; a.decay = p.decay;
+  a.W = p.W; a.decay = p.decay; a.igate = p.igate; a.stab = p.stab;
   a.H = p.H; a.T = p.T; a.dh = p.dh; a.dv = p.dv; a.dp = p.dp; a.D = p.D;
   a.phi = int(p.phi); a.decay_kind = int(p.decay_kind); a.eps = p.eps;
-  a.nonorm = p.nonorm;
+  a.fgate_exp = p.fgate_exp;
+  a.norm = p.norm;
   a.out_f32 = p.out_dtype == LA_F32 ? 1 : 0;
   // non-causal: the whole sequence into the state first, then every token
   // reads it out ([kb] section 3, non-causal sketch)
@@ -226,18 +251,21 @@ hipError_t launch_recurrent(const Problem& p, const void* q, const void* k, cons
 // ---------------------------------------------------------------- state init
 
 namespace {
-__global__ void fill_zero_kernel(float* S, int64_t nS, float* z, int64_t nz) {
+__global__ void fill_zero_kernel(float* S, int64_t nS, float* z, int64_t nz, float* m,
+                                 int64_t nm) {
   const int64_t stride = int64_t(gridDim.x) * blockDim.x;
   for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < nS; i += stride) S[i] = 0.f;
   for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < nz; i += stride) z[i] = 0.f;
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < nm; i += stride) m[i] = 0.f;
 }
 }  // namespace
 
-hipError_t launch_state_init(float* S, int64_t nS, float* z, int64_t nz, hipStream_t stream) {
+hipError_t launch_state_init(float* S, int64_t nS, float* z, int64_t nz, float* m, int64_t nm,
+                             hipStream_t stream) {
   int64_t blocks = (nS + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   if (blocks < 1) blocks = 1;
-  fill_zero_kernel<<<dim3(unsigned(blocks)), dim3(256), 0, stream>>>(S, nS, z, nz);
+  fill_zero_kernel<<<dim3(unsigned(blocks)), dim3(256), 0, stream>>>(S, nS, z, nz, m, nm);
   return hipGetLastError();
 }
 

@@ -14,7 +14,9 @@ five measured configurations):
 * ``prefill_inputs`` -- Q, K, V ~ N(0, 1) * scale, drawn in fp32 and rounded
   to the storage dtype with round-to-nearest-even; optional per-token
   per-head decay ``a = sigmoid(x)``, ``x ~ N(mean, 1)``, or RFA gate
-  ``g = sigmoid(N(0, 1))``; optional RFF projection ``W ~ N(0, I)``.
+  ``g = sigmoid(N(0, 1))``, or mLSTM gate pre-activations (input
+  ``N(0, 1)``, forget ``N(3, 1)``: sigmoid(3) ~ 0.95, the SSD workload's
+  typical decay); optional RFF projection ``W ~ N(0, I)``.
 * ``rfa_decode_step_inputs`` -- unit-norm q, k (normalised in fp64, stored
   fp32), v ~ N(0, 1), gate g = sigmoid(N(0, 1)); ``W`` drawn once per head.
 
@@ -54,6 +56,8 @@ class PrefillInputs:
     decay: Optional[torch.Tensor] = None   # [B, H, T] fp32 (SSD decay a_t)
     gate: Optional[torch.Tensor] = None    # [B, H, T] fp32 (RFA gate g_t)
     W: Optional[torch.Tensor] = None       # [H, D, d_h] fp32 (RFF projection)
+    igate: Optional[torch.Tensor] = None   # [B, H, T] fp32 (mLSTM input pre-activation)
+    fgate: Optional[torch.Tensor] = None   # [B, H, T] fp32 (mLSTM forget pre-activation)
     meta: dict = field(default_factory=dict)
 
 
@@ -64,9 +68,10 @@ def prefill_inputs(B: int, H: int, T: int, d_h: int, d_v: Optional[int] = None,
                    device="cpu") -> PrefillInputs:
     """Draw Q, K, V (in that order), then the decay/gate input, then W.
 
-    ``decay``: None, "ssd" (a = sigmoid(x), x ~ N(decay_mean, 1)) or
-    "rfa" (g = sigmoid(N(0, 1))).  Values are drawn in fp32, scaled in fp32
-    and then rounded once to ``dtype`` (round to nearest even).
+    ``decay``: None, "ssd" (a = sigmoid(x), x ~ N(decay_mean, 1)), "rfa"
+    (g = sigmoid(N(0, 1))) or "mlstm" (input pre-activations ~ N(0, 1), then
+    forget pre-activations ~ N(decay_mean, 1)).  Values are drawn in fp32,
+    scaled in fp32 and then rounded once to ``dtype`` (round to nearest even).
     """
     d_v = d_h if d_v is None else d_v
     g = _gen(seed, device)
@@ -87,6 +92,9 @@ def prefill_inputs(B: int, H: int, T: int, d_h: int, d_v: Optional[int] = None,
         out.decay = torch.sigmoid(x).float()
     elif decay == "rfa":
         out.gate = torch.sigmoid(torch.randn(B, H, T, generator=g, device=device)).float()
+    elif decay == "mlstm":
+        out.igate = torch.randn(B, H, T, generator=g, device=device)
+        out.fgate = torch.randn(B, H, T, generator=g, device=device) + decay_mean
     elif decay is not None:
         raise ValueError(f"unknown decay kind {decay!r}")
     if rff_D is not None:
@@ -142,7 +150,7 @@ def rfa_decode_batch(steps: int, N: int, H: int, d_h: int, d_v: Optional[int] = 
     return DecodeStep(q, k, v, gate.float().contiguous())
 
 
-# --- the five measured workloads, named by what they are ---------------------
+# --- the measured workloads, named by what they are --------------------------
 
 WORKLOADS = {
     "tiny_causal_t8_d4": dict(kind="prefill", B=1, H=1, T=8, d_h=4, dtype="f32",
@@ -156,6 +164,10 @@ WORKLOADS = {
                                             scale=2.0 ** -0.5),
     "rfa_decode_n256_h16_d64_D64": dict(kind="decode", N=256, H=16, d_h=64, D=64,
                                         steps=1024),
+    # the long-context shape with the mLSTM gates and identity features
+    "mlstm_prefill_b1_h8_t102400_d128": dict(kind="prefill", B=1, H=8, T=102400, d_h=128,
+                                             dtype="bf16", decay="mlstm",
+                                             scale=2.0 ** -0.5),
 }
 
 

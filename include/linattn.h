@@ -19,26 +19,44 @@
  *            attention with a scalar state (SSD)") and "Variants / Random
  *            Fourier features (RFA)" (Gaussian random projections as the
  *            feature map; a sigmoid gate g decays the old state and scales the
- *            new term by 1 - g).
+ *            new term by 1 - g) and "Variants / Matrix memory with
+ *            exponential gates (mLSTM)" (forget gate f, exponential input gate
+ *            i, read-out divided by max(|n^T q|, 1), a stabiliser state against
+ *            overflow; "Implementation sketch": the mLSTM step is this loop
+ *            with the identity feature map).
  *
  * Per (batch b, head h), for t = 0 .. T-1:
  *   S <- alpha_t S + beta_t phi(k_t) v_t^T          S: d' x d_v, fp32
  *   z <- alpha_t z + beta_t phi(k_t)                z: d',       fp32
  *   o_t = (phi(q_t)^T S) / (phi(q_t)^T z + eps)     read-out after the update
- * with (alpha, beta) = (1, 1) for LA_DECAY_NONE, (a_t, 1) for LA_DECAY_SSD and
- * (g_t, 1 - g_t) for LA_GATE_RFA; with LA_NORM_NONE the read-out is the
- * numerator alone, o_t = phi(q_t)^T S.
+ * with (alpha, beta) = (1, 1) for LA_DECAY_NONE, (a_t, 1) for LA_DECAY_SSD,
+ * (g_t, 1 - g_t) for LA_GATE_RFA and (f_t, i_t) for LA_GATE_MLSTM; with
+ * LA_NORM_NONE the read-out is the numerator alone, o_t = phi(q_t)^T S, and
+ * with LA_NORM_MAX1 it is phi(q_t)^T S / max(|phi(q_t)^T z|, 1).
+ *
+ * mLSTM gates (LA_GATE_MLSTM): `decay` holds the forget-gate pre-activations
+ * and `igate` the input-gate pre-activations; f_t = sigmoid(decay_t) (or
+ * exp(decay_t) with fgate_exp = 1) and i_t = exp(igate_t).  The page gives
+ * no formula for the stabiliser; this library keeps a per-(b, h) log-domain
+ * running maximum
+ *   m_t = max(log f_t + m_{t-1}, igate_t)
+ * in desc->stab and stores the state scaled by e^{-m}: S and z hold
+ * e^{-m_t} times the sums above (every factor applied is <= 1, so nothing
+ * overflows), and the read-outs are evaluated as the same numbers, e.g.
+ * phi(q)^T S / max(|phi(q)^T z|, e^{-m_t}) for LA_NORM_MAX1.  A zero state
+ * (la_state_init) has m = 0.
  *
  * Feature maps:
  *   LA_PHI_ELU1: phi(x) = elu(x) + 1 (alpha = 1), element-wise, d' = d_h.
  *   LA_PHI_RFF:  phi(x) = D^{-1/2} [sin(W_h x); cos(W_h x)], W_h = rff_W[h]
  *                (D x d_h, fp32), d' = 2 D; features 0..D-1 are the sines,
  *                D..2D-1 the cosines.  No q/k scaling is applied.
+ *   LA_PHI_IDENTITY: phi(x) = x, d' = d_h (the mLSTM step).
  *
  * Layouts (all row-major, contiguous, device memory, 16-byte aligned):
- *   prefill q, k [B, H, T, d_h]; v, out [B, H, T, d_v]; decay [B, H, T] fp32
- *   decode  q, k [B, H, d_h];    v, out [B, H, d_v];    decay [B, H]    fp32
- *   state   S [B, H, d', d_v] fp32; z [B, H, d'] fp32
+ *   prefill q, k [B, H, T, d_h]; v, out [B, H, T, d_v]; decay, igate [B, H, T] fp32
+ *   decode  q, k [B, H, d_h];    v, out [B, H, d_v];    decay, igate [B, H]    fp32
+ *   state   S [B, H, d', d_v] fp32; z [B, H, d'] fp32; stab [B, H] fp32 (mLSTM)
  * (for decode, B is the number of sequences).  q, k and v share one element
  * type (dtype); out is either dtype or fp32 (out_dtype).  Arithmetic is fp32
  * (MFMA operands bf16 for 16-bit inputs, with the intra-chunk scores split
@@ -79,22 +97,27 @@ typedef enum {
 
 typedef enum { LA_F32 = 0, LA_BF16 = 1, LA_F16 = 2 } la_dtype;
 
-typedef enum { LA_PHI_ELU1 = 0, LA_PHI_RFF = 1 } la_phi;
+typedef enum { LA_PHI_ELU1 = 0, LA_PHI_RFF = 1, LA_PHI_IDENTITY = 2 } la_phi;
 
 typedef enum {
   LA_DECAY_NONE = 0,  /* alpha = 1,   beta = 1                          */
   LA_DECAY_SSD = 1,   /* alpha = a_t, beta = 1      (a_t >= 0 expected)  */
-  LA_GATE_RFA = 2     /* alpha = g_t, beta = 1 - g_t                     */
+  LA_GATE_RFA = 2,    /* alpha = g_t, beta = 1 - g_t                     */
+  LA_GATE_MLSTM = 3   /* alpha = f_t, beta = i_t = exp(igate_t), state
+                         stabilised (see above)                          */
 } la_decay;
 
 typedef enum {
   LA_NORM_SUM = 0,    /* o_t = phi(q_t)^T S / (phi(q_t)^T z + eps)            */
-  LA_NORM_NONE = 1    /* o_t = phi(q_t)^T S: the normaliser is left out of the
+  LA_NORM_NONE = 1,   /* o_t = phi(q_t)^T S: the normaliser is left out of the
                          read-out ([card] "Decaying linear attention with a
                          scalar state (SSD)": the normaliser-free form, which
                          relies on a normalisation layer after the read-out).
                          z is still carried and updated, so a state can move
                          between the two forms.                            */
+  LA_NORM_MAX1 = 2    /* o_t = phi(q_t)^T S / max(|phi(q_t)^T z|, 1), the
+                         mLSTM read-out ([card] Variants / mLSTM); eps is
+                         not used                                          */
 } la_norm;
 
 typedef struct la_desc {
@@ -106,10 +129,11 @@ typedef struct la_desc {
   la_dtype dtype;        /* element type of q, k and v                            */
   la_dtype out_dtype;    /* element type of out: dtype, or LA_F32 for any dtype   */
   la_phi phi;            /* feature map                                           */
-  int rff_D;             /* RFF pairs (d' = 2 rff_D); must be 0 for ELU1          */
-  const float* rff_W;    /* device [H, rff_D, d_h] fp32; NULL for ELU1            */
+  int rff_D;             /* RFF pairs (d' = 2 rff_D); 0 for ELU1 and IDENTITY     */
+  const float* rff_W;    /* device [H, rff_D, d_h] fp32; NULL for ELU1, IDENTITY  */
   la_decay decay_kind;   /* decay / gate kind                                     */
-  const float* decay;    /* device fp32 a_t or g_t; NULL iff LA_DECAY_NONE        */
+  const float* decay;    /* device fp32 a_t, g_t or the mLSTM forget-gate
+                            pre-activations; NULL iff LA_DECAY_NONE          */
   float eps;             /* added to the denominator (finite); 1e-6 on the pages  */
   int chunk;             /* prefill chunk length, 0 = default (32); 32/64/128     */
   int segments;          /* prefill segments per (b, h), 0 = automatic            */
@@ -117,14 +141,21 @@ typedef struct la_desc {
   int noncausal;         /* prefill only: 0 = causal (default); 1 = non-causal,
                             every output reads the state of the whole sequence
                             (see la_prefill); needs LA_DECAY_NONE             */
+  const float* igate;    /* LA_GATE_MLSTM: device fp32 input-gate
+                            pre-activations, shaped like decay; else NULL   */
+  int fgate_exp;         /* LA_GATE_MLSTM: forget gate f = sigmoid(decay) (0)
+                            or exp(decay) (1); else 0                        */
+  float* stab;           /* LA_GATE_MLSTM: device fp32 stabiliser m [B, H],
+                            read and written in place like S and z; else NULL */
 } la_desc;
 
-/* Feature dimension d' of a descriptor (d_h for ELU1, 2 rff_D for RFF), or -1
- * if the descriptor is invalid.  Host only. */
+/* Feature dimension d' of a descriptor (d_h for ELU1 and IDENTITY, 2 rff_D
+ * for RFF), or -1 if the descriptor is invalid.  Host only. */
 int la_feature_dim(const la_desc* desc);
 
 /* Zero the state: S [B, H, d', d_v] and z [B, H, d'] (fp32) become 0, the
- * initial state of the recurrence ([kb] section 3: S and z start at zero).
+ * initial state of the recurrence ([kb] section 3: S and z start at zero);
+ * with LA_GATE_MLSTM the stabiliser desc->stab [B, H] becomes 0 too.
  * Enqueued on `stream`. */
 la_status la_state_init(const la_desc* desc, float* S, float* z, void* stream);
 
@@ -133,15 +164,19 @@ la_status la_state_init(const la_desc* desc, float* S, float* z, void* stream);
 la_status la_prefill_workspace_size(const la_desc* desc, size_t* bytes);
 
 /* Execution plan la_prefill will use for `desc`: chunk length, segments per
- * (b, h), and path (1 = chunked MFMA for 16-bit inputs with elu+1 and
- * d' = d_v in {64, 128}; 0 = general per-token kernel).  Host only. */
+ * (b, h), and path (1 = chunked MFMA for d' = d_v in {64, 128}: elu+1 with
+ * no decay, SSD decay or the RFA gate and bf16 or fp16 inputs, or the
+ * identity map with the mLSTM gates and bf16 inputs; 0 = general per-token
+ * kernel).  Host only. */
 la_status la_prefill_plan(const la_desc* desc, int* chunk, int* segments, int* path);
 
 /* Causal prefill over T tokens for all (b, h):
  *   in:  q, k, v (dtype), decay/gate and rff_W through desc, the initial
- *        state (S, z) -- the recurrence continues from it ([kb] section 2:
- *        the state is carried between steps);
- *   out: out [B, H, T, d_v] (out_dtype) and the final state written over (S, z).
+ *        state (S, z, and desc->stab with mLSTM gates) -- the recurrence
+ *        continues from it ([kb] section 2: the state is carried between
+ *        steps);
+ *   out: out [B, H, T, d_v] (out_dtype) and the final state written over
+ *        (S, z) (and desc->stab).
  * The result equals T applications of the recurrence above; the chunked
  * schedule re-brackets the same sums ([lesson] Researcher level,
  * "Implementation reality": quadratic inside chunks, a scan across them).
@@ -161,8 +196,9 @@ la_status la_prefill(const la_desc* desc, const void* q, const void* k, const vo
 /* The three stages la_prefill enqueues, for callers that time or interleave
  * them: 1 = per-segment state contributions (reads k, v), 2 = scan of the
  * segment states (folds in the initial state), 3 = outputs and final state
- * (reads q, k, v).  Running stages 1, 2, 3 in order with identical arguments
- * is exactly la_prefill; a stage with nothing to do returns LA_OK. */
+ * (reads q, k, v; with mLSTM gates and several segments, stage 3 writes the
+ * final stabiliser).  Running stages 1, 2, 3 in order with identical
+ * arguments is exactly la_prefill; a stage with nothing to do returns LA_OK. */
 la_status la_prefill_stage(const la_desc* desc, int stage, const void* q, const void* k,
                            const void* v, float* S, float* z, void* out,
                            void* workspace, size_t workspace_bytes, void* stream);
@@ -170,8 +206,8 @@ la_status la_prefill_stage(const la_desc* desc, int stage, const void* q, const 
 /* One autoregressive step for B sequences x H heads ([kb] section 2, causal
  * recurrence; [card] "When to use which": memory-bound decoding with a
  * fixed-size state): reads q, k [B, H, d_h], v [B, H, d_v] and the gate or
- * decay [B, H]; updates (S, z) in place and writes out [B, H, d_v].
- * desc->noncausal must be 0. */
+ * decay [B, H]; updates (S, z) (and desc->stab) in place and writes out
+ * [B, H, d_v].  desc->noncausal must be 0. */
 la_status la_decode_step(const la_desc* desc, const void* q, const void* k, const void* v,
                          float* S, float* z, void* out, void* stream);
 

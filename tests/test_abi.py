@@ -47,10 +47,13 @@ def test_plan_for_the_measured_prefills():
     # long context: chunked MFMA path, segments spread 8 heads over the chip
     c, s, p = la.prefill_plan(desc())
     assert (c, s, p) == (32, 32, 1)    # one workgroup per compute unit: 8 heads x 32 segments
-    # stage 1 cuts every segment in two: 2 * 32 state slots per head
+    # stage 1 cuts every segment in two: 2 * 32 state slots per head; then
+    # log Gamma and the mLSTM stabiliser per slot, and the mLSTM start
+    # stabiliser per segment plus the final one, each rounded to 256 bytes
     slots = 2 * s
-    assert la.prefill_workspace_size(desc()) == 8 * slots * (128 * 128 + 128) * 4 + (
-        (8 * slots * 4 + 255) // 256) * 256
+    r256 = lambda n: (n + 255) // 256 * 256
+    assert la.prefill_workspace_size(desc()) == (8 * slots * (128 * 128 + 128) * 4
+                                                 + 2 * r256(8 * slots * 4) + r256(8 * (s + 1) * 4))
     # fp32 inputs take the per-token kernel; no workspace
     d = desc(T=8, d_h=4, d_v=4, dtype_code=_lib.LA_F32)
     assert la.prefill_plan(d)[2] == 0 and la.prefill_workspace_size(d) == 0
@@ -67,8 +70,8 @@ def test_plan_for_the_measured_prefills():
 
 @pytest.mark.parametrize("field,value", [("B", 0), ("H", -1), ("T", -5), ("d_h", 0), ("d_v", 0),
                                          ("dtype", 7), ("phi", 9), ("decay_kind", 5),
-                                         ("chunk", 48), ("segments", -1), ("norm", 2),
-                                         ("noncausal", 3)])
+                                         ("chunk", 48), ("segments", -1), ("norm", 3),
+                                         ("noncausal", 3), ("fgate_exp", 1)])
 def test_bad_descriptor_fields_are_rejected(field, value):
     d = desc()
     setattr(d, field, value)
@@ -159,3 +162,31 @@ def test_noncausal_checks():
     assert la.prefill_plan(one)[1] == 1 and la.prefill_workspace_size(one) > 0
     assert la.prefill_workspace_size(desc(T=640, segments=1)) == 0
 
+
+
+def test_mlstm_descriptor_checks():
+    base = dict(T=640, d_h=128, d_v=128, dtype_code=_lib.LA_BF16)
+    ok = desc(phi="identity", **base)
+    ok.decay_kind, ok.decay, ok.igate, ok.stab = _lib.LA_GATE_MLSTM, FAKE, FAKE, FAKE
+    assert la.prefill_plan(ok)[2] == 1                      # the chunked MFMA path
+    for field in ("igate", "stab", "decay"):                # each array is required
+        d = desc(phi="identity", **base)
+        d.decay_kind, d.decay, d.igate, d.stab = _lib.LA_GATE_MLSTM, FAKE, FAKE, FAKE
+        setattr(d, field, None)
+        assert status(L.la_prefill(ctypes.byref(d), *([FAKE] * 7), 1 << 40, None)) == "LA_EINVAL"
+    d = desc(phi="identity", **base)
+    d.decay_kind, d.decay, d.igate, d.stab, d.fgate_exp = _lib.LA_GATE_MLSTM, FAKE, FAKE, FAKE, 2
+    assert status(L.la_prefill(ctypes.byref(d), *([FAKE] * 7), 1 << 40, None)) == "LA_EINVAL"
+    d = desc(**base)                                        # igate without the mLSTM gates
+    d.igate = FAKE
+    assert status(L.la_prefill(ctypes.byref(d), *([FAKE] * 7), 1 << 40, None)) == "LA_EINVAL"
+    d = desc(phi="identity", causal=False, **base)          # no gates in the non-causal form
+    d.decay_kind, d.decay, d.igate, d.stab = _lib.LA_GATE_MLSTM, FAKE, FAKE, FAKE
+    assert status(L.la_prefill(ctypes.byref(d), *([FAKE] * 7), 1 << 40, None)) == "LA_EINVAL"
+    # elu+1 with the mLSTM gates, and identity features without them, take the
+    # per-token kernel
+    d = desc(**base)
+    d.decay_kind, d.decay, d.igate, d.stab = _lib.LA_GATE_MLSTM, FAKE, FAKE, FAKE
+    assert la.prefill_plan(d)[2] == 0
+    assert la.prefill_plan(desc(phi="identity", **base))[2] == 0
+    assert L.la_feature_dim(ctypes.byref(desc(phi="identity", **base))) == 128

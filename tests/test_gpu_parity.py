@@ -60,6 +60,25 @@ def test_prefill_mfma_vs_oracle(d, decay, chunk):
         assert max(e) < TOL["bf16"], e
 
 
+@pytest.mark.parametrize("d,tail", [(128, 17), (128, 25), (128, 26), (64, 17), (64, 20)])
+@pytest.mark.parametrize("decay", ["ssd", "rfa"])
+def test_prefill_ragged_tail_in_multi_segment_state(d, tail, decay):
+    # Regression: stage 1 reads each row's log-decay prefix from the lane of
+    # its token.  With these tails the last valid rows take that value from
+    # lanes whose own rows lie past the end; the read must still run in those
+    # lanes, or the weights of the last tokens (and the final state) go wrong
+    # while every output stays right.
+    dev = gpu_device()
+    T = 12 * 32 + tail
+    x = I.prefill_inputs(1, 2, T, d, dtype="bf16", seed=21, decay=decay, scale=2.0 ** -0.5)
+    for segments in (2, 0):
+        out, S, z = run_prefill(x, dev, segments=segments)
+        o_ref, S_ref, z_ref = oracle_prefill(x)
+        e = (rel_err(out, o_ref), rel_err(S, S_ref), rel_err(z, z_ref))
+        print(d, tail, decay, segments, e)
+        assert max(e) < TOL["bf16"], e
+
+
 @pytest.mark.parametrize("decay", [None, "ssd"])
 def test_prefill_fp16_inputs(decay):
     dev = gpu_device()
