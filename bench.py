@@ -31,6 +31,11 @@ Printed as one JSON line:
                256 MB last-level cache;
   normaliser_free  the same prefill with the read-out phi(q)^T S alone;
   noncausal    the same prefill in the non-causal form;
+  mlstm        the same shape with the mLSTM gates: identity features,
+               sigmoid forget gate, exponential input gate (pre-activations
+               N(3, 1) and N(0, 1), fp32), read-out divided by
+               max(|q.z|, 1), stabilised state; algorithmic bytes add the
+               two gate arrays;
   cpu_baseline the fp64 oracle (the CPU reference the tests check against),
                on a bounded sample of the same prefill workload, one worker
                process per head.
@@ -147,13 +152,20 @@ def _events(torch):
     return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
 
-def bench_prefill(torch, la, I, steps, warmup, normalize=True, stages=True, causal=True):
+def bench_prefill(torch, la, I, steps, warmup, normalize=True, stages=True, causal=True,
+                  mlstm=False):
     dev = torch.device("cuda:0")
     B, H, T, d = PF["B"], PF["H"], PF["T"], PF["d"]
-    x = I.prefill_inputs(B, H, T, d, dtype="bf16", seed=0, scale=PF["scale"], device=dev)
+    x = I.prefill_inputs(B, H, T, d, dtype="bf16", seed=0, scale=PF["scale"], device=dev,
+                         decay="mlstm" if mlstm else None)
     q, k, v = x.q, x.k, x.v
-    desc = la.make_desc(B, H, T, d, d, la._lib.LA_BF16, eps=PF["eps"], normalize=normalize,
-                        causal=causal)
+    stab = torch.empty(B, H, dtype=torch.float32, device=dev) if mlstm else None
+    if mlstm:
+        desc = la.make_desc(B, H, T, d, d, la._lib.LA_BF16, phi="identity", eps=PF["eps"],
+                            normalize="max1", igate=x.igate, fgate=x.fgate, stab=stab)
+    else:
+        desc = la.make_desc(B, H, T, d, d, la._lib.LA_BF16, eps=PF["eps"], normalize=normalize,
+                            causal=causal)
     chunk, segments, path = la.prefill_plan(desc)
     if path != 1:
         raise RuntimeError("the long-context prefill did not take the chunked MFMA path")
@@ -331,6 +343,9 @@ def main(argv=None):
     pf_nn = bench_prefill(torch, la, I, a.steps, a.warmup, normalize=False, stages=False)
     print("[bench] prefill, non-causal form", file=sys.stderr, flush=True)
     pf_nc = bench_prefill(torch, la, I, a.steps, a.warmup, stages=False, causal=False)
+    print("[bench] prefill, mLSTM gates", file=sys.stderr, flush=True)
+    pf_ml = bench_prefill(torch, la, I, a.steps, a.warmup, mlstm=True)
+    ml_bytes = step_bytes + TH * 2 * 4 + 2 * B * H * 4     # + the two gates, the stabiliser
     cp = hbm_copy(torch)
     dec = dec_big = None
     if not a.no_decode:
@@ -381,6 +396,15 @@ def main(argv=None):
             "ms_per_step": pf_nc["ms"], "tokens_per_s": B * T / (pf_nc["ms"] * 1e-3),
             "GBs": step_bytes / (pf_nc["ms"] * 1e-3) / 1e9,
             "hbm_frac": step_bytes / (pf_nc["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "mlstm": {
+            "workload": "the same shape with the mLSTM gates: identity features, sigmoid "
+                        "forget and exponential input gates (fp32 pre-activations), "
+                        "max(|q.z|, 1) read-out, stabilised state",
+            "ms_per_step": pf_ml["ms"], "tokens_per_s": B * T / (pf_ml["ms"] * 1e-3),
+            "stage_ms": pf_ml["stage_ms"], "algorithmic_bytes": ml_bytes,
+            "GBs": ml_bytes / (pf_ml["ms"] * 1e-3) / 1e9,
+            "hbm_frac": ml_bytes / (pf_ml["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "stage3_GBs": (stage3_bytes + TH * 2 * 4) / (pf_ml["stage_ms"][2] * 1e-3) / 1e9},
     }
     if dec is not None:
         res["decode"] = {

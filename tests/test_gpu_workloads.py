@@ -13,6 +13,10 @@ the input type), against the fp64 oracle.
   edges among them) of the other six, every final state in closed form; and
   the same workload with the normaliser-free read-out, two heads end to end,
   and in the non-causal form, every output.
+* mLSTM gates on the long-context shape (identity features, sigmoid forget
+  and exponential input gates, max(|q.z|, 1) read-out): two heads end to
+  end, sampled positions of the other six, every final state (S', z', m) in
+  closed form.
 
 A 16-bit output is the fp32 result rounded to nearest even, so each element
 may sit up to half an ulp (2^-8 relative, worst case in a binade) from the
@@ -173,3 +177,40 @@ def test_long_prefill_noncausal_full():
     print("long prefill non-causal", e, "plain", rel_err(out, o_ref))
     assert max(e) < TOL["bf16"], e
 
+
+
+def test_mlstm_prefill_b1_h8_t102400_d128_sampled():
+    dev = gpu_device()
+    x = I.workload_inputs("mlstm_prefill_b1_h8_t102400_d128", seed=0)
+    B, H, T, d = x.q.shape
+    desc = la.make_desc(B, H, T, d, d, la._lib.LA_BF16, phi="identity", igate=x.igate,
+                        fgate=x.fgate, normalize="max1", stab=torch.empty(1))
+    chunk, segments, path = la.prefill_plan(desc)
+    assert path == 1
+    g = lambda t: t.to(dev)
+    out, S, z, m = la.prefill(g(x.q), g(x.k), g(x.v), phi="identity", igate=g(x.igate),
+                              fgate=g(x.fgate), normalize="max1")
+    torch.cuda.synchronize()
+    assert out.dtype == torch.bfloat16
+    out, S, z, m = (out.double().cpu().numpy(), S.cpu().numpy(), z.cpu().numpy(),
+                    m.cpu().double().numpy())
+    hs = [2, 5]
+    o_ref, S_ref, z_ref, m_ref = O.mlstm_recurrence(x.q[0, hs], x.k[0, hs], x.v[0, hs],
+                                                    x.igate[0, hs], x.fgate[0, hs])
+    r = rms(o_ref)
+    e_full = (excess_err(out[0, hs], o_ref, r), rel_err(S[0, hs], S_ref),
+              rel_err(z[0, hs], z_ref), float(np.abs(m[0, hs] - m_ref).max()))
+    rng = np.random.default_rng(6)
+    pos = sample_positions(T, chunk, segments, 12, rng)
+    worst = 0.0
+    for h in (0, 1, 3, 4, 6, 7):
+        for t in pos:
+            ref = O.mlstm_output_at(x.q[0, h, t], x.k[0, h], x.v[0, h], t, x.igate[0, h],
+                                    x.fgate[0, h])
+            worst = max(worst, excess_err(out[0, h, t], ref, r))
+    Sc, zc, mc = O.mlstm_final_state(x.k[0], x.v[0], x.igate[0], x.fgate[0])
+    e_state = (rel_err(S[0], Sc), rel_err(z[0], zc), float(np.abs(m[0] - mc).max()))
+    print("mlstm prefill 1x8x102400x128 full", e_full, "sampled", worst, "states", e_state)
+    assert max(e_full[:3]) < TOL["bf16"] and e_full[3] < 1e-3, e_full
+    assert worst < TOL["bf16"], worst
+    assert max(e_state[:2]) < TOL["bf16"] and e_state[2] < 1e-3, e_state
