@@ -569,6 +569,111 @@ def noncausal_by_definition(fq, fk, v, eps=1e-6, normalize=True):
 
 
 # --------------------------------------------------------------------------
+# Gradients of the causal prefill (training; [lesson] Developer level and
+# "Implementation reality": training runs the chunked form, which computes
+# the same function, so its gradients are those of the definition)
+# --------------------------------------------------------------------------
+
+def phi_derivative(x, phi="elu1"):
+    """d phi / dx element-wise: elu+1 has slope 1 for x > 0 and e^x below;
+    the identity has slope 1."""
+    x = _f64(x)
+    if phi == "elu1":
+        return np.where(x > 0, 1.0, np.exp(np.minimum(x, 0.0)))
+    if phi == "identity":
+        return np.ones_like(x)
+    raise ValueError(f"no derivative for feature map {phi!r}")
+
+
+def prefill_gradients(q, k, v, dout, phi="elu1", decay=None, gate=None, eps=1e-6, S0=None,
+                      z0=None, normalize=True):
+    """Gradients of L = sum_t <dout_t, o_t> for the causal prefill, from the
+    masked quadratic form (the definition) in float64, one head at a time
+    (leading dims are looped):
+
+        W_ts = (phi(q_t).phi(k_s)) beta_s prod_{r=s+1..t} alpha_r   (s <= t)
+        num_t = sum_s W_ts v_s + c_t phi(q_t)^T S0,  den_t = sum_s W_ts + c_t phi(q_t).z0
+        o_t = num_t / (den_t + eps)   (or num_t, or num_t / max(|den_t|, 1))
+
+    with c_t = prod_{r<=t} alpha_r.  Reverse-mode by hand:
+        g_num = dout / D,  g_den = -(dout . o) / D   (D the read-out's divisor)
+        dW = g_num V^T + g_den 1^T,   dphi(Q) = (dW o M) phi(K) + c (g_num S0^T + g_den z0^T)
+        dphi(K) = (dW o M)^T phi(Q) ..., dV = W^T g_num,
+    and the decay through the products M.  Returns a dict with dq, dk, dv,
+    dS0, dz0 and (with decay/gate) ddecay or dgate, all float64.
+    """
+    fq_all, fk_all = features(q, phi), features(k, phi)
+    dphq, dphk = phi_derivative(q, phi), phi_derivative(k, phi)
+    v_all, do_all = _f64(v), _f64(dout)
+    alpha_all, beta_all = decay_coefficients(decay, gate)
+    lead = fq_all.shape[:-2]
+    T, dp = fq_all.shape[-2:]
+    dv_ = v_all.shape[-1]
+    out = {n: np.zeros(lead + shp) for n, shp in (("dq", (T, q.shape[-1])), ("dk", (T, k.shape[-1])),
+                                                  ("dv", (T, dv_)), ("dS0", (dp, dv_)), ("dz0", (dp,)),
+                                                  ("dalpha", (T,)), ("dbeta", (T,)))}
+    for idx in np.ndindex(*lead):
+        fq, fk, vv, do = fq_all[idx], fk_all[idx], v_all[idx], do_all[idx]
+        al = np.ones(T) if alpha_all is None else alpha_all[idx]
+        be = np.ones(T) if beta_all is None else beta_all[idx]
+        S0i = np.zeros((dp, dv_)) if S0 is None else _f64(S0)[idx]
+        z0i = np.zeros(dp) if z0 is None else _f64(z0)[idx]
+        # P[t, s] = prod_{r=s+1..t} alpha_r (s <= t); c[t] = prod_{r<=t} alpha_r
+        P = decay_products(al, T)
+        c = np.cumprod(al)
+        A = fq @ fk.T                                   # raw scores
+        M = P * be[None, :]                             # decay and beta weights
+        W = A * M
+        num = W @ vv + c[:, None] * (fq @ S0i)
+        den = W.sum(1) + c * (fq @ z0i)
+        if normalize is True:
+            Dv = den + eps
+            o = num / Dv[:, None]
+            g_num = do / Dv[:, None]
+            g_den = -(do * o).sum(1) / Dv
+        elif normalize is False:
+            g_num = do.copy()
+            g_den = np.zeros(T)
+        elif normalize == "max1":
+            Dv = np.maximum(np.abs(den), 1.0)
+            o = num / Dv[:, None]
+            g_num = do / Dv[:, None]
+            # d/d den of max(|den|, 1): sign(den) where |den| > 1, else 0
+            g_den = np.where(np.abs(den) > 1.0, -np.sign(den) * (do * o).sum(1) / Dv, 0.0)
+        else:
+            raise ValueError(f"unknown read-out {normalize!r}")
+        dW = g_num @ vv.T + g_den[:, None]              # dL/dW_ts (s <= t used through M)
+        dA = dW * M
+        dfq = dA @ fk + c[:, None] * (g_num @ S0i.T + g_den[:, None] * z0i[None, :])
+        dfk = dA.T @ fq
+        out["dq"][idx] = dfq * dphq[idx]
+        out["dk"][idx] = dfk * dphk[idx]
+        out["dv"][idx] = W.T @ g_num
+        out["dS0"][idx] = (c[:, None] * fq).T @ g_num
+        out["dz0"][idx] = (c * g_den) @ fq
+        # decay: dL/dM_ts = dW_ts A_ts, and M_ts = beta_s prod_{r=s+1..t}
+        # alpha_r holds alpha_r exactly when s < r <= t (the start-state
+        # carry c_t when r <= t), so with every alpha_r > 0
+        #   dL/dalpha_r = [sum_{t>=r, s<r} dM_ts M_ts + sum_{t>=r} dc_t c_t] / alpha_r;
+        # dL/dbeta_s = sum_t dM_ts P_ts.
+        dM = dW * A
+        dc = (g_num * (fq @ S0i)).sum(1) + g_den * (fq @ z0i)
+        E = dM * M
+        below = np.concatenate([np.zeros((T, 1)), np.cumsum(E, axis=1)[:, :-1]], axis=1)
+        blk = np.cumsum(below[::-1], axis=0)[::-1]      # [t0, r] = sum_{t >= t0} sum_{s < r} E_ts
+        carry = np.cumsum((dc * c)[::-1])[::-1]
+        out["dalpha"][idx] = (np.diag(blk) + carry) / al
+        out["dbeta"][idx] = (dM * P).sum(0)
+    res = {n: out[n] for n in ("dq", "dk", "dv", "dS0", "dz0")}
+    if decay is not None:
+        res["ddecay"] = out["dalpha"]
+    if gate is not None:
+        # alpha = g, beta = 1 - g
+        res["dgate"] = out["dalpha"] - out["dbeta"]
+    return res
+
+
+# --------------------------------------------------------------------------
 # Accounting the pages print
 # --------------------------------------------------------------------------
 

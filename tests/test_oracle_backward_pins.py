@@ -1,0 +1,129 @@
+"""Pins for the oracle's prefill gradients: central finite differences of
+L = sum_t <dout_t, o_t> through the forward oracle (the recurrence, a
+different algorithm from the gradients' quadratic form), closed forms, and
+planted mistakes.  CPU only, float64, tiny inputs.
+"""
+import numpy as np
+import pytest
+
+from oracle import linattn_oracle as O
+
+H_FD = 1e-6
+
+
+def loss(q, k, v, do, phi, decay, gate, S0, z0, normalize, eps=1e-6):
+    o, _, _ = O.causal_linear_attention(q, k, v, phi=phi, decay=decay, gate=gate, eps=eps,
+                                        S0=S0, z0=z0, normalize=normalize)
+    return float((o * do).sum())
+
+
+def fd(f, x):
+    g = np.zeros_like(x)
+    for i in np.ndindex(x.shape):
+        xp, xm = x.copy(), x.copy()
+        xp[i] += H_FD
+        xm[i] -= H_FD
+        g[i] = (f(xp) - f(xm)) / (2 * H_FD)
+    return g
+
+
+def case(seed, T=7, d=3, dv=2, kind="none", scale=1.0):
+    rng = np.random.default_rng(seed)
+    q, k = rng.standard_normal((T, d)) * scale, rng.standard_normal((T, d)) * scale
+    v, do = rng.standard_normal((T, dv)), rng.standard_normal((T, dv))
+    S0, z0 = rng.standard_normal((d, dv)) * 0.3, np.abs(rng.standard_normal(d)) * 0.3
+    a = 1.0 / (1.0 + np.exp(-rng.standard_normal(T) - 1.0))
+    decay = a if kind == "ssd" else None
+    gate = a if kind == "rfa" else None
+    return q, k, v, do, S0, z0, decay, gate
+
+
+@pytest.mark.parametrize("phi", ["elu1", "identity"])
+@pytest.mark.parametrize("kind", ["none", "ssd", "rfa"])
+@pytest.mark.parametrize("normalize", [True, False, "max1"])
+def test_gradients_match_finite_differences(phi, kind, normalize):
+    q, k, v, do, S0, z0, decay, gate = case(3, kind=kind)
+    if phi == "identity" and normalize is True:
+        q, k = np.abs(q), np.abs(k)       # keep q.z away from 0 (signed features)
+    g = O.prefill_gradients(q, k, v, do, phi=phi, decay=decay, gate=gate, S0=S0, z0=z0,
+                            normalize=normalize)
+    f = lambda **kw: loss(**{**dict(q=q, k=k, v=v, do=do, phi=phi, decay=decay, gate=gate,
+                                    S0=S0, z0=z0, normalize=normalize), **kw})
+    checks = [("dq", q, lambda x: f(q=x)), ("dk", k, lambda x: f(k=x)),
+              ("dv", v, lambda x: f(v=x)), ("dS0", S0, lambda x: f(S0=x)),
+              ("dz0", z0, lambda x: f(z0=x))]
+    if decay is not None:
+        checks.append(("ddecay", decay, lambda x: f(decay=x)))
+    if gate is not None:
+        checks.append(("dgate", gate, lambda x: f(gate=x)))
+    for name, x, fn in checks:
+        ref = fd(fn, x)
+        np.testing.assert_allclose(g[name], ref, rtol=1e-6, atol=1e-7, err_msg=name)
+
+
+def test_gradients_are_linear_in_dout():
+    q, k, v, do, S0, z0, decay, _ = case(5, kind="ssd")
+    do2 = np.random.default_rng(9).standard_normal(do.shape)
+    g1 = O.prefill_gradients(q, k, v, do, decay=decay, S0=S0, z0=z0)
+    g2 = O.prefill_gradients(q, k, v, do2, decay=decay, S0=S0, z0=z0)
+    g12 = O.prefill_gradients(q, k, v, do + 2 * do2, decay=decay, S0=S0, z0=z0)
+    for n in ("dq", "dk", "dv", "dS0", "dz0", "ddecay"):
+        np.testing.assert_allclose(g12[n], g1[n] + 2 * g2[n], rtol=1e-10, atol=1e-12)
+
+
+def test_unnormalised_closed_forms():
+    # no normaliser, no decay: o_t = sum_{s<=t} (fq_t.fk_s) v_s + fq_t^T S0, so
+    # dv_s = sum_{t>=s} (fq_t.fk_s) do_t and dS0 = sum_t fq_t do_t^T
+    q, k, v, do, S0, z0, _, _ = case(7)
+    g = O.prefill_gradients(q, k, v, do, S0=S0, z0=z0, normalize=False)
+    fq, fk = O.phi_elu1(q), O.phi_elu1(k)
+    T = q.shape[0]
+    dv = np.zeros_like(v)
+    for s in range(T):
+        for t in range(s, T):
+            dv[s] += float(fq[t] @ fk[s]) * do[t]
+    np.testing.assert_allclose(g["dv"], dv, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(g["dS0"], fq.T @ do, rtol=1e-12, atol=1e-13)
+    np.testing.assert_array_equal(g["dz0"], 0.0)
+
+
+def test_single_token_closed_form():
+    # T = 1, zero state: o = v (fq.fk) / ((fq.fk) + eps); with eps -> the
+    # output is v whatever q and k, so dq, dk vanish up to O(eps), dv = do
+    rng = np.random.default_rng(2)
+    q, k = rng.standard_normal((1, 4)), rng.standard_normal((1, 4))
+    v, do = rng.standard_normal((1, 3)), rng.standard_normal((1, 3))
+    g = O.prefill_gradients(q, k, v, do, eps=0.0)
+    np.testing.assert_allclose(g["dv"], do, rtol=1e-14)
+    assert np.abs(g["dq"]).max() < 1e-12 and np.abs(g["dk"]).max() < 1e-12
+
+
+def _mutant(q, k, v, do, decay, mistake):
+    """A copy of the gradient with one plausible mistake (no decay, sum read-out)."""
+    fq, fk = O.phi_elu1(q), O.phi_elu1(k)
+    T = q.shape[0]
+    M = np.tril(np.ones((T, T)))
+    A = fq @ fk.T
+    W = A * M
+    num, den = W @ v, W.sum(1) + 1e-6
+    o = num / den[:, None]
+    g_num, g_den = do / den[:, None], -(do * o).sum(1) / den
+    if mistake == "no_den_term":
+        g_den = 0 * g_den
+    dW = g_num @ v.T + g_den[:, None]
+    dA = dW * M
+    if mistake == "mask_transposed":
+        dA = dW * M.T
+    dfq = dA @ fk
+    dq = dfq * O.phi_derivative(q)
+    if mistake == "no_phi_derivative":
+        dq = dfq
+    return dq
+
+
+@pytest.mark.parametrize("mistake", ["no_den_term", "mask_transposed", "no_phi_derivative"])
+def test_planted_mistakes_fail_finite_differences(mistake):
+    q, k, v, do, _, _, _, _ = case(11, scale=1.5)
+    ref = fd(lambda x: loss(x, k, v, do, "elu1", None, None, None, None, True), q)
+    assert np.abs(_mutant(q, k, v, do, None, mistake) - ref).max() > 1e-4
+    assert np.abs(_mutant(q, k, v, do, None, None) - ref).max() < 1e-7
