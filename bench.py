@@ -36,6 +36,10 @@ Printed as one JSON line:
                N(3, 1) and N(0, 1), fp32), read-out divided by
                max(|q.z|, 1), stabilised state; algorithmic bytes add the
                two gate arrays;
+  backward     la_prefill_backward (dq, dk, dv of L = sum <dout, out>) on the
+               same long-context prefill, and on the elu+1 prefill shape
+               B=4 H=8 T=2048 d=64: one workgroup per sequence walks the
+               tokens forward then backward;
   cpu_baseline the fp64 oracle (the CPU reference the tests check against),
                on a bounded sample of the same prefill workload, one worker
                process per head.
@@ -220,6 +224,29 @@ def bench_prefill(torch, la, I, steps, warmup, normalize=True, stages=True, caus
                 rep_median_ms=per[len(per) // 2], rep_min_ms=per[0])
 
 
+def bench_backward(torch, la, I, B, H, T, d, reps):
+    """ms per la_prefill_backward call (elu+1, no decay, bf16 inputs and dout)."""
+    dev = torch.device("cuda:0")
+    x = I.prefill_inputs(B, H, T, d, dtype="bf16", seed=0, scale=PF["scale"], device=dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(1)
+    do = torch.randn(B, H, T, d, generator=g, device=dev).to(torch.bfloat16)
+    ws = None
+    la.prefill_backward(x.q, x.k, x.v, do)             # warm-up
+    torch.cuda.synchronize()
+    e0, e1 = _events(torch)
+    e0.record()
+    for _ in range(reps):
+        la.prefill_backward(x.q, x.k, x.v, do, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    # algorithmic bytes: q, k, v, dout read (bf16), dq, dk, dv written (fp32)
+    nbytes = B * H * T * d * (4 * 2 + 3 * 4)
+    return dict(ms=ms, tokens_per_s=B * T / (ms * 1e-3), GBs=nbytes / (ms * 1e-3) / 1e9,
+                algorithmic_bytes=nbytes)
+
+
 def hbm_copy(torch, nbytes=1 << 30, reps=10):
     """Device-to-device streaming of `nbytes` (read + write) by two kernels,
     torch's copy and its vectorised negation (16 bytes per lane, like the
@@ -346,6 +373,9 @@ def main(argv=None):
     print("[bench] prefill, mLSTM gates", file=sys.stderr, flush=True)
     pf_ml = bench_prefill(torch, la, I, a.steps, a.warmup, mlstm=True)
     ml_bytes = step_bytes + TH * 2 * 4 + 2 * B * H * 4     # + the two gates, the stabiliser
+    print("[bench] backward", file=sys.stderr, flush=True)
+    bw_long = bench_backward(torch, la, I, B, H, T, d, 1)
+    bw_small = bench_backward(torch, la, I, 4, 8, 2048, 64, 5)
     cp = hbm_copy(torch)
     dec = dec_big = None
     if not a.no_decode:
@@ -405,6 +435,16 @@ def main(argv=None):
             "GBs": ml_bytes / (pf_ml["ms"] * 1e-3) / 1e9,
             "hbm_frac": ml_bytes / (pf_ml["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "stage3_GBs": (stage3_bytes + TH * 2 * 4) / (pf_ml["stage_ms"][2] * 1e-3) / 1e9},
+        "backward": {
+            "workload": "la_prefill_backward, elu+1, no decay, bf16 q, k, v, dout; fp32 dq, "
+                        "dk, dv; token-serial, one workgroup per sequence",
+            "long_context": {"B": B, "H": H, "T": T, "d": d, "ms": bw_long["ms"],
+                             "tokens_per_s": bw_long["tokens_per_s"],
+                             "GBs": bw_long["GBs"],
+                             "hbm_frac": bw_long["GBs"] / HBM_PEAK_GBS},
+            "elu_prefill_shape": {"B": 4, "H": 8, "T": 2048, "d": 64, "ms": bw_small["ms"],
+                                  "tokens_per_s": bw_small["tokens_per_s"],
+                                  "GBs": bw_small["GBs"]}},
     }
     if dec is not None:
         res["decode"] = {

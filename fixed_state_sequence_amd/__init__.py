@@ -23,8 +23,8 @@ from typing import Optional, Tuple
 from . import _lib
 from ._lib import LinAttnError  # noqa: F401
 
-__all__ = ["prefill", "prefill_stage", "decode_step", "state_init", "feature_dim",
-           "prefill_plan", "prefill_workspace_size", "make_desc", "LinAttnError"]
+__all__ = ["prefill", "prefill_stage", "prefill_backward", "decode_step", "state_init",
+           "feature_dim", "prefill_plan", "prefill_workspace_size", "make_desc", "LinAttnError"]
 
 
 def _torch():
@@ -246,6 +246,49 @@ def prefill_stage(stage: int, q, k, v, S, z, out, workspace, *, phi="elu1", W=No
                                            _ptr(S), _ptr(z), _ptr(out),
                                            _ptr(workspace) if nws else None, nws,
                                            _stream(q.device)))
+
+
+def prefill_backward(q, k, v, dout, *, phi: str = "elu1", decay=None, gate=None,
+                     eps: float = 1e-6, state: Optional[tuple] = None, normalize=True,
+                     state_grad: bool = False, workspace=None):
+    """Gradients of L = sum <dout, out> for la.prefill(q, k, v, ...) from the
+    initial state `state=(S0, z0)` (zero if None).  dout has out's layout and
+    dtype (q's, or float32).  Returns a dict of fp32 tensors: dq, dk, dv, and
+    ddecay (with `decay`) or dgate (with `gate`), and dS0, dz0 when
+    state_grad=True."""
+    torch = _torch()
+    desc, (B, H, T, d_h, d_v) = _prefill_desc(q, k, v, phi, None, decay, gate, eps, 0, 0,
+                                              dout.dtype, normalize, True)
+    _need(dout, "dout", device=q.device, shape=(B, H, T, d_v))
+    dp = feature_dim(d_h, phi)
+    S0 = z0 = None
+    if state is not None:
+        S0, z0 = state
+        _need(S0, "S0", device=q.device, dtype=torch.float32, shape=(B, H, dp, d_v))
+        _need(z0, "z0", device=q.device, dtype=torch.float32, shape=(B, H, dp))
+    f32 = dict(dtype=torch.float32, device=q.device)
+    g = {"dq": torch.empty(B, H, T, d_h, **f32), "dk": torch.empty(B, H, T, d_h, **f32),
+         "dv": torch.empty(B, H, T, d_v, **f32)}
+    dd = torch.empty(B, H, T, **f32) if (decay is not None or gate is not None) else None
+    dS0 = torch.empty(B, H, dp, d_v, **f32) if state_grad else None
+    dz0 = torch.empty(B, H, dp, **f32) if state_grad else None
+    n = ctypes.c_size_t(0)
+    L = _lib.lib()
+    _lib.check(L.la_prefill_backward_workspace_size(ctypes.byref(desc), ctypes.byref(n)))
+    nws = int(n.value)
+    if nws and (workspace is None or workspace.numel() * workspace.element_size() < nws):
+        workspace = torch.empty(nws, dtype=torch.uint8, device=q.device)
+    _lib.check(L.la_prefill_backward(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(S0),
+                                     _ptr(z0), _ptr(dout), _ptr(g["dq"]), _ptr(g["dk"]),
+                                     _ptr(g["dv"]), _ptr(dd), _ptr(dS0), _ptr(dz0),
+                                     _ptr(workspace) if nws else None, nws, _stream(q.device)))
+    if decay is not None:
+        g["ddecay"] = dd
+    if gate is not None:
+        g["dgate"] = dd
+    if state_grad:
+        g["dS0"], g["dz0"] = dS0, dz0
+    return g
 
 
 def decode_step(q, k, v, S, z, *, phi: str = "elu1", W=None, decay=None, gate=None,

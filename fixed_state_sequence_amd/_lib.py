@@ -54,6 +54,9 @@ _SIGNATURES = {
     "la_prefill_stage": (ctypes.c_int, [_D, ctypes.c_int, _P, _P, _P, _P, _P, _P, _P,
                                         ctypes.c_size_t, _P]),
     "la_decode_step": (ctypes.c_int, [_D, _P, _P, _P, _P, _P, _P, _P]),
+    "la_prefill_backward_workspace_size": (ctypes.c_int, [_D, ctypes.POINTER(ctypes.c_size_t)]),
+    "la_prefill_backward": (ctypes.c_int, [_D, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                           _P, ctypes.c_size_t, _P]),
     "la_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "la_last_error": (ctypes.c_char_p, []),
 }

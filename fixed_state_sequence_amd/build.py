@@ -18,7 +18,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "liblinattn.so")
 
-SOURCES = ["la_api.cpp", "la_recurrent.hip", "la_decode.hip", "la_prefill_mfma.hip"]
+SOURCES = ["la_api.cpp", "la_recurrent.hip", "la_decode.hip", "la_prefill_mfma.hip",
+           "la_backward.hip"]
 ARCH = "gfx950"
 
 

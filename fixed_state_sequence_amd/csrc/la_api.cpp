@@ -244,6 +244,59 @@ la_status la_prefill_stage(const la_desc* desc, int stage, const void* q, const 
   return run_stage(p, stage, q, k, v, S, z, out, workspace, static_cast<hipStream_t>(stream));
 }
 
+la_status la_prefill_backward_workspace_size(const la_desc* desc, size_t* bytes) {
+  if (!bytes) return fail(LA_EINVAL, "bytes is NULL");
+  la::Problem p;
+  LA_TRY(check_desc(desc, true, &p));
+  *bytes = la::backward_workspace_bytes(p);
+  return LA_OK;
+}
+
+la_status la_prefill_backward(const la_desc* desc, const void* q, const void* k, const void* v,
+                              const float* S0, const float* z0, const void* dout, float* dq,
+                              float* dk, float* dv, float* ddecay, float* dS0, float* dz0,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  la::Problem p;
+  LA_TRY(check_desc(desc, true, &p));
+  if (!la::backward_supported(p))
+    return fail(LA_EUNSUPPORTED,
+                "backward: needs a causal prefill with elu+1 or identity features, no decay, "
+                "SSD decay or the RFA gate, and widths the per-token kernel takes");
+  if ((S0 == nullptr) != (z0 == nullptr)) return fail(LA_EINVAL, "S0 and z0 go together");
+  if ((dS0 == nullptr) != (dz0 == nullptr)) return fail(LA_EINVAL, "dS0 and dz0 go together");
+  if (S0) {
+    LA_TRY(check_ptr(S0, "S0"));
+    LA_TRY(check_ptr(z0, "z0"));
+  }
+  if (dS0) {
+    LA_TRY(check_ptr(dS0, "dS0"));
+    LA_TRY(check_ptr(dz0, "dz0"));
+  }
+  if ((p.decay_kind != LA_DECAY_NONE) != (ddecay != nullptr))
+    return fail(LA_EINVAL, "ddecay is required with a decay or gate, and only then");
+  if (ddecay && !aligned(ddecay, 4)) return fail(LA_EINVAL, "ddecay must be 4-byte aligned");
+  if (p.T > 0) {
+    LA_TRY(check_ptr(q, "q"));
+    LA_TRY(check_ptr(k, "k"));
+    LA_TRY(check_ptr(v, "v"));
+    LA_TRY(check_ptr(dout, "dout"));
+    LA_TRY(check_ptr(dq, "dq"));
+    LA_TRY(check_ptr(dk, "dk"));
+    LA_TRY(check_ptr(dv, "dv"));
+  }
+  const size_t need = la::backward_workspace_bytes(p);
+  if (need > 0) {
+    if (!workspace) return fail(LA_EINVAL, "workspace is NULL (need %zu bytes)", need);
+    if (!aligned(workspace, 16)) return fail(LA_EINVAL, "workspace must be 16-byte aligned");
+    if (workspace_bytes < need)
+      return fail(LA_EINVAL, "workspace too small: %zu bytes given, %zu needed", workspace_bytes,
+                  need);
+  }
+  (void)hipGetLastError();
+  return launched(la::launch_backward(p, q, k, v, S0, z0, dout, dq, dk, dv, ddecay, dS0, dz0,
+                                      workspace, static_cast<hipStream_t>(stream)));
+}
+
 la_status la_decode_step(const la_desc* desc, const void* q, const void* k, const void* v,
                          float* S, float* z, void* out, void* stream) {
   la::Problem p;

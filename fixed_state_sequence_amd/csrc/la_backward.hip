@@ -1,0 +1,374 @@
+// Gradients of the causal prefill, one workgroup per (b, h) sequence with the
+// state slice held in registers (the layout of the per-token forward kernel).
+//
+// With L = sum_t <dout_t, o_t> and the read-out o_t = num_t / D_t
+// (num_t = S_t^T phi(q_t), D_t = phi(q_t).z_t + eps; or num_t alone; or
+// num_t / max(|phi(q_t).z_t|, 1)), the recurrence S_t = alpha_t S_{t-1} +
+// beta_t phi(k_t) v_t^T (llm-arch-kb "Linear Attention", section 2; wikillm
+// "Linear attention", Implementation sketch, SSD and RFA) gives, in reverse
+// mode:
+//   g_num_t = dout_t / D_t,  g_den_t = -(dout_t . o_t) / D_t   (read-out)
+//   dphi(q_t) = S_t g_num_t + z_t g_den_t
+//   G_t = alpha_{t+1} G_{t+1} + phi(q_t) g_num_t^T,  g_t likewise with g_den
+//   dphi(k_t) = beta_t (G_t v_t + g_t),  dv_t = beta_t G_t^T phi(k_t)
+//   dS0 = alpha_0 G_0,  dz0 = alpha_0 g_0.
+// The decay enters through the log-prefix l_t = sum_{r<=t} log alpha_r:
+// every weight is e^{l_t - l_s} beta_s, so dL/dl_t = <phi(q_t), dphi(q_t)> -
+// <phi(k_t), dphi(k_t)> and dL/dlog alpha_r = sum_{t>=r} dL/dl_t, a suffix sum
+// kept during the reverse pass; beta's own gradient is phi(k_t).(G_t v_t + g_t).
+//
+// Pass A walks t forward: it rebuilds S_t and z_t, the read-out, g_num,
+// g_den and dq, and leaves g_num_t, g_den_t and <phi(q_t), dphi(q_t)> in the
+// workspace.  Pass B walks t backward carrying G, g.  The efficient-attention
+// lesson ("Implementation reality") trains with the chunked form; this
+// token-serial kernel is the exact reference-grade path for every supported
+// configuration.
+#include "la_device.h"
+#include "la_internal.h"
+
+namespace la {
+namespace {
+
+constexpr int NT = 256;
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dout;
+  const float* S0;   // initial state or null (zero)
+  const float* z0;
+  const float* decay;
+  float* dq;
+  float* dk;
+  float* dv;
+  float* ddecay;     // [BH, T] or null
+  float* dS0;        // [BH, dp, dv] or null
+  float* dz0;
+  float* ws;         // [BH, T, dv + 2]
+  int H, T, dh, dv_, dp;
+  int phi, decay_kind, norm;
+  int dout_f32;      // dout is fp32 (else the input type)
+  float eps;
+};
+
+__device__ __forceinline__ float phi_of(float x, int phi) {
+  return phi == LA_PHI_IDENTITY ? x : elu1_accurate(x);
+}
+// derivative: elu+1 has slope 1 above 0 and e^x below; the identity 1
+__device__ __forceinline__ float dphi_of(float x, int phi) {
+  return phi == LA_PHI_IDENTITY ? 1.f : (x > 0.f ? 1.f : expf(x));
+}
+
+template <typename DT>
+__device__ __forceinline__ float load_dout(const BwdArgs& a, int64_t i) {
+  return a.dout_f32 ? static_cast<const float*>(a.dout)[i] : to_f32(static_cast<const DT*>(a.dout)[i]);
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
+template <typename DT, int NF4>
+__global__ __launch_bounds__(NT) void backward_kernel(const BwdArgs a) {
+  const int64_t bh = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int ncg = a.dv_ >> 2;     // float4 column groups (a power of two <= 64)
+  const int rpp = NT / ncg;       // state rows covered by one pass of the block
+  const int cg = tid % ncg;
+  const int r0 = tid / ncg;
+
+  __shared__ __align__(16) float s_q[256], s_k[256], s_v[256], s_do[256];
+  __shared__ __align__(16) float s_fq[256], s_fk[256], s_gn[256], s_part[256];
+  __shared__ __align__(16) float s_red[NT / 64][260];
+  __shared__ float s_sc[NT / 64][4];
+
+  const int64_t T = a.T;
+  const DT* qg = static_cast<const DT*>(a.q) + bh * T * a.dh;
+  const DT* kg = static_cast<const DT*>(a.k) + bh * T * a.dh;
+  const DT* vg = static_cast<const DT*>(a.v) + bh * T * a.dv_;
+  const int64_t do0 = bh * T * a.dv_;
+  const float* dg = a.decay ? a.decay + bh * T : nullptr;
+  float* wsg = a.ws + bh * T * (a.dv_ + 2);
+  const int wst = a.dv_ + 2;
+
+  auto coeffs = [&](int64_t t, float& al, float& be) {
+    al = 1.f;
+    be = 1.f;
+    if (a.decay_kind == LA_DECAY_SSD) {
+      al = dg[t];
+    } else if (a.decay_kind == LA_GATE_RFA) {
+      al = dg[t];
+      be = 1.f - al;
+    }
+  };
+
+  // ------------------------------------------------------------- pass A
+  float4 st[NF4];
+#pragma unroll
+  for (int i = 0; i < NF4; ++i) {
+    const int f = r0 + i * rpp;
+    st[i] = (a.S0 && f < a.dp) ? *reinterpret_cast<const float4*>(a.S0 + (bh * a.dp + f) * a.dv_ + 4 * cg)
+                               : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  float zr = (a.z0 && tid < a.dp) ? a.z0[bh * a.dp + tid] : 0.f;
+
+  for (int64_t t = 0; t < T; ++t) {
+    if (tid < a.dh) {
+      s_q[tid] = to_f32(qg[t * a.dh + tid]);
+      s_k[tid] = to_f32(kg[t * a.dh + tid]);
+    }
+    if (tid < a.dv_) {
+      s_v[tid] = to_f32(vg[t * a.dv_ + tid]);
+      s_do[tid] = load_dout<DT>(a, do0 + t * a.dv_ + tid);
+    }
+    float alpha, beta;
+    coeffs(t, alpha, beta);
+    __syncthreads();
+    if (tid < a.dp) {
+      s_fq[tid] = phi_of(s_q[tid], a.phi);
+      s_fk[tid] = phi_of(s_k[tid], a.phi);
+    }
+    __syncthreads();
+    // update and numerator partials
+    const float4 v4 = *reinterpret_cast<const float4*>(s_v + 4 * cg);
+    float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int i = 0; i < NF4; ++i) {
+      const int f = r0 + i * rpp;
+      if (f < a.dp) {
+        const float kb = beta * s_fk[f];
+        st[i].x = alpha * st[i].x + kb * v4.x;
+        st[i].y = alpha * st[i].y + kb * v4.y;
+        st[i].z = alpha * st[i].z + kb * v4.z;
+        st[i].w = alpha * st[i].w + kb * v4.w;
+        const float qf = s_fq[f];
+        num.x += qf * st[i].x;
+        num.y += qf * st[i].y;
+        num.z += qf * st[i].z;
+        num.w += qf * st[i].w;
+      }
+    }
+    float dpart = 0.f;
+    if (tid < a.dp) {
+      zr = alpha * zr + beta * s_fk[tid];
+      dpart = s_fq[tid] * zr;
+    }
+    for (int off = ncg; off < 64; off <<= 1) {
+      num.x += __shfl_xor(num.x, off);
+      num.y += __shfl_xor(num.y, off);
+      num.z += __shfl_xor(num.z, off);
+      num.w += __shfl_xor(num.w, off);
+    }
+    dpart = wave_sum(dpart);
+    if (lane < ncg) *reinterpret_cast<float4*>(&s_red[wave][4 * cg]) = num;
+    if (lane == 0) s_red[wave][256] = dpart;
+    __syncthreads();
+    // read-out: divisor, output, g_num and the dot product dout . o
+    float den = 0.f;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) den += s_red[w][256];
+    float scale;   // o = num * scale, g_num = dout * scale
+    if (a.norm == LA_NORM_NONE) scale = 1.f;
+    else if (a.norm == LA_NORM_MAX1) scale = 1.f / fmaxf(fabsf(den), 1.f);
+    else scale = 1.f / (den + a.eps);
+    float pv = 0.f;
+    if (tid < a.dv_) {
+      float n = 0.f;
+#pragma unroll
+      for (int w = 0; w < NT / 64; ++w) n += s_red[w][tid];
+      const float o = n * scale;
+      s_gn[tid] = s_do[tid] * scale;
+      pv = s_do[tid] * o;
+    }
+    pv = wave_sum(pv);
+    if (lane == 0) s_sc[wave][0] = pv;
+    __syncthreads();
+    float dot = 0.f;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) dot += s_sc[w][0];
+    float gden;
+    if (a.norm == LA_NORM_NONE) gden = 0.f;
+    else if (a.norm == LA_NORM_MAX1) gden = fabsf(den) > 1.f ? -copysignf(1.f, den) * dot * scale : 0.f;
+    else gden = -dot * scale;
+    // dphi(q_t) = S_t g_num + z_t g_den: the S part summed over the column groups
+    const float4 gn4 = *reinterpret_cast<const float4*>(s_gn + 4 * cg);
+#pragma unroll
+    for (int i = 0; i < NF4; ++i) {
+      float p = st[i].x * gn4.x + st[i].y * gn4.y + st[i].z * gn4.z + st[i].w * gn4.w;
+      for (int off = 1; off < ncg; off <<= 1) p += __shfl_xor(p, off);
+      const int f = r0 + i * rpp;
+      if (cg == 0 && f < a.dp) s_part[f] = p;
+    }
+    __syncthreads();
+    float qd = 0.f;
+    if (tid < a.dp) {
+      const float dfq = s_part[tid] + zr * gden;
+      a.dq[(bh * T + t) * a.dh + tid] = dfq * dphi_of(s_q[tid], a.phi);
+      qd = s_fq[tid] * dfq;
+    }
+    if (tid < a.dv_) wsg[t * wst + tid] = s_gn[tid];
+    qd = wave_sum(qd);
+    if (lane == 0) s_sc[wave][1] = qd;
+    __syncthreads();
+    if (tid == 0) {
+      float s = 0.f;
+#pragma unroll
+      for (int w = 0; w < NT / 64; ++w) s += s_sc[w][1];
+      wsg[t * wst + a.dv_] = gden;
+      wsg[t * wst + a.dv_ + 1] = s;
+    }
+  }
+  __syncthreads();   // pass A's workspace rows visible to every thread
+
+  // ------------------------------------------------------------- pass B
+#pragma unroll
+  for (int i = 0; i < NF4; ++i) st[i] = make_float4(0.f, 0.f, 0.f, 0.f);   // G
+  float gr = 0.f;                                                          // g
+  float R = 0.f;    // suffix sum of dL/dl_t
+  float alpha_next = 0.f;
+  for (int64_t t = T - 1; t >= 0; --t) {
+    if (tid < a.dh) {
+      s_q[tid] = to_f32(qg[t * a.dh + tid]);
+      s_k[tid] = to_f32(kg[t * a.dh + tid]);
+    }
+    if (tid < a.dv_) {
+      s_v[tid] = to_f32(vg[t * a.dv_ + tid]);
+      s_gn[tid] = wsg[t * wst + tid];
+    }
+    const float gden = wsg[t * wst + a.dv_];
+    const float qdq = wsg[t * wst + a.dv_ + 1];
+    float alpha, beta;
+    coeffs(t, alpha, beta);
+    __syncthreads();
+    if (tid < a.dp) {
+      s_fq[tid] = phi_of(s_q[tid], a.phi);
+      s_fk[tid] = phi_of(s_k[tid], a.phi);
+    }
+    __syncthreads();
+    // G_t = alpha_{t+1} G_{t+1} + phi(q_t) g_num_t^T; then G_t v_t (per row)
+    // and G_t^T phi(k_t) (per column) partials
+    const float4 gn4 = *reinterpret_cast<const float4*>(s_gn + 4 * cg);
+    const float4 v4 = *reinterpret_cast<const float4*>(s_v + 4 * cg);
+    float4 dvp = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int i = 0; i < NF4; ++i) {
+      const int f = r0 + i * rpp;
+      const float qf = f < a.dp ? s_fq[f] : 0.f;
+      const float kf = f < a.dp ? s_fk[f] : 0.f;
+      st[i].x = alpha_next * st[i].x + qf * gn4.x;
+      st[i].y = alpha_next * st[i].y + qf * gn4.y;
+      st[i].z = alpha_next * st[i].z + qf * gn4.z;
+      st[i].w = alpha_next * st[i].w + qf * gn4.w;
+      float p = st[i].x * v4.x + st[i].y * v4.y + st[i].z * v4.z + st[i].w * v4.w;
+      for (int off = 1; off < ncg; off <<= 1) p += __shfl_xor(p, off);
+      if (cg == 0 && f < a.dp) s_part[f] = p;
+      dvp.x += kf * st[i].x;
+      dvp.y += kf * st[i].y;
+      dvp.z += kf * st[i].z;
+      dvp.w += kf * st[i].w;
+    }
+    if (tid < a.dp) gr = alpha_next * gr + s_fq[tid] * gden;
+    for (int off = ncg; off < 64; off <<= 1) {
+      dvp.x += __shfl_xor(dvp.x, off);
+      dvp.y += __shfl_xor(dvp.y, off);
+      dvp.z += __shfl_xor(dvp.z, off);
+      dvp.w += __shfl_xor(dvp.w, off);
+    }
+    if (lane < ncg) *reinterpret_cast<float4*>(&s_red[wave][4 * cg]) = dvp;
+    __syncthreads();
+    float kd = 0.f;
+    if (tid < a.dp) {
+      const float raw = s_part[tid] + gr;       // G_t v_t + g_t
+      a.dk[(bh * T + t) * a.dh + tid] = beta * raw * dphi_of(s_k[tid], a.phi);
+      kd = s_fk[tid] * raw;
+    }
+    if (tid < a.dv_) {
+      float s = 0.f;
+#pragma unroll
+      for (int w = 0; w < NT / 64; ++w) s += s_red[w][tid];
+      a.dv[(bh * T + t) * a.dv_ + tid] = beta * s;
+    }
+    kd = wave_sum(kd);
+    if (lane == 0) s_sc[wave][2] = kd;
+    __syncthreads();
+    float kdk = 0.f;   // phi(k_t) . (G_t v_t + g_t), the gradient of beta_t
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) kdk += s_sc[w][2];
+    R += qdq - beta * kdk;
+    if (tid == 0 && a.ddecay) {
+      if (a.decay_kind == LA_DECAY_SSD) a.ddecay[bh * T + t] = R / alpha;
+      else if (a.decay_kind == LA_GATE_RFA) a.ddecay[bh * T + t] = R / alpha - kdk;
+    }
+    alpha_next = alpha;
+  }
+  // the start state enters S_0 as alpha_0 S0
+  if (a.dS0) {
+#pragma unroll
+    for (int i = 0; i < NF4; ++i) {
+      const int f = r0 + i * rpp;
+      if (f < a.dp) {
+        float4 x = st[i];
+        x.x *= alpha_next; x.y *= alpha_next; x.z *= alpha_next; x.w *= alpha_next;
+        *reinterpret_cast<float4*>(a.dS0 + (bh * a.dp + f) * a.dv_ + 4 * cg) = x;
+      }
+    }
+    if (tid < a.dp) a.dz0[bh * a.dp + tid] = alpha_next * gr;
+  }
+}
+
+int passes(int dp, int dv) {
+  const int ncg = dv / 4;
+  const int rpp = NT / ncg;
+  return (dp + rpp - 1) / rpp;
+}
+
+template <typename DT>
+hipError_t launch_dt(const BwdArgs& a, int64_t nbh, hipStream_t st) {
+  const int np = passes(a.dp, a.dv_);
+  const dim3 grid{unsigned(nbh)}, block{unsigned(NT)};
+  if (np <= 1) backward_kernel<DT, 1><<<grid, block, 0, st>>>(a);
+  else if (np <= 2) backward_kernel<DT, 2><<<grid, block, 0, st>>>(a);
+  else if (np <= 4) backward_kernel<DT, 4><<<grid, block, 0, st>>>(a);
+  else if (np <= 8) backward_kernel<DT, 8><<<grid, block, 0, st>>>(a);
+  else if (np <= 16) backward_kernel<DT, 16><<<grid, block, 0, st>>>(a);
+  else backward_kernel<DT, 32><<<grid, block, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool backward_supported(const Problem& p) {
+  return (p.phi == LA_PHI_ELU1 || p.phi == LA_PHI_IDENTITY) && p.dp == p.dh &&
+         p.decay_kind != LA_GATE_MLSTM && !p.noncausal && recurrent_supported(p.dh, p.dp, p.dv);
+}
+
+size_t backward_workspace_bytes(const Problem& p) {
+  return size_t(p.BH()) * size_t(p.T) * size_t(p.dv + 2) * sizeof(float);
+}
+
+hipError_t launch_backward(const Problem& p, const void* q, const void* k, const void* v,
+                           const float* S0, const float* z0, const void* dout, float* dq,
+                           float* dk, float* dv, float* ddecay, float* dS0, float* dz0,
+                           void* ws, hipStream_t stream) {
+  BwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.dout = dout; a.S0 = S0; a.z0 = z0; a.decay = p.decay;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.ddecay = ddecay; a.dS0 = dS0; a.dz0 = dz0;
+  a.ws = static_cast<float*>(ws);
+  a.H = p.H; a.T = p.T; a.dh = p.dh; a.dv_ = p.dv; a.dp = p.dp;
+  a.phi = int(p.phi); a.decay_kind = int(p.decay_kind); a.norm = p.norm;
+  a.dout_f32 = p.out_dtype == LA_F32 ? 1 : 0;
+  a.eps = p.eps;
+  switch (p.dtype) {
+    case LA_F32: return launch_dt<float>(a, p.BH(), stream);
+    case LA_BF16: return launch_dt<bf16_t>(a, p.BH(), stream);
+    case LA_F16: return launch_dt<f16_t>(a, p.BH(), stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace la

@@ -47,6 +47,15 @@ bool decode_supported(const Problem& p);
 hipError_t launch_decode(const Problem& p, const void* q, const void* k, const void* v,
                          float* S, float* z, void* out, hipStream_t stream);
 
+// Gradients of the causal prefill (per-token, two passes per sequence):
+// elu+1 or identity features, no decay / SSD / RFA, every read-out.
+bool backward_supported(const Problem& p);
+size_t backward_workspace_bytes(const Problem& p);
+hipError_t launch_backward(const Problem& p, const void* q, const void* k, const void* v,
+                           const float* S0, const float* z0, const void* dout, float* dq,
+                           float* dk, float* dv, float* ddecay, float* dS0, float* dz0,
+                           void* ws, hipStream_t stream);
+
 // Zero-fill of the state (m may be null).
 hipError_t launch_state_init(float* S, int64_t nS, float* z, int64_t nz, float* m, int64_t nm,
                              hipStream_t stream);

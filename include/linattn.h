@@ -203,6 +203,34 @@ la_status la_prefill_stage(const la_desc* desc, int stage, const void* q, const 
                            const void* v, float* S, float* z, void* out,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of device workspace la_prefill_backward needs for `desc`: B H T
+ * (d_v + 2) fp32.  Host only. */
+la_status la_prefill_backward_workspace_size(const la_desc* desc, size_t* bytes);
+
+/* Gradients of a causal prefill for training ([lesson] Developer level and
+ * "Implementation reality": training runs the same function, so these are
+ * the gradients of the definition).  With L = sum_t <dout_t, o_t> for the
+ * prefill that `desc`, q, k, v and the initial state (S0, z0) describe:
+ *   in:  q, k, v (dtype) [B, H, T, d]; dout [B, H, T, d_v] (out_dtype); the
+ *        initial state S0 [B, H, d', d_v], z0 [B, H, d'] fp32, both NULL for
+ *        a zero state; the decay or gate through desc;
+ *   out: dq, dk [B, H, T, d_h], dv [B, H, T, d_v] fp32; ddecay [B, H, T]
+ *        fp32 (dL/da_t for LA_DECAY_SSD, dL/dg_t for LA_GATE_RFA; NULL
+ *        without a decay, required with one); dS0, dz0 (dL/dS0, dL/dz0;
+ *        both NULL to skip).
+ * The decay gradient is formed through log a_t (a suffix sum of
+ * <phi(q_t), dphi(q_t)> - <phi(k_t), dphi(k_t)>, divided by a_t), so it is
+ * undefined (inf/NaN as data) where a decay or gate value is exactly 0.
+ * Supported: causal, elu+1 or identity features, LA_DECAY_NONE, LA_DECAY_SSD
+ * or LA_GATE_RFA, every read-out form, the widths the per-token kernel takes
+ * (LA_EUNSUPPORTED otherwise: RFF, the mLSTM gates, the non-causal form).
+ * One workgroup walks each (b, h) sequence token by token, forward then
+ * backward.  `workspace` holds la_prefill_backward_workspace_size() bytes. */
+la_status la_prefill_backward(const la_desc* desc, const void* q, const void* k, const void* v,
+                              const float* S0, const float* z0, const void* dout, float* dq,
+                              float* dk, float* dv, float* ddecay, float* dS0, float* dz0,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
 /* One autoregressive step for B sequences x H heads ([kb] section 2, causal
  * recurrence; [card] "When to use which": memory-bound decoding with a
  * fixed-size state): reads q, k [B, H, d_h], v [B, H, d_v] and the gate or

@@ -190,3 +190,30 @@ def test_mlstm_descriptor_checks():
     assert la.prefill_plan(d)[2] == 0
     assert la.prefill_plan(desc(phi="identity", **base))[2] == 0
     assert L.la_feature_dim(ctypes.byref(desc(phi="identity", **base))) == 128
+
+
+def test_backward_checks():
+    bw = lambda d, ddecay=None, S0=None, z0=None, dS0=None, dz0=None, nws=1 << 40: status(
+        L.la_prefill_backward(ctypes.byref(d), FAKE, FAKE, FAKE, S0, z0, FAKE, FAKE, FAKE, FAKE,
+                              ddecay, dS0, dz0, FAKE, nws, None))
+    base = dict(T=300, d_h=64, d_v=64, dtype_code=_lib.LA_BF16)
+    n = ctypes.c_size_t(0)
+    assert status(L.la_prefill_backward_workspace_size(ctypes.byref(desc(**base)), ctypes.byref(n))) == "LA_OK"
+    assert n.value == 8 * 300 * (64 + 2) * 4
+    # not covered: RFF, the mLSTM gates, the non-causal form
+    d = desc(T=16, d_h=64, d_v=64, dtype_code=_lib.LA_F32)
+    d.phi, d.rff_D, d.rff_W = _lib.LA_PHI_RFF, 32, FAKE
+    assert bw(d) == "LA_EUNSUPPORTED"
+    d = desc(phi="identity", **base)
+    d.decay_kind, d.decay, d.igate, d.stab = _lib.LA_GATE_MLSTM, FAKE, FAKE, FAKE
+    assert bw(d, ddecay=FAKE) == "LA_EUNSUPPORTED"
+    assert bw(desc(causal=False, **base)) == "LA_EUNSUPPORTED"
+    # ddecay exactly with a decay; S0/z0 and dS0/dz0 in pairs; workspace size
+    d = desc(**base)
+    d.decay_kind, d.decay = _lib.LA_DECAY_SSD, FAKE
+    assert bw(d) == "LA_EINVAL"
+    assert bw(desc(**base), ddecay=FAKE) == "LA_EINVAL"
+    assert bw(desc(**base), S0=FAKE) == "LA_EINVAL"
+    assert bw(desc(**base), dS0=FAKE) == "LA_EINVAL"
+    assert bw(desc(**base), nws=n.value - 1) == "LA_EINVAL"
+    assert "workspace" in L.la_last_error().decode()
