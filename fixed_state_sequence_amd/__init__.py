@@ -250,14 +250,15 @@ def prefill_stage(stage: int, q, k, v, S, z, out, workspace, *, phi="elu1", W=No
 
 def prefill_backward(q, k, v, dout, *, phi: str = "elu1", decay=None, gate=None,
                      eps: float = 1e-6, state: Optional[tuple] = None, normalize=True,
-                     state_grad: bool = False, workspace=None):
+                     state_grad: bool = False, segments: int = 0, workspace=None):
     """Gradients of L = sum <dout, out> for la.prefill(q, k, v, ...) from the
     initial state `state=(S0, z0)` (zero if None).  dout has out's layout and
     dtype (q's, or float32).  Returns a dict of fp32 tensors: dq, dk, dv, and
     ddecay (with `decay`) or dgate (with `gate`), and dS0, dz0 when
-    state_grad=True."""
+    state_grad=True.  `segments` (0 = the default plan) sets how many runs of
+    32-token chunks each sequence is cut into on the chunked path."""
     torch = _torch()
-    desc, (B, H, T, d_h, d_v) = _prefill_desc(q, k, v, phi, None, decay, gate, eps, 0, 0,
+    desc, (B, H, T, d_h, d_v) = _prefill_desc(q, k, v, phi, None, decay, gate, eps, 0, segments,
                                               dout.dtype, normalize, True)
     _need(dout, "dout", device=q.device, shape=(B, H, T, d_v))
     dp = feature_dim(d_h, phi)

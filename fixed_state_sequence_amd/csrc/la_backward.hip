@@ -348,6 +348,7 @@ bool backward_supported(const Problem& p) {
 }
 
 size_t backward_workspace_bytes(const Problem& p) {
+  if (backward_chunked(p)) return backward_chunked_workspace_bytes(p);
   return size_t(p.BH()) * size_t(p.T) * size_t(p.dv + 2) * sizeof(float);
 }
 
@@ -355,6 +356,8 @@ hipError_t launch_backward(const Problem& p, const void* q, const void* k, const
                            const float* S0, const float* z0, const void* dout, float* dq,
                            float* dk, float* dv, float* ddecay, float* dS0, float* dz0,
                            void* ws, hipStream_t stream) {
+  if (backward_chunked(p))
+    return launch_backward_chunked(p, q, k, v, S0, z0, dout, dq, dk, dv, dS0, dz0, ws, stream);
   BwdArgs a;
   a.q = q; a.k = k; a.v = v; a.dout = dout; a.S0 = S0; a.z0 = z0; a.decay = p.decay;
   a.dq = dq; a.dk = dk; a.dv = dv; a.ddecay = ddecay; a.dS0 = dS0; a.dz0 = dz0;

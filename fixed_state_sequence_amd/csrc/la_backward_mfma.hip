@@ -1,0 +1,764 @@
+// Gradients of the causal prefill by chunks on CDNA4 MFMA (gfx950), for
+// bf16 inputs with elu+1 features, no decay and d' = d_v = D in {64, 128}.
+//
+// With L = sum_t <dout_t, o_t>, o_t = num_t r_t (r_t = 1 / (den_t + eps), or
+// 1 / max(|den_t|, 1), or 1), the recurrence S_t = S_{t-1} + phi(k_t) v_t^T
+// (llm-arch-kb "Linear Attention", section 2) gives, with g_t = r_t dout_t and
+// h_t the gradient of the divisor (-r_t dout_t . o_t for the sum read-out):
+//   dphi(q_t) = sum_{s<=t} (g_t . v_s + h_t) phi(k_s)     (= S_t g_t + z_t h_t)
+//   dphi(k_s) = sum_{t>=s} (g_t . v_s + h_t) phi(q_t)     (= G_s v_s + gz_s)
+//   dv_s      = sum_{t>=s} (phi(q_t) . phi(k_s)) g_t      (= G_s^T phi(k_s))
+// with the gradient state G_s = sum_{t>=s} phi(q_t) g_t^T, gz_s likewise
+// with h_t.  Both sums have the masked-quadratic form of the forward pass, so
+// they take its chunked bracketing (efficient-attention lesson "Linear
+// attention", "Implementation reality": chunks, quadratic inside, a scan
+// across): inside a chunk the C x C score tiles, across chunks the states.
+//
+// Schedule (one workgroup per segment of whole 32-token chunks):
+//   forward stages 1 and 2 of the prefill: the start state of every segment;
+//   pass A (chunks in order): the forward read-out again (r_t, h_t, g_t),
+//     dq, and the segment's share of the gradient state, G_seg = sum over
+//     its tokens of phi(q_t) g_t^T (and gz_seg);
+//   reverse scan over the segments: G at every segment's end, and
+//     dS0 = G_0, dz0 = gz_0 (the initial state enters every S_t unchanged);
+//   pass B (chunks in reverse): dk and dv from the carried G.
+//
+// MFMA layout (v_mfma_f32_32x32x16_bf16, g = lane / 32, n = lane % 32): an
+// operand register holds k-values 8 g .. 8 g + 7 of row n; the accumulator
+// holds column n, rows 8 (i / 4) + 4 g + i % 4.  Score tiles are computed
+// with the token that is summed over on the accumulator's row axis, so that
+// the accumulator, packed to bf16, is the next product's operand when the
+// other operand's token axis is read in the permuted order perm_pos (every
+// token tile is stored with its rows at perm_pos(token)).
+//
+// Precision.  The gradients of the first tokens are sums of few terms and
+// the largest of the sequence (they shrink about like 1/sqrt(t) without
+// decay), so a rounding error there is measured against a much smaller rms:
+// the chunks that start before token 256 take every product with both
+// operands as bf16 high + low parts (three MFMAs: hi hi, lo hi, hi lo).
+// Elsewhere the score tiles and g enter as high + low parts, and the states
+// S and G enter the read-out and the products whose terms cancel (S g + z h
+// and G v + gz, whose differences are sum_s phi(k_s) g.(v_s - o_t) and its
+// transpose) as high + low parts; phi(q), phi(k) and the other products
+// stay bf16, their rounding errors averaging out over the chunk.
+#include "la_internal.h"
+#include "la_mfma_common.h"
+
+namespace la {
+namespace {
+
+constexpr int BCH = 32;            // chunk length
+constexpr int kExactTokens = 256;  // chunks starting before this split every operand
+
+template <int D>
+struct BL {
+  static constexpr int NW = D / 32;          // waves; wave w owns 32-wide block w
+  static constexpr int NT = 64 * NW;
+  static constexpr int NJ = D / 32;          // 32-wide blocks of D
+  static constexpr int BPR = D / 8;          // 16-byte blocks per bf16 row
+  static constexpr int TILE = BCH * D * 2;   // one token tile, bf16
+  static constexpr int FS = D + 4;           // fp32 row stride (floats)
+  // token tiles (bf16, rows at perm_pos(token), tile_off<D> swizzle)
+  static constexpr int Q = 0;                // phi(q), high part
+  static constexpr int QL = Q + TILE;        // phi(q), low part
+  static constexpr int K = QL + TILE;        // phi(k), high part
+  static constexpr int KL = K + TILE;        // phi(k), low part
+  static constexpr int V = KL + TILE;        // v
+  static constexpr int GH = V + TILE;        // g, high part
+  static constexpr int GL = GH + TILE;       // g, low part
+  static constexpr int SB = GL + TILE;       // the carried state (S in A, G in B), bf16, rows = features
+  static constexpr int SBL = SB + D * D * 2; // its low part
+  static constexpr int PD = SBL + D * D * 2; // fp32 [BCH][FS]: phi'(q) (A) or phi'(k) (B)
+  static constexpr int DO = PD + BCH * FS * 4;  // fp32 [BCH][FS]: dout (A)
+  static constexpr int F = DO + BCH * FS * 4;   // fp32 scalars, offsets below (floats)
+  static constexpr int Z = 0;                // z (A) or gz (B), carried
+  static constexpr int GZ = D;               // gz of the segment (A)
+  static constexpr int DI = 2 * D;           // phi(q_t) . z per token (A)
+  static constexpr int HT = DI + BCH;        // h_t per token
+  static constexpr int HP = HT + BCH;        // per-wave partial dout . o [NW][BCH]
+  static constexpr int NF = HP + NW * BCH;
+  static constexpr int LDS = F + NF * 4;
+};
+
+struct BwArgs {
+  const bf16_t* q;
+  const bf16_t* k;
+  const bf16_t* v;
+  const void* dout;
+  int dout_f32;
+  // start state of (b, h) and segment s at S0 + bh * s_bh + s * s_seg (z at
+  // z0 + bh * z_bh + s * s_seg); null: zero
+  const float* S0;
+  const float* z0;
+  int64_t s_bh, z_bh, s_seg;
+  float* dq;
+  float* dk;
+  float* dv;
+  float* gslot;  // [BH, nseg, D*D + D]: G_seg (pass A), then G at the segment's end
+  float* tok;    // [BH, T, 2]: r_t and h_t
+  int T, cps, nseg, norm;
+  float eps;
+};
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 x;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) x[i] = 0.f;
+  return x;
+}
+
+__device__ __forceinline__ float lds_bf16(const char* tile, int off) {
+  return __uint_as_float(uint32_t(*reinterpret_cast<const uint16_t*>(tile + off)) << 16);
+}
+
+// Element (token row `row` already permuted, feature f) of a token tile.
+template <int D>
+__device__ __forceinline__ int elem_off(int row, int f) {
+  return tile_off<D>(row, f >> 3) + ((f & 7) << 1);
+}
+
+// The accumulator rows 8 (i / 4) + 4 g + i % 4, as bf16 high and low parts:
+// the two k-steps of the next product.
+__device__ __forceinline__ void split_acc(const f32x16& x, u32x4 (&hi)[2], u32x4 (&lo)[2]) {
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      uint32_t h, l;
+      split_bf16(x[8 * ks + 2 * e], x[8 * ks + 2 * e + 1], h, l);
+      hi[ks][e] = h;
+      lo[ks][e] = l;
+    }
+}
+
+// Write a D x D state held as transposed accumulator tiles X[fb] (rows j of
+// block jb, columns f of block fb) into the bf16 tiles at rows f: high parts
+// at sb, low parts at sbl.
+template <int D>
+__device__ __forceinline__ void write_state_tile(char* sb, char* sbl, const f32x16 (&X)[D / 32],
+                                                 int jb, int g, int n) {
+#pragma unroll
+  for (int fb = 0; fb < D / 32; ++fb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      uint32_t h0, h1, l0, l1;
+      split_bf16(X[fb][4 * r], X[fb][4 * r + 1], h0, l0);
+      split_bf16(X[fb][4 * r + 2], X[fb][4 * r + 3], h1, l1);
+      const int off = tile_off<D>(32 * fb + n, 4 * jb + r) + 8 * g;
+      *reinterpret_cast<u32x2*>(sb + off) = u32x2{h0, h1};
+      *reinterpret_cast<u32x2*>(sbl + off) = u32x2{l0, l1};
+    }
+}
+
+// Raw inputs of one chunk for this thread: rows r and r + 16, block b.
+struct Raw {
+  u32x4 q[2], k[2], v[2];
+  f32x4 d[2][2];   // dout as fp32
+};
+
+template <int D>
+__device__ __forceinline__ void load_raw(const BwArgs& a, int64_t bh, int t0, int tid, Raw& x) {
+  using L = BL<D>;
+  const int b = tid % L::BPR;
+  const int64_t T = a.T;
+#pragma unroll
+  for (int rr = 0; rr < 2; ++rr) {
+    const int r = tid / L::BPR + 16 * rr;
+    const int64_t t = min(int64_t(t0 + r), T - 1);
+    const int64_t row = (bh * T + t) * D + 8 * b;
+    x.q[rr] = *reinterpret_cast<const u32x4*>(a.q + row);
+    x.k[rr] = *reinterpret_cast<const u32x4*>(a.k + row);
+    x.v[rr] = *reinterpret_cast<const u32x4*>(a.v + row);
+    if (a.dout_f32) {
+      const float* dp = static_cast<const float*>(a.dout) + row;
+      x.d[rr][0] = *reinterpret_cast<const f32x4*>(dp);
+      x.d[rr][1] = *reinterpret_cast<const f32x4*>(dp + 4);
+    } else {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const bf16_t*>(a.dout) + row);
+      float f[8];
+      unpack8(w, f, bf16_t{});
+      x.d[rr][0] = f32x4{f[0], f[1], f[2], f[3]};
+      x.d[rr][1] = f32x4{f[4], f[5], f[6], f[7]};
+    }
+  }
+}
+
+// Stage one chunk into LDS: phi(q), phi(k) (high, low), v; pass A also the
+// fp32 dout, phi'(q) and phi(q_t) . z; pass B g = r_t dout (high, low),
+// phi'(k) and h_t.  Rows past the end of the sequence are zero.
+template <int D, bool PASS_A>
+__device__ __forceinline__ void stage(const BwArgs& a, int64_t bh, int t0, int tid, const Raw& x,
+                                      char* smem) {
+  using L = BL<D>;
+  float* F = reinterpret_cast<float*>(smem + L::F);
+  const int b = tid % L::BPR;
+#pragma unroll
+  for (int rr = 0; rr < 2; ++rr) {
+    const int r = tid / L::BPR + 16 * rr;
+    const bool valid = t0 + r < a.T;
+    const int pr = perm_pos(r);
+    float xq[8], xk[8], fq[8], fk[8], pd[8];
+    unpack8(x.q[rr], xq, bf16_t{});
+    unpack8(x.k[rr], xk, bf16_t{});
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      fq[e] = valid ? elu1_accurate(xq[e]) : 0.f;
+      fk[e] = valid ? elu1_accurate(xk[e]) : 0.f;
+      // elu+1 has slope 1 above 0 and e^x = phi(x) below
+      pd[e] = valid ? (PASS_A ? (xq[e] > 0.f ? 1.f : fq[e]) : (xk[e] > 0.f ? 1.f : fk[e])) : 0.f;
+    }
+    const u32x4 qh = pack8(fq);
+    blk_write<D>(smem + L::Q, pr, b, qh);
+    blk_write<D>(smem + L::QL, pr, b, low8(fq, qh));
+    const u32x4 kh = pack8(fk);
+    blk_write<D>(smem + L::K, pr, b, kh);
+    blk_write<D>(smem + L::KL, pr, b, low8(fk, kh));
+    blk_write<D>(smem + L::V, pr, b, valid ? x.v[rr] : u32x4{0u, 0u, 0u, 0u});
+    float* pdr = reinterpret_cast<float*>(smem + L::PD) + r * L::FS + 8 * b;
+    *reinterpret_cast<f32x4*>(pdr) = f32x4{pd[0], pd[1], pd[2], pd[3]};
+    *reinterpret_cast<f32x4*>(pdr + 4) = f32x4{pd[4], pd[5], pd[6], pd[7]};
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    const f32x4 d0 = valid ? x.d[rr][0] : zero4, d1 = valid ? x.d[rr][1] : zero4;
+    if constexpr (PASS_A) {
+      float* dor = reinterpret_cast<float*>(smem + L::DO) + r * L::FS + 8 * b;
+      *reinterpret_cast<f32x4*>(dor) = d0;
+      *reinterpret_cast<f32x4*>(dor + 4) = d1;
+      float part = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part += fq[e] * F[L::Z + 8 * b + e];
+      part = row_sum<L::BPR>(part);
+      if (b == 0) F[L::DI + r] = part;
+    } else {
+      float rt = 0.f, ht = 0.f;
+      if (valid) {
+        const float2 th = *reinterpret_cast<const float2*>(a.tok + (bh * a.T + t0 + r) * 2);
+        rt = th.x;
+        ht = th.y;
+      }
+      float gv[8] = {d0[0] * rt, d0[1] * rt, d0[2] * rt, d0[3] * rt,
+                     d1[0] * rt, d1[1] * rt, d1[2] * rt, d1[3] * rt};
+      const u32x4 gh = pack8(gv);
+      blk_write<D>(smem + L::GH, pr, b, gh);
+      blk_write<D>(smem + L::GL, pr, b, low8(gv, gh));
+      if (b == 0) F[L::HT + r] = ht;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ pass A
+
+template <int D>
+__global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_a(const BwArgs a) {
+  using L = BL<D>;
+  constexpr int NJ = L::NJ;
+  __shared__ __align__(16) char smem[L::LDS];
+  float* F = reinterpret_cast<float*>(smem + L::F);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, n = lane & 31;
+  const int64_t bh = blockIdx.x / a.nseg;
+  const int seg = blockIdx.x % a.nseg;
+  const int T = a.T;
+  const int nchunks = (T + BCH - 1) / BCH;
+  const int c0 = seg * a.cps, c1 = min(c0 + a.cps, nchunks);
+
+  // start state: S^T tiles (rows j of block w, columns f of block fb)
+  f32x16 S[NJ], Gs[NJ];
+  {
+    const float* Ss = a.S0 ? a.S0 + bh * a.s_bh + int64_t(seg) * a.s_seg : nullptr;
+#pragma unroll
+    for (int fb = 0; fb < NJ; ++fb) {
+      Gs[fb] = zero16();
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int f = 32 * fb + n, j = 32 * w + 8 * (i >> 2) + 4 * g + (i & 3);
+        S[fb][i] = Ss ? Ss[f * D + j] : 0.f;
+      }
+    }
+    if (tid < D) {
+      F[L::Z + tid] = a.z0 ? a.z0[bh * a.z_bh + int64_t(seg) * a.s_seg + tid] : 0.f;
+      F[L::GZ + tid] = 0.f;
+    }
+    write_state_tile<D>(smem + L::SB, smem + L::SBL, S, w, g, n);
+  }
+  __syncthreads();
+
+  Raw raw;
+  if (c0 < c1) load_raw<D>(a, bh, c0 * BCH, tid, raw);
+  for (int c = c0; c < c1; ++c) {
+    const int t0 = c * BCH;
+    stage<D, true>(a, bh, t0, tid, raw, smem);
+    __syncthreads();   // tiles, phi(q) . z
+    if (c + 1 < c1) load_raw<D>(a, bh, t0 + BCH, tid, raw);   // next chunk, in flight meanwhile
+    const bool exact = t0 < kExactTokens;
+    const bool vt = t0 + n < T;
+
+    // scores P^T (rows s, columns t = n), causal mask, row sums
+    f32x16 sc = zero16();
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const u32x4 bq = row_operand<D>(smem + L::Q, perm_pos(n), 2 * ks + g);
+      const u32x4 ak = row_operand<D>(smem + L::K, perm_pos(n), 2 * ks + g);
+      sc = mfma(ak, bq, sc);
+      if (exact) {
+        sc = mfma(row_operand<D>(smem + L::KL, perm_pos(n), 2 * ks + g), bq, sc);
+        sc = mfma(ak, row_operand<D>(smem + L::QL, perm_pos(n), 2 * ks + g), sc);
+      }
+    }
+    float dsum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int s = 8 * (i >> 2) + 4 * g + (i & 3);
+      sc[i] = s <= n ? sc[i] : 0.f;
+      dsum += sc[i];
+    }
+    dsum = swap_sum32(dsum);
+    const float den = dsum + F[L::DI + n];
+    const float rt = a.norm == LA_NORM_NONE ? 1.f
+                     : a.norm == LA_NORM_MAX1 ? 1.f / fmaxf(fabsf(den), 1.f)
+                                              : 1.f / (den + a.eps);
+    u32x4 ph[2], pl[2];
+    split_acc(sc, ph, pl);
+
+    // numerator^T (rows j of block w, columns t): P V + phi(Q) S
+    f32x16 nu = zero16();
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const u32x4 av = tr_operand<D>(smem + L::V, 16 * ks, 32 * w, lane);
+      nu = mfma(av, ph[ks], nu);
+      nu = mfma(av, pl[ks], nu);
+    }
+#pragma unroll
+    for (int fs = 0; fs < D / 16; ++fs) {
+      const u32x4 bq = row_operand<D>(smem + L::Q, perm_pos(n), 2 * fs + g);
+      const u32x4 as = tr_operand<D>(smem + L::SB, 16 * fs, 32 * w, lane);
+      nu = mfma(as, bq, nu);
+      nu = mfma(tr_operand<D>(smem + L::SBL, 16 * fs, 32 * w, lane), bq, nu);
+      if (exact) nu = mfma(as, row_operand<D>(smem + L::QL, perm_pos(n), 2 * fs + g), nu);
+    }
+
+    // o = num r_t; g = dout r_t (bf16 high and low tiles); dout . o partials
+    float hp = 0.f;
+    const float* dor = reinterpret_cast<const float*>(smem + L::DO) + n * L::FS + 32 * w + 4 * g;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(dor + 8 * r);
+      float gv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        hp += d4[e] * (nu[4 * r + e] * rt);
+        gv[e] = vt ? d4[e] * rt : 0.f;
+      }
+      uint32_t h0, h1, l0, l1;
+      split_bf16(gv[0], gv[1], h0, l0);
+      split_bf16(gv[2], gv[3], h1, l1);
+      const int off = tile_off<D>(perm_pos(n), 4 * w + r) + 8 * g;
+      *reinterpret_cast<u32x2*>(smem + L::GH + off) = u32x2{h0, h1};
+      *reinterpret_cast<u32x2*>(smem + L::GL + off) = u32x2{l0, l1};
+    }
+    hp = swap_sum32(hp);
+    if (g == 0) F[L::HP + w * BCH + n] = hp;
+    __syncthreads();   // g tiles, partials
+
+    float dot = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < L::NW; ++ww) dot += F[L::HP + ww * BCH + n];
+    float h = 0.f;
+    if (a.norm == LA_NORM_SUM) h = -dot * rt;
+    else if (a.norm == LA_NORM_MAX1) h = fabsf(den) > 1.f ? -copysignf(1.f, den) * dot * rt : 0.f;
+    if (!vt) h = 0.f;
+    if (w == 0 && g == 0) {
+      F[L::HT + n] = h;
+      if (vt) *reinterpret_cast<float2*>(a.tok + (bh * T + t0 + n) * 2) = make_float2(rt, h);
+    }
+
+    // B^T (rows s, columns t): g_t . v_s + h_t, causal mask
+    f32x16 bs = zero16();
+#pragma unroll
+    for (int js = 0; js < D / 16; ++js) {
+      const u32x4 av = row_operand<D>(smem + L::V, perm_pos(n), 2 * js + g);
+      bs = mfma(av, row_operand<D>(smem + L::GH, perm_pos(n), 2 * js + g), bs);
+      bs = mfma(av, row_operand<D>(smem + L::GL, perm_pos(n), 2 * js + g), bs);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int s = 8 * (i >> 2) + 4 * g + (i & 3);
+      bs[i] = s <= n ? bs[i] + h : 0.f;
+    }
+    u32x4 bh_[2], bl_[2];
+    split_acc(bs, bh_, bl_);
+
+    // dphi(q)^T (rows f of block w, columns t): phi(K)^T B + S g + z h
+    f32x16 dqa = zero16();
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const u32x4 ak = tr_operand<D>(smem + L::K, 16 * ks, 32 * w, lane);
+      dqa = mfma(ak, bh_[ks], dqa);
+      dqa = mfma(ak, bl_[ks], dqa);
+      if (exact) dqa = mfma(tr_operand<D>(smem + L::KL, 16 * ks, 32 * w, lane), bh_[ks], dqa);
+    }
+    // S g and z h cancel in large part (their difference is
+    // sum_s phi(k_s) g.(v_s - o_t)): S and g enter as high + low parts
+#pragma unroll
+    for (int js = 0; js < D / 16; ++js) {
+      const u32x4 sh = row_operand<D>(smem + L::SB, 32 * w + n, 2 * js + g);
+      const u32x4 gh = row_operand<D>(smem + L::GH, perm_pos(n), 2 * js + g);
+      dqa = mfma(sh, gh, dqa);
+      dqa = mfma(row_operand<D>(smem + L::SBL, 32 * w + n, 2 * js + g), gh, dqa);
+      dqa = mfma(sh, row_operand<D>(smem + L::GL, perm_pos(n), 2 * js + g), dqa);
+    }
+    if (vt) {
+      const float* pdr = reinterpret_cast<const float*>(smem + L::PD) + n * L::FS + 32 * w + 4 * g;
+      float* dst = a.dq + (bh * T + t0 + n) * D + 32 * w + 4 * g;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const f32x4 p4 = *reinterpret_cast<const f32x4*>(pdr + 8 * r);
+        const f32x4 z4 = *reinterpret_cast<const f32x4*>(F + L::Z + 32 * w + 4 * g + 8 * r);
+        f32x4 o4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o4[e] = (dqa[4 * r + e] + z4[e] * h) * p4[e];
+        *reinterpret_cast<f32x4*>(dst + 8 * r) = o4;
+      }
+    }
+
+    // the segment's gradient state: G_seg^T += g^T phi(Q)
+#pragma unroll
+    for (int fb = 0; fb < NJ; ++fb)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const u32x4 ag = tr_operand<D>(smem + L::GH, 16 * ks, 32 * w, lane);
+        const u32x4 bq = tr_operand<D>(smem + L::Q, 16 * ks, 32 * fb, lane);
+        Gs[fb] = mfma(ag, bq, Gs[fb]);
+        if (exact) {
+          Gs[fb] = mfma(tr_operand<D>(smem + L::GL, 16 * ks, 32 * w, lane), bq, Gs[fb]);
+          Gs[fb] = mfma(ag, tr_operand<D>(smem + L::QL, 16 * ks, 32 * fb, lane), Gs[fb]);
+        }
+      }
+    // the state: S^T += V^T phi(K)
+#pragma unroll
+    for (int fb = 0; fb < NJ; ++fb)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const u32x4 av = tr_operand<D>(smem + L::V, 16 * ks, 32 * w, lane);
+        S[fb] = mfma(av, tr_operand<D>(smem + L::K, 16 * ks, 32 * fb, lane), S[fb]);
+        if (exact) S[fb] = mfma(av, tr_operand<D>(smem + L::KL, 16 * ks, 32 * fb, lane), S[fb]);
+      }
+    __syncthreads();   // every read of the old S tile and of h done
+    write_state_tile<D>(smem + L::SB, smem + L::SBL, S, w, g, n);
+    if (tid < D) {
+      float zs = 0.f, gs = 0.f;
+#pragma unroll 8
+      for (int s = 0; s < BCH; ++s) {
+        const int off = elem_off<D>(perm_pos(s), tid);
+        zs += lds_bf16(smem + L::K, off) + lds_bf16(smem + L::KL, off);
+        gs += (lds_bf16(smem + L::Q, off) + lds_bf16(smem + L::QL, off)) * F[L::HT + s];
+      }
+      F[L::Z + tid] += zs;
+      F[L::GZ + tid] += gs;
+    }
+    __syncthreads();   // state tile and z for the next chunk; tiles free
+  }
+
+  // G_seg (rows f, columns j) and gz_seg into the slot
+  float* dst = a.gslot + (bh * a.nseg + seg) * int64_t(D * D + D);
+#pragma unroll
+  for (int fb = 0; fb < NJ; ++fb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int f = 32 * fb + n, j = 32 * w + 8 * r + 4 * g;
+      *reinterpret_cast<f32x4*>(dst + f * D + j) =
+          f32x4{Gs[fb][4 * r], Gs[fb][4 * r + 1], Gs[fb][4 * r + 2], Gs[fb][4 * r + 3]};
+    }
+  if (tid < D) dst[D * D + tid] = F[L::GZ + tid];
+}
+
+// ------------------------------------------------------------ reverse scan
+
+// Per element of (G, gz) of one (b, h): the slot of segment u becomes the sum
+// of the slots after it (G at u's end); the total is dS0 (dz0).
+template <int D>
+__global__ __launch_bounds__(256) void bwd_rscan(float* gslot, int nseg, float* dS0, float* dz0) {
+  constexpr int E = D * D + D;
+  constexpr int PER = (E + 255) / 256;
+  const int64_t bh = blockIdx.x / PER;
+  const int e = (blockIdx.x % PER) * 256 + threadIdx.x;
+  if (e >= E) return;
+  float* base = gslot + bh * nseg * int64_t(E) + e;
+  float carry = 0.f;
+  for (int u = nseg - 1; u >= 0; --u) {
+    const float x = base[int64_t(u) * E];
+    base[int64_t(u) * E] = carry;
+    carry += x;
+  }
+  if (dS0) {
+    if (e < D * D) dS0[bh * D * D + e] = carry;
+    else dz0[bh * D + (e - D * D)] = carry;
+  }
+}
+
+// ------------------------------------------------------------------ pass B
+
+template <int D>
+__global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_b(const BwArgs a) {
+  using L = BL<D>;
+  constexpr int NJ = L::NJ;
+  __shared__ __align__(16) char smem[L::LDS];
+  float* F = reinterpret_cast<float*>(smem + L::F);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, n = lane & 31;
+  const int64_t bh = blockIdx.x / a.nseg;
+  const int seg = blockIdx.x % a.nseg;
+  const int T = a.T;
+  const int nchunks = (T + BCH - 1) / BCH;
+  const int c0 = seg * a.cps, c1 = min(c0 + a.cps, nchunks);
+
+  // G at the segment's end: transposed tiles (rows j of block w, columns f)
+  f32x16 G[NJ];
+  {
+    const float* src = a.gslot + (bh * a.nseg + seg) * int64_t(D * D + D);
+#pragma unroll
+    for (int fb = 0; fb < NJ; ++fb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int f = 32 * fb + n, j = 32 * w + 8 * (i >> 2) + 4 * g + (i & 3);
+        G[fb][i] = src[f * D + j];
+      }
+    if (tid < D) F[L::Z + tid] = src[D * D + tid];
+    write_state_tile<D>(smem + L::SB, smem + L::SBL, G, w, g, n);
+  }
+  __syncthreads();
+
+  Raw raw;
+  if (c0 < c1) load_raw<D>(a, bh, (c1 - 1) * BCH, tid, raw);
+  for (int c = c1 - 1; c >= c0; --c) {
+    const int t0 = c * BCH;
+    stage<D, false>(a, bh, t0, tid, raw, smem);
+    __syncthreads();   // tiles, h
+    if (c - 1 >= c0) load_raw<D>(a, bh, t0 - BCH, tid, raw);
+    const bool exact = t0 < kExactTokens;
+    const bool vs = t0 + n < T;
+
+    // scores A (rows t, columns s = n), mask t >= s
+    f32x16 at = zero16();
+#pragma unroll
+    for (int fs = 0; fs < D / 16; ++fs) {
+      const u32x4 aq = row_operand<D>(smem + L::Q, perm_pos(n), 2 * fs + g);
+      const u32x4 bk = row_operand<D>(smem + L::K, perm_pos(n), 2 * fs + g);
+      at = mfma(aq, bk, at);
+      if (exact) {
+        at = mfma(aq, row_operand<D>(smem + L::KL, perm_pos(n), 2 * fs + g), at);
+        at = mfma(row_operand<D>(smem + L::QL, perm_pos(n), 2 * fs + g), bk, at);
+      }
+    }
+    // B (rows t, columns s): g_t . v_s + h_t, mask t >= s
+    f32x16 bt = zero16();
+#pragma unroll
+    for (int js = 0; js < D / 16; ++js) {
+      const u32x4 bv = row_operand<D>(smem + L::V, perm_pos(n), 2 * js + g);
+      bt = mfma(row_operand<D>(smem + L::GH, perm_pos(n), 2 * js + g), bv, bt);
+      bt = mfma(row_operand<D>(smem + L::GL, perm_pos(n), 2 * js + g), bv, bt);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int t = 8 * (i >> 2) + 4 * g + (i & 3);
+      at[i] = t >= n ? at[i] : 0.f;
+      bt[i] = t >= n ? bt[i] + F[L::HT + t] : 0.f;
+    }
+    u32x4 ah[2], al[2], bh_[2], bl_[2];
+    split_acc(at, ah, al);
+    split_acc(bt, bh_, bl_);
+
+    // dv^T (rows j of block w, columns s): g^T A + G^T phi(k)
+    f32x16 dva = zero16();
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const u32x4 gh = tr_operand<D>(smem + L::GH, 16 * ks, 32 * w, lane);
+      const u32x4 gl = tr_operand<D>(smem + L::GL, 16 * ks, 32 * w, lane);
+      dva = mfma(gh, ah[ks], dva);
+      dva = mfma(gh, al[ks], dva);
+      dva = mfma(gl, ah[ks], dva);
+    }
+#pragma unroll
+    for (int fs = 0; fs < D / 16; ++fs) {
+      const u32x4 ag = tr_operand<D>(smem + L::SB, 16 * fs, 32 * w, lane);
+      const u32x4 bk = row_operand<D>(smem + L::K, perm_pos(n), 2 * fs + g);
+      dva = mfma(ag, bk, dva);
+      if (exact) {
+        dva = mfma(tr_operand<D>(smem + L::SBL, 16 * fs, 32 * w, lane), bk, dva);
+        dva = mfma(ag, row_operand<D>(smem + L::KL, perm_pos(n), 2 * fs + g), dva);
+      }
+    }
+    // dphi(k)^T (rows f of block w, columns s): phi(Q)^T B + G v + gz
+    f32x16 dka = zero16();
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const u32x4 aq = tr_operand<D>(smem + L::Q, 16 * ks, 32 * w, lane);
+      dka = mfma(aq, bh_[ks], dka);
+      dka = mfma(aq, bl_[ks], dka);
+      if (exact) dka = mfma(tr_operand<D>(smem + L::QL, 16 * ks, 32 * w, lane), bh_[ks], dka);
+    }
+    // G v and gz cancel in large part: G enters as high + low parts
+#pragma unroll
+    for (int js = 0; js < D / 16; ++js) {
+      const u32x4 bv = row_operand<D>(smem + L::V, perm_pos(n), 2 * js + g);
+      dka = mfma(row_operand<D>(smem + L::SB, 32 * w + n, 2 * js + g), bv, dka);
+      dka = mfma(row_operand<D>(smem + L::SBL, 32 * w + n, 2 * js + g), bv, dka);
+    }
+    if (vs) {
+      const int64_t row = (bh * T + t0 + n) * D + 32 * w + 4 * g;
+      const float* pdr = reinterpret_cast<const float*>(smem + L::PD) + n * L::FS + 32 * w + 4 * g;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        *reinterpret_cast<f32x4*>(a.dv + row + 8 * r) =
+            f32x4{dva[4 * r], dva[4 * r + 1], dva[4 * r + 2], dva[4 * r + 3]};
+        const f32x4 p4 = *reinterpret_cast<const f32x4*>(pdr + 8 * r);
+        const f32x4 z4 = *reinterpret_cast<const f32x4*>(F + L::Z + 32 * w + 4 * g + 8 * r);
+        f32x4 o4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o4[e] = (dka[4 * r + e] + z4[e]) * p4[e];
+        *reinterpret_cast<f32x4*>(a.dk + row + 8 * r) = o4;
+      }
+    }
+
+    // G^T += g^T phi(Q)
+#pragma unroll
+    for (int fb = 0; fb < NJ; ++fb)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const u32x4 ag = tr_operand<D>(smem + L::GH, 16 * ks, 32 * w, lane);
+        const u32x4 bq = tr_operand<D>(smem + L::Q, 16 * ks, 32 * fb, lane);
+        G[fb] = mfma(ag, bq, G[fb]);
+        if (exact) {
+          G[fb] = mfma(tr_operand<D>(smem + L::GL, 16 * ks, 32 * w, lane), bq, G[fb]);
+          G[fb] = mfma(ag, tr_operand<D>(smem + L::QL, 16 * ks, 32 * fb, lane), G[fb]);
+        }
+      }
+    __syncthreads();   // every read of the old G tile and of gz done
+    write_state_tile<D>(smem + L::SB, smem + L::SBL, G, w, g, n);
+    if (tid < D) {
+      float gs = 0.f;
+#pragma unroll 8
+      for (int t = 0; t < BCH; ++t) {
+        const int off = elem_off<D>(perm_pos(t), tid);
+        gs += (lds_bf16(smem + L::Q, off) + lds_bf16(smem + L::QL, off)) * F[L::HT + t];
+      }
+      F[L::Z + tid] += gs;
+    }
+    __syncthreads();
+  }
+}
+
+template <int D>
+hipError_t launch_d(const Problem& pb, const BwArgs& a, float* dS0, float* dz0, hipStream_t st) {
+  const unsigned nwg = unsigned(pb.BH() * a.nseg);
+  bwd_pass_a<D><<<dim3(nwg), dim3(64 * (D / 32)), 0, st>>>(a);
+  constexpr int PER = (D * D + D + 255) / 256;
+  bwd_rscan<D><<<dim3(unsigned(pb.BH() * PER)), dim3(256), 0, st>>>(a.gslot, a.nseg, dS0, dz0);
+  bwd_pass_b<D><<<dim3(nwg), dim3(64 * (D / 32)), 0, st>>>(a);
+  return hipGetLastError();
+}
+
+size_t r256(size_t b) { return (b + 255) / 256 * 256; }
+
+struct BwLayout {
+  size_t fwd, sinit, zinit, gslot, tok, total;
+};
+
+BwLayout layout_of(const Problem& pb) {
+  int cps, nseg, nsub, nslot;
+  mfma_split(pb, &cps, &nseg, &nsub, &nslot);
+  const size_t BH = size_t(pb.BH()), D = size_t(pb.dv);
+  BwLayout l;
+  size_t off = 0;
+  l.fwd = off;
+  off += r256(mfma_workspace_bytes(pb));
+  l.sinit = off;
+  off += r256(BH * D * D * 4);
+  l.zinit = off;
+  off += r256(BH * D * 4);
+  l.gslot = off;
+  off += r256(BH * nseg * (D * D + D) * 4);
+  l.tok = off;
+  off += r256(BH * size_t(pb.T) * 2 * 4);
+  l.total = off;
+  return l;
+}
+
+}  // namespace
+
+bool backward_chunked(const Problem& p) {
+  return p.path == 1 && p.dtype == LA_BF16 && p.phi == LA_PHI_ELU1 &&
+         p.decay_kind == LA_DECAY_NONE && !p.noncausal && p.T > 0 && p.dp == p.dv &&
+         (p.dv == 64 || p.dv == 128);
+}
+
+Problem backward_plan(const Problem& p) {
+  Problem pb = p;
+  if (p.chunk != BCH) {
+    pb.chunk = BCH;
+    pb.segments = mfma_default_segments(pb);
+  }
+  return pb;
+}
+
+size_t backward_chunked_workspace_bytes(const Problem& p) { return layout_of(backward_plan(p)).total; }
+
+hipError_t launch_backward_chunked(const Problem& p, const void* q, const void* k, const void* v,
+                                   const float* S0, const float* z0, const void* dout, float* dq,
+                                   float* dk, float* dv, float* dS0, float* dz0, void* ws,
+                                   hipStream_t stream) {
+  const Problem pb = backward_plan(p);
+  const BwLayout l = layout_of(pb);
+  char* base = static_cast<char*>(ws);
+  int cps, nseg, nsub, nslot;
+  mfma_split(pb, &cps, &nseg, &nsub, &nslot);
+  const int64_t D = pb.dv, E = D * D + D;
+  BwArgs a;
+  a.q = static_cast<const bf16_t*>(q);
+  a.k = static_cast<const bf16_t*>(k);
+  a.v = static_cast<const bf16_t*>(v);
+  a.dout = dout;
+  a.dout_f32 = pb.out_dtype == LA_F32 ? 1 : 0;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.gslot = reinterpret_cast<float*>(base + l.gslot);
+  a.tok = reinterpret_cast<float*>(base + l.tok);
+  a.T = pb.T;
+  a.cps = cps;
+  a.nseg = nseg;
+  a.norm = pb.norm;
+  a.eps = pb.eps;
+  if (nseg > 1) {
+    // the forward's stages 1 and 2 from a copy of the initial state (the scan
+    // writes the final state over it): every segment's start state
+    float* Si = reinterpret_cast<float*>(base + l.sinit);
+    float* zi = reinterpret_cast<float*>(base + l.zinit);
+    hipError_t e;
+    if (S0) {
+      e = hipMemcpyAsync(Si, S0, size_t(pb.BH()) * D * D * 4, hipMemcpyDeviceToDevice, stream);
+      if (e == hipSuccess)
+        e = hipMemcpyAsync(zi, z0, size_t(pb.BH()) * D * 4, hipMemcpyDeviceToDevice, stream);
+    } else {
+      e = launch_state_init(Si, pb.BH() * D * D, zi, pb.BH() * D, nullptr, 0, stream);
+    }
+    if (e != hipSuccess) return e;
+    void* fws = base + l.fwd;
+    e = launch_mfma_stage(pb, 1, q, k, v, Si, zi, nullptr, fws, stream);
+    if (e != hipSuccess) return e;
+    e = launch_mfma_stage(pb, 2, q, k, v, Si, zi, nullptr, fws, stream);
+    if (e != hipSuccess) return e;
+    const float* slots = reinterpret_cast<const float*>(fws);
+    a.S0 = slots;
+    a.z0 = slots + D * D;
+    a.s_bh = a.z_bh = int64_t(nslot) * E;
+    a.s_seg = int64_t(nsub) * E;
+  } else {
+    a.S0 = S0;
+    a.z0 = z0;
+    a.s_bh = D * D;
+    a.z_bh = D;
+    a.s_seg = 0;
+  }
+  if (D == 128) return launch_d<128>(pb, a, dS0, dz0, stream);
+  return launch_d<64>(pb, a, dS0, dz0, stream);
+}
+
+}  // namespace la

@@ -56,6 +56,17 @@ hipError_t launch_backward(const Problem& p, const void* q, const void* k, const
                            float* dk, float* dv, float* ddecay, float* dS0, float* dz0,
                            void* ws, hipStream_t stream);
 
+// Chunked gradients (la_backward_mfma.hip): bf16 inputs, elu+1, no decay,
+// d' = d_v in {64, 128}, T > 0.  The plan is the prefill's with 32-token
+// chunks.
+bool backward_chunked(const Problem& p);
+Problem backward_plan(const Problem& p);
+size_t backward_chunked_workspace_bytes(const Problem& p);
+hipError_t launch_backward_chunked(const Problem& p, const void* q, const void* k, const void* v,
+                                   const float* S0, const float* z0, const void* dout, float* dq,
+                                   float* dk, float* dv, float* dS0, float* dz0, void* ws,
+                                   hipStream_t stream);
+
 // Zero-fill of the state (m may be null).
 hipError_t launch_state_init(float* S, int64_t nS, float* z, int64_t nz, float* m, int64_t nm,
                              hipStream_t stream);
@@ -66,6 +77,11 @@ bool mfma_supported(const Problem& p);
 bool mfma_chunk_fits(int d, int chunk);
 int mfma_default_segments(const Problem& p);
 size_t mfma_workspace_bytes(const Problem& p);
+// The plan's chunk bookkeeping: chunks per segment, segments, stage-1
+// sub-segments per segment and workspace slots per (b, h); after stage 2,
+// slot nsub * s of (b, h) holds segment s's start state (S then z, D*D + D
+// floats per slot, at the start of the workspace).
+void mfma_split(const Problem& p, int* cps, int* nseg, int* nsub, int* nslot);
 hipError_t launch_mfma_stage(const Problem& p, int stage, const void* q, const void* k,
                              const void* v, float* S, float* z, void* out, void* ws,
                              hipStream_t stream);

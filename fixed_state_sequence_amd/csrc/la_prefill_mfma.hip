@@ -1146,6 +1146,14 @@ Split split_of(const Problem& p) {
 
 }  // namespace
 
+void mfma_split(const Problem& p, int* cps, int* nseg, int* nsub, int* nslot) {
+  const Split sp = split_of(p);
+  *cps = sp.cps;
+  *nseg = sp.nseg;
+  *nsub = sp.nsub;
+  *nslot = sp.nslot;
+}
+
 bool mfma_supported(const Problem& p) {
   // elu+1 with no decay, SSD decay or the RFA gate (bf16 or fp16 inputs);
   // identity features with the mLSTM gates, bf16 inputs only: the MFMA

@@ -199,7 +199,19 @@ def test_backward_checks():
     base = dict(T=300, d_h=64, d_v=64, dtype_code=_lib.LA_BF16)
     n = ctypes.c_size_t(0)
     assert status(L.la_prefill_backward_workspace_size(ctypes.byref(desc(**base)), ctypes.byref(n))) == "LA_OK"
+    # bf16, elu+1, no decay, d = 64: the chunked path.  Its workspace is the
+    # prefill's (32-token chunks, the default plan: 5 segments of 2 chunks,
+    # 10 stage-1 slots per head), a copy of the initial state, one gradient
+    # state per segment and two floats per token, each rounded up to 256 bytes
+    r = lambda b: (b + 255) // 256 * 256
+    BH, E = 8, 64 * 64 + 64
+    fwd = BH * 10 * E * 4 + 2 * r(BH * 10 * 4) + r(BH * 6 * 4)
+    assert n.value == r(fwd) + r(BH * 64 * 64 * 4) + r(BH * 64 * 4) + r(BH * 5 * E * 4) + r(BH * 300 * 8)
+    # fp32 inputs: the per-token kernel, B H T (d_v + 2) floats
+    d32 = desc(T=300, d_h=64, d_v=64, dtype_code=_lib.LA_F32)
+    assert status(L.la_prefill_backward_workspace_size(ctypes.byref(d32), ctypes.byref(n))) == "LA_OK"
     assert n.value == 8 * 300 * (64 + 2) * 4
+    assert status(L.la_prefill_backward_workspace_size(ctypes.byref(desc(**base)), ctypes.byref(n))) == "LA_OK"
     # not covered: RFF, the mLSTM gates, the non-causal form
     d = desc(T=16, d_h=64, d_v=64, dtype_code=_lib.LA_F32)
     d.phi, d.rff_D, d.rff_W = _lib.LA_PHI_RFF, 32, FAKE

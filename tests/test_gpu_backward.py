@@ -16,12 +16,12 @@ from conftest import rel_err, TOL, gpu_device
 pytestmark = pytest.mark.gpu
 
 
-def run(x, do, dev, phi, normalize, state=None, state_grad=True):
+def run(x, do, dev, phi, normalize, state=None, state_grad=True, segments=0):
     g = lambda t: None if t is None else t.to(dev)
     st = None if state is None else tuple(g(torch.as_tensor(s, dtype=torch.float32)) for s in state)
     out = la.prefill_backward(g(x.q), g(x.k), g(x.v), g(do), phi=phi, decay=g(x.decay),
                               gate=g(x.gate), state=st, normalize=normalize,
-                              state_grad=state_grad)
+                              state_grad=state_grad, segments=segments)
     torch.cuda.synchronize()
     return {k: v.cpu().double().numpy() for k, v in out.items()}
 
@@ -76,3 +76,42 @@ def test_backward_zero_state_equals_explicit_zero_state():
     b = run(x, do, dev, "elu1", True, state=(np.zeros((1, 3, 8, 4)), np.zeros((1, 3, 8))))
     for k in a:
         np.testing.assert_array_equal(a[k], b[k])
+
+
+# The chunked MFMA gradients (bf16, elu+1, no decay, d in {64, 128}): one,
+# the default and three segments of 32-token chunks; tails that leave a
+# chunk ragged; a sequence shorter than one chunk; every read-out form; dout
+# in bf16 and fp32; a carried-in state and its gradient.
+CHUNKED = [
+    # d, T, segments, normalize, dout fp32, with state
+    (64, 300, 0, True, False, False),
+    (128, 300, 0, True, False, True),
+    (128, 300, 1, True, True, True),
+    (128, 333, 3, True, False, False),
+    (64, 95, 3, False, False, True),
+    (128, 211, 0, "max1", False, True),
+    (64, 211, 1, "max1", True, False),
+    (128, 20, 0, True, False, True),
+    (64, 1, 0, True, True, True),
+    (128, 64, 2, False, True, False),
+]
+
+
+@pytest.mark.parametrize("d,T,segments,normalize,dout32,with_state", CHUNKED)
+def test_backward_chunked_vs_oracle(d, T, segments, normalize, dout32, with_state):
+    dev = gpu_device()
+    B, H = 1, 2
+    x = I.prefill_inputs(B, H, T, d, dtype="bf16", seed=T + d, scale=2.0 ** -0.5)
+    do = torch.randn(B, H, T, d, generator=torch.Generator().manual_seed(T))
+    if not dout32:
+        do = do.to(torch.bfloat16)
+    state = None
+    if with_state:
+        rng = np.random.default_rng(d)
+        state = (rng.standard_normal((B, H, d, d)) * 0.3, np.abs(rng.standard_normal((B, H, d))) * 3)
+    print(f"chunked backward: d={d} T={T} segments={segments} norm={normalize} "
+          f"dout32={dout32} state={with_state}", flush=True)
+    got = run(x, do, dev, "elu1", normalize, state=state, state_grad=True, segments=segments)
+    ref = O.prefill_gradients(x.q, x.k, x.v, do, S0=None if state is None else state[0],
+                              z0=None if state is None else state[1], normalize=normalize)
+    compare(got, ref, TOL["bf16"], (d, T, segments, normalize, dout32, with_state))
