@@ -38,8 +38,11 @@ Printed as one JSON line:
                two gate arrays;
   backward     la_prefill_backward (dq, dk, dv of L = sum <dout, out>) on the
                same long-context prefill, and on the elu+1 prefill shape
-               B=4 H=8 T=2048 d=64: one workgroup per sequence walks the
-               tokens forward then backward;
+               B=4 H=8 T=2048 d=64: the chunked path (segment start states
+               from the prefill's stages 1 and 2, a pass in token order for
+               dq, a reverse scan of the segments' gradient states, a pass
+               in reverse order for dk and dv); algorithmic bytes are q, k,
+               v, dout read once (bf16) and dq, dk, dv written once (fp32);
   cpu_baseline the fp64 oracle (the CPU reference the tests check against),
                on a bounded sample of the same prefill workload, one worker
                process per head.
@@ -231,8 +234,13 @@ def bench_backward(torch, la, I, B, H, T, d, reps):
     g = torch.Generator(device=dev)
     g.manual_seed(1)
     do = torch.randn(B, H, T, d, generator=g, device=dev).to(torch.bfloat16)
-    ws = None
-    la.prefill_backward(x.q, x.k, x.v, do)             # warm-up
+    desc = la.make_desc(B, H, T, d, d, la._lib.LA_BF16)
+    n = ctypes.c_size_t(0)
+    la._lib.check(la._lib.lib().la_prefill_backward_workspace_size(ctypes.byref(desc),
+                                                                   ctypes.byref(n)))
+    ws = torch.empty(max(int(n.value), 1), dtype=torch.uint8, device=dev)
+    for _ in range(3):                                 # warm-up
+        la.prefill_backward(x.q, x.k, x.v, do, workspace=ws)
     torch.cuda.synchronize()
     e0, e1 = _events(torch)
     e0.record()
@@ -374,8 +382,8 @@ def main(argv=None):
     pf_ml = bench_prefill(torch, la, I, a.steps, a.warmup, mlstm=True)
     ml_bytes = step_bytes + TH * 2 * 4 + 2 * B * H * 4     # + the two gates, the stabiliser
     print("[bench] backward", file=sys.stderr, flush=True)
-    bw_long = bench_backward(torch, la, I, B, H, T, d, 1)
-    bw_small = bench_backward(torch, la, I, 4, 8, 2048, 64, 5)
+    bw_long = bench_backward(torch, la, I, B, H, T, d, 20)
+    bw_small = bench_backward(torch, la, I, 4, 8, 2048, 64, 50)
     cp = hbm_copy(torch)
     dec = dec_big = None
     if not a.no_decode:
@@ -437,7 +445,8 @@ def main(argv=None):
             "stage3_GBs": (stage3_bytes + TH * 2 * 4) / (pf_ml["stage_ms"][2] * 1e-3) / 1e9},
         "backward": {
             "workload": "la_prefill_backward, elu+1, no decay, bf16 q, k, v, dout; fp32 dq, "
-                        "dk, dv; token-serial, one workgroup per sequence",
+                        "dk, dv; chunked: prefill stages 1-2, dq pass, reverse scan, dk/dv pass",
+            "algorithmic_bytes_per_token_head": 4 * 2 * d + 3 * 4 * d,
             "long_context": {"B": B, "H": H, "T": T, "d": d, "ms": bw_long["ms"],
                              "tokens_per_s": bw_long["tokens_per_s"],
                              "GBs": bw_long["GBs"],

@@ -31,16 +31,17 @@
 // other operand's token axis is read in the permuted order perm_pos (every
 // token tile is stored with its rows at perm_pos(token)).
 //
-// Precision.  The gradients of the first tokens are sums of few terms and
-// the largest of the sequence (they shrink about like 1/sqrt(t) without
-// decay), so a rounding error there is measured against a much smaller rms:
-// the chunks that start before token 256 take every product with both
-// operands as bf16 high + low parts (three MFMAs: hi hi, lo hi, hi lo).
-// Elsewhere the score tiles and g enter as high + low parts, and the states
-// S and G enter the read-out and the products whose terms cancel (S g + z h
-// and G v + gz, whose differences are sum_s phi(k_s) g.(v_s - o_t) and its
-// transpose) as high + low parts; phi(q), phi(k) and the other products
-// stay bf16, their rounding errors averaging out over the chunk.
+// Precision.  Every product takes both operands as bf16 high + low parts
+// (three MFMAs: hi hi, lo hi, hi lo; v is bf16 and exact), so each carries
+// about 2^-16 relative error.  Plain bf16 operands do not suffice here:
+// the read-out's error reaches h = -g.o, and the terms S g + z h (and
+// G v + gz) cancel down to sum_s phi(k_s) g.(v_s - o_t), amplifying it; the
+// states and the score sums are random-sign sums whose rounding error stays
+// near 2^-9 of their size instead of averaging out; and without decay the
+// gradients of the first tokens are the largest (about 1/sqrt(t)), so an
+// error measured against the rms of a long sequence is magnified (about
+// 90x at 102400 tokens).
+
 #include "la_internal.h"
 #include "la_mfma_common.h"
 
@@ -48,7 +49,6 @@ namespace la {
 namespace {
 
 constexpr int BCH = 32;            // chunk length
-constexpr int kExactTokens = 256;  // chunks starting before this split every operand
 
 template <int D>
 struct BL {
@@ -288,7 +288,6 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_a(const BwArgs a) {
     stage<D, true>(a, bh, t0, tid, raw, smem);
     __syncthreads();   // tiles, phi(q) . z
     if (c + 1 < c1) load_raw<D>(a, bh, t0 + BCH, tid, raw);   // next chunk, in flight meanwhile
-    const bool exact = t0 < kExactTokens;
     const bool vt = t0 + n < T;
 
     // scores P^T (rows s, columns t = n), causal mask, row sums
@@ -298,7 +297,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_a(const BwArgs a) {
       const u32x4 bq = row_operand<D>(smem + L::Q, perm_pos(n), 2 * ks + g);
       const u32x4 ak = row_operand<D>(smem + L::K, perm_pos(n), 2 * ks + g);
       sc = mfma(ak, bq, sc);
-      if (exact) {
+      {
         sc = mfma(row_operand<D>(smem + L::KL, perm_pos(n), 2 * ks + g), bq, sc);
         sc = mfma(ak, row_operand<D>(smem + L::QL, perm_pos(n), 2 * ks + g), sc);
       }
@@ -332,7 +331,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_a(const BwArgs a) {
       const u32x4 as = tr_operand<D>(smem + L::SB, 16 * fs, 32 * w, lane);
       nu = mfma(as, bq, nu);
       nu = mfma(tr_operand<D>(smem + L::SBL, 16 * fs, 32 * w, lane), bq, nu);
-      if (exact) nu = mfma(as, row_operand<D>(smem + L::QL, perm_pos(n), 2 * fs + g), nu);
+      nu = mfma(as, row_operand<D>(smem + L::QL, perm_pos(n), 2 * fs + g), nu);
     }
 
     // o = num r_t; g = dout r_t (bf16 high and low tiles); dout . o partials
@@ -393,7 +392,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_a(const BwArgs a) {
       const u32x4 ak = tr_operand<D>(smem + L::K, 16 * ks, 32 * w, lane);
       dqa = mfma(ak, bh_[ks], dqa);
       dqa = mfma(ak, bl_[ks], dqa);
-      if (exact) dqa = mfma(tr_operand<D>(smem + L::KL, 16 * ks, 32 * w, lane), bh_[ks], dqa);
+      dqa = mfma(tr_operand<D>(smem + L::KL, 16 * ks, 32 * w, lane), bh_[ks], dqa);
     }
     // S g and z h cancel in large part (their difference is
     // sum_s phi(k_s) g.(v_s - o_t)): S and g enter as high + low parts
@@ -427,7 +426,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_a(const BwArgs a) {
         const u32x4 ag = tr_operand<D>(smem + L::GH, 16 * ks, 32 * w, lane);
         const u32x4 bq = tr_operand<D>(smem + L::Q, 16 * ks, 32 * fb, lane);
         Gs[fb] = mfma(ag, bq, Gs[fb]);
-        if (exact) {
+        {
           Gs[fb] = mfma(tr_operand<D>(smem + L::GL, 16 * ks, 32 * w, lane), bq, Gs[fb]);
           Gs[fb] = mfma(ag, tr_operand<D>(smem + L::QL, 16 * ks, 32 * fb, lane), Gs[fb]);
         }
@@ -439,7 +438,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_a(const BwArgs a) {
       for (int ks = 0; ks < 2; ++ks) {
         const u32x4 av = tr_operand<D>(smem + L::V, 16 * ks, 32 * w, lane);
         S[fb] = mfma(av, tr_operand<D>(smem + L::K, 16 * ks, 32 * fb, lane), S[fb]);
-        if (exact) S[fb] = mfma(av, tr_operand<D>(smem + L::KL, 16 * ks, 32 * fb, lane), S[fb]);
+        S[fb] = mfma(av, tr_operand<D>(smem + L::KL, 16 * ks, 32 * fb, lane), S[fb]);
       }
     __syncthreads();   // every read of the old S tile and of h done
     write_state_tile<D>(smem + L::SB, smem + L::SBL, S, w, g, n);
@@ -532,7 +531,6 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_b(const BwArgs a) {
     stage<D, false>(a, bh, t0, tid, raw, smem);
     __syncthreads();   // tiles, h
     if (c - 1 >= c0) load_raw<D>(a, bh, t0 - BCH, tid, raw);
-    const bool exact = t0 < kExactTokens;
     const bool vs = t0 + n < T;
 
     // scores A (rows t, columns s = n), mask t >= s
@@ -542,7 +540,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_b(const BwArgs a) {
       const u32x4 aq = row_operand<D>(smem + L::Q, perm_pos(n), 2 * fs + g);
       const u32x4 bk = row_operand<D>(smem + L::K, perm_pos(n), 2 * fs + g);
       at = mfma(aq, bk, at);
-      if (exact) {
+      {
         at = mfma(aq, row_operand<D>(smem + L::KL, perm_pos(n), 2 * fs + g), at);
         at = mfma(row_operand<D>(smem + L::QL, perm_pos(n), 2 * fs + g), bk, at);
       }
@@ -580,7 +578,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_b(const BwArgs a) {
       const u32x4 ag = tr_operand<D>(smem + L::SB, 16 * fs, 32 * w, lane);
       const u32x4 bk = row_operand<D>(smem + L::K, perm_pos(n), 2 * fs + g);
       dva = mfma(ag, bk, dva);
-      if (exact) {
+      {
         dva = mfma(tr_operand<D>(smem + L::SBL, 16 * fs, 32 * w, lane), bk, dva);
         dva = mfma(ag, row_operand<D>(smem + L::KL, perm_pos(n), 2 * fs + g), dva);
       }
@@ -592,7 +590,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_b(const BwArgs a) {
       const u32x4 aq = tr_operand<D>(smem + L::Q, 16 * ks, 32 * w, lane);
       dka = mfma(aq, bh_[ks], dka);
       dka = mfma(aq, bl_[ks], dka);
-      if (exact) dka = mfma(tr_operand<D>(smem + L::QL, 16 * ks, 32 * w, lane), bh_[ks], dka);
+      dka = mfma(tr_operand<D>(smem + L::QL, 16 * ks, 32 * w, lane), bh_[ks], dka);
     }
     // G v and gz cancel in large part: G enters as high + low parts
 #pragma unroll
@@ -625,7 +623,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_b(const BwArgs a) {
         const u32x4 ag = tr_operand<D>(smem + L::GH, 16 * ks, 32 * w, lane);
         const u32x4 bq = tr_operand<D>(smem + L::Q, 16 * ks, 32 * fb, lane);
         G[fb] = mfma(ag, bq, G[fb]);
-        if (exact) {
+        {
           G[fb] = mfma(tr_operand<D>(smem + L::GL, 16 * ks, 32 * w, lane), bq, G[fb]);
           G[fb] = mfma(ag, tr_operand<D>(smem + L::QL, 16 * ks, 32 * fb, lane), G[fb]);
         }

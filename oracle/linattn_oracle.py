@@ -673,6 +673,74 @@ def prefill_gradients(q, k, v, dout, phi="elu1", decay=None, gate=None, eps=1e-6
     return res
 
 
+def prefill_gradients_recurrent(q, k, v, dout, phi="elu1", eps=1e-6, S0=None, z0=None,
+                                normalize=True):
+    """The same gradients as prefill_gradients for the form with no decay,
+    by reverse mode through the recurrence instead of the quadratic form
+    (O(T d' d_v) per head, for long sequences), in float64.
+
+    Forward over t ([lesson] Researcher level, Derivation: S_t = S_{t-1} +
+    phi(k_t) v_t^T, z_t likewise, o_t read from the state after token t):
+        D_t the read-out's divisor, g_t = dout_t / D_t, h_t its gradient
+        (-(dout_t . o_t) / D_t for the sum read-out),
+        dphi(q_t) = S_t g_t + z_t h_t.
+    Backward over t, with the gradient state G (d' x d_v) and gz (d'):
+        G += phi(q_t) g_t^T,  gz += phi(q_t) h_t   (every read-out at t' >= t)
+        dphi(k_t) = G v_t + gz,  dv_t = G^T phi(k_t).
+    The initial state reaches every S_t unchanged: dS0 = G, dz0 = gz after
+    the walk.  Returns a dict with dq, dk, dv, dS0, dz0.
+    """
+    fq_all, fk_all = features(q, phi), features(k, phi)
+    dphq, dphk = phi_derivative(q, phi), phi_derivative(k, phi)
+    v_all, do_all = _f64(v), _f64(dout)
+    lead = fq_all.shape[:-2]
+    T, dp = fq_all.shape[-2:]
+    dv_ = v_all.shape[-1]
+    res = {n: np.zeros(lead + shp) for n, shp in (("dq", (T, q.shape[-1])), ("dk", (T, k.shape[-1])),
+                                                  ("dv", (T, dv_)), ("dS0", (dp, dv_)), ("dz0", (dp,)))}
+    for idx in np.ndindex(*lead):
+        fq, fk, vv, do = fq_all[idx], fk_all[idx], v_all[idx], do_all[idx]
+        S = np.zeros((dp, dv_)) if S0 is None else _f64(S0)[idx].copy()
+        z = np.zeros(dp) if z0 is None else _f64(z0)[idx].copy()
+        g = np.empty((T, dv_))
+        h = np.empty(T)
+        dfq = np.empty((T, dp))
+        for t in range(T):
+            S += np.outer(fk[t], vv[t])
+            z += fk[t]
+            num = fq[t] @ S
+            den = fq[t] @ z
+            if normalize is True:
+                Dv = den + eps
+                g[t] = do[t] / Dv
+                h[t] = -(do[t] @ (num / Dv)) / Dv
+            elif normalize is False:
+                g[t] = do[t]
+                h[t] = 0.0
+            elif normalize == "max1":
+                Dv = max(abs(den), 1.0)
+                g[t] = do[t] / Dv
+                h[t] = -np.sign(den) * (do[t] @ (num / Dv)) / Dv if abs(den) > 1.0 else 0.0
+            else:
+                raise ValueError(f"unknown read-out {normalize!r}")
+            dfq[t] = S @ g[t] + z * h[t]
+        G = np.zeros((dp, dv_))
+        gz = np.zeros(dp)
+        dfk = np.empty((T, dp))
+        dvv = np.empty((T, dv_))
+        for t in range(T - 1, -1, -1):
+            G += np.outer(fq[t], g[t])
+            gz += fq[t] * h[t]
+            dfk[t] = G @ vv[t] + gz
+            dvv[t] = fk[t] @ G
+        res["dq"][idx] = dfq * dphq[idx]
+        res["dk"][idx] = dfk * dphk[idx]
+        res["dv"][idx] = dvv
+        res["dS0"][idx] = G
+        res["dz0"][idx] = gz
+    return res
+
+
 # --------------------------------------------------------------------------
 # Accounting the pages print
 # --------------------------------------------------------------------------

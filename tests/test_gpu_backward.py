@@ -115,3 +115,35 @@ def test_backward_chunked_vs_oracle(d, T, segments, normalize, dout32, with_stat
     ref = O.prefill_gradients(x.q, x.k, x.v, do, S0=None if state is None else state[0],
                               z0=None if state is None else state[1], normalize=normalize)
     compare(got, ref, TOL["bf16"], (d, T, segments, normalize, dout32, with_state))
+
+
+# The two workloads bench.py times the gradients on, at full size, in its
+# launch configuration (default plan, bf16 dout), against the oracle's
+# recurrent gradients (pinned to the quadratic form and to finite
+# differences): the elu+1 prefill shape, every sequence; the long-context
+# shape, two heads end to end (the gradients of the first tokens are the
+# largest there, about 1/sqrt(t), so the bar is met only with the early
+# chunks exact), and every head's initial-state gradient.
+
+def _workload_grads(name, seed=1):
+    dev = gpu_device()
+    x = I.workload_inputs(name, seed=0)
+    do = torch.randn(x.q.shape, generator=torch.Generator().manual_seed(seed)).to(torch.bfloat16)
+    got = run(x, do, dev, "elu1", True, state_grad=True)
+    return x, do, got
+
+
+def test_backward_elu_prefill_b4_h8_t2048_d64_full():
+    x, do, got = _workload_grads("elu_prefill_b4_h8_t2048_d64")
+    ref = O.prefill_gradients_recurrent(x.q, x.k, x.v, do)
+    compare(got, ref, TOL["bf16"], "elu prefill backward 4x8x2048x64")
+
+
+def test_backward_long_prefill_b1_h8_t102400_d128_two_heads():
+    x, do, got = _workload_grads("long_prefill_b1_h8_t102400_d128")
+    hs = [0, 5]
+    ref = O.prefill_gradients_recurrent(x.q[0, hs], x.k[0, hs], x.v[0, hs], do[0, hs])
+    compare({k: v[0, hs] for k, v in got.items()}, ref, TOL["bf16"],
+            "long prefill backward 1x8x102400x128, heads 0 and 5")
+    for k in got:
+        assert np.isfinite(got[k]).all(), k

@@ -127,3 +127,62 @@ def test_planted_mistakes_fail_finite_differences(mistake):
     ref = fd(lambda x: loss(x, k, v, do, "elu1", None, None, None, None, True), q)
     assert np.abs(_mutant(q, k, v, do, None, mistake) - ref).max() > 1e-4
     assert np.abs(_mutant(q, k, v, do, None, None) - ref).max() < 1e-7
+
+
+# ---------------------------------------------------------------------------
+# The recurrent gradients (reverse mode through the state, for long
+# sequences): finite differences directly, and the quadratic-form gradients
+# on the same inputs.
+
+@pytest.mark.parametrize("phi", ["elu1", "identity"])
+@pytest.mark.parametrize("normalize", [True, False, "max1"])
+def test_recurrent_gradients_match_finite_differences(phi, normalize):
+    q, k, v, do, S0, z0, _, _ = case(11)
+    if phi == "identity" and normalize is True:
+        q, k = np.abs(q), np.abs(k)
+    g = O.prefill_gradients_recurrent(q, k, v, do, phi=phi, S0=S0, z0=z0, normalize=normalize)
+    f = lambda **kw: loss(**{**dict(q=q, k=k, v=v, do=do, phi=phi, decay=None, gate=None,
+                                    S0=S0, z0=z0, normalize=normalize), **kw})
+    for name, x, fn in [("dq", q, lambda x: f(q=x)), ("dk", k, lambda x: f(k=x)),
+                        ("dv", v, lambda x: f(v=x)), ("dS0", S0, lambda x: f(S0=x)),
+                        ("dz0", z0, lambda x: f(z0=x))]:
+        ref = fd(fn, x)
+        assert np.abs(g[name] - ref).max() <= 1e-6 * max(1.0, np.abs(ref).max()), name
+
+
+@pytest.mark.parametrize("normalize", [True, False, "max1"])
+def test_recurrent_gradients_equal_quadratic_form(normalize):
+    rng = np.random.default_rng(5)
+    B, H, T, d, dv = 2, 2, 50, 5, 3
+    q, k = rng.standard_normal((B, H, T, d)), rng.standard_normal((B, H, T, d))
+    v, do = rng.standard_normal((B, H, T, dv)), rng.standard_normal((B, H, T, dv))
+    S0, z0 = rng.standard_normal((B, H, d, dv)) * 0.3, np.abs(rng.standard_normal((B, H, d)))
+    a = O.prefill_gradients(q, k, v, do, S0=S0, z0=z0, normalize=normalize)
+    b = O.prefill_gradients_recurrent(q, k, v, do, S0=S0, z0=z0, normalize=normalize)
+    for n in b:
+        assert np.abs(a[n] - b[n]).max() <= 1e-12 * np.abs(a[n]).max(), n
+
+
+def test_recurrent_gradients_planted_mistake_is_caught():
+    # the gradient state gathered after the read-out of token t instead of
+    # before it (G missing phi(q_t) g_t^T at t) must fail the quadratic form
+    rng = np.random.default_rng(6)
+    T, d = 20, 4
+    q, k, v, do = (rng.standard_normal((T, d)) for _ in range(4))
+    ref = O.prefill_gradients(q, k, v, do)
+    fq, fk = O.features(q), O.features(k)
+    g = O.prefill_gradients_recurrent(q, k, v, do)
+    # rebuild dk with the shifted accumulation from the oracle's own g, h
+    o, _, _ = O.causal_linear_attention(q, k, v)
+    z = np.cumsum(fk, axis=0)
+    Dv = (fq * z).sum(1) + 1e-6
+    gg = do / Dv[:, None]
+    h = -(do * o).sum(1) / Dv
+    G, gz, dfk = np.zeros((d, d)), np.zeros(d), np.zeros((T, d))
+    for t in range(T - 1, -1, -1):
+        dfk[t] = G @ v[t] + gz
+        G += np.outer(fq[t], gg[t])
+        gz += fq[t] * h[t]
+    wrong = dfk * O.phi_derivative(k)
+    assert np.abs(g["dk"] - ref["dk"]).max() < 1e-12 * np.abs(ref["dk"]).max()
+    assert np.abs(wrong - ref["dk"]).max() > 1e-3 * np.abs(ref["dk"]).max()
