@@ -128,7 +128,17 @@ def cpu_baseline(T_sample: int):
 # ------------------------------------------------------ HBM traffic (counters)
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "output_kernel_t102400_d128_hbm_traffic.txt")
-KERNEL_SOURCE = os.path.join(ROOT, "fixed_state_sequence_amd", "csrc", "la_prefill_mfma.hip")
+# the sources the output kernel's device code is compiled from
+KERNEL_SOURCES = [os.path.join(ROOT, "fixed_state_sequence_amd", "csrc", f)
+                  for f in ("la_prefill_mfma.hip", "la_mfma_common.h", "la_device.h")]
+
+
+def kernel_source_sha256():
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def profiled_traffic():
@@ -139,8 +149,7 @@ def profiled_traffic():
     try:
         with open(TRAFFIC_PROFILE) as f:
             lines = f.read().splitlines()
-        with open(KERNEL_SOURCE, "rb") as f:
-            src = hashlib.sha256(f.read()).hexdigest()
+        src = kernel_source_sha256()
     except OSError:
         return None
     kv = {}
