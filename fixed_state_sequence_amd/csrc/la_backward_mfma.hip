@@ -48,7 +48,7 @@
 namespace la {
 namespace {
 
-constexpr int BCH = 32;            // chunk length
+constexpr int BCH = 32;  // chunk length
 
 template <int D>
 struct BL {
@@ -68,15 +68,14 @@ struct BL {
   static constexpr int GL = GH + TILE;       // g, low part
   static constexpr int SB = GL + TILE;       // the carried state (S in A, G in B), bf16, rows = features
   static constexpr int SBL = SB + D * D * 2; // its low part
-  static constexpr int PD = SBL + D * D * 2; // fp32 [BCH][FS]: phi'(q) (A) or phi'(k) (B)
-  static constexpr int DO = PD + BCH * FS * 4;  // fp32 [BCH][FS]: dout (A)
+  static constexpr int DO = SBL + D * D * 2; // fp32 [BCH][FS]: dout (A)
   static constexpr int F = DO + BCH * FS * 4;   // fp32 scalars, offsets below (floats)
   static constexpr int Z = 0;                // z (A) or gz (B), carried
-  static constexpr int GZ = D;               // gz of the segment (A)
-  static constexpr int DI = 2 * D;           // phi(q_t) . z per token (A)
+  static constexpr int DI = D;               // phi(q_t) . z per token (A)
   static constexpr int HT = DI + BCH;        // h_t per token
   static constexpr int HP = HT + BCH;        // per-wave partial dout . o [NW][BCH]
-  static constexpr int NF = HP + NW * BCH;
+  static constexpr int ZP = HP + NW * BCH;   // per-wave increments of z (A) or gz (B) [NW][D]
+  static constexpr int NF = ZP + NW * D;
   static constexpr int LDS = F + NF * 4;
 };
 
@@ -105,16 +104,6 @@ __device__ __forceinline__ f32x16 zero16() {
 #pragma unroll
   for (int i = 0; i < 16; ++i) x[i] = 0.f;
   return x;
-}
-
-__device__ __forceinline__ float lds_bf16(const char* tile, int off) {
-  return __uint_as_float(uint32_t(*reinterpret_cast<const uint16_t*>(tile + off)) << 16);
-}
-
-// Element (token row `row` already permuted, feature f) of a token tile.
-template <int D>
-__device__ __forceinline__ int elem_off(int row, int f) {
-  return tile_off<D>(row, f >> 3) + ((f & 7) << 1);
 }
 
 // The accumulator rows 8 (i / 4) + 4 g + i % 4, as bf16 high and low parts:
@@ -150,6 +139,21 @@ __device__ __forceinline__ void write_state_tile(char* sb, char* sbl, const f32x
     }
 }
 
+// phi'(x) for the four features at byte offset `off` of token row (high
+// and low tiles): elu+1 has slope 1 above 0 and e^x = phi(x) below, so the
+// slope is min(phi(x), 1); high + low carry phi to about 2^-16.
+__device__ __forceinline__ f32x4 dphi4(const char* hi, const char* lo, int off) {
+  const u32x2 h = *reinterpret_cast<const u32x2*>(hi + off);
+  const u32x2 l = *reinterpret_cast<const u32x2*>(lo + off);
+  f32x4 r;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    r[2 * e] = fminf(__uint_as_float(h[e] << 16) + __uint_as_float(l[e] << 16), 1.f);
+    r[2 * e + 1] = fminf(__uint_as_float(h[e] & 0xffff0000u) + __uint_as_float(l[e] & 0xffff0000u), 1.f);
+  }
+  return r;
+}
+
 // Raw inputs of one chunk for this thread: rows r and r + 16, block b.
 struct Raw {
   u32x4 q[2], k[2], v[2];
@@ -183,40 +187,52 @@ __device__ __forceinline__ void load_raw(const BwArgs& a, int64_t bh, int t0, in
   }
 }
 
+// Sum of v[e] over the lanes of this wave that share lane % BPR (the rows
+// the wave stages), written by the first row's lanes to dst[8 b + e].
+template <int BPR>
+__device__ __forceinline__ void wave_rows_sum8(float (&v)[8], int lane, float* dst) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = group_sum<BPR>(v[e]);
+  if (lane < BPR) {
+    *reinterpret_cast<f32x4*>(dst + 8 * lane) = f32x4{v[0], v[1], v[2], v[3]};
+    *reinterpret_cast<f32x4*>(dst + 8 * lane + 4) = f32x4{v[4], v[5], v[6], v[7]};
+  }
+}
+
 // Stage one chunk into LDS: phi(q), phi(k) (high, low), v; pass A also the
-// fp32 dout, phi'(q) and phi(q_t) . z; pass B g = r_t dout (high, low),
-// phi'(k) and h_t.  Rows past the end of the sequence are zero.
+// fp32 dout, phi(q_t) . z and this wave's increments of z (sum phi(k_s));
+// pass B g = r_t dout (high, low), h_t and this wave's increments of gz
+// (sum phi(q_t) h_t).  Rows past the end of the sequence are zero.  fq
+// returns phi(q) of this thread's rows.
 template <int D, bool PASS_A>
 __device__ __forceinline__ void stage(const BwArgs& a, int64_t bh, int t0, int tid, const Raw& x,
-                                      char* smem) {
+                                      char* smem, float (&fq)[2][8]) {
   using L = BL<D>;
   float* F = reinterpret_cast<float*>(smem + L::F);
-  const int b = tid % L::BPR;
+  const int b = tid % L::BPR, lane = tid & 63, w = tid >> 6;
+  float inc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) inc[e] = 0.f;
 #pragma unroll
   for (int rr = 0; rr < 2; ++rr) {
     const int r = tid / L::BPR + 16 * rr;
     const bool valid = t0 + r < a.T;
     const int pr = perm_pos(r);
-    float xq[8], xk[8], fq[8], fk[8], pd[8];
+    float xq[8], xk[8], fk[8];
     unpack8(x.q[rr], xq, bf16_t{});
     unpack8(x.k[rr], xk, bf16_t{});
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      fq[e] = valid ? elu1_accurate(xq[e]) : 0.f;
-      fk[e] = valid ? elu1_accurate(xk[e]) : 0.f;
-      // elu+1 has slope 1 above 0 and e^x = phi(x) below
-      pd[e] = valid ? (PASS_A ? (xq[e] > 0.f ? 1.f : fq[e]) : (xk[e] > 0.f ? 1.f : fk[e])) : 0.f;
+      fq[rr][e] = valid ? elu1_fast(xq[e]) : 0.f;
+      fk[e] = valid ? elu1_fast(xk[e]) : 0.f;
     }
-    const u32x4 qh = pack8(fq);
+    const u32x4 qh = pack8(fq[rr]);
     blk_write<D>(smem + L::Q, pr, b, qh);
-    blk_write<D>(smem + L::QL, pr, b, low8(fq, qh));
+    blk_write<D>(smem + L::QL, pr, b, low8(fq[rr], qh));
     const u32x4 kh = pack8(fk);
     blk_write<D>(smem + L::K, pr, b, kh);
     blk_write<D>(smem + L::KL, pr, b, low8(fk, kh));
     blk_write<D>(smem + L::V, pr, b, valid ? x.v[rr] : u32x4{0u, 0u, 0u, 0u});
-    float* pdr = reinterpret_cast<float*>(smem + L::PD) + r * L::FS + 8 * b;
-    *reinterpret_cast<f32x4*>(pdr) = f32x4{pd[0], pd[1], pd[2], pd[3]};
-    *reinterpret_cast<f32x4*>(pdr + 4) = f32x4{pd[4], pd[5], pd[6], pd[7]};
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
     const f32x4 d0 = valid ? x.d[rr][0] : zero4, d1 = valid ? x.d[rr][1] : zero4;
     if constexpr (PASS_A) {
@@ -225,7 +241,10 @@ __device__ __forceinline__ void stage(const BwArgs& a, int64_t bh, int t0, int t
       *reinterpret_cast<f32x4*>(dor + 4) = d1;
       float part = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) part += fq[e] * F[L::Z + 8 * b + e];
+      for (int e = 0; e < 8; ++e) {
+        part += fq[rr][e] * F[L::Z + 8 * b + e];
+        inc[e] += fk[e];
+      }
       part = row_sum<L::BPR>(part);
       if (b == 0) F[L::DI + r] = part;
     } else {
@@ -241,8 +260,11 @@ __device__ __forceinline__ void stage(const BwArgs& a, int64_t bh, int t0, int t
       blk_write<D>(smem + L::GH, pr, b, gh);
       blk_write<D>(smem + L::GL, pr, b, low8(gv, gh));
       if (b == 0) F[L::HT + r] = ht;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) inc[e] += fq[rr][e] * ht;
     }
   }
+  wave_rows_sum8<L::BPR>(inc, lane, F + L::ZP + w * D);
 }
 
 // ------------------------------------------------------------------ pass A
@@ -273,40 +295,41 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_a(const BwArgs a) {
         S[fb][i] = Ss ? Ss[f * D + j] : 0.f;
       }
     }
-    if (tid < D) {
-      F[L::Z + tid] = a.z0 ? a.z0[bh * a.z_bh + int64_t(seg) * a.s_seg + tid] : 0.f;
-      F[L::GZ + tid] = 0.f;
-    }
+    if (tid < D) F[L::Z + tid] = a.z0 ? a.z0[bh * a.z_bh + int64_t(seg) * a.s_seg + tid] : 0.f;
     write_state_tile<D>(smem + L::SB, smem + L::SBL, S, w, g, n);
   }
   __syncthreads();
 
+  // this thread's share of gz_seg = sum phi(q_t) h_t (its rows, its 8 features)
+  float gzp[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) gzp[e] = 0.f;
   Raw raw;
   if (c0 < c1) load_raw<D>(a, bh, c0 * BCH, tid, raw);
   for (int c = c0; c < c1; ++c) {
     const int t0 = c * BCH;
-    stage<D, true>(a, bh, t0, tid, raw, smem);
-    __syncthreads();   // tiles, phi(q) . z
+    float fq[2][8];
+    stage<D, true>(a, bh, t0, tid, raw, smem, fq);
+    __syncthreads();   // tiles, phi(q) . z, z increments
     if (c + 1 < c1) load_raw<D>(a, bh, t0 + BCH, tid, raw);   // next chunk, in flight meanwhile
     const bool vt = t0 + n < T;
 
-    // scores P^T (rows s, columns t = n), causal mask, row sums
-    f32x16 sc = zero16();
+    // scores P^T (rows s, columns t = n), causal mask, row sums; the three
+    // hi/lo products in independent accumulators
+    f32x16 sc = zero16(), sc1 = zero16(), sc2 = zero16();
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
       const u32x4 bq = row_operand<D>(smem + L::Q, perm_pos(n), 2 * ks + g);
       const u32x4 ak = row_operand<D>(smem + L::K, perm_pos(n), 2 * ks + g);
       sc = mfma(ak, bq, sc);
-      {
-        sc = mfma(row_operand<D>(smem + L::KL, perm_pos(n), 2 * ks + g), bq, sc);
-        sc = mfma(ak, row_operand<D>(smem + L::QL, perm_pos(n), 2 * ks + g), sc);
-      }
+      sc1 = mfma(row_operand<D>(smem + L::KL, perm_pos(n), 2 * ks + g), bq, sc1);
+      sc2 = mfma(ak, row_operand<D>(smem + L::QL, perm_pos(n), 2 * ks + g), sc2);
     }
     float dsum = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int s = 8 * (i >> 2) + 4 * g + (i & 3);
-      sc[i] = s <= n ? sc[i] : 0.f;
+      sc[i] = s <= n ? sc[i] + sc1[i] + sc2[i] : 0.f;
       dsum += sc[i];
     }
     dsum = swap_sum32(dsum);
@@ -318,20 +341,20 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_a(const BwArgs a) {
     split_acc(sc, ph, pl);
 
     // numerator^T (rows j of block w, columns t): P V + phi(Q) S
-    f32x16 nu = zero16();
+    f32x16 nu = zero16(), nu1 = zero16(), nu2 = zero16();
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const u32x4 av = tr_operand<D>(smem + L::V, 16 * ks, 32 * w, lane);
       nu = mfma(av, ph[ks], nu);
-      nu = mfma(av, pl[ks], nu);
+      nu1 = mfma(av, pl[ks], nu1);
     }
 #pragma unroll
     for (int fs = 0; fs < D / 16; ++fs) {
       const u32x4 bq = row_operand<D>(smem + L::Q, perm_pos(n), 2 * fs + g);
       const u32x4 as = tr_operand<D>(smem + L::SB, 16 * fs, 32 * w, lane);
       nu = mfma(as, bq, nu);
-      nu = mfma(tr_operand<D>(smem + L::SBL, 16 * fs, 32 * w, lane), bq, nu);
-      nu = mfma(as, row_operand<D>(smem + L::QL, perm_pos(n), 2 * fs + g), nu);
+      nu1 = mfma(tr_operand<D>(smem + L::SBL, 16 * fs, 32 * w, lane), bq, nu1);
+      nu2 = mfma(as, row_operand<D>(smem + L::QL, perm_pos(n), 2 * fs + g), nu2);
     }
 
     // o = num r_t; g = dout r_t (bf16 high and low tiles); dout . o partials
@@ -343,7 +366,8 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_a(const BwArgs a) {
       float gv[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        hp += d4[e] * (nu[4 * r + e] * rt);
+        const int i = 4 * r + e;
+        hp += d4[e] * ((nu[i] + nu1[i] + nu2[i]) * rt);
         gv[e] = vt ? d4[e] * rt : 0.f;
       }
       uint32_t h0, h1, l0, l1;
@@ -370,50 +394,53 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_a(const BwArgs a) {
     }
 
     // B^T (rows s, columns t): g_t . v_s + h_t, causal mask
-    f32x16 bs = zero16();
+    f32x16 bs = zero16(), bs1 = zero16();
 #pragma unroll
     for (int js = 0; js < D / 16; ++js) {
       const u32x4 av = row_operand<D>(smem + L::V, perm_pos(n), 2 * js + g);
       bs = mfma(av, row_operand<D>(smem + L::GH, perm_pos(n), 2 * js + g), bs);
-      bs = mfma(av, row_operand<D>(smem + L::GL, perm_pos(n), 2 * js + g), bs);
+      bs1 = mfma(av, row_operand<D>(smem + L::GL, perm_pos(n), 2 * js + g), bs1);
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int s = 8 * (i >> 2) + 4 * g + (i & 3);
-      bs[i] = s <= n ? bs[i] + h : 0.f;
+      bs[i] = s <= n ? bs[i] + bs1[i] + h : 0.f;
     }
     u32x4 bh_[2], bl_[2];
     split_acc(bs, bh_, bl_);
 
-    // dphi(q)^T (rows f of block w, columns t): phi(K)^T B + S g + z h
-    f32x16 dqa = zero16();
+    // dphi(q)^T (rows f of block w, columns t): phi(K)^T B + S g + z h.
+    // S g and z h cancel in large part (their difference is
+    // sum_s phi(k_s) g.(v_s - o_t)).
+    f32x16 dq0 = zero16(), dq1 = zero16(), dq2 = zero16();
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const u32x4 ak = tr_operand<D>(smem + L::K, 16 * ks, 32 * w, lane);
-      dqa = mfma(ak, bh_[ks], dqa);
-      dqa = mfma(ak, bl_[ks], dqa);
-      dqa = mfma(tr_operand<D>(smem + L::KL, 16 * ks, 32 * w, lane), bh_[ks], dqa);
+      dq0 = mfma(ak, bh_[ks], dq0);
+      dq1 = mfma(ak, bl_[ks], dq1);
+      dq2 = mfma(tr_operand<D>(smem + L::KL, 16 * ks, 32 * w, lane), bh_[ks], dq2);
     }
-    // S g and z h cancel in large part (their difference is
-    // sum_s phi(k_s) g.(v_s - o_t)): S and g enter as high + low parts
 #pragma unroll
     for (int js = 0; js < D / 16; ++js) {
       const u32x4 sh = row_operand<D>(smem + L::SB, 32 * w + n, 2 * js + g);
       const u32x4 gh = row_operand<D>(smem + L::GH, perm_pos(n), 2 * js + g);
-      dqa = mfma(sh, gh, dqa);
-      dqa = mfma(row_operand<D>(smem + L::SBL, 32 * w + n, 2 * js + g), gh, dqa);
-      dqa = mfma(sh, row_operand<D>(smem + L::GL, perm_pos(n), 2 * js + g), dqa);
+      dq0 = mfma(sh, gh, dq0);
+      dq1 = mfma(row_operand<D>(smem + L::SBL, 32 * w + n, 2 * js + g), gh, dq1);
+      dq2 = mfma(sh, row_operand<D>(smem + L::GL, perm_pos(n), 2 * js + g), dq2);
     }
     if (vt) {
-      const float* pdr = reinterpret_cast<const float*>(smem + L::PD) + n * L::FS + 32 * w + 4 * g;
       float* dst = a.dq + (bh * T + t0 + n) * D + 32 * w + 4 * g;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const f32x4 p4 = *reinterpret_cast<const f32x4*>(pdr + 8 * r);
+        const int off = tile_off<D>(perm_pos(n), 4 * w + r) + 8 * g;
+        const f32x4 p4 = dphi4(smem + L::Q, smem + L::QL, off);
         const f32x4 z4 = *reinterpret_cast<const f32x4*>(F + L::Z + 32 * w + 4 * g + 8 * r);
         f32x4 o4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o4[e] = (dqa[4 * r + e] + z4[e] * h) * p4[e];
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * r + e;
+          o4[e] = (dq0[i] + dq1[i] + dq2[i] + z4[e] * h) * p4[e];
+        }
         *reinterpret_cast<f32x4*>(dst + 8 * r) = o4;
       }
     }
@@ -426,10 +453,8 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_a(const BwArgs a) {
         const u32x4 ag = tr_operand<D>(smem + L::GH, 16 * ks, 32 * w, lane);
         const u32x4 bq = tr_operand<D>(smem + L::Q, 16 * ks, 32 * fb, lane);
         Gs[fb] = mfma(ag, bq, Gs[fb]);
-        {
-          Gs[fb] = mfma(tr_operand<D>(smem + L::GL, 16 * ks, 32 * w, lane), bq, Gs[fb]);
-          Gs[fb] = mfma(ag, tr_operand<D>(smem + L::QL, 16 * ks, 32 * fb, lane), Gs[fb]);
-        }
+        Gs[fb] = mfma(tr_operand<D>(smem + L::GL, 16 * ks, 32 * w, lane), bq, Gs[fb]);
+        Gs[fb] = mfma(ag, tr_operand<D>(smem + L::QL, 16 * ks, 32 * fb, lane), Gs[fb]);
       }
     // the state: S^T += V^T phi(K)
 #pragma unroll
@@ -440,18 +465,19 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_a(const BwArgs a) {
         S[fb] = mfma(av, tr_operand<D>(smem + L::K, 16 * ks, 32 * fb, lane), S[fb]);
         S[fb] = mfma(av, tr_operand<D>(smem + L::KL, 16 * ks, 32 * fb, lane), S[fb]);
       }
-    __syncthreads();   // every read of the old S tile and of h done
+    __syncthreads();   // every read of the old S tile done; h visible
     write_state_tile<D>(smem + L::SB, smem + L::SBL, S, w, g, n);
     if (tid < D) {
-      float zs = 0.f, gs = 0.f;
-#pragma unroll 8
-      for (int s = 0; s < BCH; ++s) {
-        const int off = elem_off<D>(perm_pos(s), tid);
-        zs += lds_bf16(smem + L::K, off) + lds_bf16(smem + L::KL, off);
-        gs += (lds_bf16(smem + L::Q, off) + lds_bf16(smem + L::QL, off)) * F[L::HT + s];
-      }
+      float zs = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < L::NW; ++ww) zs += F[L::ZP + ww * D + tid];
       F[L::Z + tid] += zs;
-      F[L::GZ + tid] += gs;
+    }
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr) {
+      const float ht = F[L::HT + tid / L::BPR + 16 * rr];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) gzp[e] += fq[rr][e] * ht;
     }
     __syncthreads();   // state tile and z for the next chunk; tiles free
   }
@@ -466,7 +492,14 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_a(const BwArgs a) {
       *reinterpret_cast<f32x4*>(dst + f * D + j) =
           f32x4{Gs[fb][4 * r], Gs[fb][4 * r + 1], Gs[fb][4 * r + 2], Gs[fb][4 * r + 3]};
     }
-  if (tid < D) dst[D * D + tid] = F[L::GZ + tid];
+  wave_rows_sum8<L::BPR>(gzp, lane, F + L::ZP + w * D);
+  __syncthreads();
+  if (tid < D) {
+    float s = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < L::NW; ++ww) s += F[L::ZP + ww * D + tid];
+    dst[D * D + tid] = s;
+  }
 }
 
 // ------------------------------------------------------------ reverse scan
@@ -528,89 +561,88 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_b(const BwArgs a) {
   if (c0 < c1) load_raw<D>(a, bh, (c1 - 1) * BCH, tid, raw);
   for (int c = c1 - 1; c >= c0; --c) {
     const int t0 = c * BCH;
-    stage<D, false>(a, bh, t0, tid, raw, smem);
-    __syncthreads();   // tiles, h
+    float fq[2][8];
+    stage<D, false>(a, bh, t0, tid, raw, smem, fq);
+    __syncthreads();   // tiles, h, gz increments
     if (c - 1 >= c0) load_raw<D>(a, bh, t0 - BCH, tid, raw);
     const bool vs = t0 + n < T;
 
     // scores A (rows t, columns s = n), mask t >= s
-    f32x16 at = zero16();
+    f32x16 at = zero16(), at1 = zero16(), at2 = zero16();
 #pragma unroll
     for (int fs = 0; fs < D / 16; ++fs) {
       const u32x4 aq = row_operand<D>(smem + L::Q, perm_pos(n), 2 * fs + g);
       const u32x4 bk = row_operand<D>(smem + L::K, perm_pos(n), 2 * fs + g);
       at = mfma(aq, bk, at);
-      {
-        at = mfma(aq, row_operand<D>(smem + L::KL, perm_pos(n), 2 * fs + g), at);
-        at = mfma(row_operand<D>(smem + L::QL, perm_pos(n), 2 * fs + g), bk, at);
-      }
+      at1 = mfma(aq, row_operand<D>(smem + L::KL, perm_pos(n), 2 * fs + g), at1);
+      at2 = mfma(row_operand<D>(smem + L::QL, perm_pos(n), 2 * fs + g), bk, at2);
     }
     // B (rows t, columns s): g_t . v_s + h_t, mask t >= s
-    f32x16 bt = zero16();
+    f32x16 bt = zero16(), bt1 = zero16();
 #pragma unroll
     for (int js = 0; js < D / 16; ++js) {
       const u32x4 bv = row_operand<D>(smem + L::V, perm_pos(n), 2 * js + g);
       bt = mfma(row_operand<D>(smem + L::GH, perm_pos(n), 2 * js + g), bv, bt);
-      bt = mfma(row_operand<D>(smem + L::GL, perm_pos(n), 2 * js + g), bv, bt);
+      bt1 = mfma(row_operand<D>(smem + L::GL, perm_pos(n), 2 * js + g), bv, bt1);
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int t = 8 * (i >> 2) + 4 * g + (i & 3);
-      at[i] = t >= n ? at[i] : 0.f;
-      bt[i] = t >= n ? bt[i] + F[L::HT + t] : 0.f;
+      at[i] = t >= n ? at[i] + at1[i] + at2[i] : 0.f;
+      bt[i] = t >= n ? bt[i] + bt1[i] + F[L::HT + t] : 0.f;
     }
     u32x4 ah[2], al[2], bh_[2], bl_[2];
     split_acc(at, ah, al);
     split_acc(bt, bh_, bl_);
 
     // dv^T (rows j of block w, columns s): g^T A + G^T phi(k)
-    f32x16 dva = zero16();
+    f32x16 dv0 = zero16(), dv1 = zero16(), dv2 = zero16();
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const u32x4 gh = tr_operand<D>(smem + L::GH, 16 * ks, 32 * w, lane);
-      const u32x4 gl = tr_operand<D>(smem + L::GL, 16 * ks, 32 * w, lane);
-      dva = mfma(gh, ah[ks], dva);
-      dva = mfma(gh, al[ks], dva);
-      dva = mfma(gl, ah[ks], dva);
+      dv0 = mfma(gh, ah[ks], dv0);
+      dv1 = mfma(gh, al[ks], dv1);
+      dv2 = mfma(tr_operand<D>(smem + L::GL, 16 * ks, 32 * w, lane), ah[ks], dv2);
     }
 #pragma unroll
     for (int fs = 0; fs < D / 16; ++fs) {
       const u32x4 ag = tr_operand<D>(smem + L::SB, 16 * fs, 32 * w, lane);
       const u32x4 bk = row_operand<D>(smem + L::K, perm_pos(n), 2 * fs + g);
-      dva = mfma(ag, bk, dva);
-      {
-        dva = mfma(tr_operand<D>(smem + L::SBL, 16 * fs, 32 * w, lane), bk, dva);
-        dva = mfma(ag, row_operand<D>(smem + L::KL, perm_pos(n), 2 * fs + g), dva);
-      }
+      dv0 = mfma(ag, bk, dv0);
+      dv1 = mfma(tr_operand<D>(smem + L::SBL, 16 * fs, 32 * w, lane), bk, dv1);
+      dv2 = mfma(ag, row_operand<D>(smem + L::KL, perm_pos(n), 2 * fs + g), dv2);
     }
-    // dphi(k)^T (rows f of block w, columns s): phi(Q)^T B + G v + gz
-    f32x16 dka = zero16();
+    // dphi(k)^T (rows f of block w, columns s): phi(Q)^T B + G v + gz; G v
+    // and gz cancel in large part
+    f32x16 dk0 = zero16(), dk1 = zero16(), dk2 = zero16();
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const u32x4 aq = tr_operand<D>(smem + L::Q, 16 * ks, 32 * w, lane);
-      dka = mfma(aq, bh_[ks], dka);
-      dka = mfma(aq, bl_[ks], dka);
-      dka = mfma(tr_operand<D>(smem + L::QL, 16 * ks, 32 * w, lane), bh_[ks], dka);
+      dk0 = mfma(aq, bh_[ks], dk0);
+      dk1 = mfma(aq, bl_[ks], dk1);
+      dk2 = mfma(tr_operand<D>(smem + L::QL, 16 * ks, 32 * w, lane), bh_[ks], dk2);
     }
-    // G v and gz cancel in large part: G enters as high + low parts
 #pragma unroll
     for (int js = 0; js < D / 16; ++js) {
       const u32x4 bv = row_operand<D>(smem + L::V, perm_pos(n), 2 * js + g);
-      dka = mfma(row_operand<D>(smem + L::SB, 32 * w + n, 2 * js + g), bv, dka);
-      dka = mfma(row_operand<D>(smem + L::SBL, 32 * w + n, 2 * js + g), bv, dka);
+      dk0 = mfma(row_operand<D>(smem + L::SB, 32 * w + n, 2 * js + g), bv, dk0);
+      dk1 = mfma(row_operand<D>(smem + L::SBL, 32 * w + n, 2 * js + g), bv, dk1);
     }
     if (vs) {
       const int64_t row = (bh * T + t0 + n) * D + 32 * w + 4 * g;
-      const float* pdr = reinterpret_cast<const float*>(smem + L::PD) + n * L::FS + 32 * w + 4 * g;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        *reinterpret_cast<f32x4*>(a.dv + row + 8 * r) =
-            f32x4{dva[4 * r], dva[4 * r + 1], dva[4 * r + 2], dva[4 * r + 3]};
-        const f32x4 p4 = *reinterpret_cast<const f32x4*>(pdr + 8 * r);
+        f32x4 v4, o4;
+        const int off = tile_off<D>(perm_pos(n), 4 * w + r) + 8 * g;
+        const f32x4 p4 = dphi4(smem + L::K, smem + L::KL, off);
         const f32x4 z4 = *reinterpret_cast<const f32x4*>(F + L::Z + 32 * w + 4 * g + 8 * r);
-        f32x4 o4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o4[e] = (dka[4 * r + e] + z4[e]) * p4[e];
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * r + e;
+          v4[e] = dv0[i] + dv1[i] + dv2[i];
+          o4[e] = (dk0[i] + dk1[i] + dk2[i] + z4[e]) * p4[e];
+        }
+        *reinterpret_cast<f32x4*>(a.dv + row + 8 * r) = v4;
         *reinterpret_cast<f32x4*>(a.dk + row + 8 * r) = o4;
       }
     }
@@ -623,21 +655,16 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_b(const BwArgs a) {
         const u32x4 ag = tr_operand<D>(smem + L::GH, 16 * ks, 32 * w, lane);
         const u32x4 bq = tr_operand<D>(smem + L::Q, 16 * ks, 32 * fb, lane);
         G[fb] = mfma(ag, bq, G[fb]);
-        {
-          G[fb] = mfma(tr_operand<D>(smem + L::GL, 16 * ks, 32 * w, lane), bq, G[fb]);
-          G[fb] = mfma(ag, tr_operand<D>(smem + L::QL, 16 * ks, 32 * fb, lane), G[fb]);
-        }
+        G[fb] = mfma(tr_operand<D>(smem + L::GL, 16 * ks, 32 * w, lane), bq, G[fb]);
+        G[fb] = mfma(ag, tr_operand<D>(smem + L::QL, 16 * ks, 32 * fb, lane), G[fb]);
       }
     __syncthreads();   // every read of the old G tile and of gz done
     write_state_tile<D>(smem + L::SB, smem + L::SBL, G, w, g, n);
     if (tid < D) {
-      float gs = 0.f;
-#pragma unroll 8
-      for (int t = 0; t < BCH; ++t) {
-        const int off = elem_off<D>(perm_pos(t), tid);
-        gs += (lds_bf16(smem + L::Q, off) + lds_bf16(smem + L::QL, off)) * F[L::HT + t];
-      }
-      F[L::Z + tid] += gs;
+      float s = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < L::NW; ++ww) s += F[L::ZP + ww * D + tid];
+      F[L::Z + tid] += s;
     }
     __syncthreads();
   }
