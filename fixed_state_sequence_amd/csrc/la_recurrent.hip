@@ -251,18 +251,30 @@ hipError_t launch_recurrent(const Problem& p, const void* q, const void* k, cons
 // ---------------------------------------------------------------- state init
 
 namespace {
+// Zero n floats at p: 16-byte stores over the 16-byte-aligned body, scalar
+// stores for the tail (p itself is 4-byte aligned at least).
+__device__ __forceinline__ void zero_range(float* p, int64_t n, int64_t i0, int64_t stride) {
+  const int64_t head = p ? min(int64_t((16 - (reinterpret_cast<uintptr_t>(p) & 15)) & 15) / 4, n) : 0;
+  const int64_t n4 = (n - head) / 4;
+  float4* q = reinterpret_cast<float4*>(p + head);
+  for (int64_t i = i0; i < n4; i += stride) q[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int64_t i = i0; i < head; i += stride) p[i] = 0.f;
+  for (int64_t i = head + 4 * n4 + i0; i < n; i += stride) p[i] = 0.f;
+}
+
 __global__ void fill_zero_kernel(float* S, int64_t nS, float* z, int64_t nz, float* m,
                                  int64_t nm) {
   const int64_t stride = int64_t(gridDim.x) * blockDim.x;
-  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < nS; i += stride) S[i] = 0.f;
-  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < nz; i += stride) z[i] = 0.f;
-  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < nm; i += stride) m[i] = 0.f;
+  const int64_t i0 = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  zero_range(S, nS, i0, stride);
+  zero_range(z, nz, i0, stride);
+  zero_range(m, nm, i0, stride);
 }
 }  // namespace
 
 hipError_t launch_state_init(float* S, int64_t nS, float* z, int64_t nz, float* m, int64_t nm,
                              hipStream_t stream) {
-  int64_t blocks = (nS + 255) / 256;
+  int64_t blocks = (nS / 4 + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   if (blocks < 1) blocks = 1;
   fill_zero_kernel<<<dim3(unsigned(blocks)), dim3(256), 0, stream>>>(S, nS, z, nz, m, nm);
