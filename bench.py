@@ -38,7 +38,8 @@ Printed as one JSON line:
                two gate arrays;
   backward     la_prefill_backward (dq, dk, dv of L = sum <dout, out>) on the
                same long-context prefill, and on the elu+1 prefill shape
-               B=4 H=8 T=2048 d=64: the chunked path (segment start states
+               B=4 H=8 T=2048 d=64, and on the SSD-decay shape B=2 H=16
+               T=8192 d=128 with its decay: the chunked path (segment start states
                from the prefill's stages 1 and 2, a pass in token order for
                dq, a reverse scan of the segments' gradient states, a pass
                in reverse order for dk and dv); algorithmic bytes are q, k,
@@ -236,25 +237,27 @@ def bench_prefill(torch, la, I, steps, warmup, normalize=True, stages=True, caus
                 rep_median_ms=per[len(per) // 2], rep_min_ms=per[0])
 
 
-def bench_backward(torch, la, I, B, H, T, d, reps):
-    """ms per la_prefill_backward call (elu+1, no decay, bf16 inputs and dout)."""
+def bench_backward(torch, la, I, B, H, T, d, reps, decay=None, scale=PF["scale"]):
+    """ms per la_prefill_backward call (elu+1, bf16 inputs and dout; no decay,
+    or the SSD decay a = sigmoid(N(3, 1)))."""
     dev = torch.device("cuda:0")
-    x = I.prefill_inputs(B, H, T, d, dtype="bf16", seed=0, scale=PF["scale"], device=dev)
+    x = I.prefill_inputs(B, H, T, d, dtype="bf16", seed=0, scale=scale, device=dev,
+                         decay=decay)
     g = torch.Generator(device=dev)
     g.manual_seed(1)
     do = torch.randn(B, H, T, d, generator=g, device=dev).to(torch.bfloat16)
-    desc = la.make_desc(B, H, T, d, d, la._lib.LA_BF16)
+    desc = la.make_desc(B, H, T, d, d, la._lib.LA_BF16, decay=x.decay)
     n = ctypes.c_size_t(0)
     la._lib.check(la._lib.lib().la_prefill_backward_workspace_size(ctypes.byref(desc),
                                                                    ctypes.byref(n)))
     ws = torch.empty(max(int(n.value), 1), dtype=torch.uint8, device=dev)
     for _ in range(3):                                 # warm-up
-        la.prefill_backward(x.q, x.k, x.v, do, workspace=ws)
+        la.prefill_backward(x.q, x.k, x.v, do, decay=x.decay, workspace=ws)
     torch.cuda.synchronize()
     e0, e1 = _events(torch)
     e0.record()
     for _ in range(reps):
-        la.prefill_backward(x.q, x.k, x.v, do, workspace=ws)
+        la.prefill_backward(x.q, x.k, x.v, do, decay=x.decay, workspace=ws)
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
@@ -393,6 +396,7 @@ def main(argv=None):
     print("[bench] backward", file=sys.stderr, flush=True)
     bw_long = bench_backward(torch, la, I, B, H, T, d, 20)
     bw_small = bench_backward(torch, la, I, 4, 8, 2048, 64, 50)
+    bw_ssd = bench_backward(torch, la, I, 2, 16, 8192, 128, 20, decay="ssd", scale=1.0)
     cp = hbm_copy(torch)
     dec = dec_big = None
     if not a.no_decode:
@@ -453,8 +457,9 @@ def main(argv=None):
             "hbm_frac": ml_bytes / (pf_ml["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "stage3_GBs": (stage3_bytes + TH * 2 * 4) / (pf_ml["stage_ms"][2] * 1e-3) / 1e9},
         "backward": {
-            "workload": "la_prefill_backward, elu+1, no decay, bf16 q, k, v, dout; fp32 dq, "
-                        "dk, dv; chunked: prefill stages 1-2, dq pass, reverse scan, dk/dv pass",
+            "workload": "la_prefill_backward, elu+1, bf16 q, k, v, dout; fp32 dq, dk, dv (and "
+                        "dL/da with the SSD decay); chunked: prefill stages 1-2, dq pass, reverse "
+                        "scan, dk/dv pass (with a decay, a suffix-sum pass for dL/da)",
             "algorithmic_bytes_per_token_head": 4 * 2 * d + 3 * 4 * d,
             "long_context": {"B": B, "H": H, "T": T, "d": d, "ms": bw_long["ms"],
                              "tokens_per_s": bw_long["tokens_per_s"],
@@ -462,7 +467,10 @@ def main(argv=None):
                              "hbm_frac": bw_long["GBs"] / HBM_PEAK_GBS},
             "elu_prefill_shape": {"B": 4, "H": 8, "T": 2048, "d": 64, "ms": bw_small["ms"],
                                   "tokens_per_s": bw_small["tokens_per_s"],
-                                  "GBs": bw_small["GBs"]}},
+                                  "GBs": bw_small["GBs"]},
+            "ssd_prefill_shape": {"B": 2, "H": 16, "T": 8192, "d": 128, "decay": "ssd",
+                                  "ms": bw_ssd["ms"], "tokens_per_s": bw_ssd["tokens_per_s"],
+                                  "GBs": bw_ssd["GBs"]}},
     }
     if dec is not None:
         res["decode"] = {

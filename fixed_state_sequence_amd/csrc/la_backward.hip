@@ -357,7 +357,8 @@ hipError_t launch_backward(const Problem& p, const void* q, const void* k, const
                            float* dk, float* dv, float* ddecay, float* dS0, float* dz0,
                            void* ws, hipStream_t stream) {
   if (backward_chunked(p))
-    return launch_backward_chunked(p, q, k, v, S0, z0, dout, dq, dk, dv, dS0, dz0, ws, stream);
+    return launch_backward_chunked(p, q, k, v, S0, z0, dout, dq, dk, dv, ddecay, dS0, dz0, ws,
+                                   stream);
   BwdArgs a;
   a.q = q; a.k = k; a.v = v; a.dout = dout; a.S0 = S0; a.z0 = z0; a.decay = p.decay;
   a.dq = dq; a.dk = dk; a.dv = dv; a.ddecay = ddecay; a.dS0 = dS0; a.dz0 = dz0;

@@ -1,27 +1,43 @@
 // Gradients of the causal prefill by chunks on CDNA4 MFMA (gfx950), for
-// bf16 inputs with elu+1 features, no decay and d' = d_v = D in {64, 128}.
+// bf16 inputs with elu+1 features, d' = d_v = D in {64, 128}, and no decay,
+// the SSD decay or the RFA gate.
 //
 // With L = sum_t <dout_t, o_t>, o_t = num_t r_t (r_t = 1 / (den_t + eps), or
-// 1 / max(|den_t|, 1), or 1), the recurrence S_t = S_{t-1} + phi(k_t) v_t^T
-// (llm-arch-kb "Linear Attention", section 2) gives, with g_t = r_t dout_t and
-// h_t the gradient of the divisor (-r_t dout_t . o_t for the sum read-out):
-//   dphi(q_t) = sum_{s<=t} (g_t . v_s + h_t) phi(k_s)     (= S_t g_t + z_t h_t)
-//   dphi(k_s) = sum_{t>=s} (g_t . v_s + h_t) phi(q_t)     (= G_s v_s + gz_s)
-//   dv_s      = sum_{t>=s} (phi(q_t) . phi(k_s)) g_t      (= G_s^T phi(k_s))
-// with the gradient state G_s = sum_{t>=s} phi(q_t) g_t^T, gz_s likewise
-// with h_t.  Both sums have the masked-quadratic form of the forward pass, so
-// they take its chunked bracketing (efficient-attention lesson "Linear
-// attention", "Implementation reality": chunks, quadratic inside, a scan
-// across): inside a chunk the C x C score tiles, across chunks the states.
+// 1 / max(|den_t|, 1), or 1), the recurrence S_t = alpha_t S_{t-1} +
+// beta_t phi(k_t) v_t^T (llm-arch-kb "Linear Attention", section 2; wikillm
+// "Linear attention", Implementation sketch, SSD and RFA: (alpha, beta) =
+// (1, 1), (a_t, 1) or (g_t, 1 - g_t)) gives, with the weights
+// w_ts = beta_s prod_{r=s+1..t} alpha_r, g_t = r_t dout_t and h_t the
+// gradient of the divisor (-r_t dout_t . o_t for the sum read-out):
+//   dphi(q_t) = sum_{s<=t} w_ts (g_t . v_s + h_t) phi(k_s)   (= S_t g_t + z_t h_t)
+//   dphi(k_s) = sum_{t>=s} w_ts (g_t . v_s + h_t) phi(q_t)   (= beta_s (G_s v_s + gz_s))
+//   dv_s      = sum_{t>=s} w_ts (phi(q_t) . phi(k_s)) g_t    (= beta_s G_s^T phi(k_s))
+// with the gradient state G_s = sum_{t>=s} (prod_{r=s+1..t} alpha_r)
+// phi(q_t) g_t^T, gz_s likewise with h_t.  Both sums have the
+// masked-quadratic form of the forward pass, so they take its chunked
+// bracketing (efficient-attention lesson "Linear attention", "Implementation
+// reality": chunks, quadratic inside, a scan across): inside a chunk the
+// C x C score tiles, across chunks the states.  The decay enters through the
+// within-chunk log-prefix l_t = sum_{r<=t in the chunk} log alpha_r: the
+// weight of (t, s) inside a chunk is beta_s e^{l_t - l_s}, a state carried
+// into the chunk reaches token t with e^{l_t}, and key s reaches the chunk's
+// end with e^{l_last - l_s}, every factor at most 1.  The decay values'
+// gradient goes through log alpha: dL/dl_t = <phi(q_t), dphi(q_t)> -
+// <phi(k_t), dphi(k_t)>, and dL/dlog alpha_r is its suffix sum over t >= r;
+// beta's own gradient is <phi(k_s), dphi(k_s)> / beta_s.
 //
 // Schedule (one workgroup per segment of whole 32-token chunks):
 //   forward stages 1 and 2 of the prefill: the start state of every segment;
 //   pass A (chunks in order): the forward read-out again (r_t, h_t, g_t),
-//     dq, and the segment's share of the gradient state, G_seg = sum over
-//     its tokens of phi(q_t) g_t^T (and gz_seg);
+//     dq, <phi(q_t), dphi(q_t)>, and the segment's share of the gradient
+//     state, G_seg = sum over its tokens of (decay from the segment's start)
+//     phi(q_t) g_t^T (and gz_seg), with the segment's total log-decay;
 //   reverse scan over the segments: G at every segment's end, and
-//     dS0 = G_0, dz0 = gz_0 (the initial state enters every S_t unchanged);
-//   pass B (chunks in reverse): dk and dv from the carried G.
+//     dS0 = G before the first token, dz0 likewise;
+//   pass B (chunks in reverse): dk, dv and <phi(k_s), dphi(k_s)> / beta_s
+//     from the carried G;
+//   with a decay, a suffix sum per sequence turns the per-token terms into
+//   the decay or gate gradient.
 //
 // MFMA layout (v_mfma_f32_32x32x16_bf16, g = lane / 32, n = lane % 32): an
 // operand register holds k-values 8 g .. 8 g + 7 of row n; the accumulator
@@ -41,16 +57,16 @@
 // gradients of the first tokens are the largest (about 1/sqrt(t)), so an
 // error measured against the rms of a long sequence is magnified (about
 // 90x at 102400 tokens).
-
 #include "la_internal.h"
 #include "la_mfma_common.h"
 
 namespace la {
 namespace {
 
-constexpr int BCH = 32;  // chunk length
+constexpr int BCH = 32;                // chunk length
+constexpr float kLogFloorB = -80.0f;   // log alpha floor: alpha = 0 stays finite
 
-template <int D>
+template <int D, int DECAY>
 struct BL {
   static constexpr int NW = D / 32;          // waves; wave w owns 32-wide block w
   static constexpr int NT = 64 * NW;
@@ -69,13 +85,21 @@ struct BL {
   static constexpr int SB = GL + TILE;       // the carried state (S in A, G in B), bf16, rows = features
   static constexpr int SBL = SB + D * D * 2; // its low part
   static constexpr int DO = SBL + D * D * 2; // fp32 [BCH][FS]: dout (A)
-  static constexpr int F = DO + BCH * FS * 4;   // fp32 scalars, offsets below (floats)
+  // with a decay, a weighted tile pair (high, low): pass A e^{L + l_t} g_t
+  // for the gradient-state fold, then w_s phi(k_s) for the state fold; pass
+  // B e^{l_t} g_t
+  static constexpr int WH = DO + BCH * FS * 4;
+  static constexpr int WL = WH + TILE;
+  static constexpr int F = DECAY ? WL + TILE : WH;   // fp32 scalars, offsets below (floats)
   static constexpr int Z = 0;                // z (A) or gz (B), carried
   static constexpr int DI = D;               // phi(q_t) . z per token (A)
   static constexpr int HT = DI + BCH;        // h_t per token
   static constexpr int HP = HT + BCH;        // per-wave partial dout . o [NW][BCH]
   static constexpr int ZP = HP + NW * BCH;   // per-wave increments of z (A) or gz (B) [NW][D]
-  static constexpr int NF = ZP + NW * D;
+  static constexpr int LAM = ZP + NW * D;    // within-chunk log-prefix l_t [BCH]
+  static constexpr int BET = LAM + BCH;      // beta_t [BCH]
+  static constexpr int QP = BET + BCH;       // per-wave partial <phi, dphi> [NW][BCH]
+  static constexpr int NF = QP + NW * BCH;
   static constexpr int LDS = F + NF * 4;
 };
 
@@ -84,6 +108,7 @@ struct BwArgs {
   const bf16_t* k;
   const bf16_t* v;
   const void* dout;
+  const float* decay;   // [BH, T] alpha (SSD) or the gate g (RFA); null without decay
   int dout_f32;
   // start state of (b, h) and segment s at S0 + bh * s_bh + s * s_seg (z at
   // z0 + bh * z_bh + s * s_seg); null: zero
@@ -94,7 +119,10 @@ struct BwArgs {
   float* dk;
   float* dv;
   float* gslot;  // [BH, nseg, D*D + D]: G_seg (pass A), then G at the segment's end
+  float* lgam;   // [BH, nseg]: the segment's total log-decay (pass A, with a decay)
   float* tok;    // [BH, T, 2]: r_t and h_t
+  float* qd;     // [BH, T]: <phi(q_t), dphi(q_t)> (pass A, with a decay)
+  float* kd;     // [BH, T]: <phi(k_t), dphi(k_t)> / beta_t (pass B, with a decay)
   int T, cps, nseg, norm;
   float eps;
 };
@@ -139,30 +167,43 @@ __device__ __forceinline__ void write_state_tile(char* sb, char* sbl, const f32x
     }
 }
 
-// phi'(x) for the four features at byte offset `off` of token row (high
-// and low tiles): elu+1 has slope 1 above 0 and e^x = phi(x) below, so the
-// slope is min(phi(x), 1); high + low carry phi to about 2^-16.
-__device__ __forceinline__ f32x4 dphi4(const char* hi, const char* lo, int off) {
+// Four features at byte offset `off` of a token row of a high/low tile pair,
+// as fp32 (high + low carry phi to about 2^-16).
+__device__ __forceinline__ f32x4 hilo4(const char* hi, const char* lo, int off) {
   const u32x2 h = *reinterpret_cast<const u32x2*>(hi + off);
   const u32x2 l = *reinterpret_cast<const u32x2*>(lo + off);
   f32x4 r;
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
-    r[2 * e] = fminf(__uint_as_float(h[e] << 16) + __uint_as_float(l[e] << 16), 1.f);
-    r[2 * e + 1] = fminf(__uint_as_float(h[e] & 0xffff0000u) + __uint_as_float(l[e] & 0xffff0000u), 1.f);
+    r[2 * e] = __uint_as_float(h[e] << 16) + __uint_as_float(l[e] << 16);
+    r[2 * e + 1] = __uint_as_float(h[e] & 0xffff0000u) + __uint_as_float(l[e] & 0xffff0000u);
   }
   return r;
 }
 
-// Raw inputs of one chunk for this thread: rows r and r + 16, block b.
+// Features 8 b .. 8 b + 7 of tile row `row` (already permuted) of a
+// high/low tile pair, as fp32.
+template <int D>
+__device__ __forceinline__ void hilo8(const char* hi, const char* lo, int row, int b, float (&x)[8]) {
+  const int off = tile_off<D>(row, b);
+  float h[8], l[8];
+  unpack8(*reinterpret_cast<const u32x4*>(hi + off), h, bf16_t{});
+  unpack8(*reinterpret_cast<const u32x4*>(lo + off), l, bf16_t{});
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = h[e] + l[e];
+}
+
+// Raw inputs of one chunk for this thread: rows r and r + 16, block b; and
+// the decay value of token lane % 32.
 struct Raw {
   u32x4 q[2], k[2], v[2];
   f32x4 d[2][2];   // dout as fp32
+  float al;
 };
 
-template <int D>
+template <int D, int DECAY>
 __device__ __forceinline__ void load_raw(const BwArgs& a, int64_t bh, int t0, int tid, Raw& x) {
-  using L = BL<D>;
+  using L = BL<D, DECAY>;
   const int b = tid % L::BPR;
   const int64_t T = a.T;
 #pragma unroll
@@ -185,6 +226,9 @@ __device__ __forceinline__ void load_raw(const BwArgs& a, int64_t bh, int t0, in
       x.d[rr][1] = f32x4{f[4], f[5], f[6], f[7]};
     }
   }
+  x.al = 1.f;
+  if constexpr (DECAY != 0)
+    x.al = a.decay[bh * T + min(int64_t(t0 + (tid & 31)), T - 1)];
 }
 
 // Sum of v[e] over the lanes of this wave that share lane % BPR (the rows
@@ -199,17 +243,50 @@ __device__ __forceinline__ void wave_rows_sum8(float (&v)[8], int lane, float* d
   }
 }
 
+// Decay of one chunk, computed by every wave (no barrier needed): lane l
+// gets the inclusive log-prefix of token l % 32 in lam and its beta in bet,
+// the chunk total in tot.  Tokens past the end have alpha = 1, beta = 0.
+template <int DECAY>
+__device__ __forceinline__ void chunk_decay(const Raw& x, int t0, int T, int lane, float& lam,
+                                            float& bet, float& tot) {
+  const bool valid = t0 + (lane & 31) < T;
+  float la = 0.f;
+  bet = 0.f;
+  if (valid) {
+    la = fmaxf(__logf(x.al), kLogFloorB);
+    bet = DECAY == 2 ? 1.f - x.al : 1.f;
+  }
+  lam = la;
+#pragma unroll
+  for (int off = 1; off < 32; off <<= 1) {
+    const float y = __shfl_up(lam, off, 32);
+    if ((lane & 31) >= off) lam += y;
+  }
+  tot = __shfl(lam, 31, 32);
+}
+
 // Stage one chunk into LDS: phi(q), phi(k) (high, low), v; pass A also the
-// fp32 dout, phi(q_t) . z and this wave's increments of z (sum phi(k_s));
-// pass B g = r_t dout (high, low), h_t and this wave's increments of gz
-// (sum phi(q_t) h_t).  Rows past the end of the sequence are zero.  fq
-// returns phi(q) of this thread's rows.
-template <int D, bool PASS_A>
+// fp32 dout, phi(q_t) . z and this wave's increments of z (sum w_s phi(k_s));
+// pass B g = r_t dout (high, low; with a decay also e^{l_t} g), h_t and this
+// wave's increments of gz (sum e^{l_t} phi(q_t) h_t).  Rows past the end of
+// the sequence are zero.  lam, bet, tot return the chunk's decay (see
+// chunk_decay; 0, 1, 0 without).
+template <int D, int DECAY, bool PASS_A>
 __device__ __forceinline__ void stage(const BwArgs& a, int64_t bh, int t0, int tid, const Raw& x,
-                                      char* smem, float (&fq)[2][8]) {
-  using L = BL<D>;
+                                      char* smem, float& lam, float& bet, float& tot) {
+  using L = BL<D, DECAY>;
   float* F = reinterpret_cast<float*>(smem + L::F);
   const int b = tid % L::BPR, lane = tid & 63, w = tid >> 6;
+  lam = 0.f;
+  bet = 1.f;
+  tot = 0.f;
+  if constexpr (DECAY != 0) {
+    chunk_decay<DECAY>(x, t0, a.T, lane, lam, bet, tot);
+    if (w == 0 && lane < BCH) {
+      F[L::LAM + lane] = lam;
+      F[L::BET + lane] = bet;
+    }
+  }
   float inc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) inc[e] = 0.f;
@@ -218,17 +295,22 @@ __device__ __forceinline__ void stage(const BwArgs& a, int64_t bh, int t0, int t
     const int r = tid / L::BPR + 16 * rr;
     const bool valid = t0 + r < a.T;
     const int pr = perm_pos(r);
-    float xq[8], xk[8], fk[8];
-    unpack8(x.q[rr], xq, bf16_t{});
-    unpack8(x.k[rr], xk, bf16_t{});
+    float lr = 0.f, br = 1.f;   // this row's log-prefix and beta
+    if constexpr (DECAY != 0) {
+      lr = __shfl(lam, r);
+      br = __shfl(bet, r);
+    }
+    float fq[8], fk[8];
+    unpack8(x.q[rr], fq, bf16_t{});
+    unpack8(x.k[rr], fk, bf16_t{});
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      fq[rr][e] = valid ? elu1_fast(xq[e]) : 0.f;
-      fk[e] = valid ? elu1_fast(xk[e]) : 0.f;
+      fq[e] = valid ? elu1_fast(fq[e]) : 0.f;
+      fk[e] = valid ? elu1_fast(fk[e]) : 0.f;
     }
-    const u32x4 qh = pack8(fq[rr]);
+    const u32x4 qh = pack8(fq);
     blk_write<D>(smem + L::Q, pr, b, qh);
-    blk_write<D>(smem + L::QL, pr, b, low8(fq[rr], qh));
+    blk_write<D>(smem + L::QL, pr, b, low8(fq, qh));
     const u32x4 kh = pack8(fk);
     blk_write<D>(smem + L::K, pr, b, kh);
     blk_write<D>(smem + L::KL, pr, b, low8(fk, kh));
@@ -239,11 +321,12 @@ __device__ __forceinline__ void stage(const BwArgs& a, int64_t bh, int t0, int t
       float* dor = reinterpret_cast<float*>(smem + L::DO) + r * L::FS + 8 * b;
       *reinterpret_cast<f32x4*>(dor) = d0;
       *reinterpret_cast<f32x4*>(dor + 4) = d1;
+      const float wk = DECAY ? br * __expf(tot - lr) : 1.f;   // key weight to the chunk's end
       float part = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        part += fq[rr][e] * F[L::Z + 8 * b + e];
-        inc[e] += fk[e];
+        part += fq[e] * F[L::Z + 8 * b + e];
+        inc[e] += wk * fk[e];
       }
       part = row_sum<L::BPR>(part);
       if (b == 0) F[L::DI + r] = part;
@@ -259,9 +342,17 @@ __device__ __forceinline__ void stage(const BwArgs& a, int64_t bh, int t0, int t
       const u32x4 gh = pack8(gv);
       blk_write<D>(smem + L::GH, pr, b, gh);
       blk_write<D>(smem + L::GL, pr, b, low8(gv, gh));
+      const float wq = DECAY ? __expf(lr) : 1.f;   // query weight from the chunk's start
+      if constexpr (DECAY != 0) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) gv[e] *= wq;
+        const u32x4 wh = pack8(gv);
+        blk_write<D>(smem + L::WH, pr, b, wh);
+        blk_write<D>(smem + L::WL, pr, b, low8(gv, wh));
+      }
       if (b == 0) F[L::HT + r] = ht;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) inc[e] += fq[rr][e] * ht;
+      for (int e = 0; e < 8; ++e) inc[e] += wq * fq[e] * ht;
     }
   }
   wave_rows_sum8<L::BPR>(inc, lane, F + L::ZP + w * D);
@@ -269,9 +360,9 @@ __device__ __forceinline__ void stage(const BwArgs& a, int64_t bh, int t0, int t
 
 // ------------------------------------------------------------------ pass A
 
-template <int D>
+template <int D, int DECAY>
 __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_a(const BwArgs a) {
-  using L = BL<D>;
+  using L = BL<D, DECAY>;
   constexpr int NJ = L::NJ;
   __shared__ __align__(16) char smem[L::LDS];
   float* F = reinterpret_cast<float*>(smem + L::F);
@@ -300,21 +391,32 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_a(const BwArgs a) {
   }
   __syncthreads();
 
-  // this thread's share of gz_seg = sum phi(q_t) h_t (its rows, its 8 features)
+  // this thread's share of gz_seg = sum (decay from the segment's start)
+  // phi(q_t) h_t (its rows, its 8 features)
   float gzp[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) gzp[e] = 0.f;
+  float Lseg = 0.f;   // log-decay from the segment's start to the current chunk's start
   Raw raw;
-  if (c0 < c1) load_raw<D>(a, bh, c0 * BCH, tid, raw);
+  if (c0 < c1) load_raw<D, DECAY>(a, bh, c0 * BCH, tid, raw);
   for (int c = c0; c < c1; ++c) {
     const int t0 = c * BCH;
-    float fq[2][8];
-    stage<D, true>(a, bh, t0, tid, raw, smem, fq);
-    __syncthreads();   // tiles, phi(q) . z, z increments
-    if (c + 1 < c1) load_raw<D>(a, bh, t0 + BCH, tid, raw);   // next chunk, in flight meanwhile
+    float lam, bet, tot;
+    stage<D, DECAY, true>(a, bh, t0, tid, raw, smem, lam, bet, tot);
+    __syncthreads();   // tiles, phi(q) . z, z increments, decay
+    if (c + 1 < c1) load_raw<D, DECAY>(a, bh, t0 + BCH, tid, raw);   // next chunk, in flight meanwhile
     const bool vt = t0 + n < T;
+    const float eq = DECAY ? __expf(lam) : 1.f;   // e^{l_t}, t = n (lam is token n's)
 
-    // scores P^T (rows s, columns t = n), causal mask, row sums; the three
+    // causal weight of (t = n, s = row of accumulator element i):
+    // beta_s e^{l_t - l_s} for s <= t (recomputed where used: fewer live
+    // registers)
+    auto weight = [&](int i) {
+      const int s = 8 * (i >> 2) + 4 * g + (i & 3);
+      return s <= n ? (DECAY ? F[L::BET + s] * __expf(lam - F[L::LAM + s]) : 1.f) : 0.f;
+    };
+
+    // scores P^T (rows s, columns t = n), weighted, row sums; the three
     // hi/lo products in independent accumulators
     f32x16 sc = zero16(), sc1 = zero16(), sc2 = zero16();
 #pragma unroll
@@ -328,26 +430,19 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_a(const BwArgs a) {
     float dsum = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int s = 8 * (i >> 2) + 4 * g + (i & 3);
-      sc[i] = s <= n ? sc[i] + sc1[i] + sc2[i] : 0.f;
+      sc[i] = (sc[i] + sc1[i] + sc2[i]) * weight(i);
       dsum += sc[i];
     }
     dsum = swap_sum32(dsum);
-    const float den = dsum + F[L::DI + n];
+    const float den = dsum + eq * F[L::DI + n];
     const float rt = a.norm == LA_NORM_NONE ? 1.f
                      : a.norm == LA_NORM_MAX1 ? 1.f / fmaxf(fabsf(den), 1.f)
                                               : 1.f / (den + a.eps);
     u32x4 ph[2], pl[2];
     split_acc(sc, ph, pl);
 
-    // numerator^T (rows j of block w, columns t): P V + phi(Q) S
+    // numerator^T (rows j of block w, columns t): e^{l_t} phi(Q) S + P V
     f32x16 nu = zero16(), nu1 = zero16(), nu2 = zero16();
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const u32x4 av = tr_operand<D>(smem + L::V, 16 * ks, 32 * w, lane);
-      nu = mfma(av, ph[ks], nu);
-      nu1 = mfma(av, pl[ks], nu1);
-    }
 #pragma unroll
     for (int fs = 0; fs < D / 16; ++fs) {
       const u32x4 bq = row_operand<D>(smem + L::Q, perm_pos(n), 2 * fs + g);
@@ -356,9 +451,22 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_a(const BwArgs a) {
       nu1 = mfma(tr_operand<D>(smem + L::SBL, 16 * fs, 32 * w, lane), bq, nu1);
       nu2 = mfma(as, row_operand<D>(smem + L::QL, perm_pos(n), 2 * fs + g), nu2);
     }
+    if constexpr (DECAY != 0) {
+      nu *= eq;
+      nu1 *= eq;
+      nu2 *= eq;
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const u32x4 av = tr_operand<D>(smem + L::V, 16 * ks, 32 * w, lane);
+      nu = mfma(av, ph[ks], nu);
+      nu1 = mfma(av, pl[ks], nu1);
+    }
 
-    // o = num r_t; g = dout r_t (bf16 high and low tiles); dout . o partials
+    // o = num r_t; g = dout r_t (bf16 high and low tiles; with a decay also
+    // e^{Lseg + l_t} g for the gradient-state fold); dout . o partials
     float hp = 0.f;
+    const float wg = DECAY ? __expf(Lseg + lam) : 1.f;
     const float* dor = reinterpret_cast<const float*>(smem + L::DO) + n * L::FS + 32 * w + 4 * g;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -376,6 +484,12 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_a(const BwArgs a) {
       const int off = tile_off<D>(perm_pos(n), 4 * w + r) + 8 * g;
       *reinterpret_cast<u32x2*>(smem + L::GH + off) = u32x2{h0, h1};
       *reinterpret_cast<u32x2*>(smem + L::GL + off) = u32x2{l0, l1};
+      if constexpr (DECAY != 0) {
+        split_bf16(gv[0] * wg, gv[1] * wg, h0, l0);
+        split_bf16(gv[2] * wg, gv[3] * wg, h1, l1);
+        *reinterpret_cast<u32x2*>(smem + L::WH + off) = u32x2{h0, h1};
+        *reinterpret_cast<u32x2*>(smem + L::WL + off) = u32x2{l0, l1};
+      }
     }
     hp = swap_sum32(hp);
     if (g == 0) F[L::HP + w * BCH + n] = hp;
@@ -393,7 +507,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_a(const BwArgs a) {
       if (vt) *reinterpret_cast<float2*>(a.tok + (bh * T + t0 + n) * 2) = make_float2(rt, h);
     }
 
-    // B^T (rows s, columns t): g_t . v_s + h_t, causal mask
+    // B^T (rows s, columns t): (g_t . v_s + h_t) beta_s e^{l_t - l_s}
     f32x16 bs = zero16(), bs1 = zero16();
 #pragma unroll
     for (int js = 0; js < D / 16; ++js) {
@@ -402,24 +516,14 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_a(const BwArgs a) {
       bs1 = mfma(av, row_operand<D>(smem + L::GL, perm_pos(n), 2 * js + g), bs1);
     }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int s = 8 * (i >> 2) + 4 * g + (i & 3);
-      bs[i] = s <= n ? bs[i] + bs1[i] + h : 0.f;
-    }
+    for (int i = 0; i < 16; ++i) bs[i] = (bs[i] + bs1[i] + h) * weight(i);
     u32x4 bh_[2], bl_[2];
     split_acc(bs, bh_, bl_);
 
-    // dphi(q)^T (rows f of block w, columns t): phi(K)^T B + S g + z h.
-    // S g and z h cancel in large part (their difference is
+    // dphi(q)^T (rows f of block w, columns t): e^{l_t} (S g + z h) +
+    // phi(K)^T B.  S g and z h cancel in large part (their difference is
     // sum_s phi(k_s) g.(v_s - o_t)).
     f32x16 dq0 = zero16(), dq1 = zero16(), dq2 = zero16();
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const u32x4 ak = tr_operand<D>(smem + L::K, 16 * ks, 32 * w, lane);
-      dq0 = mfma(ak, bh_[ks], dq0);
-      dq1 = mfma(ak, bl_[ks], dq1);
-      dq2 = mfma(tr_operand<D>(smem + L::KL, 16 * ks, 32 * w, lane), bh_[ks], dq2);
-    }
 #pragma unroll
     for (int js = 0; js < D / 16; ++js) {
       const u32x4 sh = row_operand<D>(smem + L::SB, 32 * w + n, 2 * js + g);
@@ -428,61 +532,127 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_a(const BwArgs a) {
       dq1 = mfma(row_operand<D>(smem + L::SBL, 32 * w + n, 2 * js + g), gh, dq1);
       dq2 = mfma(sh, row_operand<D>(smem + L::GL, perm_pos(n), 2 * js + g), dq2);
     }
-    if (vt) {
+    if constexpr (DECAY != 0) {
+      dq0 *= eq;
+      dq1 *= eq;
+      dq2 *= eq;
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const u32x4 ak = tr_operand<D>(smem + L::K, 16 * ks, 32 * w, lane);
+      dq0 = mfma(ak, bh_[ks], dq0);
+      dq1 = mfma(ak, bl_[ks], dq1);
+      dq2 = mfma(tr_operand<D>(smem + L::KL, 16 * ks, 32 * w, lane), bh_[ks], dq2);
+    }
+    {
+      float qdp = 0.f;   // <phi(q_t), dphi(q_t)> over this lane's features
       float* dst = a.dq + (bh * T + t0 + n) * D + 32 * w + 4 * g;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int off = tile_off<D>(perm_pos(n), 4 * w + r) + 8 * g;
-        const f32x4 p4 = dphi4(smem + L::Q, smem + L::QL, off);
+        const f32x4 p4 = hilo4(smem + L::Q, smem + L::QL, off);
         const f32x4 z4 = *reinterpret_cast<const f32x4*>(F + L::Z + 32 * w + 4 * g + 8 * r);
         f32x4 o4;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * r + e;
-          o4[e] = (dq0[i] + dq1[i] + dq2[i] + z4[e] * h) * p4[e];
+          const float dphi = dq0[i] + dq1[i] + dq2[i] + eq * z4[e] * h;
+          // elu+1 has slope 1 above 0 and e^x = phi(x) below: min(phi, 1)
+          o4[e] = dphi * fminf(p4[e], 1.f);
+          qdp += p4[e] * dphi;
         }
-        *reinterpret_cast<f32x4*>(dst + 8 * r) = o4;
+        if (vt) *reinterpret_cast<f32x4*>(dst + 8 * r) = o4;
+      }
+      if constexpr (DECAY != 0) {
+        qdp = swap_sum32(qdp);
+        if (g == 0) F[L::QP + w * BCH + n] = qdp;
       }
     }
 
-    // the segment's gradient state: G_seg^T += g^T phi(Q)
+    // the segment's gradient state: G_seg^T += (weighted g)^T phi(Q)
+    {
+      constexpr int GA = DECAY ? L::WH : L::GH, GB = DECAY ? L::WL : L::GL;
 #pragma unroll
-    for (int fb = 0; fb < NJ; ++fb)
+      for (int fb = 0; fb < NJ; ++fb)
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const u32x4 ag = tr_operand<D>(smem + L::GH, 16 * ks, 32 * w, lane);
-        const u32x4 bq = tr_operand<D>(smem + L::Q, 16 * ks, 32 * fb, lane);
-        Gs[fb] = mfma(ag, bq, Gs[fb]);
-        Gs[fb] = mfma(tr_operand<D>(smem + L::GL, 16 * ks, 32 * w, lane), bq, Gs[fb]);
-        Gs[fb] = mfma(ag, tr_operand<D>(smem + L::QL, 16 * ks, 32 * fb, lane), Gs[fb]);
+        for (int ks = 0; ks < 2; ++ks) {
+          const u32x4 ag = tr_operand<D>(smem + GA, 16 * ks, 32 * w, lane);
+          const u32x4 bq = tr_operand<D>(smem + L::Q, 16 * ks, 32 * fb, lane);
+          Gs[fb] = mfma(ag, bq, Gs[fb]);
+          Gs[fb] = mfma(tr_operand<D>(smem + GB, 16 * ks, 32 * w, lane), bq, Gs[fb]);
+          Gs[fb] = mfma(ag, tr_operand<D>(smem + L::QL, 16 * ks, 32 * fb, lane), Gs[fb]);
+        }
+    }
+    if constexpr (DECAY == 0) {
+      // the state: S^T += V^T phi(K)
+#pragma unroll
+      for (int fb = 0; fb < NJ; ++fb)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const u32x4 av = tr_operand<D>(smem + L::V, 16 * ks, 32 * w, lane);
+          S[fb] = mfma(av, tr_operand<D>(smem + L::K, 16 * ks, 32 * fb, lane), S[fb]);
+          S[fb] = mfma(av, tr_operand<D>(smem + L::KL, 16 * ks, 32 * fb, lane), S[fb]);
+        }
+      __syncthreads();   // every read of the old S tile done; h visible
+    } else {
+      __syncthreads();   // every read of the old S tile and of the weighted g done; h visible
+      // w_s phi(k_s) (w_s = beta_s e^{l_last - l_s}) into the weighted tiles
+      const int b = tid % L::BPR;
+#pragma unroll
+      for (int rr = 0; rr < 2; ++rr) {
+        const int r = tid / L::BPR + 16 * rr;
+        const float wk = F[L::BET + r] * __expf(tot - F[L::LAM + r]);
+        float x[8];
+        hilo8<D>(smem + L::K, smem + L::KL, perm_pos(r), b, x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] *= wk;
+        const u32x4 kh = pack8(x);
+        blk_write<D>(smem + L::WH, perm_pos(r), b, kh);
+        blk_write<D>(smem + L::WL, perm_pos(r), b, low8(x, kh));
       }
-    // the state: S^T += V^T phi(K)
+      __syncthreads();   // weighted keys staged
+      // the state: S^T = e^{l_last} S^T + V^T (w phi(K))
+      const float ec = __expf(tot);
 #pragma unroll
-    for (int fb = 0; fb < NJ; ++fb)
+      for (int fb = 0; fb < NJ; ++fb) {
+        S[fb] *= ec;
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const u32x4 av = tr_operand<D>(smem + L::V, 16 * ks, 32 * w, lane);
-        S[fb] = mfma(av, tr_operand<D>(smem + L::K, 16 * ks, 32 * fb, lane), S[fb]);
-        S[fb] = mfma(av, tr_operand<D>(smem + L::KL, 16 * ks, 32 * fb, lane), S[fb]);
+        for (int ks = 0; ks < 2; ++ks) {
+          const u32x4 av = tr_operand<D>(smem + L::V, 16 * ks, 32 * w, lane);
+          S[fb] = mfma(av, tr_operand<D>(smem + L::WH, 16 * ks, 32 * fb, lane), S[fb]);
+          S[fb] = mfma(av, tr_operand<D>(smem + L::WL, 16 * ks, 32 * fb, lane), S[fb]);
+        }
       }
-    __syncthreads();   // every read of the old S tile done; h visible
+    }
     write_state_tile<D>(smem + L::SB, smem + L::SBL, S, w, g, n);
     if (tid < D) {
       float zs = 0.f;
 #pragma unroll
       for (int ww = 0; ww < L::NW; ++ww) zs += F[L::ZP + ww * D + tid];
-      F[L::Z + tid] += zs;
+      F[L::Z + tid] = (DECAY ? __expf(tot) : 1.f) * F[L::Z + tid] + zs;
     }
 #pragma unroll
     for (int rr = 0; rr < 2; ++rr) {
-      const float ht = F[L::HT + tid / L::BPR + 16 * rr];
+      const int r = tid / L::BPR + 16 * rr;
+      const float ht = F[L::HT + r] * (DECAY ? __expf(Lseg + F[L::LAM + r]) : 1.f);
+      float x[8];
+      hilo8<D>(smem + L::Q, smem + L::QL, perm_pos(r), tid % L::BPR, x);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) gzp[e] += fq[rr][e] * ht;
+      for (int e = 0; e < 8; ++e) gzp[e] += x[e] * ht;
+    }
+    if constexpr (DECAY != 0) {
+      if (w == 0 && g == 0 && vt) {
+        float s = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < L::NW; ++ww) s += F[L::QP + ww * BCH + n];
+        a.qd[bh * T + t0 + n] = s;
+      }
+      Lseg += tot;
     }
     __syncthreads();   // state tile and z for the next chunk; tiles free
   }
 
-  // G_seg (rows f, columns j) and gz_seg into the slot
+  // G_seg (rows f, columns j), gz_seg and the total log-decay into the slot
   float* dst = a.gslot + (bh * a.nseg + seg) * int64_t(D * D + D);
 #pragma unroll
   for (int fb = 0; fb < NJ; ++fb)
@@ -500,14 +670,17 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_a(const BwArgs a) {
     for (int ww = 0; ww < L::NW; ++ww) s += F[L::ZP + ww * D + tid];
     dst[D * D + tid] = s;
   }
+  if (DECAY != 0 && tid == 0) a.lgam[bh * a.nseg + seg] = Lseg;
 }
 
 // ------------------------------------------------------------ reverse scan
 
-// Per element of (G, gz) of one (b, h): the slot of segment u becomes the sum
-// of the slots after it (G at u's end); the total is dS0 (dz0).
-template <int D>
-__global__ __launch_bounds__(256) void bwd_rscan(float* gslot, int nseg, float* dS0, float* dz0) {
+// Per element of (G, gz) of one (b, h): the slot of segment u becomes G at
+// u's end, carry = G_seg(u) + Gamma_u carry over the segments from the last;
+// the final carry (G before the first token) is dS0 (dz0).
+template <int D, bool DECAY>
+__global__ __launch_bounds__(256) void bwd_rscan(float* gslot, const float* lgam, int nseg,
+                                                 float* dS0, float* dz0) {
   constexpr int E = D * D + D;
   constexpr int PER = (E + 255) / 256;
   const int64_t bh = blockIdx.x / PER;
@@ -518,7 +691,7 @@ __global__ __launch_bounds__(256) void bwd_rscan(float* gslot, int nseg, float* 
   for (int u = nseg - 1; u >= 0; --u) {
     const float x = base[int64_t(u) * E];
     base[int64_t(u) * E] = carry;
-    carry += x;
+    carry = DECAY ? fmaf(__expf(lgam[bh * nseg + u]), carry, x) : carry + x;
   }
   if (dS0) {
     if (e < D * D) dS0[bh * D * D + e] = carry;
@@ -528,9 +701,9 @@ __global__ __launch_bounds__(256) void bwd_rscan(float* gslot, int nseg, float* 
 
 // ------------------------------------------------------------------ pass B
 
-template <int D>
+template <int D, int DECAY>
 __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_b(const BwArgs a) {
-  using L = BL<D>;
+  using L = BL<D, DECAY>;
   constexpr int NJ = L::NJ;
   __shared__ __align__(16) char smem[L::LDS];
   float* F = reinterpret_cast<float*>(smem + L::F);
@@ -558,16 +731,26 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_b(const BwArgs a) {
   __syncthreads();
 
   Raw raw;
-  if (c0 < c1) load_raw<D>(a, bh, (c1 - 1) * BCH, tid, raw);
+  if (c0 < c1) load_raw<D, DECAY>(a, bh, (c1 - 1) * BCH, tid, raw);
   for (int c = c1 - 1; c >= c0; --c) {
     const int t0 = c * BCH;
-    float fq[2][8];
-    stage<D, false>(a, bh, t0, tid, raw, smem, fq);
-    __syncthreads();   // tiles, h, gz increments
-    if (c - 1 >= c0) load_raw<D>(a, bh, t0 - BCH, tid, raw);
+    float lam, bet, tot;
+    stage<D, DECAY, false>(a, bh, t0, tid, raw, smem, lam, bet, tot);
+    __syncthreads();   // tiles, h, gz increments, decay
+    if (c - 1 >= c0) load_raw<D, DECAY>(a, bh, t0 - BCH, tid, raw);
     const bool vs = t0 + n < T;
+    // key s = n: e^{l_last - l_s} to the chunk's end; beta_s
+    const float es = DECAY ? __expf(tot - lam) : 1.f;
 
-    // scores A (rows t, columns s = n), mask t >= s
+    // causal weights of (t, s = n): e^{l_t - l_s} for t >= s (beta_s later)
+    float wt[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int t = 8 * (i >> 2) + 4 * g + (i & 3);
+      wt[i] = t >= n ? (DECAY ? __expf(F[L::LAM + t] - lam) : 1.f) : 0.f;
+    }
+
+    // scores A (rows t, columns s = n)
     f32x16 at = zero16(), at1 = zero16(), at2 = zero16();
 #pragma unroll
     for (int fs = 0; fs < D / 16; ++fs) {
@@ -577,7 +760,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_b(const BwArgs a) {
       at1 = mfma(aq, row_operand<D>(smem + L::KL, perm_pos(n), 2 * fs + g), at1);
       at2 = mfma(row_operand<D>(smem + L::QL, perm_pos(n), 2 * fs + g), bk, at2);
     }
-    // B (rows t, columns s): g_t . v_s + h_t, mask t >= s
+    // B (rows t, columns s): g_t . v_s + h_t
     f32x16 bt = zero16(), bt1 = zero16();
 #pragma unroll
     for (int js = 0; js < D / 16; ++js) {
@@ -588,22 +771,16 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_b(const BwArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int t = 8 * (i >> 2) + 4 * g + (i & 3);
-      at[i] = t >= n ? at[i] + at1[i] + at2[i] : 0.f;
-      bt[i] = t >= n ? bt[i] + bt1[i] + F[L::HT + t] : 0.f;
+      at[i] = (at[i] + at1[i] + at2[i]) * wt[i];
+      bt[i] = (bt[i] + bt1[i] + F[L::HT + t]) * wt[i];
     }
     u32x4 ah[2], al[2], bh_[2], bl_[2];
     split_acc(at, ah, al);
     split_acc(bt, bh_, bl_);
 
-    // dv^T (rows j of block w, columns s): g^T A + G^T phi(k)
+    // dv^T / beta_s (rows j of block w, columns s): e^{l_last - l_s} G^T
+    // phi(k) + g^T A
     f32x16 dv0 = zero16(), dv1 = zero16(), dv2 = zero16();
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const u32x4 gh = tr_operand<D>(smem + L::GH, 16 * ks, 32 * w, lane);
-      dv0 = mfma(gh, ah[ks], dv0);
-      dv1 = mfma(gh, al[ks], dv1);
-      dv2 = mfma(tr_operand<D>(smem + L::GL, 16 * ks, 32 * w, lane), ah[ks], dv2);
-    }
 #pragma unroll
     for (int fs = 0; fs < D / 16; ++fs) {
       const u32x4 ag = tr_operand<D>(smem + L::SB, 16 * fs, 32 * w, lane);
@@ -612,9 +789,31 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_b(const BwArgs a) {
       dv1 = mfma(tr_operand<D>(smem + L::SBL, 16 * fs, 32 * w, lane), bk, dv1);
       dv2 = mfma(ag, row_operand<D>(smem + L::KL, perm_pos(n), 2 * fs + g), dv2);
     }
-    // dphi(k)^T (rows f of block w, columns s): phi(Q)^T B + G v + gz; G v
-    // and gz cancel in large part
+    if constexpr (DECAY != 0) {
+      dv0 *= es;
+      dv1 *= es;
+      dv2 *= es;
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const u32x4 gh = tr_operand<D>(smem + L::GH, 16 * ks, 32 * w, lane);
+      dv0 = mfma(gh, ah[ks], dv0);
+      dv1 = mfma(gh, al[ks], dv1);
+      dv2 = mfma(tr_operand<D>(smem + L::GL, 16 * ks, 32 * w, lane), ah[ks], dv2);
+    }
+    // dphi(k)^T / beta_s (rows f of block w, columns s): e^{l_last - l_s}
+    // (G v + gz) + phi(Q)^T B; G v and gz cancel in large part
     f32x16 dk0 = zero16(), dk1 = zero16(), dk2 = zero16();
+#pragma unroll
+    for (int js = 0; js < D / 16; ++js) {
+      const u32x4 bv = row_operand<D>(smem + L::V, perm_pos(n), 2 * js + g);
+      dk0 = mfma(row_operand<D>(smem + L::SB, 32 * w + n, 2 * js + g), bv, dk0);
+      dk1 = mfma(row_operand<D>(smem + L::SBL, 32 * w + n, 2 * js + g), bv, dk1);
+    }
+    if constexpr (DECAY != 0) {
+      dk0 *= es;
+      dk1 *= es;
+    }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const u32x4 aq = tr_operand<D>(smem + L::Q, 16 * ks, 32 * w, lane);
@@ -622,74 +821,151 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_b(const BwArgs a) {
       dk1 = mfma(aq, bl_[ks], dk1);
       dk2 = mfma(tr_operand<D>(smem + L::QL, 16 * ks, 32 * w, lane), bh_[ks], dk2);
     }
-#pragma unroll
-    for (int js = 0; js < D / 16; ++js) {
-      const u32x4 bv = row_operand<D>(smem + L::V, perm_pos(n), 2 * js + g);
-      dk0 = mfma(row_operand<D>(smem + L::SB, 32 * w + n, 2 * js + g), bv, dk0);
-      dk1 = mfma(row_operand<D>(smem + L::SBL, 32 * w + n, 2 * js + g), bv, dk1);
-    }
-    if (vs) {
+    {
+      float kdp = 0.f;   // <phi(k_s), dphi(k_s)> / beta_s over this lane's features
       const int64_t row = (bh * T + t0 + n) * D + 32 * w + 4 * g;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         f32x4 v4, o4;
         const int off = tile_off<D>(perm_pos(n), 4 * w + r) + 8 * g;
-        const f32x4 p4 = dphi4(smem + L::K, smem + L::KL, off);
+        const f32x4 p4 = hilo4(smem + L::K, smem + L::KL, off);
         const f32x4 z4 = *reinterpret_cast<const f32x4*>(F + L::Z + 32 * w + 4 * g + 8 * r);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * r + e;
-          v4[e] = dv0[i] + dv1[i] + dv2[i];
-          o4[e] = (dk0[i] + dk1[i] + dk2[i] + z4[e]) * p4[e];
+          v4[e] = bet * (dv0[i] + dv1[i] + dv2[i]);
+          const float raw_ = dk0[i] + dk1[i] + dk2[i] + es * z4[e];
+          o4[e] = bet * raw_ * fminf(p4[e], 1.f);
+          kdp += p4[e] * raw_;
         }
-        *reinterpret_cast<f32x4*>(a.dv + row + 8 * r) = v4;
-        *reinterpret_cast<f32x4*>(a.dk + row + 8 * r) = o4;
+        if (vs) {
+          *reinterpret_cast<f32x4*>(a.dv + row + 8 * r) = v4;
+          *reinterpret_cast<f32x4*>(a.dk + row + 8 * r) = o4;
+        }
+      }
+      if constexpr (DECAY != 0) {
+        kdp = swap_sum32(kdp);
+        if (g == 0) F[L::QP + w * BCH + n] = kdp;
       }
     }
 
-    // G^T += g^T phi(Q)
+    // G^T = e^{l_last} G^T + (e^{l_t} g)^T phi(Q)
+    {
+      constexpr int GA = DECAY ? L::WH : L::GH, GB = DECAY ? L::WL : L::GL;
+      const float ec = DECAY ? __expf(tot) : 1.f;
 #pragma unroll
-    for (int fb = 0; fb < NJ; ++fb)
+      for (int fb = 0; fb < NJ; ++fb) {
+        if constexpr (DECAY != 0) G[fb] *= ec;
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const u32x4 ag = tr_operand<D>(smem + L::GH, 16 * ks, 32 * w, lane);
-        const u32x4 bq = tr_operand<D>(smem + L::Q, 16 * ks, 32 * fb, lane);
-        G[fb] = mfma(ag, bq, G[fb]);
-        G[fb] = mfma(tr_operand<D>(smem + L::GL, 16 * ks, 32 * w, lane), bq, G[fb]);
-        G[fb] = mfma(ag, tr_operand<D>(smem + L::QL, 16 * ks, 32 * fb, lane), G[fb]);
+        for (int ks = 0; ks < 2; ++ks) {
+          const u32x4 ag = tr_operand<D>(smem + GA, 16 * ks, 32 * w, lane);
+          const u32x4 bq = tr_operand<D>(smem + L::Q, 16 * ks, 32 * fb, lane);
+          G[fb] = mfma(ag, bq, G[fb]);
+          G[fb] = mfma(tr_operand<D>(smem + GB, 16 * ks, 32 * w, lane), bq, G[fb]);
+          G[fb] = mfma(ag, tr_operand<D>(smem + L::QL, 16 * ks, 32 * fb, lane), G[fb]);
+        }
       }
+    }
     __syncthreads();   // every read of the old G tile and of gz done
     write_state_tile<D>(smem + L::SB, smem + L::SBL, G, w, g, n);
     if (tid < D) {
       float s = 0.f;
 #pragma unroll
       for (int ww = 0; ww < L::NW; ++ww) s += F[L::ZP + ww * D + tid];
-      F[L::Z + tid] += s;
+      F[L::Z + tid] = (DECAY ? __expf(tot) : 1.f) * F[L::Z + tid] + s;
+    }
+    if constexpr (DECAY != 0) {
+      if (w == 0 && g == 0 && vs) {
+        float s = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < L::NW; ++ww) s += F[L::QP + ww * BCH + n];
+        a.kd[bh * T + t0 + n] = s;
+      }
     }
     __syncthreads();
   }
 }
 
-template <int D>
-hipError_t launch_d(const Problem& pb, const BwArgs& a, float* dS0, float* dz0, hipStream_t st) {
+// ----------------------------------------------------- decay gradient
+
+// One 256-thread block per (b, h): R_r = sum_{t >= r} (qd_t - beta_t kd_t)
+// (dL/dlog alpha_r), then dL/da_r = R_r / a_r (SSD) or dL/dg_r = R_r / g_r -
+// kd_r (RFA: alpha = g, beta = 1 - g).  Each thread walks a contiguous run
+// of tokens; the runs' totals are suffix-summed in LDS.
+template <int DECAY>
+__global__ __launch_bounds__(256) void bwd_decay_grad(const float* decay, const float* qd,
+                                                      const float* kd, float* dd, int T) {
+  __shared__ float part[257];
+  const int64_t bh = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int per = (T + 255) / 256;
+  const int t0 = min(tid * per, T), t1 = min(t0 + per, T);
+  const float* al = decay + bh * T;
+  const float* q = qd + bh * T;
+  const float* k = kd + bh * T;
+  float s = 0.f;
+  for (int t = t0; t < t1; ++t) s += q[t] - (DECAY == 2 ? 1.f - al[t] : 1.f) * k[t];
+  part[tid] = s;
+  __syncthreads();
+  if (tid == 0) {
+    float acc = 0.f;
+    part[256] = 0.f;
+    for (int i = 255; i >= 0; --i) {
+      const float x = part[i];
+      part[i] = acc;   // the sum over the runs after run i
+      acc += x;
+    }
+  }
+  __syncthreads();
+  float R = part[tid];
+  for (int t = t1 - 1; t >= t0; --t) {
+    const float a_t = al[t];
+    R += q[t] - (DECAY == 2 ? 1.f - a_t : 1.f) * k[t];
+    dd[bh * T + t] = DECAY == 2 ? R / a_t - k[t] : R / a_t;
+  }
+}
+
+template <int D, int DECAY>
+hipError_t launch_d(const Problem& pb, const BwArgs& a, float* dS0, float* dz0, float* ddecay,
+                    hipStream_t st) {
   const unsigned nwg = unsigned(pb.BH() * a.nseg);
-  bwd_pass_a<D><<<dim3(nwg), dim3(64 * (D / 32)), 0, st>>>(a);
+  bwd_pass_a<D, DECAY><<<dim3(nwg), dim3(64 * (D / 32)), 0, st>>>(a);
   constexpr int PER = (D * D + D + 255) / 256;
-  bwd_rscan<D><<<dim3(unsigned(pb.BH() * PER)), dim3(256), 0, st>>>(a.gslot, a.nseg, dS0, dz0);
-  bwd_pass_b<D><<<dim3(nwg), dim3(64 * (D / 32)), 0, st>>>(a);
+  bwd_rscan<D, DECAY != 0><<<dim3(unsigned(pb.BH() * PER)), dim3(256), 0, st>>>(
+      a.gslot, a.lgam, a.nseg, dS0, dz0);
+  bwd_pass_b<D, DECAY><<<dim3(nwg), dim3(64 * (D / 32)), 0, st>>>(a);
+  if constexpr (DECAY != 0)
+    bwd_decay_grad<DECAY><<<dim3(unsigned(pb.BH())), dim3(256), 0, st>>>(a.decay, a.qd, a.kd,
+                                                                         ddecay, a.T);
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_kind(const Problem& pb, const BwArgs& a, float* dS0, float* dz0, float* ddecay,
+                       hipStream_t st) {
+  switch (pb.decay_kind) {
+    case LA_DECAY_NONE: return launch_d<D, 0>(pb, a, dS0, dz0, ddecay, st);
+    case LA_DECAY_SSD: return launch_d<D, 1>(pb, a, dS0, dz0, ddecay, st);
+    case LA_GATE_RFA: return launch_d<D, 2>(pb, a, dS0, dz0, ddecay, st);
+    default: break;
+  }
+  return hipErrorInvalidValue;
 }
 
 size_t r256(size_t b) { return (b + 255) / 256 * 256; }
 
 struct BwLayout {
-  size_t fwd, sinit, zinit, gslot, tok, total;
+  size_t fwd, sinit, zinit, gslot, tok, lgam, qd, kd, total;
 };
 
+// Workspace: the prefill's (for the segment start states), a copy of the
+// initial state, one gradient state per segment, two floats per token; with
+// a decay also the segments' log-decays and two more floats per token.
 BwLayout layout_of(const Problem& pb) {
   int cps, nseg, nsub, nslot;
   mfma_split(pb, &cps, &nseg, &nsub, &nslot);
-  const size_t BH = size_t(pb.BH()), D = size_t(pb.dv);
+  const size_t BH = size_t(pb.BH()), D = size_t(pb.dv), T = size_t(pb.T);
+  const bool dec = pb.decay_kind != LA_DECAY_NONE;
   BwLayout l;
   size_t off = 0;
   l.fwd = off;
@@ -701,7 +977,15 @@ BwLayout layout_of(const Problem& pb) {
   l.gslot = off;
   off += r256(BH * nseg * (D * D + D) * 4);
   l.tok = off;
-  off += r256(BH * size_t(pb.T) * 2 * 4);
+  off += r256(BH * T * 2 * 4);
+  l.lgam = l.qd = l.kd = off;
+  if (dec) {
+    off += r256(BH * nseg * 4);
+    l.qd = off;
+    off += r256(BH * T * 4);
+    l.kd = off;
+    off += r256(BH * T * 4);
+  }
   l.total = off;
   return l;
 }
@@ -710,8 +994,9 @@ BwLayout layout_of(const Problem& pb) {
 
 bool backward_chunked(const Problem& p) {
   return p.path == 1 && p.dtype == LA_BF16 && p.phi == LA_PHI_ELU1 &&
-         p.decay_kind == LA_DECAY_NONE && !p.noncausal && p.T > 0 && p.dp == p.dv &&
-         (p.dv == 64 || p.dv == 128);
+         (p.decay_kind == LA_DECAY_NONE || p.decay_kind == LA_DECAY_SSD ||
+          p.decay_kind == LA_GATE_RFA) &&
+         !p.noncausal && p.T > 0 && p.dp == p.dv && (p.dv == 64 || p.dv == 128);
 }
 
 Problem backward_plan(const Problem& p) {
@@ -727,8 +1012,8 @@ size_t backward_chunked_workspace_bytes(const Problem& p) { return layout_of(bac
 
 hipError_t launch_backward_chunked(const Problem& p, const void* q, const void* k, const void* v,
                                    const float* S0, const float* z0, const void* dout, float* dq,
-                                   float* dk, float* dv, float* dS0, float* dz0, void* ws,
-                                   hipStream_t stream) {
+                                   float* dk, float* dv, float* ddecay, float* dS0, float* dz0,
+                                   void* ws, hipStream_t stream) {
   const Problem pb = backward_plan(p);
   const BwLayout l = layout_of(pb);
   char* base = static_cast<char*>(ws);
@@ -740,12 +1025,16 @@ hipError_t launch_backward_chunked(const Problem& p, const void* q, const void* 
   a.k = static_cast<const bf16_t*>(k);
   a.v = static_cast<const bf16_t*>(v);
   a.dout = dout;
+  a.decay = pb.decay;
   a.dout_f32 = pb.out_dtype == LA_F32 ? 1 : 0;
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
   a.gslot = reinterpret_cast<float*>(base + l.gslot);
   a.tok = reinterpret_cast<float*>(base + l.tok);
+  a.lgam = reinterpret_cast<float*>(base + l.lgam);
+  a.qd = reinterpret_cast<float*>(base + l.qd);
+  a.kd = reinterpret_cast<float*>(base + l.kd);
   a.T = pb.T;
   a.cps = cps;
   a.nseg = nseg;
@@ -782,8 +1071,8 @@ hipError_t launch_backward_chunked(const Problem& p, const void* q, const void* 
     a.z_bh = D;
     a.s_seg = 0;
   }
-  if (D == 128) return launch_d<128>(pb, a, dS0, dz0, stream);
-  return launch_d<64>(pb, a, dS0, dz0, stream);
+  if (D == 128) return launch_kind<128>(pb, a, dS0, dz0, ddecay, stream);
+  return launch_kind<64>(pb, a, dS0, dz0, ddecay, stream);
 }
 
 }  // namespace la

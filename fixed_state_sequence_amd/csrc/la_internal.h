@@ -57,15 +57,15 @@ hipError_t launch_backward(const Problem& p, const void* q, const void* k, const
                            void* ws, hipStream_t stream);
 
 // Chunked gradients (la_backward_mfma.hip): bf16 inputs, elu+1, no decay,
-// d' = d_v in {64, 128}, T > 0.  The plan is the prefill's with 32-token
-// chunks.
+// the SSD decay or the RFA gate, d' = d_v in {64, 128}, T > 0.  The plan is
+// the prefill's with 32-token chunks.
 bool backward_chunked(const Problem& p);
 Problem backward_plan(const Problem& p);
 size_t backward_chunked_workspace_bytes(const Problem& p);
 hipError_t launch_backward_chunked(const Problem& p, const void* q, const void* k, const void* v,
                                    const float* S0, const float* z0, const void* dout, float* dq,
-                                   float* dk, float* dv, float* dS0, float* dz0, void* ws,
-                                   hipStream_t stream);
+                                   float* dk, float* dv, float* ddecay, float* dS0, float* dz0,
+                                   void* ws, hipStream_t stream);
 
 // Zero-fill of the state (m may be null).
 hipError_t launch_state_init(float* S, int64_t nS, float* z, int64_t nz, float* m, int64_t nm,

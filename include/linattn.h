@@ -208,8 +208,9 @@ la_status la_prefill_stage(const la_desc* desc, int stage, const void* q, const 
  * shapes with 32-token chunks, plus B H d' d_v + B H d' fp32 (a copy of the
  * initial state), B H nseg (d' d_v + d') fp32 (one gradient state per
  * segment) and B H T 2 fp32 (per token: the read-out's factor and the
- * divisor's gradient), each part rounded up to 256 bytes.  The per-token
- * path: B H T (d_v + 2) fp32. */
+ * divisor's gradient), each part rounded up to 256 bytes; with a decay also
+ * B H nseg fp32 (each segment's log-decay) and B H T 2 fp32 (per-token
+ * terms of the decay gradient).  The per-token path: B H T (d_v + 2) fp32. */
 la_status la_prefill_backward_workspace_size(const la_desc* desc, size_t* bytes);
 
 /* Gradients of a causal prefill for training ([lesson] Developer level and
@@ -229,14 +230,15 @@ la_status la_prefill_backward_workspace_size(const la_desc* desc, size_t* bytes)
  * Supported: causal, elu+1 or identity features, LA_DECAY_NONE, LA_DECAY_SSD
  * or LA_GATE_RFA, every read-out form, the widths the per-token kernel takes
  * (LA_EUNSUPPORTED otherwise: RFF, the mLSTM gates, the non-causal form).
- * Two paths.  Chunked (bf16 inputs, elu+1, no decay, d' = d_v in {64, 128},
- * T > 0): the same gradients written as masked-quadratic sums inside
- * 32-token chunks and states across them, as the forward ([lesson]
- * "Implementation reality"): the prefill's segment start states, a pass in
- * token order (dq and each segment's gradient state sum phi(q_t) g_t^T), a
- * reverse scan over the segments, and a pass in reverse order (dk, dv); the
- * segment plan is the prefill's for 32-token chunks (desc->segments, 0 =
- * default).  Otherwise one workgroup walks each (b, h) sequence token by
+ * Two paths.  Chunked (bf16 inputs, elu+1, no decay, the SSD decay or the
+ * RFA gate, d' = d_v in {64, 128}, T > 0): the same gradients written as
+ * masked-quadratic sums inside 32-token chunks and states across them, as
+ * the forward ([lesson] "Implementation reality"): the prefill's segment
+ * start states, a pass in token order (dq and each segment's gradient state
+ * sum phi(q_t) g_t^T), a reverse scan over the segments, a pass in reverse
+ * order (dk, dv) and, with a decay, a suffix sum per sequence for the decay
+ * gradient; the segment plan is the prefill's for 32-token chunks
+ * (desc->segments, 0 = default).  Otherwise one workgroup walks each (b, h) sequence token by
  * token, forward then backward.  `workspace` holds
  * la_prefill_backward_workspace_size() bytes; its contents on return are
  * scratch. */

@@ -673,41 +673,51 @@ def prefill_gradients(q, k, v, dout, phi="elu1", decay=None, gate=None, eps=1e-6
     return res
 
 
-def prefill_gradients_recurrent(q, k, v, dout, phi="elu1", eps=1e-6, S0=None, z0=None,
-                                normalize=True):
-    """The same gradients as prefill_gradients for the form with no decay,
-    by reverse mode through the recurrence instead of the quadratic form
-    (O(T d' d_v) per head, for long sequences), in float64.
+def prefill_gradients_recurrent(q, k, v, dout, phi="elu1", decay=None, gate=None, eps=1e-6,
+                                S0=None, z0=None, normalize=True):
+    """The same gradients as prefill_gradients, by reverse mode through the
+    recurrence instead of the quadratic form (O(T d' d_v) per head, for long
+    sequences), in float64.
 
-    Forward over t ([lesson] Researcher level, Derivation: S_t = S_{t-1} +
-    phi(k_t) v_t^T, z_t likewise, o_t read from the state after token t):
+    Forward over t ([lesson] Researcher level, Derivation; [card]
+    Implementation sketch: S_t = alpha_t S_{t-1} + beta_t phi(k_t) v_t^T, z_t
+    likewise, o_t read from the state after token t):
         D_t the read-out's divisor, g_t = dout_t / D_t, h_t its gradient
         (-(dout_t . o_t) / D_t for the sum read-out),
         dphi(q_t) = S_t g_t + z_t h_t.
     Backward over t, with the gradient state G (d' x d_v) and gz (d'):
-        G += phi(q_t) g_t^T,  gz += phi(q_t) h_t   (every read-out at t' >= t)
-        dphi(k_t) = G v_t + gz,  dv_t = G^T phi(k_t).
-    The initial state reaches every S_t unchanged: dS0 = G, dz0 = gz after
-    the walk.  Returns a dict with dq, dk, dv, dS0, dz0.
+        G <- alpha_{t+1} G + phi(q_t) g_t^T,  gz likewise with h_t
+        u_t = G v_t + gz,  dphi(k_t) = beta_t u_t,  dv_t = beta_t G^T phi(k_t).
+    The decay reaches the loss through the log-decay prefix: every weight
+    holds alpha_r for r between its key and its query, so
+        dL/dalpha_r = sum_{t >= r} (phi(q_t).dphi(q_t) - phi(k_t).dphi(k_t)) / alpha_r,
+        dL/dbeta_t = phi(k_t) . u_t.
+    The initial state enters S_t as prod_{r<=t} alpha_r S0: dS0 = alpha_0 G,
+    dz0 = alpha_0 gz after the walk.  Returns a dict with dq, dk, dv, dS0,
+    dz0 and ddecay (with decay) or dgate (with gate).
     """
     fq_all, fk_all = features(q, phi), features(k, phi)
     dphq, dphk = phi_derivative(q, phi), phi_derivative(k, phi)
     v_all, do_all = _f64(v), _f64(dout)
+    alpha_all, beta_all = decay_coefficients(decay, gate)
     lead = fq_all.shape[:-2]
     T, dp = fq_all.shape[-2:]
     dv_ = v_all.shape[-1]
     res = {n: np.zeros(lead + shp) for n, shp in (("dq", (T, q.shape[-1])), ("dk", (T, k.shape[-1])),
-                                                  ("dv", (T, dv_)), ("dS0", (dp, dv_)), ("dz0", (dp,)))}
+                                                  ("dv", (T, dv_)), ("dS0", (dp, dv_)), ("dz0", (dp,)),
+                                                  ("dalpha", (T,)), ("dbeta", (T,)))}
     for idx in np.ndindex(*lead):
         fq, fk, vv, do = fq_all[idx], fk_all[idx], v_all[idx], do_all[idx]
+        al = np.ones(T) if alpha_all is None else alpha_all[idx]
+        be = np.ones(T) if beta_all is None else beta_all[idx]
         S = np.zeros((dp, dv_)) if S0 is None else _f64(S0)[idx].copy()
         z = np.zeros(dp) if z0 is None else _f64(z0)[idx].copy()
         g = np.empty((T, dv_))
         h = np.empty(T)
         dfq = np.empty((T, dp))
         for t in range(T):
-            S += np.outer(fk[t], vv[t])
-            z += fk[t]
+            S = al[t] * S + be[t] * np.outer(fk[t], vv[t])
+            z = al[t] * z + be[t] * fk[t]
             num = fq[t] @ S
             den = fq[t] @ z
             if normalize is True:
@@ -728,17 +738,28 @@ def prefill_gradients_recurrent(q, k, v, dout, phi="elu1", eps=1e-6, S0=None, z0
         gz = np.zeros(dp)
         dfk = np.empty((T, dp))
         dvv = np.empty((T, dv_))
+        dl = np.empty(T)          # dL/dl_t: phi(q_t).dphi(q_t) - phi(k_t).dphi(k_t)
         for t in range(T - 1, -1, -1):
-            G += np.outer(fq[t], g[t])
-            gz += fq[t] * h[t]
-            dfk[t] = G @ vv[t] + gz
-            dvv[t] = fk[t] @ G
+            a_next = al[t + 1] if t + 1 < T else 0.0
+            G = a_next * G + np.outer(fq[t], g[t])
+            gz = a_next * gz + fq[t] * h[t]
+            u = G @ vv[t] + gz
+            dfk[t] = be[t] * u
+            dvv[t] = be[t] * (fk[t] @ G)
+            res["dbeta"][idx][t] = fk[t] @ u
+            dl[t] = fq[t] @ dfq[t] - fk[t] @ dfk[t]
         res["dq"][idx] = dfq * dphq[idx]
         res["dk"][idx] = dfk * dphk[idx]
         res["dv"][idx] = dvv
-        res["dS0"][idx] = G
-        res["dz0"][idx] = gz
-    return res
+        res["dS0"][idx] = al[0] * G
+        res["dz0"][idx] = al[0] * gz
+        res["dalpha"][idx] = np.cumsum(dl[::-1])[::-1] / al
+    out = {n: res[n] for n in ("dq", "dk", "dv", "dS0", "dz0")}
+    if decay is not None:
+        out["ddecay"] = res["dalpha"]
+    if gate is not None:
+        out["dgate"] = res["dalpha"] - res["dbeta"]
+    return out
 
 
 # --------------------------------------------------------------------------

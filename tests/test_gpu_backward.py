@@ -117,6 +117,44 @@ def test_backward_chunked_vs_oracle(d, T, segments, normalize, dout32, with_stat
     compare(got, ref, TOL["bf16"], (d, T, segments, normalize, dout32, with_state))
 
 
+# The chunked path with a decay: the SSD decay (a = sigmoid(N(3, 1)), and a
+# strongly decaying draw, sigmoid(N(-1, 1)), where e^{l} spans many orders
+# within a chunk) and the RFA gate, with their gradients dL/da and dL/dg.
+CHUNKED_DECAY = [
+    # d, T, segments, normalize, dout fp32, with state, decay, decay mean
+    (128, 300, 0, True, False, True, "ssd", 3.0),
+    (64, 333, 3, True, True, False, "rfa", 3.0),
+    (128, 95, 1, "max1", False, True, "rfa", 3.0),
+    (64, 211, 0, False, False, True, "ssd", 3.0),
+    (128, 20, 0, True, False, False, "ssd", 3.0),
+    (128, 257, 0, True, False, True, "ssd", -1.0),
+    (64, 64, 2, True, False, True, "rfa", 3.0),
+]
+
+
+@pytest.mark.parametrize("d,T,segments,normalize,dout32,with_state,decay,mean", CHUNKED_DECAY)
+def test_backward_chunked_decay_vs_oracle(d, T, segments, normalize, dout32, with_state, decay,
+                                          mean):
+    dev = gpu_device()
+    B, H = 1, 2
+    x = I.prefill_inputs(B, H, T, d, dtype="bf16", seed=T + 7 * d, scale=2.0 ** -0.5,
+                         decay=decay, decay_mean=mean)
+    do = torch.randn(B, H, T, d, generator=torch.Generator().manual_seed(T + 1))
+    if not dout32:
+        do = do.to(torch.bfloat16)
+    state = None
+    if with_state:
+        rng = np.random.default_rng(d + 1)
+        state = (rng.standard_normal((B, H, d, d)) * 0.3, np.abs(rng.standard_normal((B, H, d))) * 3)
+    print(f"chunked backward: d={d} T={T} segments={segments} norm={normalize} "
+          f"dout32={dout32} state={with_state} decay={decay} mean={mean}", flush=True)
+    got = run(x, do, dev, "elu1", normalize, state=state, state_grad=True, segments=segments)
+    ref = O.prefill_gradients(x.q, x.k, x.v, do, decay=x.decay, gate=x.gate,
+                              S0=None if state is None else state[0],
+                              z0=None if state is None else state[1], normalize=normalize)
+    compare(got, ref, TOL["bf16"], (d, T, segments, normalize, dout32, with_state, decay, mean))
+
+
 # The two workloads bench.py times the gradients on, at full size, in its
 # launch configuration (default plan, bf16 dout), against the oracle's
 # recurrent gradients (pinned to the quadratic form and to finite
@@ -145,5 +183,23 @@ def test_backward_long_prefill_b1_h8_t102400_d128_two_heads():
     ref = O.prefill_gradients_recurrent(x.q[0, hs], x.k[0, hs], x.v[0, hs], do[0, hs])
     compare({k: v[0, hs] for k, v in got.items()}, ref, TOL["bf16"],
             "long prefill backward 1x8x102400x128, heads 0 and 5")
+    for k in got:
+        assert np.isfinite(got[k]).all(), k
+
+
+def test_backward_ssd_prefill_b2_h16_t8192_d128_eight_sequences():
+    """The SSD-decay prefill workload's gradients at full size in the default
+    plan (bf16 dout), eight (b, h) sequences end to end against the oracle's
+    recurrent gradients, dL/da included."""
+    dev = gpu_device()
+    x = I.workload_inputs("ssd_prefill_b2_h16_t8192_d128", seed=0)
+    do = torch.randn(x.q.shape, generator=torch.Generator().manual_seed(1)).to(torch.bfloat16)
+    got = run(x, do, dev, "elu1", True, state_grad=True)
+    pairs = [(0, 0), (0, 5), (0, 11), (0, 15), (1, 2), (1, 7), (1, 9), (1, 14)]
+    bs, hs = [p[0] for p in pairs], [p[1] for p in pairs]
+    ref = O.prefill_gradients_recurrent(x.q[bs, hs], x.k[bs, hs], x.v[bs, hs], do[bs, hs],
+                                        decay=x.decay[bs, hs])
+    compare({k: v[bs, hs] for k, v in got.items()}, ref, TOL["bf16"],
+            "ssd prefill backward 2x16x8192x128, eight sequences")
     for k in got:
         assert np.isfinite(got[k]).all(), k

@@ -151,16 +151,36 @@ def test_recurrent_gradients_match_finite_differences(phi, normalize):
 
 
 @pytest.mark.parametrize("normalize", [True, False, "max1"])
-def test_recurrent_gradients_equal_quadratic_form(normalize):
+@pytest.mark.parametrize("kind", ["none", "ssd", "rfa"])
+def test_recurrent_gradients_equal_quadratic_form(normalize, kind):
     rng = np.random.default_rng(5)
     B, H, T, d, dv = 2, 2, 50, 5, 3
     q, k = rng.standard_normal((B, H, T, d)), rng.standard_normal((B, H, T, d))
     v, do = rng.standard_normal((B, H, T, dv)), rng.standard_normal((B, H, T, dv))
     S0, z0 = rng.standard_normal((B, H, d, dv)) * 0.3, np.abs(rng.standard_normal((B, H, d)))
-    a = O.prefill_gradients(q, k, v, do, S0=S0, z0=z0, normalize=normalize)
-    b = O.prefill_gradients_recurrent(q, k, v, do, S0=S0, z0=z0, normalize=normalize)
+    a_ = 1.0 / (1.0 + np.exp(-rng.standard_normal((B, H, T)) - 1.0))
+    decay = a_ if kind == "ssd" else None
+    gate = a_ if kind == "rfa" else None
+    a = O.prefill_gradients(q, k, v, do, decay=decay, gate=gate, S0=S0, z0=z0, normalize=normalize)
+    b = O.prefill_gradients_recurrent(q, k, v, do, decay=decay, gate=gate, S0=S0, z0=z0,
+                                      normalize=normalize)
+    assert set(a) == set(b)
     for n in b:
-        assert np.abs(a[n] - b[n]).max() <= 1e-12 * np.abs(a[n]).max(), n
+        assert np.abs(a[n] - b[n]).max() <= 1e-11 * np.abs(a[n]).max(), n
+
+
+@pytest.mark.parametrize("kind", ["ssd", "rfa"])
+def test_recurrent_decay_gradient_matches_finite_differences(kind):
+    q, k, v, do, S0, z0, decay, gate = case(12, kind=kind)
+    g = O.prefill_gradients_recurrent(q, k, v, do, decay=decay, gate=gate, S0=S0, z0=z0)
+    f = lambda **kw: loss(**{**dict(q=q, k=k, v=v, do=do, phi="elu1", decay=decay, gate=gate,
+                                    S0=S0, z0=z0, normalize=True), **kw})
+    if kind == "ssd":
+        name, x, fn = "ddecay", decay, lambda x: f(decay=x)
+    else:
+        name, x, fn = "dgate", gate, lambda x: f(gate=x)
+    ref = fd(fn, x)
+    assert np.abs(g[name] - ref).max() <= 1e-6 * max(1.0, np.abs(ref).max()), name
 
 
 def test_recurrent_gradients_planted_mistake_is_caught():
