@@ -203,3 +203,31 @@ def test_backward_ssd_prefill_b2_h16_t8192_d128_eight_sequences():
             "ssd prefill backward 2x16x8192x128, eight sequences")
     for k in got:
         assert np.isfinite(got[k]).all(), k
+
+
+def test_backward_chunked_many_short_sequences():
+    """128 sequences of 40 tokens (one segment each, a ragged second chunk)
+    with the SSD decay on the chunked path."""
+    dev = gpu_device()
+    B, H, T, d = 8, 16, 40, 64
+    x = I.prefill_inputs(B, H, T, d, dtype="bf16", seed=21, decay="ssd", scale=2.0 ** -0.5)
+    do = torch.randn(B, H, T, d, generator=torch.Generator().manual_seed(22)).to(torch.bfloat16)
+    got = run(x, do, dev, "elu1", True, state_grad=True)
+    ref = O.prefill_gradients(x.q, x.k, x.v, do, decay=x.decay)
+    compare(got, ref, TOL["bf16"], "many short sequences")
+
+
+@pytest.mark.parametrize("dtype,phi", [("f16", "elu1"), ("bf16", "identity")])
+def test_backward_per_token_path_16_bit(dtype, phi):
+    """16-bit inputs the chunked path does not take (fp16, identity features)
+    go through the per-token kernel, against the oracle on the same values."""
+    dev = gpu_device()
+    B, H, T, d = 1, 2, 70, 32
+    x = I.prefill_inputs(B, H, T, d, dtype=dtype, seed=23, decay="rfa", scale=0.5)
+    if phi == "identity":
+        x.q, x.k = x.q.abs(), x.k.abs()   # positive features keep q.z away from 0
+    dt = torch.float16 if dtype == "f16" else torch.bfloat16
+    do = torch.randn(B, H, T, d, generator=torch.Generator().manual_seed(24)).to(dt)
+    got = run(x, do, dev, phi, True, state_grad=True)
+    ref = O.prefill_gradients(x.q, x.k, x.v, do, phi=phi, gate=x.gate)
+    compare(got, ref, TOL["bf16"], (dtype, phi))
