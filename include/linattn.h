@@ -238,7 +238,8 @@ la_status la_prefill_backward_workspace_size(const la_desc* desc, size_t* bytes)
  * sum phi(q_t) g_t^T), a reverse scan over the segments, a pass in reverse
  * order (dk, dv) and, with a decay, a suffix sum per sequence for the decay
  * gradient; the segment plan is the prefill's for 32-token chunks
- * (desc->segments, 0 = default).  Otherwise one workgroup walks each (b, h) sequence token by
+ * (desc->segments when desc->chunk is 0 or 32, 0 = default; the default
+ * for any other chunk).  Otherwise one workgroup walks each (b, h) sequence token by
  * token, forward then backward.  `workspace` holds
  * la_prefill_backward_workspace_size() bytes; its contents on return are
  * scratch. */
