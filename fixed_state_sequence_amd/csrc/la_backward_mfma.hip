@@ -123,6 +123,7 @@ struct BwArgs {
   float* tok;    // [BH, T, 2]: r_t and h_t
   float* qd;     // [BH, T]: <phi(q_t), dphi(q_t)> (pass A, with a decay)
   float* kd;     // [BH, T]: <phi(k_t), dphi(k_t)> / beta_t (pass B, with a decay)
+  float* dpart;  // [BH, ceil(T / DG_TILE)]: per-tile totals of the decay gradient's terms
   int T, cps, nseg, norm;
   float eps;
 };
@@ -888,40 +889,88 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_b(const BwArgs a) {
 
 // ----------------------------------------------------- decay gradient
 
-// One 256-thread block per (b, h): R_r = sum_{t >= r} (qd_t - beta_t kd_t)
-// (dL/dlog alpha_r), then dL/da_r = R_r / a_r (SSD) or dL/dg_r = R_r / g_r -
-// kd_r (RFA: alpha = g, beta = 1 - g).  Each thread walks a contiguous run
-// of tokens; the runs' totals are suffix-summed in LDS.
+// dL/dlog alpha_r = R_r = sum_{t >= r} (qd_t - beta_t kd_t), then dL/da_r =
+// R_r / a_r (SSD) or dL/dg_r = R_r / g_r - kd_r (RFA: alpha = g, beta =
+// 1 - g).  Two passes over tiles of DG_TILE tokens of every (b, h): the
+// tiles' totals, then per tile a suffix scan (4 tokens per thread, waves by
+// shuffles, the workgroup through LDS) plus the totals of the later tiles.
+constexpr int DG_TILE = 1024;
+
+template <int DECAY>
+__device__ __forceinline__ float dl_term(const float* al, const float* qd, const float* kd,
+                                         int64_t i) {
+  return qd[i] - (DECAY == 2 ? 1.f - al[i] : 1.f) * kd[i];
+}
+
+// Sum over the 256 threads of a workgroup, returned to every thread.
+__device__ __forceinline__ float block_sum256(float x, float* red) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+  __syncthreads();   // red free from any earlier use
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  return red[0] + red[1] + red[2] + red[3];
+}
+
+template <int DECAY>
+__global__ __launch_bounds__(256) void bwd_decay_tile_sums(const float* decay, const float* qd,
+                                                           const float* kd, float* part, int T,
+                                                           int ntile) {
+  __shared__ float red[4];
+  const int64_t bh = blockIdx.x / ntile;
+  const int tile = blockIdx.x % ntile;
+  float s = 0.f;
+  for (int i = threadIdx.x; i < DG_TILE; i += 256) {
+    const int t = tile * DG_TILE + i;
+    if (t < T) s += dl_term<DECAY>(decay, qd, kd, bh * T + t);
+  }
+  s = block_sum256(s, red);
+  if (threadIdx.x == 0) part[bh * ntile + tile] = s;
+}
+
 template <int DECAY>
 __global__ __launch_bounds__(256) void bwd_decay_grad(const float* decay, const float* qd,
-                                                      const float* kd, float* dd, int T) {
-  __shared__ float part[257];
-  const int64_t bh = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int per = (T + 255) / 256;
-  const int t0 = min(tid * per, T), t1 = min(t0 + per, T);
-  const float* al = decay + bh * T;
-  const float* q = qd + bh * T;
-  const float* k = kd + bh * T;
-  float s = 0.f;
-  for (int t = t0; t < t1; ++t) s += q[t] - (DECAY == 2 ? 1.f - al[t] : 1.f) * k[t];
-  part[tid] = s;
-  __syncthreads();
-  if (tid == 0) {
-    float acc = 0.f;
-    part[256] = 0.f;
-    for (int i = 255; i >= 0; --i) {
-      const float x = part[i];
-      part[i] = acc;   // the sum over the runs after run i
-      acc += x;
-    }
+                                                      const float* kd, const float* part,
+                                                      float* dd, int T, int ntile) {
+  __shared__ float red[4];
+  const int64_t bh = blockIdx.x / ntile;
+  const int tile = blockIdx.x % ntile;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // the later tiles' totals
+  float c = 0.f;
+  for (int u = tile + 1 + tid; u < ntile; u += 256) c += part[bh * ntile + u];
+  const float carry = block_sum256(c, red);
+  // this thread's 4 tokens, their suffix sums within the thread
+  const int t0 = tile * DG_TILE + 4 * tid;
+  float x[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) x[e] = t0 + e < T ? dl_term<DECAY>(decay, qd, kd, bh * T + t0 + e) : 0.f;
+  float suf[4];
+  suf[3] = x[3];
+#pragma unroll
+  for (int e = 2; e >= 0; --e) suf[e] = x[e] + suf[e + 1];
+  // sum over the later threads of the wave (inclusive suffix, then less this
+  // thread's own total)
+  float v = suf[0];
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float y = __shfl_down(v, off);
+    if (lane + off < 64) v += y;
   }
   __syncthreads();
-  float R = part[tid];
-  for (int t = t1 - 1; t >= t0; --t) {
-    const float a_t = al[t];
-    R += q[t] - (DECAY == 2 ? 1.f - a_t : 1.f) * k[t];
-    dd[bh * T + t] = DECAY == 2 ? R / a_t - k[t] : R / a_t;
+  if (lane == 0) red[w] = v;   // the wave's total
+  __syncthreads();
+  float later = v - suf[0];
+  for (int ww = w + 1; ww < 4; ++ww) later += red[ww];
+  const float base = carry + later;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int t = t0 + e;
+    if (t < T) {
+      const int64_t i = bh * T + t;
+      const float R = base + suf[e];
+      dd[i] = DECAY == 2 ? R / decay[i] - kd[i] : R / decay[i];
+    }
   }
 }
 
@@ -934,9 +983,14 @@ hipError_t launch_d(const Problem& pb, const BwArgs& a, float* dS0, float* dz0, 
   bwd_rscan<D, DECAY != 0><<<dim3(unsigned(pb.BH() * PER)), dim3(256), 0, st>>>(
       a.gslot, a.lgam, a.nseg, dS0, dz0);
   bwd_pass_b<D, DECAY><<<dim3(nwg), dim3(64 * (D / 32)), 0, st>>>(a);
-  if constexpr (DECAY != 0)
-    bwd_decay_grad<DECAY><<<dim3(unsigned(pb.BH())), dim3(256), 0, st>>>(a.decay, a.qd, a.kd,
-                                                                         ddecay, a.T);
+  if constexpr (DECAY != 0) {
+    const int ntile = (a.T + DG_TILE - 1) / DG_TILE;
+    const unsigned nb = unsigned(pb.BH() * ntile);
+    bwd_decay_tile_sums<DECAY><<<dim3(nb), dim3(256), 0, st>>>(a.decay, a.qd, a.kd, a.dpart,
+                                                               a.T, ntile);
+    bwd_decay_grad<DECAY><<<dim3(nb), dim3(256), 0, st>>>(a.decay, a.qd, a.kd, a.dpart, ddecay,
+                                                          a.T, ntile);
+  }
   return hipGetLastError();
 }
 
@@ -955,12 +1009,13 @@ hipError_t launch_kind(const Problem& pb, const BwArgs& a, float* dS0, float* dz
 size_t r256(size_t b) { return (b + 255) / 256 * 256; }
 
 struct BwLayout {
-  size_t fwd, sinit, zinit, gslot, tok, lgam, qd, kd, total;
+  size_t fwd, sinit, zinit, gslot, tok, lgam, qd, kd, dpart, total;
 };
 
 // Workspace: the prefill's (for the segment start states), a copy of the
 // initial state, one gradient state per segment, two floats per token; with
-// a decay also the segments' log-decays and two more floats per token.
+// a decay also the segments' log-decays, two more floats per token and one
+// per tile of DG_TILE tokens.
 BwLayout layout_of(const Problem& pb) {
   int cps, nseg, nsub, nslot;
   mfma_split(pb, &cps, &nseg, &nsub, &nslot);
@@ -978,13 +1033,15 @@ BwLayout layout_of(const Problem& pb) {
   off += r256(BH * nseg * (D * D + D) * 4);
   l.tok = off;
   off += r256(BH * T * 2 * 4);
-  l.lgam = l.qd = l.kd = off;
+  l.lgam = l.qd = l.kd = l.dpart = off;
   if (dec) {
     off += r256(BH * nseg * 4);
     l.qd = off;
     off += r256(BH * T * 4);
     l.kd = off;
     off += r256(BH * T * 4);
+    l.dpart = off;
+    off += r256(BH * ((T + DG_TILE - 1) / DG_TILE) * 4);
   }
   l.total = off;
   return l;
@@ -1035,6 +1092,7 @@ hipError_t launch_backward_chunked(const Problem& p, const void* q, const void* 
   a.lgam = reinterpret_cast<float*>(base + l.lgam);
   a.qd = reinterpret_cast<float*>(base + l.qd);
   a.kd = reinterpret_cast<float*>(base + l.kd);
+  a.dpart = reinterpret_cast<float*>(base + l.dpart);
   a.T = pb.T;
   a.cps = cps;
   a.nseg = nseg;

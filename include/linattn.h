@@ -209,8 +209,8 @@ la_status la_prefill_stage(const la_desc* desc, int stage, const void* q, const 
  * initial state), B H nseg (d' d_v + d') fp32 (one gradient state per
  * segment) and B H T 2 fp32 (per token: the read-out's factor and the
  * divisor's gradient), each part rounded up to 256 bytes; with a decay also
- * B H nseg fp32 (each segment's log-decay) and B H T 2 fp32 (per-token
- * terms of the decay gradient).  The per-token path: B H T (d_v + 2) fp32. */
+ * B H nseg fp32 (each segment's log-decay), B H T 2 fp32 (per-token terms
+ * of the decay gradient) and B H ceil(T / 1024) fp32 (their tile totals).  The per-token path: B H T (d_v + 2) fp32. */
 la_status la_prefill_backward_workspace_size(const la_desc* desc, size_t* bytes);
 
 /* Gradients of a causal prefill for training ([lesson] Developer level and
