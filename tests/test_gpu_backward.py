@@ -231,3 +231,28 @@ def test_backward_per_token_path_16_bit(dtype, phi):
     got = run(x, do, dev, phi, True, state_grad=True)
     ref = O.prefill_gradients(x.q, x.k, x.v, do, phi=phi, gate=x.gate)
     compare(got, ref, TOL["bf16"], (dtype, phi))
+
+
+def test_backward_chunked_decay_zero_and_one():
+    """Decay values of exactly 0 (a full reset: the state before the token is
+    forgotten) keep dq, dk, dv and the initial-state gradients finite and
+    equal to the oracle's (dL/da itself is undefined there); decay 1 gives
+    the gradients of the form with no decay."""
+    dev = gpu_device()
+    B, H, T, d = 1, 2, 150, 64
+    x = I.prefill_inputs(B, H, T, d, dtype="bf16", seed=31, decay="ssd", scale=2.0 ** -0.5)
+    x.decay[:, :, [0, 37, 64, 99, 149]] = 0.0
+    do = torch.randn(B, H, T, d, generator=torch.Generator().manual_seed(32)).to(torch.bfloat16)
+    rng = np.random.default_rng(33)
+    state = (rng.standard_normal((B, H, d, d)) * 0.3, np.abs(rng.standard_normal((B, H, d))) * 3)
+    got = run(x, do, dev, "elu1", True, state=state, state_grad=True, segments=3)
+    ref = O.prefill_gradients(x.q, x.k, x.v, do, decay=x.decay, S0=state[0], z0=state[1])
+    keep = ("dq", "dk", "dv", "dS0", "dz0")
+    compare({k: got[k] for k in keep}, {k: ref[k] for k in keep}, TOL["bf16"], "decay with zeros")
+    # decay 1 against the chunked path with no decay
+    x.decay[:] = 1.0
+    a = run(x, do, dev, "elu1", True, state=state, state_grad=True, segments=3)
+    x1 = I.prefill_inputs(B, H, T, d, dtype="bf16", seed=31, scale=2.0 ** -0.5)
+    b = run(x1, do, dev, "elu1", True, state=state, state_grad=True, segments=3)
+    compare({k: a[k] for k in keep}, b, 1e-4, "decay 1 against no decay")
+    assert np.isfinite(a["ddecay"]).all()
