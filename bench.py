@@ -1,6 +1,7 @@
 """Benchmark of the causal linear attention hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]      (defaults K = 200, W = 50)
+                    [--chunk C] [--prefill-only] [--no-decode] [--no-cpu-baseline]
 
 A step is one causal elu+1 prefill over the long-context workload
 (B=1, H=8, T=102400, d_h = d' = d_v = 128, bf16 q, k, v ~ N(0, 1)/sqrt(2),
@@ -170,7 +171,7 @@ def _events(torch):
 
 
 def bench_prefill(torch, la, I, steps, warmup, normalize=True, stages=True, causal=True,
-                  mlstm=False):
+                  mlstm=False, chunk=0):
     dev = torch.device("cuda:0")
     B, H, T, d = PF["B"], PF["H"], PF["T"], PF["d"]
     x = I.prefill_inputs(B, H, T, d, dtype="bf16", seed=0, scale=PF["scale"], device=dev,
@@ -179,10 +180,11 @@ def bench_prefill(torch, la, I, steps, warmup, normalize=True, stages=True, caus
     stab = torch.empty(B, H, dtype=torch.float32, device=dev) if mlstm else None
     if mlstm:
         desc = la.make_desc(B, H, T, d, d, la._lib.LA_BF16, phi="identity", eps=PF["eps"],
-                            normalize="max1", igate=x.igate, fgate=x.fgate, stab=stab)
+                            normalize="max1", igate=x.igate, fgate=x.fgate, stab=stab,
+                            chunk=chunk)
     else:
         desc = la.make_desc(B, H, T, d, d, la._lib.LA_BF16, eps=PF["eps"], normalize=normalize,
-                            causal=causal)
+                            causal=causal, chunk=chunk)
     chunk, segments, path = la.prefill_plan(desc)
     if path != 1:
         raise RuntimeError("the long-context prefill did not take the chunked MFMA path")
@@ -351,6 +353,10 @@ def main(argv=None):
                     help="tokens per head in the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--chunk", type=int, default=0,
+                    help="prefill chunk length (0: the library's default plan)")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="time the long-context prefill alone (no variants, backward, decode)")
     a = ap.parse_args(argv)
     if a.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported "
@@ -359,7 +365,7 @@ def main(argv=None):
         return 2
 
     cpu = None
-    if not a.no_cpu_baseline:
+    if not a.no_cpu_baseline and not a.prefill_only:
         print(f"[bench] cpu baseline: oracle on {a.cpu_tokens} tokens x {PF['H']} heads",
               file=sys.stderr, flush=True)
         cpu = cpu_baseline(a.cpu_tokens)
@@ -374,7 +380,7 @@ def main(argv=None):
 
     print(f"[bench] prefill B={PF['B']} H={PF['H']} T={PF['T']} d={PF['d']}: "
           f"{a.warmup} warm-up + {a.steps} timed steps", file=sys.stderr, flush=True)
-    pf = bench_prefill(torch, la, I, a.steps, a.warmup)
+    pf = bench_prefill(torch, la, I, a.steps, a.warmup, chunk=a.chunk)
     B, H, T, d = PF["B"], PF["H"], PF["T"], PF["d"]
     TH = B * H * T
     tokens_per_s = B * T / (pf["ms"] * 1e-3)
@@ -386,20 +392,26 @@ def main(argv=None):
     tflops = flops / (pf["ms"] * 1e-3) / 1e12
     step_bytes = TH * 4 * d * 2 + 2 * state_bytes
 
-    print("[bench] prefill, normaliser-free read-out", file=sys.stderr, flush=True)
-    pf_nn = bench_prefill(torch, la, I, a.steps, a.warmup, normalize=False, stages=False)
-    print("[bench] prefill, non-causal form", file=sys.stderr, flush=True)
-    pf_nc = bench_prefill(torch, la, I, a.steps, a.warmup, stages=False, causal=False)
-    print("[bench] prefill, mLSTM gates", file=sys.stderr, flush=True)
-    pf_ml = bench_prefill(torch, la, I, a.steps, a.warmup, mlstm=True)
-    ml_bytes = step_bytes + TH * 2 * 4 + 2 * B * H * 4     # + the two gates, the stabiliser
-    print("[bench] backward", file=sys.stderr, flush=True)
-    bw_long = bench_backward(torch, la, I, B, H, T, d, 20)
-    bw_small = bench_backward(torch, la, I, 4, 8, 2048, 64, 50)
-    bw_ssd = bench_backward(torch, la, I, 2, 16, 8192, 128, 20, decay="ssd", scale=1.0)
     cp = hbm_copy(torch)
     dec = dec_big = None
-    if not a.no_decode:
+    if a.prefill_only:
+        extras = None
+    else:
+        print("[bench] prefill, normaliser-free read-out", file=sys.stderr, flush=True)
+        pf_nn = bench_prefill(torch, la, I, a.steps, a.warmup, normalize=False, stages=False,
+                              chunk=a.chunk)
+        print("[bench] prefill, non-causal form", file=sys.stderr, flush=True)
+        pf_nc = bench_prefill(torch, la, I, a.steps, a.warmup, stages=False, causal=False,
+                              chunk=a.chunk)
+        print("[bench] prefill, mLSTM gates", file=sys.stderr, flush=True)
+        pf_ml = bench_prefill(torch, la, I, a.steps, a.warmup, mlstm=True, chunk=a.chunk)
+        ml_bytes = step_bytes + TH * 2 * 4 + 2 * B * H * 4     # + the two gates, the stabiliser
+        print("[bench] backward", file=sys.stderr, flush=True)
+        bw_long = bench_backward(torch, la, I, B, H, T, d, 20)
+        bw_small = bench_backward(torch, la, I, 4, 8, 2048, 64, 50)
+        bw_ssd = bench_backward(torch, la, I, 2, 16, 8192, 128, 20, decay="ssd", scale=1.0)
+        extras = True
+    if not a.no_decode and not a.prefill_only:
         print(f"[bench] decode {DEC['N']} x {DEC['H']}, {DEC['steps']} steps", file=sys.stderr,
               flush=True)
         dec = bench_decode(torch, la, I, DEC["N"], DEC["steps"])
@@ -424,7 +436,8 @@ def main(argv=None):
                    "state_dtype": "fp32", "eps": PF["eps"], "decay": None,
                    "chunk": pf["chunk"], "segments": pf["segments"]},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": profiled_traffic(),
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": profiled_traffic() if pf["chunk"] == 32 else None,
                      "kernel": "output_kernel (la_prefill stage 3)",
                      "kernel_ms": s3, "algorithmic_bytes": stage3_bytes,
                      "measured_copy_GBs": cp["gbs"], "copy_kernel": cp["kernel"],
@@ -436,42 +449,45 @@ def main(argv=None):
         "mfma": {"algorithmic_flops": flops, "achieved": tflops, "peak": BF16_PEAK_TFLOPS,
                  "unit": "TFLOP/s", "frac": tflops / BF16_PEAK_TFLOPS},
         "cpu_baseline": cpu,
-        "normaliser_free": {
-            "workload": "the same prefill, read-out phi(q)^T S without the normaliser",
-            "ms_per_step": pf_nn["ms"], "tokens_per_s": B * T / (pf_nn["ms"] * 1e-3),
-            "GBs": step_bytes / (pf_nn["ms"] * 1e-3) / 1e9,
-            "hbm_frac": step_bytes / (pf_nn["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS},
-        "noncausal": {
-            "workload": "the same prefill in the non-causal form: the whole sequence into "
-                        "the state, then every token reads it out",
-            "ms_per_step": pf_nc["ms"], "tokens_per_s": B * T / (pf_nc["ms"] * 1e-3),
-            "GBs": step_bytes / (pf_nc["ms"] * 1e-3) / 1e9,
-            "hbm_frac": step_bytes / (pf_nc["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS},
-        "mlstm": {
-            "workload": "the same shape with the mLSTM gates: identity features, sigmoid "
-                        "forget and exponential input gates (fp32 pre-activations), "
-                        "max(|q.z|, 1) read-out, stabilised state",
-            "ms_per_step": pf_ml["ms"], "tokens_per_s": B * T / (pf_ml["ms"] * 1e-3),
-            "stage_ms": pf_ml["stage_ms"], "algorithmic_bytes": ml_bytes,
-            "GBs": ml_bytes / (pf_ml["ms"] * 1e-3) / 1e9,
-            "hbm_frac": ml_bytes / (pf_ml["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "stage3_GBs": (stage3_bytes + TH * 2 * 4) / (pf_ml["stage_ms"][2] * 1e-3) / 1e9},
-        "backward": {
-            "workload": "la_prefill_backward, elu+1, bf16 q, k, v, dout; fp32 dq, dk, dv (and "
-                        "dL/da with the SSD decay); chunked: prefill stages 1-2, dq pass, reverse "
-                        "scan, dk/dv pass (with a decay, a suffix-sum pass for dL/da)",
-            "algorithmic_bytes_per_token_head": 4 * 2 * d + 3 * 4 * d,
-            "long_context": {"B": B, "H": H, "T": T, "d": d, "ms": bw_long["ms"],
-                             "tokens_per_s": bw_long["tokens_per_s"],
-                             "GBs": bw_long["GBs"],
-                             "hbm_frac": bw_long["GBs"] / HBM_PEAK_GBS},
-            "elu_prefill_shape": {"B": 4, "H": 8, "T": 2048, "d": 64, "ms": bw_small["ms"],
-                                  "tokens_per_s": bw_small["tokens_per_s"],
-                                  "GBs": bw_small["GBs"]},
-            "ssd_prefill_shape": {"B": 2, "H": 16, "T": 8192, "d": 128, "decay": "ssd",
-                                  "ms": bw_ssd["ms"], "tokens_per_s": bw_ssd["tokens_per_s"],
-                                  "GBs": bw_ssd["GBs"]}},
     }
+    if extras:
+        res.update({
+            "normaliser_free": {
+                "workload": "the same prefill, read-out phi(q)^T S without the normaliser",
+                "ms_per_step": pf_nn["ms"], "tokens_per_s": B * T / (pf_nn["ms"] * 1e-3),
+                "GBs": step_bytes / (pf_nn["ms"] * 1e-3) / 1e9,
+                "hbm_frac": step_bytes / (pf_nn["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS},
+            "noncausal": {
+                "workload": "the same prefill in the non-causal form: the whole sequence into "
+                            "the state, then every token reads it out",
+                "ms_per_step": pf_nc["ms"], "tokens_per_s": B * T / (pf_nc["ms"] * 1e-3),
+                "GBs": step_bytes / (pf_nc["ms"] * 1e-3) / 1e9,
+                "hbm_frac": step_bytes / (pf_nc["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS},
+            "mlstm": {
+                "workload": "the same shape with the mLSTM gates: identity features, sigmoid "
+                            "forget and exponential input gates (fp32 pre-activations), "
+                            "max(|q.z|, 1) read-out, stabilised state",
+                "ms_per_step": pf_ml["ms"], "tokens_per_s": B * T / (pf_ml["ms"] * 1e-3),
+                "stage_ms": pf_ml["stage_ms"], "algorithmic_bytes": ml_bytes,
+                "GBs": ml_bytes / (pf_ml["ms"] * 1e-3) / 1e9,
+                "hbm_frac": ml_bytes / (pf_ml["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                "stage3_GBs": (stage3_bytes + TH * 2 * 4) / (pf_ml["stage_ms"][2] * 1e-3) / 1e9},
+            "backward": {
+                "workload": "la_prefill_backward, elu+1, bf16 q, k, v, dout; fp32 dq, dk, dv (and "
+                            "dL/da with the SSD decay); chunked: prefill stages 1-2, dq pass, reverse "
+                            "scan, dk/dv pass (with a decay, a suffix-sum pass for dL/da)",
+                "algorithmic_bytes_per_token_head": 4 * 2 * d + 3 * 4 * d,
+                "long_context": {"B": B, "H": H, "T": T, "d": d, "ms": bw_long["ms"],
+                                 "tokens_per_s": bw_long["tokens_per_s"],
+                                 "GBs": bw_long["GBs"],
+                                 "hbm_frac": bw_long["GBs"] / HBM_PEAK_GBS},
+                "elu_prefill_shape": {"B": 4, "H": 8, "T": 2048, "d": 64, "ms": bw_small["ms"],
+                                      "tokens_per_s": bw_small["tokens_per_s"],
+                                      "GBs": bw_small["GBs"]},
+                "ssd_prefill_shape": {"B": 2, "H": 16, "T": 8192, "d": 128, "decay": "ssd",
+                                      "ms": bw_ssd["ms"], "tokens_per_s": bw_ssd["tokens_per_s"],
+                                      "GBs": bw_ssd["GBs"]}},
+        })
     if dec is not None:
         res["decode"] = {
             "workload": "gated random-feature decode, fp32, D=64 pairs, d'=128, d_v=64",
