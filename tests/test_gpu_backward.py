@@ -246,7 +246,8 @@ def test_backward_chunked_decay_zero_and_one():
     rng = np.random.default_rng(33)
     state = (rng.standard_normal((B, H, d, d)) * 0.3, np.abs(rng.standard_normal((B, H, d))) * 3)
     got = run(x, do, dev, "elu1", True, state=state, state_grad=True, segments=3)
-    ref = O.prefill_gradients(x.q, x.k, x.v, do, decay=x.decay, S0=state[0], z0=state[1])
+    with np.errstate(divide="ignore", invalid="ignore"):   # dL/da at a = 0 is undefined
+        ref = O.prefill_gradients(x.q, x.k, x.v, do, decay=x.decay, S0=state[0], z0=state[1])
     keep = ("dq", "dk", "dv", "dS0", "dz0")
     compare({k: got[k] for k in keep}, {k: ref[k] for k in keep}, TOL["bf16"], "decay with zeros")
     # decay 1 against the chunked path with no decay
