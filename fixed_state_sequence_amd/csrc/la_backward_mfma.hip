@@ -194,6 +194,23 @@ __device__ __forceinline__ void hilo8(const char* hi, const char* lo, int row, i
   for (int e = 0; e < 8; ++e) x[e] = h[e] + l[e];
 }
 
+// The MFMA operands of one product, read together before its MFMAs are
+// issued, so that one wave per SIMD waits for the LDS once per product
+// rather than once per k-step: row `row` of a token or state tile over the
+// D / 16 k-steps (16-byte blocks 2 ks + g), or NK k-steps of 16 rows of a
+// transposed read at columns col0 .. col0 + 31.
+template <int D>
+__device__ __forceinline__ void row_ops(const char* tile, int row, int g, u32x4 (&o)[D / 16]) {
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) o[ks] = row_operand<D>(tile, row, 2 * ks + g);
+}
+
+template <int D, int NK>
+__device__ __forceinline__ void tr_ops(const char* tile, int col0, int lane, u32x4 (&o)[NK]) {
+#pragma unroll
+  for (int ks = 0; ks < NK; ++ks) o[ks] = tr_operand<D>(tile, 16 * ks, col0, lane);
+}
+
 // Raw inputs of one chunk for this thread: rows r and r + 16, block b; and
 // the decay value of token lane % 32.
 struct Raw {
@@ -418,15 +435,39 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_a(const BwArgs a) {
     };
 
     // scores P^T (rows s, columns t = n), weighted, row sums; the three
-    // hi/lo products in independent accumulators
+    // hi/lo products in independent accumulators.  phi(q) of token n (high,
+    // low) serves the numerator too.
+    // (KB k-steps have their operands read at once: all of them, or two
+    // with a decay at D = 128, where fewer registers are free)
+    constexpr int KS = D / 16, KB = DECAY && D == 128 ? 2 : KS;
+    constexpr bool EARLY = KB == KS;   // operands read before the epilogues, and kept
+    u32x4 oq[KS], oql[KS];
     f32x16 sc = zero16(), sc1 = zero16(), sc2 = zero16();
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      const u32x4 bq = row_operand<D>(smem + L::Q, perm_pos(n), 2 * ks + g);
-      const u32x4 ak = row_operand<D>(smem + L::K, perm_pos(n), 2 * ks + g);
-      sc = mfma(ak, bq, sc);
-      sc1 = mfma(row_operand<D>(smem + L::KL, perm_pos(n), 2 * ks + g), bq, sc1);
-      sc2 = mfma(ak, row_operand<D>(smem + L::QL, perm_pos(n), 2 * ks + g), sc2);
+    for (int k0 = 0; k0 < KS; k0 += KB) {
+      u32x4 ok[KB], okl[KB];
+#pragma unroll
+      for (int kk = 0; kk < KB; ++kk) {
+        oq[k0 + kk] = row_operand<D>(smem + L::Q, perm_pos(n), 2 * (k0 + kk) + g);
+        oql[k0 + kk] = row_operand<D>(smem + L::QL, perm_pos(n), 2 * (k0 + kk) + g);
+        ok[kk] = row_operand<D>(smem + L::K, perm_pos(n), 2 * (k0 + kk) + g);
+        okl[kk] = row_operand<D>(smem + L::KL, perm_pos(n), 2 * (k0 + kk) + g);
+      }
+#pragma unroll
+      for (int kk = 0; kk < KB; ++kk) {
+        sc = mfma(ok[kk], oq[k0 + kk], sc);
+        sc1 = mfma(okl[kk], oq[k0 + kk], sc1);
+        sc2 = mfma(ok[kk], oql[k0 + kk], sc2);
+      }
+    }
+    // the numerator's state and v operands, read while the scores finish
+    // (else after the epilogue, phi(q) read again: fewer live registers
+    // across it)
+    u32x4 os[KS], osl[KS], ov[2];
+    if constexpr (EARLY) {
+      tr_ops<D, KS>(smem + L::SB, 32 * w, lane, os);
+      tr_ops<D, KS>(smem + L::SBL, 32 * w, lane, osl);
+      tr_ops<D, 2>(smem + L::V, 32 * w, lane, ov);
     }
     float dsum = 0.f;
 #pragma unroll
@@ -441,16 +482,30 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_a(const BwArgs a) {
                                               : 1.f / (den + a.eps);
     u32x4 ph[2], pl[2];
     split_acc(sc, ph, pl);
+    if constexpr (!EARLY) tr_ops<D, 2>(smem + L::V, 32 * w, lane, ov);
 
     // numerator^T (rows j of block w, columns t): e^{l_t} phi(Q) S + P V
     f32x16 nu = zero16(), nu1 = zero16(), nu2 = zero16();
 #pragma unroll
-    for (int fs = 0; fs < D / 16; ++fs) {
-      const u32x4 bq = row_operand<D>(smem + L::Q, perm_pos(n), 2 * fs + g);
-      const u32x4 as = tr_operand<D>(smem + L::SB, 16 * fs, 32 * w, lane);
-      nu = mfma(as, bq, nu);
-      nu1 = mfma(tr_operand<D>(smem + L::SBL, 16 * fs, 32 * w, lane), bq, nu1);
-      nu2 = mfma(as, row_operand<D>(smem + L::QL, perm_pos(n), 2 * fs + g), nu2);
+    for (int k0 = 0; k0 < KS; k0 += KB) {
+      if constexpr (!EARLY) {
+        // read again here, KB k-steps at a time
+#pragma unroll
+        for (int kk = 0; kk < KB; ++kk) {
+          const int fs = k0 + kk;
+          oq[fs] = row_operand<D>(smem + L::Q, perm_pos(n), 2 * fs + g);
+          oql[fs] = row_operand<D>(smem + L::QL, perm_pos(n), 2 * fs + g);
+          os[fs] = tr_operand<D>(smem + L::SB, 16 * fs, 32 * w, lane);
+          osl[fs] = tr_operand<D>(smem + L::SBL, 16 * fs, 32 * w, lane);
+        }
+      }
+#pragma unroll
+      for (int kk = 0; kk < KB; ++kk) {
+        const int fs = k0 + kk;
+        nu = mfma(os[fs], oq[fs], nu);
+        nu1 = mfma(osl[fs], oq[fs], nu1);
+        nu2 = mfma(os[fs], oql[fs], nu2);
+      }
     }
     if constexpr (DECAY != 0) {
       nu *= eq;
@@ -459,9 +514,8 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_a(const BwArgs a) {
     }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const u32x4 av = tr_operand<D>(smem + L::V, 16 * ks, 32 * w, lane);
-      nu = mfma(av, ph[ks], nu);
-      nu1 = mfma(av, pl[ks], nu1);
+      nu = mfma(ov[ks], ph[ks], nu);
+      nu1 = mfma(ov[ks], pl[ks], nu1);
     }
 
     // o = num r_t; g = dout r_t (bf16 high and low tiles; with a decay also
@@ -508,30 +562,66 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_a(const BwArgs a) {
       if (vt) *reinterpret_cast<float2*>(a.tok + (bh * T + t0 + n) * 2) = make_float2(rt, h);
     }
 
-    // B^T (rows s, columns t): (g_t . v_s + h_t) beta_s e^{l_t - l_s}
+    // B^T (rows s, columns t): (g_t . v_s + h_t) beta_s e^{l_t - l_s}; g of
+    // token n (high, low) serves dq too
+    u32x4 ogh[KS], ogl[KS];
     f32x16 bs = zero16(), bs1 = zero16();
 #pragma unroll
-    for (int js = 0; js < D / 16; ++js) {
-      const u32x4 av = row_operand<D>(smem + L::V, perm_pos(n), 2 * js + g);
-      bs = mfma(av, row_operand<D>(smem + L::GH, perm_pos(n), 2 * js + g), bs);
-      bs1 = mfma(av, row_operand<D>(smem + L::GL, perm_pos(n), 2 * js + g), bs1);
+    for (int k0 = 0; k0 < KS; k0 += KB) {
+      u32x4 ovr[KB];
+#pragma unroll
+      for (int kk = 0; kk < KB; ++kk) {
+        ogh[k0 + kk] = row_operand<D>(smem + L::GH, perm_pos(n), 2 * (k0 + kk) + g);
+        ogl[k0 + kk] = row_operand<D>(smem + L::GL, perm_pos(n), 2 * (k0 + kk) + g);
+        ovr[kk] = row_operand<D>(smem + L::V, perm_pos(n), 2 * (k0 + kk) + g);
+      }
+#pragma unroll
+      for (int kk = 0; kk < KB; ++kk) {
+        bs = mfma(ovr[kk], ogh[k0 + kk], bs);
+        bs1 = mfma(ovr[kk], ogl[k0 + kk], bs1);
+      }
+    }
+    // dq's state and phi(k) operands, read while B finishes (else after the
+    // epilogue, g read again)
+    u32x4 osr[KS], oslr[KS], okt[2], oklt[2];
+    if constexpr (EARLY) {
+      row_ops<D>(smem + L::SB, 32 * w + n, g, osr);
+      row_ops<D>(smem + L::SBL, 32 * w + n, g, oslr);
+      tr_ops<D, 2>(smem + L::K, 32 * w, lane, okt);
+      tr_ops<D, 2>(smem + L::KL, 32 * w, lane, oklt);
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) bs[i] = (bs[i] + bs1[i] + h) * weight(i);
     u32x4 bh_[2], bl_[2];
     split_acc(bs, bh_, bl_);
+    if constexpr (!EARLY) {
+      tr_ops<D, 2>(smem + L::K, 32 * w, lane, okt);
+      tr_ops<D, 2>(smem + L::KL, 32 * w, lane, oklt);
+    }
 
     // dphi(q)^T (rows f of block w, columns t): e^{l_t} (S g + z h) +
     // phi(K)^T B.  S g and z h cancel in large part (their difference is
     // sum_s phi(k_s) g.(v_s - o_t)).
     f32x16 dq0 = zero16(), dq1 = zero16(), dq2 = zero16();
 #pragma unroll
-    for (int js = 0; js < D / 16; ++js) {
-      const u32x4 sh = row_operand<D>(smem + L::SB, 32 * w + n, 2 * js + g);
-      const u32x4 gh = row_operand<D>(smem + L::GH, perm_pos(n), 2 * js + g);
-      dq0 = mfma(sh, gh, dq0);
-      dq1 = mfma(row_operand<D>(smem + L::SBL, 32 * w + n, 2 * js + g), gh, dq1);
-      dq2 = mfma(sh, row_operand<D>(smem + L::GL, perm_pos(n), 2 * js + g), dq2);
+    for (int k0 = 0; k0 < KS; k0 += KB) {
+      if constexpr (!EARLY) {
+#pragma unroll
+        for (int kk = 0; kk < KB; ++kk) {
+          const int js = k0 + kk;
+          ogh[js] = row_operand<D>(smem + L::GH, perm_pos(n), 2 * js + g);
+          ogl[js] = row_operand<D>(smem + L::GL, perm_pos(n), 2 * js + g);
+          osr[js] = row_operand<D>(smem + L::SB, 32 * w + n, 2 * js + g);
+          oslr[js] = row_operand<D>(smem + L::SBL, 32 * w + n, 2 * js + g);
+        }
+      }
+#pragma unroll
+      for (int kk = 0; kk < KB; ++kk) {
+        const int js = k0 + kk;
+        dq0 = mfma(osr[js], ogh[js], dq0);
+        dq1 = mfma(oslr[js], ogh[js], dq1);
+        dq2 = mfma(osr[js], ogl[js], dq2);
+      }
     }
     if constexpr (DECAY != 0) {
       dq0 *= eq;
@@ -540,10 +630,9 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_a(const BwArgs a) {
     }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const u32x4 ak = tr_operand<D>(smem + L::K, 16 * ks, 32 * w, lane);
-      dq0 = mfma(ak, bh_[ks], dq0);
-      dq1 = mfma(ak, bl_[ks], dq1);
-      dq2 = mfma(tr_operand<D>(smem + L::KL, 16 * ks, 32 * w, lane), bh_[ks], dq2);
+      dq0 = mfma(okt[ks], bh_[ks], dq0);
+      dq1 = mfma(okt[ks], bl_[ks], dq1);
+      dq2 = mfma(oklt[ks], bh_[ks], dq2);
     }
     {
       float qdp = 0.f;   // <phi(q_t), dphi(q_t)> over this lane's features
@@ -571,28 +660,47 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_a(const BwArgs a) {
     }
 
     // the segment's gradient state: G_seg^T += (weighted g)^T phi(Q)
+    // (FB blocks of 32 columns have their operands read at once: all of
+    // them, or one with a decay at D = 128)
+    constexpr int FB = DECAY && D == 128 ? 1 : NJ;
     {
       constexpr int GA = DECAY ? L::WH : L::GH, GB = DECAY ? L::WL : L::GL;
+      u32x4 ag[2], agl[2];
+      tr_ops<D, 2>(smem + GA, 32 * w, lane, ag);
+      tr_ops<D, 2>(smem + GB, 32 * w, lane, agl);
 #pragma unroll
-      for (int fb = 0; fb < NJ; ++fb)
+      for (int f0 = 0; f0 < NJ; f0 += FB) {
+        u32x4 bq[FB][2], bql[FB][2];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const u32x4 ag = tr_operand<D>(smem + GA, 16 * ks, 32 * w, lane);
-          const u32x4 bq = tr_operand<D>(smem + L::Q, 16 * ks, 32 * fb, lane);
-          Gs[fb] = mfma(ag, bq, Gs[fb]);
-          Gs[fb] = mfma(tr_operand<D>(smem + GB, 16 * ks, 32 * w, lane), bq, Gs[fb]);
-          Gs[fb] = mfma(ag, tr_operand<D>(smem + L::QL, 16 * ks, 32 * fb, lane), Gs[fb]);
+        for (int f = 0; f < FB; ++f) {
+          tr_ops<D, 2>(smem + L::Q, 32 * (f0 + f), lane, bq[f]);
+          tr_ops<D, 2>(smem + L::QL, 32 * (f0 + f), lane, bql[f]);
         }
+#pragma unroll
+        for (int f = 0; f < FB; ++f)
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            Gs[f0 + f] = mfma(ag[ks], bq[f][ks], Gs[f0 + f]);
+            Gs[f0 + f] = mfma(agl[ks], bq[f][ks], Gs[f0 + f]);
+            Gs[f0 + f] = mfma(ag[ks], bql[f][ks], Gs[f0 + f]);
+          }
+      }
     }
     if constexpr (DECAY == 0) {
       // the state: S^T += V^T phi(K)
+      u32x4 av[2], bk[NJ][2], bkl[NJ][2];
+      tr_ops<D, 2>(smem + L::V, 32 * w, lane, av);
+#pragma unroll
+      for (int fb = 0; fb < NJ; ++fb) {
+        tr_ops<D, 2>(smem + L::K, 32 * fb, lane, bk[fb]);
+        tr_ops<D, 2>(smem + L::KL, 32 * fb, lane, bkl[fb]);
+      }
 #pragma unroll
       for (int fb = 0; fb < NJ; ++fb)
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          const u32x4 av = tr_operand<D>(smem + L::V, 16 * ks, 32 * w, lane);
-          S[fb] = mfma(av, tr_operand<D>(smem + L::K, 16 * ks, 32 * fb, lane), S[fb]);
-          S[fb] = mfma(av, tr_operand<D>(smem + L::KL, 16 * ks, 32 * fb, lane), S[fb]);
+          S[fb] = mfma(av[ks], bk[fb][ks], S[fb]);
+          S[fb] = mfma(av[ks], bkl[fb][ks], S[fb]);
         }
       __syncthreads();   // every read of the old S tile done; h visible
     } else {
@@ -614,14 +722,24 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_a(const BwArgs a) {
       __syncthreads();   // weighted keys staged
       // the state: S^T = e^{l_last} S^T + V^T (w phi(K))
       const float ec = __expf(tot);
+      u32x4 av[2];
+      tr_ops<D, 2>(smem + L::V, 32 * w, lane, av);
 #pragma unroll
-      for (int fb = 0; fb < NJ; ++fb) {
-        S[fb] *= ec;
+      for (int f0 = 0; f0 < NJ; f0 += FB) {
+        u32x4 bk[FB][2], bkl[FB][2];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const u32x4 av = tr_operand<D>(smem + L::V, 16 * ks, 32 * w, lane);
-          S[fb] = mfma(av, tr_operand<D>(smem + L::WH, 16 * ks, 32 * fb, lane), S[fb]);
-          S[fb] = mfma(av, tr_operand<D>(smem + L::WL, 16 * ks, 32 * fb, lane), S[fb]);
+        for (int f = 0; f < FB; ++f) {
+          tr_ops<D, 2>(smem + L::WH, 32 * (f0 + f), lane, bk[f]);
+          tr_ops<D, 2>(smem + L::WL, 32 * (f0 + f), lane, bkl[f]);
+        }
+#pragma unroll
+        for (int f = 0; f < FB; ++f) {
+          S[f0 + f] *= ec;
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            S[f0 + f] = mfma(av[ks], bk[f][ks], S[f0 + f]);
+            S[f0 + f] = mfma(av[ks], bkl[f][ks], S[f0 + f]);
+          }
         }
       }
     }
@@ -743,31 +861,68 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_b(const BwArgs a) {
     // key s = n: e^{l_last - l_s} to the chunk's end; beta_s
     const float es = DECAY ? __expf(tot - lam) : 1.f;
 
+    // Operands are read KB k-steps (FB 32-column blocks) at a time before
+    // their MFMAs: all of them, or two (one) with a decay at D = 128, where
+    // fewer registers are free.  With all at once, phi(k) and v of key n
+    // are kept from the scores and B for dv and dk, and the state operands
+    // of dv are read before the epilogue between.
+    constexpr int KS = D / 16, KB = DECAY && D == 128 ? 2 : KS;
+    constexpr int FB = DECAY && D == 128 ? 1 : NJ;
+    constexpr bool EARLY = KB == KS;
+    u32x4 ok[KS], okl[KS], ov[KS];
+
+    // scores A (rows t, columns s = n)
+    f32x16 at = zero16(), at1 = zero16(), at2 = zero16();
+#pragma unroll
+    for (int k0 = 0; k0 < KS; k0 += KB) {
+      u32x4 aq[KB], aql[KB];
+#pragma unroll
+      for (int kk = 0; kk < KB; ++kk) {
+        const int fs = k0 + kk;
+        aq[kk] = row_operand<D>(smem + L::Q, perm_pos(n), 2 * fs + g);
+        aql[kk] = row_operand<D>(smem + L::QL, perm_pos(n), 2 * fs + g);
+        ok[fs] = row_operand<D>(smem + L::K, perm_pos(n), 2 * fs + g);
+        okl[fs] = row_operand<D>(smem + L::KL, perm_pos(n), 2 * fs + g);
+      }
+#pragma unroll
+      for (int kk = 0; kk < KB; ++kk) {
+        const int fs = k0 + kk;
+        at = mfma(aq[kk], ok[fs], at);
+        at1 = mfma(aq[kk], okl[fs], at1);
+        at2 = mfma(aql[kk], ok[fs], at2);
+      }
+    }
+    // B (rows t, columns s): g_t . v_s + h_t
+    f32x16 bt = zero16(), bt1 = zero16();
+#pragma unroll
+    for (int k0 = 0; k0 < KS; k0 += KB) {
+      u32x4 gh[KB], gl[KB];
+#pragma unroll
+      for (int kk = 0; kk < KB; ++kk) {
+        const int js = k0 + kk;
+        gh[kk] = row_operand<D>(smem + L::GH, perm_pos(n), 2 * js + g);
+        gl[kk] = row_operand<D>(smem + L::GL, perm_pos(n), 2 * js + g);
+        ov[js] = row_operand<D>(smem + L::V, perm_pos(n), 2 * js + g);
+      }
+#pragma unroll
+      for (int kk = 0; kk < KB; ++kk) {
+        bt = mfma(gh[kk], ov[k0 + kk], bt);
+        bt1 = mfma(gl[kk], ov[k0 + kk], bt1);
+      }
+    }
+    // dv's state operands, read while B finishes
+    u32x4 os[KS], osl[KS];
+    if constexpr (EARLY) {
+      tr_ops<D, KS>(smem + L::SB, 32 * w, lane, os);
+      tr_ops<D, KS>(smem + L::SBL, 32 * w, lane, osl);
+    }
+
     // causal weights of (t, s = n): e^{l_t - l_s} for t >= s (beta_s later)
     float wt[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int t = 8 * (i >> 2) + 4 * g + (i & 3);
       wt[i] = t >= n ? (DECAY ? __expf(F[L::LAM + t] - lam) : 1.f) : 0.f;
-    }
-
-    // scores A (rows t, columns s = n)
-    f32x16 at = zero16(), at1 = zero16(), at2 = zero16();
-#pragma unroll
-    for (int fs = 0; fs < D / 16; ++fs) {
-      const u32x4 aq = row_operand<D>(smem + L::Q, perm_pos(n), 2 * fs + g);
-      const u32x4 bk = row_operand<D>(smem + L::K, perm_pos(n), 2 * fs + g);
-      at = mfma(aq, bk, at);
-      at1 = mfma(aq, row_operand<D>(smem + L::KL, perm_pos(n), 2 * fs + g), at1);
-      at2 = mfma(row_operand<D>(smem + L::QL, perm_pos(n), 2 * fs + g), bk, at2);
-    }
-    // B (rows t, columns s): g_t . v_s + h_t
-    f32x16 bt = zero16(), bt1 = zero16();
-#pragma unroll
-    for (int js = 0; js < D / 16; ++js) {
-      const u32x4 bv = row_operand<D>(smem + L::V, perm_pos(n), 2 * js + g);
-      bt = mfma(row_operand<D>(smem + L::GH, perm_pos(n), 2 * js + g), bv, bt);
-      bt1 = mfma(row_operand<D>(smem + L::GL, perm_pos(n), 2 * js + g), bv, bt1);
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -781,14 +936,30 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_b(const BwArgs a) {
 
     // dv^T / beta_s (rows j of block w, columns s): e^{l_last - l_s} G^T
     // phi(k) + g^T A
+    u32x4 ogt[2], oglt[2];
+    tr_ops<D, 2>(smem + L::GH, 32 * w, lane, ogt);
+    tr_ops<D, 2>(smem + L::GL, 32 * w, lane, oglt);
     f32x16 dv0 = zero16(), dv1 = zero16(), dv2 = zero16();
 #pragma unroll
-    for (int fs = 0; fs < D / 16; ++fs) {
-      const u32x4 ag = tr_operand<D>(smem + L::SB, 16 * fs, 32 * w, lane);
-      const u32x4 bk = row_operand<D>(smem + L::K, perm_pos(n), 2 * fs + g);
-      dv0 = mfma(ag, bk, dv0);
-      dv1 = mfma(tr_operand<D>(smem + L::SBL, 16 * fs, 32 * w, lane), bk, dv1);
-      dv2 = mfma(ag, row_operand<D>(smem + L::KL, perm_pos(n), 2 * fs + g), dv2);
+    for (int k0 = 0; k0 < KS; k0 += KB) {
+      if constexpr (!EARLY) {
+        // read again here, KB k-steps at a time
+#pragma unroll
+        for (int kk = 0; kk < KB; ++kk) {
+          const int fs = k0 + kk;
+          os[fs] = tr_operand<D>(smem + L::SB, 16 * fs, 32 * w, lane);
+          osl[fs] = tr_operand<D>(smem + L::SBL, 16 * fs, 32 * w, lane);
+          ok[fs] = row_operand<D>(smem + L::K, perm_pos(n), 2 * fs + g);
+          okl[fs] = row_operand<D>(smem + L::KL, perm_pos(n), 2 * fs + g);
+        }
+      }
+#pragma unroll
+      for (int kk = 0; kk < KB; ++kk) {
+        const int fs = k0 + kk;
+        dv0 = mfma(os[fs], ok[fs], dv0);
+        dv1 = mfma(osl[fs], ok[fs], dv1);
+        dv2 = mfma(os[fs], okl[fs], dv2);
+      }
     }
     if constexpr (DECAY != 0) {
       dv0 *= es;
@@ -797,19 +968,31 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_b(const BwArgs a) {
     }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const u32x4 gh = tr_operand<D>(smem + L::GH, 16 * ks, 32 * w, lane);
-      dv0 = mfma(gh, ah[ks], dv0);
-      dv1 = mfma(gh, al[ks], dv1);
-      dv2 = mfma(tr_operand<D>(smem + L::GL, 16 * ks, 32 * w, lane), ah[ks], dv2);
+      dv0 = mfma(ogt[ks], ah[ks], dv0);
+      dv1 = mfma(ogt[ks], al[ks], dv1);
+      dv2 = mfma(oglt[ks], ah[ks], dv2);
     }
     // dphi(k)^T / beta_s (rows f of block w, columns s): e^{l_last - l_s}
     // (G v + gz) + phi(Q)^T B; G v and gz cancel in large part
+    u32x4 oqt[2], oqlt[2];
+    tr_ops<D, 2>(smem + L::Q, 32 * w, lane, oqt);
+    tr_ops<D, 2>(smem + L::QL, 32 * w, lane, oqlt);
     f32x16 dk0 = zero16(), dk1 = zero16(), dk2 = zero16();
 #pragma unroll
-    for (int js = 0; js < D / 16; ++js) {
-      const u32x4 bv = row_operand<D>(smem + L::V, perm_pos(n), 2 * js + g);
-      dk0 = mfma(row_operand<D>(smem + L::SB, 32 * w + n, 2 * js + g), bv, dk0);
-      dk1 = mfma(row_operand<D>(smem + L::SBL, 32 * w + n, 2 * js + g), bv, dk1);
+    for (int k0 = 0; k0 < KS; k0 += KB) {
+      u32x4 sr[KB], srl[KB];
+#pragma unroll
+      for (int kk = 0; kk < KB; ++kk) {
+        const int js = k0 + kk;
+        sr[kk] = row_operand<D>(smem + L::SB, 32 * w + n, 2 * js + g);
+        srl[kk] = row_operand<D>(smem + L::SBL, 32 * w + n, 2 * js + g);
+        if constexpr (!EARLY) ov[js] = row_operand<D>(smem + L::V, perm_pos(n), 2 * js + g);
+      }
+#pragma unroll
+      for (int kk = 0; kk < KB; ++kk) {
+        dk0 = mfma(sr[kk], ov[k0 + kk], dk0);
+        dk1 = mfma(srl[kk], ov[k0 + kk], dk1);
+      }
     }
     if constexpr (DECAY != 0) {
       dk0 *= es;
@@ -817,10 +1000,9 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_b(const BwArgs a) {
     }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const u32x4 aq = tr_operand<D>(smem + L::Q, 16 * ks, 32 * w, lane);
-      dk0 = mfma(aq, bh_[ks], dk0);
-      dk1 = mfma(aq, bl_[ks], dk1);
-      dk2 = mfma(tr_operand<D>(smem + L::QL, 16 * ks, 32 * w, lane), bh_[ks], dk2);
+      dk0 = mfma(oqt[ks], bh_[ks], dk0);
+      dk1 = mfma(oqt[ks], bl_[ks], dk1);
+      dk2 = mfma(oqlt[ks], bh_[ks], dk2);
     }
     {
       float kdp = 0.f;   // <phi(k_s), dphi(k_s)> / beta_s over this lane's features
@@ -854,16 +1036,26 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_b(const BwArgs a) {
     {
       constexpr int GA = DECAY ? L::WH : L::GH, GB = DECAY ? L::WL : L::GL;
       const float ec = DECAY ? __expf(tot) : 1.f;
+      u32x4 ag[2], agl[2];
+      tr_ops<D, 2>(smem + GA, 32 * w, lane, ag);
+      tr_ops<D, 2>(smem + GB, 32 * w, lane, agl);
 #pragma unroll
-      for (int fb = 0; fb < NJ; ++fb) {
-        if constexpr (DECAY != 0) G[fb] *= ec;
+      for (int f0 = 0; f0 < NJ; f0 += FB) {
+        u32x4 bq[FB][2], bql[FB][2];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const u32x4 ag = tr_operand<D>(smem + GA, 16 * ks, 32 * w, lane);
-          const u32x4 bq = tr_operand<D>(smem + L::Q, 16 * ks, 32 * fb, lane);
-          G[fb] = mfma(ag, bq, G[fb]);
-          G[fb] = mfma(tr_operand<D>(smem + GB, 16 * ks, 32 * w, lane), bq, G[fb]);
-          G[fb] = mfma(ag, tr_operand<D>(smem + L::QL, 16 * ks, 32 * fb, lane), G[fb]);
+        for (int f = 0; f < FB; ++f) {
+          tr_ops<D, 2>(smem + L::Q, 32 * (f0 + f), lane, bq[f]);
+          tr_ops<D, 2>(smem + L::QL, 32 * (f0 + f), lane, bql[f]);
+        }
+#pragma unroll
+        for (int f = 0; f < FB; ++f) {
+          if constexpr (DECAY != 0) G[f0 + f] *= ec;
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            G[f0 + f] = mfma(ag[ks], bq[f][ks], G[f0 + f]);
+            G[f0 + f] = mfma(agl[ks], bq[f][ks], G[f0 + f]);
+            G[f0 + f] = mfma(ag[ks], bql[f][ks], G[f0 + f]);
+          }
         }
       }
     }
