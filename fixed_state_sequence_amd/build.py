@@ -35,10 +35,18 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE,
           "-Wno-unused-command-line-argument"]
 
 
+# Per-source code generation.  The gradient kernels hold about 500 registers
+# per lane, beyond the 256 architectural VGPRs, so accumulators spill into
+# AGPRs; with MFMA results formed in VGPRs (an LLVM AMDGPU option) far fewer
+# of them are copied back out for the VALU epilogues.
+EXTRA = {"la_backward_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [hipcc()] + lang + COMMON + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = ([hipcc()] + lang + COMMON + EXTRA.get(src, []) +
+           ["-c", os.path.join(CSRC, src), "-o", obj])
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
