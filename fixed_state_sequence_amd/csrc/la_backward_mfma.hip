@@ -434,15 +434,17 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_a(const BwArgs a) {
       return s <= n ? (DECAY ? F[L::BET + s] * __expf(lam - F[L::LAM + s]) : 1.f) : 0.f;
     };
 
-    // scores P^T (rows s, columns t = n), weighted, row sums; the three
-    // hi/lo products in independent accumulators.  phi(q) of token n (high,
+    // scores P^T (rows s, columns t = n), weighted, row sums.  The three
+    // hi/lo products of every product here accumulate in one chain: back to
+    // back on one accumulator they issue without stalls, and fewer
+    // accumulators leave fewer to sum and to hold.  phi(q) of token n (high,
     // low) serves the numerator too.
     // (KB k-steps have their operands read at once: all of them, or two
     // with a decay at D = 128, where fewer registers are free)
     constexpr int KS = D / 16, KB = DECAY && D == 128 ? 2 : KS;
     constexpr bool EARLY = KB == KS;   // operands read before the epilogues, and kept
     u32x4 oq[KS], oql[KS];
-    f32x16 sc = zero16(), sc1 = zero16(), sc2 = zero16();
+    f32x16 sc = zero16();
 #pragma unroll
     for (int k0 = 0; k0 < KS; k0 += KB) {
       u32x4 ok[KB], okl[KB];
@@ -456,8 +458,8 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_a(const BwArgs a) {
 #pragma unroll
       for (int kk = 0; kk < KB; ++kk) {
         sc = mfma(ok[kk], oq[k0 + kk], sc);
-        sc1 = mfma(okl[kk], oq[k0 + kk], sc1);
-        sc2 = mfma(ok[kk], oql[k0 + kk], sc2);
+        sc = mfma(okl[kk], oq[k0 + kk], sc);
+        sc = mfma(ok[kk], oql[k0 + kk], sc);
       }
     }
     // the numerator's state and v operands, read while the scores finish
@@ -472,7 +474,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_a(const BwArgs a) {
     float dsum = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      sc[i] = (sc[i] + sc1[i] + sc2[i]) * weight(i);
+      sc[i] = sc[i] * weight(i);
       dsum += sc[i];
     }
     dsum = swap_sum32(dsum);
@@ -485,7 +487,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_a(const BwArgs a) {
     if constexpr (!EARLY) tr_ops<D, 2>(smem + L::V, 32 * w, lane, ov);
 
     // numerator^T (rows j of block w, columns t): e^{l_t} phi(Q) S + P V
-    f32x16 nu = zero16(), nu1 = zero16(), nu2 = zero16();
+    f32x16 nu = zero16();
 #pragma unroll
     for (int k0 = 0; k0 < KS; k0 += KB) {
       if constexpr (!EARLY) {
@@ -503,19 +505,17 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_a(const BwArgs a) {
       for (int kk = 0; kk < KB; ++kk) {
         const int fs = k0 + kk;
         nu = mfma(os[fs], oq[fs], nu);
-        nu1 = mfma(osl[fs], oq[fs], nu1);
-        nu2 = mfma(os[fs], oql[fs], nu2);
+        nu = mfma(osl[fs], oq[fs], nu);
+        nu = mfma(os[fs], oql[fs], nu);
       }
     }
     if constexpr (DECAY != 0) {
       nu *= eq;
-      nu1 *= eq;
-      nu2 *= eq;
     }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       nu = mfma(ov[ks], ph[ks], nu);
-      nu1 = mfma(ov[ks], pl[ks], nu1);
+      nu = mfma(ov[ks], pl[ks], nu);
     }
 
     // o = num r_t; g = dout r_t (bf16 high and low tiles; with a decay also
@@ -530,7 +530,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_a(const BwArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int i = 4 * r + e;
-        hp += d4[e] * ((nu[i] + nu1[i] + nu2[i]) * rt);
+        hp += d4[e] * (nu[i] * rt);
         gv[e] = vt ? d4[e] * rt : 0.f;
       }
       uint32_t h0, h1, l0, l1;
@@ -565,7 +565,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_a(const BwArgs a) {
     // B^T (rows s, columns t): (g_t . v_s + h_t) beta_s e^{l_t - l_s}; g of
     // token n (high, low) serves dq too
     u32x4 ogh[KS], ogl[KS];
-    f32x16 bs = zero16(), bs1 = zero16();
+    f32x16 bs = zero16();
 #pragma unroll
     for (int k0 = 0; k0 < KS; k0 += KB) {
       u32x4 ovr[KB];
@@ -578,7 +578,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_a(const BwArgs a) {
 #pragma unroll
       for (int kk = 0; kk < KB; ++kk) {
         bs = mfma(ovr[kk], ogh[k0 + kk], bs);
-        bs1 = mfma(ovr[kk], ogl[k0 + kk], bs1);
+        bs = mfma(ovr[kk], ogl[k0 + kk], bs);
       }
     }
     // dq's state and phi(k) operands, read while B finishes (else after the
@@ -591,7 +591,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_a(const BwArgs a) {
       tr_ops<D, 2>(smem + L::KL, 32 * w, lane, oklt);
     }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) bs[i] = (bs[i] + bs1[i] + h) * weight(i);
+    for (int i = 0; i < 16; ++i) bs[i] = (bs[i] + h) * weight(i);
     u32x4 bh_[2], bl_[2];
     split_acc(bs, bh_, bl_);
     if constexpr (!EARLY) {
@@ -602,7 +602,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_a(const BwArgs a) {
     // dphi(q)^T (rows f of block w, columns t): e^{l_t} (S g + z h) +
     // phi(K)^T B.  S g and z h cancel in large part (their difference is
     // sum_s phi(k_s) g.(v_s - o_t)).
-    f32x16 dq0 = zero16(), dq1 = zero16(), dq2 = zero16();
+    f32x16 dqt = zero16();
 #pragma unroll
     for (int k0 = 0; k0 < KS; k0 += KB) {
       if constexpr (!EARLY) {
@@ -618,21 +618,19 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_a(const BwArgs a) {
 #pragma unroll
       for (int kk = 0; kk < KB; ++kk) {
         const int js = k0 + kk;
-        dq0 = mfma(osr[js], ogh[js], dq0);
-        dq1 = mfma(oslr[js], ogh[js], dq1);
-        dq2 = mfma(osr[js], ogl[js], dq2);
+        dqt = mfma(osr[js], ogh[js], dqt);
+        dqt = mfma(oslr[js], ogh[js], dqt);
+        dqt = mfma(osr[js], ogl[js], dqt);
       }
     }
     if constexpr (DECAY != 0) {
-      dq0 *= eq;
-      dq1 *= eq;
-      dq2 *= eq;
+      dqt *= eq;
     }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      dq0 = mfma(okt[ks], bh_[ks], dq0);
-      dq1 = mfma(okt[ks], bl_[ks], dq1);
-      dq2 = mfma(oklt[ks], bh_[ks], dq2);
+      dqt = mfma(okt[ks], bh_[ks], dqt);
+      dqt = mfma(okt[ks], bl_[ks], dqt);
+      dqt = mfma(oklt[ks], bh_[ks], dqt);
     }
     {
       float qdp = 0.f;   // <phi(q_t), dphi(q_t)> over this lane's features
@@ -646,7 +644,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_a(const BwArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * r + e;
-          const float dphi = dq0[i] + dq1[i] + dq2[i] + eq * z4[e] * h;
+          const float dphi = dqt[i] + eq * z4[e] * h;
           // elu+1 has slope 1 above 0 and e^x = phi(x) below: min(phi, 1)
           o4[e] = dphi * fminf(p4[e], 1.f);
           qdp += p4[e] * dphi;
@@ -872,7 +870,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_b(const BwArgs a) {
     u32x4 ok[KS], okl[KS], ov[KS];
 
     // scores A (rows t, columns s = n)
-    f32x16 at = zero16(), at1 = zero16(), at2 = zero16();
+    f32x16 at = zero16();
 #pragma unroll
     for (int k0 = 0; k0 < KS; k0 += KB) {
       u32x4 aq[KB], aql[KB];
@@ -888,12 +886,12 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_b(const BwArgs a) {
       for (int kk = 0; kk < KB; ++kk) {
         const int fs = k0 + kk;
         at = mfma(aq[kk], ok[fs], at);
-        at1 = mfma(aq[kk], okl[fs], at1);
-        at2 = mfma(aql[kk], ok[fs], at2);
+        at = mfma(aq[kk], okl[fs], at);
+        at = mfma(aql[kk], ok[fs], at);
       }
     }
     // B (rows t, columns s): g_t . v_s + h_t
-    f32x16 bt = zero16(), bt1 = zero16();
+    f32x16 bt = zero16();
 #pragma unroll
     for (int k0 = 0; k0 < KS; k0 += KB) {
       u32x4 gh[KB], gl[KB];
@@ -907,7 +905,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_b(const BwArgs a) {
 #pragma unroll
       for (int kk = 0; kk < KB; ++kk) {
         bt = mfma(gh[kk], ov[k0 + kk], bt);
-        bt1 = mfma(gl[kk], ov[k0 + kk], bt1);
+        bt = mfma(gl[kk], ov[k0 + kk], bt);
       }
     }
     // dv's state operands, read while B finishes
@@ -927,8 +925,8 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_b(const BwArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int t = 8 * (i >> 2) + 4 * g + (i & 3);
-      at[i] = (at[i] + at1[i] + at2[i]) * wt[i];
-      bt[i] = (bt[i] + bt1[i] + F[L::HT + t]) * wt[i];
+      at[i] = at[i] * wt[i];
+      bt[i] = (bt[i] + F[L::HT + t]) * wt[i];
     }
     u32x4 ah[2], al[2], bh_[2], bl_[2];
     split_acc(at, ah, al);
@@ -939,7 +937,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_b(const BwArgs a) {
     u32x4 ogt[2], oglt[2];
     tr_ops<D, 2>(smem + L::GH, 32 * w, lane, ogt);
     tr_ops<D, 2>(smem + L::GL, 32 * w, lane, oglt);
-    f32x16 dv0 = zero16(), dv1 = zero16(), dv2 = zero16();
+    f32x16 dvt = zero16();
 #pragma unroll
     for (int k0 = 0; k0 < KS; k0 += KB) {
       if constexpr (!EARLY) {
@@ -956,28 +954,26 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_b(const BwArgs a) {
 #pragma unroll
       for (int kk = 0; kk < KB; ++kk) {
         const int fs = k0 + kk;
-        dv0 = mfma(os[fs], ok[fs], dv0);
-        dv1 = mfma(osl[fs], ok[fs], dv1);
-        dv2 = mfma(os[fs], okl[fs], dv2);
+        dvt = mfma(os[fs], ok[fs], dvt);
+        dvt = mfma(osl[fs], ok[fs], dvt);
+        dvt = mfma(os[fs], okl[fs], dvt);
       }
     }
     if constexpr (DECAY != 0) {
-      dv0 *= es;
-      dv1 *= es;
-      dv2 *= es;
+      dvt *= es;
     }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      dv0 = mfma(ogt[ks], ah[ks], dv0);
-      dv1 = mfma(ogt[ks], al[ks], dv1);
-      dv2 = mfma(oglt[ks], ah[ks], dv2);
+      dvt = mfma(ogt[ks], ah[ks], dvt);
+      dvt = mfma(ogt[ks], al[ks], dvt);
+      dvt = mfma(oglt[ks], ah[ks], dvt);
     }
     // dphi(k)^T / beta_s (rows f of block w, columns s): e^{l_last - l_s}
     // (G v + gz) + phi(Q)^T B; G v and gz cancel in large part
     u32x4 oqt[2], oqlt[2];
     tr_ops<D, 2>(smem + L::Q, 32 * w, lane, oqt);
     tr_ops<D, 2>(smem + L::QL, 32 * w, lane, oqlt);
-    f32x16 dk0 = zero16(), dk1 = zero16(), dk2 = zero16();
+    f32x16 dkt = zero16();
 #pragma unroll
     for (int k0 = 0; k0 < KS; k0 += KB) {
       u32x4 sr[KB], srl[KB];
@@ -990,19 +986,18 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_b(const BwArgs a) {
       }
 #pragma unroll
       for (int kk = 0; kk < KB; ++kk) {
-        dk0 = mfma(sr[kk], ov[k0 + kk], dk0);
-        dk1 = mfma(srl[kk], ov[k0 + kk], dk1);
+        dkt = mfma(sr[kk], ov[k0 + kk], dkt);
+        dkt = mfma(srl[kk], ov[k0 + kk], dkt);
       }
     }
     if constexpr (DECAY != 0) {
-      dk0 *= es;
-      dk1 *= es;
+      dkt *= es;
     }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      dk0 = mfma(oqt[ks], bh_[ks], dk0);
-      dk1 = mfma(oqt[ks], bl_[ks], dk1);
-      dk2 = mfma(oqlt[ks], bh_[ks], dk2);
+      dkt = mfma(oqt[ks], bh_[ks], dkt);
+      dkt = mfma(oqt[ks], bl_[ks], dkt);
+      dkt = mfma(oqlt[ks], bh_[ks], dkt);
     }
     {
       float kdp = 0.f;   // <phi(k_s), dphi(k_s)> / beta_s over this lane's features
@@ -1016,8 +1011,8 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_b(const BwArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * r + e;
-          v4[e] = bet * (dv0[i] + dv1[i] + dv2[i]);
-          const float raw_ = dk0[i] + dk1[i] + dk2[i] + es * z4[e];
+          v4[e] = bet * dvt[i];
+          const float raw_ = dkt[i] + es * z4[e];
           o4[e] = bet * raw_ * fminf(p4[e], 1.f);
           kdp += p4[e] * raw_;
         }
