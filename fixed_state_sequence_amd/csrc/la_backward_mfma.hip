@@ -859,61 +859,45 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_b(const BwArgs a) {
     // key s = n: e^{l_last - l_s} to the chunk's end; beta_s
     const float es = DECAY ? __expf(tot - lam) : 1.f;
 
-    // Operands are read KB k-steps (FB 32-column blocks) at a time before
-    // their MFMAs: all of them, or two (one) with a decay at D = 128, where
-    // fewer registers are free.  With all at once, phi(k) and v of key n
-    // are kept from the scores and B for dv and dk, and the state operands
-    // of dv are read before the epilogue between.
-    constexpr int KS = D / 16, KB = DECAY && D == 128 ? 2 : KS;
-    constexpr int FB = DECAY && D == 128 ? 1 : NJ;
-    constexpr bool EARLY = KB == KS;
+    // Every product's operands are read before its MFMAs (pass B holds
+    // fewer values than pass A: all of them fit, with a decay too); phi(k)
+    // and v of key n are kept from the scores and B for dv and dk, and the
+    // state operands of dv are read before the epilogue between.
+    constexpr int KS = D / 16;
     u32x4 ok[KS], okl[KS], ov[KS];
 
     // scores A (rows t, columns s = n)
     f32x16 at = zero16();
+    {
+      u32x4 aq[KS], aql[KS];
+      row_ops<D>(smem + L::Q, perm_pos(n), g, aq);
+      row_ops<D>(smem + L::QL, perm_pos(n), g, aql);
+      row_ops<D>(smem + L::K, perm_pos(n), g, ok);
+      row_ops<D>(smem + L::KL, perm_pos(n), g, okl);
 #pragma unroll
-    for (int k0 = 0; k0 < KS; k0 += KB) {
-      u32x4 aq[KB], aql[KB];
-#pragma unroll
-      for (int kk = 0; kk < KB; ++kk) {
-        const int fs = k0 + kk;
-        aq[kk] = row_operand<D>(smem + L::Q, perm_pos(n), 2 * fs + g);
-        aql[kk] = row_operand<D>(smem + L::QL, perm_pos(n), 2 * fs + g);
-        ok[fs] = row_operand<D>(smem + L::K, perm_pos(n), 2 * fs + g);
-        okl[fs] = row_operand<D>(smem + L::KL, perm_pos(n), 2 * fs + g);
-      }
-#pragma unroll
-      for (int kk = 0; kk < KB; ++kk) {
-        const int fs = k0 + kk;
-        at = mfma(aq[kk], ok[fs], at);
-        at = mfma(aq[kk], okl[fs], at);
-        at = mfma(aql[kk], ok[fs], at);
+      for (int fs = 0; fs < KS; ++fs) {
+        at = mfma(aq[fs], ok[fs], at);
+        at = mfma(aq[fs], okl[fs], at);
+        at = mfma(aql[fs], ok[fs], at);
       }
     }
     // B (rows t, columns s): g_t . v_s + h_t
     f32x16 bt = zero16();
+    {
+      u32x4 gh[KS], gl[KS];
+      row_ops<D>(smem + L::GH, perm_pos(n), g, gh);
+      row_ops<D>(smem + L::GL, perm_pos(n), g, gl);
+      row_ops<D>(smem + L::V, perm_pos(n), g, ov);
 #pragma unroll
-    for (int k0 = 0; k0 < KS; k0 += KB) {
-      u32x4 gh[KB], gl[KB];
-#pragma unroll
-      for (int kk = 0; kk < KB; ++kk) {
-        const int js = k0 + kk;
-        gh[kk] = row_operand<D>(smem + L::GH, perm_pos(n), 2 * js + g);
-        gl[kk] = row_operand<D>(smem + L::GL, perm_pos(n), 2 * js + g);
-        ov[js] = row_operand<D>(smem + L::V, perm_pos(n), 2 * js + g);
-      }
-#pragma unroll
-      for (int kk = 0; kk < KB; ++kk) {
-        bt = mfma(gh[kk], ov[k0 + kk], bt);
-        bt = mfma(gl[kk], ov[k0 + kk], bt);
+      for (int js = 0; js < KS; ++js) {
+        bt = mfma(gh[js], ov[js], bt);
+        bt = mfma(gl[js], ov[js], bt);
       }
     }
     // dv's state operands, read while B finishes
     u32x4 os[KS], osl[KS];
-    if constexpr (EARLY) {
-      tr_ops<D, KS>(smem + L::SB, 32 * w, lane, os);
-      tr_ops<D, KS>(smem + L::SBL, 32 * w, lane, osl);
-    }
+    tr_ops<D, KS>(smem + L::SB, 32 * w, lane, os);
+    tr_ops<D, KS>(smem + L::SBL, 32 * w, lane, osl);
 
     // causal weights of (t, s = n): e^{l_t - l_s} for t >= s (beta_s later)
     float wt[16];
@@ -939,25 +923,10 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_b(const BwArgs a) {
     tr_ops<D, 2>(smem + L::GL, 32 * w, lane, oglt);
     f32x16 dvt = zero16();
 #pragma unroll
-    for (int k0 = 0; k0 < KS; k0 += KB) {
-      if constexpr (!EARLY) {
-        // read again here, KB k-steps at a time
-#pragma unroll
-        for (int kk = 0; kk < KB; ++kk) {
-          const int fs = k0 + kk;
-          os[fs] = tr_operand<D>(smem + L::SB, 16 * fs, 32 * w, lane);
-          osl[fs] = tr_operand<D>(smem + L::SBL, 16 * fs, 32 * w, lane);
-          ok[fs] = row_operand<D>(smem + L::K, perm_pos(n), 2 * fs + g);
-          okl[fs] = row_operand<D>(smem + L::KL, perm_pos(n), 2 * fs + g);
-        }
-      }
-#pragma unroll
-      for (int kk = 0; kk < KB; ++kk) {
-        const int fs = k0 + kk;
-        dvt = mfma(os[fs], ok[fs], dvt);
-        dvt = mfma(osl[fs], ok[fs], dvt);
-        dvt = mfma(os[fs], okl[fs], dvt);
-      }
+    for (int fs = 0; fs < KS; ++fs) {
+      dvt = mfma(os[fs], ok[fs], dvt);
+      dvt = mfma(osl[fs], ok[fs], dvt);
+      dvt = mfma(os[fs], okl[fs], dvt);
     }
     if constexpr (DECAY != 0) {
       dvt *= es;
@@ -974,20 +943,14 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_b(const BwArgs a) {
     tr_ops<D, 2>(smem + L::Q, 32 * w, lane, oqt);
     tr_ops<D, 2>(smem + L::QL, 32 * w, lane, oqlt);
     f32x16 dkt = zero16();
+    {
+      u32x4 sr[KS], srl[KS];
+      row_ops<D>(smem + L::SB, 32 * w + n, g, sr);
+      row_ops<D>(smem + L::SBL, 32 * w + n, g, srl);
 #pragma unroll
-    for (int k0 = 0; k0 < KS; k0 += KB) {
-      u32x4 sr[KB], srl[KB];
-#pragma unroll
-      for (int kk = 0; kk < KB; ++kk) {
-        const int js = k0 + kk;
-        sr[kk] = row_operand<D>(smem + L::SB, 32 * w + n, 2 * js + g);
-        srl[kk] = row_operand<D>(smem + L::SBL, 32 * w + n, 2 * js + g);
-        if constexpr (!EARLY) ov[js] = row_operand<D>(smem + L::V, perm_pos(n), 2 * js + g);
-      }
-#pragma unroll
-      for (int kk = 0; kk < KB; ++kk) {
-        dkt = mfma(sr[kk], ov[k0 + kk], dkt);
-        dkt = mfma(srl[kk], ov[k0 + kk], dkt);
+      for (int js = 0; js < KS; ++js) {
+        dkt = mfma(sr[js], ov[js], dkt);
+        dkt = mfma(srl[js], ov[js], dkt);
       }
     }
     if constexpr (DECAY != 0) {
@@ -1031,26 +994,22 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_b(const BwArgs a) {
     {
       constexpr int GA = DECAY ? L::WH : L::GH, GB = DECAY ? L::WL : L::GL;
       const float ec = DECAY ? __expf(tot) : 1.f;
-      u32x4 ag[2], agl[2];
+      u32x4 ag[2], agl[2], bq[NJ][2], bql[NJ][2];
       tr_ops<D, 2>(smem + GA, 32 * w, lane, ag);
       tr_ops<D, 2>(smem + GB, 32 * w, lane, agl);
 #pragma unroll
-      for (int f0 = 0; f0 < NJ; f0 += FB) {
-        u32x4 bq[FB][2], bql[FB][2];
+      for (int fb = 0; fb < NJ; ++fb) {
+        tr_ops<D, 2>(smem + L::Q, 32 * fb, lane, bq[fb]);
+        tr_ops<D, 2>(smem + L::QL, 32 * fb, lane, bql[fb]);
+      }
 #pragma unroll
-        for (int f = 0; f < FB; ++f) {
-          tr_ops<D, 2>(smem + L::Q, 32 * (f0 + f), lane, bq[f]);
-          tr_ops<D, 2>(smem + L::QL, 32 * (f0 + f), lane, bql[f]);
-        }
+      for (int fb = 0; fb < NJ; ++fb) {
+        if constexpr (DECAY != 0) G[fb] *= ec;
 #pragma unroll
-        for (int f = 0; f < FB; ++f) {
-          if constexpr (DECAY != 0) G[f0 + f] *= ec;
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            G[f0 + f] = mfma(ag[ks], bq[f][ks], G[f0 + f]);
-            G[f0 + f] = mfma(agl[ks], bq[f][ks], G[f0 + f]);
-            G[f0 + f] = mfma(ag[ks], bql[f][ks], G[f0 + f]);
-          }
+        for (int ks = 0; ks < 2; ++ks) {
+          G[fb] = mfma(ag[ks], bq[fb][ks], G[fb]);
+          G[fb] = mfma(agl[ks], bq[fb][ks], G[fb]);
+          G[fb] = mfma(ag[ks], bql[fb][ks], G[fb]);
         }
       }
     }
