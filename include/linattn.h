@@ -242,7 +242,8 @@ la_status la_prefill_backward_workspace_size(const la_desc* desc, size_t* bytes)
  * for any other chunk).  Otherwise one workgroup walks each (b, h) sequence token by
  * token, forward then backward.  `workspace` holds
  * la_prefill_backward_workspace_size() bytes; its contents on return are
- * scratch. */
+ * scratch.  T = 0: L is an empty sum; dS0 and dz0 (if given) are written as
+ * zeros and nothing else is touched (the workspace size is 0). */
 la_status la_prefill_backward(const la_desc* desc, const void* q, const void* k, const void* v,
                               const float* S0, const float* z0, const void* dout, float* dq,
                               float* dk, float* dv, float* ddecay, float* dS0, float* dz0,

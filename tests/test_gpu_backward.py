@@ -4,6 +4,8 @@ by element: dq, dk, dv, the decay or gate gradient and the initial-state
 gradients.  Bars: 1e-4 (fp32 inputs), 2e-2 (bf16 inputs), max |gpu - oracle|
 / rms(oracle) per gradient.
 """
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -257,3 +259,31 @@ def test_backward_chunked_decay_zero_and_one():
     b = run(x1, do, dev, "elu1", True, state=state, state_grad=True, segments=3)
     compare({k: a[k] for k in keep}, b, 1e-4, "decay 1 against no decay")
     assert np.isfinite(a["ddecay"]).all()
+
+
+@pytest.mark.parametrize("decay", [None, "ssd"])
+def test_backward_empty_sequence(decay):
+    """T = 0: L is an empty sum, so dL/dS0 and dL/dz0 are zero and there is
+    nothing else to write.  Called through the C ABI with dS0 and dz0 filled
+    with NaN beforehand, so an output left unwritten fails; the workspace size
+    is 0."""
+    dev = gpu_device()
+    B, H, d = 2, 3, 64
+    L = la._lib.lib()
+    one = torch.ones(1, device=dev)   # a valid pointer for the (empty) decay arrays
+    desc = la.make_desc(B, H, 0, d, d, la._lib.LA_BF16, decay=one if decay else None)
+    S0 = torch.randn(B, H, d, d, device=dev)
+    z0 = torch.rand(B, H, d, device=dev)
+    dS0 = torch.full((B, H, d, d), float("nan"), device=dev)
+    dz0 = torch.full((B, H, d), float("nan"), device=dev)
+    dd = torch.full((1,), float("nan"), device=dev) if decay else None
+    n = ctypes.c_size_t(1)
+    la._lib.check(L.la_prefill_backward_workspace_size(ctypes.byref(desc), ctypes.byref(n)))
+    assert n.value == 0
+    p = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+    la._lib.check(L.la_prefill_backward(ctypes.byref(desc), None, None, None, p(S0), p(z0), None,
+                                        None, None, None, p(dd), p(dS0), p(dz0), None, 0,
+                                        ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)))
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(dS0).item() == 0 and torch.count_nonzero(dz0).item() == 0
+    assert not torch.isnan(dS0).any() and not torch.isnan(dz0).any()
