@@ -216,10 +216,11 @@ __device__ __forceinline__ void tr_ops(const char* tile, int col0, int lane, u32
 struct Raw {
   u32x4 q[2], k[2], v[2];
   f32x4 d[2][2];   // dout as fp32
+  float2 th[2];    // pass B: r_t and h_t of rows r and r + 16 (from pass A)
   float al;
 };
 
-template <int D, int DECAY>
+template <int D, int DECAY, bool TOK = false>
 __device__ __forceinline__ void load_raw(const BwArgs& a, int64_t bh, int t0, int tid, Raw& x) {
   using L = BL<D, DECAY>;
   const int b = tid % L::BPR;
@@ -229,6 +230,7 @@ __device__ __forceinline__ void load_raw(const BwArgs& a, int64_t bh, int t0, in
     const int r = tid / L::BPR + 16 * rr;
     const int64_t t = min(int64_t(t0 + r), T - 1);
     const int64_t row = (bh * T + t) * D + 8 * b;
+    if constexpr (TOK) x.th[rr] = *reinterpret_cast<const float2*>(a.tok + (bh * T + t) * 2);
     x.q[rr] = *reinterpret_cast<const u32x4*>(a.q + row);
     x.k[rr] = *reinterpret_cast<const u32x4*>(a.k + row);
     x.v[rr] = *reinterpret_cast<const u32x4*>(a.v + row);
@@ -349,12 +351,7 @@ __device__ __forceinline__ void stage(const BwArgs& a, int64_t bh, int t0, int t
       part = row_sum<L::BPR>(part);
       if (b == 0) F[L::DI + r] = part;
     } else {
-      float rt = 0.f, ht = 0.f;
-      if (valid) {
-        const float2 th = *reinterpret_cast<const float2*>(a.tok + (bh * a.T + t0 + r) * 2);
-        rt = th.x;
-        ht = th.y;
-      }
+      const float rt = valid ? x.th[rr].x : 0.f, ht = valid ? x.th[rr].y : 0.f;
       float gv[8] = {d0[0] * rt, d0[1] * rt, d0[2] * rt, d0[3] * rt,
                      d1[0] * rt, d1[1] * rt, d1[2] * rt, d1[3] * rt};
       const u32x4 gh = pack8(gv);
@@ -848,13 +845,13 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_b(const BwArgs a) {
   __syncthreads();
 
   Raw raw;
-  if (c0 < c1) load_raw<D, DECAY>(a, bh, (c1 - 1) * BCH, tid, raw);
+  if (c0 < c1) load_raw<D, DECAY, true>(a, bh, (c1 - 1) * BCH, tid, raw);
   for (int c = c1 - 1; c >= c0; --c) {
     const int t0 = c * BCH;
     float lam, bet, tot;
     stage<D, DECAY, false>(a, bh, t0, tid, raw, smem, lam, bet, tot);
     __syncthreads();   // tiles, h, gz increments, decay
-    if (c - 1 >= c0) load_raw<D, DECAY>(a, bh, t0 - BCH, tid, raw);
+    if (c - 1 >= c0) load_raw<D, DECAY, true>(a, bh, t0 - BCH, tid, raw);
     const bool vs = t0 + n < T;
     // key s = n: e^{l_last - l_s} to the chunk's end; beta_s
     const float es = DECAY ? __expf(tot - lam) : 1.f;
