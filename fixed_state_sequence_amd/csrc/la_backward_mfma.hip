@@ -471,7 +471,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_a(const BwArgs a) {
     float dsum = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      sc[i] = sc[i] * weight(i);
+      sc[i] *= weight(i);
       dsum += sc[i];
     }
     dsum = swap_sum32(dsum);
@@ -506,9 +506,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_a(const BwArgs a) {
         nu = mfma(os[fs], oql[fs], nu);
       }
     }
-    if constexpr (DECAY != 0) {
-      nu *= eq;
-    }
+    if constexpr (DECAY != 0) nu *= eq;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       nu = mfma(ov[ks], ph[ks], nu);
@@ -620,9 +618,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_a(const BwArgs a) {
         dqt = mfma(osr[js], ogl[js], dqt);
       }
     }
-    if constexpr (DECAY != 0) {
-      dqt *= eq;
-    }
+    if constexpr (DECAY != 0) dqt *= eq;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       dqt = mfma(okt[ks], bh_[ks], dqt);
@@ -906,7 +902,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_b(const BwArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int t = 8 * (i >> 2) + 4 * g + (i & 3);
-      at[i] = at[i] * wt[i];
+      at[i] *= wt[i];
       bt[i] = (bt[i] + F[L::HT + t]) * wt[i];
     }
     u32x4 ah[2], al[2], bh_[2], bl_[2];
@@ -925,9 +921,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_b(const BwArgs a) {
       dvt = mfma(osl[fs], ok[fs], dvt);
       dvt = mfma(os[fs], okl[fs], dvt);
     }
-    if constexpr (DECAY != 0) {
-      dvt *= es;
-    }
+    if constexpr (DECAY != 0) dvt *= es;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       dvt = mfma(ogt[ks], ah[ks], dvt);
@@ -950,9 +944,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_b(const BwArgs a) {
         dkt = mfma(srl[js], ov[js], dkt);
       }
     }
-    if constexpr (DECAY != 0) {
-      dkt *= es;
-    }
+    if constexpr (DECAY != 0) dkt *= es;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       dkt = mfma(oqt[ks], bh_[ks], dkt);
