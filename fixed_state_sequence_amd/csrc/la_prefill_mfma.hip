@@ -1089,10 +1089,15 @@ hipError_t launch3(const PfArgs& a, int64_t BH, int stage, hipStream_t st) {
   } else if (stage == 2) {
     if (!scan) return hipSuccess;
     const int per_bh = (D * D + D + 255) / 256;
-    if (a.nslot <= 32)
-      segment_scan_kernel<D, 32, DECAY == 3><<<dim3(unsigned(BH * per_bh)), dim3(256), 0, st>>>(a);
+    // up to 64 slots in flight at once; 32 with the mLSTM gates, whose
+    // stabilisers take a third set of registers (64 would leave one wave
+    // per SIMD)
+    if constexpr (DECAY == 3)
+      segment_scan_kernel<D, 32, true><<<dim3(unsigned(BH * per_bh)), dim3(256), 0, st>>>(a);
+    else if (a.nslot <= 32)
+      segment_scan_kernel<D, 32, false><<<dim3(unsigned(BH * per_bh)), dim3(256), 0, st>>>(a);
     else
-      segment_scan_kernel<D, 64, DECAY == 3><<<dim3(unsigned(BH * per_bh)), dim3(256), 0, st>>>(a);
+      segment_scan_kernel<D, 64, false><<<dim3(unsigned(BH * per_bh)), dim3(256), 0, st>>>(a);
   } else if (a.nc) {
     if constexpr (DECAY != 0) return hipErrorInvalidValue;   // rejected on the host
     else output_kernel<D, C, 0, DT, true><<<dim3(unsigned(BH * a.nseg)), dim3(2 * G::NT), 0, st>>>(a);
