@@ -229,3 +229,12 @@ def test_backward_checks():
     assert bw(desc(**base), dS0=FAKE) == "LA_EINVAL"
     assert bw(desc(**base), nws=n.value - 1) == "LA_EINVAL"
     assert "workspace" in L.la_last_error().decode()
+
+
+def test_backward_empty_sequence_needs_no_workspace():
+    """T = 0 (an empty sum): no workspace, on either path."""
+    n = ctypes.c_size_t(1)
+    for dtype in (_lib.LA_BF16, _lib.LA_F32):
+        d = desc(T=0, d_h=64, d_v=64, dtype_code=dtype)
+        assert status(L.la_prefill_backward_workspace_size(ctypes.byref(d), ctypes.byref(n))) == "LA_OK"
+        assert n.value == 0
