@@ -59,6 +59,22 @@ def _need(t, name, device=None, dtype=None, shape=None):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
+def _check_W(W, phi, H, d_h, device):
+    """The random-feature matrix of every head: [H, rff_D, d_h] fp32,
+    contiguous, on q's device.  The kernels index it by head and input
+    feature, so any other shape would be read out of bounds."""
+    torch = _torch()
+    if phi != "rff":
+        if W is not None:
+            raise ValueError(f"W is only used by the random-feature map, not {phi!r}")
+        return
+    if W is None:
+        raise ValueError("phi='rff' needs W [H, rff_D, d_h]")
+    if W.dim() != 3 or W.shape[0] != H or W.shape[2] != d_h or W.shape[1] < 1:
+        raise ValueError(f"W has shape {tuple(W.shape)}, expected ({H}, rff_D, {d_h})")
+    _need(W, "W", device=device, dtype=torch.float32)
+
+
 _NORMS = {True: _lib.LA_NORM_SUM, "sum": _lib.LA_NORM_SUM, False: _lib.LA_NORM_NONE,
           "none": _lib.LA_NORM_NONE, "max1": _lib.LA_NORM_MAX1}
 
@@ -156,8 +172,7 @@ def _prefill_desc(q, k, v, phi, W, decay, gate, eps, chunk, segments, out_dtype=
     _need(k, "k", shape=(B, H, T, d_h))
     d_v = v.shape[-1]
     _need(v, "v", shape=(B, H, T, d_v))
-    if W is not None:
-        _need(W, "W", device=q.device, dtype=torch.float32)
+    _check_W(W, phi, H, d_h, q.device)
     for a, n in ((decay, "decay"), (gate, "gate"), (igate, "igate"), (fgate, "fgate")):
         if a is not None:
             _need(a, n, device=q.device, dtype=torch.float32, shape=(B, H, T))
@@ -205,7 +220,10 @@ def prefill(q, k, v, *, phi: str = "elu1", W=None, decay=None, gate=None, eps: f
     torch = _torch()
     out_dtype = out_dtype or q.dtype
     mlstm = igate is not None or fgate is not None
+    if q.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, T, d]")
     B, H = q.shape[0], q.shape[1]
+    _check_W(W, phi, H, q.shape[-1], q.device)
     if state is None:
         dp = feature_dim(q.shape[-1], phi, W.shape[-2] if W is not None else 0)
         st = state_init(B, H, dp, v.shape[-1], q.device, stab=mlstm)
@@ -311,8 +329,7 @@ def decode_step(q, k, v, S, z, *, phi: str = "elu1", W=None, decay=None, gate=No
     d_v = v.shape[-1]
     _need(k, "k", shape=(B, H, d_h))
     _need(v, "v", shape=(B, H, d_v))
-    if W is not None:
-        _need(W, "W", device=q.device, dtype=torch.float32)
+    _check_W(W, phi, H, d_h, q.device)
     for a, n in ((decay, "decay"), (gate, "gate"), (igate, "igate"), (fgate, "fgate"),
                  (stab, "stab")):
         if a is not None:

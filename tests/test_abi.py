@@ -238,3 +238,23 @@ def test_backward_empty_sequence_needs_no_workspace():
         d = desc(T=0, d_h=64, d_v=64, dtype_code=dtype)
         assert status(L.la_prefill_backward_workspace_size(ctypes.byref(d), ctypes.byref(n))) == "LA_OK"
         assert n.value == 0
+
+
+def test_mis_shaped_rff_projection_is_rejected_before_any_launch():
+    # The decode and per-token kernels index W by head and input feature:
+    # [H, rff_D, d_h].  Any other shape must be refused in the binding (the C
+    # ABI sees only a pointer), before a tensor is read.
+    import torch
+    H, d_h = 16, 64
+    for bad in (torch.zeros(H - 1, 64, d_h), torch.zeros(H, 64, d_h - 1), torch.zeros(64, d_h),
+                torch.zeros(H, 0, d_h), torch.zeros(1, H, 64, d_h)):
+        with pytest.raises(ValueError, match="W has shape"):
+            la._check_W(bad, "rff", H, d_h, None)
+    with pytest.raises(ValueError, match="needs W"):
+        la._check_W(None, "rff", H, d_h, None)
+    with pytest.raises(ValueError, match="only used by the random-feature map"):
+        la._check_W(torch.zeros(H, 64, d_h), "elu1", H, d_h, None)
+    la._check_W(None, "elu1", H, d_h, None)
+    # a well-shaped W passes the shape test and is then held to the device
+    with pytest.raises(ValueError, match="CUDA"):
+        la._check_W(torch.zeros(H, 64, d_h), "rff", H, d_h, None)

@@ -109,3 +109,21 @@ def test_decode_rff_workload_full_size_sampled():
     e = (rel_err(got, o_ref), rel_err(S[ns, hs], S_ref), rel_err(z[ns, hs], z_ref))
     print("rff decode full size", e)
     assert max(e) < TOL["f32"], e
+
+
+def test_mis_shaped_W_raises_before_any_launch():
+    # W must be [H, rff_D, d_h]: fewer heads or a wrong input width would be
+    # read out of bounds by the kernels, so the binding refuses it.
+    dev = gpu_device()
+    N, H, dh, dv, D = 4, 8, 64, 64, 64
+    st = I.rfa_decode_step_inputs(N, H, dh, dv, step=0, seed=0)
+    S, z = la.state_init(N, H, 2 * D, dv, dev)
+    q, k, v, g = (t.to(dev) for t in (st.q, st.k, st.v, st.gate))
+    for shape in ((H - 1, D, dh), (H, D, dh + 1), (D, dh)):
+        W = torch.zeros(shape, device=dev)
+        with pytest.raises(ValueError, match="W has shape"):
+            la.decode_step(q, k, v, S, z, phi="rff", W=W, gate=g)
+        with pytest.raises(ValueError, match="W has shape"):
+            la.prefill(q[:, :, None], k[:, :, None], v[:, :, None], phi="rff", W=W)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(S).item() == 0 and torch.count_nonzero(z).item() == 0
