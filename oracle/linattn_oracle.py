@@ -651,18 +651,20 @@ def prefill_gradients(q, k, v, dout, phi="elu1", decay=None, gate=None, eps=1e-6
         out["dv"][idx] = W.T @ g_num
         out["dS0"][idx] = (c[:, None] * fq).T @ g_num
         out["dz0"][idx] = (c * g_den) @ fq
-        # decay: dL/dM_ts = dW_ts A_ts, and M_ts = beta_s prod_{r=s+1..t}
-        # alpha_r holds alpha_r exactly when s < r <= t (the start-state
-        # carry c_t when r <= t), so with every alpha_r > 0
-        #   dL/dalpha_r = [sum_{t>=r, s<r} dM_ts M_ts + sum_{t>=r} dc_t c_t] / alpha_r;
-        # dL/dbeta_s = sum_t dM_ts P_ts.
+        # decay: dL/dM_ts = dW_ts A_ts.  M_ts = beta_s prod_{r'=s+1..t}
+        # alpha_r' holds alpha_r exactly when s < r <= t, as the factor
+        # between P[r-1, s] and P[t, r]; the start-state carry c_t holds it
+        # when r <= t, between c_{r-1} and P[t, r].  So, as the product over
+        # r' != r with no division (alpha_r = 0, a full reset, included):
+        #   dL/dalpha_r = sum_{t>=r} P[t, r] (sum_{s<r} dM_ts beta_s P[r-1, s]
+        #                                     + dc_t c_{r-1}),
+        # and dL/dbeta_s = sum_t dM_ts P_ts.
         dM = dW * A
         dc = (g_num * (fq @ S0i)).sum(1) + g_den * (fq @ z0i)
-        E = dM * M
-        below = np.concatenate([np.zeros((T, 1)), np.cumsum(E, axis=1)[:, :-1]], axis=1)
-        blk = np.cumsum(below[::-1], axis=0)[::-1]      # [t0, r] = sum_{t >= t0} sum_{s < r} E_ts
-        carry = np.cumsum((dc * c)[::-1])[::-1]
-        out["dalpha"][idx] = (np.diag(blk) + carry) / al
+        for r in range(T):
+            c_prev = c[r - 1] if r > 0 else 1.0
+            inner = dM[r:, :r] @ (be[:r] * P[r - 1, :r]) if r > 0 else np.zeros(T)
+            out["dalpha"][idx][r] = P[r:, r] @ (inner + dc[r:] * c_prev)
         out["dbeta"][idx] = (dM * P).sum(0)
     res = {n: out[n] for n in ("dq", "dk", "dv", "dS0", "dz0")}
     if decay is not None:
@@ -688,14 +690,19 @@ def prefill_gradients_recurrent(q, k, v, dout, phi="elu1", decay=None, gate=None
     Backward over t, with the gradient state G (d' x d_v) and gz (d'):
         G <- alpha_{t+1} G + phi(q_t) g_t^T,  gz likewise with h_t
         u_t = G v_t + gz,  dphi(k_t) = beta_t u_t,  dv_t = beta_t G^T phi(k_t).
-    The decay reaches the loss through the log-decay prefix: every weight
-    holds alpha_r for r between its key and its query, so
-        dL/dalpha_r = sum_{t >= r} (phi(q_t).dphi(q_t) - phi(k_t).dphi(k_t)) / alpha_r,
-        dL/dbeta_t = phi(k_t) . u_t.
+    The decay multiplies the previous state in S_r = alpha_r S_{r-1} + ...,
+    and G_r is the gradient of S_r, so
+        dL/dalpha_r = <G_r, S_{r-1}> + <gz_r, z_{r-1}>,
+        dL/dbeta_t = phi(k_t) . u_t,
+    with no division by alpha (alpha_r = 0, a full reset, included).  The
+    walk back needs S_{r-1} beside G_r: the forward walk keeps the state
+    every CKPT tokens, and each block of CKPT tokens is walked forward again
+    from its checkpoint before it is walked back.
     The initial state enters S_t as prod_{r<=t} alpha_r S0: dS0 = alpha_0 G,
     dz0 = alpha_0 gz after the walk.  Returns a dict with dq, dk, dv, dS0,
     dz0 and ddecay (with decay) or dgate (with gate).
     """
+    CKPT = 64
     fq_all, fk_all = features(q, phi), features(k, phi)
     dphq, dphk = phi_derivative(q, phi), phi_derivative(k, phi)
     v_all, do_all = _f64(v), _f64(dout)
@@ -715,7 +722,10 @@ def prefill_gradients_recurrent(q, k, v, dout, phi="elu1", decay=None, gate=None
         g = np.empty((T, dv_))
         h = np.empty(T)
         dfq = np.empty((T, dp))
+        ckpt = {}                 # the state before token t, every CKPT tokens
         for t in range(T):
+            if t % CKPT == 0:
+                ckpt[t] = (S.copy(), z.copy())
             S = al[t] * S + be[t] * np.outer(fk[t], vv[t])
             z = al[t] * z + be[t] * fk[t]
             num = fq[t] @ S
@@ -738,22 +748,29 @@ def prefill_gradients_recurrent(q, k, v, dout, phi="elu1", decay=None, gate=None
         gz = np.zeros(dp)
         dfk = np.empty((T, dp))
         dvv = np.empty((T, dv_))
-        dl = np.empty(T)          # dL/dl_t: phi(q_t).dphi(q_t) - phi(k_t).dphi(k_t)
-        for t in range(T - 1, -1, -1):
-            a_next = al[t + 1] if t + 1 < T else 0.0
-            G = a_next * G + np.outer(fq[t], g[t])
-            gz = a_next * gz + fq[t] * h[t]
-            u = G @ vv[t] + gz
-            dfk[t] = be[t] * u
-            dvv[t] = be[t] * (fk[t] @ G)
-            res["dbeta"][idx][t] = fk[t] @ u
-            dl[t] = fq[t] @ dfq[t] - fk[t] @ dfk[t]
+        for b0 in sorted(ckpt, reverse=True):
+            b1 = min(b0 + CKPT, T)
+            Sp, zp = ckpt[b0]
+            prev = []             # (S_{t-1}, z_{t-1}) for t in [b0, b1)
+            for t in range(b0, b1):
+                prev.append((Sp, zp))
+                Sp = al[t] * Sp + be[t] * np.outer(fk[t], vv[t])
+                zp = al[t] * zp + be[t] * fk[t]
+            for t in range(b1 - 1, b0 - 1, -1):
+                a_next = al[t + 1] if t + 1 < T else 0.0
+                G = a_next * G + np.outer(fq[t], g[t])
+                gz = a_next * gz + fq[t] * h[t]
+                u = G @ vv[t] + gz
+                dfk[t] = be[t] * u
+                dvv[t] = be[t] * (fk[t] @ G)
+                res["dbeta"][idx][t] = fk[t] @ u
+                Sm, zm = prev[t - b0]
+                res["dalpha"][idx][t] = (G * Sm).sum() + gz @ zm
         res["dq"][idx] = dfq * dphq[idx]
         res["dk"][idx] = dfk * dphk[idx]
         res["dv"][idx] = dvv
         res["dS0"][idx] = al[0] * G
         res["dz0"][idx] = al[0] * gz
-        res["dalpha"][idx] = np.cumsum(dl[::-1])[::-1] / al
     out = {n: res[n] for n in ("dq", "dk", "dv", "dS0", "dz0")}
     if decay is not None:
         out["ddecay"] = res["dalpha"]

@@ -152,9 +152,10 @@ def test_recurrent_gradients_match_finite_differences(phi, normalize):
 
 @pytest.mark.parametrize("normalize", [True, False, "max1"])
 @pytest.mark.parametrize("kind", ["none", "ssd", "rfa"])
-def test_recurrent_gradients_equal_quadratic_form(normalize, kind):
+@pytest.mark.parametrize("T", [50, 150])    # one checkpoint block of the walk back, three
+def test_recurrent_gradients_equal_quadratic_form(normalize, kind, T):
     rng = np.random.default_rng(5)
-    B, H, T, d, dv = 2, 2, 50, 5, 3
+    B, H, d, dv = 2, 2, 5, 3
     q, k = rng.standard_normal((B, H, T, d)), rng.standard_normal((B, H, T, d))
     v, do = rng.standard_normal((B, H, T, dv)), rng.standard_normal((B, H, T, dv))
     S0, z0 = rng.standard_normal((B, H, d, dv)) * 0.3, np.abs(rng.standard_normal((B, H, d)))
@@ -206,3 +207,72 @@ def test_recurrent_gradients_planted_mistake_is_caught():
     wrong = dfk * O.phi_derivative(k)
     assert np.abs(g["dk"] - ref["dk"]).max() < 1e-12 * np.abs(ref["dk"]).max()
     assert np.abs(wrong - ref["dk"]).max() > 1e-3 * np.abs(ref["dk"]).max()
+
+
+# ---------------------------------------------------------------------------
+# A decay or gate of exactly 0 is a full reset of the state.  L is a
+# polynomial in each alpha_r over the denominators, smooth through 0, so its
+# gradient there is finite and central differences around 0 pin it.  Both
+# gradient oracles take it as a product over the other decays (no division).
+
+def _zero_case(seed, kind, zeros, T=9):
+    q, k, v, do, S0, z0, decay, gate = case(seed, T=T, kind=kind)
+    a = decay if kind == "ssd" else gate
+    a[list(zeros)] = 0.0
+    return q, k, v, do, S0, z0, decay, gate
+
+
+@pytest.mark.parametrize("fn", ["quadratic", "recurrent"])
+@pytest.mark.parametrize("kind", ["ssd", "rfa"])
+@pytest.mark.parametrize("zeros", [(0,), (4,), (8,), (2, 3, 6)])
+def test_decay_gradient_at_zero_matches_finite_differences(fn, kind, zeros):
+    q, k, v, do, S0, z0, decay, gate = _zero_case(21, kind, zeros)
+    grad = O.prefill_gradients if fn == "quadratic" else O.prefill_gradients_recurrent
+    with np.errstate(all="raise"):          # no division by the zero decay anywhere
+        g = grad(q, k, v, do, decay=decay, gate=gate, S0=S0, z0=z0)
+    name = "ddecay" if kind == "ssd" else "dgate"
+    f = lambda x: loss(q, k, v, do, "elu1", x if kind == "ssd" else None,
+                       x if kind == "rfa" else None, S0, z0, True)
+    ref = fd(f, decay if kind == "ssd" else gate)
+    assert np.all(np.isfinite(g[name]))
+    np.testing.assert_allclose(g[name], ref, rtol=1e-6, atol=1e-7, err_msg=name)
+    # the other gradients stay those of the reset sequence
+    for other, x, fo in (("dq", q, lambda x: loss(x, k, v, do, "elu1", decay, gate, S0, z0, True)),
+                         ("dS0", S0, lambda x: loss(q, k, v, do, "elu1", decay, gate, x, z0, True))):
+        np.testing.assert_allclose(g[other], fd(fo, x), rtol=1e-6, atol=1e-7, err_msg=other)
+
+
+def test_decay_gradient_at_zero_is_the_state_product():
+    # With alpha_r = 0 nothing before r reaches the loss, yet dL/dalpha_r is
+    # the inner product of the gradient state after r with the state before
+    # r: here both are written out from their definitions, so a gradient
+    # that returned 0 (or dropped either state's start term) would fail.
+    rng = np.random.default_rng(31)
+    T, d, dv, r = 8, 3, 2, 5
+    q, k = rng.standard_normal((T, d)), rng.standard_normal((T, d))
+    v, do = rng.standard_normal((T, dv)), rng.standard_normal((T, dv))
+    S0, z0 = rng.standard_normal((d, dv)) * 0.3, np.abs(rng.standard_normal(d))
+    a = 1.0 / (1.0 + np.exp(-rng.standard_normal(T)))
+    a[r] = 0.0
+    fq, fk = O.phi_elu1(q), O.phi_elu1(k)
+    o, _, _ = O.causal_linear_attention(q, k, v, decay=a, S0=S0, z0=z0)
+    # S_{r-1}, z_{r-1} by the plain sums
+    Sm = np.prod(a[:r]) * S0 + sum(np.prod(a[s + 1:r]) * np.outer(fk[s], v[s]) for s in range(r))
+    zm = np.prod(a[:r]) * z0 + sum(np.prod(a[s + 1:r]) * fk[s] for s in range(r))
+    # G_r, gz_r: the read-outs at t >= r, through the state after r
+    Sr = np.zeros((d, dv)) + np.outer(fk[r], v[r])   # alpha_r = 0
+    zr = fk[r].copy()
+    G, gz = np.zeros((d, dv)), np.zeros(d)
+    for t in range(r, T):
+        if t > r:
+            Sr = a[t] * Sr + np.outer(fk[t], v[t])
+            zr = a[t] * zr + fk[t]
+        D = fq[t] @ zr + 1e-6
+        w = np.prod(a[r + 1:t + 1])
+        G += w * np.outer(fq[t], do[t] / D)
+        gz += w * fq[t] * (-(do[t] @ o[t]) / D)
+    expect = (G * Sm).sum() + gz @ zm
+    for grad in (O.prefill_gradients, O.prefill_gradients_recurrent):
+        got = grad(q, k, v, do, decay=a, S0=S0, z0=z0)["ddecay"][r]
+        assert abs(got - expect) <= 1e-12 * max(1.0, abs(expect)), (grad.__name__, got, expect)
+    assert abs(expect) > 1e-3
