@@ -88,6 +88,14 @@ struct Cfg {
   //          An output there averages few values, so a rounding error in one
   //          weight passes to the output nearly undamped; later outputs
   //          average hundreds of weights and their rounding errors cancel.
+  //   QR     the bf16 low part phi(q) - Q, laid out as Q, in the chunks that
+  //          start before token PRECISE (the scores of the first EXACT tokens
+  //          take QR too).  Without a decay the outputs shrink like 1/sqrt(t)
+  //          while the rounding of the inter-chunk read-out stays a fixed
+  //          fraction of each output, so it is the first outputs' rounding
+  //          that shows against the rms of a long sequence.  These chunks read
+  //          the state out as (S_hi + S_lo)^T (Q + QR) (three products) and
+  //          fold w phi(k) as high + low parts.
   //   KH, KL w phi(k) as bf16 high/low parts; row = perm_pos(token), natural
   //          features (read transposed: the k = token operand of the fold)
   //   VH, VL v (high/low parts only for fp16 inputs); row = perm_pos(token),
@@ -96,12 +104,14 @@ struct Cfg {
   static constexpr int B_Q = 0;
   static constexpr int B_K = B_Q + TILE;
   static constexpr int B_KR = B_K + TILE;
-  static constexpr int B_KH = B_KR + TILE;
+  static constexpr int B_QR = B_KR + TILE;
+  static constexpr int B_KH = B_QR + TILE;
   static constexpr int B_KL = B_KH + TILE;
   static constexpr int B_VH = B_KL + TILE;
   static constexpr int B_VL = B_VH + TILE;
   static constexpr int B_L = B_VL + (VS ? TILE : 0);  // lc_t, fp32 [C]
   static constexpr int EXACT = 128;
+  static constexpr int PRECISE = 1024;
   static constexpr int B_B = B_L + 4 * C;             // beta_t, fp32 [C]
   static constexpr int B_DEN = B_B + 4 * C;           // inter-chunk denominators, fp32 [C]
   static constexpr int B_M = B_DEN + 4 * C;           // mLSTM stabiliser m_t, fp32 [C]
@@ -133,6 +143,7 @@ struct Cfg {
   static_assert(RPT == C / 16, "row split");
   static_assert(C == 32 || C == 64 || C == 128, "chunk");
   static_assert(D == 64 || D == 128, "width");
+  static_assert(PRECISE >= EXACT && PRECISE % 128 == 0, "the QR tile covers the exact scores");
   static_assert(LDS <= 160 * 1024 && S1_LDS <= 160 * 1024, "LDS");
 };
 
@@ -712,6 +723,8 @@ void output_kernel(const PfArgs a) {
         return 0.f;
       }
       float dz[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      // the chunks read out and folded at high + low precision (see QR)
+      const bool prec = DECAY != 3 && tok0 < G::PRECISE;
 #pragma unroll
       for (int i = 0; i < G::RPT; ++i) {
         const int r = G::RPT * rg + i;
@@ -742,7 +755,9 @@ void output_kernel(const PfArgs a) {
           }
           den = fmaf(qx[e], zf[e], den);
         }
-        row_write_perm<D>(buf + G::B_Q, r, fb, pack8(qx));
+        const u32x4 qp = pack8(qx);
+        row_write_perm<D>(buf + G::B_Q, r, fb, qp);
+        if (prec) row_write_perm<D>(buf + G::B_QR, r, fb, low8(qx, qp));
         const u32x4 kp = pack8(kx);
         row_write_perm<D>(buf + G::B_K, r, fb, kp);
         if (tok0 < G::EXACT) row_write_perm<D>(buf + G::B_KR, r, fb, low8(kx, kp));
@@ -754,12 +769,13 @@ void output_kernel(const PfArgs a) {
           }
           const u32x4 kh = pack8(kx);
           blk_write<D>(buf + G::B_KH, perm_pos(r), fb, kh);
-          if (fin || DECAY == 3) blk_write<D>(buf + G::B_KL, perm_pos(r), fb, low8(kx, kh));
+          if (fin || DECAY == 3 || prec)
+            blk_write<D>(buf + G::B_KL, perm_pos(r), fb, low8(kx, kh));
         } else {
 #pragma unroll
           for (int e = 0; e < 8; ++e) dz[e] += kx[e];
           blk_write<D>(buf + G::B_KH, perm_pos(r), fb, kp);
-          if (fin) blk_write<D>(buf + G::B_KL, perm_pos(r), fb, low8(kx, kp));
+          if (fin || prec) blk_write<D>(buf + G::B_KL, perm_pos(r), fb, low8(kx, kp));
         }
         if constexpr (VS) {
           float vx[8];
@@ -905,6 +921,8 @@ void output_kernel(const PfArgs a) {
           for (int kk = 0; kk < G::KT; ++kk)
             acc[mt] = mfma(tr_operand<D>(buf + G::B_KL, 16 * kk, 32 * mt, lane), vh[kk], acc[mt]);
       };
+      // the chunks read out and folded at high + low precision (see QR)
+      const bool prec = !NC && DECAY != 3 && tok0 < G::PRECISE;
 #pragma unroll
       for (int tb = 0; tb < G::TB; ++tb) {
         const int tl = 32 * tb + n;   // this lane's query token within the chunk
@@ -912,34 +930,48 @@ void output_kernel(const PfArgs a) {
         // accumulators become bf16 operands, k = features) and the diagonal
         // score block in one pass over the feature k-steps
         f32x16 o = f32x16{}, p = f32x16{};
+        auto readout = [&](auto split_tag) {
+          constexpr bool SPLIT = decltype(split_tag)::value;
 #pragma unroll
-        for (int ks = 0; ks < G::KS; ++ks) {
-          const u32x4 qf = row_operand<D>(buf + G::B_Q, tl, 2 * ks + g);
-          const f32x16& sa = acc[ks >> 1];
-          const int j0 = 8 * (ks & 1);
-          if constexpr (DECAY == 3) {
-            // identity features cancel in phi(q) . S, so the state enters as
-            // bf16 high + low parts (elu+1 features are positive and average
-            // the rounding out)
-            u32x4 sh, sl;
+          for (int ks = 0; ks < G::KS; ++ks) {
+            const u32x4 qf = row_operand<D>(buf + G::B_Q, tl, 2 * ks + g);
+            const f32x16& sa = acc[ks >> 1];
+            const int j0 = 8 * (ks & 1);
+            if constexpr (DECAY == 3 || SPLIT) {
+              // the state as bf16 high + low parts: identity features cancel
+              // in phi(q) . S (mLSTM), and the first outputs of a long
+              // sequence stand out against its rms (elu+1 features are
+              // positive and average the rounding out further on)
+              u32x4 sh, sl;
 #pragma unroll
-            for (int h = 0; h < 4; ++h) {
-              uint32_t x, y;
-              split_bf16(sa[j0 + 2 * h], sa[j0 + 2 * h + 1], x, y);
-              sh[h] = x;
-              sl[h] = y;
+              for (int h = 0; h < 4; ++h) {
+                uint32_t x, y;
+                split_bf16(sa[j0 + 2 * h], sa[j0 + 2 * h + 1], x, y);
+                sh[h] = x;
+                sl[h] = y;
+              }
+              o = mfma(sh, qf, o);
+              o = mfma(sl, qf, o);
+              if constexpr (SPLIT) o = mfma(sh, row_operand<D>(buf + G::B_QR, tl, 2 * ks + g), o);
+            } else {
+              const u32x4 sf = {pack_bf16(sa[j0 + 0], sa[j0 + 1]), pack_bf16(sa[j0 + 2], sa[j0 + 3]),
+                                pack_bf16(sa[j0 + 4], sa[j0 + 5]), pack_bf16(sa[j0 + 6], sa[j0 + 7])};
+              o = mfma(sf, qf, o);
             }
-            o = mfma(sh, qf, o);
-            o = mfma(sl, qf, o);
-          } else {
-            const u32x4 sf = {pack_bf16(sa[j0 + 0], sa[j0 + 1]), pack_bf16(sa[j0 + 2], sa[j0 + 3]),
-                              pack_bf16(sa[j0 + 4], sa[j0 + 5]), pack_bf16(sa[j0 + 6], sa[j0 + 7])};
-            o = mfma(sf, qf, o);
+            if constexpr (!NC) p = mfma(row_operand<D>(buf + G::B_K, 32 * tb + n, 2 * ks + g), qf, p);
           }
-          if constexpr (!NC) p = mfma(row_operand<D>(buf + G::B_K, 32 * tb + n, 2 * ks + g), qf, p);
+        };
+        if constexpr (NC || DECAY == 3) {
+          readout(std::false_type{});
+        } else {
+          if (prec) readout(std::true_type{});
+          else readout(std::false_type{});
         }
-        if (!NC && tok0 < G::EXACT)
+        if (!NC && tok0 < G::EXACT) {
           p = low_scores<D, G::KS>(buf + G::B_KR, buf + G::B_Q, 32 * tb + n, tl, g, p);
+          if constexpr (DECAY != 3)
+            p = low_scores<D, G::KS>(buf + G::B_K, buf + G::B_QR, 32 * tb + n, tl, g, p);
+        }
         if constexpr (!NC && G::TB == 1) fold_hi();
         float lct = 0.f;
         if constexpr (DECAY != 0) {
@@ -956,8 +988,11 @@ void output_kernel(const PfArgs a) {
             for (int ks = 0; ks < G::KS; ++ks)
               p = mfma(row_operand<D>(buf + G::B_K, 32 * sb + n, 2 * ks + g),
                        row_operand<D>(buf + G::B_Q, tl, 2 * ks + g), p);
-            if (tok0 < G::EXACT)
+            if (tok0 < G::EXACT) {
               p = low_scores<D, G::KS>(buf + G::B_KR, buf + G::B_Q, 32 * sb + n, tl, g, p);
+              if constexpr (DECAY != 3)
+                p = low_scores<D, G::KS>(buf + G::B_K, buf + G::B_QR, 32 * sb + n, tl, g, p);
+            }
           }
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
@@ -1039,7 +1074,7 @@ void output_kernel(const PfArgs a) {
       }
       if constexpr (!NC) {
         if constexpr (G::TB > 1) fold_hi();
-        if (fin || DECAY == 3) fold_lo();   // mLSTM: the state always as high + low
+        if (fin || DECAY == 3 || prec) fold_lo();   // mLSTM: the state always as high + low
       }
     };
 
