@@ -18,6 +18,7 @@ LA_F32, LA_BF16, LA_F16 = 0, 1, 2
 LA_PHI_ELU1, LA_PHI_RFF, LA_PHI_IDENTITY = 0, 1, 2
 LA_DECAY_NONE, LA_DECAY_SSD, LA_GATE_RFA, LA_GATE_MLSTM = 0, 1, 2, 3
 LA_NORM_SUM, LA_NORM_NONE, LA_NORM_MAX1 = 0, 1, 2
+NOALLOC_SCRATCH_BYTES = 64 << 20      # LA_NOALLOC_SCRATCH_BYTES
 
 
 class LaDesc(ctypes.Structure):
@@ -51,6 +52,7 @@ _SIGNATURES = {
     "la_prefill_plan": (ctypes.c_int, [_D, ctypes.POINTER(ctypes.c_int),
                                        ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int)]),
     "la_prefill": (ctypes.c_int, [_D, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "la_prefill_noalloc": (ctypes.c_int, [_D, _P, _P, _P, _P, _P, _P, _P]),
     "la_prefill_stage": (ctypes.c_int, [_D, ctypes.c_int, _P, _P, _P, _P, _P, _P, _P,
                                         ctypes.c_size_t, _P]),
     "la_decode_step": (ctypes.c_int, [_D, _P, _P, _P, _P, _P, _P, _P]),

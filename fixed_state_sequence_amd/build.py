@@ -19,7 +19,7 @@ BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "liblinattn.so")
 
 SOURCES = ["la_api.cpp", "la_recurrent.hip", "la_decode.hip", "la_prefill_mfma.hip",
-           "la_backward.hip", "la_backward_mfma.hip"]
+           "la_backward.hip", "la_backward_mfma.hip", "la_noalloc.hip"]
 ARCH = "gfx950"
 
 

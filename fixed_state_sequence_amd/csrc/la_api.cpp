@@ -156,18 +156,24 @@ la_status launched(hipError_t e) {
     if (s_ != LA_OK) return s_;        \
   } while (0)
 
-la_status check_prefill_args(const la_desc* desc, const void* q, const void* k, const void* v,
-                             float* S, float* z, void* out, void* ws, size_t ws_bytes,
-                             la::Problem* p) {
-  LA_TRY(check_desc(desc, true, p));
+la_status check_prefill_ptrs(const la::Problem& p, const void* q, const void* k, const void* v,
+                             float* S, float* z, void* out) {
   LA_TRY(check_ptr(S, "S"));
   LA_TRY(check_ptr(z, "z"));
-  if (p->T > 0) {
+  if (p.T > 0) {
     LA_TRY(check_ptr(q, "q"));
     LA_TRY(check_ptr(k, "k"));
     LA_TRY(check_ptr(v, "v"));
     LA_TRY(check_ptr(out, "out"));
   }
+  return LA_OK;
+}
+
+la_status check_prefill_args(const la_desc* desc, const void* q, const void* k, const void* v,
+                             float* S, float* z, void* out, void* ws, size_t ws_bytes,
+                             la::Problem* p) {
+  LA_TRY(check_desc(desc, true, p));
+  LA_TRY(check_prefill_ptrs(*p, q, k, v, S, z, out));
   const size_t need = p->path == 1 ? la::mfma_workspace_bytes(*p) : 0;
   if (need > 0) {
     if (!ws) return fail(LA_EINVAL, "workspace is NULL (need %zu bytes)", need);
@@ -231,6 +237,29 @@ la_status la_prefill(const la_desc* desc, const void* q, const void* k, const vo
   (void)hipGetLastError();
   for (int stage = 1; stage <= 3; ++stage)
     LA_TRY(run_stage(p, stage, q, k, v, S, z, out, workspace, static_cast<hipStream_t>(stream)));
+  return LA_OK;
+}
+
+la_status la_prefill_noalloc(const la_desc* desc, const void* q, const void* k, const void* v,
+                             float* S, float* z, void* out, void* stream) {
+  la::Problem p;
+  LA_TRY(check_desc(desc, true, &p));
+  LA_TRY(check_prefill_ptrs(p, q, k, v, S, z, out));
+  const size_t need = p.path == 1 ? la::mfma_workspace_bytes(p) : 0;
+  if (need > LA_NOALLOC_SCRATCH_BYTES)
+    return fail(LA_EINVAL,
+                "la_prefill_noalloc: this prefill needs %zu bytes of workspace, above the "
+                "%zu-byte static scratch; use la_prefill with a caller workspace",
+                need, size_t(LA_NOALLOC_SCRATCH_BYTES));
+  void* ws = nullptr;
+  if (need > 0 && p.T > 0) {
+    const hipError_t e = la::noalloc_scratch(&ws);
+    if (e != hipSuccess)
+      return fail(LA_EHIP, "la_prefill_noalloc: scratch lookup failed: %s", hipGetErrorString(e));
+  }
+  (void)hipGetLastError();
+  for (int stage = 1; stage <= 3; ++stage)
+    LA_TRY(run_stage(p, stage, q, k, v, S, z, out, ws, static_cast<hipStream_t>(stream)));
   return LA_OK;
 }
 

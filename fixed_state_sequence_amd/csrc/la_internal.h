@@ -86,4 +86,8 @@ hipError_t launch_mfma_stage(const Problem& p, int stage, const void* q, const v
                              const void* v, float* S, float* z, void* out, void* ws,
                              hipStream_t stream);
 
+// Device address of this GPU's static scratch array (LA_NOALLOC_SCRATCH_BYTES;
+// la_noalloc.hip), looked up on the first call per device.
+hipError_t noalloc_scratch(void** ptr);
+
 }  // namespace la

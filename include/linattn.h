@@ -249,6 +249,27 @@ la_status la_prefill_backward(const la_desc* desc, const void* q, const void* k,
                               float* dk, float* dv, float* ddecay, float* dS0, float* dz0,
                               void* workspace, size_t workspace_bytes, void* stream);
 
+/* Size of the static device scratch behind la_prefill_noalloc: 64 MiB per
+ * GPU, held from the library's first use of that GPU until the process
+ * ends.  It covers the chunked prefill's workspace for every shape up to
+ * B H = 256 sequences at d' = d_v = 128 with the default plan (33.8 MB for
+ * B = 1, H = 8, T = 102400). */
+#define LA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* la_prefill for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation, arguments and results as la_prefill, with the workspace
+ * taken from a static per-GPU array of LA_NOALLOC_SCRATCH_BYTES instead of
+ * the caller.  Calls no allocating routine.  A descriptor whose workspace
+ * (la_prefill_workspace_size) exceeds that size is rejected with LA_EINVAL
+ * before anything is enqueued.  The first call on a GPU looks up that GPU's
+ * copy of the array (LA_EHIP if the lookup fails).  Every call on one GPU
+ * shares its array, which keeps the last call's contents (nothing in it
+ * needs to start at zero): calls that overlap on one GPU (several streams
+ * or threads) race and must be serialised by the caller. */
+la_status la_prefill_noalloc(const la_desc* desc, const void* q, const void* k, const void* v,
+                             float* S, float* z, void* out, void* stream);
+
 /* One autoregressive step for B sequences x H heads ([kb] section 2, causal
  * recurrence; [card] "When to use which": memory-bound decoding with a
  * fixed-size state): reads q, k [B, H, d_h], v [B, H, d_v] and the gate or

@@ -258,3 +258,18 @@ def test_mis_shaped_rff_projection_is_rejected_before_any_launch():
     # a well-shaped W passes the shape test and is then held to the device
     with pytest.raises(ValueError, match="CUDA"):
         la._check_W(torch.zeros(H, 64, d_h), "rff", H, d_h, None)
+
+
+def test_noalloc_prefill_rejects_a_workspace_beyond_the_static_scratch():
+    # 16 x 16 sequences of d = 128 cut into 4 segments hold 8 state slots
+    # each (135 MB) against the 64 MiB static array: refused on the host,
+    # before any HIP call (this runs without a GPU)
+    d = desc(B=16, H=16, T=8192, segments=4)
+    assert la.prefill_workspace_size(d) > _lib.NOALLOC_SCRATCH_BYTES
+    rc = L.la_prefill_noalloc(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    assert status(rc) == "LA_EINVAL"
+    msg = L.la_last_error().decode()
+    assert "static scratch" in msg and str(_lib.NOALLOC_SCRATCH_BYTES) in msg
+    # bad pointers are refused before the size is even looked at
+    rc = L.la_prefill_noalloc(ctypes.byref(desc()), FAKE, FAKE, FAKE, None, FAKE, FAKE, None)
+    assert status(rc) == "LA_EINVAL" and "S is NULL" in L.la_last_error().decode()
