@@ -16,6 +16,8 @@
 // every weight is e^{l_t - l_s} beta_s, so dL/dl_t = <phi(q_t), dphi(q_t)> -
 // <phi(k_t), dphi(k_t)> and dL/dlog alpha_r = sum_{t>=r} dL/dl_t, a suffix sum
 // kept during the reverse pass; beta's own gradient is phi(k_t).(G_t v_t + g_t).
+// dL/dalpha_r is that sum over alpha_r, except for decays below kDecayExact,
+// whose gradient decay_exact_kernel forms as <G_r, S_{r-1}> + <g_r, z_{r-1}>.
 //
 // Pass A walks t forward: it rebuilds S_t and z_t, the read-out, g_num,
 // g_den and dq, and leaves g_num_t, g_den_t and <phi(q_t), dphi(q_t)> in the
@@ -301,8 +303,10 @@ __global__ __launch_bounds__(NT) void backward_kernel(const BwdArgs a) {
     for (int w = 0; w < NT / 64; ++w) kdk += s_sc[w][2];
     R += qdq - beta * kdk;
     if (tid == 0 && a.ddecay) {
-      if (a.decay_kind == LA_DECAY_SSD) a.ddecay[bh * T + t] = R / alpha;
-      else if (a.decay_kind == LA_GATE_RFA) a.ddecay[bh * T + t] = R / alpha - kdk;
+      // near-zero decays: the exact term is added by decay_exact_kernel
+      const float da = alpha < kDecayExact ? 0.f : R / alpha;
+      if (a.decay_kind == LA_DECAY_SSD) a.ddecay[bh * T + t] = da;
+      else if (a.decay_kind == LA_GATE_RFA) a.ddecay[bh * T + t] = da - kdk;
     }
     alpha_next = alpha;
   }
@@ -319,6 +323,228 @@ __global__ __launch_bounds__(NT) void backward_kernel(const BwdArgs a) {
     }
     if (tid < a.dp) a.dz0[bh * a.dp + tid] = alpha_next * gr;
   }
+}
+
+// ------------------------------------------------ exact decay gradient
+
+// dL/dalpha_r = <G_r, S_{r-1}> + <gz_r, z_{r-1}> for every token r whose
+// decay (or gate) is below kDecayExact: the state before r multiplies
+// alpha_r in S_r = alpha_r S_{r-1} + beta_r phi(k_r) v_r^T (wikillm "Linear
+// attention", Implementation sketch), and G_r is the gradient of S_r.
+// Written out,
+//   <G_r, S_{r-1}> = sum_{t >= r} w_t phi(q_t)^T S_{r-1} g_t,
+//   w_t = prod_{r' = r+1..t} alpha_r',
+// so one workgroup walks the segment forward: it builds S_{r-1} by the
+// recurrence from the segment's start state (or from the last exact reset
+// before r, where the state restarts from zero), then reads it out against
+// every later query of the segment with weight w_t (up to the next exact
+// reset, where w drops to 0), and adds w at the segment's end times the
+// state product with the gradient state carried in from later segments.
+// One workgroup per (b, h) and tile of 256 tokens; a tile with no such token
+// returns at once.  The result is added to dd[r], which holds the gate's
+// beta term (or 0).
+constexpr int XT = 32;    // tokens staged in LDS at a time
+
+int passes(int dp, int dv);
+
+template <typename DT, int NF4>
+__global__ __launch_bounds__(NT) void decay_exact_kernel(const DecayExactArgs a, int ntile) {
+  const int64_t bh = blockIdx.x / ntile;
+  const int tile = blockIdx.x % ntile;
+  const int tid = threadIdx.x;
+  const int ncg = a.dv >> 2;
+  const int rpp = NT / ncg;
+  const int cg = tid % ncg;
+  const int r0 = tid / ncg;
+  const int64_t T = a.T;
+  const float* al = a.decay + bh * T;
+
+  __shared__ int s_list[NT];
+  __shared__ int s_n;
+  __shared__ __align__(16) float s_x[XT][256];   // phi(k) or phi(q)
+  __shared__ __align__(16) float s_y[XT][256];   // v or g
+  __shared__ float s_al[XT], s_be[XT], s_h[XT];
+  __shared__ float s_red[NT / 64];
+  __shared__ int s_ired[NT / 64];
+
+  if (tid == 0) s_n = 0;
+  __syncthreads();
+  {
+    const int64_t t = int64_t(tile) * NT + tid;
+    if (t < T && al[t] < kDecayExact) s_list[atomicAdd(&s_n, 1)] = int(t);
+  }
+  __syncthreads();
+  const int nflag = s_n;
+
+  const DT* qg = static_cast<const DT*>(a.q) + bh * T * a.dh;
+  const DT* kg = static_cast<const DT*>(a.k) + bh * T * a.dh;
+  const DT* vg = static_cast<const DT*>(a.v) + bh * T * a.dv;
+  auto phi = [&](float x) { return a.phi == LA_PHI_IDENTITY ? x : elu1_accurate(x); };
+  auto beta_of = [&](float x) { return a.decay_kind == LA_GATE_RFA ? 1.f - x : 1.f; };
+  // block-wide max of an int (every thread gets it)
+  auto block_max = [&](int x) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x = max(x, __shfl_xor(x, off));
+    __syncthreads();
+    if ((tid & 63) == 0) s_ired[tid >> 6] = x;
+    __syncthreads();
+    int m = s_ired[0];
+#pragma unroll
+    for (int w = 1; w < NT / 64; ++w) m = max(m, s_ired[w]);
+    return m;
+  };
+
+  for (int fi = 0; fi < nflag; ++fi) {
+    const int r = s_list[fi];
+    const int seg = r / a.seg_len;
+    const int seg0 = seg * a.seg_len;
+    const int seg1 = min(seg0 + a.seg_len, a.T) - 1;
+    // the last exact reset before r within the segment (the state restarts there)
+    int s_begin = -1;
+    for (int base = r - 1; base >= seg0 && s_begin < 0; base -= NT) {
+      const int t = base - tid;
+      s_begin = block_max(t >= seg0 && al[t] == 0.f ? t : -1);
+    }
+    // the first exact reset after r (later queries get weight 0)
+    int t_end = seg1;
+    for (int base = r + 1; base <= seg1; base += NT) {
+      const int t = base + tid;
+      const int z = block_max(t <= seg1 && al[t] == 0.f ? -t : -(1 << 30));
+      if (z > -(1 << 30)) {
+        t_end = -z - 1;
+        break;
+      }
+    }
+    // the state before s_begin: zero after a reset, else the segment's start
+    float4 st[NF4];
+    float zr = 0.f;
+    const bool from_start = s_begin < 0;
+    if (from_start) s_begin = seg0;
+#pragma unroll
+    for (int i = 0; i < NF4; ++i) {
+      const int f = r0 + i * rpp;
+      st[i] = (from_start && a.S0 && f < a.dp)
+                  ? *reinterpret_cast<const float4*>(a.S0 + bh * a.s_bh + seg * a.s_seg +
+                                                     int64_t(f) * a.dv + 4 * cg)
+                  : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    if (from_start && a.z0 && tid < a.dp) zr = a.z0[bh * a.z_bh + seg * a.s_seg + tid];
+
+    // stage tokens [t0, t0 + n): x = phi(k) (update) or phi(q) (read-out);
+    // y = v or g; alpha, beta and h
+    auto stage = [&](int t0, int n, bool update) {
+      __syncthreads();   // the previous block's reads done
+      const DT* xg = update ? kg : qg;
+      for (int i = tid; i < n * a.dh; i += NT) {
+        const int j = i / a.dh, f = i % a.dh;
+        s_x[j][f] = phi(to_f32(xg[int64_t(t0 + j) * a.dh + f]));
+      }
+      for (int i = tid; i < n * a.dv; i += NT) {
+        const int j = i / a.dv, c = i % a.dv;
+        const int64_t row = bh * T + t0 + j;
+        float y;
+        if (update) {
+          y = to_f32(vg[int64_t(t0 + j) * a.dv + c]);
+        } else if (a.mode == 0) {
+          const float dv = a.dout_f32 ? static_cast<const float*>(a.dout)[row * a.dv + c]
+                                      : to_f32(static_cast<const DT*>(a.dout)[row * a.dv + c]);
+          y = a.tok[2 * row] * dv;
+        } else {
+          y = a.ws[row * (a.dv + 2) + c];
+        }
+        s_y[j][c] = y;
+      }
+      if (tid < n) {
+        const int64_t row = bh * T + t0 + tid;
+        s_al[tid] = al[t0 + tid];
+        s_be[tid] = beta_of(al[t0 + tid]);
+        if (!update) s_h[tid] = a.mode == 0 ? a.tok[2 * row + 1] : a.ws[row * (a.dv + 2) + a.dv];
+      }
+      __syncthreads();
+    };
+
+    // S_{r-1}, z_{r-1}: the recurrence over [s_begin, r)
+    for (int t0 = s_begin; t0 < r; t0 += XT) {
+      const int n = min(XT, r - t0);
+      stage(t0, n, true);
+      for (int j = 0; j < n; ++j) {
+        const float alpha = s_al[j], beta = s_be[j];
+        const float4 v4 = *reinterpret_cast<const float4*>(&s_y[j][4 * cg]);
+#pragma unroll
+        for (int i = 0; i < NF4; ++i) {
+          const int f = r0 + i * rpp;
+          if (f < a.dp) {
+            const float kb = beta * s_x[j][f];
+            st[i].x = fmaf(alpha, st[i].x, kb * v4.x);
+            st[i].y = fmaf(alpha, st[i].y, kb * v4.y);
+            st[i].z = fmaf(alpha, st[i].z, kb * v4.z);
+            st[i].w = fmaf(alpha, st[i].w, kb * v4.w);
+          }
+        }
+        if (tid < a.dp) zr = fmaf(alpha, zr, beta * s_x[j][tid]);
+      }
+    }
+    // sum_{t = r..t_end} w_t (phi(q_t)^T S_{r-1} g_t + phi(q_t) . z_{r-1} h_t)
+    float acc = 0.f, w = 1.f;
+    for (int t0 = r; t0 <= t_end; t0 += XT) {
+      const int n = min(XT, t_end + 1 - t0);
+      stage(t0, n, false);
+      for (int j = 0; j < n; ++j) {
+        if (t0 + j > r) w *= s_al[j];
+        const float4 g4 = *reinterpret_cast<const float4*>(&s_y[j][4 * cg]);
+        float p = 0.f;
+#pragma unroll
+        for (int i = 0; i < NF4; ++i) {
+          const int f = r0 + i * rpp;
+          if (f < a.dp) {
+            const float sg = st[i].x * g4.x + st[i].y * g4.y + st[i].z * g4.z + st[i].w * g4.w;
+            p = fmaf(s_x[j][f], sg, p);
+          }
+        }
+        if (tid < a.dp) p = fmaf(s_x[j][tid] * zr, s_h[j], p);
+        acc = fmaf(w, p, acc);
+      }
+    }
+    // the gradient state carried in from beyond the segment's end
+    if (t_end == seg1 && a.gafter) {
+      const float* G = a.gafter + (bh * a.nseg + seg) * (int64_t(a.dp) * a.dv + a.dp);
+      float p = 0.f;
+#pragma unroll
+      for (int i = 0; i < NF4; ++i) {
+        const int f = r0 + i * rpp;
+        if (f < a.dp) {
+          const float4 g4 = *reinterpret_cast<const float4*>(G + int64_t(f) * a.dv + 4 * cg);
+          p += st[i].x * g4.x + st[i].y * g4.y + st[i].z * g4.z + st[i].w * g4.w;
+        }
+      }
+      if (tid < a.dp) p = fmaf(G[int64_t(a.dp) * a.dv + tid], zr, p);
+      acc = fmaf(w, p, acc);
+    }
+    acc = wave_sum(acc);
+    __syncthreads();
+    if ((tid & 63) == 0) s_red[tid >> 6] = acc;
+    __syncthreads();
+    if (tid == 0) {
+      float x = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < NT / 64; ++ww) x += s_red[ww];
+      a.dd[bh * T + r] += x;
+    }
+  }
+}
+
+template <typename DT>
+hipError_t launch_exact_dt(const DecayExactArgs& a, int64_t BH, hipStream_t st) {
+  const int np = passes(a.dp, a.dv);
+  const int ntile = (a.T + NT - 1) / NT;
+  const dim3 grid{unsigned(BH * ntile)}, block{unsigned(NT)};
+  if (np <= 1) decay_exact_kernel<DT, 1><<<grid, block, 0, st>>>(a, ntile);
+  else if (np <= 2) decay_exact_kernel<DT, 2><<<grid, block, 0, st>>>(a, ntile);
+  else if (np <= 4) decay_exact_kernel<DT, 4><<<grid, block, 0, st>>>(a, ntile);
+  else if (np <= 8) decay_exact_kernel<DT, 8><<<grid, block, 0, st>>>(a, ntile);
+  else if (np <= 16) decay_exact_kernel<DT, 16><<<grid, block, 0, st>>>(a, ntile);
+  else decay_exact_kernel<DT, 32><<<grid, block, 0, st>>>(a, ntile);
+  return hipGetLastError();
 }
 
 int passes(int dp, int dv) {
@@ -341,6 +567,17 @@ hipError_t launch_dt(const BwdArgs& a, int64_t nbh, hipStream_t st) {
 }
 
 }  // namespace
+
+hipError_t launch_decay_exact(const DecayExactArgs& a, la_dtype dtype, int64_t BH,
+                              hipStream_t stream) {
+  if (a.T <= 0) return hipSuccess;
+  switch (dtype) {
+    case LA_F32: return launch_exact_dt<float>(a, BH, stream);
+    case LA_BF16: return launch_exact_dt<bf16_t>(a, BH, stream);
+    case LA_F16: return launch_exact_dt<f16_t>(a, BH, stream);
+  }
+  return hipErrorInvalidValue;
+}
 
 bool backward_supported(const Problem& p) {
   return (p.phi == LA_PHI_ELU1 || p.phi == LA_PHI_IDENTITY) && p.dp == p.dh &&
@@ -367,12 +604,22 @@ hipError_t launch_backward(const Problem& p, const void* q, const void* k, const
   a.phi = int(p.phi); a.decay_kind = int(p.decay_kind); a.norm = p.norm;
   a.dout_f32 = p.out_dtype == LA_F32 ? 1 : 0;
   a.eps = p.eps;
+  hipError_t e = hipErrorInvalidValue;
   switch (p.dtype) {
-    case LA_F32: return launch_dt<float>(a, p.BH(), stream);
-    case LA_BF16: return launch_dt<bf16_t>(a, p.BH(), stream);
-    case LA_F16: return launch_dt<f16_t>(a, p.BH(), stream);
+    case LA_F32: e = launch_dt<float>(a, p.BH(), stream); break;
+    case LA_BF16: e = launch_dt<bf16_t>(a, p.BH(), stream); break;
+    case LA_F16: e = launch_dt<f16_t>(a, p.BH(), stream); break;
   }
-  return hipErrorInvalidValue;
+  if (e != hipSuccess || !ddecay) return e;
+  // near-zero decays: the exact gradient, over the whole sequence (one
+  // segment from the initial state, nothing carried in after its end)
+  DecayExactArgs x;
+  x.q = q; x.k = k; x.v = v; x.decay = p.decay; x.decay_kind = int(p.decay_kind);
+  x.phi = int(p.phi); x.mode = 1; x.tok = nullptr; x.dout = nullptr; x.dout_f32 = 0;
+  x.ws = a.ws; x.S0 = S0; x.z0 = z0; x.s_bh = int64_t(p.dp) * p.dv; x.z_bh = p.dp; x.s_seg = 0;
+  x.gafter = nullptr; x.nseg = 1; x.seg_len = p.T; x.dd = ddecay;
+  x.T = p.T; x.dh = p.dh; x.dv = p.dv; x.dp = p.dp;
+  return launch_decay_exact(x, p.dtype, p.BH(), stream);
 }
 
 }  // namespace la

@@ -1026,7 +1026,8 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_b(const BwArgs a) {
 
 // dL/dlog alpha_r = R_r = sum_{t >= r} (qd_t - beta_t kd_t), then dL/da_r =
 // R_r / a_r (SSD) or dL/dg_r = R_r / g_r - kd_r (RFA: alpha = g, beta =
-// 1 - g).  Two passes over tiles of DG_TILE tokens of every (b, h): the
+// 1 - g); for a_r below kDecayExact, the exact <G_r, S_{r-1}> term comes
+// from decay_exact_kernel instead of R_r / a_r.  Two passes over tiles of DG_TILE tokens of every (b, h): the
 // tiles' totals, then per tile a suffix scan (4 tokens per thread, waves by
 // shuffles, the workgroup through LDS) plus the totals of the later tiles.
 constexpr int DG_TILE = 1024;
@@ -1104,7 +1105,9 @@ __global__ __launch_bounds__(256) void bwd_decay_grad(const float* decay, const 
     if (t < T) {
       const int64_t i = bh * T + t;
       const float R = base + suf[e];
-      dd[i] = DECAY == 2 ? R / decay[i] - kd[i] : R / decay[i];
+      // near-zero decays: the exact term is added by decay_exact_kernel
+      const float da = decay[i] < kDecayExact ? 0.f : R / decay[i];
+      dd[i] = DECAY == 2 ? da - kd[i] : da;
     }
   }
 }
@@ -1125,6 +1128,17 @@ hipError_t launch_d(const Problem& pb, const BwArgs& a, float* dS0, float* dz0, 
                                                                a.T, ntile);
     bwd_decay_grad<DECAY><<<dim3(nb), dim3(256), 0, st>>>(a.decay, a.qd, a.kd, a.dpart, ddecay,
                                                           a.T, ntile);
+    // near-zero decays: the exact gradient from each segment's start state
+    // and the gradient state at its end (the reverse scan's slots)
+    DecayExactArgs x;
+    x.q = a.q; x.k = a.k; x.v = a.v; x.decay = a.decay; x.decay_kind = int(pb.decay_kind);
+    x.phi = LA_PHI_ELU1; x.mode = 0; x.tok = a.tok; x.dout = a.dout; x.dout_f32 = a.dout_f32;
+    x.ws = nullptr; x.S0 = a.S0; x.z0 = a.z0; x.s_bh = a.s_bh; x.z_bh = a.z_bh;
+    x.s_seg = a.s_seg; x.gafter = a.gslot; x.nseg = a.nseg; x.seg_len = a.cps * BCH;
+    x.dd = ddecay; x.T = a.T; x.dh = D; x.dv = D; x.dp = D;
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_decay_exact(x, LA_BF16, pb.BH(), st);
   }
   return hipGetLastError();
 }

@@ -67,6 +67,49 @@ hipError_t launch_backward_chunked(const Problem& p, const void* q, const void* 
                                    float* dk, float* dv, float* ddecay, float* dS0, float* dz0,
                                    void* ws, hipStream_t stream);
 
+// Decay or gate values below this take the exact decay gradient.  Both
+// backward paths form dL/dalpha_r as a suffix sum of per-token terms divided
+// by alpha_r; that sum is alpha_r <G_r, S_{r-1}> computed as a difference of
+// O(1) terms, so its rounding is magnified by 1 / alpha_r (and alpha_r = 0,
+// a full reset, gives 0/0).  For alpha_r below the threshold the backward
+// writes only the gate's beta term and launch_decay_exact adds
+// <G_r, S_{r-1}> + <gz_r, z_{r-1}>, the gradient's definition, by walking the
+// state and the read-outs around token r.
+constexpr float kDecayExact = 1.0f / 256.0f;
+
+// Inputs of the exact decay gradient for near-zero decays.  The sequence of
+// (b, h) is cut into segments of seg_len tokens (the last may be shorter);
+// segment s starts from the state (S, z) at S0 + bh s_bh + s s_seg and
+// z0 + bh z_bh + s s_seg (zero if S0 is null), and the gradient state
+// carried in from beyond its end is (G, gz) at gafter + (bh nseg + s)
+// (dp dv + dp) (zero if null).  The read-out's gradient of token t is
+// g_t = gs_t gv_t (a dv-vector) and h_t: mode 0 reads gs_t, h_t from
+// tok[2 (bh T + t)] and gv_t from dout (fp32 if dout_f32, else the input
+// type); mode 1 reads gv_t and h_t from the rows of ws ((dv + 2) floats per
+// token) with gs_t = 1.
+struct DecayExactArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* decay;
+  int decay_kind;
+  int phi;
+  int mode;
+  const float* tok;
+  const void* dout;
+  int dout_f32;
+  const float* ws;
+  const float* S0;
+  const float* z0;
+  int64_t s_bh, z_bh, s_seg;
+  const float* gafter;
+  int nseg, seg_len;
+  float* dd;
+  int T, dh, dv, dp;
+};
+hipError_t launch_decay_exact(const DecayExactArgs& a, la_dtype dtype, int64_t BH,
+                              hipStream_t stream);
+
 // Zero-fill of the state (m may be null).
 hipError_t launch_state_init(float* S, int64_t nS, float* z, int64_t nz, float* m, int64_t nm,
                              hipStream_t stream);

@@ -225,8 +225,12 @@ la_status la_prefill_backward_workspace_size(const la_desc* desc, size_t* bytes)
  *        without a decay, required with one); dS0, dz0 (dL/dS0, dL/dz0;
  *        both NULL to skip).
  * The decay gradient is formed through log a_t (a suffix sum of
- * <phi(q_t), dphi(q_t)> - <phi(k_t), dphi(k_t)>, divided by a_t), so it is
- * undefined (inf/NaN as data) where a decay or gate value is exactly 0.
+ * <phi(q_t), dphi(q_t)> - <phi(k_t), dphi(k_t)>, divided by a_t); where a
+ * decay or gate value is below 1/256 (0, a full reset, included) it is
+ * taken from its definition instead, dL/da_r = <G_r, S_{r-1}> +
+ * <gz_r, z_{r-1}> (the gradient of the state after r with the state before
+ * it), by a walk over the tokens of r's segment, which is finite and free
+ * of the division's loss of accuracy.
  * Supported: causal, elu+1 or identity features, LA_DECAY_NONE, LA_DECAY_SSD
  * or LA_GATE_RFA, every read-out form, the widths the per-token kernel takes
  * (LA_EUNSUPPORTED otherwise: RFF, the mLSTM gates, the non-causal form).

@@ -237,9 +237,10 @@ def test_backward_per_token_path_16_bit(dtype, phi):
 
 def test_backward_chunked_decay_zero_and_one():
     """Decay values of exactly 0 (a full reset: the state before the token is
-    forgotten) keep dq, dk, dv and the initial-state gradients finite and
-    equal to the oracle's (dL/da itself is undefined there); decay 1 gives
-    the gradients of the form with no decay."""
+    forgotten) keep every gradient finite and equal to the oracle's, dL/da
+    included: L is smooth in a_r at 0 and its gradient there is <G_r,
+    S_{r-1}> + <gz_r, z_{r-1}>.  Decay 1 gives the gradients of the form with
+    no decay."""
     dev = gpu_device()
     B, H, T, d = 1, 2, 150, 64
     x = I.prefill_inputs(B, H, T, d, dtype="bf16", seed=31, decay="ssd", scale=2.0 ** -0.5)
@@ -248,10 +249,10 @@ def test_backward_chunked_decay_zero_and_one():
     rng = np.random.default_rng(33)
     state = (rng.standard_normal((B, H, d, d)) * 0.3, np.abs(rng.standard_normal((B, H, d))) * 3)
     got = run(x, do, dev, "elu1", True, state=state, state_grad=True, segments=3)
-    with np.errstate(divide="ignore", invalid="ignore"):   # dL/da at a = 0 is undefined
-        ref = O.prefill_gradients(x.q, x.k, x.v, do, decay=x.decay, S0=state[0], z0=state[1])
+    ref = O.prefill_gradients(x.q, x.k, x.v, do, decay=x.decay, S0=state[0], z0=state[1])
+    assert set(got) == set(ref) and np.isfinite(got["ddecay"]).all()
+    compare(got, ref, TOL["bf16"], "decay with zeros")
     keep = ("dq", "dk", "dv", "dS0", "dz0")
-    compare({k: got[k] for k in keep}, {k: ref[k] for k in keep}, TOL["bf16"], "decay with zeros")
     # decay 1 against the chunked path with no decay
     x.decay[:] = 1.0
     a = run(x, do, dev, "elu1", True, state=state, state_grad=True, segments=3)
@@ -287,3 +288,61 @@ def test_backward_empty_sequence(decay):
     torch.cuda.synchronize()
     assert torch.count_nonzero(dS0).item() == 0 and torch.count_nonzero(dz0).item() == 0
     assert not torch.isnan(dS0).any() and not torch.isnan(dz0).any()
+
+
+@pytest.mark.parametrize("kind", ["ssd", "rfa"])
+@pytest.mark.parametrize("segments", [1, 3])
+def test_backward_chunked_near_zero_decays(kind, segments):
+    """Decay or gate values at and near 0 on the chunked path (d = 128, bf16):
+    exact resets, values below and just above the threshold where the
+    gradient is taken as <G_r, S_{r-1}> + <gz_r, z_{r-1}> instead of a suffix
+    sum over a_r, resets next to each other and at segment edges; the decay
+    gradient is compared element by element with the oracle's (which never
+    divides by a)."""
+    dev = gpu_device()
+    B, H, T, d = 1, 2, 333, 128
+    x = I.prefill_inputs(B, H, T, d, dtype="bf16", seed=41, decay=kind, scale=2.0 ** -0.5)
+    a = x.decay if kind == "ssd" else x.gate
+    special = {0: 0.0, 5: 1e-7, 6: 0.0, 7: 0.0, 40: 1e-3, 63: 0.0, 64: 0.003, 111: 0.0,
+               150: 0.0039, 151: 0.004, 224: 0.0, 300: 2e-5, 332: 0.0}
+    for t, val in special.items():
+        a[:, :, t] = val
+    do = torch.randn(B, H, T, d, generator=torch.Generator().manual_seed(42)).to(torch.bfloat16)
+    rng = np.random.default_rng(43)
+    state = (rng.standard_normal((B, H, d, d)) * 0.3, np.abs(rng.standard_normal((B, H, d))) * 3)
+    got = run(x, do, dev, "elu1", True, state=state, state_grad=True, segments=segments)
+    ref = O.prefill_gradients_recurrent(x.q, x.k, x.v, do, decay=x.decay, gate=x.gate,
+                                        S0=state[0], z0=state[1])
+    name = "ddecay" if kind == "ssd" else "dgate"
+    assert np.isfinite(got[name]).all()
+    compare(got, ref, TOL["bf16"], ("near-zero", kind, segments))
+    # the special tokens themselves, against the rms of the decay gradient
+    r = float(np.sqrt(np.mean(ref[name] ** 2)))
+    ts = sorted(special)
+    worst = float(np.abs(got[name][..., ts] - ref[name][..., ts]).max() / r)
+    print("special tokens", worst)
+    assert worst < TOL["bf16"]
+
+
+@pytest.mark.parametrize("kind", ["ssd", "rfa"])
+@pytest.mark.parametrize("phi", ["elu1", "identity"])
+def test_backward_per_token_near_zero_decays(kind, phi):
+    """The same on the per-token kernel (fp32 inputs): resets and near-zero
+    decays, the exact gradient over the whole sequence from the initial
+    state, at the fp32 bar."""
+    dev = gpu_device()
+    B, H, T, d, dv = 2, 2, 90, 16, 8
+    x = I.prefill_inputs(B, H, T, d, dv, dtype="f32", seed=44, decay=kind, scale=0.7)
+    if phi == "identity":
+        x.q, x.k = x.q.abs(), x.k.abs()
+    a = x.decay if kind == "ssd" else x.gate
+    for t, val in {0: 0.0, 3: 1e-6, 4: 0.0, 30: 0.002, 31: 0.0, 89: 0.0}.items():
+        a[:, :, t] = val
+    do = torch.randn(B, H, T, dv, generator=torch.Generator().manual_seed(45))
+    rng = np.random.default_rng(46)
+    S0 = rng.standard_normal((B, H, d, dv)) * 0.3
+    z0 = np.abs(rng.standard_normal((B, H, d))) * 0.3
+    got = run(x, do, dev, phi, True, state=(S0, z0))
+    ref = O.prefill_gradients(x.q, x.k, x.v, do, phi=phi, decay=x.decay, gate=x.gate,
+                              S0=S0, z0=z0)
+    compare(got, ref, TOL["f32"], ("per-token near-zero", kind, phi))
