@@ -89,13 +89,18 @@ struct Cfg {
   //          weight passes to the output nearly undamped; later outputs
   //          average hundreds of weights and their rounding errors cancel.
   //   QR     the bf16 low part phi(q) - Q, laid out as Q, in the chunks that
-  //          start before token PRECISE (the scores of the first EXACT tokens
-  //          take QR too).  Without a decay the outputs shrink like 1/sqrt(t)
-  //          while the rounding of the inter-chunk read-out stays a fixed
-  //          fraction of each output, so it is the first outputs' rounding
-  //          that shows against the rms of a long sequence.  These chunks read
-  //          the state out as (S_hi + S_lo)^T (Q + QR) (three products) and
-  //          fold w phi(k) as high + low parts.
+  //          read the state out at high precision: those that start before
+  //          token PRECISE without a decay, before EXACT with one (the scores
+  //          of the first EXACT tokens take QR too).  Without a decay the
+  //          outputs shrink like 1/sqrt(t) while the rounding of the
+  //          inter-chunk read-out stays a fixed fraction of each output, so it
+  //          is the first outputs' rounding that shows against the rms of a
+  //          long sequence.  A decay keeps the outputs from shrinking once it
+  //          has cut off the sequence's start, so with one these chunks also
+  //          need the decay since the segment's start to be above e^PREC_LOG
+  //          (decays of 1 behave as no decay).  They read the state out as
+  //          (S_hi + S_lo)^T (Q + QR) (three products); the chunks before
+  //          EXACT also fold w phi(k) as high + low parts.
   //   KH, KL w phi(k) as bf16 high/low parts; row = perm_pos(token), natural
   //          features (read transposed: the k = token operand of the fold)
   //   VH, VL v (high/low parts only for fp16 inputs); row = perm_pos(token),
@@ -112,6 +117,7 @@ struct Cfg {
   static constexpr int B_L = B_VL + (VS ? TILE : 0);  // lc_t, fp32 [C]
   static constexpr int EXACT = 128;
   static constexpr int PRECISE = 1024;
+  static constexpr float PREC_LOG = -8.f;
   static constexpr int B_B = B_L + 4 * C;             // beta_t, fp32 [C]
   static constexpr int B_DEN = B_B + 4 * C;           // inter-chunk denominators, fp32 [C]
   static constexpr int B_M = B_DEN + 4 * C;           // mLSTM stabiliser m_t, fp32 [C]
@@ -678,6 +684,8 @@ void output_kernel(const PfArgs a) {
     // mLSTM: stabiliser of the state before the chunk being staged
     float m0 = 0.f;
     if constexpr (DECAY == 3) m0 = from_ws ? a.ws_m0[int64_t(bh) * (nseg + 1) + seg] : a.stab[bh];
+    // log of the decay from the segment's start to the chunk being staged
+    float lrun = 0.f;
 
     using Raw = RawChunk<G::RPT, G::ND, true, !NC, DECAY == 3>;
     auto fetch = [&](Raw& r, int c) {
@@ -723,8 +731,9 @@ void output_kernel(const PfArgs a) {
         return 0.f;
       }
       float dz[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      // the chunks read out and folded at high + low precision (see QR)
-      const bool prec = DECAY != 3 && tok0 < G::PRECISE;
+      // the chunks read out (prec) and folded (exact) at high + low precision (see QR)
+      const bool prec = DECAY != 3 && tok0 < G::PRECISE && (DECAY == 0 || lrun > G::PREC_LOG);
+      const bool exact = DECAY != 3 && tok0 < G::EXACT;
 #pragma unroll
       for (int i = 0; i < G::RPT; ++i) {
         const int r = G::RPT * rg + i;
@@ -757,7 +766,7 @@ void output_kernel(const PfArgs a) {
         }
         const u32x4 qp = pack8(qx);
         row_write_perm<D>(buf + G::B_Q, r, fb, qp);
-        if (prec) row_write_perm<D>(buf + G::B_QR, r, fb, low8(qx, qp));
+        if (prec || exact) row_write_perm<D>(buf + G::B_QR, r, fb, low8(qx, qp));
         const u32x4 kp = pack8(kx);
         row_write_perm<D>(buf + G::B_K, r, fb, kp);
         if (tok0 < G::EXACT) row_write_perm<D>(buf + G::B_KR, r, fb, low8(kx, kp));
@@ -769,13 +778,13 @@ void output_kernel(const PfArgs a) {
           }
           const u32x4 kh = pack8(kx);
           blk_write<D>(buf + G::B_KH, perm_pos(r), fb, kh);
-          if (fin || DECAY == 3 || prec)
+          if (fin || DECAY == 3 || exact)
             blk_write<D>(buf + G::B_KL, perm_pos(r), fb, low8(kx, kh));
         } else {
 #pragma unroll
           for (int e = 0; e < 8; ++e) dz[e] += kx[e];
           blk_write<D>(buf + G::B_KH, perm_pos(r), fb, kp);
-          if (fin || prec) blk_write<D>(buf + G::B_KL, perm_pos(r), fb, low8(kx, kp));
+          if (fin || exact) blk_write<D>(buf + G::B_KL, perm_pos(r), fb, low8(kx, kp));
         }
         if constexpr (VS) {
           float vx[8];
@@ -807,6 +816,8 @@ void output_kernel(const PfArgs a) {
       if (ts == 0) *reinterpret_cast<float*>(buf + G::B_LT) = lgam;
       if constexpr (DECAY == 3) {
         if (c < c1) m0 = ltot + mend;   // the stabiliser after this chunk
+      } else if constexpr (DECAY != 0) {
+        if (c < c1) lrun += ltot;
       }
       // refill this register set with the chunk PDEPTH ahead (clamped)
       fetch(raw, min(c + G::PDEPTH, c1 - 1));
@@ -881,6 +892,9 @@ void output_kernel(const PfArgs a) {
         acc[mt][r] = Sstart[f * D + 32 * wave + n];
       }
 
+    // log of the decay from the segment's start to the chunk being computed
+    // (the producers' lrun, from the chunks' totals)
+    float lrun = 0.f;
     // [B] read-out of the carried state, masked intra-chunk attention,
     // normalise and store, then fold the chunk into S.
     auto compute = [&](int c, const char* buf) {
@@ -921,8 +935,11 @@ void output_kernel(const PfArgs a) {
           for (int kk = 0; kk < G::KT; ++kk)
             acc[mt] = mfma(tr_operand<D>(buf + G::B_KL, 16 * kk, 32 * mt, lane), vh[kk], acc[mt]);
       };
-      // the chunks read out and folded at high + low precision (see QR)
-      const bool prec = !NC && DECAY != 3 && tok0 < G::PRECISE;
+      // the chunks read out (prec, as the producers decided) and folded
+      // (exact) at high + low precision (see QR)
+      bool prec = !NC && DECAY == 0 && tok0 < G::PRECISE;
+      if constexpr (!NC && DECAY != 0 && DECAY != 3) prec = tok0 < G::PRECISE && lrun > G::PREC_LOG;
+      const bool exact = !NC && DECAY != 3 && tok0 < G::EXACT;
 #pragma unroll
       for (int tb = 0; tb < G::TB; ++tb) {
         const int tl = 32 * tb + n;   // this lane's query token within the chunk
@@ -1074,8 +1091,9 @@ void output_kernel(const PfArgs a) {
       }
       if constexpr (!NC) {
         if constexpr (G::TB > 1) fold_hi();
-        if (fin || DECAY == 3 || prec) fold_lo();   // mLSTM: the state always as high + low
+        if (fin || DECAY == 3 || exact) fold_lo();   // mLSTM: the state always as high + low
       }
+      if constexpr (DECAY != 0 && DECAY != 3) lrun += *reinterpret_cast<const float*>(buf + G::B_LT);
     };
 
     if constexpr (G::NBUF == 2) {
