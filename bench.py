@@ -45,6 +45,21 @@ Printed as one JSON line:
                dq, a reverse scan of the segments' gradient states, a pass
                in reverse order for dk and dv); algorithmic bytes are q, k,
                v, dout read once (bf16) and dq, dk, dv written once (fp32);
+  configs      the other prefill workloads, forward: the elu+1 prefill
+               (B=4 H=8 T=2048 d=64) and the SSD-decay prefill (B=2 H=16
+               T=8192 d=128, a = sigmoid(N(3, 1))), and the long-context one
+               again, each timed per call (state zeroing + la_prefill) warm
+               (back to back) and cold (a 1 GiB scrub written between calls,
+               outside the timed region, so nothing of the inputs is left in
+               the 256 MB last-level cache); median and minimum, algorithmic
+               bytes (q, k, v read and out written once, the decay, the state
+               read and written) and their fraction of the HBM peak;
+  mfma_peak    a measured dense bf16 MFMA rate (libla_probe.so: every wave
+               issues independent chains of v_mfma_f32_32x32x16_bf16, and of
+               v_mfma_f32_16x16x32_bf16) beside the 2.5 PFLOP/s spec;
+  mfma.executed  MFMA instructions per dispatch of the three prefill stages
+               from the committed rocprofv3 counters (null once a kernel source
+               changed) times their FLOPs, over the step time;
   cpu_baseline the fp64 oracle (the CPU reference the tests check against),
                on a bounded sample of the same prefill workload, one worker
                process per head.
@@ -141,6 +156,38 @@ def kernel_source_sha256():
         with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()
+
+
+MFMA_PROFILE = os.path.join(ROOT, "profiles", "prefill_t102400_d128_mfma_counters.txt")
+
+
+def _profile_kv(path):
+    """`key = value` lines of a committed counter summary, or None when the
+    prefill kernels' sources no longer match the hash recorded there."""
+    try:
+        with open(path) as f:
+            lines = f.read().splitlines()
+        src = kernel_source_sha256()
+    except OSError:
+        return None
+    kv = {}
+    for ln in lines:
+        if "=" in ln and not ln[:1].isspace():
+            k, v = ln.split("=", 1)
+            kv[k.strip()] = v.strip()
+    return kv if kv.get("source_sha256") == src else None
+
+
+def profiled_mfma_insts():
+    """MFMA instructions per dispatch of stages 1, 2 and 3 of the long-context
+    prefill (SQ_INSTS_MFMA; every one a 32x32x16 bf16 MFMA), or None."""
+    kv = _profile_kv(MFMA_PROFILE)
+    if kv is None:
+        return None
+    try:
+        return [float(kv[f"mfma_insts_stage{i}"]) for i in (1, 2, 3)]
+    except (KeyError, ValueError):
+        return None
 
 
 def profiled_traffic():
@@ -269,6 +316,96 @@ def bench_backward(torch, la, I, B, H, T, d, reps, decay=None, scale=PF["scale"]
                 algorithmic_bytes=nbytes)
 
 
+def bench_config(torch, la, I, name, reps=25, warmup=5, scrub_bytes=1 << 30):
+    """One forward prefill workload, per call (state zeroing + la_prefill):
+    warm (calls back to back) and cold (a scrub buffer larger than the
+    last-level cache written before every call, outside the events)."""
+    dev = torch.device("cuda:0")
+    x = I.workload_inputs(name, seed=0, device=dev)
+    B, H, T, d = x.q.shape
+    dv = x.v.shape[-1]
+    desc = la.make_desc(B, H, T, d, dv, la._lib.LA_BF16, eps=PF["eps"], decay=x.decay)
+    chunk, segments, path = la.prefill_plan(desc)
+    nws = la.prefill_workspace_size(desc)
+    ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=dev)
+    out = torch.empty(B, H, T, dv, dtype=torch.bfloat16, device=dev)
+    S = torch.empty(B, H, d, dv, dtype=torch.float32, device=dev)
+    z = torch.empty(B, H, d, dtype=torch.float32, device=dev)
+    scrub = torch.empty(scrub_bytes // 4, dtype=torch.float32, device=dev)
+    L = la._lib.lib()
+    P = ctypes.c_void_p
+    ptr = lambda t: P(t.data_ptr())
+    stream = P(torch.cuda.current_stream(dev).cuda_stream)
+    dref = ctypes.byref(desc)
+    args = (ptr(x.q), ptr(x.k), ptr(x.v), ptr(S), ptr(z), ptr(out))
+
+    def call():
+        la._lib.check(L.la_state_init(dref, ptr(S), ptr(z), stream))
+        la._lib.check(L.la_prefill(dref, *args, ptr(ws), nws, stream))
+
+    def timed(cold):
+        evs = [_events(torch) for _ in range(reps)]
+        for r in range(reps):
+            if cold:
+                scrub.fill_(float(r))
+            evs[r][0].record()
+            call()
+            evs[r][1].record()
+        torch.cuda.synchronize()
+        return sorted(a.elapsed_time(b) for a, b in evs)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    warm = timed(False)
+    cold = timed(True)
+    TH = B * H * T
+    nbytes = TH * (2 * d + 2 * dv) * 2      # q, k, v read and out written, bf16
+    nbytes += 2 * B * H * (d * dv + d) * 4 + (TH * 4 if x.decay is not None else 0)
+    res = {"B": B, "H": H, "T": T, "d": d, "decay": "ssd" if x.decay is not None else None,
+           "chunk": chunk, "segments": segments, "algorithmic_bytes": nbytes, "reps": reps}
+    for tag, ts in (("warm", warm), ("cold", cold)):
+        med = ts[len(ts) // 2]
+        res[tag] = {"median_ms": med, "min_ms": ts[0], "tokens_per_s": B * T / (med * 1e-3),
+                    "GBs": nbytes / (med * 1e-3) / 1e9,
+                    "hbm_frac": nbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    return res
+
+
+def mfma_peak(torch, nblocks=1024, iters=256, reps=5):
+    """Measured dense bf16 MFMA rate (TFLOP/s) of libla_probe.so's loops:
+    v_mfma_f32_32x32x16_bf16 and v_mfma_f32_16x16x32_bf16 chains."""
+    from fixed_state_sequence_amd import build as B_
+    if not os.path.exists(B_.PROBE_LIB_PATH):
+        return None
+    lib = ctypes.CDLL(B_.PROBE_LIB_PATH)
+    lib.la_probe_mfma.restype = ctypes.c_int
+    lib.la_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                  ctypes.c_void_p]
+    dev = torch.device("cuda:0")
+    sink = torch.empty(nblocks * 256, dtype=torch.float32, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    res = {}
+    for shape, name, per in ((0, "32x32x16", 4 * 4 * 32768), (1, "16x16x32", 4 * 8 * 16384)):
+        call = lambda: lib.la_probe_mfma(shape, nblocks, iters, ctypes.c_void_p(sink.data_ptr()),
+                                         stream)
+        if call() != 0:
+            return None
+        torch.cuda.synchronize()
+        e0, e1 = _events(torch)
+        e0.record()
+        for _ in range(reps):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        res[name] = nblocks * iters * per / (ms * 1e-3) / 1e12
+    return {"unit": "TFLOP/s", "bf16_32x32x16": res["32x32x16"], "bf16_16x16x32": res["16x16x32"],
+            "spec": BF16_PEAK_TFLOPS,
+            "loop": f"{nblocks} workgroups x 4 waves, independent accumulator chains, {iters} "
+                    f"iterations, operands in registers"}
+
+
 def hbm_copy(torch, nbytes=1 << 30, reps=10):
     """Device-to-device streaming of `nbytes` (read + write) by two kernels,
     torch's copy and its vectorised negation (16 bytes per lane, like the
@@ -344,6 +481,23 @@ def bench_decode(torch, la, I, N, steps, warmup=64):
                 state_mb=state_b / 1e6)
 
 
+def executed_mfma(pf, peak):
+    """Executed MFMA work of the prefill step from the committed counters:
+    per stage and in total, as TFLOP/s over the measured stage and step times
+    and as fractions of the spec and the measured 32x32x16 peak."""
+    insts = profiled_mfma_insts()
+    if insts is None:
+        return None
+    per = 2 * 32 * 32 * 16              # FLOPs of one v_mfma_f32_32x32x16_bf16
+    st = pf["stage_ms"]
+    stages = [n * per / (ms * 1e-3) / 1e12 if ms > 0 else 0.0 for n, ms in zip(insts, st)]
+    total = sum(insts) * per / (pf["ms"] * 1e-3) / 1e12
+    meas = peak["bf16_32x32x16"] if peak else None
+    return {"flops_per_step": sum(insts) * per, "stage_TFLOPs": stages, "achieved": total,
+            "frac": total / BF16_PEAK_TFLOPS, "frac_of_measured": total / meas if meas else None,
+            "stage3_frac": stages[2] / BF16_PEAK_TFLOPS}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -393,6 +547,13 @@ def main(argv=None):
     step_bytes = TH * 4 * d * 2 + 2 * state_bytes
 
     cp = hbm_copy(torch)
+    peak = mfma_peak(torch)
+    configs = None
+    if not a.prefill_only:
+        print("[bench] forward configs, warm and cold", file=sys.stderr, flush=True)
+        configs = {n: bench_config(torch, la, I, n) for n in
+                   ("elu_prefill_b4_h8_t2048_d64", "ssd_prefill_b2_h16_t8192_d128",
+                    "long_prefill_b1_h8_t102400_d128")}
     dec = dec_big = None
     if a.prefill_only:
         extras = None
@@ -437,6 +598,7 @@ def main(argv=None):
                    "chunk": pf["chunk"], "segments": pf["segments"]},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
+                     "path_frac": step_bytes / (pf["rep_median_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
                      "traffic": profiled_traffic() if pf["chunk"] == 32 else None,
                      "kernel": "output_kernel (la_prefill stage 3)",
                      "kernel_ms": s3, "algorithmic_bytes": stage3_bytes,
@@ -447,9 +609,13 @@ def main(argv=None):
                  "GBs": step_bytes / (pf["ms"] * 1e-3) / 1e9,
                  "hbm_frac": step_bytes / (pf["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS},
         "mfma": {"algorithmic_flops": flops, "achieved": tflops, "peak": BF16_PEAK_TFLOPS,
-                 "unit": "TFLOP/s", "frac": tflops / BF16_PEAK_TFLOPS},
+                 "unit": "TFLOP/s", "frac": tflops / BF16_PEAK_TFLOPS,
+                 "executed": executed_mfma(pf, peak)},
+        "mfma_peak": peak,
         "cpu_baseline": cpu,
     }
+    if configs is not None:
+        res["configs"] = configs
     if extras:
         res.update({
             "normaliser_free": {

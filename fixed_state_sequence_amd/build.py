@@ -17,6 +17,9 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "liblinattn.so")
+# machine-peak probes for the benchmark (not part of the linattn ABI)
+PROBE_LIB_PATH = os.path.join(HERE, "libla_probe.so")
+PROBE_SOURCES = ["la_probe.hip"]
 
 SOURCES = ["la_api.cpp", "la_recurrent.hip", "la_decode.hip", "la_prefill_mfma.hip",
            "la_backward.hip", "la_backward_mfma.hip", "la_noalloc.hip"]
@@ -58,18 +61,23 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False, jobs: int = 4) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB_PATH + ".tmp"
+def _link(objs, path: str, verbose: bool) -> None:
+    tmp = path + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"linking liblinattn.so failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB_PATH)
+        raise RuntimeError(f"linking {os.path.basename(path)} failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, path)
+
+
+def build(verbose: bool = False, jobs: int = 4) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES + PROBE_SOURCES))
+    _link(objs[:len(SOURCES)], LIB_PATH, verbose)
+    _link(objs[len(SOURCES):], PROBE_LIB_PATH, verbose)
     return LIB_PATH
 
 
