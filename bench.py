@@ -316,7 +316,8 @@ def bench_backward(torch, la, I, B, H, T, d, reps, decay=None, scale=PF["scale"]
                 algorithmic_bytes=nbytes)
 
 
-def bench_config(torch, la, I, name, reps=25, warmup=5, scrub_bytes=1 << 30):
+def bench_config(torch, la, I, name, reps=25, warmup=5, scrub_bytes=1 << 30, chunk=0,
+                 segments=0):
     """One forward prefill workload, per call (state zeroing + la_prefill):
     warm (calls back to back) and cold (a scrub buffer larger than the
     last-level cache written before every call, outside the events)."""
@@ -324,7 +325,8 @@ def bench_config(torch, la, I, name, reps=25, warmup=5, scrub_bytes=1 << 30):
     x = I.workload_inputs(name, seed=0, device=dev)
     B, H, T, d = x.q.shape
     dv = x.v.shape[-1]
-    desc = la.make_desc(B, H, T, d, dv, la._lib.LA_BF16, eps=PF["eps"], decay=x.decay)
+    desc = la.make_desc(B, H, T, d, dv, la._lib.LA_BF16, eps=PF["eps"], decay=x.decay,
+                        chunk=chunk, segments=segments)
     chunk, segments, path = la.prefill_plan(desc)
     nws = la.prefill_workspace_size(desc)
     ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=dev)
@@ -372,9 +374,12 @@ def bench_config(torch, la, I, name, reps=25, warmup=5, scrub_bytes=1 << 30):
     return res
 
 
-def mfma_peak(torch, nblocks=1024, iters=256, reps=5):
-    """Measured dense bf16 MFMA rate (TFLOP/s) of libla_probe.so's loops:
-    v_mfma_f32_32x32x16_bf16 and v_mfma_f32_16x16x32_bf16 chains."""
+# libla_probe.so shapes: (id, MFMA, independent accumulator chains per wave, FLOPs per MFMA)
+PROBE_SHAPES = ((0, "32x32x16", 4, 32768), (2, "32x32x16", 2, 32768), (1, "16x16x32", 8, 16384),
+                (3, "16x16x32", 16, 16384))
+
+
+def _probe_lib():
     from fixed_state_sequence_amd import build as B_
     if not os.path.exists(B_.PROBE_LIB_PATH):
         return None
@@ -382,28 +387,58 @@ def mfma_peak(torch, nblocks=1024, iters=256, reps=5):
     lib.la_probe_mfma.restype = ctypes.c_int
     lib.la_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
                                   ctypes.c_void_p]
+    return lib
+
+
+def _probe_rate(torch, lib, shape, nblocks, iters, reps):
+    """TFLOP/s of one probe configuration (events around `reps` launches)."""
     dev = torch.device("cuda:0")
     sink = torch.empty(nblocks * 256, dtype=torch.float32, device=dev)
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
-    res = {}
-    for shape, name, per in ((0, "32x32x16", 4 * 4 * 32768), (1, "16x16x32", 4 * 8 * 16384)):
-        call = lambda: lib.la_probe_mfma(shape, nblocks, iters, ctypes.c_void_p(sink.data_ptr()),
-                                         stream)
-        if call() != 0:
-            return None
-        torch.cuda.synchronize()
-        e0, e1 = _events(torch)
-        e0.record()
-        for _ in range(reps):
-            call()
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / reps
-        res[name] = nblocks * iters * per / (ms * 1e-3) / 1e12
-    return {"unit": "TFLOP/s", "bf16_32x32x16": res["32x32x16"], "bf16_16x16x32": res["16x16x32"],
+    _, _, ch, per = next(p for p in PROBE_SHAPES if p[0] == shape)
+    call = lambda: lib.la_probe_mfma(shape, nblocks, iters, ctypes.c_void_p(sink.data_ptr()),
+                                     stream)
+    if call() != 0:
+        return None
+    torch.cuda.synchronize()
+    e0, e1 = _events(torch)
+    e0.record()
+    for _ in range(reps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    return nblocks * 4 * ch * iters * per / (ms * 1e-3) / 1e12
+
+
+def mfma_peak(torch, nblocks=512, iters=32768, reps=5):
+    """Measured dense bf16 MFMA rate (TFLOP/s) of libla_probe.so's loops, two
+    workgroups of 4 waves per compute unit, a few milliseconds per launch:
+    v_mfma_f32_32x32x16_bf16 with 4 independent chains per wave, and
+    v_mfma_f32_16x16x32_bf16 with 16 (it needs about twice the chains, and
+    accumulator registers, to approach the same rate)."""
+    lib = _probe_lib()
+    if lib is None:
+        return None
+    r32 = _probe_rate(torch, lib, 0, nblocks, iters, reps)
+    r16 = _probe_rate(torch, lib, 3, nblocks, iters, reps)
+    if r32 is None or r16 is None:
+        return None
+    return {"unit": "TFLOP/s", "bf16_32x32x16": r32, "bf16_16x16x32": r16,
             "spec": BF16_PEAK_TFLOPS,
-            "loop": f"{nblocks} workgroups x 4 waves, independent accumulator chains, {iters} "
-                    f"iterations, operands in registers"}
+            "loop": f"{nblocks} workgroups x 4 waves, operands in registers, {iters} MFMAs per "
+                    f"chain; 4 chains per wave (32x32x16), 16 (16x16x32)"}
+
+
+def mfma_sweep(torch):
+    """Every probe shape and chain count over 1 to 16 workgroups per compute
+    unit (printed, one line each)."""
+    lib = _probe_lib()
+    for shape, name, ch, _ in PROBE_SHAPES:
+        for nb in (256, 512, 1024, 2048, 4096):
+            r = _probe_rate(torch, lib, shape, nb, 16384 * 1024 // nb, 5)
+            print(f"v_mfma_f32_{name}_bf16, {ch} chains per wave, {nb} workgroups of 4 waves: "
+                  f"{r:.0f} TFLOP/s", flush=True)
 
 
 def hbm_copy(torch, nbytes=1 << 30, reps=10):
@@ -511,6 +546,13 @@ def main(argv=None):
                     help="prefill chunk length (0: the library's default plan)")
     ap.add_argument("--prefill-only", action="store_true",
                     help="time the long-context prefill alone (no variants, backward, decode)")
+    ap.add_argument("--mfma-sweep", action="store_true",
+                    help="only sweep the MFMA peak probe (shapes, chains, workgroups) and exit")
+    ap.add_argument("--config", default=None,
+                    help="only time this forward prefill workload (inputs.WORKLOADS name), with "
+                         "--chunk and --segments, warm and cold, and print its line")
+    ap.add_argument("--segments", type=int, default=0,
+                    help="segments per sequence for --config (0: the library's default plan)")
     a = ap.parse_args(argv)
     if a.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported "
@@ -519,7 +561,7 @@ def main(argv=None):
         return 2
 
     cpu = None
-    if not a.no_cpu_baseline and not a.prefill_only:
+    if not (a.no_cpu_baseline or a.prefill_only or a.config or a.mfma_sweep):
         print(f"[bench] cpu baseline: oracle on {a.cpu_tokens} tokens x {PF['H']} heads",
               file=sys.stderr, flush=True)
         cpu = cpu_baseline(a.cpu_tokens)
@@ -531,6 +573,14 @@ def main(argv=None):
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
     la._lib.lib()
+    if a.mfma_sweep:
+        mfma_sweep(torch)
+        return 0
+    if a.config:
+        line = bench_config(torch, la, I, a.config, reps=max(a.steps, 5), warmup=a.warmup,
+                            chunk=a.chunk, segments=a.segments)
+        print(json.dumps({"config": a.config, **line}), flush=True)
+        return 0
 
     print(f"[bench] prefill B={PF['B']} H={PF['H']} T={PF['T']} d={PF['d']}: "
           f"{a.warmup} warm-up + {a.steps} timed steps", file=sys.stderr, flush=True)

@@ -114,6 +114,35 @@ __device__ __forceinline__ u32x4 tr_operand(const char* tile, int k0, int colbas
   return out;
 }
 
+// v_mfma_f32_16x16x32_bf16: lane (n = lane % 16, q = lane / 16) holds
+// k-values 8 q .. 8 q + 7 of row (A) or column (B) n; the result holds rows
+// 4 q .. 4 q + 3 of column n.
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// The transposed operand of v_mfma_f32_16x16x32_bf16 from a token-major
+// tile: lane (n, q) holds rows k0 + 8 q .. k0 + 8 q + 7 of column
+// colbase + n (the same two LDS transpose reads as tr_operand, with the four
+// 16-lane groups taking four 8-row blocks of one 16-column block).
+template <int D>
+__device__ __forceinline__ u32x4 tr_operand16(const char* tile, int k0, int colbase, int lane) {
+  const int q = lane >> 4, s = lane & 15;
+  const int c = colbase + 4 * (s & 3);
+  u32x4 out;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = k0 + 8 * q + 4 * h + (s >> 2);
+    const char* p = tile + tile_off<D>(r, c >> 3) + ((c & 7) << 1);
+    const v4i16 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p));
+    const u32x2 y = __builtin_bit_cast(u32x2, x);
+    out[2 * h] = y[0];
+    out[2 * h + 1] = y[1];
+  }
+  return out;
+}
+
 // Features 8 fb .. 8 fb + 7 of row r (4 packed bf16 pairs) at their
 // perm_pos positions: two 8-byte pieces.
 template <int D>

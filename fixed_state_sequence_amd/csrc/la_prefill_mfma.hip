@@ -48,6 +48,8 @@
 // feeds the read-out MFMA straight from registers, and the intra-chunk score
 // tile feeds the P V product the same way.  Every LDS tile is stored in that
 // permuted k-order so all operands agree.
+#include <cstdlib>
+#include <cstring>
 #include <type_traits>
 
 #include "la_device.h"
@@ -356,7 +358,11 @@ __device__ __forceinline__ float lane_value(float lo, float hi, int r) {
 // and the v tiles in one of two LDS buffers, and keep their share of z; NW
 // consumer waves fold each staged chunk into the state held in their
 // accumulators (32 value columns each).  One barrier per chunk.
-template <int D, int C, int DECAY, typename DT>
+// M16: the consumers fold on v_mfma_f32_16x16x32_bf16 (16 x 16 result tiles,
+// the whole 32-token chunk as one k-block) instead of 32x32x16 (32 x 32
+// tiles, two 16-token k-steps); the same sums in another order.  Kept to
+// measure the shape choice (LA_STAGE1_MFMA=16x16x32).
+template <int D, int C, int DECAY, typename DT, bool M16 = false>
 __global__ __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4, 4)))
 void segment_state_kernel(const PfArgs a) {
   constexpr bool VS = __is_same(DT, f16_t);   // fp16 v needs a bf16 low part too
@@ -511,6 +517,41 @@ void segment_state_kernel(const PfArgs a) {
   } else {
     // =================================================== consumer waves
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if constexpr (M16) {
+      static_assert(C == 32 && !VS && DECAY != 3, "the 16x16x32 fold covers 32-token bf16 chunks");
+      // rows = features 16 ft + 4 (lane / 16) + r, columns = 32 wave + 16 nt + lane % 16
+      f32x4 acc16[D / 16][2];
+#pragma unroll
+      for (int ft = 0; ft < D / 16; ++ft) acc16[ft][0] = acc16[ft][1] = f32x4{};
+      __syncthreads();   // the producers' first chunk
+      for (int i = 0; i < n; ++i) {
+        const char* buf = buffer(i);
+        u32x4 vb[2];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) vb[nt] = tr_operand16<D>(buf + G::S1_VH, 0, 32 * wave + 16 * nt, lane);
+#pragma unroll
+        for (int ft = 0; ft < D / 16; ++ft) {
+          const u32x4 kh = tr_operand16<D>(buf + G::S1_KH, 0, 16 * ft, lane);
+          const u32x4 kl = tr_operand16<D>(buf + G::S1_KL, 0, 16 * ft, lane);
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) {
+            acc16[ft][nt] = mfma16(kh, vb[nt], acc16[ft][nt]);
+            acc16[ft][nt] = mfma16(kl, vb[nt], acc16[ft][nt]);
+          }
+        }
+        __syncthreads();
+      }
+      const int q = lane >> 4, nn = lane & 15;
+#pragma unroll
+      for (int ft = 0; ft < D / 16; ++ft)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            dst[(16 * ft + 4 * q + r) * D + 32 * wave + 16 * nt + nn] = acc16[ft][nt][r];
+      __syncthreads();   // matches the producers' z barrier
+      return;
+    }
     f32x16 acc[G::MT];
 #pragma unroll
     for (int mt = 0; mt < G::MT; ++mt) acc[mt] = f32x16{};
@@ -1130,6 +1171,14 @@ void output_kernel(const PfArgs a) {
 
 // ---------------------------------------------------------------- dispatch
 
+// LA_STAGE1_MFMA=16x16x32 in the environment selects the stage-1 fold on
+// v_mfma_f32_16x16x32_bf16 for the 128-wide, 32-token, bf16 prefill without
+// a decay (the configuration its measurement covers); read at every launch.
+bool stage1_mfma16() {
+  const char* e = std::getenv("LA_STAGE1_MFMA");
+  return e && std::strcmp(e, "16x16x32") == 0;
+}
+
 template <int D, int C, int DECAY, typename DT>
 hipError_t launch3(const PfArgs& a, int64_t BH, int stage, hipStream_t st) {
   using G = Cfg<D, C, __is_same(DT, f16_t)>;
@@ -1138,6 +1187,13 @@ hipError_t launch3(const PfArgs& a, int64_t BH, int stage, hipStream_t st) {
   const bool scan = a.nseg > 1 || a.nc;
   if (stage == 1) {
     if (!scan) return hipSuccess;
+    if constexpr (D == 128 && C == 32 && DECAY == 0 && __is_same(DT, bf16_t)) {
+      if (stage1_mfma16()) {
+        segment_state_kernel<D, C, DECAY, DT, true>
+            <<<dim3(unsigned(BH * a.nslot)), dim3(2 * G::NT), 0, st>>>(a);
+        return hipGetLastError();
+      }
+    }
     segment_state_kernel<D, C, DECAY, DT><<<dim3(unsigned(BH * a.nslot)), dim3(2 * G::NT), 0, st>>>(a);
   } else if (stage == 2) {
     if (!scan) return hipSuccess;

@@ -71,10 +71,10 @@ __global__ __launch_bounds__(256) void mfma_16x16x32_loop(int iters, float* sink
 extern "C" {
 
 // Enqueue `nblocks` workgroups of 256 threads (4 waves), each wave issuing
-// 4 * iters (shape 0: v_mfma_f32_32x32x16_bf16) or 8 * iters (shape 1:
-// v_mfma_f32_16x16x32_bf16) MFMAs; `sink` holds nblocks * 256 floats.
-// FLOPs: nblocks * 4 * 4 * iters * 32768 (shape 0) or nblocks * 4 * 8 *
-// iters * 16384 (shape 1).  Returns a hipError_t.
+// CH independent chains of `iters` MFMAs: shape 0 v_mfma_f32_32x32x16_bf16
+// (CH = 4), 1 v_mfma_f32_16x16x32_bf16 (CH = 8), 2 the 32x32x16 with CH = 2,
+// 3 the 16x16x32 with CH = 16; `sink` holds nblocks * 256 floats.  FLOPs:
+// nblocks * 4 * CH * iters * (32768 or 16384).  Returns a hipError_t.
 int la_probe_mfma(int shape, int nblocks, int iters, float* sink, void* stream) {
   if (nblocks < 1 || iters < 1 || !sink) return int(hipErrorInvalidValue);
   const hipStream_t st = static_cast<hipStream_t>(stream);
@@ -82,6 +82,10 @@ int la_probe_mfma(int shape, int nblocks, int iters, float* sink, void* stream) 
     mfma_32x32x16_loop<4><<<dim3(unsigned(nblocks)), dim3(256), 0, st>>>(iters, sink);
   else if (shape == 1)
     mfma_16x16x32_loop<8><<<dim3(unsigned(nblocks)), dim3(256), 0, st>>>(iters, sink);
+  else if (shape == 2)   // 32x32x16 with 2 chains per wave, 8 * 32768 FLOPs per wave-iteration
+    mfma_32x32x16_loop<2><<<dim3(unsigned(nblocks)), dim3(256), 0, st>>>(iters, sink);
+  else if (shape == 3)   // 16x16x32 with 16 chains per wave
+    mfma_16x16x32_loop<16><<<dim3(unsigned(nblocks)), dim3(256), 0, st>>>(iters, sink);
   else
     return int(hipErrorInvalidValue);
   return int(hipGetLastError());

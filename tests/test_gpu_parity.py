@@ -343,3 +343,27 @@ def test_prefill_noncausal_per_token_fp32(phi):
     e = (rel_err(out, o_ref), rel_err(S, S_ref), rel_err(z, z_ref))
     assert max(e) < TOL["f32"], e
 
+
+
+def test_stage1_fold_on_16x16x32_mfma():
+    """The stage-1 fold built on v_mfma_f32_16x16x32_bf16 (selected by
+    LA_STAGE1_MFMA=16x16x32, kept to measure the MFMA shape choice) gives the
+    same segment states as the 32x32x16 fold up to summation order: outputs
+    and final state against the oracle at the bf16 bar, and against the
+    default fold to well under the bar (the read-out rounds the state to
+    bf16, so an fp32 difference can flip a rounding)."""
+    import os
+    dev = gpu_device()
+    x = I.prefill_inputs(1, 4, 3000, 128, dtype="bf16", seed=17, scale=2.0 ** -0.5)
+    ref = run_prefill(x, dev, segments=6)
+    os.environ["LA_STAGE1_MFMA"] = "16x16x32"
+    try:
+        got = run_prefill(x, dev, segments=6)
+    finally:
+        del os.environ["LA_STAGE1_MFMA"]
+    o_ref, S_ref, z_ref = oracle_prefill(x)
+    e = (rel_err(got[0], o_ref), rel_err(got[1], S_ref), rel_err(got[2], z_ref))
+    d = tuple(rel_err(g, r.cpu().numpy()) for g, r in zip(got, ref))
+    print("16x16x32 stage 1: vs oracle", e, "vs 32x32x16", d)
+    assert max(e) < TOL["bf16"], e
+    assert max(d) < 1e-3, d   # a state rounding to bf16 the other way moves an output ~1e-5
