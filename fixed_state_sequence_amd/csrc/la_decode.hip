@@ -50,12 +50,15 @@ struct DecArgs {
   float eps;
 };
 
-template <int DV, int DP>
+template <int DV, int DP, bool WIDE = false>
 struct DecCfg {
   // waves per state: a 32 KB state is split over two waves (16 rows of
   // float4 per lane), so that four waves fit per SIMD; larger states take
-  // one wave per 32 KB
-  static constexpr int WPS = DP * DV > 8192 ? DP * DV / 8192 : (DP * DV == 8192 ? 2 : 1);
+  // one wave per 32 KB.  WIDE: a 32 KB state over four waves (8 rows per
+  // lane), for state sets larger than the last-level cache (measured,
+  // 1024 x 16 states of 128 x 64: 200 -> 191 us per step; 256 x 16, which the
+  // cache holds: 49.2 -> 52.5 us, so the two-wave split stays there)
+  static constexpr int WPS = DP * DV > 8192 ? DP * DV / 8192 : (DP * DV == 8192 ? (WIDE ? 4 : 2) : 1);
   static constexpr int SPW = (NT / 64) / WPS;                      // states per workgroup
   static constexpr int CG = DV / 4;                                // float4 column groups
   static constexpr int RPI = 64 / CG;                              // rows per wave instruction
@@ -80,9 +83,9 @@ __device__ __forceinline__ void st4_stream(float* p, const float4& v) {
 }
 
 // DHMAX bounds the q, k width held in LDS (d_h <= 128 for RFF, d' for elu+1).
-template <typename DT, int DV, int DP, bool RFF, int DECAY>
+template <typename DT, int DV, int DP, bool RFF, int DECAY, bool WIDE>
 __global__ __launch_bounds__(NT) void decode_kernel(const DecArgs a) {
-  using G = DecCfg<DV, DP>;
+  using G = DecCfg<DV, DP, WIDE>;
   constexpr int DHMAX = RFF ? 128 : DP;       // q, k width held in LDS
   extern __shared__ __align__(16) float s_W[];  // RFF projection, [D][dhp]
   __shared__ __align__(16) float s_x[G::SPW][2][DHMAX];
@@ -289,19 +292,32 @@ __global__ __launch_bounds__(NT) void decode_kernel(const DecArgs a) {
   }
 }
 
-template <typename DT, int DV, int DP, bool RFF>
-hipError_t launch_decay(const DecArgs& a, la_decay kind, hipStream_t st) {
-  using G = DecCfg<DV, DP>;
+template <typename DT, int DV, int DP, bool RFF, bool WIDE>
+hipError_t launch_cfg(const DecArgs& a, la_decay kind, hipStream_t st) {
+  using G = DecCfg<DV, DP, WIDE>;
   const unsigned groups = unsigned((a.N + G::SPW - 1) / G::SPW);
   const dim3 grid{groups * unsigned(a.H)}, block{unsigned(NT)};
   const size_t lds = RFF ? size_t(DP / 2) * a.dhp * sizeof(float) : 0;
   switch (kind) {
-    case LA_DECAY_NONE: decode_kernel<DT, DV, DP, RFF, 0><<<grid, block, lds, st>>>(a); break;
-    case LA_DECAY_SSD: decode_kernel<DT, DV, DP, RFF, 1><<<grid, block, lds, st>>>(a); break;
-    case LA_GATE_RFA: decode_kernel<DT, DV, DP, RFF, 2><<<grid, block, lds, st>>>(a); break;
-    case LA_GATE_MLSTM: decode_kernel<DT, DV, DP, RFF, 3><<<grid, block, lds, st>>>(a); break;
+    case LA_DECAY_NONE: decode_kernel<DT, DV, DP, RFF, 0, WIDE><<<grid, block, lds, st>>>(a); break;
+    case LA_DECAY_SSD: decode_kernel<DT, DV, DP, RFF, 1, WIDE><<<grid, block, lds, st>>>(a); break;
+    case LA_GATE_RFA: decode_kernel<DT, DV, DP, RFF, 2, WIDE><<<grid, block, lds, st>>>(a); break;
+    case LA_GATE_MLSTM: decode_kernel<DT, DV, DP, RFF, 3, WIDE><<<grid, block, lds, st>>>(a); break;
   }
   return hipGetLastError();
+}
+
+// State sets beyond this many bytes stream from HBM rather than the 256 MB
+// last-level cache; 32 KB states then take the four-wave split.
+constexpr int64_t kLlcBytes = int64_t(256) << 20;
+
+template <typename DT, int DV, int DP, bool RFF>
+hipError_t launch_decay(const DecArgs& a, la_decay kind, hipStream_t st) {
+  if constexpr (DP * DV == 8192) {
+    if (int64_t(a.N) * a.H * (DP * DV + DP) * 4 > kLlcBytes)
+      return launch_cfg<DT, DV, DP, RFF, true>(a, kind, st);
+  }
+  return launch_cfg<DT, DV, DP, RFF, false>(a, kind, st);
 }
 
 template <typename DT, int DV, int DP>

@@ -111,6 +111,40 @@ def test_decode_rff_workload_full_size_sampled():
     assert max(e) < TOL["f32"], e
 
 
+@pytest.mark.parametrize("decay", ["rfa", "ssd", None])
+def test_decode_state_set_beyond_the_last_level_cache(decay):
+    """1027 sequences x 16 heads of 128 x 64 states (568 MB, more than the
+    256 MB last-level cache: the four-wave split of each state), 24 steps
+    from a zero state (random-feature denominators stay away from 0 as in the
+    decode workload); 40 sampled states (the last, partly filled workgroup
+    among them) followed by the oracle step by step."""
+    dev = gpu_device()
+    N, H, dh, D, steps = 1027, 16, 64, 64, 24
+    W = I.rff_projection(H, D, dh, seed=5)
+    S, z = la.state_init(N, H, 2 * D, dh, dev)
+    rng = np.random.default_rng(7)
+    ns = np.concatenate([rng.integers(0, N, 36), [N - 1, N - 2, N - 3, 0]])
+    hs = np.concatenate([rng.integers(0, H, 36), [15, 0, 7, 3]])
+    S_ref = S[ns, hs].double().cpu().numpy()
+    z_ref = z[ns, hs].double().cpu().numpy()
+    Wd = W.to(dev)
+    worst = 0.0
+    for t in range(steps):
+        st = I.rfa_decode_step_inputs(N, H, dh, step=t, seed=8, device=dev)
+        kw = {} if decay is None else ({"gate": st.gate} if decay == "rfa" else
+                                       {"decay": st.gate * 0.5 + 0.5})
+        o = la.decode_step(st.q, st.k, st.v, S, z, phi="rff", W=Wd, **kw)
+        torch.cuda.synchronize()
+        kwr = {n: t_[ns, hs].cpu() for n, t_ in kw.items()}
+        o_ref, S_ref, z_ref = O.decode_step(st.q[ns, hs].cpu(), st.k[ns, hs].cpu(),
+                                            st.v[ns, hs].cpu(), S_ref, z_ref, phi="rff",
+                                            W=W[torch.as_tensor(hs)], **kwr)
+        worst = max(worst, rel_err(o[ns, hs], o_ref))
+    e = (worst, rel_err(S[ns, hs], S_ref), rel_err(z[ns, hs], z_ref))
+    print("decode beyond the LLC", decay, e)
+    assert max(e) < TOL["f32"], e
+
+
 def test_mis_shaped_W_raises_before_any_launch():
     # W must be [H, rff_D, d_h]: fewer heads or a wrong input width would be
     # read out of bounds by the kernels, so the binding refuses it.
