@@ -617,26 +617,30 @@ void segment_state_kernel(const PfArgs a) {
 // the final one to the caller's, after every block here has read it).
 template <int D, int U, bool ML>
 __global__ __launch_bounds__(256) void segment_scan_kernel(const PfArgs a) {
+  // four consecutive state elements per thread (16-byte loads and stores)
   constexpr int E = D * D + D;
-  const int per_bh = (E + 255) / 256;
+  constexpr int E4 = E / 4;
+  static_assert(E % 4 == 0 && (D * D) % 4 == 0, "float4 elements");
+  const int per_bh = (E4 + 255) / 256;
   const int bh = blockIdx.x / per_bh;
-  const int e = (blockIdx.x % per_bh) * 256 + threadIdx.x;
+  const int e = 4 * ((blockIdx.x % per_bh) * 256 + int(threadIdx.x));
   if (e >= E) return;
   float* init = e < D * D ? a.S + int64_t(bh) * D * D + e : a.z + int64_t(bh) * D + (e - D * D);
-  float carry = *init;
+  f32x4 carry = *reinterpret_cast<const f32x4*>(init);
   float mc = ML ? a.stab[bh] : 0.f;
   float* base = a.ws_state + int64_t(bh) * a.nslot * E + e;
   const float* lg = a.ws_logg + int64_t(bh) * a.nslot;
   const float* mg = ML ? a.ws_m + int64_t(bh) * a.nslot : nullptr;
   float* m0g = ML ? a.ws_m0 + int64_t(bh) * (a.nseg + 1) : nullptr;
   for (int s0 = 0; s0 < a.nslot; s0 += U) {
-    float x[U], gm[U], mu[ML ? U : 1];
+    f32x4 x[U];
+    float gm[U], mu[ML ? U : 1];
     // unconditional loads (slot index clamped), so that all are in flight
     // together
 #pragma unroll
     for (int j = 0; j < U; ++j) {
       const int uc = min(s0 + j, a.nslot - 1);
-      x[j] = base[int64_t(uc) * E];
+      x[j] = *reinterpret_cast<const f32x4*>(base + int64_t(uc) * E);
       gm[j] = lg[uc];
       if constexpr (ML) mu[j] = mg[uc];
     }
@@ -645,20 +649,24 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(const PfArgs a) {
       const int u = s0 + j;
       if (u < a.nslot) {
         if (u % a.nsub == 0) {
-          base[int64_t(u) * E] = carry;
+          *reinterpret_cast<f32x4*>(base + int64_t(u) * E) = carry;
           if (ML && e == 0) m0g[u / a.nsub] = mc;
         }
         if constexpr (ML) {
           const float mn = fmaxf(mc + gm[j], mu[j]);
-          carry = fmaf(__expf(mc + gm[j] - mn), carry, __expf(mu[j] - mn) * x[j]);
+          const float f0 = __expf(mc + gm[j] - mn), f1 = __expf(mu[j] - mn);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) carry[i] = fmaf(f0, carry[i], f1 * x[j][i]);
           mc = mn;
         } else {
-          carry = fmaf(__expf(gm[j]), carry, x[j]);
+          const float g = __expf(gm[j]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) carry[i] = fmaf(g, carry[i], x[j][i]);
         }
       }
     }
   }
-  *init = carry;
+  *reinterpret_cast<f32x4*>(init) = carry;
   if (ML && e == 0) m0g[a.nseg] = mc;
 }
 
@@ -1197,16 +1205,12 @@ hipError_t launch3(const PfArgs& a, int64_t BH, int stage, hipStream_t st) {
     segment_state_kernel<D, C, DECAY, DT><<<dim3(unsigned(BH * a.nslot)), dim3(2 * G::NT), 0, st>>>(a);
   } else if (stage == 2) {
     if (!scan) return hipSuccess;
-    const int per_bh = (D * D + D + 255) / 256;
-    // up to 64 slots in flight at once; 32 with the mLSTM gates, whose
-    // stabilisers take a third set of registers (64 would leave one wave
-    // per SIMD)
+    const int per_bh = ((D * D + D) / 4 + 255) / 256;
+    // 16 slots of four elements in flight at once per thread (64 registers)
     if constexpr (DECAY == 3)
-      segment_scan_kernel<D, 32, true><<<dim3(unsigned(BH * per_bh)), dim3(256), 0, st>>>(a);
-    else if (a.nslot <= 32)
-      segment_scan_kernel<D, 32, false><<<dim3(unsigned(BH * per_bh)), dim3(256), 0, st>>>(a);
+      segment_scan_kernel<D, 16, true><<<dim3(unsigned(BH * per_bh)), dim3(256), 0, st>>>(a);
     else
-      segment_scan_kernel<D, 64, false><<<dim3(unsigned(BH * per_bh)), dim3(256), 0, st>>>(a);
+      segment_scan_kernel<D, 16, false><<<dim3(unsigned(BH * per_bh)), dim3(256), 0, st>>>(a);
   } else if (a.nc) {
     if constexpr (DECAY != 0) return hipErrorInvalidValue;   // rejected on the host
     else output_kernel<D, C, 0, DT, true><<<dim3(unsigned(BH * a.nseg)), dim3(2 * G::NT), 0, st>>>(a);
