@@ -31,9 +31,11 @@ Sources (the three pages the method is described on):
            overflow) and, in "Implementation sketch", the remark that the
            mLSTM step is this loop with the identity feature map.
 
-Every function is pinned by ``tests/test_oracle_pins.py`` and
-``tests/test_oracle_mlstm_pins.py`` against facts the pages or the
-mathematics fix (closed forms, brute force, printed values).
+Every function is pinned by ``tests/test_oracle_pins.py``,
+``tests/test_oracle_mlstm_pins.py`` and (the gradients)
+``tests/test_oracle_backward_pins.py`` against facts the pages or the
+mathematics fix (closed forms, brute force, printed values, central finite
+differences of the forward definition).
 
 Layout convention: ``[..., T, d]`` with any leading dims (batch, head);
 decay/gate arrays are ``[..., T]``.  Feature dimension ``d'`` is ``d_h`` for
