@@ -63,7 +63,13 @@ namespace {
 // within-chunk log-prefix; e^-80 ~ 1.8e-35 is the smallest decay applied.
 constexpr float kLogFloor = -80.0f;
 
-template <int D, int C, bool VS>
+// The output stage holds its carried state as S = e^lp acc and lets the
+// chunks' decays accumulate in lp (the fold operands take e^-lp instead)
+// while |lp| stays within this bound; past it the accumulators take the
+// factor and lp restarts from 0.  e^30 ~ 1e13 leaves fp32 ample range.
+constexpr float kDeferLog = 30.0f;
+
+template <int D, int C, bool VS, bool DMT = false>
 struct Cfg {
   static constexpr int NW = D / 32;          // waves, 32 value columns each
   static constexpr int NT = 64 * NW;         // threads per workgroup (= 2 D)
@@ -128,7 +134,13 @@ struct Cfg {
   // the first 64, so that feature blocks fb and fb + 8 (read together by a
   // wave) fall in different banks
   static constexpr int DZS = D + (D > 64 ? 4 : 0);
-  static constexpr int BUF = B_DZ + 4 * NW * DZS;
+  // DM (DMT: decays with 32-token chunks): the chunk's decay mask
+  // e^{lc_t - lc_s} beta_s (0 for s > t), fp32, row t = query token, DMS
+  // floats per row (rows 16-byte aligned, 8 rows cover the 32 banks)
+  static constexpr bool HAS_DM = DMT;
+  static constexpr int DMS = C + 4;
+  static constexpr int B_DM = B_DZ + 4 * NW * DZS;
+  static constexpr int BUF = B_DM + (DMT ? 4 * C * DMS : 0);
   // The output stage: producer waves stage chunk c + 1 into one buffer while
   // consumer waves compute chunk c from the other, when two buffers fit; each
   // buffer also carries the chunk's total log-decay.
@@ -687,7 +699,8 @@ template <int D, int C, int DECAY, typename DT, bool NC = false>
 __global__ __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void output_kernel(const PfArgs a) {
   constexpr bool VS = __is_same(DT, f16_t);   // fp16 v needs a bf16 low part too
-  using G = Cfg<D, C, VS>;
+  // decays with 32-token chunks take the decay mask from the producers (DM)
+  using G = Cfg<D, C, VS, DECAY != 0 && C == 32 && !NC>;
   __shared__ __align__(16) char smem[G::LDS];
   const int nseg = a.nseg;
   const int bh = blockIdx.x / nseg;
@@ -735,6 +748,8 @@ void output_kernel(const PfArgs a) {
     if constexpr (DECAY == 3) m0 = from_ws ? a.ws_m0[int64_t(bh) * (nseg + 1) + seg] : a.stab[bh];
     // log of the decay from the segment's start to the chunk being staged
     float lrun = 0.f;
+    // the consumers' state scale after the chunks staged so far (S = e^lp acc)
+    float lp = 0.f;
 
     using Raw = RawChunk<G::RPT, G::ND, true, !NC, DECAY == 3>;
     auto fetch = [&](Raw& r, int c) {
@@ -783,6 +798,13 @@ void output_kernel(const PfArgs a) {
       // the chunks read out (prec) and folded (exact) at high + low precision (see QR)
       const bool prec = DECAY != 3 && tok0 < G::PRECISE && (DECAY == 0 || lrun > G::PREC_LOG);
       const bool exact = DECAY != 3 && tok0 < G::EXACT;
+      // log of the carry factor: the chunk's total log-decay (mLSTM: m0 - mu_last)
+      const float lgam = DECAY == 3 ? m0 - mend : ltot;
+      // the consumers keep the state at scale e^lp: while |lp + lgam| stays
+      // within kDeferLog the decay goes into lp and the fold weights take
+      // e^-(lp + lgam); past it the consumers apply the factor (lp = 0)
+      const float lnew = lp + lgam;
+      const float lsc = DECAY != 0 && fabsf(lnew) <= kDeferLog ? lnew : 0.f;
 #pragma unroll
       for (int i = 0; i < G::RPT; ++i) {
         const int r = G::RPT * rg + i;
@@ -795,14 +817,14 @@ void output_kernel(const PfArgs a) {
           // so that e^{lct_t - lct_s} beta_s = e^{a_s - mu_t}; m_t = lc_t + mu_t
           const float mu = lane_value<C>(mlo, mhi, r), at = lane_value<C>(alo, ahi, r);
           lct = m0 - mu;
-          beta = __expf(at - mu);
-          w = tok0 + r < a.T ? __expf(at - mend) : 0.f;
+          if constexpr (!G::HAS_DM) beta = __expf(at - mu);   // else in the decay mask
+          w = tok0 + r < a.T ? __expf(at - mend - lsc) : 0.f;
           mt = lane_value<C>(lo, hi, r) + mu;
         } else if constexpr (DECAY != 0) {
           lct = lane_value<C>(lo, hi, r);
           if constexpr (DECAY == 2)
             beta = 1.f - lane_value<C>(raw.d[0], G::ND > 1 ? raw.d[G::ND - 1] : 0.f, r);
-          w = tok0 + r < a.T ? beta * __expf(ltot - lct) : 0.f;
+          w = tok0 + r < a.T ? beta * __expf(ltot - lct - lsc) : 0.f;
         }
         float den = 0.f;
 #pragma unroll
@@ -856,18 +878,46 @@ void output_kernel(const PfArgs a) {
       {
         float s0, s1;
         const int base = reduce_scatter8<G::FB>(dz, lane, s0, s1);
+        if constexpr (DECAY != 0) {   // z itself is kept at scale 1
+          const float f = __expf(lsc);
+          s0 *= f;
+          s1 *= f;
+        }
         if (G::FB == 16 || !(lane & 8))
           *reinterpret_cast<f32x2*>(reinterpret_cast<float*>(buf + G::B_DZ) + wave * G::DZS +
                                     dz_index(fb, base)) = f32x2{s0, s1};
       }
-      // log of the carry factor: the chunk's total log-decay (mLSTM: m0 - mu_last)
-      const float lgam = DECAY == 3 ? m0 - mend : ltot;
+      if constexpr (G::HAS_DM) {
+        // the decay mask of the chunk's scores, DM[t][s] = e^{lc_t - lc_s}
+        // beta_s for s <= t (mLSTM: e^{a_s - mu_t}), else 0; four entries per
+        // thread and pass, every lane in every cross-lane read
+#pragma unroll
+        for (int idx = ts; idx < C * C / 4; idx += G::NT) {
+          const int t = idx / (C / 4), s0 = 4 * (idx % (C / 4));
+          const float rt = DECAY == 3 ? lane_value<C>(mlo, mhi, t) : lane_value<C>(lo, hi, t);
+          f32x4 dm;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float x;
+            if constexpr (DECAY == 3) {
+              x = __expf(lane_value<C>(alo, ahi, s0 + e) - rt);
+            } else {
+              x = __expf(rt - lane_value<C>(lo, hi, s0 + e));
+              if constexpr (DECAY == 2)
+                x *= 1.f - lane_value<C>(raw.d[0], G::ND > 1 ? raw.d[G::ND - 1] : 0.f, s0 + e);
+            }
+            dm[e] = s0 + e <= t ? x : 0.f;
+          }
+          *reinterpret_cast<f32x4*>(buf + G::B_DM + 4 * (t * G::DMS + s0)) = dm;
+        }
+      }
       if (ts == 0) *reinterpret_cast<float*>(buf + G::B_LT) = lgam;
       if constexpr (DECAY == 3) {
         if (c < c1) m0 = ltot + mend;   // the stabiliser after this chunk
       } else if constexpr (DECAY != 0) {
         if (c < c1) lrun += ltot;
       }
+      if (c < c1) lp = lsc;
       // refill this register set with the chunk PDEPTH ahead (clamped)
       fetch(raw, min(c + G::PDEPTH, c1 - 1));
       return lgam;
@@ -944,6 +994,8 @@ void output_kernel(const PfArgs a) {
     // log of the decay from the segment's start to the chunk being computed
     // (the producers' lrun, from the chunks' totals)
     float lrun = 0.f;
+    // the state is S = e^lp acc (decays only; the producers track lp alike)
+    float lp = 0.f;
     // [B] read-out of the carried state, masked intra-chunk attention,
     // normalise and store, then fold the chunk into S.
     auto compute = [&](int c, const char* buf) {
@@ -965,10 +1017,22 @@ void output_kernel(const PfArgs a) {
       // follows the read-out directly (which has consumed the state by
       // then), so its MFMA chains overlap the masking and P V work.
       auto fold_hi = [&]() {
-        const float gam = DECAY ? __expf(*reinterpret_cast<const float*>(buf + G::B_LT)) : 1.f;
+        if constexpr (DECAY != 0) {
+          // the chunk's decay goes into lp, or into the accumulators once
+          // |lp| would pass kDeferLog (the producers, who scaled the fold
+          // weights by e^-lp, made the same choice from the same values)
+          const float lnew = lp + *reinterpret_cast<const float*>(buf + G::B_LT);
+          if (fabsf(lnew) <= kDeferLog) {
+            lp = lnew;
+          } else {
+            const float gam = __expf(lnew);
+#pragma unroll
+            for (int mt = 0; mt < G::MT; ++mt) acc[mt] *= gam;
+            lp = 0.f;
+          }
+        }
 #pragma unroll
         for (int mt = 0; mt < G::MT; ++mt) {
-          if constexpr (DECAY != 0) acc[mt] *= gam;
 #pragma unroll
           for (int kk = 0; kk < G::KT; ++kk) {
             const u32x4 kh = tr_operand<D>(buf + G::B_KH, 16 * kk, 32 * mt, lane);
@@ -989,6 +1053,7 @@ void output_kernel(const PfArgs a) {
       bool prec = !NC && DECAY == 0 && tok0 < G::PRECISE;
       if constexpr (!NC && DECAY != 0 && DECAY != 3) prec = tok0 < G::PRECISE && lrun > G::PREC_LOG;
       const bool exact = !NC && DECAY != 3 && tok0 < G::EXACT;
+      const float lp0 = lp;   // the scale of the state this chunk reads out
 #pragma unroll
       for (int tb = 0; tb < G::TB; ++tb) {
         const int tl = 32 * tb + n;   // this lane's query token within the chunk
@@ -1042,7 +1107,7 @@ void output_kernel(const PfArgs a) {
         float lct = 0.f;
         if constexpr (DECAY != 0) {
           lct = Ll[tl];
-          o *= __expf(lct);
+          o *= __expf(lct + lp0);
         }
         float dsum = 0.f;
 #pragma unroll
@@ -1060,14 +1125,29 @@ void output_kernel(const PfArgs a) {
                 p = low_scores<D, G::KS>(buf + G::B_K, buf + G::B_QR, 32 * sb + n, tl, g, p);
             }
           }
+          if constexpr (G::HAS_DM) {
+            // one 32-token block: the producers' decay mask, causal zeros included
+            const float* dml = reinterpret_cast<const float*>(buf + G::B_DM) + tl * G::DMS + 4 * g;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int sl = 32 * sb + 8 * (r >> 2) + 4 * g + (r & 3);
-            float x = p[r];
-            if constexpr (DECAY != 0) x *= __expf(lct - Ll[sl]) * Bl[sl];
-            if (sb == tb && sl > tl) x = 0.f;
-            p[r] = x;
-            dsum += x;
+            for (int j = 0; j < 4; ++j) {
+              const f32x4 m = *reinterpret_cast<const f32x4*>(dml + 8 * j);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const float x = p[4 * j + e] * m[e];
+                p[4 * j + e] = x;
+                dsum += x;
+              }
+            }
+          } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int sl = 32 * sb + 8 * (r >> 2) + 4 * g + (r & 3);
+              float x = p[r];
+              if constexpr (DECAY != 0) x *= __expf(lct - Ll[sl]) * Bl[sl];
+              if (sb == tb && sl > tl) x = 0.f;
+              p[r] = x;
+              dsum += x;
+            }
           }
           // P = P_hi + P_lo (bf16 each): the P V product then carries the
           // fp32 scores the denominator sums, to ~2^-16.
@@ -1166,12 +1246,13 @@ void output_kernel(const PfArgs a) {
     }
     if (fin) {
       float* Sd = a.S + int64_t(bh) * D * D;
+      const float sc = DECAY != 0 ? __expf(lp) : 1.f;
 #pragma unroll
       for (int mt = 0; mt < G::MT; ++mt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int f = 32 * mt + 8 * (r >> 2) + 4 * g + (r & 3);
-          Sd[f * D + 32 * wave + n] = acc[mt][r];
+          Sd[f * D + 32 * wave + n] = acc[mt][r] * sc;
         }
     }
   }
