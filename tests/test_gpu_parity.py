@@ -210,6 +210,30 @@ def test_decay_zero_and_one():
     assert rel_err(o, o_ref) < TOL["bf16"] and rel_err(S, S_ref) < TOL["bf16"]
 
 
+@pytest.mark.parametrize("kind", ["ssd", "rfa"])
+def test_decay_carry_deferred_then_applied(kind):
+    """The output stage keeps the chunks' carry factors in a running log
+    scale while it stays within a bound, then applies it to the state.
+    Decays of 1 (gate 0.999) with sparse strong ones make that scale cross
+    the bound at several places inside a segment, once within one chunk
+    (a decay of 1e-20); every output and the final state against the oracle."""
+    dev = gpu_device()
+    T = 1500
+    x = I.prefill_inputs(1, 2, T, 128, dtype="bf16", seed=21)
+    a = torch.full((1, 2, T), 1.0 if kind == "ssd" else 0.999)
+    a[:, :, 37::37] = 0.02
+    a[:, 1, 900] = 1e-20
+    kw = dict(decay=a) if kind == "ssd" else dict(gate=a)
+    o_ref, S_ref, z_ref = O.causal_linear_attention(x.q, x.k, x.v, **kw)
+    for segments in (1, 0, 3):
+        o, S, z = la.prefill(x.q.to(dev), x.k.to(dev), x.v.to(dev), segments=segments,
+                             out_dtype=torch.float32, **{n: t.to(dev) for n, t in kw.items()})
+        torch.cuda.synchronize()
+        e = (rel_err(o, o_ref), rel_err(S, S_ref), rel_err(z, z_ref))
+        print(kind, segments, e)
+        assert max(e) < TOL["bf16"], e
+
+
 def test_prefill_stages_compose_to_prefill():
     dev = gpu_device()
     x = I.prefill_inputs(1, 4, 700, 128, dtype="bf16", seed=2)
