@@ -442,7 +442,7 @@ void segment_state_kernel(const PfArgs a) {
         for (int off = 32; off >= 1; off >>= 1) cm = fmaxf(cm, __shfl_xor(cm, off));
         Mn = fmaxf(M, cm + lsuf + ltot);
         const float sc = __expf(M - Mn);
-        if (live) {
+        if (live && sc != 1.f) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) zp[e] *= sc;
         }
@@ -571,9 +571,13 @@ void segment_state_kernel(const PfArgs a) {
     // (mLSTM: the state is first rescaled to the new running maximum)
     auto fold = [&](const char* buf, int i) {
       if constexpr (DECAY == 3) {
+        // the running maximum seldom grows after the segment's last chunks
+        // (folded first), so the factor is mostly exactly 1: skip it then
         const float sc = s1_scale[i & 1];
+        if (sc != 1.f) {
 #pragma unroll
-        for (int mt = 0; mt < G::MT; ++mt) acc[mt] *= sc;
+          for (int mt = 0; mt < G::MT; ++mt) acc[mt] *= sc;
+        }
       }
       u32x4 vh[G::KT], vl[G::KT];
 #pragma unroll
