@@ -839,10 +839,12 @@ void output_kernel(const PfArgs a) {
           }
           den = fmaf(qx[e], zf[e], den);
         }
-        const u32x4 qp = pack8(qx);
+        // identity features of bf16 inputs (mLSTM): the tiles are the inputs
+        constexpr bool RAW = DECAY == 3 && __is_same(DT, bf16_t);
+        const u32x4 qp = RAW ? raw.q[i] : pack8(qx);
         row_write_perm<D>(buf + G::B_Q, r, fb, qp);
         if (prec || exact) row_write_perm<D>(buf + G::B_QR, r, fb, low8(qx, qp));
-        const u32x4 kp = pack8(kx);
+        const u32x4 kp = RAW ? raw.k[i] : pack8(kx);
         row_write_perm<D>(buf + G::B_K, r, fb, kp);
         if (tok0 < G::EXACT) row_write_perm<D>(buf + G::B_KR, r, fb, low8(kx, kp));
         if constexpr (DECAY != 0) {
