@@ -169,3 +169,47 @@ def test_backward_sweep(case):
     errs = {k: rel_err(got[k], ref[k]) for k in got}
     print("errors", errs)
     assert max(errs.values()) < TOL["bf16"], (c, errs)
+
+
+def _decode_cases(n, seed):
+    r = random.Random(seed)
+    for i in range(n):
+        phi = r.choice(["elu1", "elu1", "rff"])
+        yield dict(i=i, N=r.choice([1, 3, 7, 33]), H=r.choice([1, 2, 4]),
+                   dh=r.choice([16, 32, 64, 100, 128, 256]), dv=r.choice([16, 32, 64, 128]),
+                   phi=phi, D=r.choice([16, 32, 64, 128]) if phi == "rff" else 0,
+                   decay=r.choice([None, "ssd", "rfa"]), dtype=r.choice(["f32", "f32", "bf16"]),
+                   steps=r.randint(2, 6), seed=4000 + i)
+
+
+@pytest.mark.parametrize("case", list(_decode_cases(24, 17)), ids=lambda c: f"d{c['i']}")
+def test_decode_sweep(case):
+    """Decode steps from a zero state (the specialised kernels and the
+    per-token one, by shape), output of every step and the final state."""
+    dev = gpu_device()
+    c = case
+    print(c, flush=True)
+    N, H, dh, dv, phi, D = c["N"], c["H"], c["dh"], c["dv"], c["phi"], c["D"]
+    W = I.rff_projection(H, D, dh, seed=c["seed"]) if phi == "rff" else None
+    dp = 2 * D if phi == "rff" else dh
+    S, z = la.state_init(N, H, dp, dv, dev)
+    S_ref, z_ref = np.zeros((N, H, dp, dv)), np.zeros((N, H, dp))
+    sd = I.DTYPES[c["dtype"]]
+    worst = 0.0
+    for step in range(c["steps"]):
+        st = I.rfa_decode_step_inputs(N, H, dh, dv, step=step, seed=c["seed"])
+        q, k, v = st.q.to(sd), st.k.to(sd), st.v.to(sd)
+        kw = {}
+        if c["decay"] == "ssd":
+            kw["decay"] = st.gate * 0.5 + 0.5
+        elif c["decay"] == "rfa":
+            kw["gate"] = st.gate
+        o = la.decode_step(q.to(dev), k.to(dev), v.to(dev), S, z, phi=phi,
+                           W=None if W is None else W.to(dev),
+                           **{n: t.to(dev) for n, t in kw.items()}, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        o_ref, S_ref, z_ref = O.decode_step(q, k, v, S_ref, z_ref, phi=phi, W=W, **kw)
+        worst = max(worst, rel_err(o, o_ref))
+    e = (worst, rel_err(S, S_ref), rel_err(z, z_ref))
+    print("errors", e)
+    assert max(e) < TOL[c["dtype"]], (c, e)
