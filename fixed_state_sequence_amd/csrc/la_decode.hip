@@ -55,9 +55,10 @@ struct DecCfg {
   // waves per state: a 32 KB state is split over two waves (16 rows of
   // float4 per lane), so that four waves fit per SIMD; larger states take
   // one wave per 32 KB.  WIDE: a 32 KB state over four waves (8 rows per
-  // lane), for state sets larger than the last-level cache (measured,
-  // 1024 x 16 states of 128 x 64: 200 -> 191 us per step; 256 x 16, which the
-  // cache holds: 49.2 -> 52.5 us, so the two-wave split stays there)
+  // lane), for state sets larger than the last-level cache (measured with
+  // streamed accesses, 1024 x 16 states of 128 x 64: 200 -> 191 us per step;
+  // 256 x 16, which the cache holds: 49.2 -> 52.5 us, so the two-wave split
+  // stays there)
   static constexpr int WPS = DP * DV > 8192 ? DP * DV / 8192 : (DP * DV == 8192 ? (WIDE ? 4 : 2) : 1);
   static constexpr int SPW = (NT / 64) / WPS;                      // states per workgroup
   static constexpr int CG = DV / 4;                                // float4 column groups
@@ -71,8 +72,13 @@ struct DecCfg {
 
 __device__ __forceinline__ float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
 
-// The state is read and written exactly once per step: stream it past the
-// caches (nontemporal loads and stores).
+// The state is read and written exactly once per step.  A state set larger
+// than the last-level cache is streamed past the caches (nontemporal loads
+// and stores); a smaller one is loaded and stored normally, so that it stays
+// in that cache from one step to the next.  Measured on 128 x 64 fp32
+// states, 16 heads: up to 480 sequences (256 MB) normal accesses run at
+// 0.75-0.79 of 8 TB/s against 0.68-0.72 streamed; at 640 sequences (341 MB)
+// streaming wins (0.72 against 0.68), at 1024 (545 MB) 0.72 against 0.65.
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ float4 ld4_stream(const float* p) {
   const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
@@ -81,11 +87,14 @@ __device__ __forceinline__ float4 ld4_stream(const float* p) {
 __device__ __forceinline__ void st4_stream(float* p, const float4& v) {
   __builtin_nontemporal_store(f32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<f32x4_t*>(p));
 }
+__device__ __forceinline__ void st4(float* p, const float4& v) { *reinterpret_cast<float4*>(p) = v; }
 
 // DHMAX bounds the q, k width held in LDS (d_h <= 128 for RFF, d' for elu+1).
-template <typename DT, int DV, int DP, bool RFF, int DECAY, bool WIDE>
+// BIG: the call's state set exceeds the last-level cache (streamed state
+// accesses; 32 KB states over four waves).
+template <typename DT, int DV, int DP, bool RFF, int DECAY, bool BIG>
 __global__ __launch_bounds__(NT) void decode_kernel(const DecArgs a) {
-  using G = DecCfg<DV, DP, WIDE>;
+  using G = DecCfg<DV, DP, BIG>;
   constexpr int DHMAX = RFF ? 128 : DP;       // q, k width held in LDS
   extern __shared__ __align__(16) float s_W[];  // RFF projection, [D][dhp]
   __shared__ __align__(16) float s_x[G::SPW][2][DHMAX];
@@ -107,7 +116,8 @@ __global__ __launch_bounds__(NT) void decode_kernel(const DecArgs a) {
   float4 s[G::NI];
 #pragma unroll
   for (int i = 0; i < G::NI; ++i)
-    s[i] = ld4_stream(Sg + (row0 + i) * DV + 4 * cg);   // st points at a real state even if !valid
+    s[i] = BIG ? ld4_stream(Sg + (row0 + i) * DV + 4 * cg)   // st points at a real state even if !valid
+               : ld4(Sg + (row0 + i) * DV + 4 * cg);
   float* zg = a.z + st * DP;
   float zr[G::ZPL];
 #pragma unroll
@@ -236,7 +246,10 @@ __global__ __launch_bounds__(NT) void decode_kernel(const DecArgs a) {
   }
   if (valid) {
 #pragma unroll
-    for (int i = 0; i < G::NI; ++i) st4_stream(Sg + (row0 + i) * DV + 4 * cg, s[i]);
+    for (int i = 0; i < G::NI; ++i) {
+      if constexpr (BIG) st4_stream(Sg + (row0 + i) * DV + 4 * cg, s[i]);
+      else st4(Sg + (row0 + i) * DV + 4 * cg, s[i]);
+    }
   }
   float den = 0.f;
 #pragma unroll
@@ -292,31 +305,30 @@ __global__ __launch_bounds__(NT) void decode_kernel(const DecArgs a) {
   }
 }
 
-template <typename DT, int DV, int DP, bool RFF, bool WIDE>
+template <typename DT, int DV, int DP, bool RFF, bool BIG>
 hipError_t launch_cfg(const DecArgs& a, la_decay kind, hipStream_t st) {
-  using G = DecCfg<DV, DP, WIDE>;
+  using G = DecCfg<DV, DP, BIG>;
   const unsigned groups = unsigned((a.N + G::SPW - 1) / G::SPW);
   const dim3 grid{groups * unsigned(a.H)}, block{unsigned(NT)};
   const size_t lds = RFF ? size_t(DP / 2) * a.dhp * sizeof(float) : 0;
   switch (kind) {
-    case LA_DECAY_NONE: decode_kernel<DT, DV, DP, RFF, 0, WIDE><<<grid, block, lds, st>>>(a); break;
-    case LA_DECAY_SSD: decode_kernel<DT, DV, DP, RFF, 1, WIDE><<<grid, block, lds, st>>>(a); break;
-    case LA_GATE_RFA: decode_kernel<DT, DV, DP, RFF, 2, WIDE><<<grid, block, lds, st>>>(a); break;
-    case LA_GATE_MLSTM: decode_kernel<DT, DV, DP, RFF, 3, WIDE><<<grid, block, lds, st>>>(a); break;
+    case LA_DECAY_NONE: decode_kernel<DT, DV, DP, RFF, 0, BIG><<<grid, block, lds, st>>>(a); break;
+    case LA_DECAY_SSD: decode_kernel<DT, DV, DP, RFF, 1, BIG><<<grid, block, lds, st>>>(a); break;
+    case LA_GATE_RFA: decode_kernel<DT, DV, DP, RFF, 2, BIG><<<grid, block, lds, st>>>(a); break;
+    case LA_GATE_MLSTM: decode_kernel<DT, DV, DP, RFF, 3, BIG><<<grid, block, lds, st>>>(a); break;
   }
   return hipGetLastError();
 }
 
 // State sets beyond this many bytes stream from HBM rather than the 256 MB
-// last-level cache; 32 KB states then take the four-wave split.
+// last-level cache: streamed accesses, and 32 KB states take the four-wave
+// split.
 constexpr int64_t kLlcBytes = int64_t(256) << 20;
 
 template <typename DT, int DV, int DP, bool RFF>
 hipError_t launch_decay(const DecArgs& a, la_decay kind, hipStream_t st) {
-  if constexpr (DP * DV == 8192) {
-    if (int64_t(a.N) * a.H * (DP * DV + DP) * 4 > kLlcBytes)
-      return launch_cfg<DT, DV, DP, RFF, true>(a, kind, st);
-  }
+  if (int64_t(a.N) * a.H * (DP * DV + DP) * 4 > kLlcBytes)
+    return launch_cfg<DT, DV, DP, RFF, true>(a, kind, st);
   return launch_cfg<DT, DV, DP, RFF, false>(a, kind, st);
 }
 
