@@ -33,7 +33,8 @@ Sources (the three pages the method is described on):
 
 Every function is pinned by ``tests/test_oracle_pins.py``,
 ``tests/test_oracle_mlstm_pins.py`` and (the gradients)
-``tests/test_oracle_backward_pins.py`` against facts the pages or the
+``tests/test_oracle_backward_pins.py`` and
+``tests/test_oracle_mlstm_backward_pins.py`` against facts the pages or the
 mathematics fix (closed forms, brute force, printed values, central finite
 differences of the forward definition).
 
@@ -677,6 +678,77 @@ def prefill_gradients(q, k, v, dout, phi="elu1", decay=None, gate=None, eps=1e-6
     return res
 
 
+def _reverse_mode_head(fq, fk, vv, do, al, be, S, z, readout):
+    """Reverse mode through S_t = al_t S_{t-1} + be_t phi(k_t) v_t^T (z
+    likewise) for one head, in float64.  readout(t, num, den) gives the
+    read-out's (g_t, h_t): the gradients of L with respect to the numerator
+    and the divisor's dot product.  Returns (dphi(q), dphi(k), dv, dL/dal,
+    dL/dbe, G, gz) with G, gz the gradient state before the first token, and
+    dL/dal_r = <G_r, S_{r-1}> + <gz_r, z_{r-1}> (no division by al_r).  The
+    walk back needs S_{r-1} beside G_r: the forward walk keeps the state
+    every CKPT tokens, and each block of CKPT tokens is walked forward again
+    from its checkpoint before it is walked back."""
+    CKPT = 64
+    T, dp = fq.shape
+    dv_ = vv.shape[-1]
+    g = np.empty((T, dv_))
+    h = np.empty(T)
+    dfq = np.empty((T, dp))
+    ckpt = {}                 # the state before token t, every CKPT tokens
+    for t in range(T):
+        if t % CKPT == 0:
+            ckpt[t] = (S.copy(), z.copy())
+        S = al[t] * S + be[t] * np.outer(fk[t], vv[t])
+        z = al[t] * z + be[t] * fk[t]
+        g[t], h[t] = readout(t, fq[t] @ S, fq[t] @ z)
+        dfq[t] = S @ g[t] + z * h[t]
+    G = np.zeros((dp, dv_))
+    gz = np.zeros(dp)
+    dfk = np.empty((T, dp))
+    dvv = np.empty((T, dv_))
+    dal = np.empty(T)
+    dbe = np.empty(T)
+    for b0 in sorted(ckpt, reverse=True):
+        b1 = min(b0 + CKPT, T)
+        Sp, zp = ckpt[b0]
+        prev = []             # (S_{t-1}, z_{t-1}) for t in [b0, b1)
+        for t in range(b0, b1):
+            prev.append((Sp, zp))
+            Sp = al[t] * Sp + be[t] * np.outer(fk[t], vv[t])
+            zp = al[t] * zp + be[t] * fk[t]
+        for t in range(b1 - 1, b0 - 1, -1):
+            a_next = al[t + 1] if t + 1 < T else 0.0
+            G = a_next * G + np.outer(fq[t], g[t])
+            gz = a_next * gz + fq[t] * h[t]
+            u = G @ vv[t] + gz
+            dfk[t] = be[t] * u
+            dvv[t] = be[t] * (fk[t] @ G)
+            dbe[t] = fk[t] @ u
+            Sm, zm = prev[t - b0]
+            dal[t] = (G * Sm).sum() + gz @ zm
+    return dfq, dfk, dvv, dal, dbe, G, gz
+
+
+def _readout_grads(normalize, eps, floor=1.0):
+    """(g_t, h_t) of the read-out from its numerator and divisor dot product:
+    the sum form num / (den + eps), the numerator alone, or num / max(|den|,
+    floor).  With a state held scaled by e^{-m_t} (the mLSTM gates) the same
+    read-outs of the true state are num' / (den' + eps e^{-m_t}), e^{m_t}
+    num' and num' / max(|den'|, e^{-m_t}): eps, the scale and the floor
+    given per token."""
+    def grads(do, num, den, eps_t, scale_t, floor_t):
+        if normalize is True:
+            Dv = den + eps_t
+            return do / Dv, -(do @ (num / Dv)) / Dv
+        if normalize is False:
+            return do * scale_t, 0.0
+        if normalize == "max1":
+            Dv = max(abs(den), floor_t)
+            return do / Dv, (-np.sign(den) * (do @ (num / Dv)) / Dv if abs(den) > floor_t else 0.0)
+        raise ValueError(f"unknown read-out {normalize!r}")
+    return grads
+
+
 def prefill_gradients_recurrent(q, k, v, dout, phi="elu1", decay=None, gate=None, eps=1e-6,
                                 S0=None, z0=None, normalize=True):
     """The same gradients as prefill_gradients, by reverse mode through the
@@ -696,15 +768,11 @@ def prefill_gradients_recurrent(q, k, v, dout, phi="elu1", decay=None, gate=None
     and G_r is the gradient of S_r, so
         dL/dalpha_r = <G_r, S_{r-1}> + <gz_r, z_{r-1}>,
         dL/dbeta_t = phi(k_t) . u_t,
-    with no division by alpha (alpha_r = 0, a full reset, included).  The
-    walk back needs S_{r-1} beside G_r: the forward walk keeps the state
-    every CKPT tokens, and each block of CKPT tokens is walked forward again
-    from its checkpoint before it is walked back.
+    with no division by alpha (alpha_r = 0, a full reset, included).
     The initial state enters S_t as prod_{r<=t} alpha_r S0: dS0 = alpha_0 G,
     dz0 = alpha_0 gz after the walk.  Returns a dict with dq, dk, dv, dS0,
     dz0 and ddecay (with decay) or dgate (with gate).
     """
-    CKPT = 64
     fq_all, fk_all = features(q, phi), features(k, phi)
     dphq, dphk = phi_derivative(q, phi), phi_derivative(k, phi)
     v_all, do_all = _f64(v), _f64(dout)
@@ -715,70 +783,94 @@ def prefill_gradients_recurrent(q, k, v, dout, phi="elu1", decay=None, gate=None
     res = {n: np.zeros(lead + shp) for n, shp in (("dq", (T, q.shape[-1])), ("dk", (T, k.shape[-1])),
                                                   ("dv", (T, dv_)), ("dS0", (dp, dv_)), ("dz0", (dp,)),
                                                   ("dalpha", (T,)), ("dbeta", (T,)))}
+    grads = _readout_grads(normalize, eps)
     for idx in np.ndindex(*lead):
-        fq, fk, vv, do = fq_all[idx], fk_all[idx], v_all[idx], do_all[idx]
+        do = do_all[idx]
         al = np.ones(T) if alpha_all is None else alpha_all[idx]
         be = np.ones(T) if beta_all is None else beta_all[idx]
         S = np.zeros((dp, dv_)) if S0 is None else _f64(S0)[idx].copy()
         z = np.zeros(dp) if z0 is None else _f64(z0)[idx].copy()
-        g = np.empty((T, dv_))
-        h = np.empty(T)
-        dfq = np.empty((T, dp))
-        ckpt = {}                 # the state before token t, every CKPT tokens
-        for t in range(T):
-            if t % CKPT == 0:
-                ckpt[t] = (S.copy(), z.copy())
-            S = al[t] * S + be[t] * np.outer(fk[t], vv[t])
-            z = al[t] * z + be[t] * fk[t]
-            num = fq[t] @ S
-            den = fq[t] @ z
-            if normalize is True:
-                Dv = den + eps
-                g[t] = do[t] / Dv
-                h[t] = -(do[t] @ (num / Dv)) / Dv
-            elif normalize is False:
-                g[t] = do[t]
-                h[t] = 0.0
-            elif normalize == "max1":
-                Dv = max(abs(den), 1.0)
-                g[t] = do[t] / Dv
-                h[t] = -np.sign(den) * (do[t] @ (num / Dv)) / Dv if abs(den) > 1.0 else 0.0
-            else:
-                raise ValueError(f"unknown read-out {normalize!r}")
-            dfq[t] = S @ g[t] + z * h[t]
-        G = np.zeros((dp, dv_))
-        gz = np.zeros(dp)
-        dfk = np.empty((T, dp))
-        dvv = np.empty((T, dv_))
-        for b0 in sorted(ckpt, reverse=True):
-            b1 = min(b0 + CKPT, T)
-            Sp, zp = ckpt[b0]
-            prev = []             # (S_{t-1}, z_{t-1}) for t in [b0, b1)
-            for t in range(b0, b1):
-                prev.append((Sp, zp))
-                Sp = al[t] * Sp + be[t] * np.outer(fk[t], vv[t])
-                zp = al[t] * zp + be[t] * fk[t]
-            for t in range(b1 - 1, b0 - 1, -1):
-                a_next = al[t + 1] if t + 1 < T else 0.0
-                G = a_next * G + np.outer(fq[t], g[t])
-                gz = a_next * gz + fq[t] * h[t]
-                u = G @ vv[t] + gz
-                dfk[t] = be[t] * u
-                dvv[t] = be[t] * (fk[t] @ G)
-                res["dbeta"][idx][t] = fk[t] @ u
-                Sm, zm = prev[t - b0]
-                res["dalpha"][idx][t] = (G * Sm).sum() + gz @ zm
+        rd = lambda t, num, den: grads(do[t], num, den, eps, 1.0, 1.0)
+        dfq, dfk, dvv, dal, dbe, G, gz = _reverse_mode_head(fq_all[idx], fk_all[idx], v_all[idx],
+                                                            do, al, be, S, z, rd)
         res["dq"][idx] = dfq * dphq[idx]
         res["dk"][idx] = dfk * dphk[idx]
         res["dv"][idx] = dvv
         res["dS0"][idx] = al[0] * G
         res["dz0"][idx] = al[0] * gz
+        res["dalpha"][idx] = dal
+        res["dbeta"][idx] = dbe
     out = {n: res[n] for n in ("dq", "dk", "dv", "dS0", "dz0")}
     if decay is not None:
         out["ddecay"] = res["dalpha"]
     if gate is not None:
         out["dgate"] = res["dalpha"] - res["dbeta"]
     return out
+
+
+def mlstm_gradients(q, k, v, dout, igate, fgate, exp_form=False, eps=1e-6, S0=None, z0=None,
+                    m0=None, normalize="max1"):
+    """Gradients of L = sum_t <dout_t, o_t> for the mLSTM gates ([card]
+    "Variants / Matrix memory with exponential gates (mLSTM)"), o from
+    mlstm_recurrence, in float64: with respect to q, k, v, the forget and
+    input pre-activations, and the scaled start state (S0', z0', m0).
+
+    L depends on the true state S_t = e^{m_t} S'_t, whose recurrence has
+    alpha_t = f_t and beta_t = i_t = e^{itilde_t}; the stabiliser only picks
+    the scale it is held at.  Reverse mode runs in that scale: the scaled
+    recurrence S'_t = alpha'_t S'_{t-1} + beta'_t k_t v_t^T (alpha'_t =
+    e^{log f_t + m_{t-1} - m_t}, beta'_t = e^{itilde_t - m_t}, as in
+    mlstm_recurrence) with the scaled read-out, whose factors g'_t = e^{m_t}
+    g_t give the gradient state G'_t = e^{m_t} G_t.  Then
+        dq_t = S'_t g'_t + z'_t h'_t,  dk_t = beta'_t (G'_t v_t + gz'_t),
+        dv_t = beta'_t G'_t^T k_t,
+        dL/dlog f_r = f_r <G_r, S_{r-1}> + ... = alpha'_r (<G'_r, S'_{r-1}>
+                      + <gz'_r, z'_{r-1}>),
+        dL/ditilde_t = i_t k_t . (G_t v_t + gz_t) = beta'_t k_t . (G'_t v_t + gz'_t),
+        dL/dS0' = alpha'_0 G'_0 (S_init = e^{m0} S0'), dz0' alike,
+        dL/dm0 = <dS0', S0'> + <dz0', z0'>,
+    and dL/dfgate = dL/dlog f times d log f / dfgate: 1 - f for the sigmoid
+    gate, 1 for the exponential one.  Returns a dict with dq, dk, dv, dfgate,
+    digate, dS0, dz0 and dm0.
+    """
+    fq_all, fk_all, v_all, do_all = phi_identity(q), phi_identity(k), _f64(v), _f64(dout)
+    lf_all = log_forget(fgate, exp_form)
+    it_all = _f64(igate)
+    lead = fq_all.shape[:-2]
+    T, dp = fq_all.shape[-2:]
+    dv_ = v_all.shape[-1]
+    res = {n: np.zeros(lead + shp) for n, shp in (("dq", (T, dp)), ("dk", (T, dp)), ("dv", (T, dv_)),
+                                                  ("dfgate", (T,)), ("digate", (T,)),
+                                                  ("dS0", (dp, dv_)), ("dz0", (dp,)), ("dm0", ()))}
+    grads = _readout_grads(normalize, eps)
+    for idx in np.ndindex(*lead):
+        lf, it, do = lf_all[idx], it_all[idx], do_all[idx]
+        S = np.zeros((dp, dv_)) if S0 is None else _f64(S0)[idx].copy()
+        z = np.zeros(dp) if z0 is None else _f64(z0)[idx].copy()
+        m_prev = 0.0 if m0 is None else float(_f64(m0)[idx])
+        m = np.empty(T)
+        for t in range(T):
+            m[t] = max(lf[t] + m_prev, it[t])
+            m_prev = m[t]
+        m_before = np.concatenate([[0.0 if m0 is None else float(_f64(m0)[idx])], m[:-1]])
+        al = np.exp(lf + m_before - m)
+        be = np.exp(it - m)
+        rd = lambda t, num, den: grads(do[t], num, den, eps * np.exp(-m[t]), np.exp(m[t]),
+                                       np.exp(-m[t]))
+        S_init, z_init = S.copy(), z.copy()
+        dfq, dfk, dvv, dal, dbe, G, gz = _reverse_mode_head(fq_all[idx], fk_all[idx], v_all[idx],
+                                                            do, al, be, S, z, rd)
+        dlogf = al * dal
+        f = np.exp(lf)
+        res["dq"][idx] = dfq
+        res["dk"][idx] = dfk
+        res["dv"][idx] = dvv
+        res["dfgate"][idx] = dlogf if exp_form else dlogf * (1.0 - f)
+        res["digate"][idx] = be * dbe
+        res["dS0"][idx] = al[0] * G
+        res["dz0"][idx] = al[0] * gz
+        res["dm0"][idx] = (res["dS0"][idx] * S_init).sum() + res["dz0"][idx] @ z_init
+    return res
 
 
 # --------------------------------------------------------------------------
