@@ -268,16 +268,34 @@ def prefill_stage(stage: int, q, k, v, S, z, out, workspace, *, phi="elu1", W=No
 
 def prefill_backward(q, k, v, dout, *, phi: str = "elu1", decay=None, gate=None,
                      eps: float = 1e-6, state: Optional[tuple] = None, normalize=True,
-                     state_grad: bool = False, segments: int = 0, workspace=None):
+                     state_grad: bool = False, segments: int = 0, workspace=None,
+                     igate=None, fgate=None, fgate_exp: bool = False):
     """Gradients of L = sum <dout, out> for la.prefill(q, k, v, ...) from the
     initial state `state=(S0, z0)` (zero if None).  dout has out's layout and
     dtype (q's, or float32).  Returns a dict of fp32 tensors: dq, dk, dv, and
     ddecay (with `decay`) or dgate (with `gate`), and dS0, dz0 when
     state_grad=True.  `segments` (0 = the default plan) sets how many runs of
-    32-token chunks each sequence is cut into on the chunked path."""
+    32-token chunks each sequence is cut into on the chunked path.
+
+    mLSTM gates (`igate`, `fgate`, `fgate_exp` as for prefill, identity
+    features): `state` is the scaled (S0, z0, m0); the result has dfgate and
+    digate, and dS0, dz0 are the gradients of the scaled state."""
     torch = _torch()
+    mlstm = igate is not None or fgate is not None
+    stab = None
+    if mlstm:
+        B_, H_ = q.shape[0], q.shape[1]
+        if state is not None:
+            if len(state) != 3:
+                raise ValueError("with the mLSTM gates state is (S0, z0, m0)")
+            stab = state[2]
+            _need(stab, "m0", device=q.device, dtype=torch.float32, shape=(B_, H_))
+            state = state[:2]
+        else:
+            stab = torch.zeros(B_, H_, dtype=torch.float32, device=q.device)
     desc, (B, H, T, d_h, d_v) = _prefill_desc(q, k, v, phi, None, decay, gate, eps, 0, segments,
-                                              dout.dtype, normalize, True)
+                                              dout.dtype, normalize, True, igate, fgate,
+                                              fgate_exp, stab)
     _need(dout, "dout", device=q.device, shape=(B, H, T, d_v))
     dp = feature_dim(d_h, phi)
     S0 = z0 = None
@@ -288,7 +306,11 @@ def prefill_backward(q, k, v, dout, *, phi: str = "elu1", decay=None, gate=None,
     f32 = dict(dtype=torch.float32, device=q.device)
     g = {"dq": torch.empty(B, H, T, d_h, **f32), "dk": torch.empty(B, H, T, d_h, **f32),
          "dv": torch.empty(B, H, T, d_v, **f32)}
-    dd = torch.empty(B, H, T, **f32) if (decay is not None or gate is not None) else None
+    dd = None
+    if decay is not None or gate is not None:
+        dd = torch.empty(B, H, T, **f32)
+    elif mlstm:
+        dd = torch.empty(2, B, H, T, **f32)   # dL/dfgate, then dL/digate
     dS0 = torch.empty(B, H, dp, d_v, **f32) if state_grad else None
     dz0 = torch.empty(B, H, dp, **f32) if state_grad else None
     n = ctypes.c_size_t(0)
@@ -305,6 +327,8 @@ def prefill_backward(q, k, v, dout, *, phi: str = "elu1", decay=None, gate=None,
         g["ddecay"] = dd
     if gate is not None:
         g["dgate"] = dd
+    if mlstm:
+        g["dfgate"], g["digate"] = dd[0], dd[1]
     if state_grad:
         g["dS0"], g["dz0"] = dS0, dz0
     return g

@@ -19,9 +19,20 @@
 // dL/dalpha_r is that sum over alpha_r, except for decays below kDecayExact,
 // whose gradient decay_exact_kernel forms as <G_r, S_{r-1}> + <g_r, z_{r-1}>.
 //
+// mLSTM gates (wikillm "Linear attention", Variants / mLSTM): the state is
+// held scaled by e^{-m_t} as in the forward, S'_t = alpha'_t S'_{t-1} +
+// beta'_t k_t v_t^T with alpha'_t = e^{log f_t + m_{t-1} - m_t} and beta'_t =
+// e^{itilde_t - m_t}, and the read-out of the scaled state (readout_factor)
+// gives g'_num = e^{m_t} g_num, so the gradient state carried back is
+// G'_t = e^{m_t} G_t: the same two passes with (alpha', beta') and bounded
+// numbers throughout.  L depends on the gates through the true alpha_t =
+// f_t and beta_t = e^{itilde_t}: dL/dlog f_r is the suffix sum above
+// (times 1 - f_r for the sigmoid gate's pre-activation, 1 for the
+// exponential one) and dL/ditilde_t = beta'_t k_t . (G'_t v_t + g'_t).
+//
 // Pass A walks t forward: it rebuilds S_t and z_t, the read-out, g_num,
 // g_den and dq, and leaves g_num_t, g_den_t and <phi(q_t), dphi(q_t)> in the
-// workspace.  Pass B walks t backward carrying G, g.  The efficient-attention
+// workspace (with the mLSTM gates also alpha'_t and beta'_t).  Pass B walks t backward carrying G, g.  The efficient-attention
 // lesson ("Implementation reality") trains with the chunked form; this
 // token-serial kernel is the exact reference-grade path for every supported
 // configuration.
@@ -44,7 +55,11 @@ struct BwdArgs {
   float* dq;
   float* dk;
   float* dv;
-  float* ddecay;     // [BH, T] or null
+  float* ddecay;     // [BH, T] or null (mLSTM: dL/dfgate)
+  const float* igate;   // mLSTM input-gate pre-activations [BH, T]
+  const float* stab;    // mLSTM stabiliser of the start state [BH] (read with S0)
+  float* digate;        // mLSTM dL/digate [BH, T]
+  int fgate_exp;
   float* dS0;        // [BH, dp, dv] or null
   float* dz0;
   float* ws;         // [BH, T, dv + 2]
@@ -95,8 +110,11 @@ __global__ __launch_bounds__(NT) void backward_kernel(const BwdArgs a) {
   const DT* vg = static_cast<const DT*>(a.v) + bh * T * a.dv_;
   const int64_t do0 = bh * T * a.dv_;
   const float* dg = a.decay ? a.decay + bh * T : nullptr;
-  float* wsg = a.ws + bh * T * (a.dv_ + 2);
-  const int wst = a.dv_ + 2;
+  const bool ml = a.decay_kind == LA_GATE_MLSTM;
+  const float* ig = ml ? a.igate + bh * T : nullptr;
+  // per token: g_num (d_v), g_den, <phi(q), dphi(q)>; mLSTM also alpha', beta'
+  const int wst = a.dv_ + (ml ? 4 : 2);
+  float* wsg = a.ws + bh * T * wst;
 
   auto coeffs = [&](int64_t t, float& al, float& be) {
     al = 1.f;
@@ -118,6 +136,7 @@ __global__ __launch_bounds__(NT) void backward_kernel(const BwdArgs a) {
                                : make_float4(0.f, 0.f, 0.f, 0.f);
   }
   float zr = (a.z0 && tid < a.dp) ? a.z0[bh * a.dp + tid] : 0.f;
+  float m = (ml && a.S0) ? a.stab[bh] : 0.f;   // mLSTM stabiliser (a zero start state has m = 0)
 
   for (int64_t t = 0; t < T; ++t) {
     if (tid < a.dh) {
@@ -129,7 +148,15 @@ __global__ __launch_bounds__(NT) void backward_kernel(const BwdArgs a) {
       s_do[tid] = load_dout<DT>(a, do0 + t * a.dv_ + tid);
     }
     float alpha, beta;
-    coeffs(t, alpha, beta);
+    if (ml) {
+      const float lf = log_forget(dg[t], a.fgate_exp), it = ig[t];
+      const float mn = fmaxf(lf + m, it);
+      alpha = expf(lf + m - mn);
+      beta = expf(it - mn);
+      m = mn;
+    } else {
+      coeffs(t, alpha, beta);
+    }
     __syncthreads();
     if (tid < a.dp) {
       s_fq[tid] = phi_of(s_q[tid], a.phi);
@@ -174,10 +201,10 @@ __global__ __launch_bounds__(NT) void backward_kernel(const BwdArgs a) {
     float den = 0.f;
 #pragma unroll
     for (int w = 0; w < NT / 64; ++w) den += s_red[w][256];
-    float scale;   // o = num * scale, g_num = dout * scale
-    if (a.norm == LA_NORM_NONE) scale = 1.f;
-    else if (a.norm == LA_NORM_MAX1) scale = 1.f / fmaxf(fabsf(den), 1.f);
-    else scale = 1.f / (den + a.eps);
+    // o = num * scale, g_num = dout * scale (of the scaled state with the
+    // mLSTM gates: e^{m} times the true g_num)
+    const float scale = readout_factor(a.norm, den, a.eps, m);
+    const float floor_ = ml ? expf(-m) : 1.f;   // the max1 read-out's floor in the state's scale
     float pv = 0.f;
     if (tid < a.dv_) {
       float n = 0.f;
@@ -195,7 +222,7 @@ __global__ __launch_bounds__(NT) void backward_kernel(const BwdArgs a) {
     for (int w = 0; w < NT / 64; ++w) dot += s_sc[w][0];
     float gden;
     if (a.norm == LA_NORM_NONE) gden = 0.f;
-    else if (a.norm == LA_NORM_MAX1) gden = fabsf(den) > 1.f ? -copysignf(1.f, den) * dot * scale : 0.f;
+    else if (a.norm == LA_NORM_MAX1) gden = fabsf(den) > floor_ ? -copysignf(1.f, den) * dot * scale : 0.f;
     else gden = -dot * scale;
     // dphi(q_t) = S_t g_num + z_t g_den: the S part summed over the column groups
     const float4 gn4 = *reinterpret_cast<const float4*>(s_gn + 4 * cg);
@@ -223,6 +250,10 @@ __global__ __launch_bounds__(NT) void backward_kernel(const BwdArgs a) {
       for (int w = 0; w < NT / 64; ++w) s += s_sc[w][1];
       wsg[t * wst + a.dv_] = gden;
       wsg[t * wst + a.dv_ + 1] = s;
+      if (ml) {
+        wsg[t * wst + a.dv_ + 2] = alpha;
+        wsg[t * wst + a.dv_ + 3] = beta;
+      }
     }
   }
   __syncthreads();   // pass A's workspace rows visible to every thread
@@ -245,7 +276,12 @@ __global__ __launch_bounds__(NT) void backward_kernel(const BwdArgs a) {
     const float gden = wsg[t * wst + a.dv_];
     const float qdq = wsg[t * wst + a.dv_ + 1];
     float alpha, beta;
-    coeffs(t, alpha, beta);
+    if (ml) {
+      alpha = wsg[t * wst + a.dv_ + 2];
+      beta = wsg[t * wst + a.dv_ + 3];
+    } else {
+      coeffs(t, alpha, beta);
+    }
     __syncthreads();
     if (tid < a.dp) {
       s_fq[tid] = phi_of(s_q[tid], a.phi);
@@ -303,10 +339,16 @@ __global__ __launch_bounds__(NT) void backward_kernel(const BwdArgs a) {
     for (int w = 0; w < NT / 64; ++w) kdk += s_sc[w][2];
     R += qdq - beta * kdk;
     if (tid == 0 && a.ddecay) {
-      // near-zero decays: the exact term is added by decay_exact_kernel
-      const float da = alpha < kDecayExact ? 0.f : R / alpha;
-      if (a.decay_kind == LA_DECAY_SSD) a.ddecay[bh * T + t] = da;
-      else if (a.decay_kind == LA_GATE_RFA) a.ddecay[bh * T + t] = da - kdk;
+      if (ml) {
+        // R = dL/dlog f_t; 1 - sigmoid(x) = 1 / (1 + e^x)
+        a.ddecay[bh * T + t] = a.fgate_exp ? R : R / (1.f + expf(dg[t]));
+        a.digate[bh * T + t] = beta * kdk;
+      } else {
+        // near-zero decays: the exact term is added by decay_exact_kernel
+        const float da = alpha < kDecayExact ? 0.f : R / alpha;
+        if (a.decay_kind == LA_DECAY_SSD) a.ddecay[bh * T + t] = da;
+        else if (a.decay_kind == LA_GATE_RFA) a.ddecay[bh * T + t] = da - kdk;
+      }
     }
     alpha_next = alpha;
   }
@@ -581,12 +623,13 @@ hipError_t launch_decay_exact(const DecayExactArgs& a, la_dtype dtype, int64_t B
 
 bool backward_supported(const Problem& p) {
   return (p.phi == LA_PHI_ELU1 || p.phi == LA_PHI_IDENTITY) && p.dp == p.dh &&
-         p.decay_kind != LA_GATE_MLSTM && !p.noncausal && recurrent_supported(p.dh, p.dp, p.dv);
+         !p.noncausal && recurrent_supported(p.dh, p.dp, p.dv);
 }
 
 size_t backward_workspace_bytes(const Problem& p) {
   if (backward_chunked(p)) return backward_chunked_workspace_bytes(p);
-  return size_t(p.BH()) * size_t(p.T) * size_t(p.dv + 2) * sizeof(float);
+  const int per_token = p.dv + (p.decay_kind == LA_GATE_MLSTM ? 4 : 2);
+  return size_t(p.BH()) * size_t(p.T) * size_t(per_token) * sizeof(float);
 }
 
 hipError_t launch_backward(const Problem& p, const void* q, const void* k, const void* v,
@@ -599,6 +642,11 @@ hipError_t launch_backward(const Problem& p, const void* q, const void* k, const
   BwdArgs a;
   a.q = q; a.k = k; a.v = v; a.dout = dout; a.S0 = S0; a.z0 = z0; a.decay = p.decay;
   a.dq = dq; a.dk = dk; a.dv = dv; a.ddecay = ddecay; a.dS0 = dS0; a.dz0 = dz0;
+  const bool ml = p.decay_kind == LA_GATE_MLSTM;
+  a.igate = ml ? p.igate : nullptr;
+  a.stab = ml ? p.stab : nullptr;
+  a.digate = ml ? ddecay + p.BH() * p.T : nullptr;   // the second half of ddecay
+  a.fgate_exp = ml ? p.fgate_exp : 0;
   a.ws = static_cast<float*>(ws);
   a.H = p.H; a.T = p.T; a.dh = p.dh; a.dv_ = p.dv; a.dp = p.dp;
   a.phi = int(p.phi); a.decay_kind = int(p.decay_kind); a.norm = p.norm;
@@ -610,7 +658,7 @@ hipError_t launch_backward(const Problem& p, const void* q, const void* k, const
     case LA_BF16: e = launch_dt<bf16_t>(a, p.BH(), stream); break;
     case LA_F16: e = launch_dt<f16_t>(a, p.BH(), stream); break;
   }
-  if (e != hipSuccess || !ddecay) return e;
+  if (e != hipSuccess || !ddecay || ml) return e;
   // near-zero decays: the exact gradient, over the whole sequence (one
   // segment from the initial state, nothing carried in after its end)
   DecayExactArgs x;

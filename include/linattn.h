@@ -210,7 +210,8 @@ la_status la_prefill_stage(const la_desc* desc, int stage, const void* q, const 
  * segment) and B H T 2 fp32 (per token: the read-out's factor and the
  * divisor's gradient), each part rounded up to 256 bytes; with a decay also
  * B H nseg fp32 (each segment's log-decay), B H T 2 fp32 (per-token terms
- * of the decay gradient) and B H ceil(T / 1024) fp32 (their tile totals).  The per-token path: B H T (d_v + 2) fp32. */
+ * of the decay gradient) and B H ceil(T / 1024) fp32 (their tile totals).  The per-token path: B H T (d_v + 2) fp32, B H T (d_v + 4) fp32 with
+ * the mLSTM gates. */
 la_status la_prefill_backward_workspace_size(const la_desc* desc, size_t* bytes);
 
 /* Gradients of a causal prefill for training ([lesson] Developer level and
@@ -224,6 +225,15 @@ la_status la_prefill_backward_workspace_size(const la_desc* desc, size_t* bytes)
  *        fp32 (dL/da_t for LA_DECAY_SSD, dL/dg_t for LA_GATE_RFA; NULL
  *        without a decay, required with one); dS0, dz0 (dL/dS0, dL/dz0;
  *        both NULL to skip).
+ * mLSTM gates (LA_GATE_MLSTM, identity features; wikillm "Linear
+ * attention", Variants / mLSTM): the initial state is the scaled (S0', z0')
+ * with its stabiliser in desc->stab [B, H] (read only, and only with S0;
+ * a zero state has stabiliser 0); ddecay holds 2 B H T floats, dL/d of the
+ * forget pre-activations desc->decay then dL/d of the input pre-activations
+ * desc->igate; dS0, dz0 are dL/dS0', dL/dz0' (the stabiliser's own gradient
+ * is <dS0', S0'> + <dz0', z0'>).  The state is carried scaled by the
+ * forward's stabiliser throughout, so no intermediate overflows where the
+ * forward's does not.  Per-token path only.
  * The decay gradient is formed through log a_t (a suffix sum of
  * <phi(q_t), dphi(q_t)> - <phi(k_t), dphi(k_t)>, divided by a_t); where a
  * decay or gate value is below 1/256 (0, a full reset, included) it is
@@ -231,9 +241,10 @@ la_status la_prefill_backward_workspace_size(const la_desc* desc, size_t* bytes)
  * <gz_r, z_{r-1}> (the gradient of the state after r with the state before
  * it), by a walk over the tokens of r's segment, which is finite and free
  * of the division's loss of accuracy.
- * Supported: causal, elu+1 or identity features, LA_DECAY_NONE, LA_DECAY_SSD
- * or LA_GATE_RFA, every read-out form, the widths the per-token kernel takes
- * (LA_EUNSUPPORTED otherwise: RFF, the mLSTM gates, the non-causal form).
+ * Supported: causal, elu+1 or identity features, LA_DECAY_NONE, LA_DECAY_SSD,
+ * LA_GATE_RFA or LA_GATE_MLSTM, every read-out form, the widths the
+ * per-token kernel takes (LA_EUNSUPPORTED otherwise: RFF, the non-causal
+ * form).
  * Two paths.  Chunked (bf16 inputs, elu+1, no decay, the SSD decay or the
  * RFA gate, d' = d_v in {64, 128}, T > 0): the same gradients written as
  * masked-quadratic sums inside 32-token chunks and states across them, as

@@ -212,14 +212,20 @@ def test_backward_checks():
     assert status(L.la_prefill_backward_workspace_size(ctypes.byref(d32), ctypes.byref(n))) == "LA_OK"
     assert n.value == 8 * 300 * (64 + 2) * 4
     assert status(L.la_prefill_backward_workspace_size(ctypes.byref(desc(**base)), ctypes.byref(n))) == "LA_OK"
-    # not covered: RFF, the mLSTM gates, the non-causal form
+    # not covered: RFF, the non-causal form
     d = desc(T=16, d_h=64, d_v=64, dtype_code=_lib.LA_F32)
     d.phi, d.rff_D, d.rff_W = _lib.LA_PHI_RFF, 32, FAKE
     assert bw(d) == "LA_EUNSUPPORTED"
+    assert bw(desc(causal=False, **base)) == "LA_EUNSUPPORTED"
+    # the mLSTM gates: the per-token path, B H T (d_v + 4) floats (alpha', beta'
+    # per token beside the read-out's terms); ddecay (both gates' gradients)
+    # required
     d = desc(phi="identity", **base)
     d.decay_kind, d.decay, d.igate, d.stab = _lib.LA_GATE_MLSTM, FAKE, FAKE, FAKE
-    assert bw(d, ddecay=FAKE) == "LA_EUNSUPPORTED"
-    assert bw(desc(causal=False, **base)) == "LA_EUNSUPPORTED"
+    assert status(L.la_prefill_backward_workspace_size(ctypes.byref(d), ctypes.byref(n))) == "LA_OK"
+    assert n.value == 8 * 300 * (64 + 4) * 4
+    assert bw(d) == "LA_EINVAL"
+    assert status(L.la_prefill_backward_workspace_size(ctypes.byref(desc(**base)), ctypes.byref(n))) == "LA_OK"
     # ddecay exactly with a decay; S0/z0 and dS0/dz0 in pairs; workspace size
     d = desc(**base)
     d.decay_kind, d.decay = _lib.LA_DECAY_SSD, FAKE

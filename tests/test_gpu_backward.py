@@ -346,3 +346,82 @@ def test_backward_per_token_near_zero_decays(kind, phi):
     ref = O.prefill_gradients(x.q, x.k, x.v, do, phi=phi, decay=x.decay, gate=x.gate,
                               S0=S0, z0=z0)
     compare(got, ref, TOL["f32"], ("per-token near-zero", kind, phi))
+
+
+# ------------------------------------------------------------------ mLSTM gates
+# The per-token backward with the forward's stabilised state, against the
+# oracle's mLSTM gradients (pinned by finite differences of the stabilised
+# forward oracle): dq, dk, dv, dL/dfgate, dL/digate and the scaled start
+# state's dS0', dz0'.
+
+def _mlstm_case(B, H, T, d, dv, dtype, seed, ishift=0.0, fexp=False, positive=False):
+    x = I.prefill_inputs(B, H, T, d, dv, dtype=dtype, seed=seed, decay="mlstm", scale=0.7)
+    x.igate = x.igate + ishift
+    if fexp:
+        x.fgate = -torch.nn.functional.softplus(-x.fgate)   # log sigmoid: the exp form's input
+    if positive:
+        x.q, x.k = x.q.abs(), x.k.abs()
+    return x
+
+
+def _mlstm_run(x, do, dev, normalize, fexp, state):
+    g = lambda t: None if t is None else t.to(dev)
+    st = None if state is None else tuple(torch.as_tensor(s, dtype=torch.float32, device=dev)
+                                          for s in state)
+    out = la.prefill_backward(g(x.q), g(x.k), g(x.v), g(do), phi="identity", igate=g(x.igate),
+                              fgate=g(x.fgate), fgate_exp=fexp, state=st, normalize=normalize,
+                              state_grad=True)
+    torch.cuda.synchronize()
+    return {k: v.cpu().double().numpy() for k, v in out.items()}
+
+
+@pytest.mark.parametrize("normalize", ["max1", True, False])
+@pytest.mark.parametrize("fexp", [False, True])
+@pytest.mark.parametrize("with_state", [False, True])
+def test_backward_mlstm_fp32_vs_oracle(normalize, fexp, with_state):
+    dev = gpu_device()
+    B, H, T, d, dv = 2, 2, 67, 16, 8
+    x = _mlstm_case(B, H, T, d, dv, "f32", seed=7 + int(fexp), fexp=fexp,
+                    positive=normalize is True)
+    do = torch.randn(B, H, T, dv, generator=torch.Generator().manual_seed(9))
+    state = None
+    if with_state:
+        rng = np.random.default_rng(5)
+        state = (rng.standard_normal((B, H, d, dv)) * 0.3,
+                 np.abs(rng.standard_normal((B, H, d))) * 0.3, rng.standard_normal((B, H)))
+    got = _mlstm_run(x, do, dev, normalize, fexp, state)
+    S0, z0, m0 = (None, None, None) if state is None else state
+    ref = O.mlstm_gradients(x.q, x.k, x.v, do, x.igate, x.fgate, fexp, 1e-6, S0, z0, m0, normalize)
+    compare(got, {k: ref[k] for k in got}, TOL["f32"], ("mlstm", normalize, fexp, with_state))
+
+
+def test_backward_mlstm_input_gates_beyond_fp32():
+    """Input pre-activations near 100 (e^100 overflows fp32) and a start state
+    at the same scale (m0 near 100): the stabilised state carries the
+    gradients without overflow.  Every weight then carries e^100, so |q.z| >>
+    1 and the max1 read-out is q.S / |q.z|, which needs positive features to
+    stay well conditioned (as in the forward's test of this case)."""
+    dev = gpu_device()
+    B, H, T, d, dv = 1, 2, 50, 16, 16
+    x = _mlstm_case(B, H, T, d, dv, "f32", seed=13, ishift=100.0, positive=True)
+    do = torch.randn(B, H, T, dv, generator=torch.Generator().manual_seed(2))
+    rng = np.random.default_rng(3)
+    state = (np.abs(rng.standard_normal((B, H, d, dv))) * 0.3,
+             np.abs(rng.standard_normal((B, H, d))) * 0.3, 100.0 + rng.standard_normal((B, H)))
+    got = _mlstm_run(x, do, dev, "max1", False, state)
+    for key, val in got.items():
+        assert np.isfinite(val).all(), key
+    ref = O.mlstm_gradients(x.q, x.k, x.v, do, x.igate, x.fgate, False, 1e-6, *state,
+                            normalize="max1")
+    compare(got, {k: ref[k] for k in got}, TOL["f32"], "mlstm, input gates + 100")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_backward_mlstm_bf16_vs_oracle(d):
+    dev = gpu_device()
+    B, H, T = 1, 2, 200
+    x = _mlstm_case(B, H, T, d, d, "bf16", seed=d)
+    do = torch.randn(B, H, T, d, generator=torch.Generator().manual_seed(4)).to(torch.bfloat16)
+    got = _mlstm_run(x, do, dev, "max1", False, None)
+    ref = O.mlstm_gradients(x.q, x.k, x.v, do, x.igate, x.fgate, False, 1e-6, normalize="max1")
+    compare(got, {k: ref[k] for k in got}, TOL["bf16"], ("mlstm bf16", d))
