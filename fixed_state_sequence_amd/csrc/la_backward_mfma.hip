@@ -35,7 +35,8 @@
 //   reverse scan over the segments: G at every segment's end, and
 //     dS0 = G before the first token, dz0 likewise;
 //   pass B (chunks in reverse): dk, dv and <phi(k_s), dphi(k_s)> / beta_s
-//     from the carried G;
+//     from the carried G, held twice in registers (G and G^T, one per kind
+//     of wave; see bwd_pass_b2);
 //   with a decay, a suffix sum per sequence turns the per-token terms into
 //   the decay or gate gradient.
 //
@@ -60,6 +61,8 @@
 #include "la_internal.h"
 #include "la_mfma_common.h"
 
+#include <type_traits>
+
 namespace la {
 namespace {
 
@@ -82,23 +85,22 @@ struct BL {
   static constexpr int V = KL + TILE;        // v
   static constexpr int GH = V + TILE;        // g, high part
   static constexpr int GL = GH + TILE;       // g, low part
-  static constexpr int SB = GL + TILE;       // the carried state (S in A, G in B), bf16, rows = features
+  static constexpr int SB = GL + TILE;       // the carried state S, bf16, rows = features
   static constexpr int SBL = SB + D * D * 2; // its low part
-  static constexpr int DO = SBL + D * D * 2; // fp32 [BCH][FS]: dout (A)
-  // with a decay, a weighted tile pair (high, low): pass A e^{L + l_t} g_t
-  // for the gradient-state fold, then w_s phi(k_s) for the state fold; pass
-  // B e^{l_t} g_t
+  static constexpr int DO = SBL + D * D * 2; // fp32 [BCH][FS]: dout
+  // with a decay, a weighted tile pair (high, low): e^{L + l_t} g_t for the
+  // gradient-state fold, then w_s phi(k_s) for the state fold
   static constexpr int WH = DO + BCH * FS * 4;
   static constexpr int WL = WH + TILE;
   static constexpr int F = DECAY ? WL + TILE : WH;   // fp32 scalars, offsets below (floats)
-  static constexpr int Z = 0;                // z (A) or gz (B), carried
-  static constexpr int DI = D;               // phi(q_t) . z per token (A)
+  static constexpr int Z = 0;                // z, carried
+  static constexpr int DI = D;               // phi(q_t) . z per token
   static constexpr int HT = DI + BCH;        // h_t per token
   static constexpr int HP = HT + BCH;        // per-wave partial dout . o [NW][BCH]
-  static constexpr int ZP = HP + NW * BCH;   // per-wave increments of z (A) or gz (B) [NW][D]
+  static constexpr int ZP = HP + NW * BCH;   // per-wave increments of z [NW][D]
   static constexpr int LAM = ZP + NW * D;    // within-chunk log-prefix l_t [BCH]
   static constexpr int BET = LAM + BCH;      // beta_t [BCH]
-  static constexpr int QP = BET + BCH;       // per-wave partial <phi, dphi> [NW][BCH]
+  static constexpr int QP = BET + BCH;       // per-wave partial <phi(q), dphi(q)> [NW][BCH]
   static constexpr int NF = QP + NW * BCH;
   static constexpr int LDS = F + NF * 4;
 };
@@ -118,7 +120,7 @@ struct BwArgs {
   float* dq;
   float* dk;
   float* dv;
-  float* gslot;  // [BH, nseg, D*D + D]: G_seg (pass A), then G at the segment's end
+  float* gslot;  // [BH, nseg, D*D + D]: G_seg (pass A), then G at the segment's end (reverse scan)
   float* lgam;   // [BH, nseg]: the segment's total log-decay (pass A, with a decay)
   float* tok;    // [BH, T, 2]: r_t and h_t
   float* qd;     // [BH, T]: <phi(q_t), dphi(q_t)> (pass A, with a decay)
@@ -216,11 +218,10 @@ __device__ __forceinline__ void tr_ops(const char* tile, int col0, int lane, u32
 struct Raw {
   u32x4 q[2], k[2], v[2];
   f32x4 d[2][2];   // dout as fp32
-  float2 th[2];    // pass B: r_t and h_t of rows r and r + 16 (from pass A)
   float al;
 };
 
-template <int D, int DECAY, bool TOK = false>
+template <int D, int DECAY>
 __device__ __forceinline__ void load_raw(const BwArgs& a, int64_t bh, int t0, int tid, Raw& x) {
   using L = BL<D, DECAY>;
   const int b = tid % L::BPR;
@@ -230,7 +231,6 @@ __device__ __forceinline__ void load_raw(const BwArgs& a, int64_t bh, int t0, in
     const int r = tid / L::BPR + 16 * rr;
     const int64_t t = min(int64_t(t0 + r), T - 1);
     const int64_t row = (bh * T + t) * D + 8 * b;
-    if constexpr (TOK) x.th[rr] = *reinterpret_cast<const float2*>(a.tok + (bh * T + t) * 2);
     x.q[rr] = *reinterpret_cast<const u32x4*>(a.q + row);
     x.k[rr] = *reinterpret_cast<const u32x4*>(a.k + row);
     x.v[rr] = *reinterpret_cast<const u32x4*>(a.v + row);
@@ -285,13 +285,11 @@ __device__ __forceinline__ void chunk_decay(const Raw& x, int t0, int T, int lan
   tot = __shfl(lam, 31, 32);
 }
 
-// Stage one chunk into LDS: phi(q), phi(k) (high, low), v; pass A also the
-// fp32 dout, phi(q_t) . z and this wave's increments of z (sum w_s phi(k_s));
-// pass B g = r_t dout (high, low; with a decay also e^{l_t} g), h_t and this
-// wave's increments of gz (sum e^{l_t} phi(q_t) h_t).  Rows past the end of
-// the sequence are zero.  lam, bet, tot return the chunk's decay (see
-// chunk_decay; 0, 1, 0 without).
-template <int D, int DECAY, bool PASS_A>
+// Stage one chunk into LDS for pass A: phi(q), phi(k) (high, low), v, the
+// fp32 dout, phi(q_t) . z and this wave's increments of z (sum w_s
+// phi(k_s)).  Rows past the end of the sequence are zero.  lam, bet, tot
+// return the chunk's decay (see chunk_decay; 0, 1, 0 without).
+template <int D, int DECAY>
 __device__ __forceinline__ void stage(const BwArgs& a, int64_t bh, int t0, int tid, const Raw& x,
                                       char* smem, float& lam, float& bet, float& tot) {
   using L = BL<D, DECAY>;
@@ -337,38 +335,18 @@ __device__ __forceinline__ void stage(const BwArgs& a, int64_t bh, int t0, int t
     blk_write<D>(smem + L::V, pr, b, valid ? x.v[rr] : u32x4{0u, 0u, 0u, 0u});
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
     const f32x4 d0 = valid ? x.d[rr][0] : zero4, d1 = valid ? x.d[rr][1] : zero4;
-    if constexpr (PASS_A) {
-      float* dor = reinterpret_cast<float*>(smem + L::DO) + r * L::FS + 8 * b;
-      *reinterpret_cast<f32x4*>(dor) = d0;
-      *reinterpret_cast<f32x4*>(dor + 4) = d1;
-      const float wk = DECAY ? br * __expf(tot - lr) : 1.f;   // key weight to the chunk's end
-      float part = 0.f;
+    float* dor = reinterpret_cast<float*>(smem + L::DO) + r * L::FS + 8 * b;
+    *reinterpret_cast<f32x4*>(dor) = d0;
+    *reinterpret_cast<f32x4*>(dor + 4) = d1;
+    const float wk = DECAY ? br * __expf(tot - lr) : 1.f;   // key weight to the chunk's end
+    float part = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        part += fq[e] * F[L::Z + 8 * b + e];
-        inc[e] += wk * fk[e];
-      }
-      part = row_sum<L::BPR>(part);
-      if (b == 0) F[L::DI + r] = part;
-    } else {
-      const float rt = valid ? x.th[rr].x : 0.f, ht = valid ? x.th[rr].y : 0.f;
-      float gv[8] = {d0[0] * rt, d0[1] * rt, d0[2] * rt, d0[3] * rt,
-                     d1[0] * rt, d1[1] * rt, d1[2] * rt, d1[3] * rt};
-      const u32x4 gh = pack8(gv);
-      blk_write<D>(smem + L::GH, pr, b, gh);
-      blk_write<D>(smem + L::GL, pr, b, low8(gv, gh));
-      const float wq = DECAY ? __expf(lr) : 1.f;   // query weight from the chunk's start
-      if constexpr (DECAY != 0) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) gv[e] *= wq;
-        const u32x4 wh = pack8(gv);
-        blk_write<D>(smem + L::WH, pr, b, wh);
-        blk_write<D>(smem + L::WL, pr, b, low8(gv, wh));
-      }
-      if (b == 0) F[L::HT + r] = ht;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) inc[e] += wq * fq[e] * ht;
+    for (int e = 0; e < 8; ++e) {
+      part += fq[e] * F[L::Z + 8 * b + e];
+      inc[e] += wk * fk[e];
     }
+    part = row_sum<L::BPR>(part);
+    if (b == 0) F[L::DI + r] = part;
   }
   wave_rows_sum8<L::BPR>(inc, lane, F + L::ZP + w * D);
 }
@@ -417,7 +395,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_a(const BwArgs a) {
   for (int c = c0; c < c1; ++c) {
     const int t0 = c * BCH;
     float lam, bet, tot;
-    stage<D, DECAY, true>(a, bh, t0, tid, raw, smem, lam, bet, tot);
+    stage<D, DECAY>(a, bh, t0, tid, raw, smem, lam, bet, tot);
     __syncthreads();   // tiles, phi(q) . z, z increments, decay
     if (c + 1 < c1) load_raw<D, DECAY>(a, bh, t0 + BCH, tid, raw);   // next chunk, in flight meanwhile
     const bool vt = t0 + n < T;
@@ -809,217 +787,468 @@ __global__ __launch_bounds__(256) void bwd_rscan(float* gslot, const float* lgam
   }
 }
 
-// ------------------------------------------------------------------ pass B
+// ------------------------------------------------ pass B, split states
+
+// Pass B with the gradient state held twice in registers instead of staged
+// in LDS: waves 0 .. NJ-1 ("value waves") hold G itself, rows f and the
+// columns j of their 32-wide block, which as an MFMA operand contracts over
+// f (dv); waves NJ .. 2 NJ-1 ("feature waves") hold G^T, rows j and the
+// columns f of their block, which contracts over j (dk).  Each folds its own
+// copy every chunk (the same products, the transposed way), so no state
+// tile is split into LDS and read back, and the 64 KB that held it at D = 128
+// double-buffer the staged tiles instead: the chunk after the current one is
+// staged while the current one is computed, with one barrier per chunk.
+// Two waves share each SIMD, one of each kind: value waves compute first and
+// stage after, feature waves stage first, so one wave's VALU work meets the
+// other's MFMAs.
+//
+// An accumulator used as an operand carries its k-index in the permuted
+// order (perm_pos) of its rows: G's rows come from the columns of phi(q),
+// G^T's from those of g.  The tiles are laid out so that every other operand
+// meets that order: phi(k) is stored with its features at their perm_pos
+// positions (against G in dv), and v is read at permuted positions (two
+// 8-byte pieces, against G^T in dk); phi(q) and g stay in natural order, and
+// the scores phi(q) . phi(k) read phi(q) at permuted positions to match
+// phi(k).
+template <int D, int DECAY>
+struct BL2 {
+  static constexpr int NJ = D / 32;          // 32-wide blocks of D
+  static constexpr int NW = 2 * NJ;          // value waves, then feature waves
+  static constexpr int NT = 64 * NW;         // = 32 rows x BPR blocks: one staged block per thread
+  static constexpr int BPR = D / 8;
+  static constexpr int TILE = BCH * D * 2;
+  // one buffer: token tiles (bf16, rows at perm_pos(token), tile_off<D>)
+  static constexpr int Q = 0;                // phi(q) high (features in natural order)
+  static constexpr int QL = Q + TILE;        // phi(q) low
+  static constexpr int K = QL + TILE;        // phi(k) high (feature f at column perm_pos(f))
+  static constexpr int KL = K + TILE;        // phi(k) low
+  static constexpr int V = KL + TILE;        // v (natural)
+  static constexpr int GH = V + TILE;        // g = r_t dout high
+  static constexpr int GL = GH + TILE;       // g low
+  static constexpr int WH = GL + TILE;       // with a decay: e^{l_t} g high
+  static constexpr int WL = WH + TILE;       // and low
+  static constexpr int FB = DECAY ? WL + TILE : WH;   // per-buffer scalars (floats from FB)
+  static constexpr int LAM = 0;              // l_t [BCH]
+  static constexpr int BET = LAM + BCH;      // beta_t [BCH]
+  static constexpr int HT = BET + BCH;       // h_t [BCH]
+  static constexpr int HW = HT + BCH;        // e^{l_t} h_t of the token at tile row p [BCH]
+  static constexpr int TOT = HW + BCH;       // the chunk's total log-decay
+  static constexpr int NFB = TOT + 4;
+  static constexpr int BUF = FB + NFB * 4;   // bytes per buffer, a multiple of 16
+  static constexpr int GZ = 2 * BUF;         // gz [D] (each feature wave its block)
+  static constexpr int KP = GZ + D * 4;      // <phi(k), dphi(k)> / beta partials [2][NJ][BCH]
+  static constexpr int LDS = KP + 2 * NJ * BCH * 4;
+  static_assert(BUF % 16 == 0, "buffers stay 16-byte aligned");
+};
+
+// Row operand of k-step ks with the features in the permuted order: lane
+// group g holds features 16 ks + perm_pos(8 g + e), e = 0..7, of row r (two
+// 8-byte pieces of a tile stored in natural order).
+template <int D>
+__device__ __forceinline__ u32x4 row_operand_perm(const char* tile, int r, int ks, int g) {
+  const int p0 = 16 * ks + perm_pos(8 * g), p1 = 16 * ks + perm_pos(8 * g + 4);
+  const u32x2 x = *reinterpret_cast<const u32x2*>(tile + tile_off<D>(r, p0 >> 3) + ((p0 & 7) << 1));
+  const u32x2 y = *reinterpret_cast<const u32x2*>(tile + tile_off<D>(r, p1 >> 3) + ((p1 & 7) << 1));
+  return u32x4{x[0], x[1], y[0], y[1]};
+}
+
+// Raw inputs of one chunk for one thread: row tid / BPR, block tid % BPR;
+// and the decay value of token lane % 32.
+struct Raw2 {
+  u32x4 q, k, v;
+  f32x4 d[2];    // dout as fp32
+  float2 th;     // r_t and h_t (from pass A)
+  float al;
+};
 
 template <int D, int DECAY>
-__global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_b(const BwArgs a) {
-  using L = BL<D, DECAY>;
-  constexpr int NJ = L::NJ;
+__device__ __forceinline__ void load_raw2(const BwArgs& a, int64_t bh, int t0, int tid, Raw2& x) {
+  constexpr int BPR = D / 8;
+  const int r = tid / BPR, b = tid % BPR;
+  const int64_t T = a.T;
+  const int64_t t = min(int64_t(t0 + r), T - 1);
+  const int64_t row = (bh * T + t) * D + 8 * b;
+  x.th = *reinterpret_cast<const float2*>(a.tok + (bh * T + t) * 2);
+  x.q = *reinterpret_cast<const u32x4*>(a.q + row);
+  x.k = *reinterpret_cast<const u32x4*>(a.k + row);
+  x.v = *reinterpret_cast<const u32x4*>(a.v + row);
+  if (a.dout_f32) {
+    const float* dp = static_cast<const float*>(a.dout) + row;
+    x.d[0] = *reinterpret_cast<const f32x4*>(dp);
+    x.d[1] = *reinterpret_cast<const f32x4*>(dp + 4);
+  } else {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const bf16_t*>(a.dout) + row);
+    float f[8];
+    unpack8(w, f, bf16_t{});
+    x.d[0] = f32x4{f[0], f[1], f[2], f[3]};
+    x.d[1] = f32x4{f[4], f[5], f[6], f[7]};
+  }
+  x.al = 1.f;
+  if constexpr (DECAY != 0)
+    x.al = a.decay[bh * T + min(int64_t(t0 + (tid & 31)), T - 1)];
+}
+
+// Stage one chunk into buffer buf: phi(q) (high, low), phi(k) (high, low, at
+// permuted feature positions), v, g = r_t dout (high, low; with a decay also
+// e^{l_t} g), and the per-token scalars.  Rows past the end are zero.
+template <int D, int DECAY>
+__device__ __forceinline__ void stage2(const BwArgs& a, int t0, int tid, const Raw2& x, char* buf) {
+  using L = BL2<D, DECAY>;
+  float* F = reinterpret_cast<float*>(buf + L::FB);
+  const int r = tid / L::BPR, b = tid % L::BPR, lane = tid & 63;
+  float lam = 0.f, bet = 1.f, tot = 0.f;
+  if constexpr (DECAY != 0) {
+    Raw rx;
+    rx.al = x.al;
+    chunk_decay<DECAY>(rx, t0, a.T, lane, lam, bet, tot);
+  }
+  if (tid < BCH) {
+    F[L::LAM + tid] = lam;
+    F[L::BET + tid] = bet;
+    if (tid == 0) F[L::TOT] = tot;
+  }
+  const bool valid = t0 + r < a.T;
+  const int pr = perm_pos(r);
+  float lr = 0.f;
+  if constexpr (DECAY != 0) lr = __shfl(lam, r);
+  float fq[8], fk[8];
+  unpack8(x.q, fq, bf16_t{});
+  unpack8(x.k, fk, bf16_t{});
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    fq[e] = valid ? elu1_fast(fq[e]) : 0.f;
+    fk[e] = valid ? elu1_fast(fk[e]) : 0.f;
+  }
+  const u32x4 qh = pack8(fq);
+  blk_write<D>(buf + L::Q, pr, b, qh);
+  blk_write<D>(buf + L::QL, pr, b, low8(fq, qh));
+  const u32x4 kh = pack8(fk);
+  row_write_perm<D>(buf + L::K, pr, b, kh);
+  row_write_perm<D>(buf + L::KL, pr, b, low8(fk, kh));
+  blk_write<D>(buf + L::V, pr, b, valid ? x.v : u32x4{0u, 0u, 0u, 0u});
+  const float rt = valid ? x.th.x : 0.f, ht = valid ? x.th.y : 0.f;
+  float gv[8] = {x.d[0][0] * rt, x.d[0][1] * rt, x.d[0][2] * rt, x.d[0][3] * rt,
+                 x.d[1][0] * rt, x.d[1][1] * rt, x.d[1][2] * rt, x.d[1][3] * rt};
+  const u32x4 gh = pack8(gv);
+  blk_write<D>(buf + L::GH, pr, b, gh);
+  blk_write<D>(buf + L::GL, pr, b, low8(gv, gh));
+  const float wq = DECAY ? __expf(lr) : 1.f;   // query weight from the chunk's start
+  if constexpr (DECAY != 0) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) gv[e] *= wq;
+    const u32x4 wh = pack8(gv);
+    blk_write<D>(buf + L::WH, pr, b, wh);
+    blk_write<D>(buf + L::WL, pr, b, low8(gv, wh));
+  }
+  if (b == 0) {
+    F[L::HT + r] = ht;
+    F[L::HW + pr] = wq * ht;
+  }
+}
+
+// The causal weights of the score tile held by this lane (column s = n, rows
+// t = 8 (i / 4) + 4 g + i % 4): e^{l_t - l_s} for t >= s, else 0.
+template <int DECAY>
+__device__ __forceinline__ void causal_weights(const float* F, int LAMOFF, int g, int n,
+                                               float (&wt)[16]) {
+  const float ls = DECAY ? F[LAMOFF + n] : 0.f;
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) {
+    f32x4 lt = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (DECAY != 0) lt = *reinterpret_cast<const f32x4*>(F + LAMOFF + 8 * q4 + 4 * g);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = 8 * q4 + 4 * g + e;
+      wt[4 * q4 + e] = t >= n ? (DECAY ? __expf(lt[e] - ls) : 1.f) : 0.f;
+    }
+  }
+}
+
+template <int D, int DECAY>
+__global__ __launch_bounds__(128 * (D / 32)) void bwd_pass_b2(const BwArgs a) {
+  using L = BL2<D, DECAY>;
+  constexpr int NJ = L::NJ, KS = D / 16;
   __shared__ __align__(16) char smem[L::LDS];
-  float* F = reinterpret_cast<float*>(smem + L::F);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, n = lane & 31;
+  const bool value_wave = w < NJ;
+  const int wb = value_wave ? w : w - NJ;   // this wave's 32-wide block (j or f)
   const int64_t bh = blockIdx.x / a.nseg;
   const int seg = blockIdx.x % a.nseg;
   const int T = a.T;
   const int nchunks = (T + BCH - 1) / BCH;
   const int c0 = seg * a.cps, c1 = min(c0 + a.cps, nchunks);
+  if (c0 >= c1) return;   // the whole workgroup: no barrier is reached
 
-  // G at the segment's end: transposed tiles (rows j of block w, columns f)
-  f32x16 G[NJ];
+  // G at the segment's end (slot layout rows f, columns j): value waves
+  // hold X[fb] = rows f of block fb, columns j of block wb; feature waves
+  // X[jb] = rows j of block jb, columns f of block wb
+  f32x16 X[NJ];
   {
     const float* src = a.gslot + (bh * a.nseg + seg) * int64_t(D * D + D);
 #pragma unroll
-    for (int fb = 0; fb < NJ; ++fb)
+    for (int ob = 0; ob < NJ; ++ob)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int f = 32 * fb + n, j = 32 * w + 8 * (i >> 2) + 4 * g + (i & 3);
-        G[fb][i] = src[f * D + j];
+        const int row = 32 * ob + 8 * (i >> 2) + 4 * g + (i & 3), col = 32 * wb + n;
+        X[ob][i] = value_wave ? src[row * D + col] : src[col * D + row];
       }
-    if (tid < D) F[L::Z + tid] = src[D * D + tid];
-    write_state_tile<D>(smem + L::SB, smem + L::SBL, G, w, g, n);
+    if (!value_wave && g == 0)
+      reinterpret_cast<float*>(smem + L::GZ)[32 * wb + n] = src[D * D + 32 * wb + n];
   }
+
+  Raw2 raw;
+  load_raw2<D, DECAY>(a, bh, (c1 - 1) * BCH, tid, raw);
+  stage2<D, DECAY>(a, (c1 - 1) * BCH, tid, raw, smem);
+  if (c1 - 2 >= c0) load_raw2<D, DECAY>(a, bh, (c1 - 2) * BCH, tid, raw);
   __syncthreads();
 
-  Raw raw;
-  if (c0 < c1) load_raw<D, DECAY, true>(a, bh, (c1 - 1) * BCH, tid, raw);
-  for (int c = c1 - 1; c >= c0; --c) {
+  // one loop per kind of wave (each keeps only its own loop-invariant
+  // addresses live), the same barriers in both
+  auto chunk = [&](int c, auto value_kind) {
+    constexpr bool VW = decltype(value_kind)::value;
+    int tid_ = tid;
+    asm volatile("" : "+v"(tid_));
+    const int tid = tid_, lane = tid_ & 63, g = lane >> 5, n = lane & 31;
     const int t0 = c * BCH;
-    float lam, bet, tot;
-    stage<D, DECAY, false>(a, bh, t0, tid, raw, smem, lam, bet, tot);
-    __syncthreads();   // tiles, h, gz increments, decay
-    if (c - 1 >= c0) load_raw<D, DECAY, true>(a, bh, t0 - BCH, tid, raw);
+    const char* cur = smem + ((c1 - 1 - c) & 1) * L::BUF;
+    char* nxt = smem + ((c1 - c) & 1) * L::BUF;
+    const float* F = reinterpret_cast<const float*>(cur + L::FB);
+    const bool more = c - 1 >= c0;
+    // the next chunk (c - 1) into the other buffer, and its successor's raw
+    // inputs in flight: feature waves before their products, value waves after
+    auto stage_next = [&]() {
+      if (more) {
+        stage2<D, DECAY>(a, t0 - BCH, tid, raw, nxt);
+        if (c - 2 >= c0) load_raw2<D, DECAY>(a, bh, t0 - 2 * BCH, tid, raw);
+      }
+    };
     const bool vs = t0 + n < T;
-    // key s = n: e^{l_last - l_s} to the chunk's end; beta_s
-    const float es = DECAY ? __expf(tot - lam) : 1.f;
-
-    // Every product's operands are read before its MFMAs (pass B holds
-    // fewer values than pass A: all of them fit, with a decay too); phi(k)
-    // and v of key n are kept from the scores and B for dv and dk, and the
-    // state operands of dv are read before the epilogue between.
-    constexpr int KS = D / 16;
-    u32x4 ok[KS], okl[KS], ov[KS];
-
-    // scores A (rows t, columns s = n)
-    f32x16 at = zero16();
-    {
-      u32x4 aq[KS], aql[KS];
-      row_ops<D>(smem + L::Q, perm_pos(n), g, aq);
-      row_ops<D>(smem + L::QL, perm_pos(n), g, aql);
-      row_ops<D>(smem + L::K, perm_pos(n), g, ok);
-      row_ops<D>(smem + L::KL, perm_pos(n), g, okl);
-#pragma unroll
-      for (int fs = 0; fs < KS; ++fs) {
-        at = mfma(aq[fs], ok[fs], at);
-        at = mfma(aq[fs], okl[fs], at);
-        at = mfma(aql[fs], ok[fs], at);
-      }
-    }
-    // B (rows t, columns s): g_t . v_s + h_t
-    f32x16 bt = zero16();
-    {
-      u32x4 gh[KS], gl[KS];
-      row_ops<D>(smem + L::GH, perm_pos(n), g, gh);
-      row_ops<D>(smem + L::GL, perm_pos(n), g, gl);
-      row_ops<D>(smem + L::V, perm_pos(n), g, ov);
-#pragma unroll
-      for (int js = 0; js < KS; ++js) {
-        bt = mfma(gh[js], ov[js], bt);
-        bt = mfma(gl[js], ov[js], bt);
-      }
-    }
-    // dv's state operands, read while B finishes
-    u32x4 os[KS], osl[KS];
-    tr_ops<D, KS>(smem + L::SB, 32 * w, lane, os);
-    tr_ops<D, KS>(smem + L::SBL, 32 * w, lane, osl);
-
-    // causal weights of (t, s = n): e^{l_t - l_s} for t >= s (beta_s later)
+    const float tot = DECAY ? F[L::TOT] : 0.f;
+    const float es = DECAY ? __expf(tot - F[L::LAM + n]) : 1.f;   // key n to the chunk's end
+    const float bet = DECAY == 2 ? F[L::BET + n] : 1.f;
+    const float ec = DECAY ? __expf(tot) : 1.f;
     float wt[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int t = 8 * (i >> 2) + 4 * g + (i & 3);
-      wt[i] = t >= n ? (DECAY ? __expf(F[L::LAM + t] - lam) : 1.f) : 0.f;
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int t = 8 * (i >> 2) + 4 * g + (i & 3);
-      at[i] *= wt[i];
-      bt[i] = (bt[i] + F[L::HT + t]) * wt[i];
-    }
-    u32x4 ah[2], al[2], bh_[2], bl_[2];
-    split_acc(at, ah, al);
-    split_acc(bt, bh_, bl_);
+    constexpr int GA = DECAY ? L::WH : L::GH, GB = DECAY ? L::WL : L::GL;
 
-    // dv^T / beta_s (rows j of block w, columns s): e^{l_last - l_s} G^T
-    // phi(k) + g^T A
-    u32x4 ogt[2], oglt[2];
-    tr_ops<D, 2>(smem + L::GH, 32 * w, lane, ogt);
-    tr_ops<D, 2>(smem + L::GL, 32 * w, lane, oglt);
-    f32x16 dvt = zero16();
+    if constexpr (VW) {
+      // scores A (rows t, columns s = n): phi(q) at permuted feature
+      // positions against phi(k) stored that way
+      f32x16 at = zero16();
 #pragma unroll
-    for (int fs = 0; fs < KS; ++fs) {
-      dvt = mfma(os[fs], ok[fs], dvt);
-      dvt = mfma(osl[fs], ok[fs], dvt);
-      dvt = mfma(os[fs], okl[fs], dvt);
-    }
-    if constexpr (DECAY != 0) dvt *= es;
+      for (int k0 = 0; k0 < KS; k0 += 2) {
+        u32x4 aq[2], aql[2], bk[2], bkl[2];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      dvt = mfma(ogt[ks], ah[ks], dvt);
-      dvt = mfma(ogt[ks], al[ks], dvt);
-      dvt = mfma(oglt[ks], ah[ks], dvt);
-    }
-    // dphi(k)^T / beta_s (rows f of block w, columns s): e^{l_last - l_s}
-    // (G v + gz) + phi(Q)^T B; G v and gz cancel in large part
-    u32x4 oqt[2], oqlt[2];
-    tr_ops<D, 2>(smem + L::Q, 32 * w, lane, oqt);
-    tr_ops<D, 2>(smem + L::QL, 32 * w, lane, oqlt);
-    f32x16 dkt = zero16();
-    {
-      u32x4 sr[KS], srl[KS];
-      row_ops<D>(smem + L::SB, 32 * w + n, g, sr);
-      row_ops<D>(smem + L::SBL, 32 * w + n, g, srl);
-#pragma unroll
-      for (int js = 0; js < KS; ++js) {
-        dkt = mfma(sr[js], ov[js], dkt);
-        dkt = mfma(srl[js], ov[js], dkt);
-      }
-    }
-    if constexpr (DECAY != 0) dkt *= es;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      dkt = mfma(oqt[ks], bh_[ks], dkt);
-      dkt = mfma(oqt[ks], bl_[ks], dkt);
-      dkt = mfma(oqlt[ks], bh_[ks], dkt);
-    }
-    {
-      float kdp = 0.f;   // <phi(k_s), dphi(k_s)> / beta_s over this lane's features
-      const int64_t row = (bh * T + t0 + n) * D + 32 * w + 4 * g;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        f32x4 v4, o4;
-        const int off = tile_off<D>(perm_pos(n), 4 * w + r) + 8 * g;
-        const f32x4 p4 = hilo4(smem + L::K, smem + L::KL, off);
-        const f32x4 z4 = *reinterpret_cast<const f32x4*>(F + L::Z + 32 * w + 4 * g + 8 * r);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 4 * r + e;
-          v4[e] = bet * dvt[i];
-          const float raw_ = dkt[i] + es * z4[e];
-          o4[e] = bet * raw_ * fminf(p4[e], 1.f);
-          kdp += p4[e] * raw_;
+        for (int kk = 0; kk < 2; ++kk) {
+          aq[kk] = row_operand_perm<D>(cur + L::Q, perm_pos(n), k0 + kk, g);
+          aql[kk] = row_operand_perm<D>(cur + L::QL, perm_pos(n), k0 + kk, g);
+          bk[kk] = row_operand<D>(cur + L::K, perm_pos(n), 2 * (k0 + kk) + g);
+          bkl[kk] = row_operand<D>(cur + L::KL, perm_pos(n), 2 * (k0 + kk) + g);
         }
-        if (vs) {
-          *reinterpret_cast<f32x4*>(a.dv + row + 8 * r) = v4;
-          *reinterpret_cast<f32x4*>(a.dk + row + 8 * r) = o4;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          at = mfma(aq[kk], bk[kk], at);
+          at = mfma(aq[kk], bkl[kk], at);
+          at = mfma(aql[kk], bk[kk], at);
         }
       }
-      if constexpr (DECAY != 0) {
-        kdp = swap_sum32(kdp);
-        if (g == 0) F[L::QP + w * BCH + n] = kdp;
-      }
-    }
+      causal_weights<DECAY>(F, L::LAM, g, n, wt);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) at[i] *= wt[i];
+      u32x4 ah[2], al[2];
+      split_acc(at, ah, al);
 
-    // G^T = e^{l_last} G^T + (e^{l_t} g)^T phi(Q)
-    {
-      constexpr int GA = DECAY ? L::WH : L::GH, GB = DECAY ? L::WL : L::GL;
-      const float ec = DECAY ? __expf(tot) : 1.f;
-      u32x4 ag[2], agl[2], bq[NJ][2], bql[NJ][2];
-      tr_ops<D, 2>(smem + GA, 32 * w, lane, ag);
-      tr_ops<D, 2>(smem + GB, 32 * w, lane, agl);
+      // dv^T / beta_s (rows j of block wb, columns s): e^{l_last - l_s}
+      // G^T phi(k) + g^T A, with G from the registers (contracting over f)
+      f32x16 dvt = zero16();
 #pragma unroll
       for (int fb = 0; fb < NJ; ++fb) {
-        tr_ops<D, 2>(smem + L::Q, 32 * fb, lane, bq[fb]);
-        tr_ops<D, 2>(smem + L::QL, 32 * fb, lane, bql[fb]);
-      }
-#pragma unroll
-      for (int fb = 0; fb < NJ; ++fb) {
-        if constexpr (DECAY != 0) G[fb] *= ec;
+        u32x4 sh[2], sl[2], bk[2], bkl[2];
+        split_acc(X[fb], sh, sl);
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          G[fb] = mfma(ag[ks], bq[fb][ks], G[fb]);
-          G[fb] = mfma(agl[ks], bq[fb][ks], G[fb]);
-          G[fb] = mfma(ag[ks], bql[fb][ks], G[fb]);
+          bk[ks] = row_operand<D>(cur + L::K, perm_pos(n), 2 * (2 * fb + ks) + g);
+          bkl[ks] = row_operand<D>(cur + L::KL, perm_pos(n), 2 * (2 * fb + ks) + g);
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          dvt = mfma(sh[ks], bk[ks], dvt);
+          dvt = mfma(sl[ks], bk[ks], dvt);
+          dvt = mfma(sh[ks], bkl[ks], dvt);
         }
       }
-    }
-    __syncthreads();   // every read of the old G tile and of gz done
-    write_state_tile<D>(smem + L::SB, smem + L::SBL, G, w, g, n);
-    if (tid < D) {
-      float s = 0.f;
+      if constexpr (DECAY != 0) dvt *= es;
+      u32x4 ogt[2], oglt[2];
+      tr_ops<D, 2>(cur + L::GH, 32 * wb, lane, ogt);
+      tr_ops<D, 2>(cur + L::GL, 32 * wb, lane, oglt);
 #pragma unroll
-      for (int ww = 0; ww < L::NW; ++ww) s += F[L::ZP + ww * D + tid];
-      F[L::Z + tid] = (DECAY ? __expf(tot) : 1.f) * F[L::Z + tid] + s;
+      for (int ks = 0; ks < 2; ++ks) {
+        dvt = mfma(ogt[ks], ah[ks], dvt);
+        dvt = mfma(ogt[ks], al[ks], dvt);
+        dvt = mfma(oglt[ks], ah[ks], dvt);
+      }
+      if (vs) {
+        float* dst = a.dv + (bh * T + t0 + n) * D + 32 * wb + 4 * g;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          *reinterpret_cast<f32x4*>(dst + 8 * r) =
+              f32x4{bet * dvt[4 * r], bet * dvt[4 * r + 1], bet * dvt[4 * r + 2],
+                    bet * dvt[4 * r + 3]};
+      }
+
+      // G (rows f, columns j of block wb) = e^{l_last} G + phi(Q)^T (e^{l_t} g)
+      u32x4 ag[2], agl[2];
+      if constexpr (DECAY != 0) {
+        tr_ops<D, 2>(cur + GA, 32 * wb, lane, ag);
+        tr_ops<D, 2>(cur + GB, 32 * wb, lane, agl);
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          ag[ks] = ogt[ks];
+          agl[ks] = oglt[ks];
+        }
+      }
+#pragma unroll
+      for (int fb = 0; fb < NJ; ++fb) {
+        u32x4 bq[2], bql[2];
+        tr_ops<D, 2>(cur + L::Q, 32 * fb, lane, bq);
+        tr_ops<D, 2>(cur + L::QL, 32 * fb, lane, bql);
+        if constexpr (DECAY != 0) X[fb] *= ec;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          X[fb] = mfma(bq[ks], ag[ks], X[fb]);
+          X[fb] = mfma(bql[ks], ag[ks], X[fb]);
+          X[fb] = mfma(bq[ks], agl[ks], X[fb]);
+        }
+      }
+      stage_next();
+    } else {
+      stage_next();
+      // B (rows t, columns s = n): g_t . v_s + h_t
+      f32x16 bt = zero16();
+#pragma unroll
+      for (int k0 = 0; k0 < KS; k0 += 2) {
+        u32x4 gh[2], gl[2], ov[2];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          gh[kk] = row_operand<D>(cur + L::GH, perm_pos(n), 2 * (k0 + kk) + g);
+          gl[kk] = row_operand<D>(cur + L::GL, perm_pos(n), 2 * (k0 + kk) + g);
+          ov[kk] = row_operand<D>(cur + L::V, perm_pos(n), 2 * (k0 + kk) + g);
+        }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          bt = mfma(gh[kk], ov[kk], bt);
+          bt = mfma(gl[kk], ov[kk], bt);
+        }
+      }
+      causal_weights<DECAY>(F, L::LAM, g, n, wt);
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 h4 = *reinterpret_cast<const f32x4*>(F + L::HT + 8 * q4 + 4 * g);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bt[4 * q4 + e] = (bt[4 * q4 + e] + h4[e]) * wt[4 * q4 + e];
+      }
+      u32x4 bh_[2], bl_[2];
+      split_acc(bt, bh_, bl_);
+
+      // dphi(k)^T / beta_s (rows f of block wb, columns s): e^{l_last - l_s}
+      // (G v + gz) + phi(Q)^T B, with G^T from the registers (contracting
+      // over j) against v read at permuted positions
+      f32x16 dkt = zero16();
+#pragma unroll
+      for (int jb = 0; jb < NJ; ++jb) {
+        u32x4 sh[2], sl[2], ov[2];
+        split_acc(X[jb], sh, sl);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) ov[ks] = row_operand_perm<D>(cur + L::V, perm_pos(n), 2 * jb + ks, g);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          dkt = mfma(sh[ks], ov[ks], dkt);
+          dkt = mfma(sl[ks], ov[ks], dkt);
+        }
+      }
+      if constexpr (DECAY != 0) dkt *= es;
+      u32x4 oqt[2], oqlt[2];
+      tr_ops<D, 2>(cur + L::Q, 32 * wb, lane, oqt);
+      tr_ops<D, 2>(cur + L::QL, 32 * wb, lane, oqlt);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        dkt = mfma(oqt[ks], bh_[ks], dkt);
+        dkt = mfma(oqt[ks], bl_[ks], dkt);
+        dkt = mfma(oqlt[ks], bh_[ks], dkt);
+      }
+      float* gzl = reinterpret_cast<float*>(smem + L::GZ);
+      {
+        float kdp = 0.f;   // <phi(k_s), dphi(k_s)> / beta_s over this lane's features
+        const int64_t row = (bh * T + t0 + n) * D + 32 * wb + 4 * g;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int pc = perm_pos(32 * wb + 8 * r + 4 * g);   // stored column of these 4 features
+          const int off = tile_off<D>(perm_pos(n), pc >> 3) + ((pc & 7) << 1);
+          const f32x4 p4 = hilo4(cur + L::K, cur + L::KL, off);
+          const f32x4 z4 = *reinterpret_cast<const f32x4*>(gzl + 32 * wb + 8 * r + 4 * g);
+          f32x4 o4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float raw_ = dkt[4 * r + e] + es * z4[e];
+            o4[e] = bet * raw_ * fminf(p4[e], 1.f);
+            kdp += p4[e] * raw_;
+          }
+          if (vs) *reinterpret_cast<f32x4*>(a.dk + row + 8 * r) = o4;
+        }
+        if constexpr (DECAY != 0) {
+          kdp = swap_sum32(kdp);
+          if (g == 0) reinterpret_cast<float*>(smem + L::KP)[((c & 1) * NJ + wb) * BCH + n] = kdp;
+        }
+      }
+
+      // G^T (rows j, columns f of block wb) = e^{l_last} G^T + (e^{l_t} g)^T phi(Q)
+#pragma unroll
+      for (int jb = 0; jb < NJ; ++jb) {
+        u32x4 ag[2], agl[2];
+        tr_ops<D, 2>(cur + GA, 32 * jb, lane, ag);
+        tr_ops<D, 2>(cur + GB, 32 * jb, lane, agl);
+        if constexpr (DECAY != 0) X[jb] *= ec;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          X[jb] = mfma(ag[ks], oqt[ks], X[jb]);
+          X[jb] = mfma(agl[ks], oqt[ks], X[jb]);
+          X[jb] = mfma(ag[ks], oqlt[ks], X[jb]);
+        }
+      }
+      // gz (feature 32 wb + n) = e^{l_last} gz + sum_t e^{l_t} h_t phi(q_t):
+      // this lane's tokens are the tile rows of its phi(q) operands
+      float inc = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const f32x4 h0 = *reinterpret_cast<const f32x4*>(F + L::HW + 16 * ks + 8 * g);
+        const f32x4 h1 = *reinterpret_cast<const f32x4*>(F + L::HW + 16 * ks + 8 * g + 4);
+        float ph[8], pl[8];
+        unpack8(oqt[ks], ph, bf16_t{});
+        unpack8(oqlt[ks], pl, bf16_t{});
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          inc += (ph[e] + pl[e]) * h0[e];
+          inc += (ph[e + 4] + pl[e + 4]) * h1[e];
+        }
+      }
+      inc = swap_sum32(inc);
+      if (g == 0) gzl[32 * wb + n] = fmaf(ec, gzl[32 * wb + n], inc);
     }
-    if constexpr (DECAY != 0) {
-      if (w == 0 && g == 0 && vs) {
+    __syncthreads();   // chunk c - 1 staged; every read of chunk c's buffer done
+    if constexpr (DECAY != 0 && !VW) {
+      if (w == NJ && lane < BCH && t0 + lane < T) {
+        const float* kp = reinterpret_cast<const float*>(smem + L::KP) + (c & 1) * NJ * BCH;
         float s = 0.f;
 #pragma unroll
-        for (int ww = 0; ww < L::NW; ++ww) s += F[L::QP + ww * BCH + n];
-        a.kd[bh * T + t0 + n] = s;
+        for (int jb = 0; jb < NJ; ++jb) s += kp[jb * BCH + lane];
+        a.kd[bh * T + t0 + lane] = s;
       }
     }
-    __syncthreads();
-  }
+  };
+  if (value_wave)
+    for (int c = c1 - 1; c >= c0; --c) chunk(c, std::true_type{});
+  else
+    for (int c = c1 - 1; c >= c0; --c) chunk(c, std::false_type{});
 }
 
 // ----------------------------------------------------- decay gradient
@@ -1120,7 +1349,7 @@ hipError_t launch_d(const Problem& pb, const BwArgs& a, float* dS0, float* dz0, 
   constexpr int PER = (D * D + D + 255) / 256;
   bwd_rscan<D, DECAY != 0><<<dim3(unsigned(pb.BH() * PER)), dim3(256), 0, st>>>(
       a.gslot, a.lgam, a.nseg, dS0, dz0);
-  bwd_pass_b<D, DECAY><<<dim3(nwg), dim3(64 * (D / 32)), 0, st>>>(a);
+  bwd_pass_b2<D, DECAY><<<dim3(nwg), dim3(128 * (D / 32)), 0, st>>>(a);
   if constexpr (DECAY != 0) {
     const int ntile = (a.T + DG_TILE - 1) / DG_TILE;
     const unsigned nb = unsigned(pb.BH() * ntile);
