@@ -1,6 +1,6 @@
 // Gradients of the causal prefill by chunks on CDNA4 MFMA (gfx950), for
-// bf16 inputs with elu+1 features, d' = d_v = D in {64, 128}, and no decay,
-// the SSD decay or the RFA gate.
+// bf16 inputs, d' = d_v = D in {64, 128}: elu+1 features with no decay, the
+// SSD decay or the RFA gate, or identity features with the mLSTM gates.
 //
 // With L = sum_t <dout_t, o_t>, o_t = num_t r_t (r_t = 1 / (den_t + eps), or
 // 1 / max(|den_t|, 1), or 1), the recurrence S_t = alpha_t S_{t-1} +
@@ -25,6 +25,18 @@
 // gradient goes through log alpha: dL/dl_t = <phi(q_t), dphi(q_t)> -
 // <phi(k_t), dphi(k_t)>, and dL/dlog alpha_r is its suffix sum over t >= r;
 // beta's own gradient is <phi(k_s), dphi(k_s)> / beta_s.
+//
+// mLSTM gates (wikillm "Linear attention", Variants / mLSTM): the state is
+// carried scaled by the forward's stabiliser m_t = max(log f_t + m_{t-1},
+// itilde_t), so the recurrence is the one above with alpha'_t = e^{log f_t
+// + m_{t-1} - m_t} and beta'_t = e^{itilde_t - m_t}, both at most 1, and
+// the read-out of the scaled state has its max1 floor at e^{-m_t}.  Pass A
+// rebuilds m_t per chunk from each segment's start stabiliser (the
+// prefill's scan) and leaves log alpha'_t, beta'_t for pass B.  L depends
+// on the gates through the true alpha = f, beta = e^{itilde}: dL/dlog f_r
+// is the suffix sum above, and dL/ditilde_r = beta'_r kd_r with kd_r =
+// <phi(k_r), dphi(k_r)> / beta'_r as pass B leaves it; no gate gradient
+// divides by a decay.
 //
 // Schedule (one workgroup per segment of whole 32-token chunks):
 //   forward stages 1 and 2 of the prefill: the start state of every segment;
@@ -110,7 +122,14 @@ struct BwArgs {
   const bf16_t* k;
   const bf16_t* v;
   const void* dout;
-  const float* decay;   // [BH, T] alpha (SSD) or the gate g (RFA); null without decay
+  const float* decay;   // [BH, T] alpha (SSD), the gate g (RFA) or the mLSTM forget
+                        // pre-activation; null without decay
+  const float* igate;   // mLSTM: [BH, T] input-gate pre-activations
+  // mLSTM: the stabiliser of each segment's start state at m0 + bh * m0_bh
+  // + s (null: 0, the zero start state's)
+  const float* m0;
+  int64_t m0_bh;
+  int fgate_exp;        // mLSTM: the forget pre-activation is log f itself
   int dout_f32;
   // start state of (b, h) and segment s at S0 + bh * s_bh + s * s_seg (z at
   // z0 + bh * z_bh + s * s_seg); null: zero
@@ -126,6 +145,8 @@ struct BwArgs {
   float* qd;     // [BH, T]: <phi(q_t), dphi(q_t)> (pass A, with a decay)
   float* kd;     // [BH, T]: <phi(k_t), dphi(k_t)> / beta_t (pass B, with a decay)
   float* dpart;  // [BH, ceil(T / DG_TILE)]: per-tile totals of the decay gradient's terms
+  float* ab;     // mLSTM: [BH, T, 2]: log alpha'_t and beta'_t (pass A, for pass B)
+  float* digate; // mLSTM: [BH, T]: dL/d input-gate pre-activation
   int T, cps, nseg, norm;
   float eps;
 };
@@ -218,7 +239,8 @@ __device__ __forceinline__ void tr_ops(const char* tile, int col0, int lane, u32
 struct Raw {
   u32x4 q[2], k[2], v[2];
   f32x4 d[2][2];   // dout as fp32
-  float al;
+  float al;        // mLSTM: the forget pre-activation
+  float ig;        // mLSTM: the input-gate pre-activation
 };
 
 template <int D, int DECAY>
@@ -249,6 +271,8 @@ __device__ __forceinline__ void load_raw(const BwArgs& a, int64_t bh, int t0, in
   x.al = 1.f;
   if constexpr (DECAY != 0)
     x.al = a.decay[bh * T + min(int64_t(t0 + (tid & 31)), T - 1)];
+  if constexpr (DECAY == 3)
+    x.ig = a.igate[bh * T + min(int64_t(t0 + (tid & 31)), T - 1)];
 }
 
 // Sum of v[e] over the lanes of this wave that share lane % BPR (the rows
@@ -285,21 +309,70 @@ __device__ __forceinline__ void chunk_decay(const Raw& x, int t0, int T, int lan
   tot = __shfl(lam, 31, 32);
 }
 
+// The mLSTM gates of one chunk in the stabilised frame, computed by every
+// wave (no barrier needed): from the stabiliser m before the chunk (mst, in
+// every lane; replaced by the one after it), lane l gets for token l % 32
+// the stabiliser m_t = max(log f_t + m_{t-1}, itilde_t) in mt, the
+// inclusive log-prefix of alpha'_t = e^{log f_t + m_{t-1} - m_t} in lam and
+// beta'_t = e^{itilde_t - m_t} in bet (la: log alpha'_t itself), the chunk
+// total in tot.  m_t is a prefix over the maps x -> max(x + log f_t,
+// itilde_t), which compose as (A1, B1) then (A2, B2) = (A1 + A2, max(B1 +
+// A2, B2)).  Tokens past the end are the identity map (alpha' = 1, beta' = 0).
+__device__ __forceinline__ void chunk_decay_ml(float fpre, float ipre, int fexp, int t0, int T,
+                                               int lane, float& mst, float& mt, float& la,
+                                               float& lam, float& bet, float& tot) {
+  const int l = lane & 31;
+  const bool valid = t0 + l < T;
+  const float lf = valid ? log_forget(fpre, fexp) : 0.f;
+  float A = lf, B = valid ? ipre : -1e30f;
+#pragma unroll
+  for (int off = 1; off < 32; off <<= 1) {
+    const float Ap = __shfl_up(A, off, 32), Bp = __shfl_up(B, off, 32);
+    if (l >= off) {
+      B = fmaxf(Bp + A, B);
+      A = Ap + A;
+    }
+  }
+  mt = fmaxf(mst + A, B);
+  float mp = __shfl_up(mt, 1, 32);
+  if (l == 0) mp = mst;
+  la = valid ? fmaxf(lf + mp - mt, kLogFloorB) : 0.f;
+  bet = valid ? __expf(ipre - mt) : 0.f;
+  lam = la;
+#pragma unroll
+  for (int off = 1; off < 32; off <<= 1) {
+    const float y = __shfl_up(lam, off, 32);
+    if (l >= off) lam += y;
+  }
+  tot = __shfl(lam, 31, 32);
+  mst = __shfl(mt, 31, 32);
+}
+
 // Stage one chunk into LDS for pass A: phi(q), phi(k) (high, low), v, the
 // fp32 dout, phi(q_t) . z and this wave's increments of z (sum w_s
 // phi(k_s)).  Rows past the end of the sequence are zero.  lam, bet, tot
-// return the chunk's decay (see chunk_decay; 0, 1, 0 without).
+// return the chunk's decay (see chunk_decay; 0, 1, 0 without); with the
+// mLSTM gates (identity features) mst carries the stabiliser across chunks,
+// mt returns token lane % 32's, and log alpha', beta' go to a.ab for pass B.
 template <int D, int DECAY>
 __device__ __forceinline__ void stage(const BwArgs& a, int64_t bh, int t0, int tid, const Raw& x,
-                                      char* smem, float& lam, float& bet, float& tot) {
+                                      char* smem, float& lam, float& bet, float& tot, float& mst,
+                                      float& mt) {
   using L = BL<D, DECAY>;
   float* F = reinterpret_cast<float*>(smem + L::F);
   const int b = tid % L::BPR, lane = tid & 63, w = tid >> 6;
   lam = 0.f;
   bet = 1.f;
   tot = 0.f;
-  if constexpr (DECAY != 0) {
+  if constexpr (DECAY == 3) {
+    float la;
+    chunk_decay_ml(x.al, x.ig, a.fgate_exp, t0, a.T, lane, mst, mt, la, lam, bet, tot);
+    if (w == 0 && lane < BCH && t0 + lane < a.T)
+      *reinterpret_cast<float2*>(a.ab + (bh * a.T + t0 + lane) * 2) = make_float2(la, bet);
+  } else if constexpr (DECAY != 0) {
     chunk_decay<DECAY>(x, t0, a.T, lane, lam, bet, tot);
+  }
+  if constexpr (DECAY != 0) {
     if (w == 0 && lane < BCH) {
       F[L::LAM + lane] = lam;
       F[L::BET + lane] = bet;
@@ -323,8 +396,8 @@ __device__ __forceinline__ void stage(const BwArgs& a, int64_t bh, int t0, int t
     unpack8(x.k[rr], fk, bf16_t{});
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      fq[e] = valid ? elu1_fast(fq[e]) : 0.f;
-      fk[e] = valid ? elu1_fast(fk[e]) : 0.f;
+      fq[e] = valid ? (DECAY == 3 ? fq[e] : elu1_fast(fq[e])) : 0.f;
+      fk[e] = valid ? (DECAY == 3 ? fk[e] : elu1_fast(fk[e])) : 0.f;
     }
     const u32x4 qh = pack8(fq);
     blk_write<D>(smem + L::Q, pr, b, qh);
@@ -390,12 +463,16 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_a(const BwArgs a) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) gzp[e] = 0.f;
   float Lseg = 0.f;   // log-decay from the segment's start to the current chunk's start
+  // mLSTM: the stabiliser before the current chunk (the segment's start
+  // state's to begin with), and token n's
+  float mst = 0.f, mt = 0.f;
+  if constexpr (DECAY == 3) mst = a.m0 ? a.m0[bh * a.m0_bh + seg] : 0.f;
   Raw raw;
   if (c0 < c1) load_raw<D, DECAY>(a, bh, c0 * BCH, tid, raw);
   for (int c = c0; c < c1; ++c) {
     const int t0 = c * BCH;
     float lam, bet, tot;
-    stage<D, DECAY>(a, bh, t0, tid, raw, smem, lam, bet, tot);
+    stage<D, DECAY>(a, bh, t0, tid, raw, smem, lam, bet, tot, mst, mt);
     __syncthreads();   // tiles, phi(q) . z, z increments, decay
     if (c + 1 < c1) load_raw<D, DECAY>(a, bh, t0 + BCH, tid, raw);   // next chunk, in flight meanwhile
     const bool vt = t0 + n < T;
@@ -454,7 +531,10 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_a(const BwArgs a) {
     }
     dsum = swap_sum32(dsum);
     const float den = dsum + eq * F[L::DI + n];
-    const float rt = a.norm == LA_NORM_NONE ? 1.f
+    // the read-out factor; with the mLSTM gates of the state scaled by
+    // e^{-m_t} (token n's stabiliser), whose max1 floor is e^{-m_t}
+    const float rt = DECAY == 3 ? readout_factor(a.norm, den, a.eps, mt)
+                     : a.norm == LA_NORM_NONE ? 1.f
                      : a.norm == LA_NORM_MAX1 ? 1.f / fmaxf(fabsf(den), 1.f)
                                               : 1.f / (den + a.eps);
     u32x4 ph[2], pl[2];
@@ -528,7 +608,8 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_a(const BwArgs a) {
     for (int ww = 0; ww < L::NW; ++ww) dot += F[L::HP + ww * BCH + n];
     float h = 0.f;
     if (a.norm == LA_NORM_SUM) h = -dot * rt;
-    else if (a.norm == LA_NORM_MAX1) h = fabsf(den) > 1.f ? -copysignf(1.f, den) * dot * rt : 0.f;
+    else if (a.norm == LA_NORM_MAX1)
+      h = fabsf(den) > (DECAY == 3 ? __expf(-mt) : 1.f) ? -copysignf(1.f, den) * dot * rt : 0.f;
     if (!vt) h = 0.f;
     if (w == 0 && g == 0) {
       F[L::HT + n] = h;
@@ -616,8 +697,9 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_a(const BwArgs a) {
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * r + e;
           const float dphi = dqt[i] + eq * z4[e] * h;
-          // elu+1 has slope 1 above 0 and e^x = phi(x) below: min(phi, 1)
-          o4[e] = dphi * fminf(p4[e], 1.f);
+          // elu+1 has slope 1 above 0 and e^x = phi(x) below: min(phi, 1);
+          // identity features (mLSTM): 1
+          o4[e] = DECAY == 3 ? dphi : dphi * fminf(p4[e], 1.f);
           qdp += p4[e] * dphi;
         }
         if (vt) *reinterpret_cast<f32x4*>(dst + 8 * r) = o4;
@@ -858,7 +940,7 @@ struct Raw2 {
   u32x4 q, k, v;
   f32x4 d[2];    // dout as fp32
   float2 th;     // r_t and h_t (from pass A)
-  float al;
+  float2 al;     // alpha (mLSTM: log alpha' and beta', from pass A)
 };
 
 template <int D, int DECAY>
@@ -883,9 +965,10 @@ __device__ __forceinline__ void load_raw2(const BwArgs& a, int64_t bh, int t0, i
     x.d[0] = f32x4{f[0], f[1], f[2], f[3]};
     x.d[1] = f32x4{f[4], f[5], f[6], f[7]};
   }
-  x.al = 1.f;
-  if constexpr (DECAY != 0)
-    x.al = a.decay[bh * T + min(int64_t(t0 + (tid & 31)), T - 1)];
+  x.al = make_float2(1.f, 1.f);
+  const int64_t ta = bh * T + min(int64_t(t0 + (tid & 31)), T - 1);
+  if constexpr (DECAY == 3) x.al = *reinterpret_cast<const float2*>(a.ab + ta * 2);
+  else if constexpr (DECAY != 0) x.al.x = a.decay[ta];
 }
 
 // Stage one chunk into buffer buf: phi(q) (high, low), phi(k) (high, low, at
@@ -897,9 +980,20 @@ __device__ __forceinline__ void stage2(const BwArgs& a, int t0, int tid, const R
   float* F = reinterpret_cast<float*>(buf + L::FB);
   const int r = tid / L::BPR, b = tid % L::BPR, lane = tid & 63;
   float lam = 0.f, bet = 1.f, tot = 0.f;
-  if constexpr (DECAY != 0) {
+  if constexpr (DECAY == 3) {
+    // log alpha' and beta' as pass A left them
+    const bool vt = t0 + (lane & 31) < a.T;
+    lam = vt ? x.al.x : 0.f;
+    bet = vt ? x.al.y : 0.f;
+#pragma unroll
+    for (int off = 1; off < 32; off <<= 1) {
+      const float y = __shfl_up(lam, off, 32);
+      if ((lane & 31) >= off) lam += y;
+    }
+    tot = __shfl(lam, 31, 32);
+  } else if constexpr (DECAY != 0) {
     Raw rx;
-    rx.al = x.al;
+    rx.al = x.al.x;
     chunk_decay<DECAY>(rx, t0, a.T, lane, lam, bet, tot);
   }
   if (tid < BCH) {
@@ -916,8 +1010,8 @@ __device__ __forceinline__ void stage2(const BwArgs& a, int t0, int tid, const R
   unpack8(x.k, fk, bf16_t{});
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    fq[e] = valid ? elu1_fast(fq[e]) : 0.f;
-    fk[e] = valid ? elu1_fast(fk[e]) : 0.f;
+    fq[e] = valid ? (DECAY == 3 ? fq[e] : elu1_fast(fq[e])) : 0.f;
+    fk[e] = valid ? (DECAY == 3 ? fk[e] : elu1_fast(fk[e])) : 0.f;
   }
   const u32x4 qh = pack8(fq);
   blk_write<D>(buf + L::Q, pr, b, qh);
@@ -1025,7 +1119,7 @@ __global__ __launch_bounds__(128 * (D / 32)) void bwd_pass_b2(const BwArgs a) {
     const bool vs = t0 + n < T;
     const float tot = DECAY ? F[L::TOT] : 0.f;
     const float es = DECAY ? __expf(tot - F[L::LAM + n]) : 1.f;   // key n to the chunk's end
-    const float bet = DECAY == 2 ? F[L::BET + n] : 1.f;
+    const float bet = DECAY >= 2 ? F[L::BET + n] : 1.f;
     const float ec = DECAY ? __expf(tot) : 1.f;
     float wt[16];
     constexpr int GA = DECAY ? L::WH : L::GH, GB = DECAY ? L::WL : L::GL;
@@ -1190,7 +1284,7 @@ __global__ __launch_bounds__(128 * (D / 32)) void bwd_pass_b2(const BwArgs a) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const float raw_ = dkt[4 * r + e] + es * z4[e];
-            o4[e] = bet * raw_ * fminf(p4[e], 1.f);
+            o4[e] = DECAY == 3 ? bet * raw_ : bet * raw_ * fminf(p4[e], 1.f);
             kdp += p4[e] * raw_;
           }
           if (vs) *reinterpret_cast<f32x4*>(a.dk + row + 8 * r) = o4;
@@ -1256,15 +1350,35 @@ __global__ __launch_bounds__(128 * (D / 32)) void bwd_pass_b2(const BwArgs a) {
 // dL/dlog alpha_r = R_r = sum_{t >= r} (qd_t - beta_t kd_t), then dL/da_r =
 // R_r / a_r (SSD) or dL/dg_r = R_r / g_r - kd_r (RFA: alpha = g, beta =
 // 1 - g); for a_r below kDecayExact, the exact <G_r, S_{r-1}> term comes
-// from decay_exact_kernel instead of R_r / a_r.  Two passes over tiles of DG_TILE tokens of every (b, h): the
+// from decay_exact_kernel instead of R_r / a_r.  mLSTM gates (beta = beta'
+// of the stabilised frame): dL/dfgate_r = R_r (1 - f_r), or R_r for the
+// exponential forget gate, with no division, and dL/ditilde_r = beta'_r
+// kd_r.  Two passes over tiles of DG_TILE tokens of every (b, h): the
 // tiles' totals, then per tile a suffix scan (4 tokens per thread, waves by
 // shuffles, the workgroup through LDS) plus the totals of the later tiles.
 constexpr int DG_TILE = 1024;
 
+struct DgArgs {
+  const float* decay;   // alpha, the gate, or the mLSTM forget pre-activation
+  const float* ab;      // mLSTM: log alpha', beta' per token
+  const float* qd;
+  const float* kd;
+  float* part;
+  float* dd;
+  float* digate;        // mLSTM
+  int T, ntile, fexp;
+};
+
 template <int DECAY>
-__device__ __forceinline__ float dl_term(const float* al, const float* qd, const float* kd,
-                                         int64_t i) {
-  return qd[i] - (DECAY == 2 ? 1.f - al[i] : 1.f) * kd[i];
+__device__ __forceinline__ float beta_of(const DgArgs& g, int64_t i) {
+  if constexpr (DECAY == 2) return 1.f - g.decay[i];
+  if constexpr (DECAY == 3) return g.ab[2 * i + 1];
+  return 1.f;
+}
+
+template <int DECAY>
+__device__ __forceinline__ float dl_term(const DgArgs& g, int64_t i) {
+  return g.qd[i] - beta_of<DECAY>(g, i) * g.kd[i];
 }
 
 // Sum over the 256 threads of a workgroup, returned to every thread.
@@ -1278,26 +1392,25 @@ __device__ __forceinline__ float block_sum256(float x, float* red) {
 }
 
 template <int DECAY>
-__global__ __launch_bounds__(256) void bwd_decay_tile_sums(const float* decay, const float* qd,
-                                                           const float* kd, float* part, int T,
-                                                           int ntile) {
+__global__ __launch_bounds__(256) void bwd_decay_tile_sums(const DgArgs g) {
   __shared__ float red[4];
+  const int T = g.T, ntile = g.ntile;
   const int64_t bh = blockIdx.x / ntile;
   const int tile = blockIdx.x % ntile;
   float s = 0.f;
   for (int i = threadIdx.x; i < DG_TILE; i += 256) {
     const int t = tile * DG_TILE + i;
-    if (t < T) s += dl_term<DECAY>(decay, qd, kd, bh * T + t);
+    if (t < T) s += dl_term<DECAY>(g, bh * T + t);
   }
   s = block_sum256(s, red);
-  if (threadIdx.x == 0) part[bh * ntile + tile] = s;
+  if (threadIdx.x == 0) g.part[bh * ntile + tile] = s;
 }
 
 template <int DECAY>
-__global__ __launch_bounds__(256) void bwd_decay_grad(const float* decay, const float* qd,
-                                                      const float* kd, const float* part,
-                                                      float* dd, int T, int ntile) {
+__global__ __launch_bounds__(256) void bwd_decay_grad(const DgArgs g) {
   __shared__ float red[4];
+  const int T = g.T, ntile = g.ntile;
+  const float* part = g.part;
   const int64_t bh = blockIdx.x / ntile;
   const int tile = blockIdx.x % ntile;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -1309,7 +1422,7 @@ __global__ __launch_bounds__(256) void bwd_decay_grad(const float* decay, const 
   const int t0 = tile * DG_TILE + 4 * tid;
   float x[4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) x[e] = t0 + e < T ? dl_term<DECAY>(decay, qd, kd, bh * T + t0 + e) : 0.f;
+  for (int e = 0; e < 4; ++e) x[e] = t0 + e < T ? dl_term<DECAY>(g, bh * T + t0 + e) : 0.f;
   float suf[4];
   suf[3] = x[3];
 #pragma unroll
@@ -1334,9 +1447,15 @@ __global__ __launch_bounds__(256) void bwd_decay_grad(const float* decay, const 
     if (t < T) {
       const int64_t i = bh * T + t;
       const float R = base + suf[e];
-      // near-zero decays: the exact term is added by decay_exact_kernel
-      const float da = decay[i] < kDecayExact ? 0.f : R / decay[i];
-      dd[i] = DECAY == 2 ? da - kd[i] : da;
+      if constexpr (DECAY == 3) {
+        // 1 - sigmoid(x) = 1 / (1 + e^x)
+        g.dd[i] = g.fexp ? R : R / (1.f + __expf(g.decay[i]));
+        g.digate[i] = g.ab[2 * i + 1] * g.kd[i];
+      } else {
+        // near-zero decays: the exact term is added by decay_exact_kernel
+        const float da = g.decay[i] < kDecayExact ? 0.f : R / g.decay[i];
+        g.dd[i] = DECAY == 2 ? da - g.kd[i] : da;
+      }
     }
   }
 }
@@ -1353,10 +1472,12 @@ hipError_t launch_d(const Problem& pb, const BwArgs& a, float* dS0, float* dz0, 
   if constexpr (DECAY != 0) {
     const int ntile = (a.T + DG_TILE - 1) / DG_TILE;
     const unsigned nb = unsigned(pb.BH() * ntile);
-    bwd_decay_tile_sums<DECAY><<<dim3(nb), dim3(256), 0, st>>>(a.decay, a.qd, a.kd, a.dpart,
-                                                               a.T, ntile);
-    bwd_decay_grad<DECAY><<<dim3(nb), dim3(256), 0, st>>>(a.decay, a.qd, a.kd, a.dpart, ddecay,
-                                                          a.T, ntile);
+    DgArgs dg;
+    dg.decay = a.decay; dg.ab = a.ab; dg.qd = a.qd; dg.kd = a.kd; dg.part = a.dpart;
+    dg.dd = ddecay; dg.digate = a.digate; dg.T = a.T; dg.ntile = ntile; dg.fexp = a.fgate_exp;
+    bwd_decay_tile_sums<DECAY><<<dim3(nb), dim3(256), 0, st>>>(dg);
+    bwd_decay_grad<DECAY><<<dim3(nb), dim3(256), 0, st>>>(dg);
+    if constexpr (DECAY == 3) return hipGetLastError();   // no division by a decay
     // near-zero decays: the exact gradient from each segment's start state
     // and the gradient state at its end (the reverse scan's slots)
     DecayExactArgs x;
@@ -1379,6 +1500,7 @@ hipError_t launch_kind(const Problem& pb, const BwArgs& a, float* dS0, float* dz
     case LA_DECAY_NONE: return launch_d<D, 0>(pb, a, dS0, dz0, ddecay, st);
     case LA_DECAY_SSD: return launch_d<D, 1>(pb, a, dS0, dz0, ddecay, st);
     case LA_GATE_RFA: return launch_d<D, 2>(pb, a, dS0, dz0, ddecay, st);
+    case LA_GATE_MLSTM: return launch_d<D, 3>(pb, a, dS0, dz0, ddecay, st);
     default: break;
   }
   return hipErrorInvalidValue;
@@ -1387,13 +1509,15 @@ hipError_t launch_kind(const Problem& pb, const BwArgs& a, float* dS0, float* dz
 size_t r256(size_t b) { return (b + 255) / 256 * 256; }
 
 struct BwLayout {
-  size_t fwd, sinit, zinit, gslot, tok, lgam, qd, kd, dpart, total;
+  size_t fwd, sinit, zinit, minit, gslot, tok, lgam, qd, kd, dpart, ab, total;
 };
 
 // Workspace: the prefill's (for the segment start states), a copy of the
 // initial state, one gradient state per segment, two floats per token; with
 // a decay also the segments' log-decays, two more floats per token and one
-// per tile of DG_TILE tokens.
+// per tile of DG_TILE tokens; with the mLSTM gates two more floats per token
+// (log alpha', beta') and a zero start stabiliser per (b, h) for the
+// prefill's stages when no initial state is given.
 BwLayout layout_of(const Problem& pb) {
   int cps, nseg, nsub, nslot;
   mfma_split(pb, &cps, &nseg, &nsub, &nslot);
@@ -1407,11 +1531,13 @@ BwLayout layout_of(const Problem& pb) {
   off += r256(BH * D * D * 4);
   l.zinit = off;
   off += r256(BH * D * 4);
+  l.minit = off;
+  if (pb.decay_kind == LA_GATE_MLSTM) off += r256(BH * 4);
   l.gslot = off;
   off += r256(BH * nseg * (D * D + D) * 4);
   l.tok = off;
   off += r256(BH * T * 2 * 4);
-  l.lgam = l.qd = l.kd = l.dpart = off;
+  l.lgam = l.qd = l.kd = l.dpart = l.ab = off;
   if (dec) {
     off += r256(BH * nseg * 4);
     l.qd = off;
@@ -1420,6 +1546,8 @@ BwLayout layout_of(const Problem& pb) {
     off += r256(BH * T * 4);
     l.dpart = off;
     off += r256(BH * ((T + DG_TILE - 1) / DG_TILE) * 4);
+    l.ab = off;
+    if (pb.decay_kind == LA_GATE_MLSTM) off += r256(BH * T * 2 * 4);
   }
   l.total = off;
   return l;
@@ -1428,10 +1556,12 @@ BwLayout layout_of(const Problem& pb) {
 }  // namespace
 
 bool backward_chunked(const Problem& p) {
-  return p.path == 1 && p.dtype == LA_BF16 && p.phi == LA_PHI_ELU1 &&
-         (p.decay_kind == LA_DECAY_NONE || p.decay_kind == LA_DECAY_SSD ||
-          p.decay_kind == LA_GATE_RFA) &&
-         !p.noncausal && p.T > 0 && p.dp == p.dv && (p.dv == 64 || p.dv == 128);
+  const bool gates = (p.phi == LA_PHI_ELU1 &&
+                      (p.decay_kind == LA_DECAY_NONE || p.decay_kind == LA_DECAY_SSD ||
+                       p.decay_kind == LA_GATE_RFA)) ||
+                     (p.phi == LA_PHI_IDENTITY && p.decay_kind == LA_GATE_MLSTM);
+  return p.path == 1 && p.dtype == LA_BF16 && gates && !p.noncausal && p.T > 0 &&
+         p.dp == p.dv && (p.dv == 64 || p.dv == 128);
 }
 
 Problem backward_plan(const Problem& p) {
@@ -1471,6 +1601,14 @@ hipError_t launch_backward_chunked(const Problem& p, const void* q, const void* 
   a.qd = reinterpret_cast<float*>(base + l.qd);
   a.kd = reinterpret_cast<float*>(base + l.kd);
   a.dpart = reinterpret_cast<float*>(base + l.dpart);
+  const bool ml = pb.decay_kind == LA_GATE_MLSTM;
+  a.ab = ml ? reinterpret_cast<float*>(base + l.ab) : nullptr;
+  a.igate = ml ? pb.igate : nullptr;
+  a.fgate_exp = ml ? pb.fgate_exp : 0;
+  a.digate = ml ? ddecay + pb.BH() * pb.T : nullptr;   // the second half of ddecay
+  // the start state's stabiliser (one segment; null: a zero state, m = 0)
+  a.m0 = ml && S0 ? pb.stab : nullptr;
+  a.m0_bh = 1;
   a.T = pb.T;
   a.cps = cps;
   a.nseg = nseg;
@@ -1487,15 +1625,25 @@ hipError_t launch_backward_chunked(const Problem& p, const void* q, const void* 
       if (e == hipSuccess)
         e = hipMemcpyAsync(zi, z0, size_t(pb.BH()) * D * 4, hipMemcpyDeviceToDevice, stream);
     } else {
-      e = launch_state_init(Si, pb.BH() * D * D, zi, pb.BH() * D, nullptr, 0, stream);
+      // no initial state: zero, with the mLSTM gates also its stabiliser
+      // (the caller's stab is read only with a state)
+      float* mi = reinterpret_cast<float*>(base + l.minit);
+      e = launch_state_init(Si, pb.BH() * D * D, zi, pb.BH() * D, ml ? mi : nullptr,
+                            ml ? pb.BH() : 0, stream);
     }
     if (e != hipSuccess) return e;
+    Problem pf = pb;
+    if (ml && !S0) pf.stab = reinterpret_cast<float*>(base + l.minit);
     void* fws = base + l.fwd;
-    e = launch_mfma_stage(pb, 1, q, k, v, Si, zi, nullptr, fws, stream);
+    e = launch_mfma_stage(pf, 1, q, k, v, Si, zi, nullptr, fws, stream);
     if (e != hipSuccess) return e;
-    e = launch_mfma_stage(pb, 2, q, k, v, Si, zi, nullptr, fws, stream);
+    e = launch_mfma_stage(pf, 2, q, k, v, Si, zi, nullptr, fws, stream);
     if (e != hipSuccess) return e;
     const float* slots = reinterpret_cast<const float*>(fws);
+    if (ml) {
+      a.m0 = mfma_ws_m0(pb, fws);
+      a.m0_bh = nseg + 1;
+    }
     a.S0 = slots;
     a.z0 = slots + D * D;
     a.s_bh = a.z_bh = int64_t(nslot) * E;

@@ -125,6 +125,10 @@ size_t mfma_workspace_bytes(const Problem& p);
 // slot nsub * s of (b, h) holds segment s's start state (S then z, D*D + D
 // floats per slot, at the start of the workspace).
 void mfma_split(const Problem& p, int* cps, int* nseg, int* nsub, int* nslot);
+// With more than one segment: the mLSTM stabiliser of each segment's start
+// state after stage 2, [BH, nseg + 1] floats in the workspace ws (the final
+// one last).
+float* mfma_ws_m0(const Problem& p, void* ws);
 hipError_t launch_mfma_stage(const Problem& p, int stage, const void* q, const void* k,
                              const void* v, float* S, float* z, void* out, void* ws,
                              hipStream_t stream);

@@ -1405,6 +1405,14 @@ size_t mfma_workspace_bytes(const Problem& p) {
          round256(size_t(p.BH()) * (sp.nseg + 1) * sizeof(float));
 }
 
+float* mfma_ws_m0(const Problem& p, void* ws) {
+  const Split sp = split_of(p);
+  const size_t E = size_t(p.dv) * p.dv + p.dv;
+  const size_t n = size_t(p.BH()) * sp.nslot;
+  return reinterpret_cast<float*>(static_cast<char*>(ws) + n * E * sizeof(float) +
+                                  2 * round256(n * sizeof(float)));
+}
+
 hipError_t launch_mfma_stage(const Problem& p, int stage, const void* q, const void* k,
                              const void* v, float* S, float* z, void* out, void* ws,
                              hipStream_t stream) {
@@ -1435,8 +1443,7 @@ hipError_t launch_mfma_stage(const Problem& p, int stage, const void* q, const v
     a.ws_logg = reinterpret_cast<float*>(base);
     base += round256(n * sizeof(float));
     a.ws_m = reinterpret_cast<float*>(base);
-    base += round256(n * sizeof(float));
-    a.ws_m0 = reinterpret_cast<float*>(base);
+    a.ws_m0 = mfma_ws_m0(p, ws);
   }
   if (p.dv == 128) {
     return p.dtype == LA_BF16 ? launch_chunk<128, bf16_t>(a, p.BH(), p.chunk, p.decay_kind, stage, stream)

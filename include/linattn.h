@@ -210,8 +210,10 @@ la_status la_prefill_stage(const la_desc* desc, int stage, const void* q, const 
  * segment) and B H T 2 fp32 (per token: the read-out's factor and the
  * divisor's gradient), each part rounded up to 256 bytes; with a decay also
  * B H nseg fp32 (each segment's log-decay), B H T 2 fp32 (per-token terms
- * of the decay gradient) and B H ceil(T / 1024) fp32 (their tile totals).  The per-token path: B H T (d_v + 2) fp32, B H T (d_v + 4) fp32 with
- * the mLSTM gates. */
+ * of the decay gradient) and B H ceil(T / 1024) fp32 (their tile totals);
+ * with the mLSTM gates also B H fp32 (a zero start stabiliser) and B H T 2
+ * fp32 (log alpha'_t, beta'_t).  The per-token path: B H T (d_v + 2) fp32,
+ * B H T (d_v + 4) fp32 with the mLSTM gates. */
 la_status la_prefill_backward_workspace_size(const la_desc* desc, size_t* bytes);
 
 /* Gradients of a causal prefill for training ([lesson] Developer level and
@@ -233,7 +235,9 @@ la_status la_prefill_backward_workspace_size(const la_desc* desc, size_t* bytes)
  * desc->igate; dS0, dz0 are dL/dS0', dL/dz0' (the stabiliser's own gradient
  * is <dS0', S0'> + <dz0', z0'>).  The state is carried scaled by the
  * forward's stabiliser throughout, so no intermediate overflows where the
- * forward's does not.  Per-token path only.
+ * forward's does not: both paths take the recurrence with alpha'_t =
+ * e^{log f_t + m_{t-1} - m_t} and beta'_t = e^{itilde_t - m_t} as decay and
+ * key weight, and no gate gradient divides by a decay.
  * The decay gradient is formed through log a_t (a suffix sum of
  * <phi(q_t), dphi(q_t)> - <phi(k_t), dphi(k_t)>, divided by a_t); where a
  * decay or gate value is below 1/256 (0, a full reset, included) it is
@@ -245,8 +249,9 @@ la_status la_prefill_backward_workspace_size(const la_desc* desc, size_t* bytes)
  * LA_GATE_RFA or LA_GATE_MLSTM, every read-out form, the widths the
  * per-token kernel takes (LA_EUNSUPPORTED otherwise: RFF, the non-causal
  * form).
- * Two paths.  Chunked (bf16 inputs, elu+1, no decay, the SSD decay or the
- * RFA gate, d' = d_v in {64, 128}, T > 0): the same gradients written as
+ * Two paths.  Chunked (bf16 inputs, elu+1 with no decay, the SSD decay or
+ * the RFA gate, or identity features with the mLSTM gates; d' = d_v in
+ * {64, 128}, T > 0): the same gradients written as
  * masked-quadratic sums inside 32-token chunks and states across them, as
  * the forward ([lesson] "Implementation reality"): the prefill's segment
  * start states, a pass in token order (dq and each segment's gradient state

@@ -217,10 +217,20 @@ def test_backward_checks():
     d.phi, d.rff_D, d.rff_W = _lib.LA_PHI_RFF, 32, FAKE
     assert bw(d) == "LA_EUNSUPPORTED"
     assert bw(desc(causal=False, **base)) == "LA_EUNSUPPORTED"
-    # the mLSTM gates: the per-token path, B H T (d_v + 4) floats (alpha', beta'
-    # per token beside the read-out's terms); ddecay (both gates' gradients)
-    # required
+    # the mLSTM gates, bf16: the chunked path, as above plus a zero start
+    # stabiliser per head, each segment's log-decay, four floats per token
+    # (the decay gradient's terms, log alpha' and beta') and the tile totals;
+    # ddecay (both gates' gradients) required
     d = desc(phi="identity", **base)
+    d.decay_kind, d.decay, d.igate, d.stab = _lib.LA_GATE_MLSTM, FAKE, FAKE, FAKE
+    assert status(L.la_prefill_backward_workspace_size(ctypes.byref(d), ctypes.byref(n))) == "LA_OK"
+    assert n.value == (r(fwd) + r(BH * 64 * 64 * 4) + r(BH * 64 * 4) + r(BH * 4) + r(BH * 5 * E * 4)
+                       + r(BH * 300 * 8) + r(BH * 5 * 4) + 2 * r(BH * 300 * 4) + r(BH * 1 * 4)
+                       + r(BH * 300 * 8))
+    assert bw(d) == "LA_EINVAL"
+    # fp32 inputs: the per-token path, B H T (d_v + 4) floats (alpha', beta'
+    # per token beside the read-out's terms)
+    d = desc(phi="identity", T=300, d_h=64, d_v=64, dtype_code=_lib.LA_F32)
     d.decay_kind, d.decay, d.igate, d.stab = _lib.LA_GATE_MLSTM, FAKE, FAKE, FAKE
     assert status(L.la_prefill_backward_workspace_size(ctypes.byref(d), ctypes.byref(n))) == "LA_OK"
     assert n.value == 8 * 300 * (64 + 4) * 4

@@ -364,13 +364,13 @@ def _mlstm_case(B, H, T, d, dv, dtype, seed, ishift=0.0, fexp=False, positive=Fa
     return x
 
 
-def _mlstm_run(x, do, dev, normalize, fexp, state):
+def _mlstm_run(x, do, dev, normalize, fexp, state, segments=0):
     g = lambda t: None if t is None else t.to(dev)
     st = None if state is None else tuple(torch.as_tensor(s, dtype=torch.float32, device=dev)
                                           for s in state)
     out = la.prefill_backward(g(x.q), g(x.k), g(x.v), g(do), phi="identity", igate=g(x.igate),
                               fgate=g(x.fgate), fgate_exp=fexp, state=st, normalize=normalize,
-                              state_grad=True)
+                              state_grad=True, segments=segments)
     torch.cuda.synchronize()
     return {k: v.cpu().double().numpy() for k, v in out.items()}
 
@@ -425,3 +425,68 @@ def test_backward_mlstm_bf16_vs_oracle(d):
     got = _mlstm_run(x, do, dev, "max1", False, None)
     ref = O.mlstm_gradients(x.q, x.k, x.v, do, x.igate, x.fgate, False, 1e-6, normalize="max1")
     compare(got, {k: ref[k] for k in got}, TOL["bf16"], ("mlstm bf16", d))
+
+
+# The chunked path with the mLSTM gates (bf16, identity features, d 64/128):
+# (d, T, segments, read-out, exponential forget gate, carried-in state,
+# input-gate shift).  The sum read-out takes positive features and z0, so
+# that q.z stays away from 0; so do input gates shifted up: the max1 floor
+# e^{-m} then sits far below |q.z|, every output is q.S / |q.z|, and signed
+# features put q.z near 0 for some tokens, whose gradients (about 100 times
+# the rms at +4) no fp32 arithmetic resolves (the per-token kernel misses
+# the oracle there by as much as the chunked passes).
+MLSTM_CHUNKED = [
+    (64, 333, 0, "max1", False, False, 0.0),
+    (64, 333, 3, "max1", True, True, 0.0),
+    (128, 257, 1, "max1", False, True, 0.0),
+    (128, 640, 0, "max1", False, False, 4.0),
+    (64, 200, 2, True, False, True, 0.0),
+    (128, 161, 0, False, True, False, 0.0),
+    (64, 95, 5, "max1", False, True, 25.0),
+    (128, 31, 0, "max1", True, True, 0.0),
+]
+
+
+@pytest.mark.parametrize("d,T,segments,normalize,fexp,with_state,ishift", MLSTM_CHUNKED)
+def test_backward_mlstm_chunked_vs_oracle(d, T, segments, normalize, fexp, with_state, ishift):
+    """bf16 inputs with the mLSTM gates take the chunked passes: the
+    stabiliser rebuilt per chunk from each segment's start (the prefill's
+    scan), alpha' and beta' as decay and key weight, the gates' gradients
+    from the suffix sums.  Every gradient against the oracle's."""
+    dev = gpu_device()
+    B, H = 2, 2
+    positive = normalize is True or ishift > 0
+    x = _mlstm_case(B, H, T, d, d, "bf16", seed=T + d, ishift=ishift, fexp=fexp,
+                    positive=positive)
+    do = torch.randn(B, H, T, d, generator=torch.Generator().manual_seed(T)).to(torch.bfloat16)
+    state = None
+    if with_state:
+        rng = np.random.default_rng(d + T)
+        z0 = rng.standard_normal((B, H, d)) * 0.3
+        S0 = rng.standard_normal((B, H, d, d)) * 0.3
+        state = (np.abs(S0) if positive else S0, np.abs(z0) if positive else z0,
+                 ishift + rng.standard_normal((B, H)))
+    got = _mlstm_run(x, do, dev, normalize, fexp, state, segments)
+    S0, z0, m0 = (None, None, None) if state is None else state
+    ref = O.mlstm_gradients(x.q, x.k, x.v, do, x.igate, x.fgate, fexp, 1e-6, S0, z0, m0, normalize)
+    compare(got, {k: ref[k] for k in got}, TOL["bf16"],
+            ("mlstm chunked", d, T, segments, normalize, fexp, with_state, ishift))
+
+
+def test_backward_mlstm_chunked_equals_per_token_on_the_same_values():
+    """The chunked passes (bf16 inputs) and the per-token kernel (the same
+    values as fp32 inputs) compute the same gradients: 8 segments of a
+    4096-token sequence at d = 128, with a carried-in state."""
+    dev = gpu_device()
+    B, H, T, d = 1, 2, 4096, 128
+    x = _mlstm_case(B, H, T, d, d, "bf16", seed=41)
+    do = torch.randn(B, H, T, d, generator=torch.Generator().manual_seed(42)).to(torch.bfloat16)
+    rng = np.random.default_rng(43)
+    state = (rng.standard_normal((B, H, d, d)) * 0.3, rng.standard_normal((B, H, d)) * 0.3,
+             rng.standard_normal((B, H)))
+    got = _mlstm_run(x, do, dev, "max1", False, state, segments=8)
+    x32 = _mlstm_case(B, H, T, d, d, "bf16", seed=41)
+    for n in ("q", "k", "v"):
+        setattr(x32, n, getattr(x32, n).float())
+    ref = _mlstm_run(x32, do.float(), dev, "max1", False, state)
+    compare(got, ref, TOL["bf16"], "mlstm chunked vs per-token")
