@@ -43,7 +43,8 @@ Printed as one JSON line:
                T=8192 d=128 with its decay: the chunked path (segment start states
                from the prefill's stages 1 and 2, a pass in token order for
                dq, a reverse scan of the segments' gradient states, a pass
-               in reverse order for dk and dv); algorithmic bytes are q, k,
+               in reverse order for dk and dv), and on the mLSTM prefill
+               above (dL/dfgate and dL/digate too); algorithmic bytes are q, k,
                v, dout read once (bf16) and dq, dk, dv written once (fp32);
   configs      the other prefill workloads, forward: the elu+1 prefill
                (B=4 H=8 T=2048 d=64) and the SSD-decay prefill (B=2 H=16
@@ -287,26 +288,35 @@ def bench_prefill(torch, la, I, steps, warmup, normalize=True, stages=True, caus
 
 
 def bench_backward(torch, la, I, B, H, T, d, reps, decay=None, scale=PF["scale"]):
-    """ms per la_prefill_backward call (elu+1, bf16 inputs and dout; no decay,
-    or the SSD decay a = sigmoid(N(3, 1)))."""
+    """ms per la_prefill_backward call (bf16 inputs and dout): elu+1 with no
+    decay or the SSD decay a = sigmoid(N(3, 1)); or decay="mlstm", identity
+    features with the mLSTM gates (the prefill's mLSTM workload) and the
+    max(|q.z|, 1) read-out."""
     dev = torch.device("cuda:0")
     x = I.prefill_inputs(B, H, T, d, dtype="bf16", seed=0, scale=scale, device=dev,
                          decay=decay)
     g = torch.Generator(device=dev)
     g.manual_seed(1)
     do = torch.randn(B, H, T, d, generator=g, device=dev).to(torch.bfloat16)
-    desc = la.make_desc(B, H, T, d, d, la._lib.LA_BF16, decay=x.decay)
+    if decay == "mlstm":
+        stab = torch.zeros(B, H, dtype=torch.float32, device=dev)
+        desc = la.make_desc(B, H, T, d, d, la._lib.LA_BF16, phi="identity", normalize="max1",
+                            igate=x.igate, fgate=x.fgate, stab=stab)
+        kw = dict(phi="identity", normalize="max1", igate=x.igate, fgate=x.fgate)
+    else:
+        desc = la.make_desc(B, H, T, d, d, la._lib.LA_BF16, decay=x.decay)
+        kw = dict(decay=x.decay)
     n = ctypes.c_size_t(0)
     la._lib.check(la._lib.lib().la_prefill_backward_workspace_size(ctypes.byref(desc),
                                                                    ctypes.byref(n)))
     ws = torch.empty(max(int(n.value), 1), dtype=torch.uint8, device=dev)
     for _ in range(3):                                 # warm-up
-        la.prefill_backward(x.q, x.k, x.v, do, decay=x.decay, workspace=ws)
+        la.prefill_backward(x.q, x.k, x.v, do, workspace=ws, **kw)
     torch.cuda.synchronize()
     e0, e1 = _events(torch)
     e0.record()
     for _ in range(reps):
-        la.prefill_backward(x.q, x.k, x.v, do, decay=x.decay, workspace=ws)
+        la.prefill_backward(x.q, x.k, x.v, do, workspace=ws, **kw)
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
@@ -621,6 +631,7 @@ def main(argv=None):
         bw_long = bench_backward(torch, la, I, B, H, T, d, 20)
         bw_small = bench_backward(torch, la, I, 4, 8, 2048, 64, 50)
         bw_ssd = bench_backward(torch, la, I, 2, 16, 8192, 128, 20, decay="ssd", scale=1.0)
+        bw_ml = bench_backward(torch, la, I, B, H, T, d, 20, decay="mlstm")
         extras = True
     if not a.no_decode and not a.prefill_only:
         print(f"[bench] decode {DEC['N']} x {DEC['H']}, {DEC['steps']} steps", file=sys.stderr,
@@ -702,7 +713,10 @@ def main(argv=None):
                                       "GBs": bw_small["GBs"]},
                 "ssd_prefill_shape": {"B": 2, "H": 16, "T": 8192, "d": 128, "decay": "ssd",
                                       "ms": bw_ssd["ms"], "tokens_per_s": bw_ssd["tokens_per_s"],
-                                      "GBs": bw_ssd["GBs"]}},
+                                      "GBs": bw_ssd["GBs"]},
+                "mlstm_long_context": {"B": B, "H": H, "T": T, "d": d, "gates": "mlstm",
+                                       "ms": bw_ml["ms"], "tokens_per_s": bw_ml["tokens_per_s"],
+                                       "GBs": bw_ml["GBs"]}},
         })
     if dec is not None:
         res["decode"] = {
