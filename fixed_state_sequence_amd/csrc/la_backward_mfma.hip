@@ -938,43 +938,41 @@ __device__ __forceinline__ u32x4 row_operand_perm(const char* tile, int r, int k
 // and the decay value of token lane % 32.
 struct Raw2 {
   u32x4 q, k, v;
-  f32x4 d[2];    // dout as fp32
+  u32x4 d[2];    // dout as loaded: 8 fp32 (both words) or 8 bf16 (the first)
   float2 th;     // r_t and h_t (from pass A)
   float2 al;     // alpha (mLSTM: log alpha' and beta', from pass A)
 };
 
-template <int D, int DECAY>
+template <int D, int DECAY, bool DF32>
 __device__ __forceinline__ void load_raw2(const BwArgs& a, int64_t bh, int t0, int tid, Raw2& x) {
   constexpr int BPR = D / 8;
   const int r = tid / BPR, b = tid % BPR;
-  const int64_t T = a.T;
-  const int64_t t = min(int64_t(t0 + r), T - 1);
-  const int64_t row = (bh * T + t) * D + 8 * b;
-  x.th = *reinterpret_cast<const float2*>(a.tok + (bh * T + t) * 2);
-  x.q = *reinterpret_cast<const u32x4*>(a.q + row);
-  x.k = *reinterpret_cast<const u32x4*>(a.k + row);
-  x.v = *reinterpret_cast<const u32x4*>(a.v + row);
-  if (a.dout_f32) {
-    const float* dp = static_cast<const float*>(a.dout) + row;
-    x.d[0] = *reinterpret_cast<const f32x4*>(dp);
-    x.d[1] = *reinterpret_cast<const f32x4*>(dp + 4);
+  // the chunk's first token (uniform), and 32-bit offsets within the chunk
+  // (rows past the end read the last token)
+  const int64_t tc = bh * int64_t(a.T) + t0;
+  const uint32_t tr = uint32_t(min(t0 + r, a.T - 1) - t0);
+  const uint32_t off = tr * D + 8 * b;
+  x.th = reinterpret_cast<const float2*>(a.tok + tc * 2)[tr];
+  x.q = *reinterpret_cast<const u32x4*>(a.q + tc * D + off);
+  x.k = *reinterpret_cast<const u32x4*>(a.k + tc * D + off);
+  x.v = *reinterpret_cast<const u32x4*>(a.v + tc * D + off);
+  if constexpr (DF32) {
+    const float* dp = static_cast<const float*>(a.dout) + tc * D + off;
+    x.d[0] = *reinterpret_cast<const u32x4*>(dp);
+    x.d[1] = *reinterpret_cast<const u32x4*>(dp + 4);
   } else {
-    const u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const bf16_t*>(a.dout) + row);
-    float f[8];
-    unpack8(w, f, bf16_t{});
-    x.d[0] = f32x4{f[0], f[1], f[2], f[3]};
-    x.d[1] = f32x4{f[4], f[5], f[6], f[7]};
+    x.d[0] = *reinterpret_cast<const u32x4*>(static_cast<const bf16_t*>(a.dout) + tc * D + off);
   }
   x.al = make_float2(1.f, 1.f);
-  const int64_t ta = bh * T + min(int64_t(t0 + (tid & 31)), T - 1);
-  if constexpr (DECAY == 3) x.al = *reinterpret_cast<const float2*>(a.ab + ta * 2);
-  else if constexpr (DECAY != 0) x.al.x = a.decay[ta];
+  const uint32_t ta = uint32_t(min(t0 + (tid & 31), a.T - 1) - t0);
+  if constexpr (DECAY == 3) x.al = reinterpret_cast<const float2*>(a.ab + tc * 2)[ta];
+  else if constexpr (DECAY != 0) x.al.x = (a.decay + tc)[ta];
 }
 
 // Stage one chunk into buffer buf: phi(q) (high, low), phi(k) (high, low, at
 // permuted feature positions), v, g = r_t dout (high, low; with a decay also
 // e^{l_t} g), and the per-token scalars.  Rows past the end are zero.
-template <int D, int DECAY>
+template <int D, int DECAY, bool DF32>
 __device__ __forceinline__ void stage2(const BwArgs& a, int t0, int tid, const Raw2& x, char* buf) {
   using L = BL2<D, DECAY>;
   float* F = reinterpret_cast<float*>(buf + L::FB);
@@ -1021,8 +1019,18 @@ __device__ __forceinline__ void stage2(const BwArgs& a, int t0, int tid, const R
   row_write_perm<D>(buf + L::KL, pr, b, low8(fk, kh));
   blk_write<D>(buf + L::V, pr, b, valid ? x.v : u32x4{0u, 0u, 0u, 0u});
   const float rt = valid ? x.th.x : 0.f, ht = valid ? x.th.y : 0.f;
-  float gv[8] = {x.d[0][0] * rt, x.d[0][1] * rt, x.d[0][2] * rt, x.d[0][3] * rt,
-                 x.d[1][0] * rt, x.d[1][1] * rt, x.d[1][2] * rt, x.d[1][3] * rt};
+  float gv[8];
+  if constexpr (DF32) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      gv[e] = __uint_as_float(x.d[0][e]);
+      gv[e + 4] = __uint_as_float(x.d[1][e]);
+    }
+  } else {
+    unpack8(x.d[0], gv, bf16_t{});
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) gv[e] *= rt;
   const u32x4 gh = pack8(gv);
   blk_write<D>(buf + L::GH, pr, b, gh);
   blk_write<D>(buf + L::GL, pr, b, low8(gv, gh));
@@ -1058,7 +1066,7 @@ __device__ __forceinline__ void causal_weights(const float* F, int LAMOFF, int g
   }
 }
 
-template <int D, int DECAY>
+template <int D, int DECAY, bool DF32>
 __global__ __launch_bounds__(128 * (D / 32)) void bwd_pass_b2(const BwArgs a) {
   using L = BL2<D, DECAY>;
   constexpr int NJ = L::NJ, KS = D / 16;
@@ -1091,18 +1099,15 @@ __global__ __launch_bounds__(128 * (D / 32)) void bwd_pass_b2(const BwArgs a) {
   }
 
   Raw2 raw;
-  load_raw2<D, DECAY>(a, bh, (c1 - 1) * BCH, tid, raw);
-  stage2<D, DECAY>(a, (c1 - 1) * BCH, tid, raw, smem);
-  if (c1 - 2 >= c0) load_raw2<D, DECAY>(a, bh, (c1 - 2) * BCH, tid, raw);
+  load_raw2<D, DECAY, DF32>(a, bh, (c1 - 1) * BCH, tid, raw);
+  stage2<D, DECAY, DF32>(a, (c1 - 1) * BCH, tid, raw, smem);
+  if (c1 - 2 >= c0) load_raw2<D, DECAY, DF32>(a, bh, (c1 - 2) * BCH, tid, raw);
   __syncthreads();
 
   // one loop per kind of wave (each keeps only its own loop-invariant
   // addresses live), the same barriers in both
   auto chunk = [&](int c, auto value_kind) {
     constexpr bool VW = decltype(value_kind)::value;
-    int tid_ = tid;
-    asm volatile("" : "+v"(tid_));
-    const int tid = tid_, lane = tid_ & 63, g = lane >> 5, n = lane & 31;
     const int t0 = c * BCH;
     const char* cur = smem + ((c1 - 1 - c) & 1) * L::BUF;
     char* nxt = smem + ((c1 - c) & 1) * L::BUF;
@@ -1112,8 +1117,13 @@ __global__ __launch_bounds__(128 * (D / 32)) void bwd_pass_b2(const BwArgs a) {
     // inputs in flight: feature waves before their products, value waves after
     auto stage_next = [&]() {
       if (more) {
-        stage2<D, DECAY>(a, t0 - BCH, tid, raw, nxt);
-        if (c - 2 >= c0) load_raw2<D, DECAY>(a, bh, t0 - 2 * BCH, tid, raw);
+        // the staging addresses are recomputed from an opaque copy of the
+        // thread index: held across the loop with the products' addresses,
+        // they would not fit the registers of two waves per SIMD
+        int ts = tid;
+        asm volatile("" : "+v"(ts));
+        stage2<D, DECAY, DF32>(a, t0 - BCH, ts, raw, nxt);
+        if (c - 2 >= c0) load_raw2<D, DECAY, DF32>(a, bh, t0 - 2 * BCH, ts, raw);
       }
     };
     const bool vs = t0 + n < T;
@@ -1181,7 +1191,7 @@ __global__ __launch_bounds__(128 * (D / 32)) void bwd_pass_b2(const BwArgs a) {
         dvt = mfma(oglt[ks], ah[ks], dvt);
       }
       if (vs) {
-        float* dst = a.dv + (bh * T + t0 + n) * D + 32 * wb + 4 * g;
+        float* dst = a.dv + (bh * T + t0) * D + uint32_t(n * D + 32 * wb + 4 * g);
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           *reinterpret_cast<f32x4*>(dst + 8 * r) =
@@ -1273,7 +1283,7 @@ __global__ __launch_bounds__(128 * (D / 32)) void bwd_pass_b2(const BwArgs a) {
       float* gzl = reinterpret_cast<float*>(smem + L::GZ);
       {
         float kdp = 0.f;   // <phi(k_s), dphi(k_s)> / beta_s over this lane's features
-        const int64_t row = (bh * T + t0 + n) * D + 32 * wb + 4 * g;
+        float* dst = a.dk + (bh * T + t0) * D + uint32_t(n * D + 32 * wb + 4 * g);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int pc = perm_pos(32 * wb + 8 * r + 4 * g);   // stored column of these 4 features
@@ -1287,7 +1297,7 @@ __global__ __launch_bounds__(128 * (D / 32)) void bwd_pass_b2(const BwArgs a) {
             o4[e] = DECAY == 3 ? bet * raw_ : bet * raw_ * fminf(p4[e], 1.f);
             kdp += p4[e] * raw_;
           }
-          if (vs) *reinterpret_cast<f32x4*>(a.dk + row + 8 * r) = o4;
+          if (vs) *reinterpret_cast<f32x4*>(dst + 8 * r) = o4;
         }
         if constexpr (DECAY != 0) {
           kdp = swap_sum32(kdp);
@@ -1468,7 +1478,8 @@ hipError_t launch_d(const Problem& pb, const BwArgs& a, float* dS0, float* dz0, 
   constexpr int PER = (D * D + D + 255) / 256;
   bwd_rscan<D, DECAY != 0><<<dim3(unsigned(pb.BH() * PER)), dim3(256), 0, st>>>(
       a.gslot, a.lgam, a.nseg, dS0, dz0);
-  bwd_pass_b2<D, DECAY><<<dim3(nwg), dim3(128 * (D / 32)), 0, st>>>(a);
+  if (a.dout_f32) bwd_pass_b2<D, DECAY, true><<<dim3(nwg), dim3(128 * (D / 32)), 0, st>>>(a);
+  else bwd_pass_b2<D, DECAY, false><<<dim3(nwg), dim3(128 * (D / 32)), 0, st>>>(a);
   if constexpr (DECAY != 0) {
     const int ntile = (a.T + DG_TILE - 1) / DG_TILE;
     const unsigned nb = unsigned(pb.BH() * ntile);
