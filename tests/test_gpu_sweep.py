@@ -1,7 +1,8 @@
 """Seeded random sweeps of the GPU path against the fp64 oracle: shapes,
 chunk lengths, segment counts, decay kinds and strengths, read-outs, output
 types and carried-in states drawn together, so that combinations no
-hand-written case names are covered too.  Every case prints its draw before
+hand-written case names are covered too (forward, mLSTM forward, gradients
+with and without the mLSTM gates, decode).  Every case prints its draw before
 it runs.  Bars as everywhere: max |gpu - oracle| / rms(oracle) < 2e-2 for
 bf16 inputs (16-bit outputs: after half an ulp of the oracle per element).
 """
@@ -213,3 +214,60 @@ def test_decode_sweep(case):
     e = (worst, rel_err(S, S_ref), rel_err(z, z_ref))
     print("errors", e)
     assert max(e) < TOL[c["dtype"]], (c, e)
+
+
+def _mlstm_backward_cases(n, seed):
+    """Gradients with the mLSTM gates, bf16 inputs (the chunked passes).  The
+    sum read-out, and input gates shifted up (where the max1 floor e^{-m}
+    falls far below |q.z|), take positive features and start states, which
+    keep q.z away from 0; short sum read-out draws carry a state, as in the
+    gradient sweep above."""
+    r = random.Random(seed)
+    for i in range(n):
+        c = dict(i=i, B=r.choice([1, 2]), H=r.choice([1, 2, 3]),
+                 T=r.choice([1, 31, 33, 96, 257, r.randint(1, 600), r.randint(1, 600)]),
+                 d=r.choice([64, 128]), segments=r.choice([0, 1, 2, 3, 5]),
+                 fmean=r.choice([0.0, 3.0, 6.0]), ishift=r.choice([0.0, 0.0, 3.0]),
+                 fexp=r.random() < 0.3, normalize=r.choice(["max1", "max1", True, False]),
+                 state=r.random() < 0.5, seed=5000 + i)
+        if c["normalize"] is True and c["T"] < 16:
+            c["state"] = True   # as in the gradient sweep above: the first tokens' O(eps) terms
+        yield c
+
+
+@pytest.mark.parametrize("case", list(_mlstm_backward_cases(16, 19)), ids=lambda c: f"mb{c['i']}")
+def test_mlstm_backward_sweep(case):
+    dev = gpu_device()
+    c = case
+    print(c, flush=True)
+    B, H, T, d = c["B"], c["H"], c["T"], c["d"]
+    positive = c["normalize"] is True or c["ishift"] > 0
+    x = I.prefill_inputs(B, H, T, d, dtype="bf16", seed=c["seed"], decay="mlstm",
+                         decay_mean=c["fmean"], scale=0.7)
+    x.igate = x.igate + c["ishift"]
+    if positive:
+        x.q, x.k = x.q.abs(), x.k.abs()
+    if c["fexp"]:
+        x.fgate = -torch.nn.functional.softplus(-x.fgate)   # log sigmoid: the exp form's input
+    do = torch.randn(B, H, T, d, generator=torch.Generator().manual_seed(c["seed"] + 1))
+    do = do.to(torch.bfloat16)
+    st = S0 = z0 = m0 = None
+    if c["state"]:
+        rng = np.random.default_rng(c["seed"])
+        S0 = rng.standard_normal((B, H, d, d)) * 0.3
+        z0 = rng.standard_normal((B, H, d)) * 0.3
+        if positive:
+            S0, z0 = np.abs(S0), np.abs(z0)
+        m0 = c["ishift"] + rng.standard_normal((B, H))
+        st = tuple(torch.tensor(a, dtype=torch.float32, device=dev) for a in (S0, z0, m0))
+        S0, z0, m0 = (t.cpu().double().numpy() for t in st)
+    g = lambda t: None if t is None else t.to(dev)
+    got = la.prefill_backward(g(x.q), g(x.k), g(x.v), g(do), phi="identity", igate=g(x.igate),
+                              fgate=g(x.fgate), fgate_exp=c["fexp"], state=st,
+                              normalize=c["normalize"], state_grad=True, segments=c["segments"])
+    torch.cuda.synchronize()
+    ref = O.mlstm_gradients(x.q, x.k, x.v, do, x.igate, x.fgate, c["fexp"], 1e-6, S0, z0, m0,
+                            c["normalize"])
+    errs = {k: rel_err(got[k], ref[k]) for k in got}
+    print("errors", errs)
+    assert max(errs.values()) < TOL["bf16"], (c, errs)
