@@ -192,29 +192,40 @@ __device__ __forceinline__ void write_state_tile(char* sb, char* sbl, const f32x
 }
 
 // Four features at byte offset `off` of a token row of a high/low tile pair,
-// as fp32 (high + low carry phi to about 2^-16).
+// as fp32 (high + low carry phi to about 2^-16).  EX: the high parts are
+// exact (bf16 inputs under identity features), the low tile is not read.
+template <bool EX = false>
 __device__ __forceinline__ f32x4 hilo4(const char* hi, const char* lo, int off) {
   const u32x2 h = *reinterpret_cast<const u32x2*>(hi + off);
-  const u32x2 l = *reinterpret_cast<const u32x2*>(lo + off);
   f32x4 r;
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
-    r[2 * e] = __uint_as_float(h[e] << 16) + __uint_as_float(l[e] << 16);
-    r[2 * e + 1] = __uint_as_float(h[e] & 0xffff0000u) + __uint_as_float(l[e] & 0xffff0000u);
+    r[2 * e] = __uint_as_float(h[e] << 16);
+    r[2 * e + 1] = __uint_as_float(h[e] & 0xffff0000u);
+  }
+  if constexpr (!EX) {
+    const u32x2 l = *reinterpret_cast<const u32x2*>(lo + off);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      r[2 * e] += __uint_as_float(l[e] << 16);
+      r[2 * e + 1] += __uint_as_float(l[e] & 0xffff0000u);
+    }
   }
   return r;
 }
 
 // Features 8 b .. 8 b + 7 of tile row `row` (already permuted) of a
-// high/low tile pair, as fp32.
-template <int D>
+// high/low tile pair, as fp32 (EX as in hilo4).
+template <int D, bool EX = false>
 __device__ __forceinline__ void hilo8(const char* hi, const char* lo, int row, int b, float (&x)[8]) {
   const int off = tile_off<D>(row, b);
-  float h[8], l[8];
-  unpack8(*reinterpret_cast<const u32x4*>(hi + off), h, bf16_t{});
-  unpack8(*reinterpret_cast<const u32x4*>(lo + off), l, bf16_t{});
+  unpack8(*reinterpret_cast<const u32x4*>(hi + off), x, bf16_t{});
+  if constexpr (!EX) {
+    float l[8];
+    unpack8(*reinterpret_cast<const u32x4*>(lo + off), l, bf16_t{});
 #pragma unroll
-  for (int e = 0; e < 8; ++e) x[e] = h[e] + l[e];
+    for (int e = 0; e < 8; ++e) x[e] += l[e];
+  }
 }
 
 // The MFMA operands of one product, read together before its MFMAs are
@@ -399,12 +410,13 @@ __device__ __forceinline__ void stage(const BwArgs& a, int64_t bh, int t0, int t
       fq[e] = valid ? (DECAY == 3 ? fq[e] : elu1_fast(fq[e])) : 0.f;
       fk[e] = valid ? (DECAY == 3 ? fk[e] : elu1_fast(fk[e])) : 0.f;
     }
+    // identity features of bf16 inputs (mLSTM) are exact in bf16: no low parts
     const u32x4 qh = pack8(fq);
     blk_write<D>(smem + L::Q, pr, b, qh);
-    blk_write<D>(smem + L::QL, pr, b, low8(fq, qh));
+    if constexpr (DECAY != 3) blk_write<D>(smem + L::QL, pr, b, low8(fq, qh));
     const u32x4 kh = pack8(fk);
     blk_write<D>(smem + L::K, pr, b, kh);
-    blk_write<D>(smem + L::KL, pr, b, low8(fk, kh));
+    if constexpr (DECAY != 3) blk_write<D>(smem + L::KL, pr, b, low8(fk, kh));
     blk_write<D>(smem + L::V, pr, b, valid ? x.v[rr] : u32x4{0u, 0u, 0u, 0u});
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
     const f32x4 d0 = valid ? x.d[rr][0] : zero4, d1 = valid ? x.d[rr][1] : zero4;
@@ -430,6 +442,9 @@ template <int D, int DECAY>
 __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_a(const BwArgs a) {
   using L = BL<D, DECAY>;
   constexpr int NJ = L::NJ;
+  // identity features of bf16 inputs (the mLSTM gates) are exact in bf16:
+  // their low parts are zero, and the products with them are skipped
+  constexpr bool XQ = DECAY == 3;
   __shared__ __align__(16) char smem[L::LDS];
   float* F = reinterpret_cast<float*>(smem + L::F);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, n = lane & 31;
@@ -503,15 +518,19 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_a(const BwArgs a) {
 #pragma unroll
       for (int kk = 0; kk < KB; ++kk) {
         oq[k0 + kk] = row_operand<D>(smem + L::Q, perm_pos(n), 2 * (k0 + kk) + g);
-        oql[k0 + kk] = row_operand<D>(smem + L::QL, perm_pos(n), 2 * (k0 + kk) + g);
         ok[kk] = row_operand<D>(smem + L::K, perm_pos(n), 2 * (k0 + kk) + g);
-        okl[kk] = row_operand<D>(smem + L::KL, perm_pos(n), 2 * (k0 + kk) + g);
+        if constexpr (!XQ) {
+          oql[k0 + kk] = row_operand<D>(smem + L::QL, perm_pos(n), 2 * (k0 + kk) + g);
+          okl[kk] = row_operand<D>(smem + L::KL, perm_pos(n), 2 * (k0 + kk) + g);
+        }
       }
 #pragma unroll
       for (int kk = 0; kk < KB; ++kk) {
         sc = mfma(ok[kk], oq[k0 + kk], sc);
-        sc = mfma(okl[kk], oq[k0 + kk], sc);
-        sc = mfma(ok[kk], oql[k0 + kk], sc);
+        if constexpr (!XQ) {
+          sc = mfma(okl[kk], oq[k0 + kk], sc);
+          sc = mfma(ok[kk], oql[k0 + kk], sc);
+        }
       }
     }
     // the numerator's state and v operands, read while the scores finish
@@ -551,7 +570,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_a(const BwArgs a) {
         for (int kk = 0; kk < KB; ++kk) {
           const int fs = k0 + kk;
           oq[fs] = row_operand<D>(smem + L::Q, perm_pos(n), 2 * fs + g);
-          oql[fs] = row_operand<D>(smem + L::QL, perm_pos(n), 2 * fs + g);
+          if constexpr (!XQ) oql[fs] = row_operand<D>(smem + L::QL, perm_pos(n), 2 * fs + g);
           os[fs] = tr_operand<D>(smem + L::SB, 16 * fs, 32 * w, lane);
           osl[fs] = tr_operand<D>(smem + L::SBL, 16 * fs, 32 * w, lane);
         }
@@ -561,7 +580,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_a(const BwArgs a) {
         const int fs = k0 + kk;
         nu = mfma(os[fs], oq[fs], nu);
         nu = mfma(osl[fs], oq[fs], nu);
-        nu = mfma(os[fs], oql[fs], nu);
+        if constexpr (!XQ) nu = mfma(os[fs], oql[fs], nu);
       }
     }
     if constexpr (DECAY != 0) nu *= eq;
@@ -642,7 +661,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_a(const BwArgs a) {
       row_ops<D>(smem + L::SB, 32 * w + n, g, osr);
       row_ops<D>(smem + L::SBL, 32 * w + n, g, oslr);
       tr_ops<D, 2>(smem + L::K, 32 * w, lane, okt);
-      tr_ops<D, 2>(smem + L::KL, 32 * w, lane, oklt);
+      if constexpr (!XQ) tr_ops<D, 2>(smem + L::KL, 32 * w, lane, oklt);
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) bs[i] = (bs[i] + h) * weight(i);
@@ -650,7 +669,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_a(const BwArgs a) {
     split_acc(bs, bh_, bl_);
     if constexpr (!EARLY) {
       tr_ops<D, 2>(smem + L::K, 32 * w, lane, okt);
-      tr_ops<D, 2>(smem + L::KL, 32 * w, lane, oklt);
+      if constexpr (!XQ) tr_ops<D, 2>(smem + L::KL, 32 * w, lane, oklt);
     }
 
     // dphi(q)^T (rows f of block w, columns t): e^{l_t} (S g + z h) +
@@ -682,7 +701,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_a(const BwArgs a) {
     for (int ks = 0; ks < 2; ++ks) {
       dqt = mfma(okt[ks], bh_[ks], dqt);
       dqt = mfma(okt[ks], bl_[ks], dqt);
-      dqt = mfma(oklt[ks], bh_[ks], dqt);
+      if constexpr (!XQ) dqt = mfma(oklt[ks], bh_[ks], dqt);
     }
     {
       float qdp = 0.f;   // <phi(q_t), dphi(q_t)> over this lane's features
@@ -690,7 +709,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_a(const BwArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int off = tile_off<D>(perm_pos(n), 4 * w + r) + 8 * g;
-        const f32x4 p4 = hilo4(smem + L::Q, smem + L::QL, off);
+        const f32x4 p4 = hilo4<XQ>(smem + L::Q, smem + L::QL, off);
         const f32x4 z4 = *reinterpret_cast<const f32x4*>(F + L::Z + 32 * w + 4 * g + 8 * r);
         f32x4 o4;
 #pragma unroll
@@ -725,7 +744,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_a(const BwArgs a) {
 #pragma unroll
         for (int f = 0; f < FB; ++f) {
           tr_ops<D, 2>(smem + L::Q, 32 * (f0 + f), lane, bq[f]);
-          tr_ops<D, 2>(smem + L::QL, 32 * (f0 + f), lane, bql[f]);
+          if constexpr (!XQ) tr_ops<D, 2>(smem + L::QL, 32 * (f0 + f), lane, bql[f]);
         }
 #pragma unroll
         for (int f = 0; f < FB; ++f)
@@ -733,7 +752,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_a(const BwArgs a) {
           for (int ks = 0; ks < 2; ++ks) {
             Gs[f0 + f] = mfma(ag[ks], bq[f][ks], Gs[f0 + f]);
             Gs[f0 + f] = mfma(agl[ks], bq[f][ks], Gs[f0 + f]);
-            Gs[f0 + f] = mfma(ag[ks], bql[f][ks], Gs[f0 + f]);
+            if constexpr (!XQ) Gs[f0 + f] = mfma(ag[ks], bql[f][ks], Gs[f0 + f]);
           }
       }
     }
@@ -763,7 +782,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_a(const BwArgs a) {
         const int r = tid / L::BPR + 16 * rr;
         const float wk = F[L::BET + r] * __expf(tot - F[L::LAM + r]);
         float x[8];
-        hilo8<D>(smem + L::K, smem + L::KL, perm_pos(r), b, x);
+        hilo8<D, XQ>(smem + L::K, smem + L::KL, perm_pos(r), b, x);
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[e] *= wk;
         const u32x4 kh = pack8(x);
@@ -806,7 +825,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_a(const BwArgs a) {
       const int r = tid / L::BPR + 16 * rr;
       const float ht = F[L::HT + r] * (DECAY ? __expf(Lseg + F[L::LAM + r]) : 1.f);
       float x[8];
-      hilo8<D>(smem + L::Q, smem + L::QL, perm_pos(r), tid % L::BPR, x);
+      hilo8<D, XQ>(smem + L::Q, smem + L::QL, perm_pos(r), tid % L::BPR, x);
 #pragma unroll
       for (int e = 0; e < 8; ++e) gzp[e] += x[e] * ht;
     }
@@ -1011,12 +1030,13 @@ __device__ __forceinline__ void stage2(const BwArgs& a, int t0, int tid, const R
     fq[e] = valid ? (DECAY == 3 ? fq[e] : elu1_fast(fq[e])) : 0.f;
     fk[e] = valid ? (DECAY == 3 ? fk[e] : elu1_fast(fk[e])) : 0.f;
   }
+  // identity features of bf16 inputs (mLSTM) are exact in bf16: no low parts
   const u32x4 qh = pack8(fq);
   blk_write<D>(buf + L::Q, pr, b, qh);
-  blk_write<D>(buf + L::QL, pr, b, low8(fq, qh));
+  if constexpr (DECAY != 3) blk_write<D>(buf + L::QL, pr, b, low8(fq, qh));
   const u32x4 kh = pack8(fk);
   row_write_perm<D>(buf + L::K, pr, b, kh);
-  row_write_perm<D>(buf + L::KL, pr, b, low8(fk, kh));
+  if constexpr (DECAY != 3) row_write_perm<D>(buf + L::KL, pr, b, low8(fk, kh));
   blk_write<D>(buf + L::V, pr, b, valid ? x.v : u32x4{0u, 0u, 0u, 0u});
   const float rt = valid ? x.th.x : 0.f, ht = valid ? x.th.y : 0.f;
   float gv[8];
@@ -1070,6 +1090,7 @@ template <int D, int DECAY, bool DF32>
 __global__ __launch_bounds__(128 * (D / 32)) void bwd_pass_b2(const BwArgs a) {
   using L = BL2<D, DECAY>;
   constexpr int NJ = L::NJ, KS = D / 16;
+  constexpr bool XQ = DECAY == 3;   // exact phi(q), phi(k): no low parts (see bwd_pass_a)
   __shared__ __align__(16) char smem[L::LDS];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, n = lane & 31;
   const bool value_wave = w < NJ;
@@ -1144,15 +1165,19 @@ __global__ __launch_bounds__(128 * (D / 32)) void bwd_pass_b2(const BwArgs a) {
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
           aq[kk] = row_operand_perm<D>(cur + L::Q, perm_pos(n), k0 + kk, g);
-          aql[kk] = row_operand_perm<D>(cur + L::QL, perm_pos(n), k0 + kk, g);
           bk[kk] = row_operand<D>(cur + L::K, perm_pos(n), 2 * (k0 + kk) + g);
-          bkl[kk] = row_operand<D>(cur + L::KL, perm_pos(n), 2 * (k0 + kk) + g);
+          if constexpr (!XQ) {
+            aql[kk] = row_operand_perm<D>(cur + L::QL, perm_pos(n), k0 + kk, g);
+            bkl[kk] = row_operand<D>(cur + L::KL, perm_pos(n), 2 * (k0 + kk) + g);
+          }
         }
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
           at = mfma(aq[kk], bk[kk], at);
-          at = mfma(aq[kk], bkl[kk], at);
-          at = mfma(aql[kk], bk[kk], at);
+          if constexpr (!XQ) {
+            at = mfma(aq[kk], bkl[kk], at);
+            at = mfma(aql[kk], bk[kk], at);
+          }
         }
       }
       causal_weights<DECAY>(F, L::LAM, g, n, wt);
@@ -1171,13 +1196,13 @@ __global__ __launch_bounds__(128 * (D / 32)) void bwd_pass_b2(const BwArgs a) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           bk[ks] = row_operand<D>(cur + L::K, perm_pos(n), 2 * (2 * fb + ks) + g);
-          bkl[ks] = row_operand<D>(cur + L::KL, perm_pos(n), 2 * (2 * fb + ks) + g);
+          if constexpr (!XQ) bkl[ks] = row_operand<D>(cur + L::KL, perm_pos(n), 2 * (2 * fb + ks) + g);
         }
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           dvt = mfma(sh[ks], bk[ks], dvt);
           dvt = mfma(sl[ks], bk[ks], dvt);
-          dvt = mfma(sh[ks], bkl[ks], dvt);
+          if constexpr (!XQ) dvt = mfma(sh[ks], bkl[ks], dvt);
         }
       }
       if constexpr (DECAY != 0) dvt *= es;
@@ -1215,12 +1240,12 @@ __global__ __launch_bounds__(128 * (D / 32)) void bwd_pass_b2(const BwArgs a) {
       for (int fb = 0; fb < NJ; ++fb) {
         u32x4 bq[2], bql[2];
         tr_ops<D, 2>(cur + L::Q, 32 * fb, lane, bq);
-        tr_ops<D, 2>(cur + L::QL, 32 * fb, lane, bql);
+        if constexpr (!XQ) tr_ops<D, 2>(cur + L::QL, 32 * fb, lane, bql);
         if constexpr (DECAY != 0) X[fb] *= ec;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           X[fb] = mfma(bq[ks], ag[ks], X[fb]);
-          X[fb] = mfma(bql[ks], ag[ks], X[fb]);
+          if constexpr (!XQ) X[fb] = mfma(bql[ks], ag[ks], X[fb]);
           X[fb] = mfma(bq[ks], agl[ks], X[fb]);
         }
       }
@@ -1273,12 +1298,12 @@ __global__ __launch_bounds__(128 * (D / 32)) void bwd_pass_b2(const BwArgs a) {
       if constexpr (DECAY != 0) dkt *= es;
       u32x4 oqt[2], oqlt[2];
       tr_ops<D, 2>(cur + L::Q, 32 * wb, lane, oqt);
-      tr_ops<D, 2>(cur + L::QL, 32 * wb, lane, oqlt);
+      if constexpr (!XQ) tr_ops<D, 2>(cur + L::QL, 32 * wb, lane, oqlt);
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         dkt = mfma(oqt[ks], bh_[ks], dkt);
         dkt = mfma(oqt[ks], bl_[ks], dkt);
-        dkt = mfma(oqlt[ks], bh_[ks], dkt);
+        if constexpr (!XQ) dkt = mfma(oqlt[ks], bh_[ks], dkt);
       }
       float* gzl = reinterpret_cast<float*>(smem + L::GZ);
       {
@@ -1288,7 +1313,7 @@ __global__ __launch_bounds__(128 * (D / 32)) void bwd_pass_b2(const BwArgs a) {
         for (int r = 0; r < 4; ++r) {
           const int pc = perm_pos(32 * wb + 8 * r + 4 * g);   // stored column of these 4 features
           const int off = tile_off<D>(perm_pos(n), pc >> 3) + ((pc & 7) << 1);
-          const f32x4 p4 = hilo4(cur + L::K, cur + L::KL, off);
+          const f32x4 p4 = hilo4<XQ>(cur + L::K, cur + L::KL, off);
           const f32x4 z4 = *reinterpret_cast<const f32x4*>(gzl + 32 * wb + 8 * r + 4 * g);
           f32x4 o4;
 #pragma unroll
@@ -1316,7 +1341,7 @@ __global__ __launch_bounds__(128 * (D / 32)) void bwd_pass_b2(const BwArgs a) {
         for (int ks = 0; ks < 2; ++ks) {
           X[jb] = mfma(ag[ks], oqt[ks], X[jb]);
           X[jb] = mfma(agl[ks], oqt[ks], X[jb]);
-          X[jb] = mfma(ag[ks], oqlt[ks], X[jb]);
+          if constexpr (!XQ) X[jb] = mfma(ag[ks], oqlt[ks], X[jb]);
         }
       }
       // gz (feature 32 wb + n) = e^{l_last} gz + sum_t e^{l_t} h_t phi(q_t):
@@ -1326,13 +1351,18 @@ __global__ __launch_bounds__(128 * (D / 32)) void bwd_pass_b2(const BwArgs a) {
       for (int ks = 0; ks < 2; ++ks) {
         const f32x4 h0 = *reinterpret_cast<const f32x4*>(F + L::HW + 16 * ks + 8 * g);
         const f32x4 h1 = *reinterpret_cast<const f32x4*>(F + L::HW + 16 * ks + 8 * g + 4);
-        float ph[8], pl[8];
+        float ph[8];
         unpack8(oqt[ks], ph, bf16_t{});
-        unpack8(oqlt[ks], pl, bf16_t{});
+        if constexpr (!XQ) {
+          float pl[8];
+          unpack8(oqlt[ks], pl, bf16_t{});
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ph[e] += pl[e];
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          inc += (ph[e] + pl[e]) * h0[e];
-          inc += (ph[e + 4] + pl[e + 4]) * h1[e];
+          inc += ph[e] * h0[e];
+          inc += ph[e + 4] * h1[e];
         }
       }
       inc = swap_sum32(inc);
