@@ -436,19 +436,22 @@ def test_backward_mlstm_bf16_vs_oracle(d):
 # the rms at +4) no fp32 arithmetic resolves (the per-token kernel misses
 # the oracle there by as much as the chunked passes).
 MLSTM_CHUNKED = [
-    (64, 333, 0, "max1", False, False, 0.0),
-    (64, 333, 3, "max1", True, True, 0.0),
-    (128, 257, 1, "max1", False, True, 0.0),
-    (128, 640, 0, "max1", False, False, 4.0),
-    (64, 200, 2, True, False, True, 0.0),
-    (128, 161, 0, False, True, False, 0.0),
-    (64, 95, 5, "max1", False, True, 25.0),
-    (128, 31, 0, "max1", True, True, 0.0),
+    (64, 333, 0, "max1", False, False, 0.0, False),
+    (64, 333, 3, "max1", True, True, 0.0, False),
+    (128, 257, 1, "max1", False, True, 0.0, False),
+    (128, 640, 0, "max1", False, False, 4.0, False),
+    (64, 200, 2, True, False, True, 0.0, False),
+    (128, 161, 0, False, True, False, 0.0, False),
+    (64, 95, 5, "max1", False, True, 25.0, False),
+    (128, 31, 0, "max1", True, True, 0.0, False),
+    (128, 300, 3, "max1", False, True, 0.0, True),
+    (64, 129, 0, True, True, False, 0.0, True),
 ]
 
 
-@pytest.mark.parametrize("d,T,segments,normalize,fexp,with_state,ishift", MLSTM_CHUNKED)
-def test_backward_mlstm_chunked_vs_oracle(d, T, segments, normalize, fexp, with_state, ishift):
+@pytest.mark.parametrize("d,T,segments,normalize,fexp,with_state,ishift,dout32", MLSTM_CHUNKED)
+def test_backward_mlstm_chunked_vs_oracle(d, T, segments, normalize, fexp, with_state, ishift,
+                                          dout32):
     """bf16 inputs with the mLSTM gates take the chunked passes: the
     stabiliser rebuilt per chunk from each segment's start (the prefill's
     scan), alpha' and beta' as decay and key weight, the gates' gradients
@@ -458,7 +461,9 @@ def test_backward_mlstm_chunked_vs_oracle(d, T, segments, normalize, fexp, with_
     positive = normalize is True or ishift > 0
     x = _mlstm_case(B, H, T, d, d, "bf16", seed=T + d, ishift=ishift, fexp=fexp,
                     positive=positive)
-    do = torch.randn(B, H, T, d, generator=torch.Generator().manual_seed(T)).to(torch.bfloat16)
+    do = torch.randn(B, H, T, d, generator=torch.Generator().manual_seed(T))
+    if not dout32:
+        do = do.to(torch.bfloat16)
     state = None
     if with_state:
         rng = np.random.default_rng(d + T)
@@ -470,7 +475,7 @@ def test_backward_mlstm_chunked_vs_oracle(d, T, segments, normalize, fexp, with_
     S0, z0, m0 = (None, None, None) if state is None else state
     ref = O.mlstm_gradients(x.q, x.k, x.v, do, x.igate, x.fgate, fexp, 1e-6, S0, z0, m0, normalize)
     compare(got, {k: ref[k] for k in got}, TOL["bf16"],
-            ("mlstm chunked", d, T, segments, normalize, fexp, with_state, ishift))
+            ("mlstm chunked", d, T, segments, normalize, fexp, with_state, ishift, dout32))
 
 
 def test_backward_mlstm_chunked_equals_per_token_on_the_same_values():
