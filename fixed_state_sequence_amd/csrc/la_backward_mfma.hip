@@ -61,8 +61,9 @@
 // token tile is stored with its rows at perm_pos(token)).
 //
 // Precision.  Every product takes both operands as bf16 high + low parts
-// (three MFMAs: hi hi, lo hi, hi lo; v is bf16 and exact), so each carries
-// about 2^-16 relative error.  Plain bf16 operands do not suffice here:
+// (three MFMAs: hi hi, lo hi, hi lo), so each carries about 2^-16 relative
+// error; v, and the identity features of bf16 inputs (the mLSTM gates), are
+// exact in bf16, so the products with them take two MFMAs, or one.  Plain bf16 operands do not suffice here:
 // the read-out's error reaches h = -g.o, and the terms S g + z h (and
 // G v + gz) cancel down to sum_s phi(k_s) g.(v_s - o_t), amplifying it; the
 // states and the score sums are random-sign sums whose rounding error stays
