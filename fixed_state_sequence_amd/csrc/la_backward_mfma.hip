@@ -43,7 +43,9 @@
 //   pass A (chunks in order): the forward read-out again (r_t, h_t, g_t),
 //     dq, <phi(q_t), dphi(q_t)>, and the segment's share of the gradient
 //     state, G_seg = sum over its tokens of (decay from the segment's start)
-//     phi(q_t) g_t^T (and gz_seg), with the segment's total log-decay;
+//     phi(q_t) g_t^T (and gz_seg), with the segment's total log-decay; the
+//     state is held twice in registers (S and S^T, one per kind of wave;
+//     see bwd_pass_a2);
 //   reverse scan over the segments: G at every segment's end, and
 //     dS0 = G before the first token, dz0 likewise;
 //   pass B (chunks in reverse): dk, dv and <phi(k_s), dphi(k_s)> / beta_s
@@ -81,42 +83,6 @@ namespace {
 
 constexpr int BCH = 32;                // chunk length
 constexpr float kLogFloorB = -80.0f;   // log alpha floor: alpha = 0 stays finite
-
-template <int D, int DECAY>
-struct BL {
-  static constexpr int NW = D / 32;          // waves; wave w owns 32-wide block w
-  static constexpr int NT = 64 * NW;
-  static constexpr int NJ = D / 32;          // 32-wide blocks of D
-  static constexpr int BPR = D / 8;          // 16-byte blocks per bf16 row
-  static constexpr int TILE = BCH * D * 2;   // one token tile, bf16
-  static constexpr int FS = D + 4;           // fp32 row stride (floats)
-  // token tiles (bf16, rows at perm_pos(token), tile_off<D> swizzle)
-  static constexpr int Q = 0;                // phi(q), high part
-  static constexpr int QL = Q + TILE;        // phi(q), low part
-  static constexpr int K = QL + TILE;        // phi(k), high part
-  static constexpr int KL = K + TILE;        // phi(k), low part
-  static constexpr int V = KL + TILE;        // v
-  static constexpr int GH = V + TILE;        // g, high part
-  static constexpr int GL = GH + TILE;       // g, low part
-  static constexpr int SB = GL + TILE;       // the carried state S, bf16, rows = features
-  static constexpr int SBL = SB + D * D * 2; // its low part
-  static constexpr int DO = SBL + D * D * 2; // fp32 [BCH][FS]: dout
-  // with a decay, a weighted tile pair (high, low): e^{L + l_t} g_t for the
-  // gradient-state fold, then w_s phi(k_s) for the state fold
-  static constexpr int WH = DO + BCH * FS * 4;
-  static constexpr int WL = WH + TILE;
-  static constexpr int F = DECAY ? WL + TILE : WH;   // fp32 scalars, offsets below (floats)
-  static constexpr int Z = 0;                // z, carried
-  static constexpr int DI = D;               // phi(q_t) . z per token
-  static constexpr int HT = DI + BCH;        // h_t per token
-  static constexpr int HP = HT + BCH;        // per-wave partial dout . o [NW][BCH]
-  static constexpr int ZP = HP + NW * BCH;   // per-wave increments of z [NW][D]
-  static constexpr int LAM = ZP + NW * D;    // within-chunk log-prefix l_t [BCH]
-  static constexpr int BET = LAM + BCH;      // beta_t [BCH]
-  static constexpr int QP = BET + BCH;       // per-wave partial <phi(q), dphi(q)> [NW][BCH]
-  static constexpr int NF = QP + NW * BCH;
-  static constexpr int LDS = F + NF * 4;
-};
 
 struct BwArgs {
   const bf16_t* q;
@@ -173,25 +139,6 @@ __device__ __forceinline__ void split_acc(const f32x16& x, u32x4 (&hi)[2], u32x4
     }
 }
 
-// Write a D x D state held as transposed accumulator tiles X[fb] (rows j of
-// block jb, columns f of block fb) into the bf16 tiles at rows f: high parts
-// at sb, low parts at sbl.
-template <int D>
-__device__ __forceinline__ void write_state_tile(char* sb, char* sbl, const f32x16 (&X)[D / 32],
-                                                 int jb, int g, int n) {
-#pragma unroll
-  for (int fb = 0; fb < D / 32; ++fb)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      uint32_t h0, h1, l0, l1;
-      split_bf16(X[fb][4 * r], X[fb][4 * r + 1], h0, l0);
-      split_bf16(X[fb][4 * r + 2], X[fb][4 * r + 3], h1, l1);
-      const int off = tile_off<D>(32 * fb + n, 4 * jb + r) + 8 * g;
-      *reinterpret_cast<u32x2*>(sb + off) = u32x2{h0, h1};
-      *reinterpret_cast<u32x2*>(sbl + off) = u32x2{l0, l1};
-    }
-}
-
 // Four features at byte offset `off` of a token row of a high/low tile pair,
 // as fp32 (high + low carry phi to about 2^-16).  EX: the high parts are
 // exact (bf16 inputs under identity features), the low tile is not read.
@@ -229,62 +176,12 @@ __device__ __forceinline__ void hilo8(const char* hi, const char* lo, int row, i
   }
 }
 
-// The MFMA operands of one product, read together before its MFMAs are
-// issued, so that one wave per SIMD waits for the LDS once per product
-// rather than once per k-step: row `row` of a token or state tile over the
-// D / 16 k-steps (16-byte blocks 2 ks + g), or NK k-steps of 16 rows of a
-// transposed read at columns col0 .. col0 + 31.
-template <int D>
-__device__ __forceinline__ void row_ops(const char* tile, int row, int g, u32x4 (&o)[D / 16]) {
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) o[ks] = row_operand<D>(tile, row, 2 * ks + g);
-}
-
+// NK k-steps of a transposed operand (16 rows each) at columns col0 ..
+// col0 + 31, read together before their MFMAs are issued.
 template <int D, int NK>
 __device__ __forceinline__ void tr_ops(const char* tile, int col0, int lane, u32x4 (&o)[NK]) {
 #pragma unroll
   for (int ks = 0; ks < NK; ++ks) o[ks] = tr_operand<D>(tile, 16 * ks, col0, lane);
-}
-
-// Raw inputs of one chunk for this thread: rows r and r + 16, block b; and
-// the decay value of token lane % 32.
-struct Raw {
-  u32x4 q[2], k[2], v[2];
-  f32x4 d[2][2];   // dout as fp32
-  float al;        // mLSTM: the forget pre-activation
-  float ig;        // mLSTM: the input-gate pre-activation
-};
-
-template <int D, int DECAY>
-__device__ __forceinline__ void load_raw(const BwArgs& a, int64_t bh, int t0, int tid, Raw& x) {
-  using L = BL<D, DECAY>;
-  const int b = tid % L::BPR;
-  const int64_t T = a.T;
-#pragma unroll
-  for (int rr = 0; rr < 2; ++rr) {
-    const int r = tid / L::BPR + 16 * rr;
-    const int64_t t = min(int64_t(t0 + r), T - 1);
-    const int64_t row = (bh * T + t) * D + 8 * b;
-    x.q[rr] = *reinterpret_cast<const u32x4*>(a.q + row);
-    x.k[rr] = *reinterpret_cast<const u32x4*>(a.k + row);
-    x.v[rr] = *reinterpret_cast<const u32x4*>(a.v + row);
-    if (a.dout_f32) {
-      const float* dp = static_cast<const float*>(a.dout) + row;
-      x.d[rr][0] = *reinterpret_cast<const f32x4*>(dp);
-      x.d[rr][1] = *reinterpret_cast<const f32x4*>(dp + 4);
-    } else {
-      const u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const bf16_t*>(a.dout) + row);
-      float f[8];
-      unpack8(w, f, bf16_t{});
-      x.d[rr][0] = f32x4{f[0], f[1], f[2], f[3]};
-      x.d[rr][1] = f32x4{f[4], f[5], f[6], f[7]};
-    }
-  }
-  x.al = 1.f;
-  if constexpr (DECAY != 0)
-    x.al = a.decay[bh * T + min(int64_t(t0 + (tid & 31)), T - 1)];
-  if constexpr (DECAY == 3)
-    x.ig = a.igate[bh * T + min(int64_t(t0 + (tid & 31)), T - 1)];
 }
 
 // Sum of v[e] over the lanes of this wave that share lane % BPR (the rows
@@ -303,14 +200,14 @@ __device__ __forceinline__ void wave_rows_sum8(float (&v)[8], int lane, float* d
 // gets the inclusive log-prefix of token l % 32 in lam and its beta in bet,
 // the chunk total in tot.  Tokens past the end have alpha = 1, beta = 0.
 template <int DECAY>
-__device__ __forceinline__ void chunk_decay(const Raw& x, int t0, int T, int lane, float& lam,
+__device__ __forceinline__ void chunk_decay(float alpha, int t0, int T, int lane, float& lam,
                                             float& bet, float& tot) {
   const bool valid = t0 + (lane & 31) < T;
   float la = 0.f;
   bet = 0.f;
   if (valid) {
-    la = fmaxf(__logf(x.al), kLogFloorB);
-    bet = DECAY == 2 ? 1.f - x.al : 1.f;
+    la = fmaxf(__logf(alpha), kLogFloorB);
+    bet = DECAY == 2 ? 1.f - alpha : 1.f;
   }
   lam = la;
 #pragma unroll
@@ -358,509 +255,6 @@ __device__ __forceinline__ void chunk_decay_ml(float fpre, float ipre, int fexp,
   }
   tot = __shfl(lam, 31, 32);
   mst = __shfl(mt, 31, 32);
-}
-
-// Stage one chunk into LDS for pass A: phi(q), phi(k) (high, low), v, the
-// fp32 dout, phi(q_t) . z and this wave's increments of z (sum w_s
-// phi(k_s)).  Rows past the end of the sequence are zero.  lam, bet, tot
-// return the chunk's decay (see chunk_decay; 0, 1, 0 without); with the
-// mLSTM gates (identity features) mst carries the stabiliser across chunks,
-// mt returns token lane % 32's, and log alpha', beta' go to a.ab for pass B.
-template <int D, int DECAY>
-__device__ __forceinline__ void stage(const BwArgs& a, int64_t bh, int t0, int tid, const Raw& x,
-                                      char* smem, float& lam, float& bet, float& tot, float& mst,
-                                      float& mt) {
-  using L = BL<D, DECAY>;
-  float* F = reinterpret_cast<float*>(smem + L::F);
-  const int b = tid % L::BPR, lane = tid & 63, w = tid >> 6;
-  lam = 0.f;
-  bet = 1.f;
-  tot = 0.f;
-  if constexpr (DECAY == 3) {
-    float la;
-    chunk_decay_ml(x.al, x.ig, a.fgate_exp, t0, a.T, lane, mst, mt, la, lam, bet, tot);
-    if (w == 0 && lane < BCH && t0 + lane < a.T)
-      *reinterpret_cast<float2*>(a.ab + (bh * a.T + t0 + lane) * 2) = make_float2(la, bet);
-  } else if constexpr (DECAY != 0) {
-    chunk_decay<DECAY>(x, t0, a.T, lane, lam, bet, tot);
-  }
-  if constexpr (DECAY != 0) {
-    if (w == 0 && lane < BCH) {
-      F[L::LAM + lane] = lam;
-      F[L::BET + lane] = bet;
-    }
-  }
-  float inc[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) inc[e] = 0.f;
-#pragma unroll
-  for (int rr = 0; rr < 2; ++rr) {
-    const int r = tid / L::BPR + 16 * rr;
-    const bool valid = t0 + r < a.T;
-    const int pr = perm_pos(r);
-    float lr = 0.f, br = 1.f;   // this row's log-prefix and beta
-    if constexpr (DECAY != 0) {
-      lr = __shfl(lam, r);
-      br = __shfl(bet, r);
-    }
-    float fq[8], fk[8];
-    unpack8(x.q[rr], fq, bf16_t{});
-    unpack8(x.k[rr], fk, bf16_t{});
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      fq[e] = valid ? (DECAY == 3 ? fq[e] : elu1_fast(fq[e])) : 0.f;
-      fk[e] = valid ? (DECAY == 3 ? fk[e] : elu1_fast(fk[e])) : 0.f;
-    }
-    // identity features of bf16 inputs (mLSTM) are exact in bf16: no low parts
-    const u32x4 qh = pack8(fq);
-    blk_write<D>(smem + L::Q, pr, b, qh);
-    if constexpr (DECAY != 3) blk_write<D>(smem + L::QL, pr, b, low8(fq, qh));
-    const u32x4 kh = pack8(fk);
-    blk_write<D>(smem + L::K, pr, b, kh);
-    if constexpr (DECAY != 3) blk_write<D>(smem + L::KL, pr, b, low8(fk, kh));
-    blk_write<D>(smem + L::V, pr, b, valid ? x.v[rr] : u32x4{0u, 0u, 0u, 0u});
-    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-    const f32x4 d0 = valid ? x.d[rr][0] : zero4, d1 = valid ? x.d[rr][1] : zero4;
-    float* dor = reinterpret_cast<float*>(smem + L::DO) + r * L::FS + 8 * b;
-    *reinterpret_cast<f32x4*>(dor) = d0;
-    *reinterpret_cast<f32x4*>(dor + 4) = d1;
-    const float wk = DECAY ? br * __expf(tot - lr) : 1.f;   // key weight to the chunk's end
-    float part = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      part += fq[e] * F[L::Z + 8 * b + e];
-      inc[e] += wk * fk[e];
-    }
-    part = row_sum<L::BPR>(part);
-    if (b == 0) F[L::DI + r] = part;
-  }
-  wave_rows_sum8<L::BPR>(inc, lane, F + L::ZP + w * D);
-}
-
-// ------------------------------------------------------------------ pass A
-
-template <int D, int DECAY>
-__global__ __launch_bounds__(64 * (D / 32)) void bwd_pass_a(const BwArgs a) {
-  using L = BL<D, DECAY>;
-  constexpr int NJ = L::NJ;
-  // identity features of bf16 inputs (the mLSTM gates) are exact in bf16:
-  // their low parts are zero, and the products with them are skipped
-  constexpr bool XQ = DECAY == 3;
-  __shared__ __align__(16) char smem[L::LDS];
-  float* F = reinterpret_cast<float*>(smem + L::F);
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, n = lane & 31;
-  const int64_t bh = blockIdx.x / a.nseg;
-  const int seg = blockIdx.x % a.nseg;
-  const int T = a.T;
-  const int nchunks = (T + BCH - 1) / BCH;
-  const int c0 = seg * a.cps, c1 = min(c0 + a.cps, nchunks);
-
-  // start state: S^T tiles (rows j of block w, columns f of block fb)
-  f32x16 S[NJ], Gs[NJ];
-  {
-    const float* Ss = a.S0 ? a.S0 + bh * a.s_bh + int64_t(seg) * a.s_seg : nullptr;
-#pragma unroll
-    for (int fb = 0; fb < NJ; ++fb) {
-      Gs[fb] = zero16();
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int f = 32 * fb + n, j = 32 * w + 8 * (i >> 2) + 4 * g + (i & 3);
-        S[fb][i] = Ss ? Ss[f * D + j] : 0.f;
-      }
-    }
-    if (tid < D) F[L::Z + tid] = a.z0 ? a.z0[bh * a.z_bh + int64_t(seg) * a.s_seg + tid] : 0.f;
-    write_state_tile<D>(smem + L::SB, smem + L::SBL, S, w, g, n);
-  }
-  __syncthreads();
-
-  // this thread's share of gz_seg = sum (decay from the segment's start)
-  // phi(q_t) h_t (its rows, its 8 features)
-  float gzp[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) gzp[e] = 0.f;
-  float Lseg = 0.f;   // log-decay from the segment's start to the current chunk's start
-  // mLSTM: the stabiliser before the current chunk (the segment's start
-  // state's to begin with), and token n's
-  float mst = 0.f, mt = 0.f;
-  if constexpr (DECAY == 3) mst = a.m0 ? a.m0[bh * a.m0_bh + seg] : 0.f;
-  Raw raw;
-  if (c0 < c1) load_raw<D, DECAY>(a, bh, c0 * BCH, tid, raw);
-  for (int c = c0; c < c1; ++c) {
-    const int t0 = c * BCH;
-    float lam, bet, tot;
-    stage<D, DECAY>(a, bh, t0, tid, raw, smem, lam, bet, tot, mst, mt);
-    __syncthreads();   // tiles, phi(q) . z, z increments, decay
-    if (c + 1 < c1) load_raw<D, DECAY>(a, bh, t0 + BCH, tid, raw);   // next chunk, in flight meanwhile
-    const bool vt = t0 + n < T;
-    const float eq = DECAY ? __expf(lam) : 1.f;   // e^{l_t}, t = n (lam is token n's)
-
-    // causal weight of (t = n, s = row of accumulator element i):
-    // beta_s e^{l_t - l_s} for s <= t (recomputed where used: fewer live
-    // registers)
-    auto weight = [&](int i) {
-      const int s = 8 * (i >> 2) + 4 * g + (i & 3);
-      return s <= n ? (DECAY ? F[L::BET + s] * __expf(lam - F[L::LAM + s]) : 1.f) : 0.f;
-    };
-
-    // scores P^T (rows s, columns t = n), weighted, row sums.  The three
-    // hi/lo products of every product here accumulate in one chain: back to
-    // back on one accumulator they issue without stalls, and fewer
-    // accumulators leave fewer to sum and to hold.  phi(q) of token n (high,
-    // low) serves the numerator too.
-    // (KB k-steps have their operands read at once: all of them, or two
-    // with a decay at D = 128, where fewer registers are free)
-    constexpr int KS = D / 16, KB = DECAY && D == 128 ? 2 : KS;
-    constexpr bool EARLY = KB == KS;   // operands read before the epilogues, and kept
-    u32x4 oq[KS], oql[KS];
-    f32x16 sc = zero16();
-#pragma unroll
-    for (int k0 = 0; k0 < KS; k0 += KB) {
-      u32x4 ok[KB], okl[KB];
-#pragma unroll
-      for (int kk = 0; kk < KB; ++kk) {
-        oq[k0 + kk] = row_operand<D>(smem + L::Q, perm_pos(n), 2 * (k0 + kk) + g);
-        ok[kk] = row_operand<D>(smem + L::K, perm_pos(n), 2 * (k0 + kk) + g);
-        if constexpr (!XQ) {
-          oql[k0 + kk] = row_operand<D>(smem + L::QL, perm_pos(n), 2 * (k0 + kk) + g);
-          okl[kk] = row_operand<D>(smem + L::KL, perm_pos(n), 2 * (k0 + kk) + g);
-        }
-      }
-#pragma unroll
-      for (int kk = 0; kk < KB; ++kk) {
-        sc = mfma(ok[kk], oq[k0 + kk], sc);
-        if constexpr (!XQ) {
-          sc = mfma(okl[kk], oq[k0 + kk], sc);
-          sc = mfma(ok[kk], oql[k0 + kk], sc);
-        }
-      }
-    }
-    // the numerator's state and v operands, read while the scores finish
-    // (else after the epilogue, phi(q) read again: fewer live registers
-    // across it)
-    u32x4 os[KS], osl[KS], ov[2];
-    if constexpr (EARLY) {
-      tr_ops<D, KS>(smem + L::SB, 32 * w, lane, os);
-      tr_ops<D, KS>(smem + L::SBL, 32 * w, lane, osl);
-      tr_ops<D, 2>(smem + L::V, 32 * w, lane, ov);
-    }
-    float dsum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      sc[i] *= weight(i);
-      dsum += sc[i];
-    }
-    dsum = swap_sum32(dsum);
-    const float den = dsum + eq * F[L::DI + n];
-    // the read-out factor; with the mLSTM gates of the state scaled by
-    // e^{-m_t} (token n's stabiliser), whose max1 floor is e^{-m_t}
-    const float rt = DECAY == 3 ? readout_factor(a.norm, den, a.eps, mt)
-                     : a.norm == LA_NORM_NONE ? 1.f
-                     : a.norm == LA_NORM_MAX1 ? 1.f / fmaxf(fabsf(den), 1.f)
-                                              : 1.f / (den + a.eps);
-    u32x4 ph[2], pl[2];
-    split_acc(sc, ph, pl);
-    if constexpr (!EARLY) tr_ops<D, 2>(smem + L::V, 32 * w, lane, ov);
-
-    // numerator^T (rows j of block w, columns t): e^{l_t} phi(Q) S + P V
-    f32x16 nu = zero16();
-#pragma unroll
-    for (int k0 = 0; k0 < KS; k0 += KB) {
-      if constexpr (!EARLY) {
-        // read again here, KB k-steps at a time
-#pragma unroll
-        for (int kk = 0; kk < KB; ++kk) {
-          const int fs = k0 + kk;
-          oq[fs] = row_operand<D>(smem + L::Q, perm_pos(n), 2 * fs + g);
-          if constexpr (!XQ) oql[fs] = row_operand<D>(smem + L::QL, perm_pos(n), 2 * fs + g);
-          os[fs] = tr_operand<D>(smem + L::SB, 16 * fs, 32 * w, lane);
-          osl[fs] = tr_operand<D>(smem + L::SBL, 16 * fs, 32 * w, lane);
-        }
-      }
-#pragma unroll
-      for (int kk = 0; kk < KB; ++kk) {
-        const int fs = k0 + kk;
-        nu = mfma(os[fs], oq[fs], nu);
-        nu = mfma(osl[fs], oq[fs], nu);
-        if constexpr (!XQ) nu = mfma(os[fs], oql[fs], nu);
-      }
-    }
-    if constexpr (DECAY != 0) nu *= eq;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      nu = mfma(ov[ks], ph[ks], nu);
-      nu = mfma(ov[ks], pl[ks], nu);
-    }
-
-    // o = num r_t; g = dout r_t (bf16 high and low tiles; with a decay also
-    // e^{Lseg + l_t} g for the gradient-state fold); dout . o partials
-    float hp = 0.f;
-    const float wg = DECAY ? __expf(Lseg + lam) : 1.f;
-    const float* dor = reinterpret_cast<const float*>(smem + L::DO) + n * L::FS + 32 * w + 4 * g;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const f32x4 d4 = *reinterpret_cast<const f32x4*>(dor + 8 * r);
-      float gv[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = 4 * r + e;
-        hp += d4[e] * (nu[i] * rt);
-        gv[e] = vt ? d4[e] * rt : 0.f;
-      }
-      uint32_t h0, h1, l0, l1;
-      split_bf16(gv[0], gv[1], h0, l0);
-      split_bf16(gv[2], gv[3], h1, l1);
-      const int off = tile_off<D>(perm_pos(n), 4 * w + r) + 8 * g;
-      *reinterpret_cast<u32x2*>(smem + L::GH + off) = u32x2{h0, h1};
-      *reinterpret_cast<u32x2*>(smem + L::GL + off) = u32x2{l0, l1};
-      if constexpr (DECAY != 0) {
-        split_bf16(gv[0] * wg, gv[1] * wg, h0, l0);
-        split_bf16(gv[2] * wg, gv[3] * wg, h1, l1);
-        *reinterpret_cast<u32x2*>(smem + L::WH + off) = u32x2{h0, h1};
-        *reinterpret_cast<u32x2*>(smem + L::WL + off) = u32x2{l0, l1};
-      }
-    }
-    hp = swap_sum32(hp);
-    if (g == 0) F[L::HP + w * BCH + n] = hp;
-    __syncthreads();   // g tiles, partials
-
-    float dot = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < L::NW; ++ww) dot += F[L::HP + ww * BCH + n];
-    float h = 0.f;
-    if (a.norm == LA_NORM_SUM) h = -dot * rt;
-    else if (a.norm == LA_NORM_MAX1)
-      h = fabsf(den) > (DECAY == 3 ? __expf(-mt) : 1.f) ? -copysignf(1.f, den) * dot * rt : 0.f;
-    if (!vt) h = 0.f;
-    if (w == 0 && g == 0) {
-      F[L::HT + n] = h;
-      if (vt) *reinterpret_cast<float2*>(a.tok + (bh * T + t0 + n) * 2) = make_float2(rt, h);
-    }
-
-    // B^T (rows s, columns t): (g_t . v_s + h_t) beta_s e^{l_t - l_s}; g of
-    // token n (high, low) serves dq too
-    u32x4 ogh[KS], ogl[KS];
-    f32x16 bs = zero16();
-#pragma unroll
-    for (int k0 = 0; k0 < KS; k0 += KB) {
-      u32x4 ovr[KB];
-#pragma unroll
-      for (int kk = 0; kk < KB; ++kk) {
-        ogh[k0 + kk] = row_operand<D>(smem + L::GH, perm_pos(n), 2 * (k0 + kk) + g);
-        ogl[k0 + kk] = row_operand<D>(smem + L::GL, perm_pos(n), 2 * (k0 + kk) + g);
-        ovr[kk] = row_operand<D>(smem + L::V, perm_pos(n), 2 * (k0 + kk) + g);
-      }
-#pragma unroll
-      for (int kk = 0; kk < KB; ++kk) {
-        bs = mfma(ovr[kk], ogh[k0 + kk], bs);
-        bs = mfma(ovr[kk], ogl[k0 + kk], bs);
-      }
-    }
-    // dq's state and phi(k) operands, read while B finishes (else after the
-    // epilogue, g read again)
-    u32x4 osr[KS], oslr[KS], okt[2], oklt[2];
-    if constexpr (EARLY) {
-      row_ops<D>(smem + L::SB, 32 * w + n, g, osr);
-      row_ops<D>(smem + L::SBL, 32 * w + n, g, oslr);
-      tr_ops<D, 2>(smem + L::K, 32 * w, lane, okt);
-      if constexpr (!XQ) tr_ops<D, 2>(smem + L::KL, 32 * w, lane, oklt);
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) bs[i] = (bs[i] + h) * weight(i);
-    u32x4 bh_[2], bl_[2];
-    split_acc(bs, bh_, bl_);
-    if constexpr (!EARLY) {
-      tr_ops<D, 2>(smem + L::K, 32 * w, lane, okt);
-      if constexpr (!XQ) tr_ops<D, 2>(smem + L::KL, 32 * w, lane, oklt);
-    }
-
-    // dphi(q)^T (rows f of block w, columns t): e^{l_t} (S g + z h) +
-    // phi(K)^T B.  S g and z h cancel in large part (their difference is
-    // sum_s phi(k_s) g.(v_s - o_t)).
-    f32x16 dqt = zero16();
-#pragma unroll
-    for (int k0 = 0; k0 < KS; k0 += KB) {
-      if constexpr (!EARLY) {
-#pragma unroll
-        for (int kk = 0; kk < KB; ++kk) {
-          const int js = k0 + kk;
-          ogh[js] = row_operand<D>(smem + L::GH, perm_pos(n), 2 * js + g);
-          ogl[js] = row_operand<D>(smem + L::GL, perm_pos(n), 2 * js + g);
-          osr[js] = row_operand<D>(smem + L::SB, 32 * w + n, 2 * js + g);
-          oslr[js] = row_operand<D>(smem + L::SBL, 32 * w + n, 2 * js + g);
-        }
-      }
-#pragma unroll
-      for (int kk = 0; kk < KB; ++kk) {
-        const int js = k0 + kk;
-        dqt = mfma(osr[js], ogh[js], dqt);
-        dqt = mfma(oslr[js], ogh[js], dqt);
-        dqt = mfma(osr[js], ogl[js], dqt);
-      }
-    }
-    if constexpr (DECAY != 0) dqt *= eq;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      dqt = mfma(okt[ks], bh_[ks], dqt);
-      dqt = mfma(okt[ks], bl_[ks], dqt);
-      if constexpr (!XQ) dqt = mfma(oklt[ks], bh_[ks], dqt);
-    }
-    {
-      float qdp = 0.f;   // <phi(q_t), dphi(q_t)> over this lane's features
-      float* dst = a.dq + (bh * T + t0 + n) * D + 32 * w + 4 * g;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int off = tile_off<D>(perm_pos(n), 4 * w + r) + 8 * g;
-        const f32x4 p4 = hilo4<XQ>(smem + L::Q, smem + L::QL, off);
-        const f32x4 z4 = *reinterpret_cast<const f32x4*>(F + L::Z + 32 * w + 4 * g + 8 * r);
-        f32x4 o4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 4 * r + e;
-          const float dphi = dqt[i] + eq * z4[e] * h;
-          // elu+1 has slope 1 above 0 and e^x = phi(x) below: min(phi, 1);
-          // identity features (mLSTM): 1
-          o4[e] = DECAY == 3 ? dphi : dphi * fminf(p4[e], 1.f);
-          qdp += p4[e] * dphi;
-        }
-        if (vt) *reinterpret_cast<f32x4*>(dst + 8 * r) = o4;
-      }
-      if constexpr (DECAY != 0) {
-        qdp = swap_sum32(qdp);
-        if (g == 0) F[L::QP + w * BCH + n] = qdp;
-      }
-    }
-
-    // the segment's gradient state: G_seg^T += (weighted g)^T phi(Q)
-    // (FB blocks of 32 columns have their operands read at once: all of
-    // them, or one with a decay at D = 128)
-    constexpr int FB = DECAY && D == 128 ? 1 : NJ;
-    {
-      constexpr int GA = DECAY ? L::WH : L::GH, GB = DECAY ? L::WL : L::GL;
-      u32x4 ag[2], agl[2];
-      tr_ops<D, 2>(smem + GA, 32 * w, lane, ag);
-      tr_ops<D, 2>(smem + GB, 32 * w, lane, agl);
-#pragma unroll
-      for (int f0 = 0; f0 < NJ; f0 += FB) {
-        u32x4 bq[FB][2], bql[FB][2];
-#pragma unroll
-        for (int f = 0; f < FB; ++f) {
-          tr_ops<D, 2>(smem + L::Q, 32 * (f0 + f), lane, bq[f]);
-          if constexpr (!XQ) tr_ops<D, 2>(smem + L::QL, 32 * (f0 + f), lane, bql[f]);
-        }
-#pragma unroll
-        for (int f = 0; f < FB; ++f)
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            Gs[f0 + f] = mfma(ag[ks], bq[f][ks], Gs[f0 + f]);
-            Gs[f0 + f] = mfma(agl[ks], bq[f][ks], Gs[f0 + f]);
-            if constexpr (!XQ) Gs[f0 + f] = mfma(ag[ks], bql[f][ks], Gs[f0 + f]);
-          }
-      }
-    }
-    if constexpr (DECAY == 0) {
-      // the state: S^T += V^T phi(K)
-      u32x4 av[2], bk[NJ][2], bkl[NJ][2];
-      tr_ops<D, 2>(smem + L::V, 32 * w, lane, av);
-#pragma unroll
-      for (int fb = 0; fb < NJ; ++fb) {
-        tr_ops<D, 2>(smem + L::K, 32 * fb, lane, bk[fb]);
-        tr_ops<D, 2>(smem + L::KL, 32 * fb, lane, bkl[fb]);
-      }
-#pragma unroll
-      for (int fb = 0; fb < NJ; ++fb)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          S[fb] = mfma(av[ks], bk[fb][ks], S[fb]);
-          S[fb] = mfma(av[ks], bkl[fb][ks], S[fb]);
-        }
-      __syncthreads();   // every read of the old S tile done; h visible
-    } else {
-      __syncthreads();   // every read of the old S tile and of the weighted g done; h visible
-      // w_s phi(k_s) (w_s = beta_s e^{l_last - l_s}) into the weighted tiles
-      const int b = tid % L::BPR;
-#pragma unroll
-      for (int rr = 0; rr < 2; ++rr) {
-        const int r = tid / L::BPR + 16 * rr;
-        const float wk = F[L::BET + r] * __expf(tot - F[L::LAM + r]);
-        float x[8];
-        hilo8<D, XQ>(smem + L::K, smem + L::KL, perm_pos(r), b, x);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] *= wk;
-        const u32x4 kh = pack8(x);
-        blk_write<D>(smem + L::WH, perm_pos(r), b, kh);
-        blk_write<D>(smem + L::WL, perm_pos(r), b, low8(x, kh));
-      }
-      __syncthreads();   // weighted keys staged
-      // the state: S^T = e^{l_last} S^T + V^T (w phi(K))
-      const float ec = __expf(tot);
-      u32x4 av[2];
-      tr_ops<D, 2>(smem + L::V, 32 * w, lane, av);
-#pragma unroll
-      for (int f0 = 0; f0 < NJ; f0 += FB) {
-        u32x4 bk[FB][2], bkl[FB][2];
-#pragma unroll
-        for (int f = 0; f < FB; ++f) {
-          tr_ops<D, 2>(smem + L::WH, 32 * (f0 + f), lane, bk[f]);
-          tr_ops<D, 2>(smem + L::WL, 32 * (f0 + f), lane, bkl[f]);
-        }
-#pragma unroll
-        for (int f = 0; f < FB; ++f) {
-          S[f0 + f] *= ec;
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            S[f0 + f] = mfma(av[ks], bk[f][ks], S[f0 + f]);
-            S[f0 + f] = mfma(av[ks], bkl[f][ks], S[f0 + f]);
-          }
-        }
-      }
-    }
-    write_state_tile<D>(smem + L::SB, smem + L::SBL, S, w, g, n);
-    if (tid < D) {
-      float zs = 0.f;
-#pragma unroll
-      for (int ww = 0; ww < L::NW; ++ww) zs += F[L::ZP + ww * D + tid];
-      F[L::Z + tid] = (DECAY ? __expf(tot) : 1.f) * F[L::Z + tid] + zs;
-    }
-#pragma unroll
-    for (int rr = 0; rr < 2; ++rr) {
-      const int r = tid / L::BPR + 16 * rr;
-      const float ht = F[L::HT + r] * (DECAY ? __expf(Lseg + F[L::LAM + r]) : 1.f);
-      float x[8];
-      hilo8<D, XQ>(smem + L::Q, smem + L::QL, perm_pos(r), tid % L::BPR, x);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) gzp[e] += x[e] * ht;
-    }
-    if constexpr (DECAY != 0) {
-      if (w == 0 && g == 0 && vt) {
-        float s = 0.f;
-#pragma unroll
-        for (int ww = 0; ww < L::NW; ++ww) s += F[L::QP + ww * BCH + n];
-        a.qd[bh * T + t0 + n] = s;
-      }
-      Lseg += tot;
-    }
-    __syncthreads();   // state tile and z for the next chunk; tiles free
-  }
-
-  // G_seg (rows f, columns j), gz_seg and the total log-decay into the slot
-  float* dst = a.gslot + (bh * a.nseg + seg) * int64_t(D * D + D);
-#pragma unroll
-  for (int fb = 0; fb < NJ; ++fb)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int f = 32 * fb + n, j = 32 * w + 8 * r + 4 * g;
-      *reinterpret_cast<f32x4*>(dst + f * D + j) =
-          f32x4{Gs[fb][4 * r], Gs[fb][4 * r + 1], Gs[fb][4 * r + 2], Gs[fb][4 * r + 3]};
-    }
-  wave_rows_sum8<L::BPR>(gzp, lane, F + L::ZP + w * D);
-  __syncthreads();
-  if (tid < D) {
-    float s = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < L::NW; ++ww) s += F[L::ZP + ww * D + tid];
-    dst[D * D + tid] = s;
-  }
-  if (DECAY != 0 && tid == 0) a.lgam[bh * a.nseg + seg] = Lseg;
 }
 
 // ------------------------------------------------------------ reverse scan
@@ -1010,9 +404,7 @@ __device__ __forceinline__ void stage2(const BwArgs& a, int t0, int tid, const R
     }
     tot = __shfl(lam, 31, 32);
   } else if constexpr (DECAY != 0) {
-    Raw rx;
-    rx.al = x.al.x;
-    chunk_decay<DECAY>(rx, t0, a.T, lane, lam, bet, tot);
+    chunk_decay<DECAY>(x.al.x, t0, a.T, lane, lam, bet, tot);
   }
   if (tid < BCH) {
     F[L::LAM + tid] = lam;
@@ -1091,7 +483,7 @@ template <int D, int DECAY, bool DF32>
 __global__ __launch_bounds__(128 * (D / 32)) void bwd_pass_b2(const BwArgs a) {
   using L = BL2<D, DECAY>;
   constexpr int NJ = L::NJ, KS = D / 16;
-  constexpr bool XQ = DECAY == 3;   // exact phi(q), phi(k): no low parts (see bwd_pass_a)
+  constexpr bool XQ = DECAY == 3;   // exact phi(q), phi(k): no low parts (the header's precision note)
   __shared__ __align__(16) char smem[L::LDS];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, n = lane & 31;
   const bool value_wave = w < NJ;
@@ -1386,6 +778,724 @@ __global__ __launch_bounds__(128 * (D / 32)) void bwd_pass_b2(const BwArgs a) {
     for (int c = c1 - 1; c >= c0; --c) chunk(c, std::false_type{});
 }
 
+// ------------------------------------------------------------ pass A2
+
+// Pass A with the state held twice in registers instead of staged in LDS
+// (as pass B holds the gradient state): waves 0 .. NJ-1 ("value waves") hold
+// S itself, rows f and the columns j of their 32-wide block, which as an
+// MFMA operand contracts over f (the numerator phi(q) . S); waves NJ ..
+// 2 NJ-1 ("feature waves") hold S^T, rows j and the columns f of their block,
+// which contracts over j (dphi(q) = S g).  Each folds its own copy every
+// chunk.  A chunk takes two phases, each ended by a barrier:
+//   1. value waves: the scores, the read-out (r_t, the numerator) and g_t =
+//      r_t dout_t into LDS with the partials of dout_t . o_t; feature waves
+//      meanwhile stage the next chunk into the other buffer;
+//   2. feature waves: h_t, B, dphi(q) and their fold; value waves their fold.
+// Two waves share each SIMD, one of each kind, so one wave's VALU work meets
+// the other's MFMAs.  The staging carries z one chunk ahead: staging chunk
+// c + 1 forms z at its start from z at chunk c's start and the increments
+// staged with chunk c, and phi(q) . z with it.  dout goes from global memory
+// straight into the value waves' registers (loaded a chunk ahead).
+//
+// Operand orders: an accumulator used as an operand carries its k-index in
+// the permuted order of its rows, so phi(q) (against S) and g (against S^T)
+// are stored with their features at perm_pos positions; phi(k) and v stay
+// natural, and are read at permuted positions where they meet phi(q) (the
+// scores) or g (B).
+template <int D, int DECAY>
+struct BL3 {
+  static constexpr int NJ = D / 32;          // 32-wide blocks of D
+  static constexpr int NW = 2 * NJ;          // value waves, then feature waves
+  static constexpr int BPR = D / 8;          // 16-byte blocks per bf16 row
+  static constexpr int TILE = BCH * D * 2;
+  static constexpr bool XQ = DECAY == 3;     // exact phi: no low tiles
+  static constexpr bool WT = DECAY != 0;     // weighted key tiles (else phi(k) serves)
+  // one buffer: token tiles (bf16, rows at perm_pos(token), tile_off<D>)
+  static constexpr int Q = 0;                        // phi(q) high (features at perm_pos)
+  static constexpr int QL = Q + TILE;                // phi(q) low
+  static constexpr int K = XQ ? QL : QL + TILE;      // phi(k) high (natural)
+  static constexpr int KL = K + TILE;                // phi(k) low
+  static constexpr int V = XQ ? KL : KL + TILE;      // v (natural)
+  static constexpr int WK = V + TILE;                // w_s phi(k_s) high, w_s = beta_s e^{l_last - l_s}
+  static constexpr int WKL = WK + TILE;              // and low
+  static constexpr int FB = WT ? WKL + TILE : WK;    // per-buffer scalars (floats from FB)
+  static constexpr int LAM = 0;              // l_t [BCH]
+  static constexpr int BET = LAM + BCH;      // beta_t [BCH]
+  static constexpr int DI = BET + BCH;       // phi(q_t) . z, z at the chunk's start [BCH]
+  static constexpr int MT = DI + BCH;        // mLSTM: m_t [BCH]
+  static constexpr int TOT = MT + BCH;       // the chunk's total log-decay
+  static constexpr int ZP = TOT + 4;         // per staging wave increments of z [NJ][D]
+  static constexpr int NFB = ZP + NJ * D;
+  static constexpr int BUF = FB + NFB * 4;   // bytes per buffer, a multiple of 16
+  // shared by both buffers
+  static constexpr int G = 2 * BUF;          // g = r_t dout high (features at perm_pos)
+  static constexpr int GL = G + TILE;        // g low
+  static constexpr int WG = GL + TILE;       // with a decay: e^{L + l_t} g_t high (L: the
+                                             // log-decay from the segment's start to the chunk)
+  static constexpr int WGL = WG + TILE;      // and low
+  static constexpr int SC = WT ? WGL + TILE : WG;   // scalars (floats from SC)
+  static constexpr int Z = 0;                // z at the start of chunks of parity p [2][D]
+  static constexpr int HP = Z + 2 * D;       // dout . o partials [NJ][BCH]
+  static constexpr int RT = HP + NJ * BCH;   // r_t [BCH]
+  static constexpr int HF = RT + BCH;        // h_t / (dout_t . o_t) [BCH]
+  static constexpr int QP = HF + BCH;        // <phi(q), dphi(q)> partials [NJ][BCH]
+  static constexpr int NSC = QP + NJ * BCH;
+  static constexpr int LDS = SC + NSC * 4;
+  static_assert(BUF % 16 == 0, "buffers stay 16-byte aligned");
+};
+
+// Raw inputs of one chunk for a staging thread (feature waves): rows r and
+// r + 16, block b; and token lane % 32's decay values.
+struct Raw3 {
+  u32x4 q[2], k[2], v[2];
+  float al, ig;
+};
+
+template <int D, int DECAY>
+__device__ __forceinline__ void load_raw3(const BwArgs& a, int64_t bh, int t0, int ft, Raw3& x) {
+  constexpr int BPR = D / 8;
+  const int r = ft / BPR, b = ft % BPR;
+  const int64_t tc = bh * int64_t(a.T) + t0;
+#pragma unroll
+  for (int rr = 0; rr < 2; ++rr) {
+    const uint32_t off = uint32_t(min(t0 + r + 16 * rr, a.T - 1) - t0) * D + 8 * b;
+    x.q[rr] = *reinterpret_cast<const u32x4*>(a.q + tc * D + off);
+    x.k[rr] = *reinterpret_cast<const u32x4*>(a.k + tc * D + off);
+    x.v[rr] = *reinterpret_cast<const u32x4*>(a.v + tc * D + off);
+  }
+  x.al = 1.f;
+  x.ig = 0.f;
+  const uint32_t ta = uint32_t(min(t0 + (ft & 31), a.T - 1) - t0);
+  if constexpr (DECAY != 0) x.al = (a.decay + tc)[ta];
+  if constexpr (DECAY == 3) x.ig = (a.igate + tc)[ta];
+}
+
+// dout of token t0 + n at features 32 wb + 8 r + 4 g .. + 3, r = 0..3, for a
+// value wave: fp32 (one block per r) or bf16 (two r per block).
+template <int D, bool DF32>
+__device__ __forceinline__ void load_dout3(const BwArgs& a, int64_t bh, int t0, int wb, int n,
+                                           int g, u32x4 (&d)[DF32 ? 4 : 2]) {
+  const int64_t tc = bh * int64_t(a.T) + t0;
+  const uint32_t off = uint32_t(min(t0 + n, a.T - 1) - t0) * D + 32 * wb + 4 * g;
+  if constexpr (DF32) {
+    const float* p = static_cast<const float*>(a.dout) + tc * D + off;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) d[r] = *reinterpret_cast<const u32x4*>(p + 8 * r);
+  } else {
+    const bf16_t* p = static_cast<const bf16_t*>(a.dout) + tc * D + off;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const u32x2 x = *reinterpret_cast<const u32x2*>(p + 16 * h);
+      const u32x2 y = *reinterpret_cast<const u32x2*>(p + 16 * h + 8);
+      d[h] = u32x4{x[0], x[1], y[0], y[1]};
+    }
+  }
+}
+
+template <bool DF32>
+__device__ __forceinline__ f32x4 dout4(const u32x4 (&d)[DF32 ? 4 : 2], int r) {
+  f32x4 o;
+  if constexpr (DF32) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = __uint_as_float(d[r][e]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const uint32_t w = d[r >> 1][2 * (r & 1) + e];
+      o[2 * e] = __uint_as_float(w << 16);
+      o[2 * e + 1] = __uint_as_float(w & 0xffff0000u);
+    }
+  }
+  return o;
+}
+
+// Stage one chunk into buffer buf (feature waves; ft = thread index among
+// them): the decay (mLSTM: the gates in the stabilised frame, m_t carried in
+// mst; log alpha', beta' to a.ab), phi(q) (high, low, features at perm_pos),
+// phi(k) (high, low), v, with a decay the weighted keys w_s phi(k_s) (high,
+// low), z at the chunk's start (from the previous chunk's buffer pbuf and z
+// zprev, or zs for a segment's first chunk; null: zero) into znew, phi(q_t)
+// . z and this wave's increments of z.  Rows past the end are zero.
+template <int D, int DECAY>
+__device__ __forceinline__ void stage3(const BwArgs& a, int64_t bh, int t0, int ft, const Raw3& x,
+                                       char* buf, const char* pbuf, const float* zprev,
+                                       float* znew, bool first, const float* zs, float& mst) {
+  using L = BL3<D, DECAY>;
+  float* F = reinterpret_cast<float*>(buf + L::FB);
+  const int r0 = ft / L::BPR, b = ft % L::BPR, lane = ft & 63, fw = ft >> 6;
+  float lam = 0.f, bet = 1.f, tot = 0.f, mt = 0.f;
+  if constexpr (DECAY == 3) {
+    float la;
+    chunk_decay_ml(x.al, x.ig, a.fgate_exp, t0, a.T, lane, mst, mt, la, lam, bet, tot);
+    if (fw == 0 && lane < BCH && t0 + lane < a.T)
+      *reinterpret_cast<float2*>(a.ab + (bh * a.T + t0 + lane) * 2) = make_float2(la, bet);
+  } else if constexpr (DECAY != 0) {
+    chunk_decay<DECAY>(x.al, t0, a.T, lane, lam, bet, tot);
+  }
+  if (fw == 0 && lane < BCH) {
+    F[L::LAM + lane] = lam;
+    F[L::BET + lane] = bet;
+    if constexpr (DECAY == 3) F[L::MT + lane] = mt;
+    if (lane == 0) F[L::TOT] = tot;
+  }
+  // z at this chunk's start, features 8 b .. 8 b + 7
+  float z[8];
+  if (first) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) z[e] = zs ? zs[8 * b + e] : 0.f;
+  } else {
+    const float* Fp = reinterpret_cast<const float*>(pbuf + L::FB);
+    const float ep = DECAY ? __expf(Fp[L::TOT]) : 1.f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      f32x4 s = *reinterpret_cast<const f32x4*>(zprev + 8 * b + 4 * h);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s[e] *= ep;
+#pragma unroll
+      for (int ww = 0; ww < L::NJ; ++ww) s += *reinterpret_cast<const f32x4*>(Fp + L::ZP + ww * D + 8 * b + 4 * h);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) z[4 * h + e] = s[e];
+    }
+  }
+  if (r0 == 0) {
+    *reinterpret_cast<f32x4*>(znew + 8 * b) = f32x4{z[0], z[1], z[2], z[3]};
+    *reinterpret_cast<f32x4*>(znew + 8 * b + 4) = f32x4{z[4], z[5], z[6], z[7]};
+  }
+  float inc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) inc[e] = 0.f;
+#pragma unroll
+  for (int rr = 0; rr < 2; ++rr) {
+    const int r = r0 + 16 * rr;
+    const bool valid = t0 + r < a.T;
+    const int pr = perm_pos(r);
+    float lr = 0.f, br = 1.f;   // this row's log-prefix and beta
+    if constexpr (DECAY != 0) {
+      lr = __shfl(lam, r);
+      br = __shfl(bet, r);
+    }
+    float fq[8], fk[8];
+    unpack8(x.q[rr], fq, bf16_t{});
+    unpack8(x.k[rr], fk, bf16_t{});
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      fq[e] = valid ? (DECAY == 3 ? fq[e] : elu1_fast(fq[e])) : 0.f;
+      fk[e] = valid ? (DECAY == 3 ? fk[e] : elu1_fast(fk[e])) : 0.f;
+    }
+    const u32x4 qh = pack8(fq);
+    row_write_perm<D>(buf + L::Q, pr, b, qh);
+    if constexpr (!L::XQ) row_write_perm<D>(buf + L::QL, pr, b, low8(fq, qh));
+    const u32x4 kh = pack8(fk);
+    blk_write<D>(buf + L::K, pr, b, kh);
+    if constexpr (!L::XQ) blk_write<D>(buf + L::KL, pr, b, low8(fk, kh));
+    blk_write<D>(buf + L::V, pr, b, valid ? x.v[rr] : u32x4{0u, 0u, 0u, 0u});
+    const float wk = DECAY ? br * __expf(tot - lr) : 1.f;   // key weight to the chunk's end
+    float part = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      part += fq[e] * z[e];
+      inc[e] += wk * fk[e];
+    }
+    if constexpr (L::WT) {
+      float wv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) wv[e] = wk * fk[e];
+      const u32x4 wh = pack8(wv);
+      blk_write<D>(buf + L::WK, pr, b, wh);
+      blk_write<D>(buf + L::WKL, pr, b, low8(wv, wh));
+    }
+    part = row_sum<L::BPR>(part);
+    if (b == 0) F[L::DI + r] = part;
+  }
+  wave_rows_sum8<L::BPR>(inc, lane, F + L::ZP + fw * D);
+}
+
+// The causal weights of a tile with rows s = 8 (i / 4) + 4 g + i % 4 and
+// column t = n (token n's log-prefix lt): beta_s e^{l_t - l_s} for s <= t.
+template <int DECAY>
+__device__ __forceinline__ void causal_weights_st(const float* F, int LAMOFF, int BETOFF, float lt,
+                                                  int g, int n, float (&wt)[16]) {
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) {
+    f32x4 ls = {0.f, 0.f, 0.f, 0.f}, bs = {1.f, 1.f, 1.f, 1.f};
+    if constexpr (DECAY != 0) ls = *reinterpret_cast<const f32x4*>(F + LAMOFF + 8 * q4 + 4 * g);
+    if constexpr (DECAY >= 2) bs = *reinterpret_cast<const f32x4*>(F + BETOFF + 8 * q4 + 4 * g);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int s = 8 * q4 + 4 * g + e;
+      wt[4 * q4 + e] = s <= n ? (DECAY ? bs[e] * __expf(lt - ls[e]) : 1.f) : 0.f;
+    }
+  }
+}
+
+template <int D, int DECAY, bool DF32>
+__global__ __launch_bounds__(128 * (D / 32)) void bwd_pass_a2(const BwArgs a) {
+  using L = BL3<D, DECAY>;
+  constexpr int NJ = L::NJ, KS = D / 16;
+  constexpr bool XQ = L::XQ;
+  __shared__ __align__(16) char smem[L::LDS];
+  float* Sc = reinterpret_cast<float*>(smem + L::SC);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, n = lane & 31;
+  const bool value_wave = w < NJ;
+  const int wb = value_wave ? w : w - NJ;   // this wave's 32-wide block (j or f)
+  const int64_t bh = blockIdx.x / a.nseg;
+  const int seg = blockIdx.x % a.nseg;
+  const int T = a.T;
+  const int nchunks = (T + BCH - 1) / BCH;
+  const int c0 = seg * a.cps, c1 = min(c0 + a.cps, nchunks);
+  if (c0 >= c1) {
+    // no chunks: a zero gradient state (the whole workgroup returns, no
+    // barrier is reached)
+    float* dst = a.gslot + (bh * a.nseg + seg) * int64_t(D * D + D);
+    for (int e = tid; e < D * D + D; e += 64 * L::NW) dst[e] = 0.f;
+    if (DECAY != 0 && tid == 0) a.lgam[bh * a.nseg + seg] = 0.f;
+    return;
+  }
+
+  // the segment's start state (rows f, columns j): value waves hold X[fb] =
+  // rows f of block fb, columns j of block wb; feature waves X[jb] = rows j
+  // of block jb, columns f of block wb
+  f32x16 X[NJ];
+  {
+    const float* Ss = a.S0 ? a.S0 + bh * a.s_bh + int64_t(seg) * a.s_seg : nullptr;
+#pragma unroll
+    for (int ob = 0; ob < NJ; ++ob)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = 32 * ob + 8 * (i >> 2) + 4 * g + (i & 3), col = 32 * wb + n;
+        X[ob][i] = !Ss ? 0.f : value_wave ? Ss[row * D + col] : Ss[col * D + row];
+      }
+  }
+  const float* zs = a.z0 ? a.z0 + bh * a.z_bh + int64_t(seg) * a.s_seg : nullptr;
+  const int ft = tid - 64 * NJ;   // index among the feature waves' threads
+  float mst = 0.f;                // mLSTM: the stabiliser before the chunk staged next
+  if constexpr (DECAY == 3) mst = a.m0 ? a.m0[bh * a.m0_bh + seg] : 0.f;
+  Raw3 raw;
+  u32x4 dreg[DF32 ? 4 : 2];
+  constexpr int WA = L::WT ? L::WK : L::K, WB = L::WT ? L::WKL : L::KL;
+
+  // value waves: the read-out of the next chunk up to its factor, formed in
+  // the previous chunk's second phase; the segment's gradient state G_seg^T
+  // (rows j of block wb, columns f; both in the permuted order of the
+  // features' stored positions) and this thread's share of gz_seg (tile rows
+  // r0, r0 + 16, block b, by stored position); the log-decay from the
+  // segment's start to the current chunk
+  struct Prep {
+    u32x4 ph[2], pl[2];   // the weighted scores P (rows s, column t = n), high and low
+    float rt, hf, eq;     // r_t, h_t / (dout_t . o_t), e^{l_t}
+  } pr;
+  f32x16 Gs[NJ];
+  float gzp[8];
+  float Lseg = 0.f;
+  if (value_wave) {
+#pragma unroll
+    for (int fb = 0; fb < NJ; ++fb) Gs[fb] = zero16();
+#pragma unroll
+    for (int e = 0; e < 8; ++e) gzp[e] = 0.f;
+  }
+  // the scores of chunk c (rows s, columns t = n): phi(k) at permuted
+  // feature positions against phi(q) stored that way; the causal weights;
+  // the denominator and the read-out factor
+  auto prep = [&](int c) {
+    // the operand addresses come from an opaque copy of the lane index:
+    // held across the loop, they would not fit the registers
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int n = ln & 31, g = ln >> 5;
+    const char* cur = smem + (c & 1) * L::BUF;
+    const float* F = reinterpret_cast<const float*>(cur + L::FB);
+    f32x16 sc = zero16();
+#pragma unroll
+    for (int k0 = 0; k0 < KS; k0 += 2) {
+      u32x4 ak[2], akl[2], bq[2], bql[2];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        ak[kk] = row_operand_perm<D>(cur + L::K, perm_pos(n), k0 + kk, g);
+        bq[kk] = row_operand<D>(cur + L::Q, perm_pos(n), 2 * (k0 + kk) + g);
+        if constexpr (!XQ) {
+          akl[kk] = row_operand_perm<D>(cur + L::KL, perm_pos(n), k0 + kk, g);
+          bql[kk] = row_operand<D>(cur + L::QL, perm_pos(n), 2 * (k0 + kk) + g);
+        }
+      }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        sc = mfma(ak[kk], bq[kk], sc);
+        if constexpr (!XQ) {
+          sc = mfma(akl[kk], bq[kk], sc);
+          sc = mfma(ak[kk], bql[kk], sc);
+        }
+      }
+    }
+    const float lt = DECAY ? F[L::LAM + n] : 0.f;   // token n's log-prefix
+    pr.eq = DECAY ? __expf(lt) : 1.f;
+    float wt[16];
+    causal_weights_st<DECAY>(F, L::LAM, L::BET, lt, g, n, wt);
+    float dsum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      sc[i] *= wt[i];
+      dsum += sc[i];
+    }
+    dsum = swap_sum32(dsum);
+    const float den = dsum + pr.eq * F[L::DI + n];
+    const float mt = DECAY == 3 ? F[L::MT + n] : 0.f;
+    // the read-out factor; with the mLSTM gates of the state scaled by
+    // e^{-m_t}, whose max1 floor is e^{-m_t}
+    pr.rt = DECAY == 3 ? readout_factor(a.norm, den, a.eps, mt)
+            : a.norm == LA_NORM_NONE ? 1.f
+            : a.norm == LA_NORM_MAX1 ? 1.f / fmaxf(fabsf(den), 1.f)
+                                     : 1.f / (den + a.eps);
+    pr.hf = 0.f;
+    if (a.norm == LA_NORM_SUM) pr.hf = -pr.rt;
+    else if (a.norm == LA_NORM_MAX1)
+      pr.hf = fabsf(den) > (DECAY == 3 ? __expf(-mt) : 1.f) ? -copysignf(pr.rt, den) : 0.f;
+    split_acc(sc, pr.ph, pr.pl);
+  };
+
+  if (value_wave) {
+    load_dout3<D, DF32>(a, bh, c0 * BCH, wb, n, g, dreg);
+  } else {
+    load_raw3<D, DECAY>(a, bh, c0 * BCH, ft, raw);
+    stage3<D, DECAY>(a, bh, c0 * BCH, ft, raw, smem + (c0 & 1) * L::BUF, nullptr, nullptr,
+                     Sc + L::Z + (c0 & 1) * D, true, zs, mst);
+    if (c0 + 1 < c1) load_raw3<D, DECAY>(a, bh, (c0 + 1) * BCH, ft, raw);
+  }
+  __syncthreads();
+  if (value_wave) prep(c0);
+
+  auto chunk = [&](int c, auto value_kind) {
+    constexpr bool VW = decltype(value_kind)::value;
+    const int t0 = c * BCH;
+    const int64_t tc = bh * int64_t(T) + t0;
+    const char* cur = smem + (c & 1) * L::BUF;
+    const float* F = reinterpret_cast<const float*>(cur + L::FB);
+    const bool vt = t0 + n < T;
+
+    if constexpr (VW) {
+      // ---- phase 1: the numerator^T (rows j of block wb, columns t):
+      // e^{l_t} S^T phi(q) + V^T P, with S from the registers (contracting
+      // over f) against phi(q) stored with its features permuted
+      f32x16 nu = zero16();
+#pragma unroll
+      for (int fb = 0; fb < NJ; ++fb) {
+        u32x4 sh[2], sl[2], bq[2], bql[2];
+        split_acc(X[fb], sh, sl);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          bq[ks] = row_operand<D>(cur + L::Q, perm_pos(n), 2 * (2 * fb + ks) + g);
+          if constexpr (!XQ) bql[ks] = row_operand<D>(cur + L::QL, perm_pos(n), 2 * (2 * fb + ks) + g);
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          nu = mfma(sh[ks], bq[ks], nu);
+          nu = mfma(sl[ks], bq[ks], nu);
+          if constexpr (!XQ) nu = mfma(sh[ks], bql[ks], nu);
+        }
+      }
+      if constexpr (DECAY != 0) nu *= pr.eq;
+      {
+        u32x4 ov[2];
+        tr_ops<D, 2>(cur + L::V, 32 * wb, lane, ov);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          nu = mfma(ov[ks], pr.ph[ks], nu);
+          nu = mfma(ov[ks], pr.pl[ks], nu);
+        }
+      }
+
+      // g = r_t dout into the shared tiles (feature j at perm_pos(j): the
+      // values of r = 2 h2, 2 h2 + 1 fill one block), with a decay also
+      // e^{L + l_t} g for the gradient-state fold; dout . o partials
+      const float rt = vt ? pr.rt : 0.f;
+      const float wg = DECAY ? __expf(Lseg) * pr.eq : 1.f;
+      float hp = 0.f;
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        u32x4 gh, gl, wh, wl;
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) {
+          const int r = 2 * h2 + rr;
+          const f32x4 d4 = dout4<DF32>(dreg, r);
+          float gv[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            hp += d4[e] * nu[4 * r + e];
+            gv[e] = d4[e] * rt;
+          }
+          uint32_t h0, h1, l0, l1;
+          split_bf16(gv[0], gv[1], h0, l0);
+          split_bf16(gv[2], gv[3], h1, l1);
+          gh[2 * rr] = h0;
+          gh[2 * rr + 1] = h1;
+          gl[2 * rr] = l0;
+          gl[2 * rr + 1] = l1;
+          if constexpr (DECAY != 0) {
+            split_bf16(gv[0] * wg, gv[1] * wg, h0, l0);
+            split_bf16(gv[2] * wg, gv[3] * wg, h1, l1);
+            wh[2 * rr] = h0;
+            wh[2 * rr + 1] = h1;
+            wl[2 * rr] = l0;
+            wl[2 * rr + 1] = l1;
+          }
+        }
+        const int off = tile_off<D>(perm_pos(n), 4 * wb + 2 * h2 + g);
+        *reinterpret_cast<u32x4*>(smem + L::G + off) = gh;
+        *reinterpret_cast<u32x4*>(smem + L::GL + off) = gl;
+        if constexpr (DECAY != 0) {
+          *reinterpret_cast<u32x4*>(smem + L::WG + off) = wh;
+          *reinterpret_cast<u32x4*>(smem + L::WGL + off) = wl;
+        }
+      }
+      hp = swap_sum32(hp * pr.rt);
+      if (g == 0) Sc[L::HP + wb * BCH + n] = hp;
+      if (wb == 0 && g == 0) {
+        Sc[L::RT + n] = pr.rt;
+        Sc[L::HF + n] = pr.hf;
+      }
+
+      // the fold, after the numerator's reads of S: S (rows f, columns j of
+      // block wb) = e^{l_last} S + (w phi(K))^T V
+      const float tot = DECAY ? F[L::TOT] : 0.f;
+      {
+        const float ec = DECAY ? __expf(tot) : 1.f;
+        u32x4 bv[2];
+        tr_ops<D, 2>(cur + L::V, 32 * wb, lane, bv);
+#pragma unroll
+        for (int fb = 0; fb < NJ; ++fb) {
+          u32x4 aw[2], awl[2];
+          tr_ops<D, 2>(cur + WA, 32 * fb, lane, aw);
+          tr_ops<D, 2>(cur + WB, 32 * fb, lane, awl);
+          if constexpr (DECAY != 0) X[fb] *= ec;
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            X[fb] = mfma(aw[ks], bv[ks], X[fb]);
+            X[fb] = mfma(awl[ks], bv[ks], X[fb]);
+          }
+        }
+      }
+      __syncthreads();   // g tiles and partials; the next chunk staged
+
+      // ---- phase 2: the next chunk's dout; the segment's gradient state,
+      // G_seg^T += (e^{L + l} g)^T phi(Q), and gz_seg += sum_t e^{L + l_t}
+      // h_t phi(q_t); the next chunk's scores and read-out factor
+      const bool more = c + 1 < c1;
+      if (more) load_dout3<D, DF32>(a, bh, t0 + BCH, wb, n, g, dreg);
+      {
+        constexpr int GA = DECAY ? L::WG : L::G, GB = DECAY ? L::WGL : L::GL;
+        u32x4 ag[2], agl[2];
+        tr_ops<D, 2>(smem + GA, 32 * wb, lane, ag);
+        tr_ops<D, 2>(smem + GB, 32 * wb, lane, agl);
+#pragma unroll
+        for (int fb = 0; fb < NJ; ++fb) {
+          u32x4 bq[2], bql[2];
+          tr_ops<D, 2>(cur + L::Q, 32 * fb, lane, bq);
+          if constexpr (!XQ) tr_ops<D, 2>(cur + L::QL, 32 * fb, lane, bql);
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            Gs[fb] = mfma(ag[ks], bq[ks], Gs[fb]);
+            Gs[fb] = mfma(agl[ks], bq[ks], Gs[fb]);
+            if constexpr (!XQ) Gs[fb] = mfma(ag[ks], bql[ks], Gs[fb]);
+          }
+        }
+      }
+      {
+        const float eL = DECAY ? __expf(Lseg) : 1.f;
+        const int r0 = tid / L::BPR, b = tid % L::BPR;
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) {
+          const int r = r0 + 16 * rr;
+          float dot = 0.f;
+#pragma unroll
+          for (int ww = 0; ww < NJ; ++ww) dot += Sc[L::HP + ww * BCH + r];
+          float ht = t0 + r < T ? Sc[L::HF + r] * dot : 0.f;
+          if constexpr (DECAY != 0) ht *= eL * __expf(F[L::LAM + r]);
+          float x[8];
+          hilo8<D, XQ>(cur + L::Q, cur + L::QL, perm_pos(r), b, x);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) gzp[e] += x[e] * ht;
+        }
+      }
+      if (more) prep(c + 1);
+      Lseg += tot;
+      __syncthreads();   // every read of chunk c's buffer and of g done
+    } else {
+      // ---- phase 1: the previous chunk's <phi(q), dphi(q)>, and the next
+      // chunk staged into the other buffer (the staging addresses come from
+      // an opaque copy of the thread index: held across the loop, they would
+      // not fit the registers of two waves per SIMD)
+      if constexpr (DECAY != 0) {
+        if (wb == 0 && c > c0 && lane < BCH && t0 - BCH + lane < T) {
+          float s = 0.f;
+#pragma unroll
+          for (int ww = 0; ww < NJ; ++ww) s += Sc[L::QP + ww * BCH + lane];
+          a.qd[tc - BCH + lane] = s;
+        }
+      }
+      if (c + 1 < c1) {
+        int fs = ft;
+        asm volatile("" : "+v"(fs));
+        stage3<D, DECAY>(a, bh, t0 + BCH, fs, raw, smem + ((c + 1) & 1) * L::BUF, cur,
+                         Sc + L::Z + (c & 1) * D, Sc + L::Z + ((c + 1) & 1) * D, false, zs, mst);
+        if (c + 2 < c1) load_raw3<D, DECAY>(a, bh, t0 + 2 * BCH, fs, raw);
+      }
+      __syncthreads();   // g tiles and partials; the next chunk staged
+
+      // ---- phase 2: h_t, B, dphi(q), the fold
+      const float lt = DECAY ? F[L::LAM + n] : 0.f;   // token n's log-prefix
+      const float eq = DECAY ? __expf(lt) : 1.f;
+      float dot = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < NJ; ++ww) dot += Sc[L::HP + ww * BCH + n];
+      const float h = vt ? Sc[L::HF + n] * dot : 0.f;
+      if (wb == 0 && g == 0 && vt)
+        *reinterpret_cast<float2*>(a.tok + (tc + n) * 2) = make_float2(Sc[L::RT + n], h);
+
+      // B (rows s, columns t = n): (v_s . g_t + h_t) beta_s e^{l_t - l_s}
+      f32x16 bs = zero16();
+#pragma unroll
+      for (int k0 = 0; k0 < KS; k0 += 2) {
+        u32x4 ov[2], gh[2], gl[2];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          ov[kk] = row_operand_perm<D>(cur + L::V, perm_pos(n), k0 + kk, g);
+          gh[kk] = row_operand<D>(smem + L::G, perm_pos(n), 2 * (k0 + kk) + g);
+          gl[kk] = row_operand<D>(smem + L::GL, perm_pos(n), 2 * (k0 + kk) + g);
+        }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          bs = mfma(ov[kk], gh[kk], bs);
+          bs = mfma(ov[kk], gl[kk], bs);
+        }
+      }
+      {
+        float wt[16];
+        causal_weights_st<DECAY>(F, L::LAM, L::BET, lt, g, n, wt);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) bs[i] = (bs[i] + h) * wt[i];
+      }
+      u32x4 bh_[2], bl_[2];
+      split_acc(bs, bh_, bl_);
+
+      // dphi(q)^T (rows f of block wb, columns t): e^{l_t} (S g + z h) +
+      // phi(K)^T B, with S^T from the registers (contracting over j)
+      f32x16 dqt = zero16();
+#pragma unroll
+      for (int jb = 0; jb < NJ; ++jb) {
+        u32x4 sh[2], sl[2], gh[2], gl[2];
+        split_acc(X[jb], sh, sl);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          gh[ks] = row_operand<D>(smem + L::G, perm_pos(n), 2 * (2 * jb + ks) + g);
+          gl[ks] = row_operand<D>(smem + L::GL, perm_pos(n), 2 * (2 * jb + ks) + g);
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          dqt = mfma(sh[ks], gh[ks], dqt);
+          dqt = mfma(sl[ks], gh[ks], dqt);
+          dqt = mfma(sh[ks], gl[ks], dqt);
+        }
+      }
+      if constexpr (DECAY != 0) dqt *= eq;
+      {
+        u32x4 okt[2], oklt[2];
+        tr_ops<D, 2>(cur + L::K, 32 * wb, lane, okt);
+        if constexpr (!XQ) tr_ops<D, 2>(cur + L::KL, 32 * wb, lane, oklt);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          dqt = mfma(okt[ks], bh_[ks], dqt);
+          dqt = mfma(okt[ks], bl_[ks], dqt);
+          if constexpr (!XQ) dqt = mfma(oklt[ks], bh_[ks], dqt);
+        }
+      }
+      // the fold, issued before dphi(q)'s epilogue (its VALU work meets
+      // these MFMAs): S^T (rows j, columns f of block wb) = e^{l_last} S^T +
+      // V^T (w phi(K))
+      const float ec = DECAY ? __expf(F[L::TOT]) : 1.f;
+      u32x4 bw[2], bwl[2];
+      tr_ops<D, 2>(cur + WA, 32 * wb, lane, bw);
+      tr_ops<D, 2>(cur + WB, 32 * wb, lane, bwl);
+#pragma unroll
+      for (int jb = 0; jb < NJ; ++jb) {
+        u32x4 av[2];
+        tr_ops<D, 2>(cur + L::V, 32 * jb, lane, av);
+        if constexpr (DECAY != 0) X[jb] *= ec;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          X[jb] = mfma(av[ks], bw[ks], X[jb]);
+          X[jb] = mfma(av[ks], bwl[ks], X[jb]);
+        }
+      }
+      {
+        float qdp = 0.f;   // <phi(q_t), dphi(q_t)> over this lane's features
+        const float* zc = Sc + L::Z + (c & 1) * D;
+        float* dst = a.dq + tc * D + uint32_t(n * D + 32 * wb + 4 * g);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int pc = perm_pos(32 * wb + 8 * r + 4 * g);   // stored column of these 4 features
+          const int off = tile_off<D>(perm_pos(n), pc >> 3) + ((pc & 7) << 1);
+          const f32x4 p4 = hilo4<XQ>(cur + L::Q, cur + L::QL, off);
+          const f32x4 z4 = *reinterpret_cast<const f32x4*>(zc + 32 * wb + 8 * r + 4 * g);
+          f32x4 o4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float dphi = dqt[4 * r + e] + eq * z4[e] * h;
+            // elu+1 has slope 1 above 0 and e^x = phi(x) below: min(phi, 1);
+            // identity features (mLSTM): 1
+            o4[e] = XQ ? dphi : dphi * fminf(p4[e], 1.f);
+            qdp += p4[e] * dphi;
+          }
+          if (vt) *reinterpret_cast<f32x4*>(dst + 8 * r) = o4;
+        }
+        if constexpr (DECAY != 0) {
+          qdp = swap_sum32(qdp);
+          if (g == 0) Sc[L::QP + wb * BCH + n] = qdp;
+        }
+      }
+
+      __syncthreads();   // every read of chunk c's buffer and of g done
+    }
+  };
+  if (value_wave)
+    for (int c = c0; c < c1; ++c) chunk(c, std::true_type{});
+  else
+    for (int c = c0; c < c1; ++c) chunk(c, std::false_type{});
+
+  // the segment's gradient state into its slot: G_seg (rows f, columns j),
+  // gz_seg, the segment's total log-decay
+  float* dst = a.gslot + (bh * a.nseg + seg) * int64_t(D * D + D);
+  float* gzw = reinterpret_cast<float*>(smem + L::FB) + L::ZP;   // [NJ][D], free now
+  if (value_wave) {
+#pragma unroll
+    for (int fb = 0; fb < NJ; ++fb) {
+      const int f = perm_pos(32 * fb + n);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        *reinterpret_cast<f32x4*>(dst + f * D + perm_pos(32 * wb + 8 * r + 4 * g)) =
+            f32x4{Gs[fb][4 * r], Gs[fb][4 * r + 1], Gs[fb][4 * r + 2], Gs[fb][4 * r + 3]};
+    }
+    wave_rows_sum8<L::BPR>(gzp, lane, gzw + wb * D);
+    if (DECAY != 0 && tid == 0) a.lgam[bh * a.nseg + seg] = Lseg;
+  }
+  __syncthreads();
+  if (tid < D) {
+    float s = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < NJ; ++ww) s += gzw[ww * D + tid];
+    dst[D * D + perm_pos(tid)] = s;
+  }
+
+  // the last chunk's <phi(q), dphi(q)>
+  if constexpr (DECAY != 0) {
+    const int tl = (c1 - 1) * BCH + lane;
+    if (w == NJ && lane < BCH && tl < T) {
+      float s = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < NJ; ++ww) s += Sc[L::QP + ww * BCH + lane];
+      a.qd[bh * int64_t(T) + tl] = s;
+    }
+  }
+}
+
 // ----------------------------------------------------- decay gradient
 
 // dL/dlog alpha_r = R_r = sum_{t >= r} (qd_t - beta_t kd_t), then dL/da_r =
@@ -1505,7 +1615,8 @@ template <int D, int DECAY>
 hipError_t launch_d(const Problem& pb, const BwArgs& a, float* dS0, float* dz0, float* ddecay,
                     hipStream_t st) {
   const unsigned nwg = unsigned(pb.BH() * a.nseg);
-  bwd_pass_a<D, DECAY><<<dim3(nwg), dim3(64 * (D / 32)), 0, st>>>(a);
+  if (a.dout_f32) bwd_pass_a2<D, DECAY, true><<<dim3(nwg), dim3(128 * (D / 32)), 0, st>>>(a);
+  else bwd_pass_a2<D, DECAY, false><<<dim3(nwg), dim3(128 * (D / 32)), 0, st>>>(a);
   constexpr int PER = (D * D + D + 255) / 256;
   bwd_rscan<D, DECAY != 0><<<dim3(unsigned(pb.BH() * PER)), dim3(256), 0, st>>>(
       a.gslot, a.lgam, a.nseg, dS0, dz0);
