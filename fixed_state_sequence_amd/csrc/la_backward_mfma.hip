@@ -118,6 +118,15 @@ struct BwArgs {
   float eps;
 };
 
+// This lane's index within its wave (0..63), formed anew where it is used:
+// a value the compiler cannot move out of a loop, so the addresses derived
+// from it are not held (and spilled) across the loop.
+__device__ __forceinline__ int lane_fresh() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 __device__ __forceinline__ f32x16 zero16() {
   f32x16 x;
 #pragma unroll
@@ -1068,6 +1077,7 @@ __global__ __launch_bounds__(128 * (D / 32)) void bwd_pass_a2(const BwArgs a) {
   }
   const float* zs = a.z0 ? a.z0 + bh * a.z_bh + int64_t(seg) * a.s_seg : nullptr;
   const int ft = tid - 64 * NJ;   // index among the feature waves' threads
+  const int wsg = __builtin_amdgcn_readfirstlane(w);   // the wave index, in a scalar register
   float mst = 0.f;                // mLSTM: the stabiliser before the chunk staged next
   if constexpr (DECAY == 3) mst = a.m0 ? a.m0[bh * a.m0_bh + seg] : 0.f;
   Raw3 raw;
@@ -1273,13 +1283,9 @@ __global__ __launch_bounds__(128 * (D / 32)) void bwd_pass_a2(const BwArgs a) {
           }
         }
       }
-      __syncthreads();   // g tiles and partials; the next chunk staged
-
-      // ---- phase 2: the next chunk's dout; the segment's gradient state,
-      // G_seg^T += (e^{L + l} g)^T phi(Q), and gz_seg += sum_t e^{L + l_t}
-      // h_t phi(q_t); the next chunk's scores and read-out factor
-      const bool more = c + 1 < c1;
-      if (more) load_dout3<D, DF32>(a, bh, t0 + BCH, wb, n, g, dreg);
+      // the segment's gradient state, G_seg^T += (e^{L + l} g)^T phi(Q): the
+      // columns j of this wave's block are the ones it wrote (a wave's LDS
+      // accesses complete in order, so no barrier is needed)
       {
         constexpr int GA = DECAY ? L::WG : L::G, GB = DECAY ? L::WGL : L::GL;
         u32x4 ag[2], agl[2];
@@ -1298,6 +1304,12 @@ __global__ __launch_bounds__(128 * (D / 32)) void bwd_pass_a2(const BwArgs a) {
           }
         }
       }
+      __syncthreads();   // g tiles and partials; the next chunk staged
+
+      // ---- phase 2: the next chunk's dout; gz_seg += sum_t e^{L + l_t} h_t
+      // phi(q_t); the next chunk's scores and read-out factor
+      const bool more = c + 1 < c1;
+      if (more) load_dout3<D, DF32>(a, bh, t0 + BCH, wb, n, g, dreg);
       {
         const float eL = DECAY ? __expf(Lseg) : 1.f;
         const int r0 = tid / L::BPR, b = tid % L::BPR;
@@ -1320,9 +1332,10 @@ __global__ __launch_bounds__(128 * (D / 32)) void bwd_pass_a2(const BwArgs a) {
       __syncthreads();   // every read of chunk c's buffer and of g done
     } else {
       // ---- phase 1: the previous chunk's <phi(q), dphi(q)>, and the next
-      // chunk staged into the other buffer (the staging addresses come from
-      // an opaque copy of the thread index: held across the loop, they would
-      // not fit the registers of two waves per SIMD)
+      // chunk staged into the other buffer (its addresses formed from a
+      // fresh lane index: held across the loop, they would not fit the
+      // registers of two waves per SIMD, and a reload of a spilled one waits
+      // for every store and prefetch in flight)
       if constexpr (DECAY != 0) {
         if (wb == 0 && c > c0 && lane < BCH && t0 - BCH + lane < T) {
           float s = 0.f;
@@ -1332,8 +1345,7 @@ __global__ __launch_bounds__(128 * (D / 32)) void bwd_pass_a2(const BwArgs a) {
         }
       }
       if (c + 1 < c1) {
-        int fs = ft;
-        asm volatile("" : "+v"(fs));
+        const int fs = 64 * (wsg - NJ) + lane_fresh();
         stage3<D, DECAY>(a, bh, t0 + BCH, fs, raw, smem + ((c + 1) & 1) * L::BUF, cur,
                          Sc + L::Z + (c & 1) * D, Sc + L::Z + ((c + 1) & 1) * D, false, zs, mst);
         if (c + 2 < c1) load_raw3<D, DECAY>(a, bh, t0 + 2 * BCH, fs, raw);
@@ -1426,6 +1438,8 @@ __global__ __launch_bounds__(128 * (D / 32)) void bwd_pass_a2(const BwArgs a) {
         }
       }
       {
+        // the epilogue's addresses from a fresh lane index (as the staging's)
+        const int le = lane_fresh(), n = le & 31, g = le >> 5;
         float qdp = 0.f;   // <phi(q_t), dphi(q_t)> over this lane's features
         const float* zc = Sc + L::Z + (c & 1) * D;
         float* dst = a.dq + tc * D + uint32_t(n * D + 32 * wb + 4 * g);
