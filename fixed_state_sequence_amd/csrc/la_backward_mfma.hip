@@ -1218,6 +1218,7 @@ __global__ __launch_bounds__(128 * (D / 32)) void bwd_pass_a2(const BwArgs a) {
       // e^{L + l_t} g for the gradient-state fold; dout . o partials
       const float rt = vt ? pr.rt : 0.f;
       const float wg = DECAY ? __expf(Lseg) * pr.eq : 1.f;
+      const int lg = lane_fresh(), ng = lg & 31, gg = lg >> 5;   // the tile offsets' lane
       float hp = 0.f;
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
@@ -1248,7 +1249,7 @@ __global__ __launch_bounds__(128 * (D / 32)) void bwd_pass_a2(const BwArgs a) {
             wl[2 * rr + 1] = l1;
           }
         }
-        const int off = tile_off<D>(perm_pos(n), 4 * wb + 2 * h2 + g);
+        const int off = tile_off<D>(perm_pos(ng), 4 * wb + 2 * h2 + gg);
         *reinterpret_cast<u32x4*>(smem + L::G + off) = gh;
         *reinterpret_cast<u32x4*>(smem + L::GL + off) = gl;
         if constexpr (DECAY != 0) {
