@@ -394,8 +394,9 @@ __device__ __forceinline__ void load_raw2(const BwArgs& a, int64_t bh, int t0, i
 
 // Stage one chunk into buffer buf: phi(q) (high, low), phi(k) (high, low, at
 // permuted feature positions), v, g = r_t dout (high, low; with a decay also
-// e^{l_t} g), and the per-token scalars.  Rows past the end are zero.
-template <int D, int DECAY, bool DF32>
+// e^{l_t} g), and the per-token scalars.  Rows past the end are zero (FULL:
+// the chunk lies wholly inside the sequence, and no row is tested).
+template <int D, int DECAY, bool DF32, bool FULL = false>
 __device__ __forceinline__ void stage2(const BwArgs& a, int t0, int tid, const Raw2& x, char* buf) {
   using L = BL2<D, DECAY>;
   float* F = reinterpret_cast<float*>(buf + L::FB);
@@ -420,7 +421,7 @@ __device__ __forceinline__ void stage2(const BwArgs& a, int t0, int tid, const R
     F[L::BET + tid] = bet;
     if (tid == 0) F[L::TOT] = tot;
   }
-  const bool valid = t0 + r < a.T;
+  const bool valid = FULL || t0 + r < a.T;
   const int pr = perm_pos(r);
   float lr = 0.f;
   if constexpr (DECAY != 0) lr = __shfl(lam, r);
@@ -545,7 +546,7 @@ __global__ __launch_bounds__(128 * (D / 32)) void bwd_pass_b2(const BwArgs a) {
         // they would not fit the registers of two waves per SIMD
         int ts = tid;
         asm volatile("" : "+v"(ts));
-        stage2<D, DECAY, DF32>(a, t0 - BCH, ts, raw, nxt);
+        stage2<D, DECAY, DF32, true>(a, t0 - BCH, ts, raw, nxt);   // every chunk but the last is whole
         if (c - 2 >= c0) load_raw2<D, DECAY, DF32>(a, bh, t0 - 2 * BCH, ts, raw);
       }
     };
@@ -973,49 +974,55 @@ __device__ __forceinline__ void stage3(const BwArgs& a, int64_t bh, int t0, int 
   float inc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) inc[e] = 0.f;
+  // the rows; a chunk wholly inside the sequence takes no validity selects
+  auto rows = [&](auto full_kind) {
+    constexpr bool FULL = decltype(full_kind)::value;
 #pragma unroll
-  for (int rr = 0; rr < 2; ++rr) {
-    const int r = r0 + 16 * rr;
-    const bool valid = t0 + r < a.T;
-    const int pr = perm_pos(r);
-    float lr = 0.f, br = 1.f;   // this row's log-prefix and beta
-    if constexpr (DECAY != 0) {
-      lr = __shfl(lam, r);
-      br = __shfl(bet, r);
-    }
-    float fq[8], fk[8];
-    unpack8(x.q[rr], fq, bf16_t{});
-    unpack8(x.k[rr], fk, bf16_t{});
+    for (int rr = 0; rr < 2; ++rr) {
+      const int r = r0 + 16 * rr;
+      const bool valid = FULL || t0 + r < a.T;
+      const int pr = perm_pos(r);
+      float lr = 0.f, br = 1.f;   // this row's log-prefix and beta
+      if constexpr (DECAY != 0) {
+        lr = __shfl(lam, r);
+        br = __shfl(bet, r);
+      }
+      float fq[8], fk[8];
+      unpack8(x.q[rr], fq, bf16_t{});
+      unpack8(x.k[rr], fk, bf16_t{});
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      fq[e] = valid ? (DECAY == 3 ? fq[e] : elu1_fast(fq[e])) : 0.f;
-      fk[e] = valid ? (DECAY == 3 ? fk[e] : elu1_fast(fk[e])) : 0.f;
-    }
-    const u32x4 qh = pack8(fq);
-    row_write_perm<D>(buf + L::Q, pr, b, qh);
-    if constexpr (!L::XQ) row_write_perm<D>(buf + L::QL, pr, b, low8(fq, qh));
-    const u32x4 kh = pack8(fk);
-    blk_write<D>(buf + L::K, pr, b, kh);
-    if constexpr (!L::XQ) blk_write<D>(buf + L::KL, pr, b, low8(fk, kh));
-    blk_write<D>(buf + L::V, pr, b, valid ? x.v[rr] : u32x4{0u, 0u, 0u, 0u});
-    const float wk = DECAY ? br * __expf(tot - lr) : 1.f;   // key weight to the chunk's end
-    float part = 0.f;
+      for (int e = 0; e < 8; ++e) {
+        fq[e] = valid ? (DECAY == 3 ? fq[e] : elu1_fast(fq[e])) : 0.f;
+        fk[e] = valid ? (DECAY == 3 ? fk[e] : elu1_fast(fk[e])) : 0.f;
+      }
+      const u32x4 qh = pack8(fq);
+      row_write_perm<D>(buf + L::Q, pr, b, qh);
+      if constexpr (!L::XQ) row_write_perm<D>(buf + L::QL, pr, b, low8(fq, qh));
+      const u32x4 kh = pack8(fk);
+      blk_write<D>(buf + L::K, pr, b, kh);
+      if constexpr (!L::XQ) blk_write<D>(buf + L::KL, pr, b, low8(fk, kh));
+      blk_write<D>(buf + L::V, pr, b, valid ? x.v[rr] : u32x4{0u, 0u, 0u, 0u});
+      const float wk = DECAY ? br * __expf(tot - lr) : 1.f;   // key weight to the chunk's end
+      float part = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      part += fq[e] * z[e];
-      inc[e] += wk * fk[e];
-    }
-    if constexpr (L::WT) {
-      float wv[8];
+      for (int e = 0; e < 8; ++e) {
+        part += fq[e] * z[e];
+        inc[e] += wk * fk[e];
+      }
+      if constexpr (L::WT) {
+        float wv[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) wv[e] = wk * fk[e];
-      const u32x4 wh = pack8(wv);
-      blk_write<D>(buf + L::WK, pr, b, wh);
-      blk_write<D>(buf + L::WKL, pr, b, low8(wv, wh));
+        for (int e = 0; e < 8; ++e) wv[e] = wk * fk[e];
+        const u32x4 wh = pack8(wv);
+        blk_write<D>(buf + L::WK, pr, b, wh);
+        blk_write<D>(buf + L::WKL, pr, b, low8(wv, wh));
+      }
+      part = row_sum<L::BPR>(part);
+      if (b == 0) F[L::DI + r] = part;
     }
-    part = row_sum<L::BPR>(part);
-    if (b == 0) F[L::DI + r] = part;
-  }
+  };
+  if (t0 + BCH <= a.T) rows(std::true_type{});
+  else rows(std::false_type{});
   wave_rows_sum8<L::BPR>(inc, lane, F + L::ZP + fw * D);
 }
 
