@@ -451,6 +451,45 @@ def mfma_sweep(torch):
                   f"{r:.0f} TFLOP/s", flush=True)
 
 
+def issue_probe(torch, nblocks=256, mf_iters=20000, va_iters=10000, reps=5):
+    """libla_probe.so's issue-overlap probe (one 8-wave workgroup per compute
+    unit, waves w and w + 4 on one SIMD): ms per launch of MFMA waves alone
+    (2 chains x mf_iters v_mfma_f32_32x32x16_bf16 each), one VALU wave per
+    SIMD (32 chains x va_iters fp32 FMAs), two VALU waves per SIMD (twice the
+    VALU work), and one MFMA plus one VALU wave per SIMD (printed)."""
+    lib = _probe_lib()
+    if lib is None:
+        print("libla_probe.so is not built", flush=True)
+        return None
+    lib.la_probe_issue.restype = ctypes.c_int
+    lib.la_probe_issue.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_void_p, ctypes.c_void_p]
+    dev = torch.device("cuda:0")
+    sink = torch.empty(nblocks * 512, dtype=torch.float32, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    ms = {}
+    for mode in (0, 1, 2, 3):
+        call = lambda: lib.la_probe_issue(mode, nblocks, mf_iters, va_iters,
+                                          ctypes.c_void_p(sink.data_ptr()), stream)
+        if call() != 0:
+            return None
+        torch.cuda.synchronize()
+        e0, e1 = _events(torch)
+        e0.record()
+        for _ in range(reps):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        ms[mode] = e0.elapsed_time(e1) / reps
+    print(f"MFMA waves alone (one per SIMD, {2 * mf_iters} MFMAs each): {ms[0]:.3f} ms", flush=True)
+    print(f"one VALU wave per SIMD ({32 * va_iters} FMAs each): {ms[1]:.3f} ms", flush=True)
+    print(f"two VALU waves per SIMD (twice the work): {ms[2]:.3f} ms = {ms[2] / ms[1]:.2f} x one wave's",
+          flush=True)
+    print(f"one MFMA and one VALU wave per SIMD: {ms[3]:.3f} ms = {ms[3] / ms[1]:.2f} x the VALU wave "
+          f"alone, {ms[3] / (ms[0] + ms[1]):.2f} x the two alone in turn", flush=True)
+    return ms
+
+
 def hbm_copy(torch, nbytes=1 << 30, reps=10):
     """Device-to-device streaming of `nbytes` (read + write) by two kernels,
     torch's copy and its vectorised negation (16 bytes per lane, like the
@@ -556,6 +595,8 @@ def main(argv=None):
                     help="prefill chunk length (0: the library's default plan)")
     ap.add_argument("--prefill-only", action="store_true",
                     help="time the long-context prefill alone (no variants, backward, decode)")
+    ap.add_argument("--issue-probe", action="store_true",
+                    help="time the VALU/MFMA issue-overlap probe (libla_probe.so) and exit")
     ap.add_argument("--mfma-sweep", action="store_true",
                     help="only sweep the MFMA peak probe (shapes, chains, workgroups) and exit")
     ap.add_argument("--config", default=None,
@@ -571,7 +612,7 @@ def main(argv=None):
         return 2
 
     cpu = None
-    if not (a.no_cpu_baseline or a.prefill_only or a.config or a.mfma_sweep):
+    if not (a.no_cpu_baseline or a.prefill_only or a.config or a.mfma_sweep or a.issue_probe):
         print(f"[bench] cpu baseline: oracle on {a.cpu_tokens} tokens x {PF['H']} heads",
               file=sys.stderr, flush=True)
         cpu = cpu_baseline(a.cpu_tokens)
@@ -583,6 +624,9 @@ def main(argv=None):
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
     la._lib.lib()
+    if a.issue_probe:
+        issue_probe(torch)
+        return 0
     if a.mfma_sweep:
         mfma_sweep(torch)
         return 0
