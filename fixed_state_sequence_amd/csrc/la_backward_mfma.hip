@@ -218,13 +218,18 @@ __device__ __forceinline__ void chunk_decay(float alpha, int t0, int T, int lane
     la = fmaxf(__logf(alpha), kLogFloorB);
     bet = DECAY == 2 ? 1.f - alpha : 1.f;
   }
-  lam = la;
-#pragma unroll
-  for (int off = 1; off < 32; off <<= 1) {
-    const float y = __shfl_up(lam, off, 32);
-    if ((lane & 31) >= off) lam += y;
-  }
-  tot = __shfl(lam, 31, 32);
+  lam = wave_scan<32>(la, 0.f, ScanAdd{});
+  tot = lane_bcast(lam, 31);
+}
+
+// One step of a prefix over the maps x -> max(x + A, B): the map of the lane
+// that the DPP control CTRL reaches (the identity (0, -1e30) where none) is
+// composed before this lane's.
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ void maxplus_step(float& A, float& B) {
+  const float Ap = dpp_or<CTRL, ROWS>(A, 0.f), Bp = dpp_or<CTRL, ROWS>(B, -1e30f);
+  B = fmaxf(Bp + A, B);
+  A = Ap + A;
 }
 
 // The mLSTM gates of one chunk in the stabilised frame, computed by every
@@ -243,27 +248,20 @@ __device__ __forceinline__ void chunk_decay_ml(float fpre, float ipre, int fexp,
   const bool valid = t0 + l < T;
   const float lf = valid ? log_forget(fpre, fexp) : 0.f;
   float A = lf, B = valid ? ipre : -1e30f;
-#pragma unroll
-  for (int off = 1; off < 32; off <<= 1) {
-    const float Ap = __shfl_up(A, off, 32), Bp = __shfl_up(B, off, 32);
-    if (l >= off) {
-      B = fmaxf(Bp + A, B);
-      A = Ap + A;
-    }
-  }
+  // the prefix over lanes 0-31 (and 32-63 alike) in the steps of wave_scan
+  maxplus_step<0x111>(A, B);
+  maxplus_step<0x112>(A, B);
+  maxplus_step<0x114>(A, B);
+  maxplus_step<0x118>(A, B);
+  maxplus_step<0x142, 0xA>(A, B);
   mt = fmaxf(mst + A, B);
-  float mp = __shfl_up(mt, 1, 32);
+  float mp = dpp_or<0x138>(mt, mst);   // wave_shr:1, the previous token's m
   if (l == 0) mp = mst;
   la = valid ? fmaxf(lf + mp - mt, kLogFloorB) : 0.f;
   bet = valid ? __expf(ipre - mt) : 0.f;
-  lam = la;
-#pragma unroll
-  for (int off = 1; off < 32; off <<= 1) {
-    const float y = __shfl_up(lam, off, 32);
-    if (l >= off) lam += y;
-  }
-  tot = __shfl(lam, 31, 32);
-  mst = __shfl(mt, 31, 32);
+  lam = wave_scan<32>(la, 0.f, ScanAdd{});
+  tot = lane_bcast(lam, 31);
+  mst = lane_bcast(mt, 31);
 }
 
 // ------------------------------------------------------------ reverse scan
@@ -405,14 +403,9 @@ __device__ __forceinline__ void stage2(const BwArgs& a, int t0, int tid, const R
   if constexpr (DECAY == 3) {
     // log alpha' and beta' as pass A left them
     const bool vt = t0 + (lane & 31) < a.T;
-    lam = vt ? x.al.x : 0.f;
+    lam = wave_scan<32>(vt ? x.al.x : 0.f, 0.f, ScanAdd{});
     bet = vt ? x.al.y : 0.f;
-#pragma unroll
-    for (int off = 1; off < 32; off <<= 1) {
-      const float y = __shfl_up(lam, off, 32);
-      if ((lane & 31) >= off) lam += y;
-    }
-    tot = __shfl(lam, 31, 32);
+    tot = lane_bcast(lam, 31);
   } else if constexpr (DECAY != 0) {
     chunk_decay<DECAY>(x.al.x, t0, a.T, lane, lam, bet, tot);
   }

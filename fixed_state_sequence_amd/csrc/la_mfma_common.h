@@ -254,6 +254,40 @@ __device__ __forceinline__ int reduce_scatter8(const float (&v)[8], int lane, fl
   return 4 * (lane >> 5) + 2 * ((lane >> 4) & 1);
 }
 
+// Inclusive scans over the lanes of a wave without LDS traffic (gfx9 DPP):
+// shifts by 1, 2, 4 and 8 lanes within each row of 16, then each row's last
+// lane carried into the next row by row broadcasts.  W = 32 scans lanes 0-31
+// and 32-63 separately, W = 64 the whole wave.  A lane whose shifted source
+// lies before its row's start, or a row left out of a broadcast, reads the
+// identity idn.
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ float dpp_or(float x, float idn) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, idn),
+                                                               __builtin_bit_cast(int, x), CTRL,
+                                                               ROWS, 0xF, false));
+}
+struct ScanAdd {
+  __device__ float operator()(float a, float b) const { return a + b; }
+};
+struct ScanMax {
+  __device__ float operator()(float a, float b) const { return fmaxf(a, b); }
+};
+template <int W, class Op>
+__device__ __forceinline__ float wave_scan(float x, float idn, Op op) {
+  static_assert(W == 32 || W == 64, "scan width");
+  x = op(x, dpp_or<0x111>(x, idn));        // row_shr:1
+  x = op(x, dpp_or<0x112>(x, idn));        // row_shr:2
+  x = op(x, dpp_or<0x114>(x, idn));        // row_shr:4
+  x = op(x, dpp_or<0x118>(x, idn));        // row_shr:8
+  x = op(x, dpp_or<0x142, 0xA>(x, idn));   // row_bcast:15 into rows 1 and 3
+  if constexpr (W == 64) x = op(x, dpp_or<0x143, 0xC>(x, idn));   // row_bcast:31 into rows 2, 3
+  return x;
+}
+// Lane l's value of x in every lane (v_readlane: a scalar result).
+__device__ __forceinline__ float lane_bcast(float x, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+}
+
 template <int FB>
 __device__ __forceinline__ float group_sum(float x) {
   if constexpr (FB == 8) x += dpp<0x128>(x);     // row_ror:8

@@ -297,20 +297,13 @@ __device__ __forceinline__ void chunk_logprefix(const float (&d)[ND], int lane, 
                                                 float& hi, float& total) {
   lo = IS_LOG ? d[0] : fmaxf(__logf(d[0]), kLogFloor);
   hi = ND > 1 ? (IS_LOG ? d[ND - 1] : fmaxf(__logf(d[ND - 1]), kLogFloor)) : 0.f;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const float a = __shfl_up(lo, off);
-    const float b = __shfl_up(hi, off);
-    if (lane >= off) {
-      lo += a;
-      hi += b;
-    }
-  }
+  (void)lane;
+  lo = wave_scan<C <= 32 ? 32 : 64>(lo, 0.f, ScanAdd{});
   if constexpr (C > 64) {
-    hi += __shfl(lo, 63);
-    total = __shfl(hi, 63);
+    hi = wave_scan<64>(hi, 0.f, ScanAdd{}) + lane_bcast(lo, 63);
+    total = lane_bcast(hi, 63);
   } else {
-    total = __shfl(lo, C - 1);
+    total = lane_bcast(lo, C - 1);
   }
 }
 
@@ -325,23 +318,14 @@ __device__ __forceinline__ void chunk_runmax(const float (&ig)[ND], float lo, fl
                                              float& mhi, float& mend) {
   alo = ig[0] - lo;
   ahi = ND > 1 ? ig[ND - 1] - hi : kNoToken;
-  mlo = alo;
-  mhi = ahi;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const float x = __shfl_up(mlo, off);
-    const float y = __shfl_up(mhi, off);
-    if (lane >= off) {
-      mlo = fmaxf(mlo, x);
-      mhi = fmaxf(mhi, y);
-    }
-  }
-  mlo = fmaxf(mlo, m0);
+  (void)lane;
+  mlo = fmaxf(wave_scan<C <= 32 ? 32 : 64>(alo, kNoToken, ScanMax{}), m0);
   if constexpr (C > 64) {
-    mhi = fmaxf(mhi, __shfl(mlo, 63));
-    mend = __shfl(mhi, 63);
+    mhi = fmaxf(wave_scan<64>(ahi, kNoToken, ScanMax{}), lane_bcast(mlo, 63));
+    mend = lane_bcast(mhi, 63);
   } else {
-    mend = __shfl(mlo, C - 1);
+    mhi = ahi;
+    mend = lane_bcast(mlo, C - 1);
   }
 }
 
@@ -437,9 +421,7 @@ void segment_state_kernel(const PfArgs a) {
       if constexpr (DECAY == 3) {
         alo = raw.ig[0] - lo;
         ahi = G::ND > 1 ? raw.ig[G::ND - 1] - hi : kNoToken;
-        float cm = fmaxf(alo, ahi);
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) cm = fmaxf(cm, __shfl_xor(cm, off));
+        const float cm = lane_bcast(wave_scan<64>(fmaxf(alo, ahi), kNoToken, ScanMax{}), 63);
         Mn = fmaxf(M, cm + lsuf + ltot);
         const float sc = __expf(M - Mn);
         if (live && sc != 1.f) {
