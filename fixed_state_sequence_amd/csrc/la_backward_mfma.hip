@@ -1363,6 +1363,28 @@ __global__ __launch_bounds__(128 * (D / 32)) void bwd_pass_a2(const BwArgs a) {
       if (wb == 0 && g == 0 && vt)
         *reinterpret_cast<float2*>(a.tok + (tc + n) * 2) = make_float2(Sc[L::RT + n], h);
 
+      // dphi(q)^T (rows f of block wb, columns t): e^{l_t} (S g + z h) +
+      // phi(K)^T B, with S^T from the registers (contracting over j); the
+      // S g products first, so that the state's split meets B's MFMAs
+      f32x16 dqt = zero16();
+#pragma unroll
+      for (int jb = 0; jb < NJ; ++jb) {
+        u32x4 sh[2], sl[2], gh[2], gl[2];
+        split_acc(X[jb], sh, sl);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          gh[ks] = row_operand<D>(smem + L::G, perm_pos(n), 2 * (2 * jb + ks) + g);
+          gl[ks] = row_operand<D>(smem + L::GL, perm_pos(n), 2 * (2 * jb + ks) + g);
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          dqt = mfma(sh[ks], gh[ks], dqt);
+          dqt = mfma(sl[ks], gh[ks], dqt);
+          dqt = mfma(sh[ks], gl[ks], dqt);
+        }
+      }
+      if constexpr (DECAY != 0) dqt *= eq;
+
       // B (rows s, columns t = n): (v_s . g_t + h_t) beta_s e^{l_t - l_s}
       f32x16 bs = zero16();
 #pragma unroll
@@ -1389,26 +1411,6 @@ __global__ __launch_bounds__(128 * (D / 32)) void bwd_pass_a2(const BwArgs a) {
       u32x4 bh_[2], bl_[2];
       split_acc(bs, bh_, bl_);
 
-      // dphi(q)^T (rows f of block wb, columns t): e^{l_t} (S g + z h) +
-      // phi(K)^T B, with S^T from the registers (contracting over j)
-      f32x16 dqt = zero16();
-#pragma unroll
-      for (int jb = 0; jb < NJ; ++jb) {
-        u32x4 sh[2], sl[2], gh[2], gl[2];
-        split_acc(X[jb], sh, sl);
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          gh[ks] = row_operand<D>(smem + L::G, perm_pos(n), 2 * (2 * jb + ks) + g);
-          gl[ks] = row_operand<D>(smem + L::GL, perm_pos(n), 2 * (2 * jb + ks) + g);
-        }
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          dqt = mfma(sh[ks], gh[ks], dqt);
-          dqt = mfma(sl[ks], gh[ks], dqt);
-          dqt = mfma(sh[ks], gl[ks], dqt);
-        }
-      }
-      if constexpr (DECAY != 0) dqt *= eq;
       {
         u32x4 okt[2], oklt[2];
         tr_ops<D, 2>(cur + L::K, 32 * wb, lane, okt);
