@@ -552,6 +552,29 @@ __global__ __launch_bounds__(128 * (D / 32)) void bwd_pass_b2(const BwArgs a) {
     constexpr int GA = DECAY ? L::WH : L::GH, GB = DECAY ? L::WL : L::GL;
 
     if constexpr (VW) {
+      // dv^T / beta_s (rows j of block wb, columns s): e^{l_last - l_s}
+      // G^T phi(k) + g^T A, with G from the registers (contracting over f);
+      // the G products first, so that the state's split meets the scores'
+      // MFMAs
+      f32x16 dvt = zero16();
+#pragma unroll
+      for (int fb = 0; fb < NJ; ++fb) {
+        u32x4 sh[2], sl[2], bk[2], bkl[2];
+        split_acc(X[fb], sh, sl);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          bk[ks] = row_operand<D>(cur + L::K, perm_pos(n), 2 * (2 * fb + ks) + g);
+          if constexpr (!XQ) bkl[ks] = row_operand<D>(cur + L::KL, perm_pos(n), 2 * (2 * fb + ks) + g);
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          dvt = mfma(sh[ks], bk[ks], dvt);
+          dvt = mfma(sl[ks], bk[ks], dvt);
+          if constexpr (!XQ) dvt = mfma(sh[ks], bkl[ks], dvt);
+        }
+      }
+      if constexpr (DECAY != 0) dvt *= es;
+
       // scores A (rows t, columns s = n): phi(q) at permuted feature
       // positions against phi(k) stored that way
       f32x16 at = zero16();
@@ -582,26 +605,6 @@ __global__ __launch_bounds__(128 * (D / 32)) void bwd_pass_b2(const BwArgs a) {
       u32x4 ah[2], al[2];
       split_acc(at, ah, al);
 
-      // dv^T / beta_s (rows j of block wb, columns s): e^{l_last - l_s}
-      // G^T phi(k) + g^T A, with G from the registers (contracting over f)
-      f32x16 dvt = zero16();
-#pragma unroll
-      for (int fb = 0; fb < NJ; ++fb) {
-        u32x4 sh[2], sl[2], bk[2], bkl[2];
-        split_acc(X[fb], sh, sl);
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          bk[ks] = row_operand<D>(cur + L::K, perm_pos(n), 2 * (2 * fb + ks) + g);
-          if constexpr (!XQ) bkl[ks] = row_operand<D>(cur + L::KL, perm_pos(n), 2 * (2 * fb + ks) + g);
-        }
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          dvt = mfma(sh[ks], bk[ks], dvt);
-          dvt = mfma(sl[ks], bk[ks], dvt);
-          if constexpr (!XQ) dvt = mfma(sh[ks], bkl[ks], dvt);
-        }
-      }
-      if constexpr (DECAY != 0) dvt *= es;
       u32x4 ogt[2], oglt[2];
       tr_ops<D, 2>(cur + L::GH, 32 * wb, lane, ogt);
       tr_ops<D, 2>(cur + L::GL, 32 * wb, lane, oglt);
@@ -648,6 +651,25 @@ __global__ __launch_bounds__(128 * (D / 32)) void bwd_pass_b2(const BwArgs a) {
       stage_next();
     } else {
       stage_next();
+      // dphi(k)^T / beta_s (rows f of block wb, columns s): e^{l_last - l_s}
+      // (G v + gz) + phi(Q)^T B, with G^T from the registers (contracting
+      // over j) against v read at permuted positions; the G^T products first,
+      // so that the state's split meets B's MFMAs
+      f32x16 dkt = zero16();
+#pragma unroll
+      for (int jb = 0; jb < NJ; ++jb) {
+        u32x4 sh[2], sl[2], ov[2];
+        split_acc(X[jb], sh, sl);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) ov[ks] = row_operand_perm<D>(cur + L::V, perm_pos(n), 2 * jb + ks, g);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          dkt = mfma(sh[ks], ov[ks], dkt);
+          dkt = mfma(sl[ks], ov[ks], dkt);
+        }
+      }
+      if constexpr (DECAY != 0) dkt *= es;
+
       // B (rows t, columns s = n): g_t . v_s + h_t
       f32x16 bt = zero16();
 #pragma unroll
@@ -675,23 +697,6 @@ __global__ __launch_bounds__(128 * (D / 32)) void bwd_pass_b2(const BwArgs a) {
       u32x4 bh_[2], bl_[2];
       split_acc(bt, bh_, bl_);
 
-      // dphi(k)^T / beta_s (rows f of block wb, columns s): e^{l_last - l_s}
-      // (G v + gz) + phi(Q)^T B, with G^T from the registers (contracting
-      // over j) against v read at permuted positions
-      f32x16 dkt = zero16();
-#pragma unroll
-      for (int jb = 0; jb < NJ; ++jb) {
-        u32x4 sh[2], sl[2], ov[2];
-        split_acc(X[jb], sh, sl);
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) ov[ks] = row_operand_perm<D>(cur + L::V, perm_pos(n), 2 * jb + ks, g);
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          dkt = mfma(sh[ks], ov[ks], dkt);
-          dkt = mfma(sl[ks], ov[ks], dkt);
-        }
-      }
-      if constexpr (DECAY != 0) dkt *= es;
       u32x4 oqt[2], oqlt[2];
       tr_ops<D, 2>(cur + L::Q, 32 * wb, lane, oqt);
       if constexpr (!XQ) tr_ops<D, 2>(cur + L::QL, 32 * wb, lane, oqlt);
