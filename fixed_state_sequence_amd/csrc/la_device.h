@@ -35,9 +35,13 @@ __device__ __forceinline__ float elu1_fast(float x) { return fmaxf(x + 1.f, __ex
 
 // log f of an mLSTM forget gate from its pre-activation x (wikillm "Linear
 // attention", Variants / mLSTM: a sigmoid forget gate, or an exponential
-// one): log sigmoid(x) = min(x, 0) - log(1 + e^{-|x|}), or x itself.
+// one): log sigmoid(x) = min(x, 0) - log(1 + e^{-|x|}), or x itself.  The
+// hardware exp2/log2 instructions serve: log(1 + y) for y = e^{-|x|} in
+// (0, 1] comes within about 1e-7 absolute of log1p(y) (where 1 + y rounds to
+// 1, y itself is below 6e-8), in a few instructions where the library's
+// accurate exp and log1p take long range-reduction sequences.
 __device__ __forceinline__ float log_forget(float x, int exp_form) {
-  return exp_form ? x : fminf(x, 0.f) - log1pf(expf(-fabsf(x)));
+  return exp_form ? x : fminf(x, 0.f) - __logf(1.f + __expf(-fabsf(x)));
 }
 
 // Reciprocal-like read-out factor for the three read-out forms, of a state
