@@ -317,7 +317,7 @@ template <int D, int DECAY>
 struct BL2 {
   static constexpr int NJ = D / 32;          // 32-wide blocks of D
   static constexpr int NW = 2 * NJ;          // value waves, then feature waves
-  static constexpr int NT = 64 * NW;         // = 32 rows x BPR blocks: one staged block per thread
+  static constexpr int NT = 64 * NW;         // threads per workgroup; each kind of wave stages two rows per thread
   static constexpr int BPR = D / 8;
   static constexpr int TILE = BCH * D * 2;
   // one buffer: token tiles (bf16, rows at perm_pos(token), tile_off<D>)
@@ -355,112 +355,147 @@ __device__ __forceinline__ u32x4 row_operand_perm(const char* tile, int r, int k
   return u32x4{x[0], x[1], y[0], y[1]};
 }
 
-// Raw inputs of one chunk for one thread: row tid / BPR, block tid % BPR;
-// and the decay value of token lane % 32.
+// Pass B2's staging is split by kind of wave.  Each thread covers rows r0
+// and r0 + 16 of feature block b (r0 = i / BPR, b = i % BPR, i = its index
+// among the threads of its kind).  The value waves' threads stage phi(q),
+// g = r_t dout (with a decay also e^{l_t} g), the decay's prefix, beta and
+// total, and h_t; the feature waves' threads stage v.  The value waves
+// stage after their products, the feature waves before theirs; the feature
+// waves' products are the longer part of a chunk, so they get the least of
+// the staging.  phi(k) goes with the value waves' part, except with identity
+// features (mLSTM), where it is the raw k and costs little to stage: there
+// the feature waves take it (measured faster both ways round).
+template <int DECAY>
+constexpr bool b2_k_on_value() { return DECAY != 3; }
+
+// Raw inputs of one chunk for one thread of the split staging.
 struct Raw2 {
-  u32x4 q, k, v;
-  u32x4 d[2];    // dout as loaded: 8 fp32 (both words) or 8 bf16 (the first)
-  float2 th;     // r_t and h_t (from pass A)
-  float2 al;     // alpha (mLSTM: log alpha' and beta', from pass A)
+  u32x4 x[2];         // value threads: q of both rows; feature threads: v
+  u32x4 y[2];         // k of both rows (for the kind that stages phi(k))
+  u32x4 d[2][2];      // value threads: dout of both rows as loaded (8 fp32: both words; 8 bf16: the first)
+  float2 th[2];       // value threads: r_t and h_t of both rows (from pass A)
+  float2 al;          // value threads: alpha of token lane % 32 (mLSTM: log alpha', beta', from pass A)
 };
 
-template <int D, int DECAY, bool DF32>
-__device__ __forceinline__ void load_raw2(const BwArgs& a, int64_t bh, int t0, int tid, Raw2& x) {
+template <int D, int DECAY, bool DF32, bool VR>
+__device__ __forceinline__ void load_raw2(const BwArgs& a, int64_t bh, int t0, int i, Raw2& x) {
   constexpr int BPR = D / 8;
-  const int r = tid / BPR, b = tid % BPR;
+  constexpr bool KH = VR == b2_k_on_value<DECAY>();   // phi(k) staged here
+  const int r0 = i / BPR, b = i % BPR;
   // the chunk's first token (uniform), and 32-bit offsets within the chunk
   // (rows past the end read the last token)
   const int64_t tc = bh * int64_t(a.T) + t0;
-  const uint32_t tr = uint32_t(min(t0 + r, a.T - 1) - t0);
-  const uint32_t off = tr * D + 8 * b;
-  x.th = reinterpret_cast<const float2*>(a.tok + tc * 2)[tr];
-  x.q = *reinterpret_cast<const u32x4*>(a.q + tc * D + off);
-  x.k = *reinterpret_cast<const u32x4*>(a.k + tc * D + off);
-  x.v = *reinterpret_cast<const u32x4*>(a.v + tc * D + off);
-  if constexpr (DF32) {
-    const float* dp = static_cast<const float*>(a.dout) + tc * D + off;
-    x.d[0] = *reinterpret_cast<const u32x4*>(dp);
-    x.d[1] = *reinterpret_cast<const u32x4*>(dp + 4);
-  } else {
-    x.d[0] = *reinterpret_cast<const u32x4*>(static_cast<const bf16_t*>(a.dout) + tc * D + off);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t tr = uint32_t(min(t0 + r0 + 16 * h, a.T - 1) - t0);
+    const uint32_t off = tr * D + 8 * b;
+    if constexpr (KH) x.y[h] = *reinterpret_cast<const u32x4*>(a.k + tc * D + off);
+    if constexpr (VR) {
+      x.x[h] = *reinterpret_cast<const u32x4*>(a.q + tc * D + off);
+      x.th[h] = reinterpret_cast<const float2*>(a.tok + tc * 2)[tr];
+      if constexpr (DF32) {
+        const float* dp = static_cast<const float*>(a.dout) + tc * D + off;
+        x.d[h][0] = *reinterpret_cast<const u32x4*>(dp);
+        x.d[h][1] = *reinterpret_cast<const u32x4*>(dp + 4);
+      } else {
+        x.d[h][0] = *reinterpret_cast<const u32x4*>(static_cast<const bf16_t*>(a.dout) + tc * D + off);
+      }
+    } else {
+      x.x[h] = *reinterpret_cast<const u32x4*>(a.v + tc * D + off);
+    }
   }
-  x.al = make_float2(1.f, 1.f);
-  const uint32_t ta = uint32_t(min(t0 + (tid & 31), a.T - 1) - t0);
-  if constexpr (DECAY == 3) x.al = reinterpret_cast<const float2*>(a.ab + tc * 2)[ta];
-  else if constexpr (DECAY != 0) x.al.x = (a.decay + tc)[ta];
+  if constexpr (VR) {
+    x.al = make_float2(1.f, 1.f);
+    const uint32_t ta = uint32_t(min(t0 + (i & 31), a.T - 1) - t0);
+    if constexpr (DECAY == 3) x.al = reinterpret_cast<const float2*>(a.ab + tc * 2)[ta];
+    else if constexpr (DECAY != 0) x.al.x = (a.decay + tc)[ta];
+  }
 }
 
-// Stage one chunk into buffer buf: phi(q) (high, low), phi(k) (high, low, at
-// permuted feature positions), v, g = r_t dout (high, low; with a decay also
-// e^{l_t} g), and the per-token scalars.  Rows past the end are zero (FULL:
-// the chunk lies wholly inside the sequence, and no row is tested).
-template <int D, int DECAY, bool DF32, bool FULL = false>
-__device__ __forceinline__ void stage2(const BwArgs& a, int t0, int tid, const Raw2& x, char* buf) {
+// Stage this thread's part of one chunk into buffer buf: phi(q) (high, low),
+// phi(k) (high, low, at permuted feature positions), v, g = r_t dout (high,
+// low; with a decay also e^{l_t} g), and the per-token scalars.  Rows past
+// the end are zero (FULL: the chunk lies wholly inside the sequence, and no
+// row is tested).
+template <int D, int DECAY, bool DF32, bool VR, bool FULL = false>
+__device__ __forceinline__ void stage2(const BwArgs& a, int t0, int i, const Raw2& x, char* buf) {
   using L = BL2<D, DECAY>;
+  constexpr bool KH = VR == b2_k_on_value<DECAY>();   // phi(k) staged here
   float* F = reinterpret_cast<float*>(buf + L::FB);
-  const int r = tid / L::BPR, b = tid % L::BPR, lane = tid & 63;
+  const int r0 = i / L::BPR, b = i % L::BPR, lane = i & 63;
   float lam = 0.f, bet = 1.f, tot = 0.f;
-  if constexpr (DECAY == 3) {
-    // log alpha' and beta' as pass A left them
-    const bool vt = t0 + (lane & 31) < a.T;
-    lam = wave_scan<32>(vt ? x.al.x : 0.f, 0.f, ScanAdd{});
-    bet = vt ? x.al.y : 0.f;
-    tot = lane_bcast(lam, 31);
-  } else if constexpr (DECAY != 0) {
-    chunk_decay<DECAY>(x.al.x, t0, a.T, lane, lam, bet, tot);
-  }
-  if (tid < BCH) {
-    F[L::LAM + tid] = lam;
-    F[L::BET + tid] = bet;
-    if (tid == 0) F[L::TOT] = tot;
-  }
-  const bool valid = FULL || t0 + r < a.T;
-  const int pr = perm_pos(r);
-  float lr = 0.f;
-  if constexpr (DECAY != 0) lr = __shfl(lam, r);
-  float fq[8], fk[8];
-  unpack8(x.q, fq, bf16_t{});
-  unpack8(x.k, fk, bf16_t{});
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    fq[e] = valid ? (DECAY == 3 ? fq[e] : elu1_fast(fq[e])) : 0.f;
-    fk[e] = valid ? (DECAY == 3 ? fk[e] : elu1_fast(fk[e])) : 0.f;
-  }
-  // identity features of bf16 inputs (mLSTM) are exact in bf16: no low parts
-  const u32x4 qh = pack8(fq);
-  blk_write<D>(buf + L::Q, pr, b, qh);
-  if constexpr (DECAY != 3) blk_write<D>(buf + L::QL, pr, b, low8(fq, qh));
-  const u32x4 kh = pack8(fk);
-  row_write_perm<D>(buf + L::K, pr, b, kh);
-  if constexpr (DECAY != 3) row_write_perm<D>(buf + L::KL, pr, b, low8(fk, kh));
-  blk_write<D>(buf + L::V, pr, b, valid ? x.v : u32x4{0u, 0u, 0u, 0u});
-  const float rt = valid ? x.th.x : 0.f, ht = valid ? x.th.y : 0.f;
-  float gv[8];
-  if constexpr (DF32) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      gv[e] = __uint_as_float(x.d[0][e]);
-      gv[e + 4] = __uint_as_float(x.d[1][e]);
+  if constexpr (VR) {
+    if constexpr (DECAY == 3) {
+      // log alpha' and beta' as pass A left them
+      const bool vt = t0 + (lane & 31) < a.T;
+      lam = wave_scan<32>(vt ? x.al.x : 0.f, 0.f, ScanAdd{});
+      bet = vt ? x.al.y : 0.f;
+      tot = lane_bcast(lam, 31);
+    } else if constexpr (DECAY != 0) {
+      chunk_decay<DECAY>(x.al.x, t0, a.T, lane, lam, bet, tot);
     }
-  } else {
-    unpack8(x.d[0], gv, bf16_t{});
+    if (i < BCH) {
+      F[L::LAM + i] = lam;
+      F[L::BET + i] = bet;
+      if (i == 0) F[L::TOT] = tot;
+    }
   }
 #pragma unroll
-  for (int e = 0; e < 8; ++e) gv[e] *= rt;
-  const u32x4 gh = pack8(gv);
-  blk_write<D>(buf + L::GH, pr, b, gh);
-  blk_write<D>(buf + L::GL, pr, b, low8(gv, gh));
-  const float wq = DECAY ? __expf(lr) : 1.f;   // query weight from the chunk's start
-  if constexpr (DECAY != 0) {
+  for (int h = 0; h < 2; ++h) {
+    const int r = r0 + 16 * h;
+    const bool valid = FULL || t0 + r < a.T;
+    const int pr = perm_pos(r);
+    if constexpr (KH) {
+      float fk[8];
+      unpack8(x.y[h], fk, bf16_t{});
 #pragma unroll
-    for (int e = 0; e < 8; ++e) gv[e] *= wq;
-    const u32x4 wh = pack8(gv);
-    blk_write<D>(buf + L::WH, pr, b, wh);
-    blk_write<D>(buf + L::WL, pr, b, low8(gv, wh));
-  }
-  if (b == 0) {
-    F[L::HT + r] = ht;
-    F[L::HW + pr] = wq * ht;
+      for (int e = 0; e < 8; ++e) fk[e] = valid ? (DECAY == 3 ? fk[e] : elu1_fast(fk[e])) : 0.f;
+      // identity features of bf16 inputs (mLSTM) are exact in bf16: no low parts
+      const u32x4 kh = pack8(fk);
+      row_write_perm<D>(buf + L::K, pr, b, kh);
+      if constexpr (DECAY != 3) row_write_perm<D>(buf + L::KL, pr, b, low8(fk, kh));
+    }
+    if constexpr (VR) {
+      float fq[8];
+      unpack8(x.x[h], fq, bf16_t{});
+#pragma unroll
+      for (int e = 0; e < 8; ++e) fq[e] = valid ? (DECAY == 3 ? fq[e] : elu1_fast(fq[e])) : 0.f;
+      const u32x4 qh = pack8(fq);
+      blk_write<D>(buf + L::Q, pr, b, qh);
+      if constexpr (DECAY != 3) blk_write<D>(buf + L::QL, pr, b, low8(fq, qh));
+      float lr = 0.f;
+      if constexpr (DECAY != 0) lr = __shfl(lam, r);
+      const float rt = valid ? x.th[h].x : 0.f, ht = valid ? x.th[h].y : 0.f;
+      float gv[8];
+      if constexpr (DF32) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          gv[e] = __uint_as_float(x.d[h][0][e]);
+          gv[e + 4] = __uint_as_float(x.d[h][1][e]);
+        }
+      } else {
+        unpack8(x.d[h][0], gv, bf16_t{});
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) gv[e] *= rt;
+      const u32x4 gh = pack8(gv);
+      blk_write<D>(buf + L::GH, pr, b, gh);
+      blk_write<D>(buf + L::GL, pr, b, low8(gv, gh));
+      const float wq = DECAY ? __expf(lr) : 1.f;   // query weight from the chunk's start
+      if constexpr (DECAY != 0) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) gv[e] *= wq;
+        const u32x4 wh = pack8(gv);
+        blk_write<D>(buf + L::WH, pr, b, wh);
+        blk_write<D>(buf + L::WL, pr, b, low8(gv, wh));
+      }
+      if (b == 0) {
+        F[L::HT + r] = ht;
+        F[L::HW + pr] = wq * ht;
+      }
+    } else {
+      blk_write<D>(buf + L::V, pr, b, valid ? x.x[h] : u32x4{0u, 0u, 0u, 0u});
+    }
   }
 }
 
@@ -515,10 +550,18 @@ __global__ __launch_bounds__(128 * (D / 32)) void bwd_pass_b2(const BwArgs a) {
       reinterpret_cast<float*>(smem + L::GZ)[32 * wb + n] = src[D * D + 32 * wb + n];
   }
 
+  // the last chunk staged, the one before it loaded; each kind of wave its
+  // part (si: the thread's index among the threads of its kind)
   Raw2 raw;
-  load_raw2<D, DECAY, DF32>(a, bh, (c1 - 1) * BCH, tid, raw);
-  stage2<D, DECAY, DF32>(a, (c1 - 1) * BCH, tid, raw, smem);
-  if (c1 - 2 >= c0) load_raw2<D, DECAY, DF32>(a, bh, (c1 - 2) * BCH, tid, raw);
+  const int si = tid & (64 * NJ - 1);
+  auto first = [&](auto value_kind) {
+    constexpr bool VR = decltype(value_kind)::value;
+    load_raw2<D, DECAY, DF32, VR>(a, bh, (c1 - 1) * BCH, si, raw);
+    stage2<D, DECAY, DF32, VR>(a, (c1 - 1) * BCH, si, raw, smem);
+    if (c1 - 2 >= c0) load_raw2<D, DECAY, DF32, VR>(a, bh, (c1 - 2) * BCH, si, raw);
+  };
+  if (value_wave) first(std::true_type{});
+  else first(std::false_type{});
   __syncthreads();
 
   // one loop per kind of wave (each keeps only its own loop-invariant
@@ -539,8 +582,9 @@ __global__ __launch_bounds__(128 * (D / 32)) void bwd_pass_b2(const BwArgs a) {
         // they would not fit the registers of two waves per SIMD
         int ts = tid;
         asm volatile("" : "+v"(ts));
-        stage2<D, DECAY, DF32, true>(a, t0 - BCH, ts, raw, nxt);   // every chunk but the last is whole
-        if (c - 2 >= c0) load_raw2<D, DECAY, DF32>(a, bh, t0 - 2 * BCH, ts, raw);
+        ts &= 64 * NJ - 1;
+        stage2<D, DECAY, DF32, VW, true>(a, t0 - BCH, ts, raw, nxt);   // every chunk but the last is whole
+        if (c - 2 >= c0) load_raw2<D, DECAY, DF32, VW>(a, bh, t0 - 2 * BCH, ts, raw);
       }
     };
     const bool vs = t0 + n < T;
