@@ -1013,9 +1013,7 @@ __device__ __forceinline__ void stage3(const BwArgs& a, int64_t bh, int t0, int 
     *reinterpret_cast<f32x4*>(znew + 8 * b) = f32x4{z[0], z[1], z[2], z[3]};
     *reinterpret_cast<f32x4*>(znew + 8 * b + 4) = f32x4{z[4], z[5], z[6], z[7]};
   }
-  float inc[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) inc[e] = 0.f;
+  float inc[8];   // set by the first row (adding to 0.f would cost an instruction each)
   // the rows; a chunk wholly inside the sequence takes no validity selects
   auto rows = [&](auto full_kind) {
     constexpr bool FULL = decltype(full_kind)::value;
@@ -1049,7 +1047,7 @@ __device__ __forceinline__ void stage3(const BwArgs& a, int64_t bh, int t0, int 
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         part += fq[e] * z[e];
-        inc[e] += wk * fk[e];
+        inc[e] = rr == 0 ? wk * fk[e] : fmaf(wk, fk[e], inc[e]);
       }
       if constexpr (L::WT) {
         float wv[8];

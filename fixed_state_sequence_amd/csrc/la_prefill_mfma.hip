@@ -233,12 +233,18 @@ __device__ __forceinline__ void fetch_chunk(RawChunk<RPT, ND, HAS_Q, HAS_KV, HAS
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
     const int t = min(tok0 + RPT * rg + i, T - 1);
-    // 32-bit element offsets within the (b, h) slab (T D < 2^31 is checked on the host)
-    const uint32_t off = uint32_t(t) * D + 8 * fb;
-    if constexpr (HAS_Q) r.q[i] = *reinterpret_cast<const u32x4*>(qg + off);
+    // 32-bit byte offsets within the (b, h) slab (T D < 2^31 elements of 2
+    // bytes is checked on the host), so that each load takes the slab's
+    // uniform base as its scalar address and one offset register
+    static_assert(sizeof(DT) == 2, "bf16 or fp16 inputs");
+    const uint32_t ob = (uint32_t(t) * D + 8 * fb) * uint32_t(sizeof(DT));
+    auto at = [&](const DT* base) {
+      return *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(base) + ob);
+    };
+    if constexpr (HAS_Q) r.q[i] = at(qg);
     if constexpr (HAS_KV) {
-      r.k[i] = *reinterpret_cast<const u32x4*>(kg + off);
-      r.v[i] = *reinterpret_cast<const u32x4*>(vg + off);
+      r.k[i] = at(kg);
+      r.v[i] = at(vg);
     }
   }
   if constexpr (DECAY != 0) {
@@ -780,7 +786,9 @@ void output_kernel(const PfArgs a) {
         fetch(raw, min(c + G::PDEPTH, c1 - 1));
         return 0.f;
       }
-      float dz[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      // this thread's z increments: its first row sets them (adding to 0.f
+      // would cost an instruction each, kept for the sign of zero)
+      float dz[8];
       // the chunks read out (prec) and folded (exact) at high + low precision (see QR)
       const bool prec = DECAY != 3 && tok0 < G::PRECISE && (DECAY == 0 || lrun > G::PREC_LOG);
       const bool exact = DECAY != 3 && tok0 < G::EXACT;
@@ -833,7 +841,7 @@ void output_kernel(const PfArgs a) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             kx[e] *= w;
-            dz[e] += kx[e];
+            dz[e] = i == 0 ? kx[e] : dz[e] + kx[e];
           }
           const u32x4 kh = pack8(kx);
           blk_write<D>(buf + G::B_KH, perm_pos(r), fb, kh);
@@ -841,7 +849,7 @@ void output_kernel(const PfArgs a) {
             blk_write<D>(buf + G::B_KL, perm_pos(r), fb, low8(kx, kh));
         } else {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) dz[e] += kx[e];
+          for (int e = 0; e < 8; ++e) dz[e] = i == 0 ? kx[e] : dz[e] + kx[e];
           blk_write<D>(buf + G::B_KH, perm_pos(r), fb, kp);
           if (fin || exact) blk_write<D>(buf + G::B_KL, perm_pos(r), fb, low8(kx, kp));
         }
