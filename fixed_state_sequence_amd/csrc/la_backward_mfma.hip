@@ -355,6 +355,15 @@ __device__ __forceinline__ u32x4 row_operand_perm(const char* tile, int r, int k
   return u32x4{x[0], x[1], y[0], y[1]};
 }
 
+// A load at a uniform base plus a 32-bit byte offset: the global load's
+// scalar-address form, one offset register, where an element offset widened
+// to 64 bits costs a 64-bit vector add per load.  The offsets here stay
+// within a chunk's rows.
+template <class V, class T>
+__device__ __forceinline__ V ld_at(const T* base, uint32_t byte_off) {
+  return *reinterpret_cast<const V*>(reinterpret_cast<const char*>(base) + byte_off);
+}
+
 // Pass B2's staging is split by kind of wave.  Each thread covers rows r0
 // and r0 + 16 of feature block b (r0 = i / BPR, b = i % BPR, i = its index
 // among the threads of its kind).  The value waves' threads stage phi(q),
@@ -389,26 +398,26 @@ __device__ __forceinline__ void load_raw2(const BwArgs& a, int64_t bh, int t0, i
   for (int h = 0; h < 2; ++h) {
     const uint32_t tr = uint32_t(min(t0 + r0 + 16 * h, a.T - 1) - t0);
     const uint32_t off = tr * D + 8 * b;
-    if constexpr (KH) x.y[h] = *reinterpret_cast<const u32x4*>(a.k + tc * D + off);
+    if constexpr (KH) x.y[h] = ld_at<u32x4>(a.k + tc * D, 2 * off);
     if constexpr (VR) {
-      x.x[h] = *reinterpret_cast<const u32x4*>(a.q + tc * D + off);
-      x.th[h] = reinterpret_cast<const float2*>(a.tok + tc * 2)[tr];
+      x.x[h] = ld_at<u32x4>(a.q + tc * D, 2 * off);
+      x.th[h] = ld_at<float2>(a.tok + tc * 2, 8 * tr);
       if constexpr (DF32) {
-        const float* dp = static_cast<const float*>(a.dout) + tc * D + off;
-        x.d[h][0] = *reinterpret_cast<const u32x4*>(dp);
-        x.d[h][1] = *reinterpret_cast<const u32x4*>(dp + 4);
+        const float* dp = static_cast<const float*>(a.dout) + tc * D;
+        x.d[h][0] = ld_at<u32x4>(dp, 4 * off);
+        x.d[h][1] = ld_at<u32x4>(dp, 4 * off + 16);
       } else {
-        x.d[h][0] = *reinterpret_cast<const u32x4*>(static_cast<const bf16_t*>(a.dout) + tc * D + off);
+        x.d[h][0] = ld_at<u32x4>(static_cast<const bf16_t*>(a.dout) + tc * D, 2 * off);
       }
     } else {
-      x.x[h] = *reinterpret_cast<const u32x4*>(a.v + tc * D + off);
+      x.x[h] = ld_at<u32x4>(a.v + tc * D, 2 * off);
     }
   }
   if constexpr (VR) {
     x.al = make_float2(1.f, 1.f);
     const uint32_t ta = uint32_t(min(t0 + (i & 31), a.T - 1) - t0);
-    if constexpr (DECAY == 3) x.al = reinterpret_cast<const float2*>(a.ab + tc * 2)[ta];
-    else if constexpr (DECAY != 0) x.al.x = (a.decay + tc)[ta];
+    if constexpr (DECAY == 3) x.al = ld_at<float2>(a.ab + tc * 2, 8 * ta);
+    else if constexpr (DECAY != 0) x.al.x = ld_at<float>(a.decay + tc, 4 * ta);
   }
 }
 
@@ -911,15 +920,15 @@ __device__ __forceinline__ void load_raw3(const BwArgs& a, int64_t bh, int t0, i
 #pragma unroll
   for (int rr = 0; rr < 2; ++rr) {
     const uint32_t off = uint32_t(min(t0 + r + 16 * rr, a.T - 1) - t0) * D + 8 * b;
-    x.q[rr] = *reinterpret_cast<const u32x4*>(a.q + tc * D + off);
-    x.k[rr] = *reinterpret_cast<const u32x4*>(a.k + tc * D + off);
-    x.v[rr] = *reinterpret_cast<const u32x4*>(a.v + tc * D + off);
+    x.q[rr] = ld_at<u32x4>(a.q + tc * D, 2 * off);
+    x.k[rr] = ld_at<u32x4>(a.k + tc * D, 2 * off);
+    x.v[rr] = ld_at<u32x4>(a.v + tc * D, 2 * off);
   }
   x.al = 1.f;
   x.ig = 0.f;
   const uint32_t ta = uint32_t(min(t0 + (ft & 31), a.T - 1) - t0);
-  if constexpr (DECAY != 0) x.al = (a.decay + tc)[ta];
-  if constexpr (DECAY == 3) x.ig = (a.igate + tc)[ta];
+  if constexpr (DECAY != 0) x.al = ld_at<float>(a.decay + tc, 4 * ta);
+  if constexpr (DECAY == 3) x.ig = ld_at<float>(a.igate + tc, 4 * ta);
 }
 
 // dout of token t0 + n at features 32 wb + 8 r + 4 g .. + 3, r = 0..3, for a
@@ -930,15 +939,15 @@ __device__ __forceinline__ void load_dout3(const BwArgs& a, int64_t bh, int t0, 
   const int64_t tc = bh * int64_t(a.T) + t0;
   const uint32_t off = uint32_t(min(t0 + n, a.T - 1) - t0) * D + 32 * wb + 4 * g;
   if constexpr (DF32) {
-    const float* p = static_cast<const float*>(a.dout) + tc * D + off;
+    const float* p = static_cast<const float*>(a.dout) + tc * D;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) d[r] = *reinterpret_cast<const u32x4*>(p + 8 * r);
+    for (int r = 0; r < 4; ++r) d[r] = ld_at<u32x4>(p, 4 * off + 32 * r);
   } else {
-    const bf16_t* p = static_cast<const bf16_t*>(a.dout) + tc * D + off;
+    const bf16_t* p = static_cast<const bf16_t*>(a.dout) + tc * D;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const u32x2 x = *reinterpret_cast<const u32x2*>(p + 16 * h);
-      const u32x2 y = *reinterpret_cast<const u32x2*>(p + 16 * h + 8);
+      const u32x2 x = ld_at<u32x2>(p, 2 * off + 32 * h);
+      const u32x2 y = ld_at<u32x2>(p, 2 * off + 32 * h + 16);
       d[h] = u32x4{x[0], x[1], y[0], y[1]};
     }
   }
