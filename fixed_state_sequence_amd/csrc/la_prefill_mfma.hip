@@ -799,14 +799,32 @@ void output_kernel(const PfArgs a) {
       // e^-(lp + lgam); past it the consumers apply the factor (lp = 0)
       const float lnew = lp + lgam;
       const float lsc = DECAY != 0 && fabsf(lnew) <= kDeferLog ? lnew : 0.f;
+      // mLSTM with one token per lane (C <= 64): the per-token factors below
+      // are formed once, in the token's lane, and the rows read them from
+      // there (the same operations on the same values as forming them per row)
+      constexpr bool TOKF = DECAY == 3 && G::ND == 1;
+      float wl = 0.f, efl = 0.f;
+      if constexpr (TOKF) {
+        const float lctl = m0 - mlo;
+        wl = tok0 + lane < a.T ? __expf(alo - mend - lsc) : 0.f;
+        efl = __expf(lctl);
+        if (wave == 0 && lane < C) {
+          Ll[lane] = lctl;
+          Bl[lane] = G::HAS_DM ? 1.f : __expf(alo - mlo);
+          Ml[lane] = lo + mlo;
+        }
+      }
 #pragma unroll
       for (int i = 0; i < G::RPT; ++i) {
         const int r = G::RPT * rg + i;
         float qx[8], kx[8];
         unpack8(raw.q[i], qx, DT{});
         unpack8(raw.k[i], kx, DT{});
-        float lct = 0.f, w = 1.f, beta = 1.f, mt = 0.f;
-        if constexpr (DECAY == 3) {
+        float lct = 0.f, w = 1.f, beta = 1.f, mt = 0.f, ef = 1.f;
+        if constexpr (TOKF) {
+          w = lane_value<C>(wl, 0.f, r);
+          ef = lane_value<C>(efl, 0.f, r);
+        } else if constexpr (DECAY == 3) {
           // lct := m0 - mu_t (inter-chunk factor e^{lct}); beta := e^{a_t - mu_t},
           // so that e^{lct_t - lct_s} beta_s = e^{a_s - mu_t}; m_t = lc_t + mu_t
           const float mu = lane_value<C>(mlo, mhi, r), at = lane_value<C>(alo, ahi, r);
@@ -864,11 +882,15 @@ void output_kernel(const PfArgs a) {
         }
         den = row_sum<G::FB>(den);
         if (fb == 0) {
-          if constexpr (DECAY != 0) den *= __expf(lct);
-          denl[r] = den;
-          Ll[r] = lct;
-          Bl[r] = beta;
-          if constexpr (DECAY == 3) Ml[r] = mt;
+          if constexpr (TOKF) {
+            denl[r] = den * ef;
+          } else {
+            if constexpr (DECAY != 0) den *= __expf(lct);
+            denl[r] = den;
+            Ll[r] = lct;
+            Bl[r] = beta;
+            if constexpr (DECAY == 3) Ml[r] = mt;
+          }
         }
       }
       {
